@@ -1,0 +1,248 @@
+"""Python wrapper of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. It never imports the
+HIP library package and the HIP library never imports it.
+
+Every function takes and returns numpy arrays. Element types are named by
+the tags of ``workloads`` ("f32", "bf16", "i8", "u8"); bf16 tensors travel
+as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_TYPE = {"f32": 0, "bf16": 1, "i8": 2, "u8": 3}
+_ACT = {"identity": 0, "relu": 1, "leaky_relu": 2}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load oracle/liboracle.so, compiling it with gcc first if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = C.CDLL(_build.LIB)
+        vp, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
+        L.oracle_bf16_to_f32.argtypes = [C.c_uint16]
+        L.oracle_bf16_to_f32.restype = C.c_float
+        L.oracle_f32_to_bf16.argtypes = [C.c_float]
+        L.oracle_f32_to_bf16.restype = C.c_uint16
+        L.oracle_quantize_linear.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp]
+        L.oracle_dequantize_linear.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
+        L.oracle_quantize_rows.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, vp]
+        L.oracle_quantize_cols.argtypes = [vp, i32, i64, i64, i32, vp, vp]
+        L.oracle_colsum.argtypes = [vp, i64, i64, vp]
+        L.oracle_int_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.oracle_epilogue.argtypes = [vp, vp, vp, i32, vp, i32, f32, i64, i64, i32, vp]
+        L.oracle_dqip_forward.argtypes = [vp, i32, vp, i32, vp, i64, i64, i64,
+                                          vp, i64, i32, i32, vp, i32, f32, i32,
+                                          vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_qlinear_conv.argtypes = [vp, i32, i64, i64, i64, i64, f32, i32,
+                                          vp, i32, i64, i64, i64, vp, vp, i64, vp,
+                                          f32, i32, i32, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with status {rc}")
+
+
+def _np_type(tag):
+    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "u8": np.uint8}[tag]
+
+
+# ------------------------------------------------------------------ helpers
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    L = lib()
+    b = _c(bits, np.uint16).reshape(-1)
+    return np.array([L.oracle_bf16_to_f32(int(v)) for v in b], np.float32).reshape(np.shape(bits))
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    L = lib()
+    a = _c(x, np.float32).reshape(-1)
+    return np.array([L.oracle_f32_to_bf16(float(v)) for v in a], np.uint16).reshape(np.shape(x))
+
+
+def _axis(ndim, axis):
+    if axis is None:
+        return -1
+    if axis < -ndim or axis >= ndim:
+        raise ValueError("axis out of range")
+    return axis + ndim if axis < 0 else axis
+
+
+def _params(scale, zp, n_expected):
+    s = _c(np.atleast_1d(scale), np.float32)
+    z = _c(np.atleast_1d(np.zeros_like(s, dtype=np.int32) if zp is None else zp), np.int32)
+    if s.size != n_expected or z.size != n_expected:
+        raise ValueError("scale / zero point length does not match the axis")
+    return s, z
+
+
+# ------------------------------------------------------- QuantizeLinear etc.
+
+def quantize_linear(x, scale, zp, *, axis=None, y_type="i8"):
+    """y = saturate(rne(x / scale) + zp); axis None = per tensor."""
+    x = _c(x, np.float32)
+    ax = _axis(x.ndim, axis)
+    s, z = _params(scale, zp, 1 if ax < 0 else x.shape[ax])
+    shape = np.array(x.shape if x.ndim else (1,), np.int64)
+    y = np.empty(x.shape, _np_type(y_type))
+    rc = lib().oracle_quantize_linear(_p(x), max(x.ndim, 1), _p(shape), ax, _p(s), _p(z),
+                                      _TYPE[y_type], _p(y))
+    _check(rc, "quantize_linear")
+    return y
+
+
+def dequantize_linear(x, scale, zp, *, axis=None):
+    """y = (x - zp) * scale; x int8 or uint8; axis None = per tensor."""
+    x = np.ascontiguousarray(x)
+    xt = "u8" if x.dtype == np.uint8 else "i8"
+    ax = _axis(x.ndim, axis)
+    s, z = _params(scale, zp, 1 if ax < 0 else x.shape[ax])
+    shape = np.array(x.shape if x.ndim else (1,), np.int64)
+    y = np.empty(x.shape, np.float32)
+    rc = lib().oracle_dequantize_linear(_p(x), _TYPE[xt], max(x.ndim, 1), _p(shape), ax,
+                                        _p(s), _p(z), _p(y))
+    _check(rc, "dequantize_linear")
+    return y
+
+
+# ---------------------------------------- dynamic quantized inner product
+
+def quantize_rows(A, typeA="f32", rows=None):
+    """Per-row dynamic quantization of A [M,K] -> (uA, scaleA, zeroA)."""
+    A = _c(A, _np_type(typeA))
+    M, K = A.shape
+    r = None if rows is None else _c(rows, np.int64)
+    n = M if r is None else r.size
+    uA = np.empty((n, K), np.uint8)
+    sA = np.empty(n, np.float32)
+    zA = np.empty(n, np.int32)
+    _check(lib().oracle_quantize_rows(_p(A), _TYPE[typeA], M, K, _p(r), n, _p(uA),
+                                      _p(sA), _p(zA)), "quantize_rows")
+    return uA, sA, zA
+
+
+def quantize_cols(B, typeB="f32", avoid=False):
+    """Per-column dynamic quantization of B [K,N] -> (iB [K,N], scaleB [N])."""
+    B = _c(B, _np_type(typeB))
+    K, N = B.shape
+    iB = np.empty((K, N), np.int8)
+    sB = np.empty(N, np.float32)
+    _check(lib().oracle_quantize_cols(_p(B), _TYPE[typeB], K, N, int(bool(avoid)), _p(iB),
+                                      _p(sB)), "quantize_cols")
+    return iB, sB
+
+
+def colsum(iB):
+    iB = _c(iB, np.int8)
+    K, N = iB.shape
+    out = np.empty(N, np.int32)
+    _check(lib().oracle_colsum(_p(iB), K, N, _p(out)), "colsum")
+    return out
+
+
+def int_gemm(uA, zeroA, iB):
+    uA = _c(uA, np.uint8)
+    zA = _c(zeroA, np.int32)
+    iB = _c(iB, np.int8)
+    M, K = uA.shape
+    N = iB.shape[1]
+    acc = np.empty((M, N), np.int32)
+    _check(lib().oracle_int_gemm(_p(uA), _p(zA), _p(iB), M, N, K, _p(acc)), "int_gemm")
+    return acc
+
+
+def epilogue(acc, scaleA, scaleB, bias=None, *, has_bias=None, act="identity",
+             alpha=0.01, typeC="f32"):
+    acc = _c(acc, np.int32)
+    M, N = acc.shape
+    sA = _c(scaleA, np.float32)
+    sB = _c(scaleB, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    hb = (b is not None) if has_bias is None else bool(has_bias)
+    C_ = np.empty((M, N), _np_type(typeC))
+    _check(lib().oracle_epilogue(_p(acc), _p(sA), _p(sB), int(hb), _p(b), _ACT[act],
+                                 float(alpha), M, N, _TYPE[typeC], _p(C_)), "epilogue")
+    return C_
+
+
+def dqip_forward(case, rows=None):
+    """Forward of one inner-product case (a dict as made by ``workloads``).
+
+    Returns a dict with C and every intermediate: uA, scaleA, zeroA (for the
+    selected rows), iB [K,N], scaleB, colsumB, acc. ``rows`` selects a subset
+    of the rows of A (all rows when None)."""
+    M, N, K = case["M"], case["N"], case["K"]
+    A = _c(case["A"], _np_type(case["typeA"]))
+    B = _c(case["B"], _np_type(case["typeB"]))
+    sB_in = None if case.get("scaleB") is None else _c(case["scaleB"], np.float32)
+    if case["typeB"] == "i8" and sB_in is None:
+        raise ValueError("an int8 B needs its per-column scales")
+    r = None if rows is None else _c(rows, np.int64)
+    n = M if r is None else r.size
+    bias = case.get("bias")
+    b = None if bias is None else _c(bias, np.float32)
+    hb = int(case.get("has_bias", b is not None))
+    out = dict(uA=np.empty((n, K), np.uint8), scaleA=np.empty(n, np.float32),
+               zeroA=np.empty(n, np.int32), iB=np.empty((K, N), np.int8),
+               scaleB=np.empty(N, np.float32), acc=np.empty((n, N), np.int32),
+               C=np.empty((n, N), _np_type(case["typeC"])))
+    rc = lib().oracle_dqip_forward(
+        _p(A), _TYPE[case["typeA"]], _p(B), _TYPE[case["typeB"]], _p(sB_in), M, N, K,
+        _p(r), n, int(bool(case["avoid"])), hb, _p(b), _ACT[case["act"]],
+        float(case.get("alpha", 0.01)), _TYPE[case["typeC"]], _p(out["C"]), _p(out["uA"]),
+        _p(out["scaleA"]), _p(out["zeroA"]), _p(out["iB"]), _p(out["scaleB"]), _p(out["acc"]))
+    _check(rc, "dqip_forward")
+    out["colsumB"] = colsum(out["iB"])
+    return out
+
+
+# ------------------------------------------------------------- QLinearConv
+
+def qlinear_conv(x, x_scale, x_zp, w, w_scale, w_zp, y_scale, y_zp, *, bias=None,
+                 y_type="u8"):
+    """2-D QLinearConv, stride 1, no padding, group 1; x [N,C,H,W], w [M,C,kH,kW]."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    if w.ndim == 2:
+        w = w.reshape(w.shape[0], w.shape[1], 1, 1)
+    Nb, Cc, H, W = x.shape
+    M, Cw, kH, kW = w.shape
+    if Cw != Cc:
+        raise ValueError("channel mismatch")
+    ws = _c(np.atleast_1d(w_scale), np.float32)
+    wz = _c(np.atleast_1d(w_zp), np.int32)
+    if ws.size != wz.size:
+        raise ValueError("w_scale / w_zero_point shapes differ")
+    b = None if bias is None else _c(bias, np.int32)
+    y = np.empty((Nb, M, H - kH + 1, W - kW + 1), _np_type(y_type))
+    xt = "u8" if x.dtype == np.uint8 else "i8"
+    wt = "u8" if w.dtype == np.uint8 else "i8"
+    rc = lib().oracle_qlinear_conv(_p(x), _TYPE[xt], Nb, Cc, H, W, float(np.float32(x_scale)),
+                                   int(x_zp), _p(w), _TYPE[wt], M, kH, kW, _p(ws), _p(wz),
+                                   ws.size, _p(b), float(np.float32(y_scale)), int(y_zp),
+                                   _TYPE[y_type], _p(y))
+    _check(rc, "qlinear_conv")
+    return y

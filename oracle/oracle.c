@@ -1,0 +1,392 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the dynamic quantized inner
+ * product, QuantizeLinear / DequantizeLinear and requantizing QLinearConv.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library. The product
+ * library never calls it, includes it or shares a helper, header, table or
+ * constant with it.
+ *
+ * What each function follows (page title, section):
+ *  - Simd "SynetDynamicQuantizedInnerProduct16b Class Reference", Detailed
+ *    Description: A[i,k] -> uA[i,k], scaleA[i], zeroA[i]; B[k,j] -> iB[k,j],
+ *    scaleB[j]; sum over k of (uA - zeroA) * iB; val = sum * scaleA * scaleB;
+ *    C = ConvertToTypeC(Activate(val + bias)). Same page, Init(): the
+ *    avoidOverflow flag narrows B's range to [-64, 63]; SetParams(): B has
+ *    K*N elements, per-output-channel scales for an already quantized B,
+ *    bias NULL means zeros.
+ *  - onnxruntime quantization_defs.cc, QuantizeLinear doc:
+ *    y = saturate(x / y_scale + y_zero_point), x / y_scale rounded to
+ *    nearest with ties to even, saturating to [0,255] or [-128,127];
+ *    scale / zero point per tensor or per 'axis'.
+ *  - same page, DequantizeLinear doc: y = (x - x_zero_point) * x_scale.
+ *  - ONNX "QLinearConv" (opset 10), operator description and inputs: bias is
+ *    int32, quantized with scale x_scale * w_scale and zero point 0; w scale
+ *    and zero point per tensor or per output channel.
+ *
+ * Where the pages leave a step open, this oracle takes these readings:
+ *  R1  uA: asymmetric min/max per row with 0 inside the range:
+ *      lo = min(0, min_k A), hi = max(0, max_k A).
+ *  R2  scaleA = (hi - lo) / 255 (fp32 subtract, then IEEE fp32 divide).
+ *  R3  zeroA = saturate_[0,255](rne(-lo / scaleA)).
+ *  R4  an all-zero row (hi == lo) or all-zero column has scale 1.0f and
+ *      zero point 0, so every code is the zero point.
+ *  R5  B is symmetric: scaleB = max_k |B| / qmax, qmax = 127 (63 with
+ *      avoidOverflow), iB = saturate_[qmin,qmax](rne(B / scaleB)),
+ *      qmin = -128 (-64).
+ *  R6  every dynamic quantizer rounds the IEEE fp32 quotient half-to-even,
+ *      as QuantizeLinear does.
+ *  R7  the epilogue runs in fp32 in the printed order:
+ *      val = ((float)sum * scaleA) * scaleB; val = val + bias; activation;
+ *      then fp32 or bf16 (round to nearest even).
+ *  R8  activations: identity, relu (val > 0 ? val : 0), leaky relu
+ *      (val < 0 ? val * alpha : val).
+ *  R11 requantization (QLinearConv): real = ((float)acc * x_scale) * w_scale,
+ *      then QuantizeLinear with y_scale / y_zero_point.
+ *
+ * Arithmetic: fp32 where the pages fix fp32 tensors, IEEE division,
+ * nearbyintf in the default round-to-nearest mode for ties-to-even, int64
+ * for every integer sum. Built with -O2 -ffp-contract=off and no fast-math,
+ * so no product is fused into an add.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_OVERFLOW (-7)
+
+/* element type tags, as passed by the Python wrapper */
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_I8 2
+#define ORC_U8 3
+
+#define ORC_ACT_IDENTITY 0
+#define ORC_ACT_RELU 1
+#define ORC_ACT_LEAKY 2
+
+/* ---------------------------------------------------------------- helpers */
+
+/* bf16 -> fp32: a bf16 value is the top half of an fp32 bit pattern. */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)b << 16;
+    return v.f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, on the dropped 16 bits. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    union { uint32_t u; float f; } v;
+    v.f = f;
+    if (isnan(f)) return (uint16_t)((v.u >> 16) | 0x40u);
+    uint32_t upper = v.u >> 16;
+    uint32_t lower = v.u & 0xFFFFu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* round half to even (nearbyintf uses the current mode, which is the C
+ * default round-to-nearest-even; nothing here changes it) */
+static float rne(float v) { return nearbyintf(v); }
+
+/* saturate an integral float plus an integer offset into [lo, hi]; done in
+ * double, where rne(x)+zp is exact, so +-inf and huge values saturate too */
+static int sat_add(float r, int zp, int lo, int hi)
+{
+    double v = (double)r + (double)zp;
+    if (v < (double)lo) return lo;
+    if (v > (double)hi) return hi;
+    return (int)v;
+}
+
+static float load_real(const void* p, int type, int64_t idx)
+{
+    if (type == ORC_BF16) return oracle_bf16_to_f32(((const uint16_t*)p)[idx]);
+    return ((const float*)p)[idx];
+}
+
+static int load_int8(const void* p, int type, int64_t idx)
+{
+    if (type == ORC_U8) return ((const uint8_t*)p)[idx];
+    return ((const int8_t*)p)[idx];
+}
+
+static void store_int8(void* p, int type, int64_t idx, int v)
+{
+    if (type == ORC_U8) ((uint8_t*)p)[idx] = (uint8_t)v;
+    else ((int8_t*)p)[idx] = (int8_t)v;
+}
+
+static int64_t inner_size(int ndim, const int64_t* shape, int axis)
+{
+    int64_t inner = 1;
+    for (int d = axis + 1; d < ndim; ++d) inner *= shape[d];
+    return inner;
+}
+
+static int64_t total_size(int ndim, const int64_t* shape)
+{
+    int64_t n = 1;
+    for (int d = 0; d < ndim; ++d) n *= shape[d];
+    return n;
+}
+
+/* ------------------------------------------------------- QuantizeLinear */
+
+/* y = saturate(rne(x / scale[c]) + zp[c]); c = 0 per tensor (axis < 0),
+ * else the index along 'axis'. y_type is ORC_I8 or ORC_U8. */
+int oracle_quantize_linear(const float* x, int ndim, const int64_t* shape,
+                           int axis, const float* scale, const int32_t* zp,
+                           int y_type, void* y)
+{
+    if (axis >= ndim) return ORC_ERR_ARG;
+    int lo = (y_type == ORC_U8) ? 0 : -128;
+    int hi = (y_type == ORC_U8) ? 255 : 127;
+    int64_t n = total_size(ndim, shape);
+    int64_t inner = axis < 0 ? n : inner_size(ndim, shape, axis);
+    int64_t cdim = axis < 0 ? 1 : shape[axis];
+    for (int64_t idx = 0; idx < n; ++idx) {
+        int64_t c = axis < 0 ? 0 : (idx / inner) % cdim;
+        float q = x[idx] / scale[c];
+        store_int8(y, y_type, idx, sat_add(rne(q), zp[c], lo, hi));
+    }
+    return ORC_OK;
+}
+
+/* ----------------------------------------------------- DequantizeLinear */
+
+/* y = (float)(x - zp[c]) * scale[c]; x_type is ORC_I8 or ORC_U8. */
+int oracle_dequantize_linear(const void* x, int x_type, int ndim,
+                             const int64_t* shape, int axis,
+                             const float* scale, const int32_t* zp, float* y)
+{
+    if (axis >= ndim) return ORC_ERR_ARG;
+    int64_t n = total_size(ndim, shape);
+    int64_t inner = axis < 0 ? n : inner_size(ndim, shape, axis);
+    int64_t cdim = axis < 0 ? 1 : shape[axis];
+    for (int64_t idx = 0; idx < n; ++idx) {
+        int64_t c = axis < 0 ? 0 : (idx / inner) % cdim;
+        int d = load_int8(x, x_type, idx) - zp[c];
+        y[idx] = (float)d * scale[c];
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------- dynamic quantization of A */
+
+/* One row of A -> uA row, scaleA, zeroA (readings R1-R4, R6). */
+static void quantize_row(const void* A, int typeA, int64_t K, int64_t i,
+                         uint8_t* u, float* scale_out, int32_t* zero_out)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = load_real(A, typeA, i * K + k);
+        if (a < lo) lo = a;
+        if (a > hi) hi = a;
+    }
+    float scale;
+    int zero;
+    if (hi == lo) {
+        scale = 1.0f;
+        zero = 0;
+    } else {
+        scale = (hi - lo) / 255.0f;
+        zero = sat_add(rne(-lo / scale), 0, 0, 255);
+    }
+    for (int64_t k = 0; k < K; ++k) {
+        float a = load_real(A, typeA, i * K + k);
+        u[k] = (uint8_t)sat_add(rne(a / scale), zero, 0, 255);
+    }
+    *scale_out = scale;
+    *zero_out = zero;
+}
+
+/* rows: indices of the rows to quantize (NULL = all M rows, nrows = M).
+ * uA is [nrows, K]; scaleA, zeroA are [nrows]. */
+int oracle_quantize_rows(const void* A, int typeA, int64_t M, int64_t K,
+                         const int64_t* rows, int64_t nrows, uint8_t* uA,
+                         float* scaleA, int32_t* zeroA)
+{
+    if (typeA != ORC_F32 && typeA != ORC_BF16) return ORC_ERR_ARG;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= M) return ORC_ERR_ARG;
+        quantize_row(A, typeA, K, i, uA + r * K, &scaleA[r], &zeroA[r]);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------- dynamic quantization of B */
+
+/* B [K,N] row-major -> iB [K,N], scaleB [N] (readings R4-R6). */
+int oracle_quantize_cols(const void* B, int typeB, int64_t K, int64_t N,
+                         int avoidOverflow, int8_t* iB, float* scaleB)
+{
+    if (typeB != ORC_F32 && typeB != ORC_BF16) return ORC_ERR_ARG;
+    int qmax = avoidOverflow ? 63 : 127;
+    int qmin = avoidOverflow ? -64 : -128;
+    for (int64_t j = 0; j < N; ++j) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float b = fabsf(load_real(B, typeB, k * N + j));
+            if (b > amax) amax = b;
+        }
+        float scale = amax > 0.0f ? amax / (float)qmax : 1.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float b = load_real(B, typeB, k * N + j);
+            iB[k * N + j] = (int8_t)sat_add(rne(b / scale), 0, qmin, qmax);
+        }
+        scaleB[j] = scale;
+    }
+    return ORC_OK;
+}
+
+/* ReduceSumInteger of iB over axis 0: colsum[j] = sum_k iB[k,j]. */
+int oracle_colsum(const int8_t* iB, int64_t K, int64_t N, int32_t* colsum)
+{
+    for (int64_t j = 0; j < N; ++j) {
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; ++k) s += iB[k * N + j];
+        colsum[j] = (int32_t)s;
+    }
+    return ORC_OK;
+}
+
+/* -------------------------------------------------- integer inner product */
+
+/* acc[r,j] = sum_k (uA[r,k] - zeroA[r]) * iB[k,j], in int64; fails if a
+ * result does not fit int32. */
+int oracle_int_gemm(const uint8_t* uA, const int32_t* zeroA, const int8_t* iB,
+                    int64_t M, int64_t N, int64_t K, int32_t* acc)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k)
+                sum += ((int64_t)uA[i * K + k] - zeroA[i]) * iB[k * N + j];
+            if (sum > INT32_MAX || sum < INT32_MIN) return ORC_ERR_OVERFLOW;
+            acc[i * N + j] = (int32_t)sum;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------ epilogue */
+
+static float activate(float v, int act, float alpha)
+{
+    if (act == ORC_ACT_RELU) return v > 0.0f ? v : 0.0f;
+    if (act == ORC_ACT_LEAKY) return v < 0.0f ? v * alpha : v;
+    return v;
+}
+
+/* C[r,j] = Convert(Activate(((float)acc * scaleA[r]) * scaleB[j] (+ bias[j])))
+ * has_bias = 0 skips the add; has_bias = 1 with bias NULL adds zeros. */
+int oracle_epilogue(const int32_t* acc, const float* scaleA,
+                    const float* scaleB, int has_bias, const float* bias,
+                    int act, float alpha, int64_t M, int64_t N, int typeC,
+                    void* C)
+{
+    if (typeC != ORC_F32 && typeC != ORC_BF16) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            float val = (float)acc[i * N + j] * scaleA[i];
+            val = val * scaleB[j];
+            if (has_bias) val = val + (bias ? bias[j] : 0.0f);
+            val = activate(val, act, alpha);
+            if (typeC == ORC_BF16)
+                ((uint16_t*)C)[i * N + j] = oracle_f32_to_bf16(val);
+            else
+                ((float*)C)[i * N + j] = val;
+        }
+    }
+    return ORC_OK;
+}
+
+/* --------------------------------------------- the whole forward pass */
+
+/*
+ * Forward over the selected rows of A (rows NULL = all M rows).
+ * typeB: ORC_F32 / ORC_BF16 (quantized here, per column) or ORC_I8 (already
+ * quantized; scaleB_in gives its per-column scales).
+ * Optional outputs (NULL to skip): uA [nrows,K], scaleA/zeroA [nrows],
+ * iB [K,N], scaleB [N], acc [nrows,N]. C is [nrows,N] of typeC.
+ * The caller provides work_uA [nrows*K], work_iB [K*N] (when typeB is not
+ * I8), work_acc [nrows*N], work_scaleB [N] and work_sz [2*nrows] when it
+ * does not ask for the matching optional output.
+ */
+int oracle_dqip_forward(const void* A, int typeA, const void* B, int typeB,
+                        const float* scaleB_in, int64_t M, int64_t N, int64_t K,
+                        const int64_t* rows, int64_t nrows, int avoidOverflow,
+                        int has_bias, const float* bias, int act, float alpha,
+                        int typeC, void* C, uint8_t* uA, float* scaleA,
+                        int32_t* zeroA, int8_t* iB, float* scaleB, int32_t* acc)
+{
+    if (!A || !B || !C || !uA || !scaleA || !zeroA || !iB || !scaleB || !acc)
+        return ORC_ERR_ARG;
+    int rc = oracle_quantize_rows(A, typeA, M, K, rows, nrows, uA, scaleA, zeroA);
+    if (rc) return rc;
+    if (typeB == ORC_I8) {
+        const int8_t* b = (const int8_t*)B;
+        for (int64_t t = 0; t < K * N; ++t) iB[t] = b[t];
+        for (int64_t j = 0; j < N; ++j) scaleB[j] = scaleB_in[j];
+    } else {
+        rc = oracle_quantize_cols(B, typeB, K, N, avoidOverflow, iB, scaleB);
+        if (rc) return rc;
+    }
+    rc = oracle_int_gemm(uA, zeroA, iB, nrows, N, K, acc);
+    if (rc) return rc;
+    return oracle_epilogue(acc, scaleA, scaleB, has_bias, bias, act, alpha,
+                           nrows, N, typeC, C);
+}
+
+/* -------------------------------------------------------- QLinearConv */
+
+/*
+ * 2-D QLinearConv, stride 1, no padding, no dilation, group 1.
+ * x [Nb, C, H, W] (x_type I8/U8), w [M, C, kH, kW] (w_type I8/U8),
+ * w_scale / w_zp of length w_len (1 = per tensor, M = per output channel),
+ * bias [M] int32 or NULL, y [Nb, M, H-kH+1, W-kW+1] (y_type I8/U8).
+ * acc = sum (w - w_zp) * (x - x_zp) + bias;
+ * real = ((float)acc * x_scale) * w_scale[m];  y = QuantizeLinear(real).
+ */
+int oracle_qlinear_conv(const void* x, int x_type, int64_t Nb, int64_t C,
+                        int64_t H, int64_t W, float x_scale, int32_t x_zp,
+                        const void* w, int w_type, int64_t M, int64_t kH,
+                        int64_t kW, const float* w_scale, const int32_t* w_zp,
+                        int64_t w_len, const int32_t* bias, float y_scale,
+                        int32_t y_zp, int y_type, void* y)
+{
+    if (kH > H || kW > W || (w_len != 1 && w_len != M)) return ORC_ERR_ARG;
+    int64_t oH = H - kH + 1, oW = W - kW + 1;
+    int lo = (y_type == ORC_U8) ? 0 : -128;
+    int hi = (y_type == ORC_U8) ? 255 : 127;
+    for (int64_t n = 0; n < Nb; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t wi = (w_len == 1) ? 0 : m;
+            for (int64_t oh = 0; oh < oH; ++oh)
+                for (int64_t ow = 0; ow < oW; ++ow) {
+                    int64_t acc = 0;
+                    for (int64_t c = 0; c < C; ++c)
+                        for (int64_t r = 0; r < kH; ++r)
+                            for (int64_t s = 0; s < kW; ++s) {
+                                int64_t xi = ((n * C + c) * H + oh + r) * W + ow + s;
+                                int64_t wk = ((m * C + c) * kH + r) * kW + s;
+                                acc += (int64_t)(load_int8(w, w_type, wk) - w_zp[wi]) *
+                                       (load_int8(x, x_type, xi) - x_zp);
+                            }
+                    if (bias) acc += bias[m];
+                    if (acc > INT32_MAX || acc < INT32_MIN) return ORC_ERR_OVERFLOW;
+                    float real = (float)(int32_t)acc * x_scale;
+                    real = real * w_scale[wi];
+                    float q = real / y_scale;
+                    int64_t yi = ((n * M + m) * oH + oh) * oW + ow;
+                    store_int8(y, y_type, yi, sat_add(rne(q), y_zp, lo, hi));
+                }
+        }
+    return ORC_OK;
+}

@@ -1,0 +1,228 @@
+"""Seeded synthetic inputs for the dynamic quantized inner product and for
+QuantizeLinear / DequantizeLinear.
+
+This module only draws random numbers and lays them out. It holds none of the
+method's arithmetic (no scales, no rounding to integer codes, no sums), so the
+CPU oracle and the HIP library can both be fed from it without sharing any
+computation. Every generator is a numpy PCG64 stream with a fixed seed.
+
+The shapes and value distributions follow the workloads that the method's
+pages describe in words (no public dataset or benchmark suite is involved):
+
+* ``dqip_small``   -- inner product M=64, N=64, K=128, fp32 A and constant fp32 B.
+* ``dqip_ramp``    -- the 4x8x16 ramp of the usage example in the
+  "SynetDynamicQuantizedInnerProduct16b" class reference (Detailed
+  Description): A[i] = i*0.01f, B[i] = i*0.02f, bias 0.1f, avoidOverflow on.
+* ``qdq_per_axis`` -- QuantizeLinear input [64,256,56,56] NCHW, per-channel
+  (axis 1) scales and int8 zero points, with planted half-way ties and
+  far-out-of-range values.
+* ``dqip_large``   -- 4096^3, bf16 A with 1% outliers, constant int8 B.
+* ``dqip_lstm``    -- the input and the recurrent gate projections of a
+  quantized LSTM (hidden 512, input 512, seq 128 x batch 32).
+* ``dqip_dynamic_b`` -- 8192^2 fp32 A and fp32 B quantized on every call,
+  avoidOverflow on.
+* ``qconv1x1``     -- a 1x1 QLinearConv over uint8 x [8,256,56,56].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32_MAX = np.float32(np.finfo(np.float32).max)
+
+# dtype tags shared by both sides' Python wrappers (plain names, no arithmetic)
+F32, BF16, I8, U8 = "f32", "bf16", "i8", "u8"
+IDENTITY, RELU, LEAKY_RELU = "identity", "relu", "leaky_relu"
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (torch's round-to-nearest-even conversion)
+    and return the raw 16-bit patterns as uint16."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact: the bits become the high half)."""
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _case(M, N, K, A, B, *, typeA, typeB, typeC, constB, bias, act,
+          avoid, scaleB=None, alpha=0.01, name=""):
+    return dict(name=name, M=M, N=N, K=K, A=A, B=B, typeA=typeA, typeB=typeB,
+                typeC=typeC, constB=constB, bias=bias, act=act, alpha=alpha,
+                avoid=avoid, scaleB=scaleB)
+
+
+# ----------------------------------------------------------------------------
+# dynamic quantized inner product cases
+# ----------------------------------------------------------------------------
+
+def dqip_small(seed: int = 0):
+    """M=64, N=64, K=128: A ~U(-1,1), constant fp32 B ~N(0,0.05) quantized per
+    column to [-127,127], bias ~U(-0.1,0.1), identity, fp32 out."""
+    r = rng(seed)
+    M, N, K = 64, 64, 128
+    A = r.uniform(-1.0, 1.0, (M, K)).astype(np.float32)
+    B = r.normal(0.0, 0.05, (K, N)).astype(np.float32)
+    bias = r.uniform(-0.1, 0.1, N).astype(np.float32)
+    return _case(M, N, K, A, B, typeA=F32, typeB=F32, typeC=F32, constB=True,
+                 bias=bias, act=IDENTITY, avoid=False, name="dqip 64x64x128 f32")
+
+
+def dqip_ramp():
+    """The usage example's 4x8x16 ramp (no randomness)."""
+    M, N, K = 4, 8, 16
+    A = (np.arange(M * K, dtype=np.float32) * np.float32(0.01)).reshape(M, K)
+    B = (np.arange(K * N, dtype=np.float32) * np.float32(0.02)).reshape(K, N)
+    bias = np.full(N, 0.1, dtype=np.float32)
+    return _case(M, N, K, A, B, typeA=F32, typeB=F32, typeC=F32, constB=True,
+                 bias=bias, act=IDENTITY, avoid=True, name="ramp 4x8x16")
+
+
+def dqip_random(M, N, K, *, seed, typeA=F32, typeB=F32, typeC=F32, constB=True,
+                bias=True, act=IDENTITY, avoid=False, alpha=0.01,
+                a_dist="normal", b_std=0.05, outliers=0.0, zero_rows=(),
+                zero_cols=()):
+    """A general random case for parity sweeps over odd shapes.
+
+    typeB=I8 draws B ~U{-127..127} with scaleB ~U(0.001,0.01); otherwise B is
+    fp32 ~N(0,b_std) (stored as bf16 bits for typeB=BF16). ``zero_rows`` /
+    ``zero_cols`` plant all-zero rows of A / columns of B."""
+    r = rng(seed)
+    if a_dist == "uniform":
+        A = r.uniform(-1.0, 1.0, (M, K)).astype(np.float32)
+    else:
+        A = r.normal(0.0, 1.0, (M, K)).astype(np.float32)
+    if outliers:
+        mask = r.random((M, K)) < outliers
+        A = np.where(mask, A * np.float32(20.0), A).astype(np.float32)
+    for i in zero_rows:
+        A[i, :] = 0.0
+    scaleB = None
+    if typeB == I8:
+        B = r.integers(-127, 128, (K, N), dtype=np.int64).astype(np.int8)
+        scaleB = r.uniform(0.001, 0.01, N).astype(np.float32)
+        for j in zero_cols:
+            B[:, j] = 0
+    else:
+        B = r.normal(0.0, b_std, (K, N)).astype(np.float32)
+        for j in zero_cols:
+            B[:, j] = 0.0
+    biasv = r.uniform(-0.1, 0.1, N).astype(np.float32) if bias else None
+    if typeA == BF16:
+        A = to_bf16_bits(A)
+    if typeB == BF16:
+        B = to_bf16_bits(B)
+    return _case(M, N, K, A, B, typeA=typeA, typeB=typeB, typeC=typeC,
+                 constB=constB, bias=biasv, act=act, avoid=avoid,
+                 scaleB=scaleB, alpha=alpha, name=f"dqip {M}x{N}x{K} seed{seed}")
+
+
+def dqip_large(seed: int = 2, M: int = 4096, N: int = 4096, K: int = 4096):
+    """4096^3: A bf16 from N(0,1) with a Bernoulli(0.01) mask of x20 outliers,
+    constant pre-quantized int8 B ~U{-127..127}, scaleB ~U(0.001,0.01),
+    bias ~U(-1,1), ReLU, bf16 out."""
+    r = rng(seed)
+    A = r.standard_normal((M, K), dtype=np.float32)
+    mask = r.random((M, K), dtype=np.float32) < np.float32(0.01)
+    A[mask] *= np.float32(20.0)
+    B = r.integers(-127, 128, (K, N), dtype=np.int8)
+    scaleB = r.uniform(0.001, 0.01, N).astype(np.float32)
+    bias = r.uniform(-1.0, 1.0, N).astype(np.float32)
+    return _case(M, N, K, to_bf16_bits(A), B, typeA=BF16, typeB=I8, typeC=BF16,
+                 constB=True, bias=bias, act=RELU, avoid=False, scaleB=scaleB,
+                 name=f"dqip {M}x{N}x{K} bf16 A, const int8 B, relu, bf16 out")
+
+
+def dqip_lstm(seed: int = 3, recurrent: bool = False):
+    """Quantized LSTM gate projections, hidden 512, input 512, 4*hidden = 2048
+    gate columns. Input GEMM: M = seq 128 x batch 32 = 4096, K = 512.
+    Recurrent step: M = batch 32, K = hidden 512. Per-channel int8 weights
+    ~U{-127..127}, scales ~U(0.001,0.01), bias ~U(-0.1,0.1), A ~U(-1,1),
+    identity, fp32 out."""
+    r = rng(seed + (100 if recurrent else 0))
+    M = 32 if recurrent else 4096
+    K, N = 512, 2048
+    A = r.uniform(-1.0, 1.0, (M, K)).astype(np.float32)
+    W = r.integers(-127, 128, (K, N), dtype=np.int8)
+    scale = r.uniform(0.001, 0.01, N).astype(np.float32)
+    bias = r.uniform(-0.1, 0.1, N).astype(np.float32)
+    kind = "recurrent" if recurrent else "input"
+    return _case(M, N, K, A, W, typeA=F32, typeB=I8, typeC=F32, constB=True,
+                 bias=bias, act=IDENTITY, avoid=False, scaleB=scale,
+                 name=f"lstm {kind} gates {M}x{N}x{K}")
+
+
+def dqip_dynamic_b(seed: int = 4, M: int = 8192, N: int = 8192, K: int = 8192):
+    """Non-constant B: A fp32 ~N(0,1), B fp32 ~N(0,0.02) quantized per column
+    on every call with avoidOverflow, no bias, identity, fp32 out."""
+    r = rng(seed)
+    A = r.standard_normal((M, K), dtype=np.float32)
+    B = (r.standard_normal((K, N), dtype=np.float32) * np.float32(0.02))
+    return _case(M, N, K, A, B, typeA=F32, typeB=F32, typeC=F32, constB=False,
+                 bias=None, act=IDENTITY, avoid=True,
+                 name=f"dqip {M}x{N}x{K} dynamic fp32 B, avoidOverflow")
+
+
+# ----------------------------------------------------------------------------
+# QuantizeLinear / DequantizeLinear
+# ----------------------------------------------------------------------------
+
+def qdq_per_axis(seed: int = 1, shape=(64, 256, 56, 56), axis: int = 1,
+                 plant_every: int = 4096):
+    """x ~N(0,1) NCHW, per-channel y_scale ~U(0.005,0.05) and int8 zero points
+    ~U{-10..10}. At 1 in ``plant_every`` seeded positions x is set to a value
+    whose quotient x/scale is exactly k+1/2 (k ~U{-140..140}); at another 1 in
+    ``plant_every`` positions x is one of +-{1e3, 1e6, FLT_MAX}."""
+    r = rng(seed)
+    shape = tuple(int(s) for s in shape)
+    C = shape[axis]
+    x = r.standard_normal(shape, dtype=np.float32)
+    scale = r.uniform(0.005, 0.05, C).astype(np.float32)
+    zp = r.integers(-10, 11, C).astype(np.int8)
+    inner = int(np.prod(shape[axis + 1:], dtype=np.int64))
+    flat = x.reshape(-1)
+    n = flat.size
+    n_plant = max(1, n // plant_every)
+    # half-way ties: x = fl32((k + 1/2) * s), kept only where fl32(x / s) is
+    # exactly k + 1/2 (the check is IEEE fp32 division, done by numpy)
+    pos = r.choice(n, size=n_plant, replace=False)
+    ch = (pos // inner) % C
+    k = r.integers(-140, 141, n_plant).astype(np.float32)
+    half = k + np.float32(0.5)
+    cand = (half * scale[ch]).astype(np.float32)
+    exact = (cand / scale[ch]).astype(np.float32) == half
+    flat[pos[exact]] = cand[exact]
+    # far out of range
+    pos2 = r.choice(n, size=n_plant, replace=False)
+    mags = np.array([1e3, 1e6, F32_MAX], dtype=np.float32)
+    vals = mags[r.integers(0, 3, n_plant)] * np.where(
+        r.random(n_plant) < 0.5, np.float32(-1.0), np.float32(1.0))
+    flat[pos2] = vals.astype(np.float32)
+    return dict(x=x, axis=axis, scale=scale, zp=zp, n_ties=int(exact.sum()),
+                name=f"qdq {list(shape)} axis {axis}")
+
+
+# ----------------------------------------------------------------------------
+# 1x1 QLinearConv
+# ----------------------------------------------------------------------------
+
+def qconv1x1(seed: int = 4, batch: int = 8, C: int = 256, M: int = 256,
+             H: int = 56, W: int = 56):
+    """uint8 x ~U{0..255} with x_zp 128 and x_scale 0.01; int8 w [M,C]
+    ~U{-127..127}, w_zp 0, per-output-channel w_scale ~U(0.0005,0.002);
+    int32 bias ~U{-10000..10000}; y_scale 0.02, y_zp 128, uint8 y."""
+    r = rng(seed + 1000)
+    x = r.integers(0, 256, (batch, C, H, W), dtype=np.int64).astype(np.uint8)
+    w = r.integers(-127, 128, (M, C), dtype=np.int64).astype(np.int8)
+    w_scale = r.uniform(0.0005, 0.002, M).astype(np.float32)
+    bias = r.integers(-10000, 10001, M, dtype=np.int64).astype(np.int32)
+    return dict(x=x, x_scale=np.float32(0.01), x_zp=128, w=w, w_scale=w_scale,
+                bias=bias, y_scale=np.float32(0.02), y_zp=128,
+                name=f"qlinearconv 1x1 x[{batch},{C},{H},{W}] -> {M} ch")
