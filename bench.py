@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the dynamic quantized inner product on one MI355X.
+
+One step = one dqip_forward of the 4096^3 workload (bf16 A with 1% x20
+outliers quantized per row, constant int8 B, fp32 epilogue with ReLU, bf16
+C): the row-quantization kernel and the int8-MFMA GEMM with its fused
+dequantizing epilogue. `value` is 2*M*N*K / (wall time per step), inputs
+resident in HBM, K steps back to back between two device synchronizations.
+
+The same JSON line carries:
+  roofline     -- the GEMM kernel's achieved int8 TOP/s (HIP events recorded
+                  by the library around that kernel on the forward's stream)
+                  against the 5.0 POP/s dense int8 MFMA peak;
+  secondary    -- QuantizeLinear / DequantizeLinear on [64,256,56,56]
+                  (GB/s, cold and warm cache), and the other inner-product
+                  workloads (64x64x128 latency, the LSTM gate projections,
+                  8192^3 with a B quantized on every call);
+  cpu_baseline -- the CPU oracle on a bounded sample of rows of the same
+                  4096^3 workload, single-threaded.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
+FLUSH_BYTES = 512 << 20   # larger than the 256 MiB Infinity Cache
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev_tensor(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+class Dqip:
+    """One initialized context with its device inputs (bench-side helper)."""
+
+    DT = {"f32": 0, "bf16": 1, "i8": 2, "u8": 3}
+    ACT = {"identity": 0, "relu": 1, "leaky_relu": 2}
+
+    def __init__(self, dq, torch, case):
+        self.dq, self.case = dq, case
+        M, N, K = case["M"], case["N"], case["K"]
+        self.h = dq.dqip_init(M, N, K, self.DT[case["typeA"]], self.DT[case["typeB"]],
+                              self.DT[case["typeC"]], case["constB"], case["bias"] is not None,
+                              self.ACT[case["act"]], case["avoid"])
+        self.A = dev_tensor(case["A"], torch)
+        B = dev_tensor(case["B"], torch)
+        sB = None if case.get("scaleB") is None else dev_tensor(case["scaleB"], torch)
+        bias = None if case["bias"] is None else dev_tensor(case["bias"], torch)
+        if case["constB"]:
+            dq.dqip_set_params(self.h, B, sB, bias, None)
+            self.B = None
+            del B
+        else:
+            dq.dqip_set_params(self.h, None, None, bias, None)
+            self.B = B
+        cdt = torch.float32 if case["typeC"] == "f32" else torch.int16
+        self.C = torch.empty((M, N), dtype=cdt, device="cuda")
+        self.buf = torch.empty(dq.dqip_external_buffer_size(self.h), dtype=torch.uint8,
+                               device="cuda")
+        self.ops = 2.0 * M * N * K
+
+    def forward(self):
+        self.dq.dqip_forward(self.h, self.A, self.B, self.buf, self.C)
+
+    def timed(self, torch, steps, warmup):
+        """Back-to-back forwards: (wall ms per step, per-phase ms per call)."""
+        for _ in range(warmup):
+            self.forward()
+        torch.cuda.synchronize()
+        self.dq.dqip_profile_begin(self.h, steps)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.forward()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms, calls = self.dq.dqip_profile_end(self.h)
+        return (t1 - t0) * 1e3 / steps, [m / max(calls, 1) for m in ms]
+
+    def release(self):
+        self.dq.dqip_release(self.h)
+
+
+def traffic_record(kernel_file):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), kept
+    only while the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "dynamic_quantized_gemm_amd", "csrc", kernel_file)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    entry = rec.get(kernel_file)
+    if not entry or entry.get("source_sha256") != sha:
+        return None
+    return entry
+
+
+def bench_qdq(dq, torch, steps):
+    """QuantizeLinear and DequantizeLinear, per axis, [64,256,56,56] fp32 <->
+    int8: GB/s of algorithmic bytes (4 + 1 per element), cold (Infinity
+    Cache flushed before every call) and warm (back to back)."""
+    import workloads as W
+
+    case = W.qdq_per_axis(seed=1)
+    x = dev_tensor(case["x"], torch)
+    s = dev_tensor(case["scale"], torch)
+    z = dev_tensor(case["zp"], torch)
+    n = x.numel()
+    y = torch.empty(x.shape, dtype=torch.int8, device="cuda")
+    r = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    q = lambda: dq.qlinear_quantize(x, s, z, dq.DQ_I8, y, axis=1)  # noqa: E731
+    d = lambda: dq.qlinear_dequantize(y, dq.DQ_I8, s, z, r, axis=1)  # noqa: E731
+    out = {}
+    for name, fn in (("quantize", q), ("dequantize", d)):
+        for _ in range(3):
+            fn()
+        cold = []
+        for i in range(steps):
+            flush.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        warm = e0.elapsed_time(e1) / steps
+        cold_ms = float(np.median(cold))
+        gb = 5.0 * n / 1e9
+        out[name] = {"us_cold": round(cold_ms * 1e3, 2), "GBps_cold": round(gb / (cold_ms / 1e3), 1),
+                     "frac_cold": round(gb / (cold_ms / 1e3) / HBM_PEAK_GBS, 3),
+                     "us_warm": round(warm * 1e3, 2), "GBps_warm": round(gb / (warm / 1e3), 1)}
+    out["workload"] = "x fp32 [64,256,56,56] NCHW <-> int8, per-channel (axis 1) scale/zero point"
+    out["bytes_per_call"] = 5 * n
+    del flush
+    return out
+
+
+def bench_dqip_case(dq, torch, case, steps, warmup):
+    d = Dqip(dq, torch, case)
+    try:
+        ms, ph = d.timed(torch, steps, warmup)
+    finally:
+        d.release()
+    return {"workload": case["name"], "us_per_forward": round(ms * 1e3, 2),
+            "TOPS": round(d.ops / (ms / 1e3) / 1e12, 2),
+            "phase_us": {"quant_a": round(ph[0] * 1e3, 2), "quant_b": round(ph[1] * 1e3, 2),
+                         "gemm": round(ph[2] * 1e3, 2)},
+            "gemm_TOPS": round(d.ops / (ph[2] / 1e3) / 1e12, 2) if ph[2] > 0 else None}
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The oracle as it is (single-threaded C) on a sample of rows of the
+    same workload, scaled to TOP/s of the whole inner product."""
+    import oracle
+
+    N, K = case["N"], case["K"]
+    t0 = time.perf_counter()
+    oracle.dqip_forward(case, rows=np.arange(2))
+    t_probe = time.perf_counter() - t0
+    rows = int(max(2, min(512, 2 * budget_s / max(t_probe, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.dqip_forward(case, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows} of {case['M']} rows of the same workload (row quantization of the "
+                      f"sample, full B, {rows}x{N}x{K} integer sums, epilogue), {dt:.1f} s on 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline only: no secondary configs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this library has no multi-GPU path, so --gpus "
+              f"{args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_quantized_gemm_amd as dq
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dq.load()
+    torch.cuda.set_device(0)
+
+    log("bench: generating the 4096^3 workload")
+    case = W.dqip_large()
+    d = Dqip(dq, torch, case)
+    info = dq.dqip_info(d.h)
+    log(f"bench: {info}")
+    ms, phases = d.timed(torch, args.steps, args.warmup)
+    d.release()
+    value = d.ops / (ms / 1e3) / 1e12
+    gemm_ms = phases[2]
+    achieved = d.ops / (gemm_ms / 1e3) / 1e12
+    log(f"bench: {ms * 1e3:.1f} us/forward = {value:.1f} TOPS; gemm {gemm_ms * 1e3:.1f} us = "
+        f"{achieved:.1f} TOPS; quant_a {phases[0] * 1e3:.1f} us")
+    tr = traffic_record("gemm_i8.hip")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                "traffic": None if tr is None else tr["bytes_per_launch"],
+                "kernel": "gemm_i8 (int8 MFMA, fused dequant/bias/ReLU/bf16 epilogue)",
+                "avg_launch_us": round(gemm_ms * 1e3, 2),
+                "ops_per_launch": d.ops}
+
+    secondary = {"dqip_4096_phases_us": {"quant_a": round(phases[0] * 1e3, 2),
+                                         "gemm": round(gemm_ms * 1e3, 2)},
+                 "quant_a_GBps": round((case["M"] * case["K"] * 3) / (phases[0] / 1e3) / 1e9, 1)}
+    if not args.quick:
+        steps2 = max(10, args.steps // 2)
+        log("bench: QuantizeLinear / DequantizeLinear [64,256,56,56]")
+        secondary["qdq"] = bench_qdq(dq, torch, steps2)
+        log(f"bench: {secondary['qdq']}")
+        for name, mk in (("dqip_64x64x128", W.dqip_small),
+                         ("lstm_input_4096x2048x512", lambda: W.dqip_lstm(recurrent=False)),
+                         ("lstm_recurrent_32x2048x512", lambda: W.dqip_lstm(recurrent=True)),
+                         ("dqip_8192_dynamic_b", W.dqip_dynamic_b)):
+            log(f"bench: {name}")
+            secondary[name] = bench_dqip_case(dq, torch, mk(), steps2, 3)
+            log(f"bench: {secondary[name]}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(case)
+        log(f"bench: {cpu}")
+
+    line = {
+        "metric": "dyn-quant GEMM TOPS (% int8 MFMA peak) + Quantize/DequantizeLinear GB/s",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "dynamic quantized inner product M=N=K=4096: bf16 A ~N(0,1) with "
+                               "1% x20 outliers, constant int8 B with per-column scales, fp32 "
+                               "bias, ReLU, bf16 C",
+                   "M": 4096, "N": 4096, "K": 4096, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+        "info": info,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""Python binding of libdqip.so: the dynamic quantized inner product and
+QuantizeLinear / DequantizeLinear on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+The functions carry the names of the C entry points declared in
+``include/dqip.h``; tensors are torch tensors on the GPU (their data pointers
+are passed), ``stream`` defaults to torch's current stream. A missing library
+raises: there is no fallback.
+"""
+from ._binding import (  # noqa: F401
+    DQ_ACT_IDENTITY, DQ_ACT_LEAKY_RELU, DQ_ACT_RELU, DQ_BF16, DQ_ERR_ALLOC, DQ_ERR_ARG,
+    DQ_ERR_HIP, DQ_ERR_RANGE, DQ_ERR_STATE, DQ_ERR_TYPE, DQ_F32, DQ_I8, DQ_K_MAX, DQ_OK,
+    DQ_PER_TENSOR, DQ_U8, DQError, LIB_PATH, dqip_enabled, dqip_external_buffer_size,
+    dqip_forward, dqip_forward_accumulators, dqip_info, dqip_init, dqip_internal_buffer_size,
+    dqip_last_error, dqip_profile_begin, dqip_profile_end, dqip_read_quantized_a, dqip_read_quantized_b, dqip_release,
+    dqip_set_params, exported_symbols, load, qlinear_dequantize, qlinear_quantize,
+)

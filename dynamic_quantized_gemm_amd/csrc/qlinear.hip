@@ -1,0 +1,306 @@
+// qlinear.hip -- QuantizeLinear / DequantizeLinear for gfx950.
+//
+// Operators: onnxruntime quantization_defs.cc, QuantizeLinear doc
+// (y = saturate(x / y_scale + y_zero_point), the quotient rounded to nearest
+// with ties to even, saturating to [0,255] or [-128,127]) and
+// DequantizeLinear doc (y = (x - x_zero_point) * x_scale); scale and zero
+// point per tensor or per 'axis'.
+//
+// Both kernels are element-wise and bound by HBM bandwidth: every thread
+// moves one 16-byte vector of 8-bit codes and the four matching 16-byte
+// vectors of fp32, so each wave issues fully coalesced 1 KiB / 4 KiB
+// transactions. The tensor is viewed as [outer, C, inner]; the channel of
+// element e is (e / inner) % C, found with multiply-high division by
+// constants precomputed on the host. When inner is a multiple of 16 a
+// 16-element vector never straddles two channels and the channel is found
+// once per vector.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "dq_device.h"
+
+namespace {
+
+// Division of a 32-bit unsigned n by a runtime constant d >= 1 with one
+// multiply-high: q = (umulhi(n, m) + n) >> s, s = ceil(log2 d),
+// m = floor(2^32 (2^s - d) / d) + 1 (Granlund & Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, round-up variant).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.s = 0;
+    while ((1ull << f.s) < d) ++f.s;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    uint32_t hi = __umulhi(n, f.m);
+    return (uint32_t)(((uint64_t)hi + n) >> f.s);
+}
+
+struct AxisMap {
+    FastDiv inner, cdim;
+    int per_axis;
+};
+
+__device__ __forceinline__ uint32_t channel_of(uint32_t e, const AxisMap& a) {
+    if (!a.per_axis) return 0;
+    uint32_t q = fdiv(e, a.inner);
+    return q - fdiv(q, a.cdim) * a.cdim.d;
+}
+
+__device__ __forceinline__ uint32_t channel_of64(uint64_t e, uint64_t inner, uint64_t cdim) {
+    return (uint32_t)((e / inner) % cdim);
+}
+
+template <bool U8>
+__device__ __forceinline__ int load_zp(const void* zp, uint32_t c) {
+    if (!zp) return 0;
+    return U8 ? (int)((const uint8_t*)zp)[c] : (int)((const int8_t*)zp)[c];
+}
+
+template <bool U8>
+__device__ __forceinline__ int quant1(float x, float s, int zp) {
+    return dq::sat_add(dq::rne(x / s), zp, U8 ? 0 : -128, U8 ? 255 : 127);
+}
+
+// ---------------------------------------------------------------- quantize
+
+// VEC: 16 elements per thread through 16-byte loads and one 16-byte store
+// (x, y 16-byte aligned, n < 2^32). CH16: the 16 elements share a channel.
+template <bool U8, bool VEC, bool CH16>
+__global__ void __launch_bounds__(256)
+k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
+                  uint64_t cdim64, const float* __restrict__ scale,
+                  const void* __restrict__ zp, uint8_t* __restrict__ y) {
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (VEC) {
+        const uint64_t e0 = t * 16;
+        if (e0 + 16 <= n) {
+            const dq::f4* xv = reinterpret_cast<const dq::f4*>(x + e0);
+            dq::f4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(xv + i);
+            const float* f = reinterpret_cast<const float*>(v);
+            uint32_t out[4];
+            if (CH16) {
+                const uint32_t c = channel_of((uint32_t)e0, am);
+                const float s = scale[c];
+                const int z = load_zp<U8>(zp, c);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t packed = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        packed |= ((uint32_t)quant1<U8>(f[4 * w + b], s, z) & 0xffu) << (8 * b);
+                    out[w] = packed;
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t packed = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t c = channel_of((uint32_t)(e0 + 4 * w + b), am);
+                        packed |= ((uint32_t)quant1<U8>(f[4 * w + b], scale[c], load_zp<U8>(zp, c)) & 0xffu)
+                                  << (8 * b);
+                    }
+                    out[w] = packed;
+                }
+            }
+            const dq::u4 o = {out[0], out[1], out[2], out[3]};
+            __builtin_nontemporal_store(o, reinterpret_cast<dq::u4*>(y + e0));
+        } else {
+            for (uint64_t e = e0; e < n; ++e) {
+                const uint32_t c = channel_of((uint32_t)e, am);
+                y[e] = (uint8_t)quant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+            }
+        }
+    } else {
+        // one element per thread, any alignment, any size
+        if (t < n) {
+            const uint32_t c = am.per_axis ? channel_of64(t, inner64, cdim64) : 0;
+            y[t] = (uint8_t)quant1<U8>(x[t], scale[c], load_zp<U8>(zp, c));
+        }
+    }
+}
+
+// -------------------------------------------------------------- dequantize
+
+template <bool U8>
+__device__ __forceinline__ float dequant1(uint32_t byte, float s, int zp) {
+    const int q = U8 ? (int)(byte & 0xffu) : (int)(int8_t)(byte & 0xffu);
+    return (float)(q - zp) * s;
+}
+
+template <bool U8, bool VEC, bool CH16>
+__global__ void __launch_bounds__(256)
+k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
+                    uint64_t cdim64, const float* __restrict__ scale,
+                    const void* __restrict__ zp, float* __restrict__ y) {
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (VEC) {
+        const uint64_t e0 = t * 16;
+        if (e0 + 16 <= n) {
+            const dq::u4 q = __builtin_nontemporal_load(reinterpret_cast<const dq::u4*>(x + e0));
+            const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+            dq::f4 out[4];
+            float* f = reinterpret_cast<float*>(out);
+            if (CH16) {
+                const uint32_t c = channel_of((uint32_t)e0, am);
+                const float s = scale[c];
+                const int z = load_zp<U8>(zp, c);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) f[i] = dequant1<U8>(qw[i >> 2] >> (8 * (i & 3)), s, z);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t c = channel_of((uint32_t)(e0 + i), am);
+                    f[i] = dequant1<U8>(qw[i >> 2] >> (8 * (i & 3)), scale[c], load_zp<U8>(zp, c));
+                }
+            }
+            dq::f4* yv = reinterpret_cast<dq::f4*>(y + e0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(out[i], yv + i);
+        } else {
+            for (uint64_t e = e0; e < n; ++e) {
+                const uint32_t c = channel_of((uint32_t)e, am);
+                y[e] = dequant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+            }
+        }
+    } else {
+        if (t < n) {
+            const uint32_t c = am.per_axis ? channel_of64(t, inner64, cdim64) : 0;
+            y[t] = dequant1<U8>(x[t], scale[c], load_zp<U8>(zp, c));
+        }
+    }
+}
+
+// ------------------------------------------------------------------- host
+
+struct Plan {
+    uint64_t n = 0, inner = 1, cdim = 1;
+    int per_axis = 0;
+};
+
+int make_plan(int ndim, const int64_t* shape, int axis, Plan* p) {
+    if (ndim < 1 || ndim > 8) DQ_FAIL(DQ_ERR_ARG, "ndim must be in [1, 8], got %d", ndim);
+    if (!shape) DQ_FAIL(DQ_ERR_ARG, "shape is NULL");
+    uint64_t n = 1;
+    for (int d = 0; d < ndim; ++d) {
+        if (shape[d] < 0) DQ_FAIL(DQ_ERR_ARG, "shape[%d] = %lld is negative", d, (long long)shape[d]);
+        if (shape[d] != 0 && n > (UINT64_C(1) << 62) / (uint64_t)shape[d])
+            DQ_FAIL(DQ_ERR_ARG, "tensor too large");
+        n *= (uint64_t)shape[d];
+    }
+    p->n = n;
+    if (axis == DQ_PER_TENSOR) {
+        p->per_axis = 0;
+        return DQ_OK;
+    }
+    if (axis < -ndim || axis >= ndim)
+        DQ_FAIL(DQ_ERR_RANGE, "axis %d out of range for a rank-%d tensor", axis, ndim);
+    if (axis < 0) axis += ndim;
+    uint64_t inner = 1;
+    for (int d = axis + 1; d < ndim; ++d) inner *= (uint64_t)shape[d];
+    p->inner = inner ? inner : 1;
+    p->cdim = (uint64_t)shape[axis];
+    p->per_axis = p->cdim > 1 ? 1 : 0;  // a length-1 axis is per tensor
+    return DQ_OK;
+}
+
+AxisMap make_axis_map(const Plan& p, bool small) {
+    AxisMap am{};
+    am.per_axis = p.per_axis;
+    if (p.per_axis && small) {
+        am.inner = make_fastdiv((uint32_t)p.inner);
+        am.cdim = make_fastdiv((uint32_t)p.cdim);
+    }
+    return am;
+}
+
+template <typename Launch>
+int dispatch(const Plan& p, const void* in, const void* out, Launch&& launch) {
+    const bool small = p.n < (UINT64_C(1) << 32) && p.inner < (UINT64_C(1) << 32) &&
+                       p.cdim < (UINT64_C(1) << 32);
+    const bool aligned = ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    const bool vec = small && aligned;
+    const bool ch16 = !p.per_axis || p.inner % 16 == 0;
+    const AxisMap am = make_axis_map(p, small);
+    const uint64_t threads = vec ? (p.n + 15) / 16 : p.n;
+    const uint64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffffull) DQ_FAIL(DQ_ERR_ARG, "tensor too large");
+    launch(vec, ch16, am, (unsigned)blocks);
+    return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" int qlinear_quantize(const float* x, int ndim, const int64_t* shape, int axis,
+                                const float* y_scale, const void* y_zero_point,
+                                dq_dtype y_type, void* y, void* stream) {
+    Plan p;
+    int rc = make_plan(ndim, shape, axis, &p);
+    if (rc) return rc;
+    if (y_type != DQ_I8 && y_type != DQ_U8)
+        DQ_FAIL(DQ_ERR_TYPE, "QuantizeLinear output must be int8 or uint8");
+    if (p.n == 0) return DQ_OK;
+    if (!x || !y || !y_scale) DQ_FAIL(DQ_ERR_ARG, "x, y and y_scale must not be NULL");
+    hipStream_t s = (hipStream_t)stream;
+    const bool u8 = y_type == DQ_U8;
+    rc = dispatch(p, x, y, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
+#define DQ_QL(U, V, C)                                                                     \
+    hipLaunchKernelGGL((k_quantize_linear<U, V, C>), dim3(blocks), dim3(256), 0, s, x, p.n, \
+                       am, p.inner, p.cdim, y_scale, y_zero_point, (uint8_t*)y)
+        if (u8) {
+            if (!vec) DQ_QL(true, false, true);
+            else if (ch16) DQ_QL(true, true, true);
+            else DQ_QL(true, true, false);
+        } else {
+            if (!vec) DQ_QL(false, false, true);
+            else if (ch16) DQ_QL(false, true, true);
+            else DQ_QL(false, true, false);
+        }
+#undef DQ_QL
+    });
+    if (rc) return rc;
+    DQ_LAUNCH_CHECK("quantize_linear");
+    return DQ_OK;
+}
+
+extern "C" int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim, const int64_t* shape,
+                                  int axis, const float* x_scale, const void* x_zero_point,
+                                  float* y, void* stream) {
+    Plan p;
+    int rc = make_plan(ndim, shape, axis, &p);
+    if (rc) return rc;
+    if (x_type != DQ_I8 && x_type != DQ_U8)
+        DQ_FAIL(DQ_ERR_TYPE, "DequantizeLinear input must be int8 or uint8");
+    if (p.n == 0) return DQ_OK;
+    if (!x || !y || !x_scale) DQ_FAIL(DQ_ERR_ARG, "x, y and x_scale must not be NULL");
+    hipStream_t s = (hipStream_t)stream;
+    const bool u8 = x_type == DQ_U8;
+    rc = dispatch(p, x, y, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
+#define DQ_DQL(U, V, C)                                                                       \
+    hipLaunchKernelGGL((k_dequantize_linear<U, V, C>), dim3(blocks), dim3(256), 0, s,          \
+                       (const uint8_t*)x, p.n, am, p.inner, p.cdim, x_scale, x_zero_point, y)
+        if (u8) {
+            if (!vec) DQ_DQL(true, false, true);
+            else if (ch16) DQ_DQL(true, true, true);
+            else DQ_DQL(true, true, false);
+        } else {
+            if (!vec) DQ_DQL(false, false, true);
+            else if (ch16) DQ_DQL(false, true, true);
+            else DQ_DQL(false, true, false);
+        }
+#undef DQ_DQL
+    });
+    if (rc) return rc;
+    DQ_LAUNCH_CHECK("dequantize_linear");
+    return DQ_OK;
+}

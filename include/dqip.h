@@ -1,0 +1,199 @@
+/*
+ * dqip.h -- C ABI of libdqip.so: the dynamic quantized inner product and the
+ * QuantizeLinear / DequantizeLinear element-wise operators on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers (A, B, C, buf, weight, scale, bias, x, y, scales, zero
+ *    points, inspection outputs) are DEVICE pointers on the current HIP
+ *    device, owned by the caller. `params` and `shape` are HOST pointers.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it asynchronously, except where an entry point
+ *    says it synchronizes; the caller keeps its buffers alive until the
+ *    stream has completed.
+ *  - Every call returns a status (DQ_OK = 0, else a negative DQ_ERR_*).
+ *    All arguments are checked before anything is launched: on an error
+ *    nothing is enqueued and no output is touched. dqip_last_error() then
+ *    returns a message (per thread). A launch failure returns DQ_ERR_HIP.
+ *    A device fault surfaces at the caller's synchronization.
+ *  - Matrices are dense and row-major: A [M,K], B [K,N] (element B[k,j] at
+ *    k*N + j), C [M,N]. Per-column vectors (scales, bias, column sums) are [N].
+ */
+#ifndef DQIP_H
+#define DQIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types: fp32, bf16 (raw 16-bit patterns), int8, uint8. */
+typedef enum { DQ_F32 = 0, DQ_BF16 = 1, DQ_I8 = 2, DQ_U8 = 3 } dq_dtype;
+
+/* Activations applied after dequantization and bias. Leaky ReLU takes its
+ * slope from params[0] of dqip_set_params (default 0.01). */
+typedef enum { DQ_ACT_IDENTITY = 0, DQ_ACT_RELU = 1, DQ_ACT_LEAKY_RELU = 2 } dq_act;
+
+enum {
+    DQ_OK = 0,
+    DQ_ERR_ARG = -1,   /* NULL where required, size out of range, misaligned buf */
+    DQ_ERR_TYPE = -2,  /* type combination the method does not define        */
+    DQ_ERR_STATE = -3, /* no context, or forward before a required set_params */
+    DQ_ERR_RANGE = -4, /* K beyond DQ_K_MAX, axis out of range                */
+    DQ_ERR_ALLOC = -5, /* device allocation failed                            */
+    DQ_ERR_HIP = -6    /* a HIP runtime call or a kernel launch failed        */
+};
+
+/* axis value selecting per-tensor quantization in qlinear_* */
+#define DQ_PER_TENSOR INT32_MIN
+
+/* Largest K: the exact int32 sum needs 255 * 128 * K < 2^31. */
+#define DQ_K_MAX 65536
+
+typedef struct dqip_ctx dqip_ctx;
+
+/* ------------------------------------------------------------------------
+ * Dynamic quantized inner product.
+ * Defined by Simd "SynetDynamicQuantizedInnerProduct16b Class Reference",
+ * Detailed Description: A[i,k] -> uA[i,k] (uint8), scaleA[i], zeroA[i];
+ * B[k,j] -> iB[k,j] (int8), scaleB[j]; sum_k (uA - zeroA) * iB in integers;
+ * val = sum * scaleA[i] * scaleB[j]; C = Convert(Activate(val + bias[j])).
+ * This library quantizes A per row with min/max over the row and 0 in range:
+ *   scaleA = (hi - lo) / 255, zeroA = sat[0,255](rne(-lo / scaleA)),
+ *   uA = sat[0,255](rne(A / scaleA) + zeroA)
+ * and B per column, symmetric: scaleB = max|B| / qmax,
+ *   iB = sat[qmin,qmax](rne(B / scaleB)), (qmin,qmax) = (-128,127), or
+ *   (-64,63) with avoidOverflow; an all-zero row/column has scale 1 and
+ *   zero point 0. Divisions are IEEE fp32, rounding is half to even.
+ * The epilogue is fp32: ((float)sum * scaleA) * scaleB, + bias, activation,
+ * then fp32 or bf16 (round to nearest even).
+ * ---------------------------------------------------------------------- */
+
+/* Init(): create or re-create a context (same page, Init()).
+ * *ctx NULL creates one. A non-NULL *ctx whose M, N, K, types, constB,
+ * bias, activation and avoidOverflow all equal the arguments is kept as is
+ * (parameters set earlier stay); otherwise it is released and re-created,
+ * and dqip_set_params is needed again when constB is set.
+ * typeA, typeC in {DQ_F32, DQ_BF16}. typeB in {DQ_F32, DQ_I8} when constB
+ * (DQ_I8 = B already quantized, avoidOverflow then ignored), in
+ * {DQ_F32, DQ_BF16} when not. 1 <= M, N <= 2^31-1, 1 <= K <= DQ_K_MAX.
+ * Allocates the context's device buffers on the current device.
+ * Errors: DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_RANGE, DQ_ERR_ALLOC, DQ_ERR_HIP. */
+int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype typeA,
+              dq_dtype typeB, dq_dtype typeC, int constB, int bias,
+              dq_act activation, int avoidOverflow);
+
+/* Enable(): 1 if ctx is a created context, else 0. */
+int dqip_enabled(const dqip_ctx* ctx);
+
+/* InternalBufferSize(): device bytes held by the context now: packed
+ * quantized B, its column sums and scales, bias, activation parameters and,
+ * once a forward ran with buf == NULL, the fallback work buffer. 0 for NULL. */
+size_t dqip_internal_buffer_size(const dqip_ctx* ctx);
+
+/* ExternalBufferSize(): bytes the caller may pass as `buf` to dqip_forward:
+ * the quantized copy of A with its per-row scales and zero points, plus,
+ * when B is not constant, the quantized B with its scales and column sums.
+ * 0 for NULL. */
+size_t dqip_external_buffer_size(const dqip_ctx* ctx);
+
+/* Info(): "<arch> <kernels>" description of the selected implementation,
+ * owned by the context, valid until it is released. NULL for NULL. */
+const char* dqip_info(const dqip_ctx* ctx);
+
+/* SetParams() (same page, SetParams()).
+ * weight: B with K*N elements of typeB (device); required when constB, else
+ *   ignored (may be NULL). An fp32 B is quantized here, once.
+ * scale: per-column fp32 scales [N] (device); required iff typeB == DQ_I8.
+ * bias: [N] fp32 (device) or NULL (zeros); used when the context has bias.
+ * params: activation parameters (HOST); params[0] is the leaky-ReLU slope;
+ *   NULL keeps the default 0.01.
+ * Enqueues on `stream`, then synchronizes it, so the caller may free its
+ * inputs on return. Errors: DQ_ERR_STATE, DQ_ERR_ARG, DQ_ERR_HIP. */
+int dqip_set_params(dqip_ctx* ctx, const void* weight, const float* scale,
+                    const float* bias, const float* params, void* stream);
+
+/* Forward() (same page, Forward()): C = the inner product of A and B.
+ * A: [M,K] of typeA. B: [K,N] of typeB when B is not constant (quantized on
+ * every call), ignored and may be NULL when constant. C: [M,N] of typeC.
+ * buf: NULL (the context's own work buffer, allocated on first use) or at
+ * least dqip_external_buffer_size() bytes, 256-byte aligned; it receives
+ * the quantized A (and B) and must not be shared by calls in flight.
+ * Asynchronous on `stream`. Errors: DQ_ERR_STATE (not created, or constant
+ * B without dqip_set_params), DQ_ERR_ARG, DQ_ERR_ALLOC, DQ_ERR_HIP. */
+int dqip_forward(dqip_ctx* ctx, const void* A, const void* B, void* buf,
+                 void* C, void* stream);
+
+/* Clear(): release the context and its device buffers (NULL is a no-op).
+ * The caller makes sure no enqueued work still uses them. */
+void dqip_release(dqip_ctx* ctx);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* dqip_last_error(void);
+
+/* ---- inspection of the quantized operands (for parity checks) -------- */
+
+/* Unpacks the quantized A left in `buf` (NULL = the internal buffer) by the
+ * last dqip_forward: uA [M,K] uint8, scaleA [M] fp32, zeroA [M] int32. Any
+ * output may be NULL. Asynchronous on `stream`. */
+int dqip_read_quantized_a(const dqip_ctx* ctx, const void* buf, uint8_t* uA,
+                          float* scaleA, int32_t* zeroA, void* stream);
+
+/* Unpacks the quantized B -- the context's constant B, or the one the last
+ * dqip_forward left in `buf` when B is not constant -- as iB [K,N] int8,
+ * scaleB [N] fp32 and colsumB [N] int32 (sum over k of iB). Any output may
+ * be NULL. Asynchronous on `stream`. */
+int dqip_read_quantized_b(const dqip_ctx* ctx, const void* buf, int8_t* iB,
+                          float* scaleB, int32_t* colsumB, void* stream);
+
+/* dqip_forward with the integer sums as output: acc [M,N] int32 holds
+ * sum_k (uA[i,k] - zeroA[i]) * iB[k,j] instead of C (no epilogue). */
+int dqip_forward_accumulators(dqip_ctx* ctx, const void* A, const void* B,
+                              void* buf, int32_t* acc, void* stream);
+
+/* ---- per-kernel timing (for benchmarks) ------------------------------ */
+
+/* Phases of one dqip_forward, in launch order. */
+enum { DQ_PHASE_QUANT_A = 0, DQ_PHASE_QUANT_B = 1, DQ_PHASE_GEMM = 2, DQ_PHASES = 3 };
+
+/* After dqip_profile_begin(ctx, capacity) each of the next `capacity`
+ * dqip_forward / dqip_forward_accumulators calls records HIP events on its
+ * stream around each phase's kernels (nothing else changes; no sync).
+ * dqip_profile_end waits for the recorded events and writes, per phase, the
+ * summed milliseconds to ms[DQ_PHASES] (DQ_PHASE_QUANT_B stays 0 for a
+ * constant B) and the number of recorded calls to *calls; it then stops
+ * recording. Errors: DQ_ERR_STATE, DQ_ERR_ARG (capacity < 1), DQ_ERR_HIP. */
+int dqip_profile_begin(dqip_ctx* ctx, int capacity);
+int dqip_profile_end(dqip_ctx* ctx, float* ms, int* calls);
+
+/* ------------------------------------------------------------------------
+ * QuantizeLinear / DequantizeLinear.
+ * Defined by onnxruntime quantization_defs.cc, QuantizeLinear and
+ * DequantizeLinear docs: y = saturate(x / y_scale + y_zero_point) with
+ * x / y_scale rounded to nearest, ties to even (IEEE fp32 division),
+ * saturating to [0,255] (uint8) or [-128,127] (int8); and
+ * y = (x - x_zero_point) * x_scale. Scale and zero point are one value
+ * (axis = DQ_PER_TENSOR) or one per index of dimension `axis` (negative
+ * axis counts from the end).
+ * x, y: dense row-major tensors of the given shape (HOST array of ndim
+ * sizes, 1 <= ndim <= 8, each >= 0; zero elements is a no-op). Scales are
+ * fp32, zero points have the 8-bit type (NULL = 0).
+ * Asynchronous on `stream`. Errors: DQ_ERR_ARG, DQ_ERR_TYPE (x must be
+ * DQ_F32 to quantize, int8/uint8 to dequantize), DQ_ERR_RANGE (axis),
+ * DQ_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+int qlinear_quantize(const float* x, int ndim, const int64_t* shape, int axis,
+                     const float* y_scale, const void* y_zero_point,
+                     dq_dtype y_type, void* y, void* stream);
+
+int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim,
+                       const int64_t* shape, int axis, const float* x_scale,
+                       const void* x_zero_point, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQIP_H */

@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: libdqip.so loads, exports every entry point that
+include/dqip.h declares, and rejects bad arguments before touching the GPU
+(no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dqip.h")
+
+
+@pytest.fixture(scope="module")
+def dq():
+    import dynamic_quantized_gemm_amd as dq
+    from dynamic_quantized_gemm_amd import build
+
+    if not os.path.exists(dq.LIB_PATH):
+        build.build()
+    dq.load()
+    return dq
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    skip = {"sizeof", "defined", "if"}
+    return sorted({n for n in names if n not in skip and (n.startswith("dqip_") or n.startswith("qlinear_"))})
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("dqip_init", "dqip_set_params", "dqip_forward", "qlinear_quantize",
+              "qlinear_dequantize", "dqip_release", "dqip_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(dq):
+    lib = C.CDLL(dq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in dqip.h but not exported"
+    # and the binding wraps each of them under the same name
+    assert set(declared_functions()) == set(dq.exported_symbols())
+    for name in declared_functions():
+        assert callable(getattr(dq, name))
+
+
+def test_no_torch_types_in_the_header():
+    text = open(HEADER).read()
+    code = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    assert "torch" not in code.lower()
+    assert "at::" not in code and "c10" not in code
+    assert "#include <hip" not in code  # plain C: the stream is a void*
+
+
+def _init_rc(dq, *args):
+    h = C.c_void_p(None)
+    return dq.load().dqip_init(C.byref(h), *args), h.value
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 8, 16, 0, 0, 0, 1, 1, 0, 0), "ARG"),            # M = 0
+    ((4, 0, 16, 0, 0, 0, 1, 1, 0, 0), "ARG"),            # N = 0
+    ((4, 8, 0, 0, 0, 0, 1, 1, 0, 0), "ARG"),             # K = 0
+    ((4, 8, 65537, 0, 0, 0, 1, 1, 0, 0), "RANGE"),       # K > DQ_K_MAX
+    ((4, 8, 16, 2, 0, 0, 1, 1, 0, 0), "TYPE"),           # typeA int8
+    ((4, 8, 16, 0, 0, 3, 1, 1, 0, 0), "TYPE"),           # typeC uint8
+    ((4, 8, 16, 0, 2, 0, 0, 1, 0, 0), "TYPE"),           # int8 B, not constant
+    ((4, 8, 16, 0, 1, 0, 1, 1, 0, 0), "TYPE"),           # bf16 B, constant
+    ((4, 8, 16, 0, 3, 0, 1, 1, 0, 0), "TYPE"),           # uint8 B
+    ((4, 8, 16, 0, 0, 0, 1, 1, 7, 0), "ARG"),            # unknown activation
+])
+def test_init_rejects_bad_arguments(dq, args, code):
+    rc, h = _init_rc(dq, *args)
+    assert rc == getattr(dq, "DQ_ERR_" + code)
+    assert h is None
+    assert dq.dqip_last_error()
+
+
+def test_null_context_calls(dq):
+    lib = dq.load()
+    assert lib.dqip_enabled(None) == 0
+    assert lib.dqip_internal_buffer_size(None) == 0
+    assert lib.dqip_external_buffer_size(None) == 0
+    assert lib.dqip_info(None) is None
+    assert lib.dqip_forward(None, 1, None, None, 1, None) == dq.DQ_ERR_STATE
+    assert lib.dqip_set_params(None, 1, None, None, None, None) == dq.DQ_ERR_STATE
+    assert lib.dqip_forward_accumulators(None, 1, None, None, 1, None) == dq.DQ_ERR_STATE
+    lib.dqip_release(None)
+    rc = lib.dqip_init(None, 4, 8, 16, 0, 0, 0, 1, 1, 0, 0)
+    assert rc == dq.DQ_ERR_ARG
+
+
+def _shape(s):
+    return (C.c_int64 * len(s))(*s)
+
+
+def test_qlinear_rejects_bad_arguments(dq):
+    lib = dq.load()
+    shp = _shape([2, 3, 4])
+    # ndim out of range
+    assert lib.qlinear_quantize(1, 0, shp, dq.DQ_PER_TENSOR, 1, None, dq.DQ_I8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_quantize(1, 9, shp, dq.DQ_PER_TENSOR, 1, None, dq.DQ_I8, 1, None) == dq.DQ_ERR_ARG
+    # axis out of range
+    assert lib.qlinear_quantize(1, 3, shp, 3, 1, None, dq.DQ_I8, 1, None) == dq.DQ_ERR_RANGE
+    assert lib.qlinear_quantize(1, 3, shp, -4, 1, None, dq.DQ_I8, 1, None) == dq.DQ_ERR_RANGE
+    # output type
+    assert lib.qlinear_quantize(1, 3, shp, 1, 1, None, dq.DQ_F32, 1, None) == dq.DQ_ERR_TYPE
+    assert lib.qlinear_dequantize(1, dq.DQ_BF16, 3, shp, 1, 1, None, 1, None) == dq.DQ_ERR_TYPE
+    # NULL tensors
+    assert lib.qlinear_quantize(None, 3, shp, 1, 1, None, dq.DQ_I8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_dequantize(1, dq.DQ_I8, 3, shp, 1, None, None, 1, None) == dq.DQ_ERR_ARG
+    # negative dimension
+    bad = _shape([2, -1])
+    assert lib.qlinear_quantize(1, 2, bad, dq.DQ_PER_TENSOR, 1, None, dq.DQ_I8, 1, None) == dq.DQ_ERR_ARG
+    # zero elements: a no-op that succeeds without a device
+    empty = _shape([4, 0, 3])
+    assert lib.qlinear_quantize(None, 3, empty, 1, None, None, dq.DQ_U8, None, None) == dq.DQ_OK
+    assert lib.qlinear_dequantize(None, dq.DQ_U8, 3, empty, 1, None, None, None, None) == dq.DQ_OK
+
+
+def test_fastdiv_constants_cover_every_quotient():
+    # the per-axis kernels find the channel with q = (umulhi(n, m) + n) >> s;
+    # the host-side constants must give the exact quotient for all n < 2^32.
+    # Checked here on the CPU with the same construction, for divisors that
+    # the axis sizes of the workloads and awkward values produce.
+    import numpy as np
+
+    def consts(d):
+        s = 0
+        while (1 << s) < d:
+            s += 1
+        m = ((1 << 32) * ((1 << s) - d)) // d + 1
+        return m, s
+
+    r = np.random.default_rng(5)
+    for d in [1, 2, 3, 7, 49, 56, 64, 255, 256, 3136, 12544, 802816, 2 ** 31 - 1, 2 ** 32 - 1]:
+        m, s = consts(d)
+        assert m < 2 ** 32
+        ns = np.concatenate([r.integers(0, 2 ** 32, 20000, dtype=np.uint64),
+                             np.array([0, 1, d - 1, d, d + 1, 2 ** 32 - 1], dtype=np.uint64)])
+        ns = ns[ns < 2 ** 32]
+        hi = (ns * np.uint64(m)) >> np.uint64(32)
+        q = (hi + ns) >> np.uint64(s)
+        assert np.array_equal(q, ns // np.uint64(d)), d

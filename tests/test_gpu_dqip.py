@@ -1,0 +1,217 @@
+"""GPU parity of the dynamic quantized inner product against the CPU oracle.
+
+Integer outputs (uA, zeroA, iB, column sums, int32 sums) must be bit-exact,
+and so must scaleA / scaleB (IEEE division on both sides). C must be within
+1e-5 relative (fp32; reference magnitude |C| + |bias|) or 1 ulp (bf16)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_case import assert_close_c, log, run_dqip
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(case, got, want, rows=None, check_b=True):
+    r = slice(None) if rows is None else rows
+    for key in ("uA", "scaleA", "zeroA"):
+        if key in got:
+            g = got[key][r]
+            w = want[key]
+            assert np.array_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                                  w.view(np.uint32) if w.dtype == np.float32 else w), key
+    if check_b and "iB" in got:
+        assert np.array_equal(got["iB"], want["iB"]), "iB"
+        assert np.array_equal(got["scaleB"].view(np.uint32), want["scaleB"].view(np.uint32)), "scaleB"
+        assert np.array_equal(got["colsumB"], want["colsumB"]), "colsumB"
+    if "acc" in got:
+        assert np.array_equal(got["acc"][r], want["acc"]), "int32 sums"
+    return assert_close_c(got["C"][r], want["C"], case["typeC"], case.get("bias"))
+
+
+def test_ramp_usage_example(gpu):
+    log("dqip ramp 4x8x16")
+    case = W.dqip_ramp()
+    got = run_dqip(gpu, case)
+    exact = _compare(case, got, oracle.dqip_forward(case))
+    log(f"  {exact}% of C bit-identical; info: {got['info']}")
+
+
+def test_small_64x64x128(gpu):
+    log("dqip 64x64x128")
+    case = W.dqip_small()
+    _compare(case, run_dqip(gpu, case), oracle.dqip_forward(case))
+
+
+SWEEP = [
+    # (M, N, K, typeA, typeB, constB, typeC, act, avoid)
+    (1, 1, 1, "f32", "f32", True, "f32", "identity", False),
+    (7, 13, 29, "f32", "f32", True, "f32", "relu", True),
+    (129, 130, 200, "bf16", "i8", True, "bf16", "relu", False),
+    (257, 63, 513, "f32", "f32", False, "f32", "leaky_relu", True),
+    (33, 300, 1000, "bf16", "bf16", False, "bf16", "identity", False),
+    (128, 128, 128, "f32", "i8", True, "f32", "identity", False),
+    (200, 77, 4100, "f32", "f32", False, "bf16", "relu", False),
+    (64, 256, 333, "bf16", "f32", True, "f32", "leaky_relu", False),
+    (5, 1, 70, "f32", "bf16", False, "f32", "identity", True),
+    (300, 5, 16, "bf16", "i8", True, "f32", "relu", False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,tA,tB,constB,tC,act,avoid", SWEEP)
+def test_sweep_odd_shapes(gpu, M, N, K, tA, tB, constB, tC, act, avoid):
+    log(f"dqip sweep {M}x{N}x{K} A:{tA} B:{tB} const:{constB} C:{tC} {act} avoid:{avoid}")
+    case = W.dqip_random(M, N, K, seed=M * 7 + N * 3 + K, typeA=tA, typeB=tB, typeC=tC,
+                         constB=constB, act=act, avoid=avoid, alpha=0.1, outliers=0.01,
+                         zero_rows=(0,) if M > 2 else (), zero_cols=(N - 1,) if N > 2 else ())
+    _compare(case, run_dqip(gpu, case, ext_buf=(M % 2 == 1)), oracle.dqip_forward(case))
+
+
+def test_no_bias_flag_and_null_bias(gpu):
+    log("dqip bias handling")
+    case = W.dqip_random(40, 24, 96, seed=3, bias=False)
+    _compare(case, run_dqip(gpu, case), oracle.dqip_forward(case))
+    # bias flag set but NULL bias pointer: zeros are added
+    case2 = dict(case, has_bias=True)
+    got = run_dqip(gpu, case2)
+    want = oracle.dqip_forward(dict(case2, bias=None))
+    _compare(case, got, want)
+
+
+def test_internal_and_external_buffers_agree_and_repeat_bitwise(gpu):
+    log("dqip buffers + determinism")
+    case = W.dqip_random(300, 260, 700, seed=11, typeA="bf16", typeB="f32", constB=False,
+                         typeC="bf16", act="relu", avoid=True)
+    a = run_dqip(gpu, case, ext_buf=False, repeat=3)
+    b = run_dqip(gpu, case, ext_buf=True, repeat=2)
+    for key in ("C", "uA", "iB", "acc", "colsumB"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_reinit_keeps_or_recreates(gpu):
+    import torch
+
+    log("dqip re-init")
+    case = W.dqip_random(16, 32, 64, seed=12, typeB="i8")
+    got = run_dqip(gpu, case, keep_ctx=True)
+    h = got["ctx"]
+    try:
+        # same parameters: the context and its set parameters are kept
+        h2 = gpu.dqip_init(16, 32, 64, gpu.DQ_F32, gpu.DQ_I8, gpu.DQ_F32, True, True,
+                           gpu.DQ_ACT_IDENTITY, False, ctx=h)
+        assert h2 == h
+        A = torch.from_numpy(case["A"]).cuda()
+        C = torch.empty((16, 32), device="cuda")
+        gpu.dqip_forward(h2, A, None, None, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), got["C"])
+        # a change (activation): re-created, set_params needed again
+        h3 = gpu.dqip_init(16, 32, 64, gpu.DQ_F32, gpu.DQ_I8, gpu.DQ_F32, True, True,
+                           gpu.DQ_ACT_RELU, False, ctx=h2)
+        with pytest.raises(gpu.DQError) as e:
+            gpu.dqip_forward(h3, A, None, None, C)
+        assert e.value.status == gpu.DQ_ERR_STATE
+        h = h3
+    finally:
+        gpu.dqip_release(h)
+
+
+def test_argument_errors_on_device(gpu):
+    import torch
+
+    log("dqip argument errors")
+    h = gpu.dqip_init(8, 8, 8, gpu.DQ_F32, gpu.DQ_F32, gpu.DQ_F32, False, False,
+                      gpu.DQ_ACT_IDENTITY, False)
+    try:
+        A = torch.zeros((8, 8), device="cuda")
+        C = torch.empty((8, 8), device="cuda")
+        with pytest.raises(gpu.DQError) as e:  # non-constant B missing
+            gpu.dqip_forward(h, A, None, None, C)
+        assert e.value.status == gpu.DQ_ERR_ARG
+        buf = torch.empty(gpu.dqip_external_buffer_size(h) + 512, dtype=torch.uint8, device="cuda")
+        with pytest.raises(gpu.DQError) as e:  # misaligned buf
+            gpu.dqip_forward(h, A, A, buf.data_ptr() + 1, C)
+        assert e.value.status == gpu.DQ_ERR_ARG
+        with pytest.raises(gpu.DQError) as e:
+            gpu.dqip_read_quantized_a(h, None, None)  # internal buffer never used
+        assert e.value.status == gpu.DQ_ERR_STATE
+    finally:
+        gpu.dqip_release(h)
+    h = gpu.dqip_init(8, 8, 8, gpu.DQ_F32, gpu.DQ_I8, gpu.DQ_F32, True, False,
+                      gpu.DQ_ACT_IDENTITY, False)
+    try:
+        B = torch.zeros((8, 8), dtype=torch.int8, device="cuda")
+        with pytest.raises(gpu.DQError) as e:  # int8 B without scales
+            gpu.dqip_set_params(h, B, None, None, None)
+        assert e.value.status == gpu.DQ_ERR_ARG
+        with pytest.raises(gpu.DQError) as e:  # forward before set_params
+            gpu.dqip_forward(h, torch.zeros((8, 8), device="cuda"), None, None,
+                             torch.empty((8, 8), device="cuda"))
+        assert e.value.status == gpu.DQ_ERR_STATE
+    finally:
+        gpu.dqip_release(h)
+
+
+def test_extreme_sums_stay_exact(gpu):
+    """Every row spans [-x, +x] and B saturates: the int32 sums reach
+    255*128*K magnitudes at K = 16384 and must still be exact."""
+    log("dqip extreme sums")
+    M, N, K = 64, 64, 16384
+    A = np.empty((M, K), np.float32)
+    A[:, :] = 1.0
+    A[:, 0] = -1e-30  # lo just below 0: zeroA = 0, every other code 255
+    B = np.full((K, N), -128, np.int8)
+    B[:, 1::2] = 127
+    case = dict(name="extreme", M=M, N=N, K=K, A=A, B=B, typeA="f32", typeB="i8", typeC="f32",
+                constB=True, bias=None, act="identity", alpha=0.01, avoid=False,
+                scaleB=np.full(N, 1e-3, np.float32))
+    want = oracle.dqip_forward(case)
+    assert abs(int(want["acc"].min())) > 2 ** 29
+    _compare(case, run_dqip(gpu, case), want)
+
+
+# ------------------------------------------------------------ full sizes
+
+def _sample_rows(M, seed, n=12):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], r.integers(0, M, n)])).astype(np.int64)
+
+
+def _compare_sampled(case, got, rows):
+    want = oracle.dqip_forward(case, rows=rows)
+    return _compare(case, got, want, rows=rows)
+
+
+def test_full_4096_bf16_relu(gpu):
+    log("dqip full 4096x4096x4096 bf16 A, int8 B, relu, bf16 out")
+    case = W.dqip_large()
+    got = run_dqip(gpu, case, accumulators=True)
+    # quantized A: every row bit-exact
+    uA, sA, zA = oracle.quantize_rows(case["A"], "bf16")
+    assert np.array_equal(got["uA"], uA) and np.array_equal(got["zeroA"], zA)
+    assert np.array_equal(got["scaleA"].view(np.uint32), sA.view(np.uint32))
+    assert np.array_equal(got["iB"], case["B"])
+    assert np.array_equal(got["colsumB"], oracle.colsum(case["B"]))
+    rows = _sample_rows(case["M"], 1)
+    _compare_sampled(case, got, rows)
+
+
+@pytest.mark.parametrize("recurrent", [False, True])
+def test_full_lstm_gates(gpu, recurrent):
+    log(f"dqip lstm gates recurrent={recurrent}")
+    case = W.dqip_lstm(recurrent=recurrent)
+    got = run_dqip(gpu, case)
+    if recurrent:
+        _compare(case, got, oracle.dqip_forward(case))
+    else:
+        _compare_sampled(case, got, _sample_rows(case["M"], 2, n=64))
+
+
+def test_full_8192_dynamic_b(gpu):
+    log("dqip full 8192^3 dynamic fp32 B, avoidOverflow")
+    case = W.dqip_dynamic_b()
+    got = run_dqip(gpu, case, accumulators=False)
+    rows = _sample_rows(case["M"], 3, n=6)
+    want = oracle.dqip_forward(case, rows=rows)
+    _compare(case, got, want, rows=rows, check_b=True)

@@ -1,0 +1,118 @@
+"""GPU parity of QuantizeLinear / DequantizeLinear against the CPU oracle:
+bit-exact on every element (integer codes and single-rounding fp32)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_case import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_q(dq, x, scale, zp, axis, y_type):
+    import torch
+
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    sd = torch.from_numpy(np.atleast_1d(scale).astype(np.float32)).cuda()
+    zd = None if zp is None else torch.from_numpy(np.atleast_1d(zp)).cuda()
+    y = torch.empty(x.shape, dtype=torch.int8 if y_type == "i8" else torch.uint8, device="cuda")
+    dq.qlinear_quantize(xd, sd, zd, dq.DQ_I8 if y_type == "i8" else dq.DQ_U8, y,
+                        axis=dq.DQ_PER_TENSOR if axis is None else axis)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _run_dq(dq, q, scale, zp, axis):
+    import torch
+
+    qd = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+    sd = torch.from_numpy(np.atleast_1d(scale).astype(np.float32)).cuda()
+    zd = None if zp is None else torch.from_numpy(np.atleast_1d(zp)).cuda()
+    y = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dq.qlinear_dequantize(qd, dq.DQ_U8 if q.dtype == np.uint8 else dq.DQ_I8, sd, zd, y,
+                          axis=dq.DQ_PER_TENSOR if axis is None else axis)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _check_both(dq, x, scale, zp, axis, y_type):
+    ax = None if axis is None else axis
+    want = oracle.quantize_linear(x, scale, zp, axis=ax, y_type=y_type)
+    got = _run_q(dq, x, scale, zp, axis, y_type)
+    assert np.array_equal(got, want), f"{(got != want).sum()} codes differ"
+    back_want = oracle.dequantize_linear(want, scale, zp, axis=ax)
+    back = _run_dq(dq, want, scale, zp, axis)
+    assert np.array_equal(back.view(np.uint32), back_want.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape,axis", [
+    ((2, 16, 9, 11), 1),     # inner 99: channel per element
+    ((4, 32, 8, 8), 1),      # inner 64: channel per 16-vector
+    ((3, 5, 7), 0),          # leading axis
+    ((3, 5, 7), 2),          # last axis, inner 1
+    ((3, 5, 7), -2),         # negative axis
+    ((1000003,), None),      # per tensor, ragged tail
+    ((17,), 0),              # tiny, per element scales
+])
+@pytest.mark.parametrize("y_type", ["i8", "u8"])
+def test_qdq_parity_small(gpu, shape, axis, y_type):
+    log(f"qdq small shape={shape} axis={axis} {y_type}")
+    ax = 0 if axis is None else axis
+    case = W.qdq_per_axis(seed=7, shape=shape, axis=ax % len(shape), plant_every=13)
+    x = case["x"]
+    C = shape[ax]
+    if axis is None:
+        scale, zp = np.float32([0.02]), np.array([3 if y_type == "u8" else -3])
+    else:
+        scale = case["scale"]
+        zp = case["zp"]
+    if y_type == "u8":
+        zp = (np.asarray(zp).astype(np.int32) + 120).astype(np.uint8)
+    else:
+        zp = np.asarray(zp).astype(np.int8)
+    _check_both(gpu, x, scale, zp, axis, y_type)
+
+
+def test_qdq_zero_point_absent_means_zero(gpu):
+    log("qdq zp NULL")
+    x = W.qdq_per_axis(seed=8, shape=(2, 4, 33), axis=1, plant_every=5)["x"]
+    s = np.float32([0.01, 0.02, 0.03, 0.04])
+    got = _run_q(gpu, x, s, None, 1, "i8")
+    assert np.array_equal(got, oracle.quantize_linear(x, s, np.zeros(4, np.int8), axis=1))
+
+
+def test_qdq_unaligned_views_take_the_scalar_path(gpu):
+    import torch
+
+    log("qdq unaligned")
+    x = W.qdq_per_axis(seed=9, shape=(3, 7, 41), axis=1, plant_every=7)["x"]
+    scale = np.linspace(0.01, 0.05, 7).astype(np.float32)
+    zp = np.arange(-3, 4).astype(np.int8)
+    flat = torch.from_numpy(np.concatenate([[0.0], x.reshape(-1)]).astype(np.float32)).cuda()
+    xv = flat[1:]  # 4-byte aligned, not 16-byte aligned
+    y = torch.empty(x.size + 1, dtype=torch.int8, device="cuda")[1:]
+    gpu.qlinear_quantize(xv, torch.from_numpy(scale).cuda(), torch.from_numpy(zp).cuda(),
+                         gpu.DQ_I8, y, axis=1, shape=x.shape)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().reshape(x.shape),
+                          oracle.quantize_linear(x, scale, zp, axis=1))
+
+
+def test_qdq_empty_tensor_is_a_no_op(gpu):
+    import torch
+
+    x = torch.empty((4, 0, 3), dtype=torch.float32, device="cuda")
+    y = torch.empty((4, 0, 3), dtype=torch.int8, device="cuda")
+    s = torch.ones(1, device="cuda")
+    gpu.qlinear_quantize(x, s, None, gpu.DQ_I8, y)
+    torch.cuda.synchronize()
+
+
+def test_qdq_full_size_per_axis(gpu):
+    """The per-channel workload at its full size, [64,256,56,56] NCHW, axis 1,
+    int8 output with ties and saturation planted: every element compared."""
+    log("qdq full [64,256,56,56]")
+    case = W.qdq_per_axis(seed=1)
+    assert case["n_ties"] > 1000
+    _check_both(gpu, case["x"], case["scale"], case["zp"], 1, "i8")
