@@ -36,12 +36,72 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Four fp32 values to packed bf16 with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u2 f32x4_to_bf16x4(f4 v) {
+    const f2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+    const bf16x2 a = __builtin_convertvector(lo, bf16x2);
+    const bf16x2 b = __builtin_convertvector(hi, bf16x2);
+    const u2 r = {__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)};
+    return r;
+}
+
 // saturate(r + zp) into [lo, hi] for an integral float r (possibly +-inf):
 // clamping r to [lo - zp, hi - zp] first is exact, since both bounds are
 // small integers, and keeps the int conversion in range.
 __device__ __forceinline__ int sat_add(float r, int zp, int lo, int hi) {
     float c = __builtin_fminf(__builtin_fmaxf(r, (float)(lo - zp)), (float)(hi - zp));
     return (int)c + zp;
+}
+
+// Quotient x / s where only its rounding to an integer matters (the
+// quantizers). y = 1/s is the correctly rounded reciprocal, computed once
+// per scale. One residual step, q = q0 + (x - q0*s) * y with both products
+// fused, returns the IEEE quotient for every |x/s| >= 1/4 (checked over all
+// 2^32 fp32 x for a set of scales), so rne(q) matches rne(x / s) at every tie
+// and boundary; below 1/4 both round to 0. Beyond 2^24 the product q0 is
+// used as is: it saturates exactly like the quotient. A scale whose
+// reciprocal is not a normal number takes the IEEE division.
+struct QDiv {
+    float s, y;
+    bool fast;
+};
+
+__device__ __forceinline__ QDiv make_qdiv(float s) {
+    QDiv d;
+    d.s = s;
+    d.y = 1.0f / s;
+    const float ay = __builtin_fabsf(d.y);
+    d.fast = ay >= 1.17549435e-38f && ay <= 3.40282347e+38f;
+    return d;
+}
+
+__device__ __forceinline__ float qdiv(float x, const QDiv& d) {
+    if (!d.fast) return x / d.s;
+    const float q0 = x * d.y;
+    if (!(__builtin_fabsf(q0) <= 16777216.0f)) return q0;
+    const float r = __builtin_fmaf(-q0, d.s, x);
+    return __builtin_fmaf(r, d.y, q0);
+}
+
+// The residual step alone, for callers that have checked d.fast and whose
+// quotients are bounded (|x / s| <= 2^24) by construction.
+__device__ __forceinline__ float qdiv_fast(float x, const QDiv& d) {
+    const float q0 = x * d.y;
+    const float r = __builtin_fmaf(-q0, d.s, x);
+    return __builtin_fmaf(r, d.y, q0);
+}
+
+// Byte offset of element (r, k) of an operand packed in MFMA fragment order:
+// 1 KiB fragments of 32 rows x 32 k, fragment (r/32, k/32) at index
+// (r/32) * KF + k/32 (KF = Kp/32); inside it, lane slot (r%32) + 32*((k%32)/16)
+// holds the 16 codes k%32 in [0,16) or [16,32) of row r. One ds_read_b128 /
+// global_load_dwordx4 per lane at slot*16 yields the v_mfma_i32_32x32x32_i8
+// operand for rows (or columns) r%32.
+__host__ __device__ __forceinline__ size_t frag_offset(size_t r, size_t k, size_t KF) {
+    return (((r >> 5) * KF + (k >> 5)) << 10) + (((r & 31) + ((k & 16) << 1)) << 4) + (k & 15);
 }
 
 // Wave-wide min / max over 64 lanes (butterfly over xor shuffles).

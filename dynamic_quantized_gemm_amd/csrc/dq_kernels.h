@@ -6,28 +6,35 @@
 
 #include "dqip.h"
 
-// K is padded to a multiple of this in the packed operands: sA [M][Kp] and
-// iBt [N][Kp]. The padding of iBt is zero, so it adds nothing to a sum.
+// Packed operands (MFMA fragment order, see frag_offset in dq_device.h):
+// sA [Mp x Kp] holds uA - 128, iBp [Np x Kp] holds iB transposed (column j
+// of B is packed row j). K is padded to Kp (multiple of 128) with zero codes
+// in iBp, so the padding adds nothing to a sum; M and N are padded to
+// multiples of 256 (the largest tile) and the padding rows / columns are
+// never stored to C. Per-column vectors (scaleB, colsum, bias) hold Np
+// entries so the epilogue can read them in 16-byte vectors.
 constexpr int kKpAlign = 128;
+constexpr int kMNAlign = 256;
 
 inline size_t dq_kp(size_t K) { return (K + kKpAlign - 1) / kKpAlign * kKpAlign; }
+inline size_t dq_mnp(size_t X) { return (X + kMNAlign - 1) / kMNAlign * kMNAlign; }
 
 // Per-row dynamic quantization of A [M,K] (fp32 or bf16):
-// sA [M][Kp] = uA - 128 (int8), scaleA [M], zeroA [M].
+// sA (packed, uA - 128), scaleA [M], zeroA [M].
 int dq_launch_quant_rows(const void* A, bool bf16, int M, int K, int Kp, int8_t* sA,
                          float* scaleA, int32_t* zeroA, hipStream_t s);
 
-// B [K,N] -> iBt [N][Kp] (transposed, zero padded), colsum [N], and for an
-// fp32/bf16 B also scaleB [N] (per-column symmetric quantization). For an
-// int8 B the codes are packed as given and scaleB is left alone.
+// B [K,N] -> iBp (packed, zero K padding), colsum [N], and for an fp32/bf16 B
+// also scaleB [N] (per-column symmetric quantization). For an int8 B the
+// codes are packed as given and scaleB is left alone.
 // amax: N words of scratch (fp32 / bf16 B only).
 int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, int avoid,
-                         int8_t* iBt, float* scaleB, int32_t* colsum, uint32_t* amax,
+                         int8_t* iBp, float* scaleB, int32_t* colsum, uint32_t* amax,
                          hipStream_t s);
 
-// Inspection: sA [M][Kp] -> uA [M,K]; iBt [N][Kp] -> iB [K,N].
+// Inspection: packed sA -> uA [M,K]; packed iBp -> iB [K,N].
 int dq_launch_unpack_a(const int8_t* sA, int M, int K, int Kp, uint8_t* uA, hipStream_t s);
-int dq_launch_unpack_b(const int8_t* iBt, int K, int N, int Kp, int8_t* iB, hipStream_t s);
+int dq_launch_unpack_b(const int8_t* iBp, int K, int N, int Kp, int8_t* iB, hipStream_t s);
 
 enum { DQ_OUT_F32 = 0, DQ_OUT_BF16 = 1, DQ_OUT_ACC = 2 };
 
@@ -43,8 +50,8 @@ struct DqEpilogue {
     void* C;            // [M,N]
 };
 
-// acc = sA * iBt^T + (128 - zeroA[i]) * colsumB[j], then the epilogue.
-int dq_launch_gemm(const int8_t* sA, const int8_t* iBt, int M, int N, int Kp,
+// acc = sA * iB + (128 - zeroA[i]) * colsumB[j], then the epilogue.
+int dq_launch_gemm(const int8_t* sA, const int8_t* iBp, int M, int N, int Kp,
                    const DqEpilogue& ep, hipStream_t s);
 
 // A short description of the kernels dq_launch_gemm picks for a shape.

@@ -49,11 +49,11 @@ struct dqip_ctx {
     float alpha;
     int params_set;
     // context-owned device memory
-    int8_t* iBt;       // [N][Kp] (constant B)
-    float* scaleB;     // [N]     (constant B)
-    int32_t* colsum;   // [N]     (constant B)
+    int8_t* iBt;       // [Np x Kp] packed (constant B)
+    float* scaleB;     // [Np]    (constant B)
+    int32_t* colsum;   // [Np]    (constant B)
     uint32_t* amax;    // [N]     column-maxima scratch for set_params
-    float* biasv;      // [N]     (bias flag)
+    float* biasv;      // [Np]    (bias flag; zero past N)
     void* work;        // fallback work buffer (first forward with buf NULL)
     size_t owned_bytes;
     WorkLayout lay;
@@ -66,22 +66,25 @@ struct dqip_ctx {
 
 namespace {
 
+// Work buffer: packed sA [Mp x Kp], scaleA, zeroA [M]; for a non-constant B
+// also packed iB [Np x Kp], scaleB, colsum [Np] and the column maxima [N].
 WorkLayout make_layout(size_t M, size_t N, size_t Kp, int constB) {
     WorkLayout l{};
+    const size_t Mp = dq_mnp(M), Np = dq_mnp(N);
     size_t o = 0;
     l.sA = o;
-    o = align_up(o + M * Kp);
+    o = align_up(o + Mp * Kp);
     l.scaleA = o;
     o = align_up(o + 4 * M);
     l.zeroA = o;
     o = align_up(o + 4 * M);
     if (!constB) {
         l.iBt = o;
-        o = align_up(o + N * Kp);
+        o = align_up(o + Np * Kp);
         l.scaleB = o;
-        o = align_up(o + 4 * N);
+        o = align_up(o + 4 * Np);
         l.colsum = o;
-        o = align_up(o + 4 * N);
+        o = align_up(o + 4 * Np);
         l.amax = o;
         o = align_up(o + 4 * N);
     }
@@ -264,16 +267,17 @@ extern "C" int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype 
     c->params_set = 0;
     c->lay = make_layout(M, N, c->Kp, constB);
     int rc = DQ_OK;
+    const size_t Np = dq_mnp(N);
     if (constB) {
-        if (!rc) rc = dev_alloc(c, (void**)&c->iBt, N * c->Kp);
-        if (!rc) rc = dev_alloc(c, (void**)&c->scaleB, 4 * N);
-        if (!rc) rc = dev_alloc(c, (void**)&c->colsum, 4 * N);
+        if (!rc) rc = dev_alloc(c, (void**)&c->iBt, Np * c->Kp);
+        if (!rc) rc = dev_alloc(c, (void**)&c->scaleB, 4 * Np);
+        if (!rc) rc = dev_alloc(c, (void**)&c->colsum, 4 * Np);
         if (!rc) rc = dev_alloc(c, (void**)&c->amax, 4 * N);
     }
     if (!rc && bias) {
-        rc = dev_alloc(c, (void**)&c->biasv, 4 * N);
+        rc = dev_alloc(c, (void**)&c->biasv, 4 * Np);
         if (!rc) {
-            hipError_t e = hipMemset(c->biasv, 0, 4 * N);
+            hipError_t e = hipMemset(c->biasv, 0, 4 * Np);
             if (e != hipSuccess) {
                 dq_set_error("hipMemset failed: %s", hipGetErrorString(e));
                 rc = DQ_ERR_HIP;
@@ -287,7 +291,7 @@ extern "C" int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype 
     }
     char buf[256];
     snprintf(buf, sizeof buf,
-             "gfx950 A:%s B:%s%s C:%s | quant_rows wave-per-row | %s%s | %s",
+             "gfx950 A:%s B:%s%s C:%s | quant_rows wave-per-row, fragment-packed | %s%s | %s",
              dtype_name(typeA), dtype_name(typeB), constB ? "(const)" : "(dynamic)",
              dtype_name(typeC), constB ? "" : "quant_cols absmax+pack | ",
              avoidOverflow ? "B range [-64,63]" : "B range [-128,127]",

@@ -6,14 +6,15 @@
 // DequantizeLinear doc (y = (x - x_zero_point) * x_scale); scale and zero
 // point per tensor or per 'axis'.
 //
-// Both kernels are element-wise and bound by HBM bandwidth: every thread
-// moves one 16-byte vector of 8-bit codes and the four matching 16-byte
-// vectors of fp32, so each wave issues fully coalesced 1 KiB / 4 KiB
-// transactions. The tensor is viewed as [outer, C, inner]; the channel of
-// element e is (e / inner) % C, found with multiply-high division by
-// constants precomputed on the host. When inner is a multiple of 16 a
-// 16-element vector never straddles two channels and the channel is found
-// once per vector.
+// Both kernels are element-wise and bound by HBM bandwidth: each wave
+// instruction moves one contiguous 1 KiB of fp32 (16 bytes per lane) or the
+// matching 256 bytes of 8-bit codes (4 per lane). The tensor is viewed as
+// [outer, C, inner]; the channel of element e is (e / inner) % C, found with
+// multiply-high division by constants precomputed on the host. When inner
+// is a multiple of 4 a 4-element vector never straddles two channels and the
+// channel (and the reciprocal of its scale) is found once per vector. The
+// quotient x / y_scale is rounded through dq::qdiv, which gives the IEEE
+// quotient's rounding to an integer.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -71,58 +72,51 @@ __device__ __forceinline__ int quant1(float x, float s, int zp) {
 
 // ---------------------------------------------------------------- quantize
 
-// VEC: 16 elements per thread through 16-byte loads and one 16-byte store
-// (x, y 16-byte aligned, n < 2^32). CH16: the 16 elements share a channel.
-template <bool U8, bool VEC, bool CH16>
+// VEC: a 256-thread block covers 4096 consecutive elements as four
+// 1024-element slices; in slice q thread t handles elements 4t .. 4t+3, so
+// every load instruction of a wave reads 1 KiB of fp32 contiguously and
+// every store writes 256 contiguous bytes (x 16-byte aligned, y 4-byte
+// aligned, n < 2^32). CH4: inner % 4 == 0, so four adjacent elements share
+// one channel.
+template <bool U8, bool VEC, bool CH4>
 __global__ void __launch_bounds__(256)
 k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
                   uint64_t cdim64, const float* __restrict__ scale,
                   const void* __restrict__ zp, uint8_t* __restrict__ y) {
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (VEC) {
-        const uint64_t e0 = t * 16;
-        if (e0 + 16 <= n) {
-            const dq::f4* xv = reinterpret_cast<const dq::f4*>(x + e0);
-            dq::f4 v[4];
+        const uint32_t base = blockIdx.x * 4096u + threadIdx.x * 4u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(xv + i);
-            const float* f = reinterpret_cast<const float*>(v);
-            uint32_t out[4];
-            if (CH16) {
-                const uint32_t c = channel_of((uint32_t)e0, am);
-                const float s = scale[c];
-                const int z = load_zp<U8>(zp, c);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t packed = 0;
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e0 = base + q * 1024u;
+            if ((uint64_t)e0 + 4 <= n) {
+                const dq::f4 v = __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(x + e0));
+                uint32_t packed = 0;
+                if (CH4) {
+                    const uint32_t c = channel_of(e0, am);
+                    const dq::QDiv d = dq::make_qdiv(scale[c]);
+                    const int z = load_zp<U8>(zp, c);
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
-                        packed |= ((uint32_t)quant1<U8>(f[4 * w + b], s, z) & 0xffu) << (8 * b);
-                    out[w] = packed;
-                }
-            } else {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t packed = 0;
+                        packed |= ((uint32_t)dq::sat_add(dq::rne(dq::qdiv(v[b], d)), z, U8 ? 0 : -128,
+                                                         U8 ? 255 : 127) & 0xffu) << (8 * b);
+                } else {
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const uint32_t c = channel_of((uint32_t)(e0 + 4 * w + b), am);
-                        packed |= ((uint32_t)quant1<U8>(f[4 * w + b], scale[c], load_zp<U8>(zp, c)) & 0xffu)
-                                  << (8 * b);
+                        const uint32_t c = channel_of(e0 + b, am);
+                        packed |= ((uint32_t)quant1<U8>(v[b], scale[c], load_zp<U8>(zp, c)) & 0xffu) << (8 * b);
                     }
-                    out[w] = packed;
                 }
-            }
-            const dq::u4 o = {out[0], out[1], out[2], out[3]};
-            __builtin_nontemporal_store(o, reinterpret_cast<dq::u4*>(y + e0));
-        } else {
-            for (uint64_t e = e0; e < n; ++e) {
-                const uint32_t c = channel_of((uint32_t)e, am);
-                y[e] = (uint8_t)quant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                *reinterpret_cast<uint32_t*>(y + e0) = packed;
+            } else {
+                for (uint64_t e = e0; e < n && e < (uint64_t)e0 + 4; ++e) {
+                    const uint32_t c = channel_of((uint32_t)e, am);
+                    y[e] = (uint8_t)quant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                }
             }
         }
     } else {
         // one element per thread, any alignment, any size
+        const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
         if (t < n) {
             const uint32_t c = am.per_axis ? channel_of64(t, inner64, cdim64) : 0;
             y[t] = (uint8_t)quant1<U8>(x[t], scale[c], load_zp<U8>(zp, c));
@@ -138,42 +132,45 @@ __device__ __forceinline__ float dequant1(uint32_t byte, float s, int zp) {
     return (float)(q - zp) * s;
 }
 
-template <bool U8, bool VEC, bool CH16>
+// VEC: the same 4096-element block split as quantize: in slice q thread t
+// reads the 4 codes 4t .. 4t+3 (256 contiguous bytes per wave) and writes
+// their 4 fp32 values (1 KiB contiguous per wave).
+template <bool U8, bool VEC, bool CH4>
 __global__ void __launch_bounds__(256)
 k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
                     uint64_t cdim64, const float* __restrict__ scale,
                     const void* __restrict__ zp, float* __restrict__ y) {
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (VEC) {
-        const uint64_t e0 = t * 16;
-        if (e0 + 16 <= n) {
-            const dq::u4 q = __builtin_nontemporal_load(reinterpret_cast<const dq::u4*>(x + e0));
-            const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-            dq::f4 out[4];
-            float* f = reinterpret_cast<float*>(out);
-            if (CH16) {
-                const uint32_t c = channel_of((uint32_t)e0, am);
-                const float s = scale[c];
-                const int z = load_zp<U8>(zp, c);
+        const uint32_t base = blockIdx.x * 4096u + threadIdx.x * 4u;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) f[i] = dequant1<U8>(qw[i >> 2] >> (8 * (i & 3)), s, z);
-            } else {
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e0 = base + q * 1024u;
+            if ((uint64_t)e0 + 4 <= n) {
+                const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(x + e0));
+                dq::f4 out;
+                if (CH4) {
+                    const uint32_t c = channel_of(e0, am);
+                    const float s = scale[c];
+                    const int z = load_zp<U8>(zp, c);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t c = channel_of((uint32_t)(e0 + i), am);
-                    f[i] = dequant1<U8>(qw[i >> 2] >> (8 * (i & 3)), scale[c], load_zp<U8>(zp, c));
+                    for (int b = 0; b < 4; ++b) out[b] = dequant1<U8>(w >> (8 * b), s, z);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t c = channel_of(e0 + b, am);
+                        out[b] = dequant1<U8>(w >> (8 * b), scale[c], load_zp<U8>(zp, c));
+                    }
                 }
-            }
-            dq::f4* yv = reinterpret_cast<dq::f4*>(y + e0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(out[i], yv + i);
-        } else {
-            for (uint64_t e = e0; e < n; ++e) {
-                const uint32_t c = channel_of((uint32_t)e, am);
-                y[e] = dequant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                *reinterpret_cast<dq::f4*>(y + e0) = out;
+            } else {
+                for (uint64_t e = e0; e < n && e < (uint64_t)e0 + 4; ++e) {
+                    const uint32_t c = channel_of((uint32_t)e, am);
+                    y[e] = dequant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                }
             }
         }
     } else {
+        const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
         if (t < n) {
             const uint32_t c = am.per_axis ? channel_of64(t, inner64, cdim64) : 0;
             y[t] = dequant1<U8>(x[t], scale[c], load_zp<U8>(zp, c));
@@ -224,16 +221,17 @@ AxisMap make_axis_map(const Plan& p, bool small) {
     return am;
 }
 
+// f32 side 16-byte aligned and 8-bit side 4-byte aligned for the vector
+// kernels; anything else takes the one-element-per-thread kernels.
 template <typename Launch>
-int dispatch(const Plan& p, const void* in, const void* out, Launch&& launch) {
-    const bool small = p.n < (UINT64_C(1) << 32) && p.inner < (UINT64_C(1) << 32) &&
+int dispatch(const Plan& p, const void* f32_side, const void* i8_side, Launch&& launch) {
+    const bool small = p.n < (UINT64_C(1) << 32) - 4096 && p.inner < (UINT64_C(1) << 32) &&
                        p.cdim < (UINT64_C(1) << 32);
-    const bool aligned = ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    const bool aligned = ((uintptr_t)f32_side % 16 == 0) && ((uintptr_t)i8_side % 4 == 0);
     const bool vec = small && aligned;
-    const bool ch16 = !p.per_axis || p.inner % 16 == 0;
+    const bool ch16 = !p.per_axis || p.inner % 4 == 0;
     const AxisMap am = make_axis_map(p, small);
-    const uint64_t threads = vec ? (p.n + 15) / 16 : p.n;
-    const uint64_t blocks = (threads + 255) / 256;
+    const uint64_t blocks = vec ? (p.n + 4095) / 4096 : (p.n + 255) / 256;
     if (blocks > 0x7fffffffull) DQ_FAIL(DQ_ERR_ARG, "tensor too large");
     launch(vec, ch16, am, (unsigned)blocks);
     return DQ_OK;
@@ -285,7 +283,7 @@ extern "C" int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim, cons
     if (!x || !y || !x_scale) DQ_FAIL(DQ_ERR_ARG, "x, y and x_scale must not be NULL");
     hipStream_t s = (hipStream_t)stream;
     const bool u8 = x_type == DQ_U8;
-    rc = dispatch(p, x, y, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
+    rc = dispatch(p, y, x, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
 #define DQ_DQL(U, V, C)                                                                       \
     hipLaunchKernelGGL((k_dequantize_linear<U, V, C>), dim3(blocks), dim3(256), 0, s,          \
                        (const uint8_t*)x, p.n, am, p.inner, p.cdim, x_scale, x_zero_point, y)

@@ -10,9 +10,9 @@
 // (qmin, qmax) = (-128, 127), or (-64, 63) with avoidOverflow, scale 1 for an
 // all-zero column.
 //
-// Output layout (the packed MFMA operand): iBt [N][Kp], i.e. B transposed so
-// that each column's K codes are contiguous, K zero-padded to Kp, and
-// colsum[j] = sum_k iB[k,j] (ReduceSumInteger over axis 0).
+// Output layout: iBp, B transposed (column j of B becomes packed row j) in
+// MFMA fragment order, K zero-padded to Kp, and colsum[j] = sum_k iB[k,j]
+// (ReduceSumInteger over axis 0).
 //
 // Kernels:
 //  - k_zero:        clears the column maxima and sums (fill kernel; no memset
@@ -22,8 +22,9 @@
 //                   merged with an integer atomicMax on the fp32 bit pattern
 //                   (monotone for values >= 0).
 //  - k_pack_cols:   64x64 tiles: coalesced loads, quantize, transpose through
-//                   LDS, 16-byte row stores of iBt, and the column sums from
-//                   the transposed tile (integer atomics: exact, any order).
+//                   LDS, 16-byte stores of four whole packed fragments, and
+//                   the column sums from the transposed tile (integer
+//                   atomics: exact in any order).
 #include "dq_device.h"
 #include "dq_kernels.h"
 
@@ -85,7 +86,7 @@ k_col_absmax(const void* __restrict__ B, int K, int N, int kchunk, uint32_t* __r
 template <int IN>
 __global__ void __launch_bounds__(256)
 k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax,
-            const uint32_t* __restrict__ amax, int8_t* __restrict__ iBt,
+            const uint32_t* __restrict__ amax, int8_t* __restrict__ iBp,
             float* __restrict__ scaleB, int32_t* __restrict__ colsum) {
     __shared__ float s_scale[kT];
     __shared__ __attribute__((aligned(16))) uint8_t tile[kT * kTS];  // [n][k]
@@ -129,7 +130,10 @@ k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax
         }
     }
     __syncthreads();
-    // write iBt rows: thread -> column n = tid / 4, 16 codes at (tid % 4) * 16
+    // write the tile's four packed fragments (4 KiB, every 128-byte line
+    // whole): thread -> column nn = tid / 4 of the tile, 16 codes of k-group
+    // part = tid % 4, i.e. fragment (n / 32, (k0 + 16 part) / 32), lane slot
+    // (n % 32) + 32 * (part % 2)
     const int nn = tid / 4;
     const int part = tid % 4;
     const uint8_t* src = tile + nn * kTS + part * 16;
@@ -146,23 +150,23 @@ k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax
     const int n = n0 + nn;
     if (n < N) {
         const dq::u4 o = {w0, w1, w2, w3};
-        *reinterpret_cast<dq::u4*>(iBt + (size_t)n * Kp + k0 + part * 16) = o;
+        *reinterpret_cast<dq::u4*>(iBp + dq::frag_offset((size_t)n, (size_t)(k0 + part * 16), (size_t)(Kp / 32))) = o;
         if (part == 0 && sum != 0) atomicAdd(&colsum[n], sum);
     }
 }
 
 __global__ void __launch_bounds__(256)
-k_unpack_b(const int8_t* __restrict__ iBt, int K, int N, int Kp, int8_t* __restrict__ iB) {
+k_unpack_b(const int8_t* __restrict__ iBp, int K, int N, int Kp, int8_t* __restrict__ iB) {
     const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= (size_t)K * N) return;
     const size_t k = t / N, j = t % N;
-    iB[t] = iBt[j * Kp + k];
+    iB[t] = iBp[dq::frag_offset(j, k, (size_t)(Kp / 32))];
 }
 
 }  // namespace
 
 int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, int avoid,
-                         int8_t* iBt, float* scaleB, int32_t* colsum, uint32_t* amax,
+                         int8_t* iBp, float* scaleB, int32_t* colsum, uint32_t* amax,
                          hipStream_t s) {
     const int qmax = avoid ? 63 : 127;
     const int qmin = avoid ? -64 : -128;
@@ -172,7 +176,7 @@ int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, in
     DQ_LAUNCH_CHECK("zero");
     if (typeB == DQ_I8) {
         hipLaunchKernelGGL((k_pack_cols<2>), pgrid, dim3(256), 0, s, B, K, N, Kp, qmin, qmax,
-                           amax, iBt, scaleB, colsum);
+                           amax, iBp, scaleB, colsum);
         DQ_LAUNCH_CHECK("pack_cols");
         return DQ_OK;
     }
@@ -195,17 +199,18 @@ int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, in
     DQ_LAUNCH_CHECK("col_absmax");
     if (bf16)
         hipLaunchKernelGGL((k_pack_cols<1>), pgrid, dim3(256), 0, s, B, K, N, Kp, qmin, qmax, amax,
-                           iBt, scaleB, colsum);
+                           iBp, scaleB, colsum);
     else
         hipLaunchKernelGGL((k_pack_cols<0>), pgrid, dim3(256), 0, s, B, K, N, Kp, qmin, qmax, amax,
-                           iBt, scaleB, colsum);
+                           iBp, scaleB, colsum);
     DQ_LAUNCH_CHECK("pack_cols");
     return DQ_OK;
 }
 
-int dq_launch_unpack_b(const int8_t* iBt, int K, int N, int Kp, int8_t* iB, hipStream_t s) {
+int dq_launch_unpack_b(const int8_t* iBp, int K, int N, int Kp, int8_t* iB, hipStream_t s) {
     const size_t n = (size_t)K * N;
-    hipLaunchKernelGGL(k_unpack_b, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, iBt, K, N,
+    if ((n + 255) / 256 > 0x7fffffffu) DQ_FAIL(DQ_ERR_ARG, "tensor too large to unpack");
+    hipLaunchKernelGGL(k_unpack_b, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, iBp, K, N,
                        Kp, iB);
     DQ_LAUNCH_CHECK("unpack_b");
     return DQ_OK;

@@ -7,47 +7,75 @@
 //   lo = min(0, min_k A), hi = max(0, max_k A),
 //   scaleA = (hi - lo) / 255, zeroA = sat[0,255](rne(-lo / scaleA)),
 //   uA = sat[0,255](rne(A / scaleA) + zeroA),
-// with scale 1 and zero point 0 for an all-zero row. The quotient is the
-// IEEE fp32 one and rne is half to even, as QuantizeLinear (onnxruntime
+// with scale 1 and zero point 0 for an all-zero row. The quotient rounds as
+// the IEEE fp32 one, and rne is half to even, as QuantizeLinear (onnxruntime
 // quantization_defs.cc) states for its own quotient.
 //
-// Output: sA = uA - 128 as int8 (the int8 MFMA is signed x signed); the
-// GEMM adds (128 - zeroA) * colsum(iB) back, which is exact in int32.
+// Output: sA = uA - 128 as int8 (the int8 MFMA is signed x signed), packed in
+// MFMA fragment order; the GEMM adds (128 - zeroA) * colsum(iB) back, which
+// is exact in int32.
 //
-// Design: one 64-lane wave per row, four rows per 256-thread workgroup. A
-// row of up to 8 Ki fp32 / 16 Ki bf16 values is read once with coalesced
-// 16-byte loads and kept in VGPRs between the min/max reduction (xor
-// shuffles, no LDS, no barrier) and the quantization, so A crosses HBM once.
-// Longer or misaligned rows take a two-pass lane-strided kernel whose second
-// pass hits L2.
+// Design: one 64-lane wave per row, eight consecutive rows per 512-thread
+// workgroup, so every 128-byte line of the packed output (eight rows x 16
+// codes) is written whole by one workgroup. Lane l owns
+// groups of 16 consecutive k (group g = l + 64 v); a row of up to 8 Ki values
+// is read once with 16-byte loads and kept in VGPRs between the min/max
+// reduction (xor shuffles, no LDS, no barrier) and the quantization, so A
+// crosses HBM once and sA is written once, 16 bytes per lane. Longer rows
+// take the streaming variant, whose second pass re-reads the row from L2.
 #include "dq_device.h"
 #include "dq_kernels.h"
 
 namespace {
 
-template <bool BF16>
-__device__ __forceinline__ void minmax_vec(const dq::u4& v, float& lo, float& hi) {
-    if (BF16) {
+constexpr int kRowsPerWave = 1;
+constexpr int kWavesPerBlock = 8;
+constexpr int kRowsPerBlock = kWavesPerBlock * kRowsPerWave;
+constexpr int kThreads = 64 * kWavesPerBlock;
+
+// 16 consecutive values of a row as fp32 (bf16 widened), from k0.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load16(const void* __restrict__ A, size_t row_base, int k0, int K,
+                                       float (&x)[16]) {
+    if (VEC) {
+        if (BF16) {
+            const dq::u4* p = reinterpret_cast<const dq::u4*>(
+                reinterpret_cast<const uint16_t*>(A) + row_base + k0);
+            const dq::u4 a = __builtin_nontemporal_load(p);
+            const dq::u4 b = __builtin_nontemporal_load(p + 1);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float a0 = dq::bf16_bits_to_f32(v[w] & 0xffffu);
-            const float a1 = dq::bf16_bits_to_f32(v[w] >> 16);
-            lo = __builtin_fminf(lo, __builtin_fminf(a0, a1));
-            hi = __builtin_fmaxf(hi, __builtin_fmaxf(a0, a1));
+            for (int w = 0; w < 4; ++w) {
+                x[2 * w] = dq::bf16_bits_to_f32(a[w] & 0xffffu);
+                x[2 * w + 1] = dq::bf16_bits_to_f32(a[w] >> 16);
+                x[8 + 2 * w] = dq::bf16_bits_to_f32(b[w] & 0xffffu);
+                x[8 + 2 * w + 1] = dq::bf16_bits_to_f32(b[w] >> 16);
+            }
+        } else {
+            const dq::f4* p = reinterpret_cast<const dq::f4*>(
+                reinterpret_cast<const float*>(A) + row_base + k0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const dq::f4 v = __builtin_nontemporal_load(p + q);
+                x[4 * q] = v[0];
+                x[4 * q + 1] = v[1];
+                x[4 * q + 2] = v[2];
+                x[4 * q + 3] = v[3];
+            }
         }
     } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float a = __uint_as_float(v[w]);
-            lo = __builtin_fminf(lo, a);
-            hi = __builtin_fmaxf(hi, a);
+        for (int e = 0; e < 16; ++e) {
+            const int k = k0 + e;
+            float v = 0.0f;  // past the row end: 0 is inside [lo, hi] already
+            if (k < K) {
+                if (BF16)
+                    v = dq::bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(A)[row_base + k]);
+                else
+                    v = reinterpret_cast<const float*>(A)[row_base + k];
+            }
+            x[e] = v;
         }
     }
-}
-
-__device__ __forceinline__ uint32_t code(float a, float scale, int zero) {
-    // uA - 128 as a byte: sat(rne(a/s) + zero) in [0,255], top bit flipped
-    return (uint32_t)dq::sat_add(dq::rne(a / scale), zero, 0, 255) ^ 0x80u;
 }
 
 __device__ __forceinline__ void row_params(float lo, float hi, float& scale, int& zero) {
@@ -60,128 +88,163 @@ __device__ __forceinline__ void row_params(float lo, float hi, float& scale, int
     }
 }
 
-// NV 16-byte vectors per lane; requires K % (16 / sizeof(elem)) == 0, a
-// 16-byte aligned A and K <= 64 * NV * elems_per_vector.
-template <bool BF16, int NV>
-__global__ void __launch_bounds__(256)
-k_quant_rows(const void* __restrict__ A, int M, int K, int Kp, int8_t* __restrict__ sA,
-             float* __restrict__ scaleA, int32_t* __restrict__ zeroA) {
-    constexpr int EPV = BF16 ? 8 : 4;
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const int nvec = K / EPV;
-    const dq::u4* src = reinterpret_cast<const dq::u4*>(
-        reinterpret_cast<const char*>(A) + (size_t)row * (size_t)K * (BF16 ? 2 : 4));
-    dq::u4 v[NV];
-    float lo = 0.0f, hi = 0.0f;
+// 16 codes uA - 128 of one group, stored as one 16-byte vector. FAST: the
+// row's scale has a normal reciprocal, and |A / scale| <= 256 holds by the
+// scale's construction, so the bounded residual division applies.
+// sA = sat[0,255](rne(q) + zero) - 128 = (int)clamp(rne(q), -zero, 255 - zero)
+// + (zero - 128), taken as a byte.
+template <bool FAST>
+__device__ __forceinline__ void store_group(int8_t* __restrict__ sA, size_t row, int g, int KF,
+                                            const float (&x)[16], const dq::QDiv& d, int zero) {
+    const float lo = (float)(-zero), hi = (float)(255 - zero);
+    const int shift = zero - 128;
+    uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int vi = i * 64 + lane;
-        if (vi < nvec) {
-            v[i] = __builtin_nontemporal_load(src + vi);
-            minmax_vec<BF16>(v[i], lo, hi);
+    for (int q = 0; q < 4; ++q) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float qt = FAST ? dq::qdiv_fast(x[4 * q + b], d) : x[4 * q + b] / d.s;
+            const float r = __builtin_fminf(__builtin_fmaxf(dq::rne(qt), lo), hi);
+            packed |= ((uint32_t)((int)r + shift) & 0xffu) << (8 * b);
         }
+        w[q] = packed;
     }
-    lo = dq::wave_min(lo);
-    hi = dq::wave_max(hi);
-    float scale;
-    int zero;
-    row_params(lo, hi, scale, zero);
-    int8_t* dst = sA + (size_t)row * Kp;
+    const dq::u4 o = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<dq::u4*>(sA + dq::frag_offset(row, (size_t)g * 16, KF)) = o;
+}
+
+// Row statistics are identical in every lane after the reductions; reading
+// them from lane 0 makes scale, zero point and the division path scalar
+// (wave-uniform), so the row takes one branch instead of one per element.
+__device__ __forceinline__ void uniform_minmax(float& lo, float& hi) {
+    lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dq::wave_min(lo))));
+    hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dq::wave_max(hi))));
+}
+
+// Row cached in VGPRs: NV groups of 16 per lane (K <= 1024 * NV).
+// VEC: K % 16 == 0 and a 16-byte aligned A (every group is a full vector).
+template <bool BF16, bool VEC, int NV>
+__global__ void __launch_bounds__(kThreads)
+k_quant_rows(const void* __restrict__ A, int M, int K, int KF, int8_t* __restrict__ sA,
+             float* __restrict__ scaleA, int32_t* __restrict__ zeroA) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ngroups = (K + 15) >> 4;
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+        const int row = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave + rr;
+        if (row >= M) return;
+        const size_t base = (size_t)row * (size_t)K;
+        float x[NV][16];
+        float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int vi = i * 64 + lane;
-        if (vi < nvec) {
-            if (BF16) {
-                uint32_t w[2] = {0, 0};
+        for (int v = 0; v < NV; ++v) {
+            const int g = lane + 64 * v;
+            if (g < ngroups) {
+                load16<BF16, VEC>(A, base, g * 16, K, x[v]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t bits = (v[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    w[e >> 2] |= code(dq::bf16_bits_to_f32(bits), scale, zero) << (8 * (e & 3));
+                for (int e = 0; e < 16; ++e) {
+                    lo = __builtin_fminf(lo, x[v][e]);
+                    hi = __builtin_fmaxf(hi, x[v][e]);
                 }
-                const dq::u2 o = {w[0], w[1]};
-                *reinterpret_cast<dq::u2*>(dst + (size_t)vi * 8) = o;
-            } else {
-                uint32_t w = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w |= code(__uint_as_float(v[i][e]), scale, zero) << (8 * e);
-                *reinterpret_cast<uint32_t*>(dst + (size_t)vi * 4) = w;
             }
         }
-    }
-    if (lane == 0) {
-        scaleA[row] = scale;
-        zeroA[row] = zero;
+        uniform_minmax(lo, hi);
+        float scale;
+        int zero;
+        row_params(lo, hi, scale, zero);
+        const dq::QDiv d = dq::make_qdiv(scale);
+        if (d.fast) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int g = lane + 64 * v;
+                if (g < ngroups) store_group<true>(sA, row, g, KF, x[v], d, zero);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int g = lane + 64 * v;
+                if (g < ngroups) store_group<false>(sA, row, g, KF, x[v], d, zero);
+            }
+        }
+        if (lane == 0) {
+            scaleA[row] = scale;
+            zeroA[row] = zero;
+        }
     }
 }
 
-// Any K, any alignment: two lane-strided passes over the row.
-template <bool BF16>
-__global__ void __launch_bounds__(256)
-k_quant_rows_generic(const void* __restrict__ A, int M, int K, int Kp, int8_t* __restrict__ sA,
-                     float* __restrict__ scaleA, int32_t* __restrict__ zeroA) {
+// Any K: min/max pass, then a second pass that re-reads each group.
+template <bool BF16, bool VEC>
+__global__ void __launch_bounds__(kThreads)
+k_quant_rows_stream(const void* __restrict__ A, int M, int K, int KF, int8_t* __restrict__ sA,
+                    float* __restrict__ scaleA, int32_t* __restrict__ zeroA) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const size_t base = (size_t)row * (size_t)K;
-    auto load = [&](int k) -> float {
-        if (BF16) return dq::bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(A)[base + k]);
-        return reinterpret_cast<const float*>(A)[base + k];
-    };
-    float lo = 0.0f, hi = 0.0f;
-    for (int k = lane; k < K; k += 64) {
-        const float a = load(k);
-        lo = __builtin_fminf(lo, a);
-        hi = __builtin_fmaxf(hi, a);
+    const int wave = threadIdx.x >> 6;
+    const int ngroups = (K + 15) >> 4;
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+        const int row = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave + rr;
+        if (row >= M) return;
+        const size_t base = (size_t)row * (size_t)K;
+        float lo = 0.0f, hi = 0.0f;
+        for (int g = lane; g < ngroups; g += 64) {
+            float x[16];
+            load16<BF16, VEC>(A, base, g * 16, K, x);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                lo = __builtin_fminf(lo, x[e]);
+                hi = __builtin_fmaxf(hi, x[e]);
+            }
+        }
+        uniform_minmax(lo, hi);
+        float scale;
+        int zero;
+        row_params(lo, hi, scale, zero);
+        const dq::QDiv d = dq::make_qdiv(scale);
+        for (int g = lane; g < ngroups; g += 64) {
+            float x[16];
+            load16<BF16, VEC>(A, base, g * 16, K, x);
+            if (d.fast) store_group<true>(sA, row, g, KF, x, d, zero);
+            else store_group<false>(sA, row, g, KF, x, d, zero);
+        }
+        if (lane == 0) {
+            scaleA[row] = scale;
+            zeroA[row] = zero;
+        }
     }
-    lo = dq::wave_min(lo);
-    hi = dq::wave_max(hi);
-    float scale;
-    int zero;
-    row_params(lo, hi, scale, zero);
-    int8_t* dst = sA + (size_t)row * Kp;
-    for (int k = lane; k < K; k += 64) dst[k] = (int8_t)code(load(k), scale, zero);
-    if (lane == 0) {
-        scaleA[row] = scale;
-        zeroA[row] = zero;
-    }
+}
+
+template <bool BF16, bool VEC>
+void launch_rows(dim3 grid, hipStream_t s, const void* A, int M, int K, int KF, int8_t* sA,
+                 float* scaleA, int32_t* zeroA) {
+    const int ngroups = (K + 15) / 16;
+    const int nv = (ngroups + 63) / 64;
+    if (nv <= 1)
+        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 1>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+    else if (nv <= 2)
+        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 2>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+    else if (nv <= 4)
+        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 4>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+    else if (nv <= 8)
+        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 8>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+    else
+        hipLaunchKernelGGL((k_quant_rows_stream<BF16, VEC>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
 }
 
 }  // namespace
 
 int dq_launch_quant_rows(const void* A, bool bf16, int M, int K, int Kp, int8_t* sA,
                          float* scaleA, int32_t* zeroA, hipStream_t s) {
-    const int epv = bf16 ? 8 : 4;
-    const bool vec_ok = K % epv == 0 && (uintptr_t)A % 16 == 0;
-    const int nvec = K / epv;
-    const int nv = (nvec + 63) / 64;  // vectors per lane
-    const dim3 grid((unsigned)((M + 3) / 4)), block(256);
-#define DQ_QR(B, NV)                                                                        \
-    hipLaunchKernelGGL((k_quant_rows<B, NV>), grid, block, 0, s, A, M, K, Kp, sA, scaleA, \
-                       zeroA)
-#define DQ_QR_SWITCH(B)                   \
-    if (nv <= 1) DQ_QR(B, 1);             \
-    else if (nv <= 2) DQ_QR(B, 2);        \
-    else if (nv <= 4) DQ_QR(B, 4);        \
-    else if (nv <= 8) DQ_QR(B, 8);        \
-    else if (nv <= 16) DQ_QR(B, 16);      \
-    else DQ_QR(B, 32);
-    if (vec_ok && nv <= 32) {
-        if (bf16) {
-            DQ_QR_SWITCH(true)
-        } else {
-            DQ_QR_SWITCH(false)
-        }
-    } else if (bf16) {
-        hipLaunchKernelGGL((k_quant_rows_generic<true>), grid, block, 0, s, A, M, K, Kp, sA,
-                           scaleA, zeroA);
+    const bool vec = K % 16 == 0 && (uintptr_t)A % 16 == 0;
+    const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+    const int KF = Kp / 32;
+    if (bf16) {
+        if (vec) launch_rows<true, true>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
+        else launch_rows<true, false>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
     } else {
-        hipLaunchKernelGGL((k_quant_rows_generic<false>), grid, block, 0, s, A, M, K, Kp, sA,
-                           scaleA, zeroA);
+        if (vec) launch_rows<false, true>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
+        else launch_rows<false, false>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
     }
-#undef DQ_QR_SWITCH
-#undef DQ_QR
     DQ_LAUNCH_CHECK("quant_rows");
     return DQ_OK;
 }
@@ -190,18 +253,19 @@ int dq_launch_quant_rows(const void* A, bool bf16, int M, int K, int Kp, int8_t*
 
 namespace {
 __global__ void __launch_bounds__(256)
-k_unpack_a(const int8_t* __restrict__ sA, int M, int K, int Kp, uint8_t* __restrict__ uA) {
+k_unpack_a(const int8_t* __restrict__ sA, int M, int K, int KF, uint8_t* __restrict__ uA) {
     const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= (size_t)M * K) return;
     const size_t i = t / K, k = t % K;
-    uA[t] = (uint8_t)sA[i * Kp + k] ^ 0x80u;
+    uA[t] = (uint8_t)sA[dq::frag_offset(i, k, KF)] ^ 0x80u;
 }
 }  // namespace
 
 int dq_launch_unpack_a(const int8_t* sA, int M, int K, int Kp, uint8_t* uA, hipStream_t s) {
     const size_t n = (size_t)M * K;
+    if ((n + 255) / 256 > 0x7fffffffu) DQ_FAIL(DQ_ERR_ARG, "tensor too large to unpack");
     hipLaunchKernelGGL(k_unpack_a, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, sA, M, K,
-                       Kp, uA);
+                       Kp / 32, uA);
     DQ_LAUNCH_CHECK("unpack_a");
     return DQ_OK;
 }

@@ -154,10 +154,11 @@ def test_argument_errors_on_device(gpu):
 
 
 def test_extreme_sums_stay_exact(gpu):
-    """Every row spans [-x, +x] and B saturates: the int32 sums reach
-    255*128*K magnitudes at K = 16384 and must still be exact."""
+    """K at its maximum (65536), every code of A at 255 with zero point 0 and
+    B at -128 / 127: the int32 sums reach -255*128*65535 = -2,139,095,040 + ...
+    next to the int32 limit, and must still be exact."""
     log("dqip extreme sums")
-    M, N, K = 64, 64, 16384
+    M, N, K = 64, 64, 65536
     A = np.empty((M, K), np.float32)
     A[:, :] = 1.0
     A[:, 0] = -1e-30  # lo just below 0: zeroA = 0, every other code 255
@@ -167,7 +168,8 @@ def test_extreme_sums_stay_exact(gpu):
                 constB=True, bias=None, act="identity", alpha=0.01, avoid=False,
                 scaleB=np.full(N, 1e-3, np.float32))
     want = oracle.dqip_forward(case)
-    assert abs(int(want["acc"].min())) > 2 ** 29
+    assert int(want["acc"].min()) == -255 * 128 * (K - 1)
+    assert abs(int(want["acc"].min())) > 2 ** 30
     _compare(case, run_dqip(gpu, case), want)
 
 
