@@ -57,6 +57,10 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # resolve every symbol now: a kernel whose host stub the compiler dropped
+    # shows up here as an undefined symbol instead of at first use
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     return LIB
 

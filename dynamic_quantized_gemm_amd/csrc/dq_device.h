@@ -104,6 +104,48 @@ __host__ __device__ __forceinline__ size_t frag_offset(size_t r, size_t k, size_
     return (((r >> 5) * KF + (k >> 5)) << 10) + (((r & 31) + ((k & 16) << 1)) << 4) + (k & 15);
 }
 
+// s_waitcnt on the vector-memory counter alone: wait until at most N vector
+// memory operations of this wave are outstanding (encoding of the gfx9
+// family: vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt in
+// bits 6:4 and lgkmcnt in bits 11:8 left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): the wave's 64 lanes land as one contiguous
+// 1 KiB block at lds_block (wave-uniform), lane l at offset 16 l. A plain
+// __device__ function (not a lambda, which would also be compiled for the
+// host and invalidate the kernel there).
+__device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_block) {
+    __builtin_amdgcn_global_load_lds(gsrc, lds_block, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence: no wait on outstanding vector
+// memory operations (the caller has waited for what it needs). The empty
+// asm statements with a memory clobber keep the compiler from moving memory
+// accesses across it; the scheduling barrier does the same for the
+// machine scheduler.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// Reads one accumulator register that an MFMA left in the accumulation
+// register file (AGPRs). Handing the value to an explicit read at its point
+// of use keeps the register allocator from copying every accumulator into
+// ordinary VGPRs at once when a large tile's main loop ends (which spills).
+__device__ __forceinline__ int32_t acc_read(int32_t a) {
+    int32_t v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
 // Wave-wide min / max over 64 lanes (butterfly over xor shuffles).
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll

@@ -8,12 +8,12 @@
 
 // Packed operands (MFMA fragment order, see frag_offset in dq_device.h):
 // sA [Mp x Kp] holds uA - 128, iBp [Np x Kp] holds iB transposed (column j
-// of B is packed row j). K is padded to Kp (multiple of 128) with zero codes
+// of B is packed row j). K is padded to Kp (multiple of 256) with zero codes
 // in iBp, so the padding adds nothing to a sum; M and N are padded to
 // multiples of 256 (the largest tile) and the padding rows / columns are
 // never stored to C. Per-column vectors (scaleB, colsum, bias) hold Np
 // entries so the epilogue can read them in 16-byte vectors.
-constexpr int kKpAlign = 128;
+constexpr int kKpAlign = 256;
 constexpr int kMNAlign = 256;
 
 inline size_t dq_kp(size_t K) { return (K + kKpAlign - 1) / kKpAlign * kKpAlign; }

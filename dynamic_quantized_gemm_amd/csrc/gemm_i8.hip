@@ -20,32 +20,39 @@
 // Operands arrive packed in MFMA fragment order (1 KiB = 32 rows x 32 k,
 // laid out exactly as v_mfma_i32_32x32x32_i8 takes them: lane l holds 16
 // codes of row l % 32), so
-//  - every global load is one 16-byte load per lane over a contiguous 1 KiB,
-//  - every LDS write and read is lane-contiguous (no bank conflicts, no
+//  - every global -> LDS copy moves one contiguous 1 KiB per wave, 16 bytes
+//    per lane, and lands in LDS in the same order,
+//  - every LDS read is lane-contiguous (ds_read_b128, no bank conflicts, no
 //    swizzle arithmetic),
-//  - no bounds checks are needed: M, N are padded to 256 and K to 128.
+//  - no bounds checks are needed: M, N are padded to 256 and K to 256.
 //
 // Kernel k_gemm<WM, WN, FM, FN, KS>: a workgroup of WM x WN waves computes a
 // (WM*FM*32) x (WN*FN*32) tile of C; each wave owns FM x FN 32x32 blocks
-// (16 int32 accumulators per lane per block). K advances 32*KS per step: the
-// step's fragments are staged global -> VGPR -> LDS into a double buffer
-// while the previous step is multiplied, one barrier per step. Within a
-// step the next step's global loads and the next sub-step's LDS reads are
-// interleaved one by one with the MFMAs (scheduling groups), so the vector
-// memory path, the LDS and the matrix cores work at the same time. The
-// largest configuration, 256x256x128 with four 128x128 waves (256
-// accumulator AGPRs per lane, 128 KiB of LDS), multiplies for 2048 MFMA
-// cycles per step.
+// (16 int32 accumulators per lane per block). K advances 32*KS = 64 per
+// step. The fragments of a step go global -> LDS directly (gfx950
+// global_load_lds_dwordx4, no trip through VGPRs) into a ring of four stage
+// buffers: while step t is multiplied out of its stage, the copies for steps
+// t+1 .. t+3 are in flight, so a copy has three steps of matrix work to
+// arrive. The compiler does not see these copies as LDS writes, so the
+// kernel waits for them itself (s_waitcnt vmcnt with the count of copies
+// still allowed in flight) and crosses one bare s_barrier per step. Within a
+// step the copies and the next sub-step's LDS reads are interleaved one by
+// one with the MFMAs (scheduling groups), so the vector memory path, the LDS
+// and the matrix cores work at the same time. The largest configuration,
+// 256x256 with four 128x128 waves, keeps 256 accumulator registers per lane
+// in AGPRs and multiplies for 1024 MFMA cycles per wave per step.
 //
 // The MFMA's first operand is the B fragment and its second the A fragment,
 // so the accumulator block is C^T: lane l holds row (l % 32) of the block and,
 // in accumulators 4g..4g+3, the four adjacent columns 8g + 4(l/32) + 0..3.
 // Epilogue: the tile's row and column parameters are staged in LDS when the
-// kernel starts; each wave finishes one 32-row strip at a time in
-// registers (activation and bias are template parameters: no per-element
-// branches), writes it to a wave-private, XOR-swizzled LDS strip and stores
-// it back as whole row segments, 16 bytes per lane, so the stores of one
-// strip overlap the arithmetic of the next.
+// kernel starts; after the main loop each wave owns one quarter of the stage
+// memory. Its rows are finished in passes of as many 32-row strips as fit
+// there: for each column group (loaded once per pass) the accumulators are
+// read one by one out of the AGPRs, corrected, scaled, biased and activated
+// in registers (activation and bias are template parameters: no per-element
+// branches) and written to an XOR-swizzled LDS image of the pass, which then
+// goes back to C as whole row segments, 16 bytes per lane.
 //
 // Tile order: consecutive workgroups land on different XCDs (round robin),
 // so the workgroup index is first regrouped per XCD, then rastered in
@@ -79,9 +86,18 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     constexpr int BM = BMF * 32, BN = BNF * 32;
     constexpr int AF = BMF * KS;        // A fragments per step
     constexpr int TF = AF + BNF * KS;   // all fragments per step
-    constexpr int FPW = (TF + NW - 1) / NW;
-    constexpr int FPK = (FPW + KS - 1) / KS;  // global loads per sub-step
-    __shared__ __attribute__((aligned(16))) int8_t lds[2][TF * 1024];
+    static_assert(TF % NW == 0, "every wave copies the same number of fragments");
+    constexpr int FPW = TF / NW;              // fragment copies per wave per step
+    constexpr int FPK = (FPW + KS - 1) / KS;  // fragment copies per sub-step
+    constexpr int NSTAGE = 4;                 // LDS ring: steps t .. t + 3
+    constexpr int SBYTES = TF * 1024;         // bytes per stage
+    // four separate arrays (not one indexed array): each gets its own alias
+    // scope, so the compiler can see that a step's LDS reads never touch
+    // the stage its in-flight copies write, and adds no waits for them
+    __shared__ __attribute__((aligned(16))) int8_t st0[SBYTES];
+    __shared__ __attribute__((aligned(16))) int8_t st1[SBYTES];
+    __shared__ __attribute__((aligned(16))) int8_t st2[SBYTES];
+    __shared__ __attribute__((aligned(16))) int8_t st3[SBYTES];
     __shared__ __attribute__((aligned(16))) int32_t s_cs[BN];
     __shared__ __attribute__((aligned(16))) float s_sb[BN];
     __shared__ __attribute__((aligned(16))) float s_bias[BN];
@@ -115,8 +131,7 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         const int g = f < AF ? f : f - AF;
         return base + ((size_t)(g / KS) * KF + (size_t)t * KS + g % KS) * 1024;
     };
-    constexpr bool kAllActive = TF % NW == 0;
-    auto active = [&](int i) { return i < FPW && (kAllActive || wave + i * NW < TF); };
+    const int nsteps = KF / KS;
 
     // row / column parameters of the tile (column vectors hold Np entries)
     for (int c = threadIdx.x; c < BN; c += NT) {
@@ -132,15 +147,40 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         if (OUT != DQ_OUT_ACC) s_sa[r] = ep.scaleA[row];
     }
 
-    dq::v4i stage[FPW];
+    // Fragment copies go straight from global memory to LDS
+    // (global_load_lds_dwordx4: a wave's 64 lanes x 16 bytes land as one
+    // contiguous 1 KiB block, exactly a packed fragment), without VGPRs.
+    // Step t lives in LDS stage t % 4; the copies of step t + 3 are issued
+    // while step t is multiplied. The compiler does not track these writes,
+    // so the waits are explicit: at the top of step t this wave waits until
+    // at most the copies of steps t + 1 and t + 2 are outstanding (vector
+    // memory operations complete in order), then the barrier makes every
+    // wave's copies of step t visible and certifies that stage (t - 1) % 4,
+    // the target of step t + 3, is no longer read. Steps past the end
+    // re-load the last step (in bounds, never read), which keeps the loop
+    // body free of conditional code.
+    auto stage = [&](auto S) -> int8_t* {
+        constexpr int k = decltype(S)::value % NSTAGE;
+        if constexpr (k == 0) return st0;
+        else if constexpr (k == 1) return st1;
+        else if constexpr (k == 2) return st2;
+        else return st3;
+    };
+    auto copy = [&](int i, int t, int8_t* dst) {
+        const int f = wave + i * NW;
+        const int tc = min(t, nsteps - 1);
+        dq::copy16_to_lds(frag_src(f, tc) + lofs, dst + f * 1024);
+    };
 #pragma unroll
-    for (int i = 0; i < FPW; ++i)
-        if (active(i)) stage[i] = *reinterpret_cast<const dq::v4i*>(frag_src(wave + i * NW, 0) + lofs);
+    for (int i = 0; i < FPW; ++i) copy(i, 0, st0);
 #pragma unroll
-    for (int i = 0; i < FPW; ++i)
-        if (active(i)) *reinterpret_cast<dq::v4i*>(&lds[0][(wave + i * NW) * 1024 + lofs]) = stage[i];
-    __syncthreads();
+    for (int i = 0; i < FPW; ++i) copy(i, 1, st1);
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) copy(i, 2, st2);
 
+    // a tile this large keeps its accumulators in AGPRs (16 registers per
+    // 32x32 block): read them one by one in the epilogue
+    constexpr bool kAgpr = FM * FN * 16 > 128;
     dq::v16i acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -149,11 +189,10 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // One step: the MFMAs of buffer L; when FETCH, the global loads of step
-    // `next` (FPK per sub-step) and, always, the LDS reads of sub-step kk+1
-    // are interleaved with the MFMAs of sub-step kk.
-    auto step = [&](const int8_t* L, auto fetch, int next) {
-        constexpr bool FETCH = decltype(fetch)::value;
+    // One step: the MFMAs of stage L, with the copies of step `ahead` and
+    // the LDS reads of sub-step kk + 1 interleaved one by one with the MFMAs
+    // of sub-step kk.
+    auto step = [&](const int8_t* L, int ahead, int8_t* dst) {
         dq::v4i fa[2][FM], fb[2][FN];
         auto read = [&](int kk, int set) {
 #pragma unroll
@@ -168,59 +207,72 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             const int set = kk & 1;
-            if (FETCH) {
 #pragma unroll
-                for (int q = 0; q < FPK; ++q) {
-                    const int i = kk * FPK + q;
-                    if (active(i)) stage[i] = *reinterpret_cast<const dq::v4i*>(frag_src(wave + i * NW, next) + lofs);
-                }
-            }
+            for (int q = 0; q < FPK; ++q)
+                if (kk * FPK + q < FPW) copy(kk * FPK + q, ahead, dst);
             if (kk + 1 < KS) read(kk + 1, set ^ 1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
-            // order: one MFMA, then one global load and one LDS read, ...
+            // order: one MFMA, then one copy and one LDS read, ...
 #pragma unroll
             for (int m = 0; m < FM * FN; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (FETCH && m < FPK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (m < FPK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 if (kk + 1 < KS && m < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // main loop; the last step is peeled so the loop body has no
-    // conditional code (a rolled condition here makes the compiler keep the
-    // accumulators in scratch)
-    const int nsteps = KF / KS;
-    for (int t = 0; t + 1 < nsteps; ++t) {
-        const int cur = t & 1;
-        step(lds[cur], std::true_type{}, t + 1);
-#pragma unroll
-        for (int i = 0; i < FPW; ++i)
-            if (active(i)) *reinterpret_cast<dq::v4i*>(&lds[cur ^ 1][(wave + i * NW) * 1024 + lofs]) = stage[i];
-        __syncthreads();
+    // unrolled by the ring size so every stage reference is static (the
+    // step count is a multiple of 4: Kp is a multiple of 256)
+    auto one = [&](auto S, int t) {
+        // not __syncthreads(): its fence would wait for every outstanding
+        // copy. This wave's copies of step t are done (explicit count) and
+        // its LDS reads of step t - 1 were consumed by that step's MFMAs;
+        // the bare barrier then publishes step t and frees stage t - 1.
+        dq::wait_vmcnt<2 * FPW>();
+        dq::lds_barrier();
+        step(stage(S), t + NSTAGE - 1, stage(std::integral_constant<int, decltype(S)::value + NSTAGE - 1>{}));
+    };
+    for (int t = 0; t < nsteps; t += NSTAGE) {
+        one(std::integral_constant<int, 0>{}, t);
+        one(std::integral_constant<int, 1>{}, t + 1);
+        one(std::integral_constant<int, 2>{}, t + 2);
+        one(std::integral_constant<int, 3>{}, t + 3);
     }
-    step(lds[(nsteps - 1) & 1], std::false_type{}, 0);
+    dq::wait_vmcnt<0>();  // the trailing copies land before LDS is reused
 
-    // ---- epilogue (see the header): wave-private strips of 32 rows
+    // ---- epilogue (see the header). The wave's output rows are cut into
+    // strips of 32 (one per A fragment row); as many strips as fit in the
+    // wave's private 1/4 of the stage memory are finished per pass. Column
+    // groups are the outer loop, so each group's column parameters are read
+    // from LDS once for all strips of the pass, and the strips give
+    // independent work to hide the reads' latency.
     constexpr int OB = OUT == DQ_OUT_BF16 ? 2 : 4;  // bytes per output
     constexpr int RB = FN * 32 * OB;                // bytes per strip row
     constexpr int CPR = RB / 16;                    // 16-byte chunks per strip row
     constexpr int EPC = 16 / OB;                    // elements per chunk
     constexpr int SB = 32 * RB;                     // bytes per strip
-    static_assert(NW * SB <= 2 * TF * 1024, "epilogue strips do not fit in LDS");
-    int8_t* strip = &lds[0][0] + wave * SB;
+    constexpr int SPP = (SBYTES / SB) < FM ? (SBYTES / SB) : FM;  // strips per pass
+    static_assert(SPP >= 1 && FM % SPP == 0 && NW <= NSTAGE, "epilogue strips do not fit in LDS");
+    int8_t* region = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
     __syncthreads();  // every wave is done reading the stage buffers
+    const int rs = lane & 31;  // row inside a strip
+    const int col0 = n0 + wn * FN * 32;
 #pragma clang loop unroll(full)
-    for (int i = 0; i < FM; ++i) {
-        const int rt = (wm * FM + i) * 32 + (lane & 31);  // tile row
-        const int rs = lane & 31;                        // strip row
-        const uint32_t za = (uint32_t)(128 - s_za[rt]);
-        const float sA = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
+    for (int p0 = 0; p0 < FM; p0 += SPP) {
+        uint32_t za[SPP];
+        float sA[SPP];
+#pragma unroll
+        for (int u = 0; u < SPP; ++u) {
+            const int rt = (wm * FM + p0 + u) * 32 + rs;  // tile row
+            za[u] = (uint32_t)(128 - s_za[rt]);
+            sA[u] = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
+        }
 #pragma clang loop unroll(full)
         for (int j = 0; j < FN; ++j) {
 #pragma clang loop unroll(full)
@@ -228,43 +280,51 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                 const int cs_ = j * 32 + 8 * g + 4 * (lane >> 5);  // strip column
                 const int ct = wn * FN * 32 + cs_;                  // tile column
                 const dq::v4i cs = *reinterpret_cast<const dq::v4i*>(&s_cs[ct]);
-                int32_t sum[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sum[e] = (int32_t)((uint32_t)acc[i][j][4 * g + e] + za * (uint32_t)cs[e]);
+                dq::f4 sB = {0.0f, 0.0f, 0.0f, 0.0f}, bv = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (OUT != DQ_OUT_ACC) sB = *reinterpret_cast<const dq::f4*>(&s_sb[ct]);
+                if (OUT != DQ_OUT_ACC && BIAS) bv = *reinterpret_cast<const dq::f4*>(&s_bias[ct]);
                 const int byte = cs_ * OB;
-                int8_t* dst = strip + rs * RB + (((byte >> 4) ^ (rs & (CPR - 1))) << 4) + (byte & 15);
-                if (OUT == DQ_OUT_ACC) {
-                    const dq::v4i v = {sum[0], sum[1], sum[2], sum[3]};
-                    *reinterpret_cast<dq::v4i*>(dst) = v;
-                } else {
-                    const dq::f4 sB = *reinterpret_cast<const dq::f4*>(&s_sb[ct]);
-                    dq::f4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
-                    if (BIAS) bv = *reinterpret_cast<const dq::f4*>(&s_bias[ct]);
-                    dq::f4 val;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float v = (float)sum[e] * sA;
-                        v = v * sB[e];
-                        if (BIAS) v = v + bv[e];
-                        val[e] = activate<ACT>(v, ep.alpha);
+                for (int u = 0; u < SPP; ++u) {
+                    int32_t sum[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sum[e] = (int32_t)((uint32_t)(kAgpr ? dq::acc_read(acc[p0 + u][j][4 * g + e])
+                                                             : acc[p0 + u][j][4 * g + e]) +
+                                           za[u] * (uint32_t)cs[e]);
+                    int8_t* dst = region + u * SB + rs * RB + (((byte >> 4) ^ (rs & (CPR - 1))) << 4) + (byte & 15);
+                    if (OUT == DQ_OUT_ACC) {
+                        const dq::v4i v = {sum[0], sum[1], sum[2], sum[3]};
+                        *reinterpret_cast<dq::v4i*>(dst) = v;
+                    } else {
+                        dq::f4 val;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float v = (float)sum[e] * sA[u];
+                            v = v * sB[e];
+                            if (BIAS) v = v + bv[e];
+                            val[e] = activate<ACT>(v, ep.alpha);
+                        }
+                        if (OUT == DQ_OUT_BF16)
+                            *reinterpret_cast<dq::u2*>(dst) = dq::f32x4_to_bf16x4(val);
+                        else
+                            *reinterpret_cast<dq::f4*>(dst) = val;
                     }
-                    if (OUT == DQ_OUT_BF16)
-                        *reinterpret_cast<dq::u2*>(dst) = dq::f32x4_to_bf16x4(val);
-                    else
-                        *reinterpret_cast<dq::f4*>(dst) = val;
                 }
+                // one column group at a time: keeps the accumulator reads and
+                // parameter loads of later groups from being hoisted here
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // the strip back as row segments: chunk q -> strip row q / CPR;
+        // the pass back as row segments: chunk q -> row q / CPR of the pass;
         // LDS operations of one wave complete in order, so no barrier
-        const int row0 = m0 + (wm * FM + i) * 32;
-        const int col0 = n0 + wn * FN * 32;
-#pragma unroll
-        for (int q = lane; q < 32 * CPR; q += 64) {
-            const int r = q / CPR, c = q % CPR;
+        const int row0 = m0 + (wm * FM + p0) * 32;
+#pragma unroll 4
+        for (int q = lane; q < SPP * 32 * CPR; q += 64) {
+            const int r = q / CPR, c = q % CPR;  // r: row of the pass
             const int row = row0 + r, col = col0 + c * EPC;
-            const dq::v4i v = *reinterpret_cast<const dq::v4i*>(strip + r * RB + ((c ^ (r & (CPR - 1))) << 4));
+            const dq::v4i v = *reinterpret_cast<const dq::v4i*>(region + (r >> 5) * SB + (r & 31) * RB +
+                                                                 ((c ^ (r & (CPR - 1))) << 4));
             if (row < M && col < N) {
                 int8_t* C = reinterpret_cast<int8_t*>(ep.C) + ((size_t)row * N + col) * OB;
                 if (vec_store && col + EPC <= N) {
@@ -309,6 +369,8 @@ void launch_act(dim3 grid, hipStream_t s, const int8_t* Ap, const int8_t* Bp, in
 template <int WM, int WN, int FM, int FN, int KS>
 int launch(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpilogue& ep,
            hipStream_t s) {
+    static_assert(KS == 2 && kKpAlign % 256 == 0,
+                  "the main loop needs a step count that is a multiple of 4: 64 per step, Kp % 256 == 0");
     constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const size_t tiles = (size_t)tiles_m * tiles_n;
@@ -348,16 +410,16 @@ int pick(int M, int N) {
 int dq_launch_gemm(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpilogue& ep,
                    hipStream_t s) {
     switch (pick(M, N)) {
-        case 2: return launch<2, 2, 4, 4, 4>(Ap, Bp, M, N, Kp, ep, s);
-        case 1: return launch<2, 2, 2, 2, 4>(Ap, Bp, M, N, Kp, ep, s);
-        default: return launch<1, 1, 1, 1, 4>(Ap, Bp, M, N, Kp, ep, s);
+        case 2: return launch<2, 2, 4, 4, 2>(Ap, Bp, M, N, Kp, ep, s);
+        case 1: return launch<2, 2, 2, 2, 2>(Ap, Bp, M, N, Kp, ep, s);
+        default: return launch<1, 1, 1, 1, 2>(Ap, Bp, M, N, Kp, ep, s);
     }
 }
 
 const char* dq_gemm_info(int M, int N, int) {
     switch (pick(M, N)) {
-        case 2: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 256x256x128 (4 waves x 128x128), fragment-packed operands, LDS double buffer, fused dequant epilogue";
-        case 1: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 128x128x128 (4 waves x 64x64), fragment-packed operands, LDS double buffer, fused dequant epilogue";
-        default: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 32x32x128 (1 wave), fragment-packed operands, fused dequant epilogue";
+        case 2: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 256x256, k-step 64 (4 waves x 128x128, accumulators in AGPRs), 4-stage global->LDS DMA ring, fused dequant epilogue";
+        case 1: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 128x128, k-step 64 (4 waves x 64x64), 4-stage global->LDS DMA ring, fused dequant epilogue";
+        default: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 32x32, k-step 64 (1 wave), 4-stage global->LDS DMA ring, fused dequant epilogue";
     }
 }
