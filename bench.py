@@ -106,20 +106,88 @@ class Dqip:
         self.dq.dqip_release(self.h)
 
 
-def traffic_record(kernel_file):
+GEMM_SOURCES = ("csrc/gemm_i8.hip", "csrc/dq_device.h", "csrc/dq_kernels.h")
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(ROOT, "dynamic_quantized_gemm_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_record(kernel):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/), kept
-    only while the kernel source is unchanged since the counters were taken."""
+    only while the kernel's sources are unchanged since the counters were
+    taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "dynamic_quantized_gemm_amd", "csrc", kernel_file)
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    entry = rec.get(kernel_file)
-    if not entry or entry.get("source_sha256") != sha:
+    entry = rec.get(kernel)
+    if not entry or entry.get("source_sha256") != source_digest(entry.get("sources", [])):
         return None
     return entry
+
+
+def _counter_means(csv_path, counter, match):
+    """Mean Counter_Value (KiB) per dispatch of the kernels whose name
+    contains `match`, from a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+
+    vals = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and match in row["Kernel_Name"]:
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{match}' in {csv_path}")
+    return list(vals.values())
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_match):
+    """profiles/traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE and
+    WRITE_SIZE of the GEMM (bench.py --quick) and of the plain 1 GiB copy
+    (bench.py --copy-calibration). Each GEMM counter is scaled by
+    copy bytes / what the same counter reads for the copy."""
+    n = 1 << 30
+    big = lambda v: [x for x in v if x * 1024 > n / 2]  # the 1 GiB copies only
+    cf = big(_counter_means(copy_fetch_csv, "FETCH_SIZE", "copyBuffer"))
+    cw = big(_counter_means(copy_write_csv, "WRITE_SIZE", "copyBuffer"))
+    f_scale = n / (1024 * sum(cf) / len(cf))
+    w_scale = n / (1024 * sum(cw) / len(cw))
+    gf = _counter_means(fetch_csv, "FETCH_SIZE", kernel_match)
+    gw = _counter_means(write_csv, "WRITE_SIZE", kernel_match)
+    fetch = 1024 * sum(gf) / len(gf) * f_scale
+    write = 1024 * sum(gw) / len(gw) * w_scale
+    rec = {"gemm_i8": {
+        "kernel": kernel_match, "dispatches": [len(gf), len(gw)],
+        "fetch_bytes": round(fetch), "write_bytes": round(write),
+        "bytes_per_launch": round(fetch + write),
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "copy_counter_kib": [round(sum(cf) / len(cf), 1), round(sum(cw) / len(cw), 1)],
+        "sources": list(GEMM_SOURCES), "source_sha256": source_digest(GEMM_SOURCES)}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["gemm_i8"]))
+
+
+def copy_calibration(torch, mib=1024, reps=10):
+    """A plain device-to-device copy of known size, for scaling the L2
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps, "read_bytes_per_copy": n,
+                      "write_bytes_per_copy": n}), flush=True)
 
 
 def bench_qdq(dq, torch, steps):
@@ -209,7 +277,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline only: no secondary configs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scales the HBM traffic counters)")
+    ap.add_argument("--write-traffic", nargs=4,
+                    metavar=("GEMM_FETCH_CSV", "GEMM_WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="no GPU: write profiles/traffic.json from rocprofv3 --pmc outputs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, kernel_match="k_gemm<2, 2, 4, 4, 2, 1, 1, true>")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path, so --gpus "
               f"{args.gpus} is not supported", file=sys.stderr)
@@ -221,8 +297,11 @@ def main():
     import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dq.load()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    dq.load()
 
     log("bench: generating the 4096^3 workload")
     case = W.dqip_large()
@@ -236,7 +315,7 @@ def main():
     achieved = d.ops / (gemm_ms / 1e3) / 1e12
     log(f"bench: {ms * 1e3:.1f} us/forward = {value:.1f} TOPS; gemm {gemm_ms * 1e3:.1f} us = "
         f"{achieved:.1f} TOPS; quant_a {phases[0] * 1e3:.1f} us")
-    tr = traffic_record("gemm_i8.hip")
+    tr = traffic_record("gemm_i8")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
                 "traffic": None if tr is None else tr["bytes_per_launch"],

@@ -19,10 +19,19 @@ constexpr int kMNAlign = 256;
 inline size_t dq_kp(size_t K) { return (K + kKpAlign - 1) / kKpAlign * kKpAlign; }
 inline size_t dq_mnp(size_t X) { return (X + kMNAlign - 1) / kMNAlign * kMNAlign; }
 
+// Optional timing of one launcher call: the first kernel it launches records
+// `start` when it begins and the last records `stop` when it ends (taken from
+// the dispatches themselves, hipExtLaunchKernel), so the elapsed time is the
+// kernels' own. NULL events: no timing.
+struct DqTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // Per-row dynamic quantization of A [M,K] (fp32 or bf16):
 // sA (packed, uA - 128), scaleA [M], zeroA [M].
 int dq_launch_quant_rows(const void* A, bool bf16, int M, int K, int Kp, int8_t* sA,
-                         float* scaleA, int32_t* zeroA, hipStream_t s);
+                         float* scaleA, int32_t* zeroA, hipStream_t s, DqTiming t = {});
 
 // B [K,N] -> iBp (packed, zero K padding), colsum [N], and for an fp32/bf16 B
 // also scaleB [N] (per-column symmetric quantization). For an int8 B the
@@ -30,7 +39,7 @@ int dq_launch_quant_rows(const void* A, bool bf16, int M, int K, int Kp, int8_t*
 // amax: N words of scratch (fp32 / bf16 B only).
 int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, int avoid,
                          int8_t* iBp, float* scaleB, int32_t* colsum, uint32_t* amax,
-                         hipStream_t s);
+                         hipStream_t s, DqTiming t = {});
 
 // Inspection: packed sA -> uA [M,K]; packed iBp -> iB [K,N].
 int dq_launch_unpack_a(const int8_t* sA, int M, int K, int Kp, uint8_t* uA, hipStream_t s);
@@ -52,7 +61,7 @@ struct DqEpilogue {
 
 // acc = sA * iB + (128 - zeroA[i]) * colsumB[j], then the epilogue.
 int dq_launch_gemm(const int8_t* sA, const int8_t* iBp, int M, int N, int Kp,
-                   const DqEpilogue& ep, hipStream_t s);
+                   const DqEpilogue& ep, hipStream_t s, DqTiming t = {});
 
 // A short description of the kernels dq_launch_gemm picks for a shape.
 const char* dq_gemm_info(int M, int N, int Kp);

@@ -58,8 +58,10 @@ struct dqip_ctx {
     size_t owned_bytes;
     WorkLayout lay;
     std::string info;
-    // per-phase timing: 4 events per recorded call (phase boundaries)
+    // per-phase timing: a start and a stop event per phase of each recorded
+    // call, and which phases of the call launched kernels
     std::vector<hipEvent_t> prof_events;
+    std::vector<uint8_t> prof_ran;
     int prof_capacity = 0;
     int prof_calls = 0;
 };
@@ -95,16 +97,26 @@ WorkLayout make_layout(size_t M, size_t N, size_t Kp, int constB) {
 void free_profile_events(dqip_ctx* c) {
     for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
     c->prof_events.clear();
+    c->prof_ran.clear();
     c->prof_capacity = 0;
     c->prof_calls = 0;
 }
 
-// Records phase boundary `b` (0..3) of the current call when profiling.
-int prof_mark(dqip_ctx* c, int b, hipStream_t s) {
-    if (c->prof_calls >= c->prof_capacity) return DQ_OK;
-    DQ_HIP_CHECK(hipEventRecord(c->prof_events[4 * c->prof_calls + b], s));
-    if (b == 3) ++c->prof_calls;
-    return DQ_OK;
+constexpr int kEventsPerCall = 2 * DQ_PHASES;
+
+// Timing events for phase `p` of the current call (none when not profiling
+// or when the capacity is used up); marks the phase as run.
+DqTiming prof_phase(dqip_ctx* c, int p) {
+    DqTiming t;
+    if (c->prof_calls >= c->prof_capacity) return t;
+    t.start = c->prof_events[(size_t)kEventsPerCall * c->prof_calls + 2 * p];
+    t.stop = c->prof_events[(size_t)kEventsPerCall * c->prof_calls + 2 * p + 1];
+    c->prof_ran[c->prof_calls] |= (uint8_t)(1u << p);
+    return t;
+}
+
+void prof_call_done(dqip_ctx* c) {
+    if (c->prof_calls < c->prof_capacity) ++c->prof_calls;
 }
 
 void free_ctx_memory(dqip_ctx* c) {
@@ -181,14 +193,14 @@ int run_forward(dqip_ctx* c, const void* A, const void* B, void* buf, void* out,
     uint8_t* w = nullptr;
     rc = resolve_work(c, buf, &w);
     if (rc) return rc;
+    if (c->prof_calls < c->prof_capacity) c->prof_ran[c->prof_calls] = 0;
     const int M = (int)c->M, N = (int)c->N, K = (int)c->K, Kp = (int)c->Kp;
     int8_t* sA = (int8_t*)(w + c->lay.sA);
     float* scaleA = (float*)(w + c->lay.scaleA);
     int32_t* zeroA = (int32_t*)(w + c->lay.zeroA);
-    if ((rc = prof_mark(c, 0, s))) return rc;
-    rc = dq_launch_quant_rows(A, c->typeA == DQ_BF16, M, K, Kp, sA, scaleA, zeroA, s);
+    rc = dq_launch_quant_rows(A, c->typeA == DQ_BF16, M, K, Kp, sA, scaleA, zeroA, s,
+                              prof_phase(c, DQ_PHASE_QUANT_A));
     if (rc) return rc;
-    if ((rc = prof_mark(c, 1, s))) return rc;
     const int8_t* iBt = c->iBt;
     const float* scaleB = c->scaleB;
     const int32_t* colsum = c->colsum;
@@ -197,13 +209,13 @@ int run_forward(dqip_ctx* c, const void* A, const void* B, void* buf, void* out,
         float* sB = (float*)(w + c->lay.scaleB);
         int32_t* cs = (int32_t*)(w + c->lay.colsum);
         uint32_t* am = (uint32_t*)(w + c->lay.amax);
-        rc = dq_launch_quant_cols(B, c->typeB, K, N, Kp, c->avoid, qB, sB, cs, am, s);
+        rc = dq_launch_quant_cols(B, c->typeB, K, N, Kp, c->avoid, qB, sB, cs, am, s,
+                                  prof_phase(c, DQ_PHASE_QUANT_B));
         if (rc) return rc;
         iBt = qB;
         scaleB = sB;
         colsum = cs;
     }
-    if ((rc = prof_mark(c, 2, s))) return rc;
     DqEpilogue ep;
     ep.scaleA = scaleA;
     ep.zeroA = zeroA;
@@ -214,9 +226,10 @@ int run_forward(dqip_ctx* c, const void* A, const void* B, void* buf, void* out,
     ep.alpha = c->alpha;
     ep.out = mode;
     ep.C = out;
-    rc = dq_launch_gemm(sA, iBt, M, N, Kp, ep, s);
+    rc = dq_launch_gemm(sA, iBt, M, N, Kp, ep, s, prof_phase(c, DQ_PHASE_GEMM));
     if (rc) return rc;
-    return prof_mark(c, 3, s);
+    prof_call_done(c);
+    return DQ_OK;
 }
 
 }  // namespace
@@ -359,7 +372,8 @@ extern "C" int dqip_profile_begin(dqip_ctx* c, int capacity) {
     if (!c) DQ_FAIL(DQ_ERR_STATE, "context is NULL");
     if (capacity < 1) DQ_FAIL(DQ_ERR_ARG, "capacity must be >= 1");
     free_profile_events(c);
-    c->prof_events.assign(4 * (size_t)capacity, nullptr);
+    c->prof_events.assign((size_t)kEventsPerCall * capacity, nullptr);
+    c->prof_ran.assign((size_t)capacity, 0);
     for (size_t i = 0; i < c->prof_events.size(); ++i) {
         hipError_t e = hipEventCreate(&c->prof_events[i]);
         if (e != hipSuccess) {
@@ -379,11 +393,13 @@ extern "C" int dqip_profile_end(dqip_ctx* c, float* ms, int* calls) {
     for (int p = 0; p < DQ_PHASES; ++p) ms[p] = 0.0f;
     const int n = c->prof_calls;
     for (int i = 0; i < n; ++i) {
-        hipEvent_t* ev = &c->prof_events[4 * (size_t)i];
-        hipError_t e = hipEventSynchronize(ev[3]);
+        const hipEvent_t* ev = &c->prof_events[(size_t)kEventsPerCall * i];
+        hipError_t e = hipSuccess;
         for (int p = 0; p < DQ_PHASES && e == hipSuccess; ++p) {
+            if (!(c->prof_ran[i] & (1u << p))) continue;  // no kernels in this phase
             float t = 0.0f;
-            e = hipEventElapsedTime(&t, ev[p], ev[p + 1]);
+            e = hipEventSynchronize(ev[2 * p + 1]);
+            if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[2 * p], ev[2 * p + 1]);
             ms[p] += t;
         }
         if (e != hipSuccess) {

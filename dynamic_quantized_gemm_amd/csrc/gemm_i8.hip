@@ -61,6 +61,8 @@
 #include "dq_device.h"
 #include "dq_kernels.h"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 namespace {
@@ -347,16 +349,16 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
 }
 
 template <int WM, int WN, int FM, int FN, int KS, int OUT, int ACT, bool BIAS>
-void launch_one(dim3 grid, hipStream_t s, const int8_t* Ap, const int8_t* Bp, int M, int N, int KF,
-                int tiles_m, int tiles_n, int vec_store, const DqEpilogue& ep) {
-    hipLaunchKernelGGL((k_gemm<WM, WN, FM, FN, KS, OUT, ACT, BIAS>), grid, dim3(WM * WN * 64), 0, s,
-                       Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+void launch_one(dim3 grid, hipStream_t s, DqTiming t, const int8_t* Ap, const int8_t* Bp, int M,
+                int N, int KF, int tiles_m, int tiles_n, int vec_store, const DqEpilogue& ep) {
+    hipExtLaunchKernelGGL((k_gemm<WM, WN, FM, FN, KS, OUT, ACT, BIAS>), grid, dim3(WM * WN * 64), 0,
+                          s, t.start, t.stop, 0, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
 }
 
 template <int WM, int WN, int FM, int FN, int KS, int OUT>
-void launch_act(dim3 grid, hipStream_t s, const int8_t* Ap, const int8_t* Bp, int M, int N, int KF,
+void launch_act(dim3 grid, hipStream_t s, DqTiming t, const int8_t* Ap, const int8_t* Bp, int M, int N, int KF,
                 int tiles_m, int tiles_n, int vec_store, const DqEpilogue& ep) {
-#define DQ_G(ACT, BIAS) launch_one<WM, WN, FM, FN, KS, OUT, ACT, BIAS>(grid, s, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep)
+#define DQ_G(ACT, BIAS) launch_one<WM, WN, FM, FN, KS, OUT, ACT, BIAS>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep)
     const bool bias = ep.bias != nullptr;
     switch (ep.act) {
         case DQ_ACT_RELU: if (bias) DQ_G(DQ_ACT_RELU, true); else DQ_G(DQ_ACT_RELU, false); break;
@@ -368,7 +370,7 @@ void launch_act(dim3 grid, hipStream_t s, const int8_t* Ap, const int8_t* Bp, in
 
 template <int WM, int WN, int FM, int FN, int KS>
 int launch(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpilogue& ep,
-           hipStream_t s) {
+           hipStream_t s, DqTiming t) {
     static_assert(KS == 2 && kKpAlign % 256 == 0,
                   "the main loop needs a step count that is a multiple of 4: 64 per step, Kp % 256 == 0");
     constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
@@ -382,13 +384,13 @@ int launch(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpi
     const int KF = Kp / 32;
     switch (ep.out) {
         case DQ_OUT_ACC:
-            launch_one<WM, WN, FM, FN, KS, DQ_OUT_ACC, DQ_ACT_IDENTITY, false>(grid, s, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+            launch_one<WM, WN, FM, FN, KS, DQ_OUT_ACC, DQ_ACT_IDENTITY, false>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
             break;
         case DQ_OUT_BF16:
-            launch_act<WM, WN, FM, FN, KS, DQ_OUT_BF16>(grid, s, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+            launch_act<WM, WN, FM, FN, KS, DQ_OUT_BF16>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
             break;
         default:
-            launch_act<WM, WN, FM, FN, KS, DQ_OUT_F32>(grid, s, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+            launch_act<WM, WN, FM, FN, KS, DQ_OUT_F32>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
             break;
     }
     DQ_LAUNCH_CHECK("gemm_i8");
@@ -408,11 +410,11 @@ int pick(int M, int N) {
 }  // namespace
 
 int dq_launch_gemm(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpilogue& ep,
-                   hipStream_t s) {
+                   hipStream_t s, DqTiming t) {
     switch (pick(M, N)) {
-        case 2: return launch<2, 2, 4, 4, 2>(Ap, Bp, M, N, Kp, ep, s);
-        case 1: return launch<2, 2, 2, 2, 2>(Ap, Bp, M, N, Kp, ep, s);
-        default: return launch<1, 1, 1, 1, 2>(Ap, Bp, M, N, Kp, ep, s);
+        case 2: return launch<2, 2, 4, 4, 2>(Ap, Bp, M, N, Kp, ep, s, t);
+        case 1: return launch<2, 2, 2, 2, 2>(Ap, Bp, M, N, Kp, ep, s, t);
+        default: return launch<1, 1, 1, 1, 2>(Ap, Bp, M, N, Kp, ep, s, t);
     }
 }
 

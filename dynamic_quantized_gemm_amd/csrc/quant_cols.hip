@@ -28,6 +28,8 @@
 #include "dq_device.h"
 #include "dq_kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace {
 
 constexpr int kT = 64;       // tile edge (k and n)
@@ -167,16 +169,16 @@ k_unpack_b(const int8_t* __restrict__ iBp, int K, int N, int Kp, int8_t* __restr
 
 int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, int avoid,
                          int8_t* iBp, float* scaleB, int32_t* colsum, uint32_t* amax,
-                         hipStream_t s) {
+                         hipStream_t s, DqTiming t) {
     const int qmax = avoid ? 63 : 127;
     const int qmin = avoid ? -64 : -128;
     const dim3 pgrid((unsigned)((N + kT - 1) / kT), (unsigned)(Kp / kT));
-    hipLaunchKernelGGL(k_zero, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, amax, N,
-                       colsum);
+    hipExtLaunchKernelGGL(k_zero, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, t.start,
+                          nullptr, 0, amax, N, colsum);
     DQ_LAUNCH_CHECK("zero");
     if (typeB == DQ_I8) {
-        hipLaunchKernelGGL((k_pack_cols<2>), pgrid, dim3(256), 0, s, B, K, N, Kp, qmin, qmax,
-                           amax, iBp, scaleB, colsum);
+        hipExtLaunchKernelGGL((k_pack_cols<2>), pgrid, dim3(256), 0, s, nullptr, t.stop, 0, B, K, N,
+                              Kp, qmin, qmax, amax, iBp, scaleB, colsum);
         DQ_LAUNCH_CHECK("pack_cols");
         return DQ_OK;
     }
@@ -198,11 +200,11 @@ int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, in
     }
     DQ_LAUNCH_CHECK("col_absmax");
     if (bf16)
-        hipLaunchKernelGGL((k_pack_cols<1>), pgrid, dim3(256), 0, s, B, K, N, Kp, qmin, qmax, amax,
-                           iBp, scaleB, colsum);
+        hipExtLaunchKernelGGL((k_pack_cols<1>), pgrid, dim3(256), 0, s, nullptr, t.stop, 0, B, K, N,
+                              Kp, qmin, qmax, amax, iBp, scaleB, colsum);
     else
-        hipLaunchKernelGGL((k_pack_cols<0>), pgrid, dim3(256), 0, s, B, K, N, Kp, qmin, qmax, amax,
-                           iBp, scaleB, colsum);
+        hipExtLaunchKernelGGL((k_pack_cols<0>), pgrid, dim3(256), 0, s, nullptr, t.stop, 0, B, K, N,
+                              Kp, qmin, qmax, amax, iBp, scaleB, colsum);
     DQ_LAUNCH_CHECK("pack_cols");
     return DQ_OK;
 }

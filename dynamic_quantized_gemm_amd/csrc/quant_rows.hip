@@ -26,6 +26,8 @@
 #include "dq_device.h"
 #include "dq_kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace {
 
 constexpr int kRowsPerWave = 1;
@@ -215,35 +217,35 @@ k_quant_rows_stream(const void* __restrict__ A, int M, int K, int KF, int8_t* __
 }
 
 template <bool BF16, bool VEC>
-void launch_rows(dim3 grid, hipStream_t s, const void* A, int M, int K, int KF, int8_t* sA,
-                 float* scaleA, int32_t* zeroA) {
+void launch_rows(dim3 grid, hipStream_t s, DqTiming t, const void* A, int M, int K, int KF,
+                 int8_t* sA, float* scaleA, int32_t* zeroA) {
     const int ngroups = (K + 15) / 16;
     const int nv = (ngroups + 63) / 64;
     if (nv <= 1)
-        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 1>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+        hipExtLaunchKernelGGL((k_quant_rows<BF16, VEC, 1>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
     else if (nv <= 2)
-        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 2>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+        hipExtLaunchKernelGGL((k_quant_rows<BF16, VEC, 2>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
     else if (nv <= 4)
-        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 4>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+        hipExtLaunchKernelGGL((k_quant_rows<BF16, VEC, 4>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
     else if (nv <= 8)
-        hipLaunchKernelGGL((k_quant_rows<BF16, VEC, 8>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+        hipExtLaunchKernelGGL((k_quant_rows<BF16, VEC, 8>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
     else
-        hipLaunchKernelGGL((k_quant_rows_stream<BF16, VEC>), grid, dim3(kThreads), 0, s, A, M, K, KF, sA, scaleA, zeroA);
+        hipExtLaunchKernelGGL((k_quant_rows_stream<BF16, VEC>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
 }
 
 }  // namespace
 
 int dq_launch_quant_rows(const void* A, bool bf16, int M, int K, int Kp, int8_t* sA,
-                         float* scaleA, int32_t* zeroA, hipStream_t s) {
+                         float* scaleA, int32_t* zeroA, hipStream_t s, DqTiming t) {
     const bool vec = K % 16 == 0 && (uintptr_t)A % 16 == 0;
     const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
     const int KF = Kp / 32;
     if (bf16) {
-        if (vec) launch_rows<true, true>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
-        else launch_rows<true, false>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
+        if (vec) launch_rows<true, true>(grid, s, t, A, M, K, KF, sA, scaleA, zeroA);
+        else launch_rows<true, false>(grid, s, t, A, M, K, KF, sA, scaleA, zeroA);
     } else {
-        if (vec) launch_rows<false, true>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
-        else launch_rows<false, false>(grid, s, A, M, K, KF, sA, scaleA, zeroA);
+        if (vec) launch_rows<false, true>(grid, s, t, A, M, K, KF, sA, scaleA, zeroA);
+        else launch_rows<false, false>(grid, s, t, A, M, K, KF, sA, scaleA, zeroA);
     }
     DQ_LAUNCH_CHECK("quant_rows");
     return DQ_OK;

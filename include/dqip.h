@@ -159,8 +159,11 @@ int dqip_forward_accumulators(dqip_ctx* ctx, const void* A, const void* B,
 enum { DQ_PHASE_QUANT_A = 0, DQ_PHASE_QUANT_B = 1, DQ_PHASE_GEMM = 2, DQ_PHASES = 3 };
 
 /* After dqip_profile_begin(ctx, capacity) each of the next `capacity`
- * dqip_forward / dqip_forward_accumulators calls records HIP events on its
- * stream around each phase's kernels (nothing else changes; no sync).
+ * dqip_forward / dqip_forward_accumulators calls has the first kernel of each
+ * phase record a start event and the last kernel a stop event, taken from the
+ * kernel dispatches themselves (hipExtLaunchKernel), so a phase's time is its
+ * kernels' execution time without launch gaps (nothing else changes; no
+ * sync).
  * dqip_profile_end waits for the recorded events and writes, per phase, the
  * summed milliseconds to ms[DQ_PHASES] (DQ_PHASE_QUANT_B stays 0 for a
  * constant B) and the number of recorded calls to *calls; it then stops
