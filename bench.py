@@ -190,6 +190,38 @@ def copy_calibration(torch, mib=1024, reps=10):
                       "write_bytes_per_copy": n}), flush=True)
 
 
+def time_cold_warm(fn, torch, steps, flush):
+    """(median ms per call with the Infinity Cache flushed before each call,
+    mean ms per call back to back); HIP events on torch's current stream,
+    which is the stream the library launches on."""
+    for _ in range(3):
+        fn()
+    cold = []
+    for i in range(steps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return float(np.median(cold)), e0.elapsed_time(e1) / steps
+
+
+def _bw_record(nbytes, cold_ms, warm_ms):
+    gb = nbytes / 1e9
+    return {"us_cold": round(cold_ms * 1e3, 2), "GBps_cold": round(gb / (cold_ms / 1e3), 1),
+            "frac_cold": round(gb / (cold_ms / 1e3) / HBM_PEAK_GBS, 3),
+            "us_warm": round(warm_ms * 1e3, 2), "GBps_warm": round(gb / (warm_ms / 1e3), 1)}
+
+
 def bench_qdq(dq, torch, steps):
     """QuantizeLinear and DequantizeLinear, per axis, [64,256,56,56] fp32 <->
     int8: GB/s of algorithmic bytes (4 + 1 per element), cold (Infinity
@@ -208,32 +240,39 @@ def bench_qdq(dq, torch, steps):
     d = lambda: dq.qlinear_dequantize(y, dq.DQ_I8, s, z, r, axis=1)  # noqa: E731
     out = {}
     for name, fn in (("quantize", q), ("dequantize", d)):
-        for _ in range(3):
-            fn()
-        cold = []
-        for i in range(steps):
-            flush.fill_(float(i))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            e1.synchronize()
-            cold.append(e0.elapsed_time(e1))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        e1.synchronize()
-        warm = e0.elapsed_time(e1) / steps
-        cold_ms = float(np.median(cold))
-        gb = 5.0 * n / 1e9
-        out[name] = {"us_cold": round(cold_ms * 1e3, 2), "GBps_cold": round(gb / (cold_ms / 1e3), 1),
-                     "frac_cold": round(gb / (cold_ms / 1e3) / HBM_PEAK_GBS, 3),
-                     "us_warm": round(warm * 1e3, 2), "GBps_warm": round(gb / (warm / 1e3), 1)}
+        out[name] = _bw_record(5 * n, *time_cold_warm(fn, torch, steps, flush))
     out["workload"] = "x fp32 [64,256,56,56] NCHW <-> int8, per-channel (axis 1) scale/zero point"
     out["bytes_per_call"] = 5 * n
+    del flush
+    return out
+
+
+def bench_qconv(dq, torch, steps):
+    """The requantizing 1x1 QLinearConv, uint8 x [8,256,56,56] (x_zp 128),
+    int8 w [256,256] per-channel scales, int32 bias, uint8 y: GB/s of
+    algorithmic bytes (x + w + y + parameters), cold and warm."""
+    import workloads as W
+
+    c = W.qconv1x1()
+    N, C, H, Wd = c["x"].shape
+    M = c["w"].shape[0]
+    x = dev_tensor(c["x"], torch)
+    w = dev_tensor(c["w"], torch)
+    xs = dev_tensor(np.array([c["x_scale"]], np.float32), torch)
+    ys = dev_tensor(np.array([c["y_scale"]], np.float32), torch)
+    xz = dev_tensor(np.array([c["x_zp"]], np.uint8), torch)
+    yz = dev_tensor(np.array([c["y_zp"]], np.uint8), torch)
+    ws = dev_tensor(c["w_scale"], torch)
+    b = dev_tensor(c["bias"], torch)
+    y = torch.empty((N, M, H, Wd), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    fn = lambda: dq.qlinear_conv1x1(x, dq.DQ_U8, xs, xz, w, dq.DQ_I8, ws, None, ys, yz,  # noqa: E731
+                                    dq.DQ_U8, b, y)
+    nbytes = N * C * H * Wd + N * M * H * Wd + M * C + 8 * M + 10
+    out = _bw_record(nbytes, *time_cold_warm(fn, torch, steps, flush))
+    out["TOPS_cold"] = round(2.0 * N * M * C * H * Wd / (out["us_cold"] * 1e-6) / 1e12, 1)
+    out["workload"] = c["name"]
+    out["bytes_per_call"] = nbytes
     del flush
     return out
 
@@ -331,6 +370,9 @@ def main():
         log("bench: QuantizeLinear / DequantizeLinear [64,256,56,56]")
         secondary["qdq"] = bench_qdq(dq, torch, steps2)
         log(f"bench: {secondary['qdq']}")
+        log("bench: QLinearConv 1x1 [8,256,56,56]")
+        secondary["qlinearconv_1x1"] = bench_qconv(dq, torch, steps2)
+        log(f"bench: {secondary['qlinearconv_1x1']}")
         for name, mk in (("dqip_64x64x128", W.dqip_small),
                          ("lstm_input_4096x2048x512", lambda: W.dqip_lstm(recurrent=False)),
                          ("lstm_recurrent_32x2048x512", lambda: W.dqip_lstm(recurrent=True)),

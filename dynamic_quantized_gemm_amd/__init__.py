@@ -13,5 +13,5 @@ from ._binding import (  # noqa: F401
     DQ_PER_TENSOR, DQ_U8, DQError, LIB_PATH, dqip_enabled, dqip_external_buffer_size,
     dqip_forward, dqip_forward_accumulators, dqip_info, dqip_init, dqip_internal_buffer_size,
     dqip_last_error, dqip_profile_begin, dqip_profile_end, dqip_read_quantized_a, dqip_read_quantized_b, dqip_release,
-    dqip_set_params, exported_symbols, load, qlinear_dequantize, qlinear_quantize,
+    dqip_set_params, exported_symbols, load, qlinear_conv1x1, qlinear_dequantize, qlinear_quantize,
 )

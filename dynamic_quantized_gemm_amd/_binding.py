@@ -41,6 +41,10 @@ _SIGNATURES = {
                                    C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
     "qlinear_dequantize": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "qlinear_conv1x1": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int64,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int64,
+                                  C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                  C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
 }
 
 
@@ -200,3 +204,24 @@ def qlinear_dequantize(x, x_type, x_scale, x_zero_point, y, axis=DQ_PER_TENSOR, 
                                      _ptr(x_zero_point), _ptr(y), _stream(stream)),
            "qlinear_dequantize")
     del keep
+
+
+def qlinear_conv1x1(x, x_type, x_scale, x_zero_point, w, w_type, w_scale, w_zero_point,
+                    y_scale, y_zero_point, y_type, bias, y, *, N=None, C_=None, HW=None, M=None,
+                    w_len=None, stream=None):
+    """x: [N, C, H, W] (or [N, C, HW]) 8-bit tensor; w: [M, C] (or [M, C, 1, 1]);
+    y: [N, M, H, W] 8-bit tensor (written). Scales / zero points / bias are
+    device tensors or None (zero points and bias); sizes default to the
+    tensors' shapes."""
+    if N is None:
+        N, C_ = int(x.shape[0]), int(x.shape[1])
+        HW = 1
+        for d in x.shape[2:]:
+            HW *= int(d)
+        M = int(w.shape[0])
+    if w_len is None:
+        w_len = int(w_scale.numel())
+    _check(load().qlinear_conv1x1(_ptr(x), x_type, N, C_, HW, _ptr(x_scale), _ptr(x_zero_point),
+                                  _ptr(w), w_type, M, _ptr(w_scale), _ptr(w_zero_point), w_len,
+                                  _ptr(y_scale), _ptr(y_zero_point), y_type, _ptr(bias), _ptr(y),
+                                  _stream(stream)), "qlinear_conv1x1")

@@ -1,0 +1,320 @@
+// qconv1x1.hip -- requantizing 1x1 QLinearConv on gfx950 matrix cores.
+//
+// ONNX "QLinearConv" (opset 10), description and inputs: x and w are 8-bit
+// tensors with scales and zero points (w per tensor or per output channel),
+// the optional bias is int32 with scale x_scale * w_scale and zero point 0,
+// and y is requantized with y_scale / y_zero_point. For a 1x1 kernel with
+// stride 1, no padding and one group, image n is a matrix product:
+//   acc[m,p] = sum_c (w[m,c] - w_zp[m]) * (x[n,c,p] - x_zp) + bias[m]
+//   real     = ((float)acc * x_scale) * w_scale[m]
+//   y[n,m,p] = saturate(rne(real / y_scale) + y_zp)
+// (requantization read as dequantize, then QuantizeLinear: IEEE quotient,
+// ties to even, saturation to the 8-bit range of y).
+//
+// The int8 MFMA multiplies signed by signed. With shifts a = 128 for a uint8
+// w (0 for int8) and b = 128 for a uint8 x (0 for int8), the operands
+// w^ = w - a and x^ = x - b are int8 and the sum splits exactly:
+//   acc = sum_c w^ x^ + (b - x_zp) * R[m] + (a - w_zp[m]) * S[p]
+//         + C * (a - w_zp[m]) * (b - x_zp) + bias[m]
+// with R[m] = sum_c w^[m,c] (from the weight fragments each lane holds) and
+// S[p] = sum_c x^[c,p] (one extra MFMA against an all-ones operand, only when
+// some a - w_zp[m] can be non-zero). The MFMA part is bounded by
+// C * 128 * 128 < 2^31 for C <= 32768, and the corrections are added in
+// wrapping 32-bit arithmetic, which yields acc exactly whenever acc fits in
+// int32.
+//
+// Kernel k_qconv1x1: a workgroup of 4 waves computes 256 output channels x 64
+// pixels of one image, each wave 64 channels x 64 pixels (2 x 2 blocks of
+// 32x32). Per chunk of 256 input channels, every lane keeps its weight
+// fragments in registers: w is [M, C] row-major, so a 32-channel run of one
+// output channel is already the k-contiguous MFMA operand and is loaded as
+// is. The image tile x[c, p] (pixels contiguous) is loaded with 4-byte loads
+// along pixels, transposed 4x4 bytes in registers and written to LDS in
+// fragment order (pixel rows, 16 channels per lane slot), from where each
+// wave reads its operands with ds_read_b128. Each lane's accumulators hold
+// one output channel (lane % 32) and, in accumulators 4g..4g+3, four
+// consecutive pixels, so the requantized codes pack into 32-bit words; they
+// are staged in LDS per wave and stored as 16-byte row segments.
+#include "dq_device.h"
+#include "dq_kernels.h"
+
+namespace {
+
+constexpr int kP = 64;        // pixels per tile
+constexpr int kMT = 256;      // output channels per tile (4 waves x 64)
+constexpr int kKC = 256;      // input channels per chunk
+constexpr int kYPitch = 80;   // LDS bytes per staged output row (64 + 16)
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int load_zp(const uint8_t* zp, size_t i, bool u8) {
+    if (!zp) return 0;
+    return u8 ? (int)zp[i] : (int)(int8_t)zp[i];
+}
+
+// Byte i of each of d0..d3, as one word (d0 in the low byte).
+__device__ __forceinline__ uint32_t gather_byte(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
+                                                int i) {
+    const int s = 8 * i;
+    return ((d0 >> s) & 0xffu) | (((d1 >> s) & 0xffu) << 8) | (((d2 >> s) & 0xffu) << 16) |
+           (((d3 >> s) & 0xffu) << 24);
+}
+
+// Four consecutive bytes x[row, p .. p+3] as a word; bytes at p >= HW read as
+// `pad`. VEC: HW % 4 == 0 and x 4-byte aligned, so the word is whole or out.
+template <bool VEC>
+__device__ __forceinline__ uint32_t load_x4(const uint8_t* row, int p, int HW, uint32_t pad) {
+    if (VEC) return p < HW ? *reinterpret_cast<const uint32_t*>(row + p) : pad;
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t b = p + e < HW ? (uint32_t)row[p + e] : ((pad >> (8 * e)) & 0xffu);
+        v |= b << (8 * e);
+    }
+    return v;
+}
+
+template <bool XU8, bool WU8, bool YU8, bool XSUM, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_qconv1x1(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int C, int HW, int M,
+    const float* __restrict__ x_scale_p, const uint8_t* __restrict__ x_zp_p,
+    const float* __restrict__ w_scale, const uint8_t* __restrict__ w_zp, int w_per_channel,
+    const float* __restrict__ y_scale_p, const uint8_t* __restrict__ y_zp_p,
+    const int32_t* __restrict__ bias, int wvec, uint8_t* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) int8_t xs[(kP / 32) * (kKC / 32) * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t ys[kMT * kYPitch];
+
+    constexpr uint32_t kXor = 0x80808080u;
+    constexpr int kA = WU8 ? 128 : 0;  // shift of w
+    constexpr int kB = XU8 ? 128 : 0;  // shift of x
+    // raw byte that becomes x^ = 0 after the shift (padding channels / pixels)
+    constexpr uint32_t kXPad = XU8 ? kXor : 0u;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p0 = blockIdx.x * kP;
+    const int mw0 = blockIdx.y * kMT + 64 * wave;  // first output channel of this wave
+    const size_t n = blockIdx.z;
+    const uint8_t* xn = x + n * (size_t)C * HW;
+
+    typedef dq::v4i v4i;
+    dq::v16i acc[2][2];  // [pixel block][channel block]
+    dq::v16i sacc[2];    // column sums of x^ per pixel block (XSUM)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[i][0][r] = 0;
+            acc[i][1][r] = 0;
+            sacc[i][r] = 0;
+        }
+    }
+    int32_t rsum[2] = {0, 0};  // this lane's share of R for its two channels
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+    for (int ch0 = 0; ch0 < C; ch0 += kKC) {
+        // weight fragments: channel m = mw0 + 32 jb + lane % 32, input
+        // channels ch0 + 32 kk + 16 (lane / 32) .. + 15
+        v4i wf[2][kKC / 32];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int m = mw0 + 32 * jb + (lane & 31);
+            const uint8_t* wrow = w + (size_t)(m < M ? m : 0) * C;
+#pragma unroll
+            for (int kk = 0; kk < kKC / 32; ++kk) {
+                const int c = ch0 + 32 * kk + 16 * (lane >> 5);
+                v4i v = {0, 0, 0, 0};
+                if (m < M && c < C) {
+                    if (wvec) {
+                        v = *reinterpret_cast<const v4i*>(wrow + c);
+                        if (WU8) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] ^= (int)kXor;
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const uint32_t b = c + e < C ? (uint32_t)wrow[c + e] ^ (WU8 ? 0x80u : 0u) : 0u;
+                            v[e >> 2] |= (int)(b << (8 * (e & 3)));
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rsum[jb] = __builtin_amdgcn_sdot4(v[e], 0x01010101, rsum[jb], false);
+                wf[jb][kk] = v;
+            }
+        }
+
+        // the image tile: lane handles 4 pixels (p0 + 4 (tid % 16) ..) of
+        // 16 input channels (ch0 + 16 (tid / 16) ..)
+        __syncthreads();  // the previous chunk's operand reads are done
+        {
+            const int pq = tid & 15, cg = tid >> 4;
+            const int p = p0 + 4 * pq;
+            uint32_t d[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int c = ch0 + 16 * cg + j;
+                d[j] = c < C ? load_x4<VEC>(xn + (size_t)c * HW, p, HW, kXPad) : kXPad;
+                if (XU8) d[j] ^= kXor;
+            }
+            const int kb = (16 * cg) >> 5, h = cg & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * pq + i;  // pixel row of the tile
+                v4i slot;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    slot[q] = (int)gather_byte(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3], i);
+                *reinterpret_cast<v4i*>(&xs[((r >> 5) * (kKC / 32) + kb) * 1024 + ((r & 31) + 32 * h) * 16]) = slot;
+            }
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int kk = 0; kk < kKC / 32; ++kk) {
+            const v4i xf0 = *reinterpret_cast<const v4i*>(&xs[(0 * (kKC / 32) + kk) * 1024 + lane * 16]);
+            const v4i xf1 = *reinterpret_cast<const v4i*>(&xs[(1 * (kKC / 32) + kk) * 1024 + lane * 16]);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                acc[0][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf0, wf[jb][kk], acc[0][jb], 0, 0, 0);
+                acc[1][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf1, wf[jb][kk], acc[1][jb], 0, 0, 0);
+            }
+            if (XSUM) {
+                sacc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf0, ones, sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf1, ones, sacc[1], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- requantizing epilogue
+    const float x_scale = x_scale_p[0];
+    const int x_zp = load_zp(x_zp_p, 0, XU8);
+    const dq::QDiv yd = dq::make_qdiv(y_scale_p[0]);
+    const int y_zp = load_zp(y_zp_p, 0, YU8);
+    constexpr int lo = YU8 ? 0 : -128, hi = YU8 ? 255 : 127;
+    uint8_t* ysw = ys + 64 * wave * kYPitch;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const int m = mw0 + 32 * jb + (lane & 31);
+        const bool mok = m < M;
+        const int wi = w_per_channel ? m : 0;
+        const int32_t R = rsum[jb] + __shfl_xor(rsum[jb], 32);
+        const int coef = kA - (mok ? load_zp(w_zp, wi, WU8) : 0);
+        const float ws = mok ? w_scale[wi] : 0.0f;
+        const uint32_t rowc = (uint32_t)(kB - x_zp) * (uint32_t)R +
+                              (uint32_t)C * ((uint32_t)coef * (uint32_t)(kB - x_zp)) +
+                              (uint32_t)(mok && bias ? bias[m] : 0);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    uint32_t v = (uint32_t)acc[ib][jb][r] + rowc;
+                    if (XSUM) v += (uint32_t)coef * (uint32_t)sacc[ib][r];
+                    float real = (float)(int32_t)v * x_scale;
+                    real = real * ws;
+                    const int code = dq::sat_add(dq::rne(dq::qdiv(real, yd)), y_zp, lo, hi);
+                    word |= ((uint32_t)code & 0xffu) << (8 * e);
+                }
+                const int pp = 32 * ib + 8 * g + 4 * (lane >> 5);  // pixel of the tile
+                *reinterpret_cast<uint32_t*>(&ysw[(32 * jb + (lane & 31)) * kYPitch + pp]) = word;
+            }
+        }
+    }
+    // the wave's 64 staged rows back as 16-byte segments (LDS operations of
+    // one wave complete in order: no barrier)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int u = lane + 64 * it;
+        const int rr = u >> 2, q = u & 3;
+        const int m = mw0 + rr, p = p0 + 16 * q;
+        if (m < M && p < HW) {
+            const v4i v = *reinterpret_cast<const v4i*>(&ysw[rr * kYPitch + 16 * q]);
+            uint8_t* dst = y + (n * M + m) * (size_t)HW + p;
+            if (VEC) {
+                *reinterpret_cast<v4i*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (p + e < HW) dst[e] = (uint8_t)((uint32_t)v[e >> 2] >> (8 * (e & 3)));
+            }
+        }
+    }
+}
+
+template <bool XU8, bool WU8, bool YU8, bool XSUM>
+void launch_v(bool vec, dim3 grid, hipStream_t s, const uint8_t* x, const uint8_t* w, int C, int HW,
+              int M, const float* xs, const uint8_t* xz, const float* ws, const uint8_t* wz, int wpc,
+              const float* ys, const uint8_t* yz, const int32_t* bias, int wvec, uint8_t* y) {
+    if (vec)
+        hipLaunchKernelGGL((k_qconv1x1<XU8, WU8, YU8, XSUM, true>), grid, dim3(kThreads), 0, s, x, w, C,
+                           HW, M, xs, xz, ws, wz, wpc, ys, yz, bias, wvec, y);
+    else
+        hipLaunchKernelGGL((k_qconv1x1<XU8, WU8, YU8, XSUM, false>), grid, dim3(kThreads), 0, s, x, w, C,
+                           HW, M, xs, xz, ws, wz, wpc, ys, yz, bias, wvec, y);
+}
+
+template <bool XU8, bool WU8, bool YU8>
+void launch_s(bool xsum, bool vec, dim3 grid, hipStream_t s, const uint8_t* x, const uint8_t* w, int C,
+              int HW, int M, const float* xs, const uint8_t* xz, const float* ws, const uint8_t* wz,
+              int wpc, const float* ys, const uint8_t* yz, const int32_t* bias, int wvec, uint8_t* y) {
+    if (xsum)
+        launch_v<XU8, WU8, YU8, true>(vec, grid, s, x, w, C, HW, M, xs, xz, ws, wz, wpc, ys, yz, bias, wvec, y);
+    else
+        launch_v<XU8, WU8, YU8, false>(vec, grid, s, x, w, C, HW, M, xs, xz, ws, wz, wpc, ys, yz, bias, wvec, y);
+}
+
+bool is_8bit(dq_dtype t) { return t == DQ_I8 || t == DQ_U8; }
+
+}  // namespace
+
+extern "C" int qlinear_conv1x1(const void* x, dq_dtype x_type, int64_t N, int64_t C, int64_t HW,
+                               const float* x_scale, const void* x_zero_point, const void* w,
+                               dq_dtype w_type, int64_t M, const float* w_scale,
+                               const void* w_zero_point, int64_t w_len, const float* y_scale,
+                               const void* y_zero_point, dq_dtype y_type, const int32_t* bias,
+                               void* y, void* stream) {
+    if (!is_8bit(x_type) || !is_8bit(w_type) || !is_8bit(y_type))
+        DQ_FAIL(DQ_ERR_TYPE, "x, w and y must be DQ_I8 or DQ_U8");
+    if (N < 0 || C < 1 || HW < 0 || M < 0) DQ_FAIL(DQ_ERR_ARG, "need N, HW, M >= 0 and C >= 1");
+    if (C > 32768) DQ_FAIL(DQ_ERR_RANGE, "C = %lld exceeds 32768 (int32 sums)", (long long)C);
+    if (w_len != 1 && w_len != M) DQ_FAIL(DQ_ERR_ARG, "w_len must be 1 or M");
+    if (N == 0 || HW == 0 || M == 0) return DQ_OK;
+    if (!x || !w || !x_scale || !w_scale || !y_scale || !y)
+        DQ_FAIL(DQ_ERR_ARG, "x, w, y and the scales must not be NULL");
+    if (HW > 0x7fffffffLL - kP || N > 65535 || (M + kMT - 1) / kMT > 65535)
+        DQ_FAIL(DQ_ERR_RANGE, "shape too large for one launch");
+    const dim3 grid((unsigned)((HW + kP - 1) / kP), (unsigned)((M + kMT - 1) / kMT), (unsigned)N);
+    const bool vec = HW % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0;
+    const int wvec = C % 16 == 0 && (uintptr_t)w % 16 == 0;
+    // S[p] is needed unless every w zero point equals the shift of w (0 for
+    // int8); a non-NULL zero point of a uint8 w or any zero point tensor of
+    // an int8 w is taken as possibly needing it.
+    const bool xsum = w_type == DQ_U8 || w_zero_point != nullptr;
+    const hipStream_t s = (hipStream_t)stream;
+    const uint8_t* xb = (const uint8_t*)x;
+    const uint8_t* wb = (const uint8_t*)w;
+    const uint8_t* xz = (const uint8_t*)x_zero_point;
+    const uint8_t* wz = (const uint8_t*)w_zero_point;
+    const uint8_t* yz = (const uint8_t*)y_zero_point;
+    uint8_t* yb = (uint8_t*)y;
+    const int wpc = w_len == M && M > 1;
+    const int Ci = (int)C, HWi = (int)HW, Mi = (int)M;
+#define DQ_C(XU, WU, YU)                                                                          \
+    launch_s<XU, WU, YU>(xsum, vec, grid, s, xb, wb, Ci, HWi, Mi, x_scale, xz, w_scale, wz, wpc, \
+                         y_scale, yz, bias, wvec, yb)
+    const bool xu = x_type == DQ_U8, wu = w_type == DQ_U8, yu = y_type == DQ_U8;
+    if (xu) {
+        if (wu) { if (yu) DQ_C(true, true, true); else DQ_C(true, true, false); }
+        else { if (yu) DQ_C(true, false, true); else DQ_C(true, false, false); }
+    } else {
+        if (wu) { if (yu) DQ_C(false, true, true); else DQ_C(false, true, false); }
+        else { if (yu) DQ_C(false, false, true); else DQ_C(false, false, false); }
+    }
+#undef DQ_C
+    DQ_LAUNCH_CHECK("qlinear_conv1x1");
+    return DQ_OK;
+}

@@ -195,6 +195,38 @@ int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim,
                        const int64_t* shape, int axis, const float* x_scale,
                        const void* x_zero_point, float* y, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Requantizing 1x1 QLinearConv (stride 1, no padding, one group).
+ * Defined by the ONNX "QLinearConv" operator (opset 10), description and
+ * inputs: x, w and y are 8-bit tensors; x and y have one scale and zero
+ * point each, w one per tensor or one per output channel; the optional bias
+ * is int32, already quantized with scale x_scale * w_scale and zero point 0.
+ * For each image n, output channel m and pixel p:
+ *   acc  = sum_c (w[m,c] - w_zp[m]) * (x[n,c,p] - x_zp) + bias[m]
+ *   real = ((float)acc * x_scale) * w_scale[m]
+ *   y[n,m,p] = saturate(rne(real / y_scale) + y_zp)
+ * with an IEEE fp32 quotient rounded to nearest, ties to even, and
+ * saturation to [0,255] (uint8 y) or [-128,127] (int8 y).
+ * x: [N, C, HW] (NCHW with H*W = HW), y: [N, M, HW], w: [M, C], all dense
+ * row-major DEVICE tensors. x_scale, y_scale: one fp32 on the device.
+ * x_zero_point / y_zero_point: one value of x's / y's type on the device
+ * (NULL = 0). w_scale: w_len fp32, w_zero_point: w_len values of w's type
+ * (NULL = 0), w_len = 1 or M. bias: M int32 (NULL = none).
+ * The sum is exact while acc fits in int32 (C <= 32768 bounds the product
+ * part; the caller keeps bias within range).
+ * Asynchronous on `stream`. Zero N, HW or M is a no-op. Errors:
+ * DQ_ERR_TYPE (a type other than DQ_I8 / DQ_U8), DQ_ERR_ARG (C < 1,
+ * negative sizes, w_len, NULL tensors or scales), DQ_ERR_RANGE (C > 32768,
+ * a grid beyond one launch), DQ_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+int qlinear_conv1x1(const void* x, dq_dtype x_type, int64_t N, int64_t C,
+                    int64_t HW, const float* x_scale, const void* x_zero_point,
+                    const void* w, dq_dtype w_type, int64_t M,
+                    const float* w_scale, const void* w_zero_point,
+                    int64_t w_len, const float* y_scale,
+                    const void* y_zero_point, dq_dtype y_type,
+                    const int32_t* bias, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,6 +121,34 @@ def test_qlinear_rejects_bad_arguments(dq):
     assert lib.qlinear_dequantize(None, dq.DQ_U8, 3, empty, 1, None, None, None, None) == dq.DQ_OK
 
 
+def test_qlinear_conv1x1_rejects_bad_arguments(dq):
+    lib = dq.load()
+    U8, I8 = dq.DQ_U8, dq.DQ_I8
+
+    def call(xt=U8, N=2, C=8, HW=16, wt=I8, M=4, w_len=4, yt=U8, x=1, w=1, xs=1, ws=1, ys=1, y=1):
+        return lib.qlinear_conv1x1(x, xt, N, C, HW, xs, None, w, wt, M, ws, None, w_len, ys, None,
+                                   yt, None, y, None)
+
+    # 8-bit types only
+    assert call(xt=dq.DQ_F32) == dq.DQ_ERR_TYPE
+    assert call(wt=dq.DQ_BF16) == dq.DQ_ERR_TYPE
+    assert call(yt=dq.DQ_F32) == dq.DQ_ERR_TYPE
+    # sizes, channel limit, per-channel length
+    assert call(C=0) == dq.DQ_ERR_ARG
+    assert call(N=-1) == dq.DQ_ERR_ARG
+    assert call(C=32769) == dq.DQ_ERR_RANGE
+    assert call(w_len=3) == dq.DQ_ERR_ARG
+    # NULL tensors and scales
+    assert call(x=None) == dq.DQ_ERR_ARG
+    assert call(ws=None) == dq.DQ_ERR_ARG
+    assert call(y=None) == dq.DQ_ERR_ARG
+    # a launch beyond the grid limits
+    assert call(N=70000) == dq.DQ_ERR_RANGE
+    # empty outputs: a no-op that succeeds without a device
+    assert call(N=0, x=None, w=None, xs=None, ws=None, ys=None, y=None) == dq.DQ_OK
+    assert call(M=0, w_len=1, x=None, y=None) == dq.DQ_OK
+
+
 def test_fastdiv_constants_cover_every_quotient():
     # the per-axis kernels find the channel with q = (umulhi(n, m) + n) >> s;
     # the host-side constants must give the exact quotient for all n < 2^32.

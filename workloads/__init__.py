@@ -226,3 +226,33 @@ def qconv1x1(seed: int = 4, batch: int = 8, C: int = 256, M: int = 256,
     return dict(x=x, x_scale=np.float32(0.01), x_zp=128, w=w, w_scale=w_scale,
                 bias=bias, y_scale=np.float32(0.02), y_zp=128,
                 name=f"qlinearconv 1x1 x[{batch},{C},{H},{W}] -> {M} ch")
+
+
+def qconv_random(N: int, C: int, HW: int, M: int, *, seed: int, x_type: str = "u8",
+                 w_type: str = "i8", y_type: str = "u8", per_channel: bool = True,
+                 bias: bool = True, w_zp: bool = False):
+    """A random 1x1 QLinearConv case: x [N,C,HW] and w [M,C] uniform over
+    their 8-bit ranges, zero points uniform over the type's range (w's only
+    when w_zp, else absent = 0), x_scale 0.01, w_scale ~U(0.0005,0.002),
+    int32 bias ~U{-20000..20000}. y_scale is set from C so that the outputs
+    spread over the 8-bit range and both saturation ends occur."""
+    r = rng(seed + 2000)
+
+    def codes(t, shape):
+        lo, hi = (0, 256) if t == "u8" else (-128, 128)
+        return r.integers(lo, hi, shape, dtype=np.int64).astype(np.uint8 if t == "u8" else np.int8)
+
+    x = codes(x_type, (N, C, HW))
+    w = codes(w_type, (M, C))
+    wl = M if per_channel else 1
+    wz = codes(w_type, (wl,)) if w_zp else None
+    x_zp = codes(x_type, (1,))
+    y_zp = codes(y_type, (1,))
+    w_scale = r.uniform(0.0005, 0.002, wl).astype(np.float32)
+    b = r.integers(-20000, 20001, M, dtype=np.int64).astype(np.int32) if bias else None
+    # a w zero point away from w's centre adds a coherent term of size ~C
+    spread = 20.0 if (w_zp or w_type == "u8") else 1.0
+    y_scale = np.float32(spread * 0.01 * 0.00125 * 128.0 * 74.0 * np.sqrt(C) / 100.0)
+    return dict(x=x, x_type=x_type, x_scale=np.float32(0.01), x_zp=x_zp, w=w, w_type=w_type,
+                w_scale=w_scale, w_zp=wz, bias=b, y_scale=y_scale, y_zp=y_zp, y_type=y_type,
+                name=f"qconv1x1 N{N} C{C} HW{HW} M{M} x:{x_type} w:{w_type} y:{y_type}")
