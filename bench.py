@@ -93,8 +93,10 @@ class Dqip:
         t0 = time.perf_counter()
         for _ in range(steps):
             self.forward()
+        te = time.perf_counter()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        self.enqueue_us = (te - t0) * 1e6 / steps
         self.dq.dqip_profile_begin(self.h, steps)
         for _ in range(steps):
             self.forward()
@@ -353,7 +355,7 @@ def main():
     gemm_ms = phases[2]
     achieved = d.ops / (gemm_ms / 1e3) / 1e12
     log(f"bench: {ms * 1e3:.1f} us/forward = {value:.1f} TOPS; gemm {gemm_ms * 1e3:.1f} us = "
-        f"{achieved:.1f} TOPS; quant_a {phases[0] * 1e3:.1f} us")
+        f"{achieved:.1f} TOPS; quant_a {phases[0] * 1e3:.1f} us; host enqueue {d.enqueue_us:.1f} us/forward")
     tr = traffic_record("gemm_i8")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
@@ -363,7 +365,8 @@ def main():
                 "ops_per_launch": d.ops}
 
     secondary = {"dqip_4096_phases_us": {"quant_a": round(phases[0] * 1e3, 2),
-                                         "gemm": round(gemm_ms * 1e3, 2)},
+                                         "gemm": round(gemm_ms * 1e3, 2),
+                                         "host_enqueue": round(d.enqueue_us, 2)},
                  "quant_a_GBps": round((case["M"] * case["K"] * 3) / (phases[0] / 1e3) / 1e9, 1)}
     if not args.quick:
         steps2 = max(10, args.steps // 2)

@@ -114,6 +114,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The same, and also wait until every LDS operation of this wave has
+// completed (lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 // 16 bytes per lane from global memory straight into LDS (gfx950
 // global_load_lds_dwordx4): the wave's 64 lanes land as one contiguous
 // 1 KiB block at lds_block (wave-uniform), lane l at offset 16 l. A plain
@@ -146,21 +154,37 @@ __device__ __forceinline__ int32_t acc_read(int32_t a) {
     return v;
 }
 
-// Wave-wide min / max over 64 lanes (butterfly over xor shuffles).
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = __builtin_fminf(v, __shfl_xor(v, o, kWave));
-    return v;
+// Wave-wide min / max over 64 lanes, returned as a wave-uniform value.
+// Within each row of 16 lanes, four DPP moves combine every lane with its
+// partners (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror:
+// after them every lane of the row holds the row's result); the four rows
+// are then combined from lanes 0, 16, 32 and 48 with v_readlane. DPP moves
+// stay inside the VALU (no LDS round trip as a shuffle would take), so the
+// chain is short.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+__device__ __forceinline__ float wave_min_uniform(float v) {
+    v = __builtin_fminf(v, dpp_f<kDppXor1>(v));
+    v = __builtin_fminf(v, dpp_f<kDppXor2>(v));
+    v = __builtin_fminf(v, dpp_f<kDppRowHalfMirror>(v));
+    v = __builtin_fminf(v, dpp_f<kDppRowMirror>(v));
+    return __builtin_fminf(__builtin_fminf(lane_f(v, 0), lane_f(v, 16)),
+                           __builtin_fminf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_max_uniform(float v) {
+    v = __builtin_fmaxf(v, dpp_f<kDppXor1>(v));
+    v = __builtin_fmaxf(v, dpp_f<kDppXor2>(v));
+    v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+    v = __builtin_fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return __builtin_fmaxf(__builtin_fmaxf(lane_f(v, 0), lane_f(v, 16)),
+                           __builtin_fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 }  // namespace dq

@@ -154,13 +154,10 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     // contiguous 1 KiB block, exactly a packed fragment), without VGPRs.
     // Step t lives in LDS stage t % 4; the copies of step t + 3 are issued
     // while step t is multiplied. The compiler does not track these writes,
-    // so the waits are explicit: at the top of step t this wave waits until
-    // at most the copies of steps t + 1 and t + 2 are outstanding (vector
-    // memory operations complete in order), then the barrier makes every
-    // wave's copies of step t visible and certifies that stage (t - 1) % 4,
-    // the target of step t + 3, is no longer read. Steps past the end
-    // re-load the last step (in bounds, never read), which keeps the loop
-    // body free of conditional code.
+    // so the waits are explicit (vector memory operations complete in
+    // order; see the step below). Steps past the end re-load the last step
+    // (in bounds, never used), which keeps the loop body free of
+    // conditional code.
     auto stage = [&](auto S) -> int8_t* {
         constexpr int k = decltype(S)::value % NSTAGE;
         if constexpr (k == 0) return st0;
@@ -191,55 +188,67 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // One step: the MFMAs of stage L, with the copies of step `ahead` and
-    // the LDS reads of sub-step kk + 1 interleaved one by one with the MFMAs
-    // of sub-step kk.
-    auto step = [&](const int8_t* L, int ahead, int8_t* dst) {
-        dq::v4i fa[2][FM], fb[2][FN];
-        auto read = [&](int kk, int set) {
+    // Operand fragments of a sub-step (two register sets: one feeds the
+    // MFMAs while the other is being read).
+    static_assert(KS == 2, "a step is two 32-deep sub-steps");
+    dq::v4i fa[2][FM], fb[2][FN];
+    auto read = [&](const int8_t* L, int kk, int set) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[set][i] = *reinterpret_cast<const dq::v4i*>(L + ((wm * FM + i) * KS + kk) * 1024 + lofs);
+        for (int i = 0; i < FM; ++i)
+            fa[set][i] = *reinterpret_cast<const dq::v4i*>(L + ((wm * FM + i) * KS + kk) * 1024 + lofs);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[set][j] = *reinterpret_cast<const dq::v4i*>(L + (AF + (wn * FN + j) * KS + kk) * 1024 + lofs);
+    };
+    // One sub-step: the MFMAs on register set `set`, with FPK copies of step
+    // `ahead` (copy slots q0 ..) and the reads of (Lr, kr) into the other
+    // set interleaved one by one: one MFMA, then one copy and one read, ...
+    auto half = [&](int set, int q0, int ahead, int8_t* dst, const int8_t* Lr, int kr) {
+#pragma unroll
+        for (int q = 0; q < FPK; ++q)
+            if (q0 + q < FPW) copy(q0 + q, ahead, dst);
+        read(Lr, kr, set ^ 1);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                fb[set][j] = *reinterpret_cast<const dq::v4i*>(L + (AF + (wn * FN + j) * KS + kk) * 1024 + lofs);
-        };
-        read(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int set = kk & 1;
-#pragma unroll
-            for (int q = 0; q < FPK; ++q)
-                if (kk * FPK + q < FPW) copy(kk * FPK + q, ahead, dst);
-            if (kk + 1 < KS) read(kk + 1, set ^ 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
-            // order: one MFMA, then one copy and one LDS read, ...
-#pragma unroll
-            for (int m = 0; m < FM * FN; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (m < FPK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                if (kk + 1 < KS && m < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < FM * FN; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < FPK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (m < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // unrolled by the ring size so every stage reference is static (the
-    // step count is a multiple of 4: Kp is a multiple of 256)
+    // Step t multiplies stage L = t % 4; its first sub-step's fragments were
+    // read during step t - 1. The one barrier of the step sits between its
+    // two sub-steps: before it, this wave's reads of L have completed
+    // (lgkmcnt 0) and its copies of step t + 1 have landed (at most the
+    // copies of step t + 2 and the first half of step t + 3's are still in
+    // flight); after it, every wave's copies of step t + 1 are visible, so
+    // the second sub-step can read step t + 1's first fragments, and no wave
+    // reads L any more, so the copies of step t + 4, issued from step t + 1
+    // on, may overwrite it. No LDS read waits behind a barrier.
+    // Not __syncthreads(): its fence would wait for every outstanding copy.
     auto one = [&](auto S, int t) {
-        // not __syncthreads(): its fence would wait for every outstanding
-        // copy. This wave's copies of step t are done (explicit count) and
-        // its LDS reads of step t - 1 were consumed by that step's MFMAs;
-        // the bare barrier then publishes step t and frees stage t - 1.
-        dq::wait_vmcnt<2 * FPW>();
+        using SN = std::integral_constant<int, decltype(S)::value + 1>;
+        using SA = std::integral_constant<int, decltype(S)::value + NSTAGE - 1>;
+        const int8_t* L = stage(S);
+        int8_t* dst = stage(SA{});
+        half(0, 0, t + NSTAGE - 1, dst, L, 1);
+        dq::wait_vmcnt_lgkm0<FPW + FPK>();
         dq::lds_barrier();
-        step(stage(S), t + NSTAGE - 1, stage(std::integral_constant<int, decltype(S)::value + NSTAGE - 1>{}));
+        half(1, FPK, t + NSTAGE - 1, dst, stage(SN{}), 0);
     };
+    // step 0's copies, then its first fragments
+    dq::wait_vmcnt_lgkm0<2 * FPW>();
+    dq::lds_barrier();
+    read(st0, 0, 0);
+    // unrolled by the ring size so every stage reference is static (the
+    // step count is a multiple of 4: Kp is a multiple of 256); the last
+    // step's look-ahead reads a re-loaded stage and is never used
     for (int t = 0; t < nsteps; t += NSTAGE) {
         one(std::integral_constant<int, 0>{}, t);
         one(std::integral_constant<int, 1>{}, t + 1);

@@ -43,8 +43,8 @@ __device__ __forceinline__ void load16(const void* __restrict__ A, size_t row_ba
         if (BF16) {
             const dq::u4* p = reinterpret_cast<const dq::u4*>(
                 reinterpret_cast<const uint16_t*>(A) + row_base + k0);
-            const dq::u4 a = __builtin_nontemporal_load(p);
-            const dq::u4 b = __builtin_nontemporal_load(p + 1);
+            const dq::u4 a = p[0];
+            const dq::u4 b = p[1];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 x[2 * w] = dq::bf16_bits_to_f32(a[w] & 0xffffu);
@@ -57,7 +57,7 @@ __device__ __forceinline__ void load16(const void* __restrict__ A, size_t row_ba
                 reinterpret_cast<const float*>(A) + row_base + k0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const dq::f4 v = __builtin_nontemporal_load(p + q);
+                const dq::f4 v = p[q];
                 x[4 * q] = v[0];
                 x[4 * q + 1] = v[1];
                 x[4 * q + 2] = v[2];
@@ -116,12 +116,12 @@ __device__ __forceinline__ void store_group(int8_t* __restrict__ sA, size_t row,
     *reinterpret_cast<dq::u4*>(sA + dq::frag_offset(row, (size_t)g * 16, KF)) = o;
 }
 
-// Row statistics are identical in every lane after the reductions; reading
-// them from lane 0 makes scale, zero point and the division path scalar
-// (wave-uniform), so the row takes one branch instead of one per element.
+// Row statistics come out of the reductions as wave-uniform values, which
+// makes scale, zero point and the division path scalar, so the row takes one
+// branch instead of one per element.
 __device__ __forceinline__ void uniform_minmax(float& lo, float& hi) {
-    lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dq::wave_min(lo))));
-    hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dq::wave_max(hi))));
+    lo = dq::wave_min_uniform(lo);
+    hi = dq::wave_max_uniform(hi);
 }
 
 // Row cached in VGPRs: NV groups of 16 per lane (K <= 1024 * NV).
@@ -176,6 +176,145 @@ k_quant_rows(const void* __restrict__ A, int M, int K, int KF, int8_t* __restric
     }
 }
 
+// ---- persistent variant with the next row prefetched (vector loads only)
+//
+// Each wave quantizes rows w, w + W, w + 2W, ... (W waves in the grid) and
+// issues the loads of its next row before it works on the current one, so
+// the row's arithmetic overlaps the next row's memory traffic. Rows stay in
+// VGPRs as loaded (NV groups of 16 values: 2 x 16 bytes of bf16 or 4 x 16
+// bytes of fp32 per group).
+constexpr int kPfWaves = 4096;  // four waves per SIMD on 256 CUs
+
+template <bool BF16, int NV>
+struct RawRow {
+    static constexpr int U = BF16 ? 2 : 4;  // 16-byte vectors per group
+    dq::u4 v[NV][U];
+};
+
+template <bool BF16, int NV>
+__device__ __forceinline__ void load_row(const void* __restrict__ A, int row, int K, int lane,
+                                         RawRow<BF16, NV>& r) {
+    constexpr int U = RawRow<BF16, NV>::U;
+    const int ngroups = K >> 4;
+    const dq::u4* base = reinterpret_cast<const dq::u4*>(
+        reinterpret_cast<const char*>(A) + (size_t)row * K * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int g = lane + 64 * v;
+#pragma unroll
+        for (int u = 0; u < U; ++u) r.v[v][u] = g < ngroups ? base[(size_t)g * U + u] : dq::u4{0, 0, 0, 0};
+    }
+}
+
+// Element e (0..15) of group v as fp32 (a bf16 value is the top half of its
+// fp32 bit pattern).
+template <bool BF16, int NV>
+__device__ __forceinline__ float elem(const RawRow<BF16, NV>& r, int v, int e) {
+    if (BF16) {
+        const uint32_t w = r.v[v][e >> 3][(e >> 1) & 3];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    return __uint_as_float(r.v[v][e >> 2][e & 3]);
+}
+
+// Quantizes one row held in registers. Fast path (the scale has a normal
+// reciprocal; |A / scale| <= 256 by construction): q = corrected quotient;
+// adding 1.5 * 2^23 rounds q half to even into the low mantissa bits
+// (the float add rounds to nearest even, and 1.5 * 2^23 is even), so the
+// bit pattern is 0x4B400000 + rne(q); a median against the integers
+// 1.5 * 2^23 - zero and 1.5 * 2^23 + 255 - zero clamps it to
+// rne(q) + zero in [0, 255]; the low bytes of four codes are packed and
+// zero - 128 is added to every byte at once (a carry-free bytewise add),
+// giving uA - 128.
+template <bool BF16, int NV>
+__device__ __forceinline__ void quantize_row(const RawRow<BF16, NV>& r, int row, int K, int KF,
+                                             int lane, int8_t* __restrict__ sA,
+                                             float* __restrict__ scaleA,
+                                             int32_t* __restrict__ zeroA) {
+    const int ngroups = K >> 4;
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        if (lane + 64 * v < ngroups) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float x = elem(r, v, e);
+                lo = __builtin_fminf(lo, x);
+                hi = __builtin_fmaxf(hi, x);
+            }
+        }
+    }
+    uniform_minmax(lo, hi);
+    float scale;
+    int zero;
+    row_params(lo, hi, scale, zero);
+    const dq::QDiv d = dq::make_qdiv(scale);
+    if (d.fast) {
+        constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+        // 1.5 * 2^23 + n is exact for |n| < 2^22, so the clamp bounds are too
+        const float lof = kMagic - (float)zero, hif = kMagic + (float)(255 - zero);
+        const uint32_t C = (uint32_t)((zero - 128) & 0xff) * 0x01010101u;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int g = lane + 64 * v;
+            if (g >= ngroups) continue;
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t b[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = dq::qdiv_fast(elem(r, v, 4 * q + e), d) + kMagic;
+                    b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t, lof, hif));
+                }
+                const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+                w[q] = ((packed & 0x7f7f7f7fu) + (C & 0x7f7f7f7fu)) ^ ((packed ^ C) & 0x80808080u);
+            }
+            const dq::u4 o = {w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<dq::u4*>(sA + dq::frag_offset(row, (size_t)g * 16, KF)) = o;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int g = lane + 64 * v;
+            if (g >= ngroups) continue;
+            float x[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = elem(r, v, e);
+            store_group<false>(sA, row, g, KF, x, d, zero);
+        }
+    }
+    if (lane == 0) {
+        scaleA[row] = scale;
+        zeroA[row] = zero;
+    }
+}
+
+template <bool BF16, int NV>
+__global__ void __launch_bounds__(256)
+k_quant_rows_pf(const void* __restrict__ A, int M, int K, int KF, int8_t* __restrict__ sA,
+                float* __restrict__ scaleA, int32_t* __restrict__ zeroA) {
+    const int lane = threadIdx.x & 63;
+    const int W = gridDim.x * 4;
+    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    RawRow<BF16, NV> ra, rb;
+    load_row(A, row, K, lane, ra);
+    // ping-pong between two register buffers (no copies between them)
+    for (;;) {
+        int next = row + W;
+        if (next < M) load_row(A, next, K, lane, rb);
+        quantize_row(ra, row, K, KF, lane, sA, scaleA, zeroA);
+        if (next >= M) return;
+        row = next;
+        next = row + W;
+        if (next < M) load_row(A, next, K, lane, ra);
+        quantize_row(rb, row, K, KF, lane, sA, scaleA, zeroA);
+        if (next >= M) return;
+        row = next;
+    }
+}
+
 // Any K: min/max pass, then a second pass that re-reads each group.
 template <bool BF16, bool VEC>
 __global__ void __launch_bounds__(kThreads)
@@ -216,11 +355,27 @@ k_quant_rows_stream(const void* __restrict__ A, int M, int K, int KF, int8_t* __
     }
 }
 
+template <bool BF16, int NV>
+void launch_pf(hipStream_t s, DqTiming t, const void* A, int M, int K, int KF, int8_t* sA,
+               float* scaleA, int32_t* zeroA) {
+    const int waves = M < kPfWaves ? M : kPfWaves;
+    hipExtLaunchKernelGGL((k_quant_rows_pf<BF16, NV>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
+                          t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
+}
+
 template <bool BF16, bool VEC>
 void launch_rows(dim3 grid, hipStream_t s, DqTiming t, const void* A, int M, int K, int KF,
                  int8_t* sA, float* scaleA, int32_t* zeroA) {
     const int ngroups = (K + 15) / 16;
     const int nv = (ngroups + 63) / 64;
+    // prefetching variant where two rows fit in registers (<= 64 VGPRs each)
+    if (VEC && nv <= (BF16 ? 8 : 4)) {
+        if (nv <= 1) launch_pf<BF16, 1>(s, t, A, M, K, KF, sA, scaleA, zeroA);
+        else if (nv <= 2) launch_pf<BF16, 2>(s, t, A, M, K, KF, sA, scaleA, zeroA);
+        else if (nv <= 4) launch_pf<BF16, 4>(s, t, A, M, K, KF, sA, scaleA, zeroA);
+        else launch_pf<BF16, (BF16 ? 8 : 4)>(s, t, A, M, K, KF, sA, scaleA, zeroA);
+        return;
+    }
     if (nv <= 1)
         hipExtLaunchKernelGGL((k_quant_rows<BF16, VEC, 1>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
     else if (nv <= 2)

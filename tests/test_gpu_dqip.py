@@ -68,6 +68,32 @@ def test_sweep_odd_shapes(gpu, M, N, K, tA, tB, constB, tC, act, avoid):
     _compare(case, run_dqip(gpu, case, ext_buf=(M % 2 == 1)), oracle.dqip_forward(case))
 
 
+ROW_PATHS = [
+    # (M, K, typeA): register-resident rows of 1..8 groups of 16 per lane,
+    # several rows per wave (M above the persistent grid), odd row counts
+    (5000, 2048, "f32"),
+    (2049, 4096, "f32"),
+    (3000, 1024, "bf16"),
+    (2100, 8192, "bf16"),
+    (4099, 512, "f32"),
+]
+
+
+@pytest.mark.parametrize("M,K,tA", ROW_PATHS)
+def test_row_quantizer_paths(gpu, M, K, tA):
+    """Every uA / scaleA / zeroA bit-exact for the row-quantizer variants;
+    C checked on sampled rows."""
+    log(f"dqip row quantizer M={M} K={K} A:{tA}")
+    case = W.dqip_random(M, 16, K, seed=M + K, typeA=tA, typeB="i8", typeC="f32", constB=True,
+                         outliers=0.01, zero_rows=(0, M // 2, M - 1))
+    got = run_dqip(gpu, case, accumulators=False)
+    uA, sA, zA = oracle.quantize_rows(case["A"], tA)
+    assert np.array_equal(got["zeroA"], zA)
+    assert np.array_equal(got["scaleA"].view(np.uint32), sA.view(np.uint32))
+    assert np.array_equal(got["uA"], uA)
+    _compare_sampled(case, got, _sample_rows(M, 5))
+
+
 def test_no_bias_flag_and_null_bias(gpu):
     log("dqip bias handling")
     case = W.dqip_random(40, 24, 96, seed=3, bias=False)
