@@ -8,7 +8,8 @@
 //
 // Both kernels are element-wise and bound by HBM bandwidth: each wave
 // instruction moves one contiguous 1 KiB of fp32 (16 bytes per lane) or the
-// matching 256 bytes of 8-bit codes (4 per lane). The tensor is viewed as
+// matching 256 bytes of 8-bit codes (4 per lane), and a lane requests all
+// four of its vectors before it computes. The tensor is viewed as
 // [outer, C, inner]; the channel of element e is (e / inner) % C, found with
 // multiply-high division by constants precomputed on the host. When inner
 // is a multiple of 4 a 4-element vector never straddles two channels and the
@@ -124,6 +125,95 @@ k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t 
     }
 }
 
+// TAB: the 4096 elements of a block cover at most kTabMax channels (per
+// tensor, or per axis with inner >= 64 and inner % 4 == 0, so the four
+// elements of a vector share a channel). The block first builds a table of
+// those channels' scale, correctly rounded reciprocal and zero point in LDS
+// (one division per channel instead of one per vector), then each lane
+// quantizes four 4-element vectors whose loads are 1 KiB contiguous per
+// wave instruction. Fast path (normal reciprocal): q0 = x * (1/s) clamped
+// to +-2^22 (an input so large that x / s overflows saturates either way,
+// and the clamp keeps the residual finite), q = q0 + (x - q0 s) (1/s) (the
+// IEEE quotient's rounding to an integer, see dq::qdiv); q + 1.5 * 2^23
+// rounds it half to even into the low mantissa bits, a median clamps it to
+// the saturation bounds minus the zero point, and the zero point is added
+// to the four packed low bytes at once (carry-free bytewise add).
+constexpr int kTabMax = 66;  // 4096 / 64 + 2
+
+template <bool U8>
+__global__ void __launch_bounds__(256)
+k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float* __restrict__ scale,
+               const void* __restrict__ zp, uint8_t* __restrict__ y) {
+    __shared__ float t_s[kTabMax], t_y[kTabMax], t_lo[kTabMax], t_hi[kTabMax];
+    __shared__ uint32_t t_z[kTabMax];
+    __shared__ int t_fast[kTabMax];
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    constexpr float kBig = 4194304.0f;     // 2^22
+    const uint32_t eb = blockIdx.x * 4096u;
+    const uint32_t last = (uint64_t)eb + 4095 < n ? eb + 4095u : (uint32_t)(n - 1);
+    // "rows" of inner elements: channel of row r is r % C
+    const uint32_t r0 = am.per_axis ? fdiv(eb, am.inner) : 0;
+    const uint32_t nrows = am.per_axis ? fdiv(last, am.inner) - r0 + 1 : 1;
+    for (uint32_t k = threadIdx.x; k < nrows; k += 256) {
+        const uint32_t row = r0 + k;
+        const uint32_t c = am.per_axis ? row - fdiv(row, am.cdim) * am.cdim.d : 0;
+        const float sc = scale[c];
+        const int z = load_zp<U8>(zp, c);
+        const dq::QDiv d = dq::make_qdiv(sc);
+        t_s[k] = sc;
+        t_y[k] = d.y;
+        t_fast[k] = d.fast;
+        t_z[k] = (uint32_t)(z & 0xff) * 0x01010101u;
+        t_lo[k] = kMagic + (float)((U8 ? 0 : -128) - z);
+        t_hi[k] = kMagic + (float)((U8 ? 255 : 127) - z);
+    }
+    __syncthreads();
+    const uint32_t base = eb + threadIdx.x * 4u;
+    dq::f4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t e0 = base + q * 1024u;
+        v[q] = (uint64_t)e0 + 4 <= n ? __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(x + e0))
+                                     : dq::f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t e0 = base + q * 1024u;
+        if ((uint64_t)e0 >= n) break;
+        const uint32_t k = am.per_axis ? fdiv(e0, am.inner) - r0 : 0;
+        if ((uint64_t)e0 + 4 > n) {  // the tensor's last partial vector
+            for (uint64_t e = e0; e < n; ++e) {
+                const uint32_t c = channel_of((uint32_t)e, am);
+                y[e] = (uint8_t)quant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+            }
+            break;
+        }
+        uint32_t w;
+        if (t_fast[k]) {
+            const float sc = t_s[k], ry = t_y[k], lof = t_lo[k], hif = t_hi[k];
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xe = v[q][e];
+                const float q0 = __builtin_amdgcn_fmed3f(xe * ry, -kBig, kBig);
+                const float r = __builtin_fmaf(-q0, sc, xe);
+                const float t = __builtin_fmaf(r, ry, q0) + kMagic;
+                b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t, lof, hif));
+            }
+            const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+            const uint32_t Z = t_z[k];
+            w = ((packed & 0x7f7f7f7fu) + (Z & 0x7f7f7f7fu)) ^ ((packed ^ Z) & 0x80808080u);
+        } else {
+            const float sc = t_s[k];
+            const int z = (int)(U8 ? (t_z[k] & 0xffu) : (uint32_t)(int8_t)(t_z[k] & 0xffu));
+            w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w |= ((uint32_t)quant1<U8>(v[q][e], sc, z) & 0xffu) << (8 * e);
+        }
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(y + e0));
+    }
+}
+
 // -------------------------------------------------------------- dequantize
 
 template <bool U8>
@@ -142,11 +232,18 @@ k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint6
                     const void* __restrict__ zp, float* __restrict__ y) {
     if (VEC) {
         const uint32_t base = blockIdx.x * 4096u + threadIdx.x * 4u;
+        // every slice's codes are requested before the first store
+        uint32_t wq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e0 = base + q * 1024u;
+            wq[q] = (uint64_t)e0 + 4 <= n ? *reinterpret_cast<const uint32_t*>(x + e0) : 0u;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t e0 = base + q * 1024u;
             if ((uint64_t)e0 + 4 <= n) {
-                const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(x + e0));
+                const uint32_t w = wq[q];
                 dq::f4 out;
                 if (CH4) {
                     const uint32_t c = channel_of(e0, am);
@@ -161,7 +258,7 @@ k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint6
                         out[b] = dequant1<U8>(w >> (8 * b), scale[c], load_zp<U8>(zp, c));
                     }
                 }
-                *reinterpret_cast<dq::f4*>(y + e0) = out;
+                __builtin_nontemporal_store(out, reinterpret_cast<dq::f4*>(y + e0));
             } else {
                 for (uint64_t e = e0; e < n && e < (uint64_t)e0 + 4; ++e) {
                     const uint32_t c = channel_of((uint32_t)e, am);
@@ -251,6 +348,21 @@ extern "C" int qlinear_quantize(const float* x, int ndim, const int64_t* shape, 
     if (!x || !y || !y_scale) DQ_FAIL(DQ_ERR_ARG, "x, y and y_scale must not be NULL");
     hipStream_t s = (hipStream_t)stream;
     const bool u8 = y_type == DQ_U8;
+    const bool small = p.n < (UINT64_C(1) << 32) - 4096 && p.inner < (UINT64_C(1) << 32) &&
+                       p.cdim < (UINT64_C(1) << 32);
+    if (small && (!p.per_axis || (p.inner >= 64 && p.inner % 4 == 0)) && (uintptr_t)x % 16 == 0 &&
+        (uintptr_t)y % 4 == 0) {
+        const AxisMap am = make_axis_map(p, true);
+        const unsigned blocks = (unsigned)((p.n + 4095) / 4096);
+        if (u8)
+            hipLaunchKernelGGL((k_quantize_tab<true>), dim3(blocks), dim3(256), 0, s, x, p.n, am, y_scale,
+                               y_zero_point, (uint8_t*)y);
+        else
+            hipLaunchKernelGGL((k_quantize_tab<false>), dim3(blocks), dim3(256), 0, s, x, p.n, am, y_scale,
+                               y_zero_point, (uint8_t*)y);
+        DQ_LAUNCH_CHECK("quantize_linear");
+        return DQ_OK;
+    }
     rc = dispatch(p, x, y, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
 #define DQ_QL(U, V, C)                                                                     \
     hipLaunchKernelGGL((k_quantize_linear<U, V, C>), dim3(blocks), dim3(256), 0, s, x, p.n, \

@@ -49,6 +49,8 @@ def _check_both(dq, x, scale, zp, axis, y_type):
 @pytest.mark.parametrize("shape,axis", [
     ((2, 16, 9, 11), 1),     # inner 99: channel per element
     ((4, 32, 8, 8), 1),      # inner 64: channel per 16-vector
+    ((5, 48, 4, 4), 1),      # inner 16: a new channel every 16 elements
+    ((7, 3, 32), 1),         # inner 32
     ((3, 5, 7), 0),          # leading axis
     ((3, 5, 7), 2),          # last axis, inner 1
     ((3, 5, 7), -2),         # negative axis
