@@ -122,6 +122,12 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until every LDS operation of this wave has completed (lgkmcnt 0),
+// leaving vector memory operations in flight.
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // 16 bytes per lane from global memory straight into LDS (gfx950
 // global_load_lds_dwordx4): the wave's 64 lanes land as one contiguous
 // 1 KiB block at lds_block (wave-uniform), lane l at offset 16 l. A plain

@@ -245,6 +245,281 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1(
     }
 }
 
+// ---- persistent variant: M <= 256 and C <= 256 (the weights of a wave fit in
+// its registers for the whole launch).
+//
+// Work items are (image, 32-pixel tile). A workgroup loads its weight
+// fragments once, then walks items g, g + G, ...: the raw image bytes of
+// the next item are requested before the current item's MFMAs and
+// requantization run, the tile is transposed into one of two LDS buffers
+// (one barrier per item: the buffer written for item i + 2 was last read
+// before every wave passed item i + 1's barrier), and each wave finishes 64
+// output channels x 32 pixels. The requantization rounds as the other
+// quantizers do: a corrected quotient clamped to +-2^22, 1.5 * 2^23 added for
+// round-half-even, a median clamp and a bytewise zero-point add.
+constexpr int kPP = 32;          // pixels per item
+constexpr int kPersistentGroups = 512;
+constexpr int kYPitchP = 48;     // LDS bytes per staged output row (32 + 16)
+
+// The raw bytes of an item: lane handles pixels p .. p+3 (p = p0 + 4 (tid % 8))
+// of channels 8 (tid / 8) .. + 7 (pad: bytes that become x^ = 0).
+// FULL (every pixel in range, 4-byte loads): every lane loads from a clamped
+// channel and the caller replaces channels past C by the pad when it uses
+// the words, so the loads are unconditional and nothing waits for them
+// before their use.
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void load_item(const uint8_t* __restrict__ xn, int C, int HW, int p, int cg,
+                                          uint32_t pad, uint32_t (&d)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int c = 8 * cg + j;
+        if (FULL) {
+            // raw word; channels past C are replaced by the pad at use
+            d[j] = *reinterpret_cast<const uint32_t*>(xn + (size_t)(c < C ? c : C - 1) * HW + p);
+        } else {
+            d[j] = c < C ? load_x4<VEC>(xn + (size_t)c * HW, p, HW, pad) : pad;
+        }
+    }
+}
+
+// The wave's staged 64 rows x 32 pixels of one item back to y as 16-byte
+// segments (lane handles two).
+template <bool VEC, bool FULL>
+__device__ __forceinline__ void store_staged(const uint8_t* ysw, uint8_t* __restrict__ y, int n, int p0,
+                                             int mw0, int M, int HW, int lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = lane + 64 * k;
+        const int rr = u >> 1, q = u & 1;
+        const int m = mw0 + rr, p = p0 + 16 * q;
+        if (FULL || (m < M && p < HW)) {
+            const dq::v4i v = *reinterpret_cast<const dq::v4i*>(&ysw[rr * kYPitchP + 16 * q]);
+            uint8_t* dst = y + ((size_t)n * M + m) * (size_t)HW + p;
+            if (VEC || FULL) {
+                *reinterpret_cast<dq::v4i*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (p + e < HW) dst[e] = (uint8_t)((uint32_t)v[e >> 2] >> (8 * (e & 3)));
+            }
+        }
+    }
+}
+
+template <bool XU8, bool WU8, bool YU8, bool XSUM, bool VEC, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_qconv1x1_p(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int C, int HW, int M,
+    const float* __restrict__ x_scale_p, const uint8_t* __restrict__ x_zp_p,
+    const float* __restrict__ w_scale, const uint8_t* __restrict__ w_zp, int w_per_channel,
+    const float* __restrict__ y_scale_p, const uint8_t* __restrict__ y_zp_p,
+    const int32_t* __restrict__ bias, int wvec, int nitems, int tiles, int per_xcd,
+    uint8_t* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) int8_t xs0[(kKC / 32) * 1024];
+    __shared__ __attribute__((aligned(16))) int8_t xs1[(kKC / 32) * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t ys[kMT * kYPitchP];
+
+    constexpr uint32_t kXor = 0x80808080u;
+    constexpr int kA = WU8 ? 128 : 0;
+    constexpr int kB = XU8 ? 128 : 0;
+    constexpr uint32_t kXPad = XU8 ? kXor : 0u;
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    constexpr float kBig = 4194304.0f;     // 2^22
+    typedef dq::v4i v4i;
+
+    // XCD-aware item order: workgroups go round robin over the 8 XCDs, so
+    // XCD (blockIdx % 8) owns the item range [xcd * per_xcd, ...), and its
+    // workgroups walk that range with a stride of their count. Consecutive
+    // workgroups of an XCD then hold the four 32-pixel tiles of one 128-byte
+    // line of x at the same time and share its fetch in the XCD's L2.
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8, stride = gridDim.x / 8;
+    const int first = xcd * per_xcd;
+    const int end = min(first + per_xcd, nitems);
+    int item = first + local;
+    if (item >= end) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int mw0 = 64 * wave;
+
+    // every load that does not depend on another is issued first: the first
+    // item's image bytes, the per-tensor and per-channel parameters, then the
+    // weights, so their latencies overlap
+    const int pq = tid & 7, cg = tid >> 3;
+    uint32_t d[8];
+    int prev_n = 0, prev_p0 = 0;
+    {
+        const int n = item / tiles, p0 = (item - n * tiles) * kPP;
+        load_item<VEC, FULL>(x + (size_t)n * C * HW, C, HW, p0 + 4 * pq, cg, kXPad, d);
+    }
+    const float x_scale = x_scale_p[0];
+    const float y_scale = y_scale_p[0];
+    const int x_zp = load_zp(x_zp_p, 0, XU8);
+    const int y_zp = load_zp(y_zp_p, 0, YU8);
+    int wzp[2], bia[2];
+    float wsc[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const int m = mw0 + 32 * jb + (lane & 31);
+        const bool mok = m < M;
+        const int wi = w_per_channel ? m : 0;
+        wzp[jb] = mok ? load_zp(w_zp, wi, WU8) : 0;
+        wsc[jb] = mok ? w_scale[wi] : 0.0f;
+        bia[jb] = mok && bias ? bias[m] : 0;
+    }
+
+    // weight fragments of the wave (channels mw0 + 32 jb + lane % 32), once
+    v4i wf[2][kKC / 32];
+    int32_t rsum[2] = {0, 0};
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const int m = mw0 + 32 * jb + (lane & 31);
+        const uint8_t* wrow = w + (size_t)(m < M ? m : 0) * C;
+#pragma unroll
+        for (int kk = 0; kk < kKC / 32; ++kk) {
+            const int c = 32 * kk + 16 * (lane >> 5);
+            v4i v = {0, 0, 0, 0};
+            if (m < M && c < C) {
+                if (wvec) {
+                    v = *reinterpret_cast<const v4i*>(wrow + c);
+                    if (WU8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] ^= (int)kXor;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const uint32_t b = c + e < C ? (uint32_t)wrow[c + e] ^ (WU8 ? 0x80u : 0u) : 0u;
+                        v[e >> 2] |= (int)(b << (8 * (e & 3)));
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rsum[jb] = __builtin_amdgcn_sdot4(v[e], 0x01010101, rsum[jb], false);
+            wf[jb][kk] = v;
+        }
+    }
+
+    // per-channel and per-tensor constants of the requantization
+    const dq::QDiv yd = dq::make_qdiv(y_scale);
+    constexpr int lo = YU8 ? 0 : -128, hi = YU8 ? 255 : 127;
+    const float lof = kMagic + (float)(lo - y_zp), hif = kMagic + (float)(hi - y_zp);
+    const uint32_t Yz = (uint32_t)(y_zp & 0xff) * 0x01010101u;
+    uint32_t rowc[2];
+    int coef[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const int32_t R = rsum[jb] + __shfl_xor(rsum[jb], 32);
+        coef[jb] = kA - wzp[jb];
+        rowc[jb] = (uint32_t)(kB - x_zp) * (uint32_t)R +
+                   (uint32_t)C * ((uint32_t)coef[jb] * (uint32_t)(kB - x_zp)) + (uint32_t)bia[jb];
+    }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    uint8_t* ysw = ys + 64 * wave * kYPitchP;
+
+    for (int it = 0;; ++it) {
+        const int n = item / tiles, p0 = (item - n * tiles) * kPP;
+        int8_t* xs = (it & 1) ? xs1 : xs0;
+        // transpose: for pixel i, channels 8 cg .. 8 cg + 7 as 8 bytes of a slot
+        {
+            if (FULL) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) d[j] = 8 * cg + j < C ? d[j] : kXPad;
+            }
+            const int kb = cg >> 2, h = (cg >> 1) & 1, off = 8 * (cg & 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo4 = gather_byte(d[0] ^ (XU8 ? kXor : 0u), d[1] ^ (XU8 ? kXor : 0u),
+                                                 d[2] ^ (XU8 ? kXor : 0u), d[3] ^ (XU8 ? kXor : 0u), i);
+                const uint32_t hi4 = gather_byte(d[4] ^ (XU8 ? kXor : 0u), d[5] ^ (XU8 ? kXor : 0u),
+                                                 d[6] ^ (XU8 ? kXor : 0u), d[7] ^ (XU8 ? kXor : 0u), i);
+                const dq::u2 pr = {lo4, hi4};
+                *reinterpret_cast<dq::u2*>(&xs[kb * 1024 + ((4 * pq + i) + 32 * h) * 16 + off]) = pr;
+            }
+        }
+        // this wave's tile writes are done; the bare barrier then publishes
+        // the tile (not __syncthreads(): its fence would also wait for the
+        // previous item's output stores)
+        dq::wait_lgkm0();
+        dq::lds_barrier();
+        // the previous item's codes leave before the next item's loads are
+        // issued: no store sits between those loads and their use, so
+        // waiting for them never waits for a store
+        if (it > 0) store_staged<VEC, FULL>(ysw, y, prev_n, prev_p0, mw0, M, HW, lane);
+        const int next = item + stride;
+        if (next < end) {
+            const int nn = next / tiles, np0 = (next - nn * tiles) * kPP;
+            load_item<VEC, FULL>(x + (size_t)nn * C * HW, C, HW, np0 + 4 * pq, cg, kXPad, d);
+        }
+        dq::v16i acc[2], sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[0][r] = 0;
+            acc[1][r] = 0;
+            sacc[r] = 0;
+        }
+        // all of the item's operand fragments first, then the MFMAs
+        v4i xfr[kKC / 32];
+#pragma unroll
+        for (int kk = 0; kk < kKC / 32; ++kk) xfr[kk] = *reinterpret_cast<const v4i*>(&xs[kk * 1024 + lane * 16]);
+#pragma unroll
+        for (int kk = 0; kk < kKC / 32; ++kk) {
+            const v4i xf = xfr[kk];
+            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf, wf[0][kk], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf, wf[1][kk], acc[1], 0, 0, 0);
+            if (XSUM) sacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf, ones, sacc, 0, 0, 0);
+        }
+        // requantize: lane holds channel (lane % 32) of block jb and, in
+        // accumulators 4g .. 4g+3, pixels 8g + 4 (lane / 32) + 0..3
+        if (yd.fast) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint32_t b[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t v = (uint32_t)acc[jb][4 * g + e] + rowc[jb];
+                        if (XSUM) v += (uint32_t)coef[jb] * (uint32_t)sacc[4 * g + e];
+                        float real = (float)(int32_t)v * x_scale;
+                        real = real * wsc[jb];
+                        const float q0 = __builtin_amdgcn_fmed3f(real * yd.y, -kBig, kBig);
+                        const float r = __builtin_fmaf(-q0, yd.s, real);
+                        const float t = __builtin_fmaf(r, yd.y, q0) + kMagic;
+                        b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t, lof, hif));
+                    }
+                    const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+                    const uint32_t word = ((packed & 0x7f7f7f7fu) + (Yz & 0x7f7f7f7fu)) ^ ((packed ^ Yz) & 0x80808080u);
+                    const int pp = 8 * g + 4 * (lane >> 5);
+                    *reinterpret_cast<uint32_t*>(&ysw[(32 * jb + (lane & 31)) * kYPitchP + pp]) = word;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t v = (uint32_t)acc[jb][4 * g + e] + rowc[jb];
+                        if (XSUM) v += (uint32_t)coef[jb] * (uint32_t)sacc[4 * g + e];
+                        float real = (float)(int32_t)v * x_scale;
+                        real = real * wsc[jb];
+                        const int code = dq::sat_add(dq::rne(real / yd.s), y_zp, lo, hi);
+                        word |= ((uint32_t)code & 0xffu) << (8 * e);
+                    }
+                    const int pp = 8 * g + 4 * (lane >> 5);
+                    *reinterpret_cast<uint32_t*>(&ysw[(32 * jb + (lane & 31)) * kYPitchP + pp]) = word;
+                }
+            }
+        }
+        prev_n = n;
+        prev_p0 = p0;
+        if (next >= end) break;
+        item = next;
+    }
+    store_staged<VEC, FULL>(ysw, y, prev_n, prev_p0, mw0, M, HW, lane);
+}
+
 template <bool XU8, bool WU8, bool YU8, bool XSUM>
 void launch_v(bool vec, dim3 grid, hipStream_t s, const uint8_t* x, const uint8_t* w, int C, int HW,
               int M, const float* xs, const uint8_t* xz, const float* ws, const uint8_t* wz, int wpc,
@@ -287,7 +562,6 @@ extern "C" int qlinear_conv1x1(const void* x, dq_dtype x_type, int64_t N, int64_
         DQ_FAIL(DQ_ERR_ARG, "x, w, y and the scales must not be NULL");
     if (HW > 0x7fffffffLL - kP || N > 65535 || (M + kMT - 1) / kMT > 65535)
         DQ_FAIL(DQ_ERR_RANGE, "shape too large for one launch");
-    const dim3 grid((unsigned)((HW + kP - 1) / kP), (unsigned)((M + kMT - 1) / kMT), (unsigned)N);
     const bool vec = HW % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0;
     const int wvec = C % 16 == 0 && (uintptr_t)w % 16 == 0;
     // S[p] is needed unless every w zero point equals the shift of w (0 for
@@ -303,6 +577,45 @@ extern "C" int qlinear_conv1x1(const void* x, dq_dtype x_type, int64_t N, int64_
     uint8_t* yb = (uint8_t*)y;
     const int wpc = w_len == M && M > 1;
     const int Ci = (int)C, HWi = (int)HW, Mi = (int)M;
+    if (M <= kMT && C <= kKC) {
+        // persistent variant: items of (image, 32-pixel tile) spread evenly
+        // over at most kPersistentGroups workgroups
+        const long long tiles = (HW + kPP - 1) / kPP, items = N * tiles;
+        if (items > 0x7fffffffLL) DQ_FAIL(DQ_ERR_RANGE, "shape too large for one launch");
+        // per XCD: a range of items (a multiple of 4 tiles, one 128-pixel
+        // line) and a multiple of 4 workgroups, about two items each, at
+        // most kPersistentGroups / 8
+        const long long per_xcd = ((items + 7) / 8 + 3) / 4 * 4;
+        long long g8 = ((per_xcd + 1) / 2 + 3) / 4 * 4;
+        if (g8 > kPersistentGroups / 8) g8 = kPersistentGroups / 8;
+        const unsigned groups = (unsigned)(8 * g8);
+        const int ni = (int)items, nt = (int)tiles, px = (int)per_xcd;
+        // FULL: all 256 channels and every pixel of every tile exist, so no
+        // load or store is conditional
+        const bool full = vec && M == kMT && HW % kPP == 0;
+#define DQ_P(XU, WU, YU, XS, V, F)                                                                         \
+    hipLaunchKernelGGL((k_qconv1x1_p<XU, WU, YU, XS, V, F>), dim3(groups), dim3(kThreads), 0, s, xb, wb, Ci, \
+                       HWi, Mi, x_scale, xz, w_scale, wz, wpc, y_scale, yz, bias, wvec, ni, nt, px, yb)
+#define DQ_PX(XU, WU, YU, XS) \
+    if (full) DQ_P(XU, WU, YU, XS, true, true); else if (vec) DQ_P(XU, WU, YU, XS, true, false); \
+    else DQ_P(XU, WU, YU, XS, false, false);
+#define DQ_PV(XU, WU, YU) \
+    if (xsum) { DQ_PX(XU, WU, YU, true) } else { DQ_PX(XU, WU, YU, false) }
+        const bool xu = x_type == DQ_U8, wu = w_type == DQ_U8, yu = y_type == DQ_U8;
+        if (xu) {
+            if (wu) { if (yu) { DQ_PV(true, true, true) } else { DQ_PV(true, true, false) } }
+            else { if (yu) { DQ_PV(true, false, true) } else { DQ_PV(true, false, false) } }
+        } else {
+            if (wu) { if (yu) { DQ_PV(false, true, true) } else { DQ_PV(false, true, false) } }
+            else { if (yu) { DQ_PV(false, false, true) } else { DQ_PV(false, false, false) } }
+        }
+#undef DQ_PV
+#undef DQ_PX
+#undef DQ_P
+        DQ_LAUNCH_CHECK("qlinear_conv1x1");
+        return DQ_OK;
+    }
+    const dim3 grid((unsigned)((HW + kP - 1) / kP), (unsigned)((M + kMT - 1) / kMT), (unsigned)N);
 #define DQ_C(XU, WU, YU)                                                                          \
     launch_s<XU, WU, YU>(xsum, vec, grid, s, xb, wb, Ci, HWi, Mi, x_scale, xz, w_scale, wz, wpc, \
                          y_scale, yz, bias, wvec, yb)
