@@ -406,7 +406,8 @@ def main():
     secondary = {"dqip_4096_phases_us": {"quant_a": round(phases[0] * 1e3, 2),
                                          "gemm": round(gemm_ms * 1e3, 2),
                                          "host_enqueue": round(d.enqueue_us, 2)},
-                 "quant_a_GBps": round((case["M"] * case["K"] * 3) / (phases[0] / 1e3) / 1e9, 1)}
+                 "quant_a_GBps": (round((case["M"] * case["K"] * 3) / (phases[0] / 1e3) / 1e9, 1)
+                                  if phases[0] > 0 else None)}
     if not args.quick:
         steps2 = max(10, args.steps // 2)
         log("bench: QuantizeLinear / DequantizeLinear [64,256,56,56]")

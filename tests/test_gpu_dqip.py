@@ -94,6 +94,27 @@ def test_row_quantizer_paths(gpu, M, K, tA):
     _compare_sampled(case, got, _sample_rows(M, 5))
 
 
+@pytest.mark.parametrize("tA,tB", [("f32", "f32"), ("bf16", "bf16")])
+def test_tiny_scales_stay_exact(gpu, tA, tB):
+    """Rows of A and columns of B scaled down until their quantization scales
+    fall below 2^-100 and into the subnormal range: there the quantizers'
+    reciprocal-and-residual quotient is not exact and the IEEE division must
+    be taken; every code, scale and zero point stays bit-exact."""
+    log(f"dqip tiny scales A:{tA} B:{tB}")
+    case = W.dqip_random(70, 68, 300, seed=21, typeA="f32", typeB="f32", typeC="f32",
+                         constB=False, outliers=0.01)
+    A, B = case["A"], case["B"]
+    for i, f in ((1, 1e-33), (2, 1e-36), (3, 1e-38), (4, 3e-39)):
+        A[i] *= np.float32(f)
+    for j, f in ((1, 1e-33), (2, 1e-36), (5, 1e-37), (8, 3e-38)):
+        B[:, j] *= np.float32(f)
+    if tA == "bf16":
+        case["A"], case["typeA"] = W.to_bf16_bits(A), "bf16"
+    if tB == "bf16":
+        case["B"], case["typeB"] = W.to_bf16_bits(B), "bf16"
+    _compare(case, run_dqip(gpu, case), oracle.dqip_forward(case))
+
+
 def test_no_bias_flag_and_null_bias(gpu):
     log("dqip bias handling")
     case = W.dqip_random(40, 24, 96, seed=3, bias=False)
