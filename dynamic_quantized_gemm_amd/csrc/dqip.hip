@@ -302,9 +302,9 @@ extern "C" int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype 
         delete c;
         return rc;
     }
-    char buf[256];
+    char buf[512];
     snprintf(buf, sizeof buf,
-             "gfx950 A:%s B:%s%s C:%s | quant_rows wave-per-row, fragment-packed | %s%s | %s",
+             "gfx950 A:%s B:%s%s C:%s | quant_rows 8-row blocks staged in LDS, whole-line fragment stores | %s%s | %s",
              dtype_name(typeA), dtype_name(typeB), constB ? "(const)" : "(dynamic)",
              dtype_name(typeC), constB ? "" : "quant_cols absmax+pack | ",
              avoidOverflow ? "B range [-64,63]" : "B range [-128,127]",
