@@ -276,24 +276,40 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     const int col0 = n0 + wn * FN * 32;
 #pragma clang loop unroll(full)
     for (int p0 = 0; p0 < FM; p0 += SPP) {
-        uint32_t za[SPP];
+        // the correction (128 - zeroA) * colsum on the 24-bit multiplier (full
+        // rate; a 32-bit product would take the quarter-rate 64-bit multiply-
+        // add): |128 - zeroA| <= 128 and -2^23 <= colsum < 2^23 for K <= 65536,
+        // so the product is exact and the wrapping add gives the exact sum
+        int za[SPP];
         float sA[SPP];
 #pragma unroll
         for (int u = 0; u < SPP; ++u) {
             const int rt = (wm * FM + p0 + u) * 32 + rs;  // tile row
-            za[u] = (uint32_t)(128 - s_za[rt]);
+            za[u] = 128 - s_za[rt];
             sA[u] = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
         }
+        // column groups jg = 4 j + g; each group's parameters are read from
+        // LDS one group ahead, so their latency hides behind the previous
+        // group's arithmetic
+        dq::v4i csv[2];
+        dq::f4 sBv[2], bvv[2];
+        auto params = [&](int jg, int set) {
+            const int ct = wn * FN * 32 + (jg >> 2) * 32 + 8 * (jg & 3) + 4 * (lane >> 5);  // tile column
+            csv[set] = *reinterpret_cast<const dq::v4i*>(&s_cs[ct]);
+            if (OUT != DQ_OUT_ACC) sBv[set] = *reinterpret_cast<const dq::f4*>(&s_sb[ct]);
+            if (OUT != DQ_OUT_ACC && BIAS) bvv[set] = *reinterpret_cast<const dq::f4*>(&s_bias[ct]);
+        };
+        params(0, 0);
 #pragma clang loop unroll(full)
-        for (int j = 0; j < FN; ++j) {
-#pragma clang loop unroll(full)
-            for (int g = 0; g < 4; ++g) {
+        for (int jg = 0; jg < FN * 4; ++jg) {
+            const int j = jg >> 2, g = jg & 3, set = jg & 1;
+            if (jg + 1 < FN * 4) params(jg + 1, set ^ 1);
+            {
                 const int cs_ = j * 32 + 8 * g + 4 * (lane >> 5);  // strip column
-                const int ct = wn * FN * 32 + cs_;                  // tile column
-                const dq::v4i cs = *reinterpret_cast<const dq::v4i*>(&s_cs[ct]);
+                const dq::v4i cs = csv[set];
                 dq::f4 sB = {0.0f, 0.0f, 0.0f, 0.0f}, bv = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (OUT != DQ_OUT_ACC) sB = *reinterpret_cast<const dq::f4*>(&s_sb[ct]);
-                if (OUT != DQ_OUT_ACC && BIAS) bv = *reinterpret_cast<const dq::f4*>(&s_bias[ct]);
+                if (OUT != DQ_OUT_ACC) sB = sBv[set];
+                if (OUT != DQ_OUT_ACC && BIAS) bv = bvv[set];
                 const int byte = cs_ * OB;
 #pragma unroll
                 for (int u = 0; u < SPP; ++u) {
@@ -302,7 +318,7 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                     for (int e = 0; e < 4; ++e)
                         sum[e] = (int32_t)((uint32_t)(kAgpr ? dq::acc_read(acc[p0 + u][j][4 * g + e])
                                                              : acc[p0 + u][j][4 * g + e]) +
-                                           za[u] * (uint32_t)cs[e]);
+                                           (uint32_t)__mul24(za[u], cs[e]));
                     int8_t* dst = region + u * SB + rs * RB + (((byte >> 4) ^ (rs & (CPR - 1))) << 4) + (byte & 15);
                     if (OUT == DQ_OUT_ACC) {
                         const dq::v4i v = {sum[0], sum[1], sum[2], sum[3]};
@@ -322,15 +338,15 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                             *reinterpret_cast<dq::f4*>(dst) = val;
                     }
                 }
-                // one column group at a time: keeps the accumulator reads and
-                // parameter loads of later groups from being hoisted here
+                // one column group at a time: keeps the accumulator reads of
+                // later groups from being hoisted here (which would spill)
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         // the pass back as row segments: chunk q -> row q / CPR of the pass;
         // LDS operations of one wave complete in order, so no barrier
         const int row0 = m0 + (wm * FM + p0) * 32;
-#pragma unroll 4
+#pragma unroll 8
         for (int q = lane; q < SPP * 32 * CPR; q += 64) {
             const int r = q / CPR, c = q % CPR;  // r: row of the pass
             const int row = row0 + r, col = col0 + c * EPC;
