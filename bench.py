@@ -193,11 +193,12 @@ def copy_calibration(torch, mib=1024, reps=10):
 
 
 def time_cold_warm(fn, torch, steps, flush):
-    """(median ms per call with the caches flushed before each call, mean ms
-    per call back to back); HIP events on torch's current stream, which is
-    the stream the library launches on. The flush READS a buffer twice the
-    Infinity Cache's size: that evicts the call's data without leaving
-    dirty lines whose write-back the timed call would pay for."""
+    """((median, p10, p90) ms per call with the caches flushed before each
+    call, mean ms per call back to back); HIP events on torch's current
+    stream, which is the stream the library launches on. The flush READS a
+    buffer twice the Infinity Cache's size: that evicts the call's data
+    without leaving dirty lines whose write-back the timed call would pay
+    for."""
     for _ in range(3):
         fn()
     cold = []
@@ -216,12 +217,15 @@ def time_cold_warm(fn, torch, steps, flush):
         fn()
     e1.record()
     e1.synchronize()
-    return float(np.median(cold)), e0.elapsed_time(e1) / steps
+    pct = tuple(float(np.percentile(cold, q)) for q in (50, 10, 90))
+    return pct, e0.elapsed_time(e1) / steps
 
 
-def _bw_record(nbytes, cold_ms, warm_ms):
+def _bw_record(nbytes, cold, warm_ms):
     gb = nbytes / 1e9
-    return {"us_cold": round(cold_ms * 1e3, 2), "GBps_cold": round(gb / (cold_ms / 1e3), 1),
+    cold_ms = cold[0]
+    return {"us_cold": round(cold_ms * 1e3, 2), "us_cold_p10": round(cold[1] * 1e3, 2),
+            "us_cold_p90": round(cold[2] * 1e3, 2), "GBps_cold": round(gb / (cold_ms / 1e3), 1),
             "frac_cold": round(gb / (cold_ms / 1e3) / HBM_PEAK_GBS, 3),
             "us_warm": round(warm_ms * 1e3, 2), "GBps_warm": round(gb / (warm_ms / 1e3), 1)}
 
@@ -282,7 +286,7 @@ def bench_qdq(dq, torch, steps):
     del xs, ys, rs
     out["workload"] = "x fp32 [64,256,56,56] NCHW <-> int8, per-channel (axis 1) scale/zero point"
     out["bytes_per_call"] = 5 * n
-    out["timing"] = ("cold: median of calls each after a 512 MiB read flush; warm: back to back on "
+    out["timing"] = ("cold: median (p10, p90) of calls each after a 512 MiB read flush; warm: back to back on "
                      "one buffer set; stream: back to back over 5 buffer sets (1.3 GB), median of 3 "
                      "loops")
     return out
@@ -318,13 +322,19 @@ def bench_qconv(dq, torch, steps):
     return out
 
 
-def bench_dqip_case(dq, torch, case, steps, warmup):
+def bench_dqip_case(dq, torch, case, steps, warmup, flush):
+    """Back-to-back forwards (warm: a recurrence keeps its weights cache-
+    resident), their per-phase kernel times, and single forwards after a
+    cache flush (cold: median, p10, p90)."""
     d = Dqip(dq, torch, case)
     try:
         ms, ph = d.timed(torch, steps, warmup)
+        cold, _ = time_cold_warm(d.forward, torch, steps, flush)
     finally:
         d.release()
     return {"workload": case["name"], "us_per_forward": round(ms * 1e3, 2),
+            "us_cold": round(cold[0] * 1e3, 2), "us_cold_p10": round(cold[1] * 1e3, 2),
+            "us_cold_p90": round(cold[2] * 1e3, 2),
             "TOPS": round(d.ops / (ms / 1e3) / 1e12, 2),
             "phase_us": {"quant_a": round(ph[0] * 1e3, 2), "quant_b": round(ph[1] * 1e3, 2),
                          "gemm": round(ph[2] * 1e3, 2)},
@@ -416,13 +426,15 @@ def main():
         log("bench: QLinearConv 1x1 [8,256,56,56]")
         secondary["qlinearconv_1x1"] = bench_qconv(dq, torch, steps2)
         log(f"bench: {secondary['qlinearconv_1x1']}")
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         for name, mk in (("dqip_64x64x128", W.dqip_small),
                          ("lstm_input_4096x2048x512", lambda: W.dqip_lstm(recurrent=False)),
                          ("lstm_recurrent_32x2048x512", lambda: W.dqip_lstm(recurrent=True)),
                          ("dqip_8192_dynamic_b", W.dqip_dynamic_b)):
             log(f"bench: {name}")
-            secondary[name] = bench_dqip_case(dq, torch, mk(), steps2, 3)
+            secondary[name] = bench_dqip_case(dq, torch, mk(), steps2, 3, flush)
             log(f"bench: {secondary[name]}")
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline:
