@@ -151,6 +151,16 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
     constexpr float kBig = 4194304.0f;     // 2^22
     const uint32_t eb = blockIdx.x * 4096u;
     const uint32_t last = (uint64_t)eb + 4095 < n ? eb + 4095u : (uint32_t)(n - 1);
+    // the block's x first: the channel table below is built while these
+    // loads are in flight
+    const uint32_t base = eb + threadIdx.x * 4u;
+    dq::f4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t e0 = base + q * 1024u;
+        v[q] = (uint64_t)e0 + 4 <= n ? __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(x + e0))
+                                     : dq::f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     // "rows" of inner elements: channel of row r is r % C
     const uint32_t r0 = am.per_axis ? fdiv(eb, am.inner) : 0;
     const uint32_t nrows = am.per_axis ? fdiv(last, am.inner) - r0 + 1 : 1;
@@ -168,14 +178,6 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
         t_hi[k] = kMagic + (float)((U8 ? 255 : 127) - z);
     }
     __syncthreads();
-    const uint32_t base = eb + threadIdx.x * 4u;
-    dq::f4 v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t e0 = base + q * 1024u;
-        v[q] = (uint64_t)e0 + 4 <= n ? __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(x + e0))
-                                     : dq::f4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t e0 = base + q * 1024u;
