@@ -48,6 +48,10 @@ def lib() -> C.CDLL:
         L.oracle_qlinear_conv.argtypes = [vp, i32, i64, i64, i64, i64, f32, i32,
                                           vp, i32, i64, i64, i64, vp, vp, i64, vp,
                                           f32, i32, i32, vp]
+        L.oracle_quantize_tensor_u8.argtypes = [vp, i64, vp, vp, vp]
+        L.oracle_qgemm.argtypes = [vp, i32, i32, i64, i64, f32, i32, vp, i32, i32, i64,
+                                   vp, i64, vp, i64, vp, i64, i64, f32, vp, i32, f32, i32,
+                                   vp, vp]
         _lib = L
     return _lib
 
@@ -246,3 +250,80 @@ def qlinear_conv(x, x_scale, x_zp, w, w_scale, w_zp, y_scale, y_zp, *, bias=None
                                    _TYPE[y_type], _p(y))
     _check(rc, "qlinear_conv")
     return y
+
+
+# ------------------------------------------------ QGemm family (R15-R19)
+
+def _tag8(a):
+    return "u8" if a.dtype == np.uint8 else "i8"
+
+
+def quantize_tensor_u8(A):
+    """Whole-tensor dynamic quantization to uint8 (R19): (scale, zero point, q)."""
+    a = _c(A, np.float32)
+    q = np.empty(a.shape, np.uint8)
+    sc = np.zeros(1, np.float32)
+    zp = np.zeros(1, np.int32)
+    _check(lib().oracle_quantize_tensor_u8(_p(a), a.size, _p(sc), _p(zp), _p(q)),
+           "quantize_tensor_u8")
+    return np.float32(sc[0]), int(zp[0]), q
+
+
+def qgemm(A, B, a_scale, a_zp, b_scale, b_zp=None, *, transA=False, transB=False, C=None,
+          alpha=1.0, bias=None, y_scale=None, y_zp=0, y_type=None, with_acc=False):
+    """R15-R18. A: (M,K) 8-bit, or (K,M) with transA; B: (K,N), or (N,K) with
+    transB. b_scale / b_zp: scalars or length N. C: int32 broadcastable to
+    (M,N) (shapes (), (N,), (1,N), (M,1), (M,N)). y_type None: float Y;
+    "u8" / "i8": requantized with y_scale / y_zp. with_acc also returns the
+    int32 sums sum + C."""
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    M, K = (A.shape[1], A.shape[0]) if transA else A.shape
+    Kb, N = (B.shape[1], B.shape[0]) if transB else B.shape
+    if Kb != K:
+        raise ValueError("inner dimensions differ")
+    bs = _c(np.atleast_1d(b_scale), np.float32)
+    bz = None if b_zp is None else _c(np.atleast_1d(b_zp), np.int32)
+    cm, c_rs, c_cs = None, 0, 0
+    if C is not None:
+        c = np.asarray(C, np.int32)
+        if c.ndim == 0 or c.size == 1:
+            cm = _c(c.reshape(1), np.int32)
+        elif c.ndim == 1:
+            if c.shape[0] != N:
+                raise ValueError("C does not broadcast")
+            cm, c_cs = _c(c, np.int32), 1
+        else:
+            if c.shape[0] not in (1, M) or c.shape[1] not in (1, N):
+                raise ValueError("C does not broadcast")
+            cm = _c(c, np.int32)
+            c_rs = c.shape[1] if c.shape[0] == M else 0
+            c_cs = 1 if c.shape[1] == N else 0
+    bv = None if bias is None else _c(bias, np.float32)
+    if y_type is None:
+        Y = np.empty((M, N), np.float32)
+        yt, ys = "f32", 1.0
+    else:
+        Y = np.empty((M, N), _np_type(y_type))
+        yt, ys = y_type, float(np.float32(y_scale))
+    acc = np.empty((M, N), np.int32) if with_acc else None
+    rc = lib().oracle_qgemm(_p(A), _TYPE[_tag8(A)], int(bool(transA)), M, K,
+                            float(np.float32(a_scale)), int(a_zp), _p(B), _TYPE[_tag8(B)],
+                            int(bool(transB)), N, _p(bs), bs.size, _p(bz),
+                            0 if bz is None else bz.size, _p(cm), c_rs, c_cs,
+                            float(np.float32(alpha)), _p(bv), _TYPE[yt], ys, int(y_zp), _p(Y),
+                            _p(acc))
+    _check(rc, "qgemm")
+    return (Y, acc) if with_acc else Y
+
+
+def matmul_integer_to_float(A, B, a_scale, b_scale, a_zp=0, b_zp=None, bias=None):
+    """MatMulIntegerToFloat (R15, R17): float Y = sum * a_scale * b_scale + bias."""
+    return qgemm(A, B, a_scale, a_zp, b_scale, b_zp, bias=bias)
+
+
+def dynamic_quantize_matmul(A, B, b_scale, b_zp=None, bias=None):
+    """DynamicQuantizeMatMul (R19): A float quantized per tensor to uint8,
+    then MatMulIntegerToFloat."""
+    sc, zp, q = quantize_tensor_u8(A)
+    return qgemm(q, B, sc, zp, b_scale, b_zp, bias=bias)

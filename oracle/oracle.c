@@ -43,6 +43,21 @@
  *      (val < 0 ? val * alpha : val).
  *  R11 requantization (QLinearConv): real = ((float)acc * x_scale) * w_scale,
  *      then QuantizeLinear with y_scale / y_zero_point.
+ *  - onnxruntime quantization_defs.cc, schemas QGemm, MatMulIntegerToFloat
+ *    and DynamicQuantizeMatMul (inputs, types and attributes only; no
+ *    formula is printed):
+ *  R15 sum[m,n] = sum_k (A[m,k] - a_zp) * (B[k,n] - b_zp[n]); a_scale and a_zp
+ *      per tensor; b_scale, b_zp per tensor or per column n (b_zp default 0);
+ *      transA / transB select A as (K,M) and B as (N,K).
+ *  R16 QGemm's C is int32 with zero point 0 in the scale alpha * a_scale *
+ *      b_scale (beta read as 1), so it is added to the integer sum, broadcast
+ *      to (M,N) (strides 0 on broadcast axes).
+ *  R17 real = ((float)(sum + C) * (alpha * a_scale)) * b_scale[n], alpha *
+ *      a_scale rounded to fp32 once; + bias[n] for MatMulIntegerToFloat and
+ *      DynamicQuantizeMatMul.
+ *  R18 an 8-bit QGemm output: y = saturate(rne(real / y_scale) + y_zp).
+ *  R19 DynamicQuantizeMatMul quantizes A per tensor to uint8 with R1-R4 over
+ *      the whole tensor, then computes R15 + R17.
  *
  * Arithmetic: fp32 where the pages fix fp32 tensors, IEEE division,
  * nearbyintf in the default round-to-nearest mode for ties-to-even, int64
@@ -387,6 +402,71 @@ int oracle_qlinear_conv(const void* x, int x_type, int64_t Nb, int64_t C,
                     int64_t yi = ((n * M + m) * oH + oh) * oW + ow;
                     store_int8(y, y_type, yi, sat_add(rne(q), y_zp, lo, hi));
                 }
+        }
+    return ORC_OK;
+}
+
+/* --------------------------------------------------- QGemm family (R15-R19) */
+
+/* The whole tensor A (n values) to uint8 with one scale and zero point: R1-R4
+ * applied to all of A at once (R19). */
+int oracle_quantize_tensor_u8(const float* A, int64_t n, float* scale, int32_t* zp, uint8_t* q)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        if (A[i] < lo) lo = A[i];
+        if (A[i] > hi) hi = A[i];
+    }
+    float s = 1.0f;
+    int z = 0;
+    if (hi != lo) {
+        float range = hi - lo;
+        s = range / 255.0f;
+        z = sat_add(rne(-lo / s), 0, 0, 255);
+    }
+    for (int64_t i = 0; i < n; ++i) q[i] = (uint8_t)sat_add(rne(A[i] / s), z, 0, 255);
+    *scale = s;
+    *zp = z;
+    return ORC_OK;
+}
+
+/* R15-R18. A is (M,K) row-major, or (K,M) with transA; B is (K,N), or (N,K)
+ * with transB. b_scale / b_zp have 1 or N entries (b_zp NULL: 0). C (NULL:
+ * none) is read at m * c_rs + n * c_cs. y_type ORC_F32 gives float Y;
+ * ORC_U8 / ORC_I8 requantize with y_scale / y_zp. acc_out (optional)
+ * receives sum + C as int32. Returns ORC_ERR_OVERFLOW when sum + C leaves
+ * int32. */
+int oracle_qgemm(const void* A, int a_type, int transA, int64_t M, int64_t K, float a_scale,
+                 int32_t a_zp, const void* B, int b_type, int transB, int64_t N,
+                 const float* b_scale, int64_t b_scale_len, const int32_t* b_zp,
+                 int64_t b_zp_len, const int32_t* Cm, int64_t c_rs, int64_t c_cs, float alpha,
+                 const float* bias, int y_type, float y_scale, int32_t y_zp, void* Y,
+                 int32_t* acc_out)
+{
+    if ((b_scale_len != 1 && b_scale_len != N) || (b_zp && b_zp_len != 1 && b_zp_len != N))
+        return ORC_ERR_ARG;
+    float sa = alpha * a_scale;
+    int lo = (y_type == ORC_U8) ? 0 : -128;
+    int hi = (y_type == ORC_U8) ? 255 : 127;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t zb = b_zp ? b_zp[b_zp_len == 1 ? 0 : n] : 0;
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t ai = transA ? k * M + m : m * K + k;
+                int64_t bi = transB ? n * K + k : k * N + n;
+                sum += (int64_t)(load_int8(A, a_type, ai) - a_zp) * (load_int8(B, b_type, bi) - zb);
+            }
+            if (Cm) sum += Cm[m * c_rs + n * c_cs];
+            if (sum > INT32_MAX || sum < INT32_MIN) return ORC_ERR_OVERFLOW;
+            if (acc_out) acc_out[m * N + n] = (int32_t)sum;
+            float real = (float)(int32_t)sum * sa;
+            real = real * b_scale[b_scale_len == 1 ? 0 : n];
+            if (bias) real = real + bias[n];
+            if (y_type == ORC_F32)
+                ((float*)Y)[m * N + n] = real;
+            else
+                store_int8(Y, y_type, m * N + n, sat_add(rne(real / y_scale), y_zp, lo, hi));
         }
     return ORC_OK;
 }

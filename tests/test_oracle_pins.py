@@ -467,3 +467,126 @@ def test_qlinear_conv_1x1_brute_force_and_exact_requantization():
     sure = frac > 1e-5
     assert sure.mean() > 0.99 and (want[sure] == 255).any() and (want[sure] == 0).any()
     assert np.array_equal(y[sure].astype(np.float64), want[sure])
+
+
+# ================================================== QGemm family (R15-R19)
+# onnxruntime quantization_defs.cc, schemas QGemm, MatMulIntegerToFloat and
+# DynamicQuantizeMatMul: inputs A, B with scales and zero points (B's per
+# tensor or per column), QGemm's int32 C, alpha, transA / transB and the
+# optional 8-bit output; the readings are R15-R19 in oracle.c.
+
+def _q8(r, shape, u8):
+    return (r.integers(0, 256, shape).astype(np.uint8) if u8
+            else r.integers(-128, 128, shape).astype(np.int8))
+
+
+def test_qgemm_unit_scales_zero_points_is_the_integer_matmul():
+    # a_scale = b_scale = alpha = 1 and zero points 0: Y is A @ B (numpy's
+    # int64 matmul; every |sum| < 2^24, so exact in fp32)
+    r = np.random.default_rng(40)
+    for ua, ub in ((True, False), (False, True), (True, True), (False, False)):
+        A, B = _q8(r, (9, 31), ua), _q8(r, (31, 5), ub)
+        Y = oracle.qgemm(A, B, 1.0, 0, 1.0)
+        assert np.array_equal(Y, (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float32))
+
+
+def test_qgemm_zero_point_shift_invariance():
+    # (A + t) - (a_zp + t) = A - a_zp: moving a code range and its zero point
+    # together leaves every sum and output unchanged; likewise per column of B
+    r = np.random.default_rng(41)
+    A = r.integers(20, 200, (6, 40)).astype(np.uint8)
+    B = r.integers(-100, 100, (40, 7)).astype(np.int8)
+    bz = r.integers(-20, 21, 7).astype(np.int32)
+    bs = r.uniform(0.01, 0.02, 7).astype(np.float32)
+    Y0, acc0 = oracle.qgemm(A, B, 0.05, 17, bs, bz, with_acc=True)
+    Y1, acc1 = oracle.qgemm((A + 33).astype(np.uint8), B, 0.05, 50, bs, bz, with_acc=True)
+    assert np.array_equal(acc0, acc1) and np.array_equal(Y0, Y1)
+    tcol = np.arange(7, dtype=np.int32) - 3
+    B2 = (B.astype(np.int32) + tcol[None, :]).astype(np.int8)
+    Y2, acc2 = oracle.qgemm(A, B2, 0.05, 17, bs, bz + tcol, with_acc=True)
+    assert np.array_equal(acc0, acc2) and np.array_equal(Y0, Y2)
+    # and a non-zero a_zp really enters: sum changes by -a_zp * column sums
+    _, acc3 = oracle.qgemm(A, B, 0.05, 18, bs, bz, with_acc=True)
+    colsum = (B.astype(np.int64) - bz[None, :]).sum(axis=0)
+    assert np.array_equal(acc0.astype(np.int64) - acc3, np.broadcast_to(colsum, acc0.shape))
+
+
+def test_qgemm_transposed_operands():
+    r = np.random.default_rng(42)
+    A, B = _q8(r, (5, 12), True), _q8(r, (12, 4), False)
+    args = dict(a_scale=0.1, a_zp=9, b_scale=np.float32([0.2, 0.3, 0.4, 0.5]),
+                b_zp=np.int32([1, -2, 3, 0]))
+    Y = oracle.qgemm(A, B, **args)
+    assert np.array_equal(oracle.qgemm(np.ascontiguousarray(A.T), B, transA=True, **args), Y)
+    assert np.array_equal(oracle.qgemm(A, np.ascontiguousarray(B.T), transB=True, **args), Y)
+    assert np.array_equal(oracle.qgemm(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T),
+                                       transA=True, transB=True, **args), Y)
+
+
+def test_qgemm_brute_force_with_c_broadcasts_alpha_and_bias():
+    # Python integers for the sums, numpy fp32 scalars in R17's order
+    r = np.random.default_rng(43)
+    M, N, K = 4, 5, 9
+    A, B = _q8(r, (M, K), False), _q8(r, (K, N), True)
+    a_scale, a_zp, alpha = np.float32(0.03), -5, np.float32(1.5)
+    bs = r.uniform(0.01, 0.05, N).astype(np.float32)
+    bz = r.integers(100, 156, N).astype(np.int32)
+    bias = r.uniform(-1, 1, N).astype(np.float32)
+    Cs = {"MN": r.integers(-500, 500, (M, N)), "N": r.integers(-500, 500, N),
+          "1N": r.integers(-500, 500, (1, N)), "M1": r.integers(-500, 500, (M, 1)),
+          "scalar": np.int64(321)}
+    for name, Cm in Cs.items():
+        Cb = np.broadcast_to(np.asarray(Cm, np.int64), (M, N))
+        Y, acc = oracle.qgemm(A, B, a_scale, a_zp, bs, bz, C=np.asarray(Cm, np.int32),
+                              alpha=alpha, bias=bias, with_acc=True)
+        sa = np.float32(alpha * a_scale)
+        for m in range(M):
+            for n in range(N):
+                s = sum((int(A[m, k]) - a_zp) * (int(B[k, n]) - int(bz[n])) for k in range(K))
+                s += int(Cb[m, n])
+                assert acc[m, n] == s, (name, m, n)
+                v = np.float32(np.float32(np.float32(s) * sa) * bs[n]) + bias[n]
+                assert Y[m, n] == np.float32(v), (name, m, n)
+
+
+def test_qgemm_requantized_output_ties_and_saturation():
+    # unit scales, y_scale 2: real / y_scale = sum / 2, a tie at every odd
+    # sum; K = 1 with B = 1 makes the sums the codes of A themselves
+    A = np.int8([[1], [3], [5], [-1], [-3], [100], [-128], [127]])
+    B = np.int8([[1]])
+    y = oracle.qgemm(A, B, 1.0, 0, 1.0, y_scale=2.0, y_zp=10, y_type="i8")
+    # sum/2 =      0.5  1.5  2.5  -0.5  -1.5  50   -64  63.5
+    want = np.int8([0, 2, 2, 0, -2, 50, -64, 64]) + 10
+    assert np.array_equal(y.ravel(), want.astype(np.int32).clip(-128, 127).astype(np.int8))
+    # saturation at both ends of uint8
+    y = oracle.qgemm(A, B, 1.0, 0, 1.0, y_scale=0.25, y_zp=128, y_type="u8")
+    assert y.ravel()[5] == 255 and y.ravel()[6] == 0
+
+
+def test_dynamic_quantize_matmul_per_tensor_hand_values():
+    # lo = -1, hi = 127/128: scale = (255/128)/255 = 1/128 exactly and
+    # zp = rne(128) = 128; q(x) = rne(128 x) + 128
+    A = np.float32([[-1.0, 127 / 128], [0.5, 3 / 256], [5 / 256, 0.0]])
+    sc, zp, q = oracle.quantize_tensor_u8(A)
+    assert sc == np.float32(1 / 128) and zp == 128
+    #                     -128+128  127+128  64+128  rne(1.5)=2  rne(2.5)=2  0+128
+    assert np.array_equal(q, np.uint8([[0, 255], [192, 130], [130, 128]]))
+    # all zeros: scale 1, zero point 0, codes 0 (R4 over the tensor)
+    sc, zp, q = oracle.quantize_tensor_u8(np.zeros((2, 3), np.float32))
+    assert sc == 1.0 and zp == 0 and not q.any()
+    # the composition: DynamicQuantizeMatMul = MatMulIntegerToFloat of the
+    # quantized tensor with its scale and zero point
+    r = np.random.default_rng(44)
+    A = r.normal(0, 1, (7, 33)).astype(np.float32)
+    B = _q8(r, (33, 6), False)
+    bs = r.uniform(0.01, 0.05, 6).astype(np.float32)
+    bias = r.uniform(-1, 1, 6).astype(np.float32)
+    sc, zp, q = oracle.quantize_tensor_u8(A)
+    assert q.max() == 255 or q.min() == 0
+    assert np.array_equal(oracle.dynamic_quantize_matmul(A, B, bs, bias=bias),
+                          oracle.matmul_integer_to_float(q, B, sc, bs, a_zp=zp, bias=bias))
+    # and it approximates the float product within the quantization error
+    exact = A.astype(np.float64) @ (B.astype(np.float64) * bs[None, :]) + bias
+    bound = 0.5 * float(sc) * np.abs(B.astype(np.float64) * bs[None, :]).sum(axis=0)
+    Y = oracle.dynamic_quantize_matmul(A, B, bs, bias=bias)
+    assert (np.abs(Y - exact) <= bound[None, :] * 1.001 + 1e-5).all()
