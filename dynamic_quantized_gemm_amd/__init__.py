@@ -14,4 +14,6 @@ from ._binding import (  # noqa: F401
     dqip_forward, dqip_forward_accumulators, dqip_info, dqip_init, dqip_internal_buffer_size,
     dqip_last_error, dqip_profile_begin, dqip_profile_end, dqip_read_quantized_a, dqip_read_quantized_b, dqip_release,
     dqip_set_params, exported_symbols, load, qlinear_conv1x1, qlinear_dequantize, qlinear_quantize,
+    DQ_QGEMM_K_MAX, dq_qgemm_forward, dq_qgemm_forward_accumulators, dq_qgemm_info, dq_qgemm_init,
+    dq_qgemm_release, dq_qgemm_set_b,
 )

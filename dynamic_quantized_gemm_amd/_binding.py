@@ -16,6 +16,7 @@ DQ_OK, DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_STATE, DQ_ERR_RANGE, DQ_ERR_ALLOC, DQ_ERR
     0, -1, -2, -3, -4, -5, -6)
 DQ_PER_TENSOR = -(2 ** 31)
 DQ_K_MAX = 65536
+DQ_QGEMM_K_MAX = 32768
 
 _lib = None
 
@@ -45,6 +46,18 @@ _SIGNATURES = {
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int64,
                                   C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                   C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dq_qgemm_init": (C.c_int, [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int,
+                                C.c_int, C.c_int, C.c_int, C.c_int, C.c_float]),
+    "dq_qgemm_set_b": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                 C.c_int64, C.c_void_p]),
+    "dq_qgemm_forward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_int64, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p]),
+    "dq_qgemm_forward_accumulators": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                                C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
+                                                C.c_void_p]),
+    "dq_qgemm_info": (C.c_char_p, [C.c_void_p]),
+    "dq_qgemm_release": (None, [C.c_void_p]),
 }
 
 
@@ -225,3 +238,54 @@ def qlinear_conv1x1(x, x_type, x_scale, x_zero_point, w, w_type, w_scale, w_zero
                                   _ptr(w), w_type, M, _ptr(w_scale), _ptr(w_zero_point), w_len,
                                   _ptr(y_scale), _ptr(y_zero_point), y_type, _ptr(bias), _ptr(y),
                                   _stream(stream)), "qlinear_conv1x1")
+
+
+# ------------------------------------------- QGemm / MatMulIntegerToFloat
+
+def dq_qgemm_init(M, N, K, a_type, transA, b_type, transB, y_type, alpha=1.0):
+    """Returns the context handle (an int)."""
+    h = C.c_void_p()
+    _check(load().dq_qgemm_init(C.byref(h), M, N, K, a_type, int(bool(transA)), b_type,
+                                int(bool(transB)), y_type, float(alpha)), "dq_qgemm_init")
+    return h.value
+
+
+def dq_qgemm_set_b(ctx, B, b_scale, b_zero_point=None, stream=None):
+    """B: 8-bit tensor ([K,N], or [N,K] with transB); b_scale: fp32 tensor of
+    1 or N values; b_zero_point: tensor of B's type (1 or N values) or None."""
+    bz_len = 0 if b_zero_point is None else int(b_zero_point.numel())
+    _check(load().dq_qgemm_set_b(ctx, _ptr(B), _ptr(b_scale), int(b_scale.numel()),
+                                 _ptr(b_zero_point), bz_len, _stream(stream)), "dq_qgemm_set_b")
+
+
+def _c_shape(C_):
+    if C_ is None:
+        return 0, 0
+    if C_.dim() <= 1:
+        return 1, int(C_.numel())
+    return int(C_.shape[0]), int(C_.shape[1])
+
+
+def dq_qgemm_forward(ctx, A, a_scale, a_zero_point, C_, bias, y_scale, y_zero_point, Y,
+                     stream=None):
+    """C_: int32 tensor of shape (), (N,), (1, N), (M, 1) or (M, N), or None."""
+    cr, cc = _c_shape(C_)
+    _check(load().dq_qgemm_forward(ctx, _ptr(A), _ptr(a_scale), _ptr(a_zero_point), _ptr(C_), cr,
+                                   cc, _ptr(bias), _ptr(y_scale), _ptr(y_zero_point), _ptr(Y),
+                                   _stream(stream)), "dq_qgemm_forward")
+
+
+def dq_qgemm_forward_accumulators(ctx, A, a_scale, a_zero_point, C_, acc, stream=None):
+    cr, cc = _c_shape(C_)
+    _check(load().dq_qgemm_forward_accumulators(ctx, _ptr(A), _ptr(a_scale), _ptr(a_zero_point),
+                                                _ptr(C_), cr, cc, _ptr(acc), _stream(stream)),
+           "dq_qgemm_forward_accumulators")
+
+
+def dq_qgemm_info(ctx):
+    r = load().dq_qgemm_info(ctx)
+    return r.decode() if r else None
+
+
+def dq_qgemm_release(ctx):
+    load().dq_qgemm_release(ctx)

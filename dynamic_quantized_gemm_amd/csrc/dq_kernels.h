@@ -41,11 +41,20 @@ int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, in
                          int8_t* iBp, float* scaleB, int32_t* colsum, uint32_t* amax,
                          hipStream_t s, DqTiming t = {});
 
+// 8-bit src [K, R] (row-major, R columns) -> packed [Rp x Kp]: column r of
+// src becomes packed row r, as int8 (uint8 codes minus 128), K padded with
+// zeros; sums[r] = sum over k of the packed codes.
+int dq_launch_pack_cols8(const void* src, bool u8, int K, int R, int Kp, int8_t* dst,
+                         int32_t* sums, hipStream_t s);
+
+// The quantized matrix products (qgemm.hip): packs of an 8-bit [R, K] source
+// by rows, and of an fp32 [M, K] tensor quantized per tensor to uint8.
+
 // Inspection: packed sA -> uA [M,K]; packed iBp -> iB [K,N].
 int dq_launch_unpack_a(const int8_t* sA, int M, int K, int Kp, uint8_t* uA, hipStream_t s);
 int dq_launch_unpack_b(const int8_t* iBp, int K, int N, int Kp, int8_t* iB, hipStream_t s);
 
-enum { DQ_OUT_F32 = 0, DQ_OUT_BF16 = 1, DQ_OUT_ACC = 2 };
+enum { DQ_OUT_F32 = 0, DQ_OUT_BF16 = 1, DQ_OUT_ACC = 2, DQ_OUT_U8 = 3, DQ_OUT_I8 = 4 };
 
 struct DqEpilogue {
     const float* scaleA;
@@ -57,9 +66,17 @@ struct DqEpilogue {
     float alpha;        // leaky-ReLU slope
     int out;            // DQ_OUT_*
     void* C;            // [M,N]
+    // optional terms of the quantized matrix products (all NULL for dqip):
+    const int32_t* rowsumA = nullptr;  // with zeroB: sum += rowsumA[i] * zeroB[j]
+    const int32_t* zeroB = nullptr;
+    const int32_t* addC = nullptr;     // int32 added to the sum, at i * c_rs + j * c_cs
+    long long c_rs = 0, c_cs = 0;
+    const float* y_scale = nullptr;    // DQ_OUT_U8 / DQ_OUT_I8: device scalar
+    const void* y_zp = nullptr;        // device scalar of the output's type (NULL: 0)
 };
 
-// acc = sA * iB + (128 - zeroA[i]) * colsumB[j], then the epilogue.
+// acc = sA * iB + (128 - zeroA[i]) * colsumB[j] (+ rowsumA[i] * zeroB[j])
+// (+ addC[i, j]), then the epilogue.
 int dq_launch_gemm(const int8_t* sA, const int8_t* iBp, int M, int N, int Kp,
                    const DqEpilogue& ep, hipStream_t s, DqTiming t = {});
 

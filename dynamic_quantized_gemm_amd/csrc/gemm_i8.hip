@@ -77,7 +77,7 @@ __device__ __forceinline__ float activate(float v, float alpha) {
     return v;
 }
 
-template <int WM, int WN, int FM, int FN, int KS, int OUT, int ACT, bool BIAS>
+template <int WM, int WN, int FM, int FN, int KS, int OUT, int ACT, bool BIAS, bool EXT>
 __global__ void __launch_bounds__(WM * WN * 64)
 k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int N, int KF,
        int tiles_m, int tiles_n, int vec_store, DqEpilogue ep) {
@@ -105,6 +105,9 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     __shared__ __attribute__((aligned(16))) float s_bias[BN];
     __shared__ float s_sa[BM];
     __shared__ int32_t s_za[BM];
+    // EXT (the quantized matrix products): B zero points against A's row sums
+    __shared__ int32_t s_rb[EXT ? BM : 1];
+    __shared__ __attribute__((aligned(16))) int32_t s_zb[EXT ? BN : 4];
 
     const int lane = threadIdx.x & 63;
     // wave-uniform values live in SGPRs: every fragment address is a scalar
@@ -138,6 +141,7 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     // row / column parameters of the tile (column vectors hold Np entries)
     for (int c = threadIdx.x; c < BN; c += NT) {
         s_cs[c] = ep.colsumB[n0 + c];
+        if (EXT) s_zb[c] = ep.zeroB ? ep.zeroB[n0 + c] : 0;
         if (OUT != DQ_OUT_ACC) {
             s_sb[c] = ep.scaleB[n0 + c];
             s_bias[c] = BIAS ? ep.bias[n0 + c] : 0.0f;
@@ -146,6 +150,7 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     for (int r = threadIdx.x; r < BM; r += NT) {
         const int row = min(m0 + r, M - 1);
         s_za[r] = ep.zeroA[row];
+        if (EXT) s_rb[r] = ep.rowsumA ? ep.rowsumA[row] : 0;
         if (OUT != DQ_OUT_ACC) s_sa[r] = ep.scaleA[row];
     }
 
@@ -263,7 +268,8 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     // groups are the outer loop, so each group's column parameters are read
     // from LDS once for all strips of the pass, and the strips give
     // independent work to hide the reads' latency.
-    constexpr int OB = OUT == DQ_OUT_BF16 ? 2 : 4;  // bytes per output
+    constexpr bool Q8 = OUT == DQ_OUT_U8 || OUT == DQ_OUT_I8;  // requantized 8-bit output
+    constexpr int OB = Q8 ? 1 : OUT == DQ_OUT_BF16 ? 2 : 4;    // bytes per output
     constexpr int RB = FN * 32 * OB;                // bytes per strip row
     constexpr int CPR = RB / 16;                    // 16-byte chunks per strip row
     constexpr int EPC = 16 / OB;                    // elements per chunk
@@ -274,28 +280,47 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     __syncthreads();  // every wave is done reading the stage buffers
     const int rs = lane & 31;  // row inside a strip
     const int col0 = n0 + wn * FN * 32;
+    // requantization of an 8-bit output: y = sat(rne(val / y_scale) + y_zp),
+    // with the corrected quotient where the scale allows it (as the
+    // quantizers round), the 1.5 * 2^23 rounding add, a median clamp against
+    // the saturation bounds minus the zero point, and the zero point added to
+    // four packed codes at once (carry-free bytewise add)
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    dq::QDiv yd = {1.0f, 1.0f, true};
+    int yz = 0;
+    float ylo = 0.0f, yhi = 0.0f;
+    if (Q8) {
+        yd = dq::make_qdiv(ep.y_scale[0]);
+        if (ep.y_zp) yz = OUT == DQ_OUT_U8 ? (int)*reinterpret_cast<const uint8_t*>(ep.y_zp)
+                                           : (int)*reinterpret_cast<const int8_t*>(ep.y_zp);
+        ylo = (float)((OUT == DQ_OUT_U8 ? 0 : -128) - yz);
+        yhi = (float)((OUT == DQ_OUT_U8 ? 255 : 127) - yz);
+    }
+    const uint32_t yZ = (uint32_t)(yz & 0xff) * 0x01010101u;
 #pragma clang loop unroll(full)
     for (int p0 = 0; p0 < FM; p0 += SPP) {
         // the correction (128 - zeroA) * colsum on the 24-bit multiplier (full
         // rate; a 32-bit product would take the quarter-rate 64-bit multiply-
         // add): |128 - zeroA| <= 128 and -2^23 <= colsum < 2^23 for K <= 65536,
         // so the product is exact and the wrapping add gives the exact sum
-        int za[SPP];
+        int za[SPP], rb[SPP];
         float sA[SPP];
 #pragma unroll
         for (int u = 0; u < SPP; ++u) {
             const int rt = (wm * FM + p0 + u) * 32 + rs;  // tile row
             za[u] = 128 - s_za[rt];
+            rb[u] = EXT ? s_rb[rt] : 0;
             sA[u] = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
         }
         // column groups jg = 4 j + g; each group's parameters are read from
         // LDS one group ahead, so their latency hides behind the previous
         // group's arithmetic
-        dq::v4i csv[2];
+        dq::v4i csv[2], zbv[2];
         dq::f4 sBv[2], bvv[2];
         auto params = [&](int jg, int set) {
             const int ct = wn * FN * 32 + (jg >> 2) * 32 + 8 * (jg & 3) + 4 * (lane >> 5);  // tile column
             csv[set] = *reinterpret_cast<const dq::v4i*>(&s_cs[ct]);
+            if (EXT) zbv[set] = *reinterpret_cast<const dq::v4i*>(&s_zb[ct]);
             if (OUT != DQ_OUT_ACC) sBv[set] = *reinterpret_cast<const dq::f4*>(&s_sb[ct]);
             if (OUT != DQ_OUT_ACC && BIAS) bvv[set] = *reinterpret_cast<const dq::f4*>(&s_bias[ct]);
         };
@@ -319,6 +344,24 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                         sum[e] = (int32_t)((uint32_t)(kAgpr ? dq::acc_read(acc[p0 + u][j][4 * g + e])
                                                              : acc[p0 + u][j][4 * g + e]) +
                                            (uint32_t)__mul24(za[u], cs[e]));
+                    if (EXT) {
+                        // B zero points: + rowsumA[i] * zb[j], where rowsumA holds
+                        // sum_k A^[i,k] + K * (shift - a_zp), |.| <= 255 K < 2^23
+                        // for K <= 32768, and |zb| <= 255: exact on the 24-bit
+                        // multiplier; then the int32 C, broadcast through its
+                        // strides (wrapping adds)
+                        const dq::v4i zb = zbv[set];
+                        const int row = min(m0 + (wm * FM + p0 + u) * 32 + rs, M - 1);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            sum[e] = (int32_t)((uint32_t)sum[e] + (uint32_t)__mul24(rb[u], zb[e]));
+                            if (ep.addC) {
+                                const int col = min(col0 + cs_ + e, N - 1);
+                                sum[e] = (int32_t)((uint32_t)sum[e] +
+                                                   (uint32_t)ep.addC[(long long)row * ep.c_rs + (long long)col * ep.c_cs]);
+                            }
+                        }
+                    }
                     int8_t* dst = region + u * SB + rs * RB + (((byte >> 4) ^ (rs & (CPR - 1))) << 4) + (byte & 15);
                     if (OUT == DQ_OUT_ACC) {
                         const dq::v4i v = {sum[0], sum[1], sum[2], sum[3]};
@@ -332,10 +375,30 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                             if (BIAS) v = v + bv[e];
                             val[e] = activate<ACT>(v, ep.alpha);
                         }
-                        if (OUT == DQ_OUT_BF16)
+                        if (Q8) {
+                            uint32_t b[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float t;
+                                if (yd.fast) {
+                                    const float q0 = __builtin_amdgcn_fmed3f(val[e] * yd.y, -4194304.0f, 4194304.0f);
+                                    const float r = __builtin_fmaf(-q0, yd.s, val[e]);
+                                    t = __builtin_amdgcn_fmed3f(__builtin_fmaf(r, yd.y, q0) + kMagic,
+                                                                kMagic + ylo, kMagic + yhi);
+                                } else {
+                                    t = kMagic + __builtin_fminf(__builtin_fmaxf(dq::rne(val[e] / yd.s), ylo), yhi);
+                                }
+                                b[e] = (uint32_t)__float_as_int(t);
+                            }
+                            const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) |
+                                                    ((b[2] & 0xffu) << 16) | (b[3] << 24);
+                            *reinterpret_cast<uint32_t*>(dst) =
+                                ((packed & 0x7f7f7f7fu) + (yZ & 0x7f7f7f7fu)) ^ ((packed ^ yZ) & 0x80808080u);
+                        } else if (OUT == DQ_OUT_BF16) {
                             *reinterpret_cast<dq::u2*>(dst) = dq::f32x4_to_bf16x4(val);
-                        else
+                        } else {
                             *reinterpret_cast<dq::f4*>(dst) = val;
+                        }
                     }
                 }
                 // one column group at a time: keeps the accumulator reads of
@@ -361,7 +424,9 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                     for (int e = 0; e < EPC; ++e) {
                         if (col + e < N) {
                             const uint32_t w = (uint32_t)v[(e * OB) >> 2];
-                            if (OB == 2)
+                            if (OB == 1)
+                                reinterpret_cast<uint8_t*>(C)[e] = (uint8_t)(w >> (8 * (e & 3)));
+                            else if (OB == 2)
                                 reinterpret_cast<uint16_t*>(C)[e] = (uint16_t)(w >> (16 * (e & 1)));
                             else
                                 reinterpret_cast<uint32_t*>(C)[e] = w;
@@ -373,10 +438,10 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     }
 }
 
-template <int WM, int WN, int FM, int FN, int KS, int OUT, int ACT, bool BIAS>
+template <int WM, int WN, int FM, int FN, int KS, int OUT, int ACT, bool BIAS, bool EXT = false>
 void launch_one(dim3 grid, hipStream_t s, DqTiming t, const int8_t* Ap, const int8_t* Bp, int M,
                 int N, int KF, int tiles_m, int tiles_n, int vec_store, const DqEpilogue& ep) {
-    hipExtLaunchKernelGGL((k_gemm<WM, WN, FM, FN, KS, OUT, ACT, BIAS>), grid, dim3(WM * WN * 64), 0,
+    hipExtLaunchKernelGGL((k_gemm<WM, WN, FM, FN, KS, OUT, ACT, BIAS, EXT>), grid, dim3(WM * WN * 64), 0,
                           s, t.start, t.stop, 0, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
 }
 
@@ -403,10 +468,34 @@ int launch(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpi
     const size_t tiles = (size_t)tiles_m * tiles_n;
     if (tiles > 0x7fffffffu) DQ_FAIL(DQ_ERR_ARG, "problem too large for one launch");
     // whole 16-byte chunks of C rows: 8 bf16 or 4 fp32 / int32 per chunk
-    const int ob = ep.out == DQ_OUT_BF16 ? 2 : 4;
+    const int ob = (ep.out == DQ_OUT_U8 || ep.out == DQ_OUT_I8) ? 1 : ep.out == DQ_OUT_BF16 ? 2 : 4;
     const int vec_store = (uintptr_t)ep.C % 16 == 0 && ((size_t)N * ob) % 16 == 0;
     const dim3 grid((unsigned)tiles);
     const int KF = Kp / 32;
+    // the quantized matrix products: B zero points, int32 C and 8-bit output
+    // (identity activation); the inner product takes the plain epilogue
+    if (ep.rowsumA || ep.zeroB || ep.addC || ep.out == DQ_OUT_U8 || ep.out == DQ_OUT_I8) {
+        const bool bias = ep.bias != nullptr;
+        switch (ep.out) {
+            case DQ_OUT_U8:
+                launch_one<WM, WN, FM, FN, KS, DQ_OUT_U8, DQ_ACT_IDENTITY, false, true>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+                break;
+            case DQ_OUT_I8:
+                launch_one<WM, WN, FM, FN, KS, DQ_OUT_I8, DQ_ACT_IDENTITY, false, true>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+                break;
+            case DQ_OUT_ACC:
+                launch_one<WM, WN, FM, FN, KS, DQ_OUT_ACC, DQ_ACT_IDENTITY, false, true>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+                break;
+            default:
+                if (bias)
+                    launch_one<WM, WN, FM, FN, KS, DQ_OUT_F32, DQ_ACT_IDENTITY, true, true>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+                else
+                    launch_one<WM, WN, FM, FN, KS, DQ_OUT_F32, DQ_ACT_IDENTITY, false, true>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);
+                break;
+        }
+        DQ_LAUNCH_CHECK("gemm_i8");
+        return DQ_OK;
+    }
     switch (ep.out) {
         case DQ_OUT_ACC:
             launch_one<WM, WN, FM, FN, KS, DQ_OUT_ACC, DQ_ACT_IDENTITY, false>(grid, s, t, Ap, Bp, M, N, KF, tiles_m, tiles_n, vec_store, ep);

@@ -1,0 +1,546 @@
+// qgemm.hip -- the quantized matrix products of the onnxruntime schemas
+// QGemm, MatMulIntegerToFloat and DynamicQuantizeMatMul on gfx950.
+//
+// onnxruntime quantization_defs.cc gives these operators' inputs, types and
+// attributes but prints no formula; this library computes (the readings are
+// stated where the operators are declared, include/dqip.h):
+//   sum[m,n] = sum_k (A[m,k] - a_zp) * (B[k,n] - b_zp[n])   (exact, int32)
+//   real     = ((float)(sum + C[m,n]) * (alpha * a_scale)) * b_scale[n] (+ bias[n])
+//   Y        = real, or saturate(rne(real / y_scale) + y_zp) for an 8-bit Y,
+// with b_scale / b_zp per tensor or per column, A given as (K,M) under transA
+// and B as (N,K) under transB, and for DynamicQuantizeMatMul A (fp32)
+// quantized per tensor to uint8 first, with the row quantizer's rule over
+// the whole tensor: lo = min(0, min A), hi = max(0, max A),
+// scale = (hi - lo) / 255, zp = saturate(rne(-lo / scale)).
+//
+// The products run on the int8 GEMM of gemm_i8.hip. A uint8 operand enters
+// as code - 128 (shift s = 128, 0 for int8), so with A^ = A - sa and
+// B^ = B - sb:
+//   sum = sum_k A^ B^ + (sa - a_zp) * colsum(B^)[n]
+//         + (sb - b_zp[n]) * (rowsum(A^)[m] + K * (sa - a_zp)),
+// all in wrapping int32 (exact whenever the true sum fits, which K <= 32768
+// guarantees). The GEMM takes the first correction from its zeroA / colsum
+// vectors (zeroA = a_zp + 128 - sa) and the second from rowsumA / zeroB.
+//
+// Kernels here:
+//  - k_pack_rows<SRC>: an [R, K] source (int8, uint8, or fp32 quantized per
+//    tensor) to packed MFMA fragments, with the row sums of the packed codes
+//    and, for A, the per-row epilogue vectors. Lane (r = lane % 8, j =
+//    lane / 8) of a wave takes 16-code group 8 * (8 it + w) + j of row r of
+//    the block's eight rows, so one store instruction writes eight whole
+//    128-byte lines of the packed operand (each line holds one group of
+//    eight consecutive rows) and one 8-bit load instruction reads eight
+//    whole 128-byte row segments.
+//  - k_tensor_minmax: the per-tensor min / max of an fp32 A (atomics on an
+//    order-preserving integer encoding of the fp32 bits), 0 included.
+//  - k_a_params / k_b_params: per-row and per-column vectors for the GEMM.
+// Transposed 8-bit sources (A under transA, B without transB) go through the
+// column packer of quant_cols.hip.
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "dq_device.h"
+#include "dq_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+enum { SRC_I8 = 0, SRC_U8 = 1, SRC_F32 = 2 };
+
+// fp32 <-> an unsigned integer with the same order (atomicMin / atomicMax)
+__device__ __forceinline__ uint32_t f2ord(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Per-tensor quantization parameters from the min / max words (the row
+// quantizer's rule over the whole tensor).
+__device__ __forceinline__ void tensor_params(const uint32_t* mm, float& scale, int& zero) {
+    const float lo = ord2f(mm[0]), hi = ord2f(mm[1]);
+    if (hi == lo) {
+        scale = 1.0f;
+        zero = 0;
+    } else {
+        scale = (hi - lo) / 255.0f;
+        zero = dq::sat_add(dq::rne(-lo / scale), 0, 0, 255);
+    }
+}
+
+__device__ __forceinline__ int load_zp8(const void* zp, bool u8) {
+    if (!zp) return 0;
+    return u8 ? (int)*reinterpret_cast<const uint8_t*>(zp) : (int)*reinterpret_cast<const int8_t*>(zp);
+}
+
+__global__ void k_minmax_init(uint32_t* mm) {
+    if (threadIdx.x < 2) mm[threadIdx.x] = 0x80000000u;  // the encoding of +0.0
+}
+
+// Min / max of n fp32 values (0 included through the initial words).
+template <bool VEC>
+__global__ void __launch_bounds__(256) k_tensor_minmax(const float* __restrict__ A, size_t n,
+                                                        uint32_t* __restrict__ mm) {
+    float lo = 0.0f, hi = 0.0f;
+    const size_t stride = (size_t)gridDim.x * 256;
+    if (VEC) {
+        const dq::f4* a4 = reinterpret_cast<const dq::f4*>(A);
+        for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4; i += stride) {
+            const dq::f4 v = a4[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo = __builtin_fminf(lo, v[e]);
+                hi = __builtin_fmaxf(hi, v[e]);
+            }
+        }
+    } else {
+        for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+            lo = __builtin_fminf(lo, A[i]);
+            hi = __builtin_fmaxf(hi, A[i]);
+        }
+    }
+    lo = dq::wave_min_uniform(lo);
+    hi = dq::wave_max_uniform(hi);
+    if ((threadIdx.x & 63) == 0) {
+        atomicMin(&mm[0], f2ord(lo));
+        atomicMax(&mm[1], f2ord(hi));
+    }
+}
+
+// What k_pack_rows writes besides the packed codes when it packs A (zeroA
+// NULL: a B operand, sums only).
+struct RowOut {
+    int32_t* sums;      // [R]: row sum of the packed codes (+ K * (sa - a_zp) for A)
+    int32_t* zeroA;     // [R]: a_zp + 128 - sa
+    float* scaleA;      // [R]: alpha * a_scale
+    const float* a_scale;
+    const void* a_zp;   // device scalar of A's type (NULL: 0)
+    const uint32_t* mm; // SRC_F32: the tensor's min / max words
+    float alpha;
+};
+
+// 16 codes of group g of row `row` (zero past K or past R), as packed int8.
+template <int SRC, bool VEC>
+__device__ __forceinline__ dq::u4 load_group(const void* __restrict__ src, int R, int K, int row, int g,
+                                             const dq::QDiv& d, int zero) {
+    const int k0 = 16 * g;
+    dq::u4 o = {0u, 0u, 0u, 0u};
+    if (row >= R || k0 >= K) return o;
+    if (SRC != SRC_F32) {
+        const uint8_t* p = reinterpret_cast<const uint8_t*>(src) + (size_t)row * K + k0;
+        if (VEC) {
+            o = *reinterpret_cast<const dq::u4*>(p);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (k0 + e < K) o[e >> 2] |= (uint32_t)p[e] << (8 * (e & 3));
+        }
+        if (SRC == SRC_U8) {
+            // code - 128 as int8 is the code with its top bit flipped; bytes
+            // past K stay zero
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t m = 0x80808080u;
+                if (!VEC) {
+                    const int kq = k0 + 4 * q;
+                    m = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (kq + e < K) m |= 0x80u << (8 * e);
+                }
+                o[q] ^= m;
+            }
+        }
+        return o;
+    }
+    // fp32, quantized with the tensor's scale / zero point to uint8 and
+    // packed as code - 128 (corrected quotient, rounding add, median clamp,
+    // as the row quantizer); bytes past K stay zero
+    const float* p = reinterpret_cast<const float*>(src) + (size_t)row * K + k0;
+    float x[16];
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const dq::f4 v = reinterpret_cast<const dq::f4*>(p)[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = k0 + e < K ? p[e] : 0.0f;
+    }
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const float lof = kMagic - (float)zero, hif = kMagic + (float)(255 - zero);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + 4 * q + e;
+            uint32_t code;  // uA in [0, 255]
+            if (d.fast) {
+                const float t = dq::qdiv_fast(x[4 * q + e], d) + kMagic;
+                code = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t, lof, hif)) + (uint32_t)zero;
+            } else {
+                code = (uint32_t)dq::sat_add(dq::rne(x[4 * q + e] / d.s), zero, 0, 255);
+            }
+            if (VEC || k < K) w |= ((code & 0xffu) ^ 0x80u) << (8 * e);
+        }
+        o[q] = w;
+    }
+    return o;
+}
+
+// A block packs rows 8 b .. 8 b + 7 over all of Kp (padding groups are
+// zero). Rows past R are packed as zeros (the buffer holds Rp rows).
+template <int SRC, bool VEC>
+__global__ void __launch_bounds__(256)
+k_pack_rows(const void* __restrict__ src, int R, int K, int Kp, int8_t* __restrict__ dst, RowOut out) {
+    __shared__ int32_t s_sum[4][8];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 7, j = lane >> 3;
+    const int row = 8 * blockIdx.x + r;
+    const int KF = Kp / 32, ngp = Kp / 16;
+    dq::QDiv d = {1.0f, 1.0f, true};
+    int zero = 0;
+    if (SRC == SRC_F32) {
+        float scale;
+        tensor_params(out.mm, scale, zero);
+        d = dq::make_qdiv(scale);
+    }
+    int sum = 0;
+#pragma unroll 4
+    for (int g = 8 * w + j; g < ngp; g += 32) {
+        const dq::u4 o = load_group<SRC, VEC>(src, R, K, row, g, d, zero);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum = __builtin_amdgcn_sdot4((int)o[q], 0x01010101, sum, false);
+        *reinterpret_cast<dq::u4*>(dst + dq::frag_offset((size_t)row, (size_t)g * 16, (size_t)KF)) = o;
+    }
+    // the row's sum: lanes r, r + 8, ..., r + 56 of each wave, then the waves
+    sum += __shfl_xor(sum, 8, 64);
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    if (j == 0) s_sum[w][r] = sum;
+    __syncthreads();
+    if (threadIdx.x < 8 && row < R) {
+        int total = s_sum[0][r] + s_sum[1][r] + s_sum[2][r] + s_sum[3][r];
+        if (out.zeroA) {
+            // A: the per-row vectors of the GEMM's epilogue
+            int azp, sa;
+            float ascale;
+            if (SRC == SRC_F32) {
+                tensor_params(out.mm, ascale, azp);  // the scale and zero point used above
+                sa = 128;
+            } else {
+                azp = load_zp8(out.a_zp, SRC == SRC_U8);
+                sa = SRC == SRC_U8 ? 128 : 0;
+                ascale = out.a_scale[0];
+            }
+            total = (int)((uint32_t)total + (uint32_t)K * (uint32_t)(sa - azp));
+            out.zeroA[row] = azp + 128 - sa;
+            out.scaleA[row] = out.alpha * ascale;
+        }
+        out.sums[row] = total;
+    }
+}
+
+// A packed by the column packer (transA): sums hold the row sums of the
+// packed codes; add K * (sa - a_zp) and write the per-row vectors.
+__global__ void __launch_bounds__(256)
+k_a_params(int M, int K, bool u8, const float* __restrict__ a_scale, const void* __restrict__ a_zp,
+           float alpha, int32_t* __restrict__ sums, int32_t* __restrict__ zeroA, float* __restrict__ scaleA) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= M) return;
+    const int azp = load_zp8(a_zp, u8), sa = u8 ? 128 : 0;
+    sums[i] = (int)((uint32_t)sums[i] + (uint32_t)K * (uint32_t)(sa - azp));
+    zeroA[i] = azp + 128 - sa;
+    scaleA[i] = alpha * a_scale[0];
+}
+
+// Per-column vectors of B for j < Np: scaleB, zb = sb - b_zp (zero past N).
+__global__ void __launch_bounds__(256)
+k_b_params(int N, int Np, bool u8, const float* __restrict__ b_scale, int bs_len,
+           const void* __restrict__ b_zp, int bz_len, float* __restrict__ scaleB, int32_t* __restrict__ zb) {
+    const int jj = blockIdx.x * 256 + threadIdx.x;
+    if (jj >= Np) return;
+    if (jj >= N) {
+        scaleB[jj] = 0.0f;
+        zb[jj] = 0;
+        return;
+    }
+    scaleB[jj] = b_scale[bs_len == 1 ? 0 : jj];
+    int z = 0;
+    if (b_zp) {
+        const int k = bz_len == 1 ? 0 : jj;
+        z = u8 ? (int)reinterpret_cast<const uint8_t*>(b_zp)[k] : (int)reinterpret_cast<const int8_t*>(b_zp)[k];
+    }
+    zb[jj] = (u8 ? 128 : 0) - z;
+}
+
+template <int SRC>
+int launch_pack_rows(const void* src, int R, int K, int Kp, int8_t* dst, const RowOut& out, hipStream_t s) {
+    const size_t esz = SRC == SRC_F32 ? 4 : 1;
+    const bool vec = K % 16 == 0 && (uintptr_t)src % 16 == 0 && (esz * (size_t)K) % 16 == 0;
+    const dim3 grid((unsigned)((R + 7) / 8));
+    if (vec)
+        hipLaunchKernelGGL((k_pack_rows<SRC, true>), grid, dim3(256), 0, s, src, R, K, Kp, dst, out);
+    else
+        hipLaunchKernelGGL((k_pack_rows<SRC, false>), grid, dim3(256), 0, s, src, R, K, Kp, dst, out);
+    DQ_LAUNCH_CHECK("pack_rows");
+    return DQ_OK;
+}
+
+const char* tname(dq_dtype t) {
+    switch (t) {
+        case DQ_F32: return "f32";
+        case DQ_BF16: return "bf16";
+        case DQ_I8: return "i8";
+        case DQ_U8: return "u8";
+    }
+    return "?";
+}
+
+}  // namespace
+
+struct dq_qgemm_ctx {
+    int device;
+    int M, N, K, Kp;
+    dq_dtype a_type, b_type, y_type;
+    int transA, transB;
+    float alpha;
+    int b_set;
+    int zb_any;          // some column has sb - b_zp != 0
+    std::vector<void*> owned;
+    // B (set once)
+    int8_t* Bp;          // [Np x Kp]
+    int32_t* colsum;     // [Np]
+    float* scaleB;       // [Np]
+    int32_t* zb;         // [Np]
+    float* biasv;        // [Np]: a forward's bias, zero past N
+    // per forward
+    int8_t* Ap;          // [Mp x Kp]
+    int32_t* rowsum;     // [Mp]
+    int32_t* zeroA;      // [Mp]
+    float* scaleA;       // [Mp]
+    uint32_t* mm;        // 2 words: per-tensor min / max (fp32 A)
+    std::string info;
+};
+
+namespace {
+
+int ctx_alloc(dq_qgemm_ctx* c, void** p, size_t bytes) {
+    hipError_t e = hipMalloc(p, bytes ? bytes : 1);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        DQ_FAIL(DQ_ERR_ALLOC, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    }
+    c->owned.push_back(*p);
+    return DQ_OK;
+}
+
+void ctx_free(dq_qgemm_ctx* c) {
+    for (void* p : c->owned) (void)hipFree(p);
+    c->owned.clear();
+}
+
+int check_device(const dq_qgemm_ctx* c) {
+    int dev = -1;
+    DQ_HIP_CHECK(hipGetDevice(&dev));
+    if (dev != c->device)
+        DQ_FAIL(DQ_ERR_STATE, "context was created on device %d, current device is %d", c->device, dev);
+    return DQ_OK;
+}
+
+int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, const int32_t* Cm,
+        int64_t c_rows, int64_t c_cols, const float* bias, const float* y_scale, const void* y_zp,
+        void* Y, int mode, hipStream_t s) {
+    if (!c) DQ_FAIL(DQ_ERR_STATE, "context is NULL");
+    if (!c->b_set) DQ_FAIL(DQ_ERR_STATE, "dq_qgemm_set_b has not been called");
+    if (!A || !Y) DQ_FAIL(DQ_ERR_ARG, "A and Y must not be NULL");
+    if (c->a_type == DQ_F32) {
+        if (a_scale || a_zp) DQ_FAIL(DQ_ERR_ARG, "an fp32 A is quantized by the call: a_scale and a_zero_point must be NULL");
+    } else if (!a_scale) {
+        DQ_FAIL(DQ_ERR_ARG, "a_scale is NULL");
+    }
+    if (Cm && !((c_rows == 1 || c_rows == c->M) && (c_cols == 1 || c_cols == c->N)))
+        DQ_FAIL(DQ_ERR_ARG, "C of shape (%lld, %lld) does not broadcast to (%d, %d)", (long long)c_rows,
+                (long long)c_cols, c->M, c->N);
+    if (bias && (mode != DQ_OUT_F32 && mode != DQ_OUT_ACC))
+        DQ_FAIL(DQ_ERR_ARG, "bias is only defined for an fp32 Y");
+    const bool q8 = mode == DQ_OUT_U8 || mode == DQ_OUT_I8;
+    if (q8 && !y_scale) DQ_FAIL(DQ_ERR_ARG, "an 8-bit Y needs y_scale");
+    if (!q8 && (y_scale || y_zp)) DQ_FAIL(DQ_ERR_ARG, "y_scale / y_zero_point are only defined for an 8-bit Y");
+    int rc = check_device(c);
+    if (rc) return rc;
+    const int M = c->M, N = c->N, K = c->K, Kp = c->Kp;
+    // A -> packed, row sums and per-row vectors
+    if (c->a_type == DQ_F32) {
+        const size_t n = (size_t)M * K;
+        hipLaunchKernelGGL(k_minmax_init, dim3(1), dim3(64), 0, s, c->mm);
+        const bool vec = (uintptr_t)A % 16 == 0 && n % 4 == 0;
+        const size_t need = (vec ? n / 4 : n + 255) / 256 + 1;
+        const unsigned blocks = (unsigned)(need < 2048 ? need : 2048);
+        if (vec)
+            hipLaunchKernelGGL((k_tensor_minmax<true>), dim3(blocks), dim3(256), 0, s, (const float*)A, n, c->mm);
+        else
+            hipLaunchKernelGGL((k_tensor_minmax<false>), dim3(blocks), dim3(256), 0, s, (const float*)A, n, c->mm);
+        DQ_LAUNCH_CHECK("tensor_minmax");
+        RowOut o{c->rowsum, c->zeroA, c->scaleA, nullptr, nullptr, c->mm, c->alpha};
+        rc = launch_pack_rows<SRC_F32>(A, M, K, Kp, c->Ap, o, s);
+    } else if (!c->transA) {
+        RowOut o{c->rowsum, c->zeroA, c->scaleA, a_scale, a_zp, nullptr, c->alpha};
+        rc = c->a_type == DQ_U8 ? launch_pack_rows<SRC_U8>(A, M, K, Kp, c->Ap, o, s)
+                                : launch_pack_rows<SRC_I8>(A, M, K, Kp, c->Ap, o, s);
+    } else {
+        rc = dq_launch_pack_cols8(A, c->a_type == DQ_U8, K, M, Kp, c->Ap, c->rowsum, s);
+        if (!rc) {
+            hipLaunchKernelGGL(k_a_params, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, M, K,
+                               c->a_type == DQ_U8, a_scale, a_zp, c->alpha, c->rowsum, c->zeroA, c->scaleA);
+            DQ_LAUNCH_CHECK("a_params");
+        }
+    }
+    if (rc) return rc;
+    if (bias) DQ_HIP_CHECK(hipMemcpyAsync(c->biasv, bias, 4 * (size_t)N, hipMemcpyDeviceToDevice, s));
+    DqEpilogue ep;
+    ep.scaleA = c->scaleA;
+    ep.zeroA = c->zeroA;
+    ep.scaleB = c->scaleB;
+    ep.colsumB = c->colsum;
+    ep.bias = bias ? c->biasv : nullptr;
+    ep.act = DQ_ACT_IDENTITY;
+    ep.alpha = 0.0f;
+    ep.out = mode;
+    ep.C = Y;
+    if (c->zb_any) {
+        ep.rowsumA = c->rowsum;
+        ep.zeroB = c->zb;
+    }
+    if (Cm) {
+        ep.addC = Cm;
+        ep.c_rs = c_rows == 1 ? 0 : c_cols;
+        ep.c_cs = c_cols == 1 ? 0 : 1;
+    }
+    ep.y_scale = y_scale;
+    ep.y_zp = y_zp;
+    return dq_launch_gemm(c->Ap, c->Bp, M, N, Kp, ep, s);
+}
+
+}  // namespace
+
+extern "C" int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K, dq_dtype a_type,
+                             int transA, dq_dtype b_type, int transB, dq_dtype y_type, float alpha) {
+    if (!ctx) DQ_FAIL(DQ_ERR_ARG, "ctx is NULL");
+    *ctx = nullptr;
+    if (M < 1 || N < 1 || K < 1) DQ_FAIL(DQ_ERR_ARG, "M, N, K must be >= 1");
+    if (M > 0x7fffffff - 256 || N > 0x7fffffff - 256) DQ_FAIL(DQ_ERR_RANGE, "M and N must fit in int32");
+    if (K > DQ_QGEMM_K_MAX) DQ_FAIL(DQ_ERR_RANGE, "K = %lld exceeds %d (int32 sums)", (long long)K, DQ_QGEMM_K_MAX);
+    if (a_type != DQ_F32 && a_type != DQ_U8 && a_type != DQ_I8) DQ_FAIL(DQ_ERR_TYPE, "a_type must be f32, u8 or i8");
+    if (a_type == DQ_F32 && transA) DQ_FAIL(DQ_ERR_ARG, "transA is defined for an 8-bit A only");
+    if (b_type != DQ_U8 && b_type != DQ_I8) DQ_FAIL(DQ_ERR_TYPE, "b_type must be u8 or i8");
+    if (y_type != DQ_F32 && y_type != DQ_U8 && y_type != DQ_I8) DQ_FAIL(DQ_ERR_TYPE, "y_type must be f32, u8 or i8");
+    dq_qgemm_ctx* c = new dq_qgemm_ctx();
+    int rc = DQ_OK;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        DQ_FAIL(DQ_ERR_HIP, "hipGetDevice failed");
+    }
+    c->M = (int)M;
+    c->N = (int)N;
+    c->K = (int)K;
+    c->Kp = (int)dq_kp((size_t)K);
+    c->a_type = a_type;
+    c->b_type = b_type;
+    c->y_type = y_type;
+    c->transA = transA ? 1 : 0;
+    c->transB = transB ? 1 : 0;
+    c->alpha = alpha;
+    const size_t Mp = dq_mnp((size_t)M), Np = dq_mnp((size_t)N), Kp = (size_t)c->Kp;
+    if (!rc) rc = ctx_alloc(c, (void**)&c->Bp, Np * Kp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->colsum, 4 * Np);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->scaleB, 4 * Np);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->zb, 4 * Np);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->biasv, 4 * Np);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->Ap, Mp * Kp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->rowsum, 4 * Mp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->zeroA, 4 * Mp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->scaleA, 4 * Mp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->mm, kAlign);
+    if (!rc && hipMemset(c->biasv, 0, 4 * Np) != hipSuccess) rc = DQ_ERR_HIP;
+    if (rc) {
+        ctx_free(c);
+        delete c;
+        return rc;
+    }
+    char buf[320];
+    snprintf(buf, sizeof buf, "gfx950 qgemm A:%s%s%s B:%s%s Y:%s | %s", tname(a_type),
+             a_type == DQ_F32 ? " (quantized per tensor to u8)" : "", transA ? " transposed" : "",
+             tname(b_type), transB ? " transposed" : "", tname(y_type),
+             dq_gemm_info((int)M, (int)N, c->Kp));
+    c->info = buf;
+    *ctx = c;
+    return DQ_OK;
+}
+
+extern "C" int dq_qgemm_set_b(dq_qgemm_ctx* c, const void* B, const float* b_scale, int64_t b_scale_len,
+                              const void* b_zero_point, int64_t b_zero_point_len, void* stream) {
+    if (!c) DQ_FAIL(DQ_ERR_STATE, "context is NULL");
+    if (!B || !b_scale) DQ_FAIL(DQ_ERR_ARG, "B and b_scale must not be NULL");
+    if (b_scale_len != 1 && b_scale_len != c->N) DQ_FAIL(DQ_ERR_ARG, "b_scale must have 1 or N entries");
+    if (b_zero_point && b_zero_point_len != 1 && b_zero_point_len != c->N)
+        DQ_FAIL(DQ_ERR_ARG, "b_zero_point must have 1 or N entries");
+    int rc = check_device(c);
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const int N = c->N, K = c->K, Kp = c->Kp;
+    const bool u8 = c->b_type == DQ_U8;
+    if (c->transB) {
+        RowOut o{c->colsum, nullptr, nullptr, nullptr, nullptr, nullptr, 1.0f};
+        rc = u8 ? launch_pack_rows<SRC_U8>(B, N, K, Kp, c->Bp, o, s)
+                : launch_pack_rows<SRC_I8>(B, N, K, Kp, c->Bp, o, s);
+    } else {
+        rc = dq_launch_pack_cols8(B, u8, K, N, Kp, c->Bp, c->colsum, s);
+    }
+    if (rc) return rc;
+    const int Np = (int)dq_mnp((size_t)N);
+    hipLaunchKernelGGL(k_b_params, dim3((unsigned)((Np + 255) / 256)), dim3(256), 0, s, N, Np, u8, b_scale,
+                       (int)b_scale_len, b_zero_point, (int)b_zero_point_len, c->scaleB, c->zb);
+    DQ_LAUNCH_CHECK("b_params");
+    // whether any column's sb - b_zp is non-zero (decides the row-sum term)
+    std::vector<int32_t> hz((size_t)N);
+    DQ_HIP_CHECK(hipMemcpyAsync(hz.data(), c->zb, 4 * (size_t)N, hipMemcpyDeviceToHost, s));
+    DQ_HIP_CHECK(hipStreamSynchronize(s));
+    c->zb_any = 0;
+    for (int32_t z : hz) c->zb_any |= z != 0;
+    c->b_set = 1;
+    return DQ_OK;
+}
+
+extern "C" int dq_qgemm_forward(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zero_point,
+                                const int32_t* C, int64_t c_rows, int64_t c_cols, const float* bias,
+                                const float* y_scale, const void* y_zero_point, void* Y, void* stream) {
+    if (!c) DQ_FAIL(DQ_ERR_STATE, "context is NULL");
+    const int mode = c->y_type == DQ_U8 ? DQ_OUT_U8 : c->y_type == DQ_I8 ? DQ_OUT_I8 : DQ_OUT_F32;
+    return run(c, A, a_scale, a_zero_point, C, c_rows, c_cols, bias, y_scale, y_zero_point, Y, mode,
+               (hipStream_t)stream);
+}
+
+extern "C" int dq_qgemm_forward_accumulators(dq_qgemm_ctx* c, const void* A, const float* a_scale,
+                                             const void* a_zero_point, const int32_t* C, int64_t c_rows,
+                                             int64_t c_cols, int32_t* acc, void* stream) {
+    return run(c, A, a_scale, a_zero_point, C, c_rows, c_cols, nullptr, nullptr, nullptr, acc, DQ_OUT_ACC,
+               (hipStream_t)stream);
+}
+
+extern "C" const char* dq_qgemm_info(const dq_qgemm_ctx* c) { return c ? c->info.c_str() : nullptr; }
+
+extern "C" void dq_qgemm_release(dq_qgemm_ctx* c) {
+    if (!c) return;
+    ctx_free(c);
+    delete c;
+}

@@ -118,7 +118,8 @@ k_col_absmax_v4(const void* __restrict__ B, int K, int N, uint32_t* __restrict__
     if (j < N) atomicMax(&amax[j], __float_as_uint(mm));
 }
 
-// One 64(k) x 64(n) tile per workgroup. IN: 0 fp32, 1 bf16, 2 int8.
+// One 64(k) x 64(n) tile per workgroup. IN: 0 fp32, 1 bf16, 2 int8, 3 uint8
+// (packed as code - 128, the int8 the MFMA takes).
 template <int IN>
 __global__ void __launch_bounds__(256)
 k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax,
@@ -129,7 +130,7 @@ k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax
     const int tid = threadIdx.x;
     const int n0 = blockIdx.x * kT;
     const int k0 = blockIdx.y * kT;
-    if (IN != 2 && tid < kT) {
+    if (IN < 2 && tid < kT) {
         const int n = n0 + tid;
         float sc = 1.0f;
         if (n < N) {
@@ -147,7 +148,7 @@ k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax
     {
         const int ln = tid & 63;
         const int n = n0 + ln;
-        const float sc = IN != 2 ? s_scale[ln] : 1.0f;
+        const float sc = IN < 2 ? s_scale[ln] : 1.0f;
 #pragma unroll 4
         for (int i = 0; i < kT / 4; ++i) {
             const int kk = (tid >> 6) + 4 * i;
@@ -157,6 +158,8 @@ k_pack_cols(const void* __restrict__ B, int K, int N, int Kp, int qmin, int qmax
                 const size_t idx = (size_t)k * N + n;
                 if (IN == 2) {
                     q = reinterpret_cast<const int8_t*>(B)[idx];
+                } else if (IN == 3) {
+                    q = (int)reinterpret_cast<const uint8_t*>(B)[idx] - 128;
                 } else {
                     const float b = load_b<IN == 1>(B, idx);
                     q = dq::sat_add(dq::rne(b / sc), 0, qmin, qmax);
@@ -348,6 +351,24 @@ int dq_launch_quant_cols(const void* B, dq_dtype typeB, int K, int N, int Kp, in
         hipExtLaunchKernelGGL((k_pack_cols<0>), pgrid, dim3(256), 0, s, nullptr, t.stop, 0, B, K, N,
                               Kp, qmin, qmax, amax, iBp, scaleB, colsum);
     DQ_LAUNCH_CHECK("pack_cols");
+    return DQ_OK;
+}
+
+int dq_launch_pack_cols8(const void* src, bool u8, int K, int R, int Kp, int8_t* dst,
+                         int32_t* sums, hipStream_t s) {
+    const dim3 pgrid((unsigned)((R + kT - 1) / kT), (unsigned)(Kp / kT));
+    // the sums are accumulated with atomics: clear them first (a fill
+    // kernel, so the sequence stays valid under stream capture)
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(sums), R, sums);
+    DQ_LAUNCH_CHECK("zero");
+    if (u8)
+        hipLaunchKernelGGL((k_pack_cols<3>), pgrid, dim3(256), 0, s, src, K, R, Kp, 0, 0, nullptr, dst,
+                           nullptr, sums);
+    else
+        hipLaunchKernelGGL((k_pack_cols<2>), pgrid, dim3(256), 0, s, src, K, R, Kp, 0, 0, nullptr, dst,
+                           nullptr, sums);
+    DQ_LAUNCH_CHECK("pack_cols8");
     return DQ_OK;
 }
 

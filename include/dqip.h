@@ -227,6 +227,74 @@ int qlinear_conv1x1(const void* x, dq_dtype x_type, int64_t N, int64_t C,
                     const void* y_zero_point, dq_dtype y_type,
                     const int32_t* bias, void* y, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Quantized matrix products: QGemm, MatMulIntegerToFloat and
+ * DynamicQuantizeMatMul.
+ * onnxruntime quantization_defs.cc, schemas QGemm, MatMulIntegerToFloat and
+ * DynamicQuantizeMatMul, give the inputs (8-bit A and B with scales and zero
+ * points, B's per tensor or per column; QGemm's int32 C "quantized with zero
+ * point 0 and scale alpha / beta * a_scale * b_scale"; optional y_scale /
+ * y_zero_point making Y 8-bit), the attributes (transA, transB, alpha) and
+ * the types, but no formula. This library computes, for m < M, n < N:
+ *   sum[m,n] = sum_k (A[m,k] - a_zp) * (B[k,n] - b_zp[n])      (exact int32)
+ *   real     = ((float)(sum + C[m,n]) * fl(alpha * a_scale)) * b_scale[n]
+ *              + bias[n]                       (fp32, in this order)
+ *   Y[m,n]   = real (fp32 Y), or saturate(rne(real / y_scale) + y_zp)
+ * (beta is read as 1; the IEEE fp32 quotient is rounded to nearest, ties to
+ * even, as QuantizeLinear states). MatMulIntegerToFloat is an 8-bit A with
+ * an fp32 Y and optional bias; DynamicQuantizeMatMul is an fp32 A, which
+ * each forward quantizes per tensor to uint8 with lo = min(0, min A),
+ * hi = max(0, max A), a_scale = (hi - lo) / 255 (1 if hi == lo),
+ * a_zp = saturate(rne(-lo / a_scale)); QGemm adds C, alpha, transA and an
+ * 8-bit Y. Life cycle as dqip: init, set the constant B once, forward.
+ *
+ * dq_qgemm_init: shapes (1 <= M, N < 2^31 - 256, 1 <= K <= DQ_QGEMM_K_MAX,
+ * so every sum fits in int32), a_type DQ_F32 / DQ_U8 / DQ_I8 (DQ_F32 =
+ * dynamic quantization, not with transA), transA (A given as [K,M]),
+ * b_type DQ_U8 / DQ_I8, transB (B given as [N,K]), y_type DQ_F32 / DQ_U8 /
+ * DQ_I8, alpha. Allocates every device buffer of the context (none later).
+ * Errors: DQ_ERR_ARG, DQ_ERR_RANGE, DQ_ERR_TYPE, DQ_ERR_ALLOC, DQ_ERR_HIP.
+ *
+ * dq_qgemm_set_b: B ([K,N], or [N,K] with transB, dense row-major DEVICE
+ * tensor of b_type), b_scale (b_scale_len = 1 or N fp32 on the device),
+ * b_zero_point (b_zero_point_len = 1 or N values of b_type on the device,
+ * NULL = 0). Packs B into the context; the caller may free its tensors when
+ * the call returns (it synchronizes `stream`). Errors: DQ_ERR_STATE,
+ * DQ_ERR_ARG, DQ_ERR_HIP.
+ *
+ * dq_qgemm_forward: A ([M,K], or [K,M] with transA, dense row-major DEVICE
+ * tensor of a_type); a_scale (one fp32 on the device; NULL for an fp32 A);
+ * a_zero_point (one value of a_type on the device, NULL = 0; NULL for an
+ * fp32 A); C (int32 DEVICE tensor of shape [c_rows, c_cols], c_rows = 1 or
+ * M and c_cols = 1 or N, broadcast to [M,N]; NULL = none); bias (N fp32 on
+ * the device, fp32 Y only; NULL = none); y_scale / y_zero_point (8-bit Y:
+ * one fp32 and one value of y_type on the device, zero point NULL = 0;
+ * NULL for an fp32 Y); Y ([M,N] dense row-major DEVICE tensor of y_type).
+ * Asynchronous on `stream`. Errors: DQ_ERR_STATE (no B yet, other device),
+ * DQ_ERR_ARG, DQ_ERR_HIP.
+ * dq_qgemm_forward_accumulators: the same with the int32 sum + C written to
+ * acc [M,N] (inspection).
+ * ---------------------------------------------------------------------- */
+#define DQ_QGEMM_K_MAX 32768
+
+typedef struct dq_qgemm_ctx dq_qgemm_ctx;
+
+int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K, dq_dtype a_type,
+                  int transA, dq_dtype b_type, int transB, dq_dtype y_type, float alpha);
+int dq_qgemm_set_b(dq_qgemm_ctx* ctx, const void* B, const float* b_scale, int64_t b_scale_len,
+                   const void* b_zero_point, int64_t b_zero_point_len, void* stream);
+int dq_qgemm_forward(dq_qgemm_ctx* ctx, const void* A, const float* a_scale,
+                     const void* a_zero_point, const int32_t* C, int64_t c_rows, int64_t c_cols,
+                     const float* bias, const float* y_scale, const void* y_zero_point, void* Y,
+                     void* stream);
+int dq_qgemm_forward_accumulators(dq_qgemm_ctx* ctx, const void* A, const float* a_scale,
+                                  const void* a_zero_point, const int32_t* C, int64_t c_rows,
+                                  int64_t c_cols, int32_t* acc, void* stream);
+/* A short description of the kernels the context runs (owned by it). */
+const char* dq_qgemm_info(const dq_qgemm_ctx* ctx);
+/* Frees the context and its device memory; NULL is a no-op. */
+void dq_qgemm_release(dq_qgemm_ctx* ctx);
+
 #ifdef __cplusplus
 }
 #endif

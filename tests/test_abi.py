@@ -27,7 +27,8 @@ def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
     skip = {"sizeof", "defined", "if"}
-    return sorted({n for n in names if n not in skip and (n.startswith("dqip_") or n.startswith("qlinear_"))})
+    return sorted({n for n in names
+                   if n not in skip and n.startswith(("dqip_", "qlinear_", "dq_"))})
 
 
 def test_header_declares_the_api():
@@ -45,6 +46,39 @@ def test_library_exports_every_declared_symbol(dq):
     assert set(declared_functions()) == set(dq.exported_symbols())
     for name in declared_functions():
         assert callable(getattr(dq, name))
+
+
+def test_header_declares_the_quantized_matrix_products():
+    names = declared_functions()
+    for n in ("dq_qgemm_init", "dq_qgemm_set_b", "dq_qgemm_forward",
+              "dq_qgemm_forward_accumulators", "dq_qgemm_info", "dq_qgemm_release"):
+        assert n in names
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 8, 16, 3, 0, 2, 0, 0, 1.0), "ARG"),        # M = 0
+    ((4, 8, 0, 3, 0, 2, 0, 0, 1.0), "ARG"),         # K = 0
+    ((4, 8, 32769, 3, 0, 2, 0, 0, 1.0), "RANGE"),   # K beyond DQ_QGEMM_K_MAX
+    ((4, 8, 16, 1, 0, 2, 0, 0, 1.0), "TYPE"),       # bf16 A
+    ((4, 8, 16, 0, 1, 2, 0, 0, 1.0), "ARG"),        # fp32 A with transA
+    ((4, 8, 16, 3, 0, 0, 0, 0, 1.0), "TYPE"),       # fp32 B
+    ((4, 8, 16, 3, 0, 2, 0, 1, 1.0), "TYPE"),       # bf16 Y
+])
+def test_qgemm_init_rejects_bad_arguments(dq, args, code):
+    h = C.c_void_p(None)
+    rc = dq.load().dq_qgemm_init(C.byref(h), *args)
+    assert rc == getattr(dq, "DQ_ERR_" + code) and h.value is None
+    assert dq.dqip_last_error()
+
+
+def test_qgemm_null_handles(dq):
+    L = dq.load()
+    assert L.dq_qgemm_init(None, 4, 4, 4, 3, 0, 2, 0, 0, 1.0) == dq.DQ_ERR_ARG
+    assert L.dq_qgemm_set_b(None, None, None, 1, None, 0, None) == dq.DQ_ERR_STATE
+    assert L.dq_qgemm_forward(None, None, None, None, None, 0, 0, None, None, None, None,
+                              None) == dq.DQ_ERR_STATE
+    assert L.dq_qgemm_info(None) is None
+    L.dq_qgemm_release(None)
 
 
 def test_no_torch_types_in_the_header():
