@@ -322,6 +322,41 @@ def bench_qconv(dq, torch, steps):
     return out
 
 
+def bench_qgemm(dq, torch, kind, steps, flush):
+    """The quantized matrix products at 4096^3 (workloads.qgemm_case): TOP/s
+    of 2MNK over the whole forward (A packing or per-tensor quantization and
+    the GEMM), back to back and cold."""
+    import workloads as W
+
+    c = W.qgemm_case(kind)
+    M, N, K = c["M"], c["N"], c["K"]
+    a_t = dq.DQ_F32 if kind == "dqmm" else dq.DQ_U8
+    y_t = dq.DQ_U8 if kind == "qgemm" else dq.DQ_F32
+    h = dq.dq_qgemm_init(M, N, K, a_t, False, dq.DQ_I8, False, y_t, 1.0)
+    try:
+        dq.dq_qgemm_set_b(h, dev_tensor(c["B"], torch), dev_tensor(c["b_scale"], torch),
+                          dev_tensor(c["b_zp"].astype(np.int8), torch))
+        A = dev_tensor(c["A"], torch)
+        a_s = None if kind == "dqmm" else dev_tensor(np.float32([c["a_scale"]]), torch)
+        a_z = None if kind == "dqmm" else dev_tensor(np.uint8([c["a_zp"]]), torch)
+        Cm = dev_tensor(c["C"], torch) if "C" in c else None
+        bias = dev_tensor(c["bias"], torch) if "bias" in c else None
+        ys = dev_tensor(np.float32([c["y_scale"]]), torch) if kind == "qgemm" else None
+        yz = dev_tensor(np.uint8([c["y_zp"]]), torch) if kind == "qgemm" else None
+        Y = torch.empty((M, N), dtype=torch.uint8 if kind == "qgemm" else torch.float32,
+                        device="cuda")
+        fn = lambda: dq.dq_qgemm_forward(h, A, a_s, a_z, Cm, bias, ys, yz, Y)  # noqa: E731
+        cold, warm = time_cold_warm(fn, torch, steps, flush)
+        info = dq.dq_qgemm_info(h)
+    finally:
+        dq.dq_qgemm_release(h)
+    ops = 2.0 * M * N * K
+    return {"workload": c["name"], "us_per_forward": round(warm * 1e3, 2),
+            "TOPS": round(ops / (warm / 1e3) / 1e12, 1),
+            "us_cold": round(cold[0] * 1e3, 2), "us_cold_p10": round(cold[1] * 1e3, 2),
+            "us_cold_p90": round(cold[2] * 1e3, 2), "info": info}
+
+
 def bench_dqip_case(dq, torch, case, steps, warmup, flush):
     """Back-to-back forwards (warm: a recurrence keeps its weights cache-
     resident), their per-phase kernel times, and single forwards after a
@@ -433,6 +468,12 @@ def main():
                          ("dqip_8192_dynamic_b", W.dqip_dynamic_b)):
             log(f"bench: {name}")
             secondary[name] = bench_dqip_case(dq, torch, mk(), steps2, 3, flush)
+            log(f"bench: {secondary[name]}")
+        for kind, name in (("mitf", "matmul_integer_to_float_4096"),
+                           ("dqmm", "dynamic_quantize_matmul_4096"),
+                           ("qgemm", "qgemm_u8_4096")):
+            log(f"bench: {name}")
+            secondary[name] = bench_qgemm(dq, torch, kind, steps2, flush)
             log(f"bench: {secondary[name]}")
         del flush
 

@@ -71,6 +71,7 @@ struct DqEpilogue {
     const int32_t* zeroB = nullptr;
     const int32_t* addC = nullptr;     // int32 added to the sum, at i * c_rs + j * c_cs
     long long c_rs = 0, c_cs = 0;
+    int c_mode = 0;                    // 0 none, 1 per column (or one value), 2 per row, 3 [M,N]
     const float* y_scale = nullptr;    // DQ_OUT_U8 / DQ_OUT_I8: device scalar
     const void* y_zp = nullptr;        // device scalar of the output's type (NULL: 0)
 };

@@ -108,6 +108,9 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     // EXT (the quantized matrix products): B zero points against A's row sums
     __shared__ int32_t s_rb[EXT ? BM : 1];
     __shared__ __attribute__((aligned(16))) int32_t s_zb[EXT ? BN : 4];
+    // EXT: a C broadcast along rows (one value per column) or along columns
+    __shared__ int32_t s_crow[EXT ? BM : 1];
+    __shared__ __attribute__((aligned(16))) int32_t s_ccol[EXT ? BN : 4];
 
     const int lane = threadIdx.x & 63;
     // wave-uniform values live in SGPRs: every fragment address is a scalar
@@ -141,7 +144,10 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     // row / column parameters of the tile (column vectors hold Np entries)
     for (int c = threadIdx.x; c < BN; c += NT) {
         s_cs[c] = ep.colsumB[n0 + c];
-        if (EXT) s_zb[c] = ep.zeroB ? ep.zeroB[n0 + c] : 0;
+        if (EXT) {
+            s_zb[c] = ep.zeroB ? ep.zeroB[n0 + c] : 0;
+            s_ccol[c] = ep.c_mode == 1 ? ep.addC[(long long)min(n0 + c, N - 1) * ep.c_cs] : 0;
+        }
         if (OUT != DQ_OUT_ACC) {
             s_sb[c] = ep.scaleB[n0 + c];
             s_bias[c] = BIAS ? ep.bias[n0 + c] : 0.0f;
@@ -150,7 +156,10 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     for (int r = threadIdx.x; r < BM; r += NT) {
         const int row = min(m0 + r, M - 1);
         s_za[r] = ep.zeroA[row];
-        if (EXT) s_rb[r] = ep.rowsumA ? ep.rowsumA[row] : 0;
+        if (EXT) {
+            s_rb[r] = ep.rowsumA ? ep.rowsumA[row] : 0;
+            s_crow[r] = ep.c_mode == 2 ? ep.addC[(long long)row * ep.c_rs] : 0;
+        }
         if (OUT != DQ_OUT_ACC) s_sa[r] = ep.scaleA[row];
     }
 
@@ -303,24 +312,28 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         // rate; a 32-bit product would take the quarter-rate 64-bit multiply-
         // add): |128 - zeroA| <= 128 and -2^23 <= colsum < 2^23 for K <= 65536,
         // so the product is exact and the wrapping add gives the exact sum
-        int za[SPP], rb[SPP];
+        int za[SPP], rb[SPP], cr[SPP];
         float sA[SPP];
 #pragma unroll
         for (int u = 0; u < SPP; ++u) {
             const int rt = (wm * FM + p0 + u) * 32 + rs;  // tile row
             za[u] = 128 - s_za[rt];
             rb[u] = EXT ? s_rb[rt] : 0;
+            cr[u] = EXT ? s_crow[rt] : 0;
             sA[u] = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
         }
         // column groups jg = 4 j + g; each group's parameters are read from
         // LDS one group ahead, so their latency hides behind the previous
         // group's arithmetic
-        dq::v4i csv[2], zbv[2];
+        dq::v4i csv[2], zbv[2], ccv[2];
         dq::f4 sBv[2], bvv[2];
         auto params = [&](int jg, int set) {
             const int ct = wn * FN * 32 + (jg >> 2) * 32 + 8 * (jg & 3) + 4 * (lane >> 5);  // tile column
             csv[set] = *reinterpret_cast<const dq::v4i*>(&s_cs[ct]);
-            if (EXT) zbv[set] = *reinterpret_cast<const dq::v4i*>(&s_zb[ct]);
+            if (EXT) {
+                zbv[set] = *reinterpret_cast<const dq::v4i*>(&s_zb[ct]);
+                ccv[set] = *reinterpret_cast<const dq::v4i*>(&s_ccol[ct]);
+            }
             if (OUT != DQ_OUT_ACC) sBv[set] = *reinterpret_cast<const dq::f4*>(&s_sb[ct]);
             if (OUT != DQ_OUT_ACC && BIAS) bvv[set] = *reinterpret_cast<const dq::f4*>(&s_bias[ct]);
         };
@@ -348,14 +361,15 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                         // B zero points: + rowsumA[i] * zb[j], where rowsumA holds
                         // sum_k A^[i,k] + K * (shift - a_zp), |.| <= 255 K < 2^23
                         // for K <= 32768, and |zb| <= 255: exact on the 24-bit
-                        // multiplier; then the int32 C, broadcast through its
-                        // strides (wrapping adds)
-                        const dq::v4i zb = zbv[set];
+                        // multiplier; then the int32 C (a broadcast C from LDS,
+                        // a full [M,N] C from memory; wrapping adds)
+                        const dq::v4i zb = zbv[set], cc = ccv[set];
                         const int row = min(m0 + (wm * FM + p0 + u) * 32 + rs, M - 1);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            sum[e] = (int32_t)((uint32_t)sum[e] + (uint32_t)__mul24(rb[u], zb[e]));
-                            if (ep.addC) {
+                            sum[e] = (int32_t)((uint32_t)sum[e] + (uint32_t)__mul24(rb[u], zb[e]) +
+                                               (uint32_t)cr[u] + (uint32_t)cc[e]);
+                            if (ep.c_mode == 3) {
                                 const int col = min(col0 + cs_ + e, N - 1);
                                 sum[e] = (int32_t)((uint32_t)sum[e] +
                                                    (uint32_t)ep.addC[(long long)row * ep.c_rs + (long long)col * ep.c_cs]);

@@ -60,10 +60,17 @@ __device__ __forceinline__ float ord2f(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// Per-tensor quantization parameters from the min / max words (the row
-// quantizer's rule over the whole tensor).
+// The tensor's min / max land in kMmSlots slot pairs (workgroup b adds to
+// slot b % kMmSlots), so no single address takes every workgroup's atomics;
+// mm[0 .. kMmSlots) hold minima, mm[kMmSlots .. 2 kMmSlots) maxima.
+constexpr int kMmSlots = 64;
+
+// Per-tensor quantization parameters from the slots (the row quantizer's
+// rule over the whole tensor); a whole wave calls it and gets uniform values.
 __device__ __forceinline__ void tensor_params(const uint32_t* mm, float& scale, int& zero) {
-    const float lo = ord2f(mm[0]), hi = ord2f(mm[1]);
+    const int lane = threadIdx.x & 63;
+    const float lo = dq::wave_min_uniform(ord2f(mm[lane]));
+    const float hi = dq::wave_max_uniform(ord2f(mm[kMmSlots + lane]));
     if (hi == lo) {
         scale = 1.0f;
         zero = 0;
@@ -79,7 +86,7 @@ __device__ __forceinline__ int load_zp8(const void* zp, bool u8) {
 }
 
 __global__ void k_minmax_init(uint32_t* mm) {
-    if (threadIdx.x < 2) mm[threadIdx.x] = 0x80000000u;  // the encoding of +0.0
+    if (threadIdx.x < 2 * kMmSlots) mm[threadIdx.x] = 0x80000000u;  // the encoding of +0.0
 }
 
 // Min / max of n fp32 values (0 included through the initial words).
@@ -104,11 +111,20 @@ __global__ void __launch_bounds__(256) k_tensor_minmax(const float* __restrict__
             hi = __builtin_fmaxf(hi, A[i]);
         }
     }
+    __shared__ float s_lo[4], s_hi[4];
     lo = dq::wave_min_uniform(lo);
     hi = dq::wave_max_uniform(hi);
     if ((threadIdx.x & 63) == 0) {
-        atomicMin(&mm[0], f2ord(lo));
-        atomicMax(&mm[1], f2ord(hi));
+        s_lo[threadIdx.x >> 6] = lo;
+        s_hi[threadIdx.x >> 6] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        lo = __builtin_fminf(__builtin_fminf(s_lo[0], s_lo[1]), __builtin_fminf(s_lo[2], s_lo[3]));
+        hi = __builtin_fmaxf(__builtin_fmaxf(s_hi[0], s_hi[1]), __builtin_fmaxf(s_hi[2], s_hi[3]));
+        const int slot = blockIdx.x % kMmSlots;
+        atomicMin(&mm[slot], f2ord(lo));
+        atomicMax(&mm[kMmSlots + slot], f2ord(hi));
     }
 }
 
@@ -208,10 +224,10 @@ k_pack_rows(const void* __restrict__ src, int R, int K, int Kp, int8_t* __restri
     const int KF = Kp / 32, ngp = Kp / 16;
     dq::QDiv d = {1.0f, 1.0f, true};
     int zero = 0;
+    float tscale = 1.0f;
     if (SRC == SRC_F32) {
-        float scale;
-        tensor_params(out.mm, scale, zero);
-        d = dq::make_qdiv(scale);
+        tensor_params(out.mm, tscale, zero);  // the whole wave, before any branch
+        d = dq::make_qdiv(tscale);
     }
     int sum = 0;
 #pragma unroll 4
@@ -234,7 +250,8 @@ k_pack_rows(const void* __restrict__ src, int R, int K, int Kp, int8_t* __restri
             int azp, sa;
             float ascale;
             if (SRC == SRC_F32) {
-                tensor_params(out.mm, ascale, azp);  // the scale and zero point used above
+                azp = zero;  // the tensor's scale and zero point, as used above
+                ascale = tscale;
                 sa = 128;
             } else {
                 azp = load_zp8(out.a_zp, SRC == SRC_U8);
@@ -327,7 +344,7 @@ struct dq_qgemm_ctx {
     int32_t* rowsum;     // [Mp]
     int32_t* zeroA;      // [Mp]
     float* scaleA;       // [Mp]
-    uint32_t* mm;        // 2 words: per-tensor min / max (fp32 A)
+    uint32_t* mm;        // 2 x kMmSlots words: per-tensor min / max slots (fp32 A)
     std::string info;
 };
 
@@ -382,7 +399,7 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
     // A -> packed, row sums and per-row vectors
     if (c->a_type == DQ_F32) {
         const size_t n = (size_t)M * K;
-        hipLaunchKernelGGL(k_minmax_init, dim3(1), dim3(64), 0, s, c->mm);
+        hipLaunchKernelGGL(k_minmax_init, dim3(1), dim3(2 * kMmSlots), 0, s, c->mm);
         const bool vec = (uintptr_t)A % 16 == 0 && n % 4 == 0;
         const size_t need = (vec ? n / 4 : n + 255) / 256 + 1;
         const unsigned blocks = (unsigned)(need < 2048 ? need : 2048);
@@ -425,6 +442,7 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
         ep.addC = Cm;
         ep.c_rs = c_rows == 1 ? 0 : c_cols;
         ep.c_cs = c_cols == 1 ? 0 : 1;
+        ep.c_mode = c_rows == 1 ? 1 : c_cols == 1 ? 2 : 3;
     }
     ep.y_scale = y_scale;
     ep.y_zp = y_zp;
@@ -470,7 +488,7 @@ extern "C" int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K
     if (!rc) rc = ctx_alloc(c, (void**)&c->rowsum, 4 * Mp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->zeroA, 4 * Mp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->scaleA, 4 * Mp);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->mm, kAlign);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->mm, 2 * kMmSlots * sizeof(uint32_t));
     if (!rc && hipMemset(c->biasv, 0, 4 * Np) != hipSuccess) rc = DQ_ERR_HIP;
     if (rc) {
         ctx_free(c);

@@ -22,6 +22,11 @@ pages describe in words (no public dataset or benchmark suite is involved):
 * ``dqip_dynamic_b`` -- 8192^2 fp32 A and fp32 B quantized on every call,
   avoidOverflow on.
 * ``qconv1x1``     -- a 1x1 QLinearConv over uint8 x [8,256,56,56].
+* ``qgemm_case``   -- the quantized matrix products of the ORT schemas
+  (MatMulIntegerToFloat, DynamicQuantizeMatMul, QGemm) at M=N=K=4096 by
+  default: uint8 A with a zero point (or fp32 A ~N(0,1) with 1% x20
+  outliers), int8 B with per-column scales and small per-column zero
+  points, bias / int32 C per column, uint8 output for QGemm.
 """
 from __future__ import annotations
 
@@ -256,3 +261,31 @@ def qconv_random(N: int, C: int, HW: int, M: int, *, seed: int, x_type: str = "u
     return dict(x=x, x_type=x_type, x_scale=np.float32(0.01), x_zp=x_zp, w=w, w_type=w_type,
                 w_scale=w_scale, w_zp=wz, bias=b, y_scale=y_scale, y_zp=y_zp, y_type=y_type,
                 name=f"qconv1x1 N{N} C{C} HW{HW} M{M} x:{x_type} w:{w_type} y:{y_type}")
+
+
+def qgemm_case(kind: str, seed: int = 5, M: int = 4096, N: int = 4096, K: int = 4096):
+    """kind: "mitf" (MatMulIntegerToFloat: uint8 A ~U{0..255}, a_zp 128,
+    a_scale 0.02; fp32 Y with bias), "dqmm" (DynamicQuantizeMatMul: fp32 A
+    ~N(0,1) with a Bernoulli(0.01) mask of x20 outliers; bias) or "qgemm"
+    (QGemm: uint8 A as for mitf, int32 C per column ~U{-20000..20000},
+    alpha 1, uint8 Y with y_scale 0.05, y_zp 128). B is int8 ~U{-127..127}
+    [K,N] with per-column scales ~U(0.0005, 0.002) and zero points
+    ~U{-8..8}; bias ~U(-1, 1)."""
+    r = rng(seed)
+    case = dict(kind=kind, M=M, N=N, K=K, name=f"{kind} {M}x{N}x{K}")
+    if kind == "dqmm":
+        A = r.normal(0.0, 1.0, (M, K)).astype(np.float32)
+        mask = r.random((M, K)) < 0.01
+        case["A"] = np.where(mask, A * np.float32(20.0), A).astype(np.float32)
+    else:
+        case["A"] = r.integers(0, 256, (M, K), dtype=np.int64).astype(np.uint8)
+        case["a_scale"], case["a_zp"] = np.float32(0.02), 128
+    case["B"] = r.integers(-127, 128, (K, N), dtype=np.int64).astype(np.int8)
+    case["b_scale"] = r.uniform(0.0005, 0.002, N).astype(np.float32)
+    case["b_zp"] = r.integers(-8, 9, N).astype(np.int32)
+    if kind == "qgemm":
+        case["C"] = r.integers(-20000, 20001, N).astype(np.int32)
+        case["y_scale"], case["y_zp"] = np.float32(0.05), 128
+    else:
+        case["bias"] = r.uniform(-1.0, 1.0, N).astype(np.float32)
+    return case
