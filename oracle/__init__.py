@@ -52,6 +52,12 @@ def lib() -> C.CDLL:
         L.oracle_qgemm.argtypes = [vp, i32, i32, i64, i64, f32, i32, vp, i32, i32, i64,
                                    vp, i64, vp, i64, vp, i64, i64, f32, vp, i32, f32, i32,
                                    vp, vp]
+        L.oracle_broadcast_shape.argtypes = [i32, vp, i32, vp, vp, vp]
+        L.oracle_qlinear_binary.argtypes = [i32, i32, vp, i32, vp, f32, i32, vp, i32, vp,
+                                            f32, i32, f32, i32, vp]
+        L.oracle_qlinear_unary.argtypes = [i32, i32, vp, i64, f32, i32, f32, i32, f32, vp]
+        L.oracle_reduce.argtypes = [i32, i32, vp, i32, vp, i32, f32, i32, f32, i32, vp]
+        L.oracle_qlinear_concat.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, f32, i32, vp]
         _lib = L
     return _lib
 
@@ -327,3 +333,142 @@ def dynamic_quantize_matmul(A, B, b_scale, b_zp=None, bias=None):
     then MatMulIntegerToFloat."""
     sc, zp, q = quantize_tensor_u8(A)
     return qgemm(q, B, sc, zp, b_scale, b_zp, bias=bias)
+
+
+# ------------------------------------ element-wise quantized family (R20-R23)
+
+def broadcast_shape(sa, sb):
+    """numpy multidirectional broadcasting of two shapes, as the oracle does it."""
+    a = np.asarray(sa, np.int64)
+    b = np.asarray(sb, np.int64)
+    out = np.zeros(8, np.int64)
+    ny = C.c_int(0)
+    rc = lib().oracle_broadcast_shape(a.size, _p(a), b.size, _p(b), C.byref(ny), _p(out))
+    if rc != 0:
+        raise ValueError("shapes do not broadcast")
+    return tuple(int(v) for v in out[:ny.value])
+
+
+def _binary(op, A, a_scale, a_zp, B, b_scale, b_zp, c_scale, c_zp):
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    if A.dtype != B.dtype or A.dtype not in (np.uint8, np.int8):
+        raise ValueError("A and B must share one 8-bit type")
+    shape = broadcast_shape(A.shape, B.shape)
+    Y = np.empty(shape, np.int32 if op == 2 else A.dtype)
+    sa = np.asarray(A.shape, np.int64)
+    sb = np.asarray(B.shape, np.int64)
+    rc = lib().oracle_qlinear_binary(op, _TYPE[_tag8(A)], _p(A), A.ndim, _p(sa),
+                                     float(np.float32(a_scale)), int(a_zp), _p(B), B.ndim,
+                                     _p(sb), float(np.float32(b_scale)), int(b_zp),
+                                     float(np.float32(c_scale)), int(c_zp), _p(Y))
+    _check(rc, "qlinear_binary")
+    return Y
+
+
+def qlinear_add(A, a_scale, a_zp, B, b_scale, b_zp, c_scale, c_zp):
+    """QLinearAdd (R20): quantize(A_scale*(A-A_zp) + B_scale*(B-B_zp))."""
+    return _binary(0, A, a_scale, a_zp, B, b_scale, b_zp, c_scale, c_zp)
+
+
+def qlinear_mul(A, a_scale, a_zp, B, b_scale, b_zp, c_scale, c_zp):
+    """QLinearMul (R20): quantize((A-A_zp)*(B-B_zp) * (A_scale*B_scale))."""
+    return _binary(1, A, a_scale, a_zp, B, b_scale, b_zp, c_scale, c_zp)
+
+
+def mul_integer(A, a_zp, B, b_zp):
+    """MulInteger: int32 (A-A_zp)*(B-B_zp), broadcast."""
+    return _binary(2, A, 1.0, a_zp, B, 1.0, b_zp, 1.0, 0)
+
+
+def _unary(op, X, x_scale, x_zp, y_scale, y_zp, alpha):
+    X = np.ascontiguousarray(X)
+    Y = np.empty(X.shape, X.dtype)
+    rc = lib().oracle_qlinear_unary(op, _TYPE[_tag8(X)], _p(X), X.size,
+                                    float(np.float32(x_scale)), int(x_zp),
+                                    float(np.float32(y_scale)), int(y_zp),
+                                    float(np.float32(alpha)), _p(Y))
+    _check(rc, "qlinear_unary")
+    return Y
+
+
+def qlinear_leaky_relu(X, x_scale, x_zp, y_scale, y_zp, alpha=0.01):
+    """QLinearLeakyRelu (R20): quantize(alpha*x) for x < 0, else quantize(x)."""
+    return _unary(0, X, x_scale, x_zp, y_scale, y_zp, alpha)
+
+
+def qlinear_sigmoid(X, x_scale, x_zp, y_scale, y_zp):
+    """QLinearSigmoid (R21)."""
+    return _unary(1, X, x_scale, x_zp, y_scale, y_zp, 0.0)
+
+
+def _axes_mask(ndim, axes):
+    if axes is None:
+        return (1 << ndim) - 1
+    m = 0
+    for a in axes:
+        if not -ndim <= a < ndim:
+            raise ValueError("axis out of range")
+        m |= 1 << (a % ndim)
+    return m
+
+
+def _reduced_shape(shape, mask, keepdims):
+    out = []
+    for d, n in enumerate(shape):
+        if mask & (1 << d):
+            if keepdims:
+                out.append(1)
+        else:
+            out.append(n)
+    return tuple(out)
+
+
+def reduce_sum_integer(X, axes=None, keepdims=True):
+    """ReduceSumInteger: exact sum; int32 for int8 input, uint32 for uint8."""
+    X = np.ascontiguousarray(X)
+    mask = _axes_mask(X.ndim, axes)
+    Y = np.empty(_reduced_shape(X.shape, mask, keepdims),
+                 np.uint32 if X.dtype == np.uint8 else np.int32)
+    s = np.asarray(X.shape, np.int64)
+    rc = lib().oracle_reduce(0, _TYPE[_tag8(X)], _p(X), X.ndim, _p(s), mask, 1.0, 0, 1.0, 0,
+                             _p(Y))
+    _check(rc, "reduce_sum_integer")
+    return Y
+
+
+def qlinear_reduce_mean(X, x_scale, x_zp, y_scale, y_zp, axes=None, keepdims=True):
+    """QLinearReduceMean (R22)."""
+    X = np.ascontiguousarray(X)
+    mask = _axes_mask(X.ndim, axes)
+    Y = np.empty(_reduced_shape(X.shape, mask, keepdims), X.dtype)
+    s = np.asarray(X.shape, np.int64)
+    rc = lib().oracle_reduce(1, _TYPE[_tag8(X)], _p(X), X.ndim, _p(s), mask,
+                             float(np.float32(x_scale)), int(x_zp),
+                             float(np.float32(y_scale)), int(y_zp), _p(Y))
+    _check(rc, "qlinear_reduce_mean")
+    return Y
+
+
+def qlinear_concat(inputs, y_scale, y_zp, axis):
+    """QLinearConcat (R23). inputs: list of (tensor, scale, zero point), all
+    of one 8-bit type and one shape except along axis."""
+    xs = [np.ascontiguousarray(t) for t, _, _ in inputs]
+    t0 = xs[0]
+    ax = axis % t0.ndim
+    for x in xs:
+        if x.dtype != t0.dtype or x.ndim != t0.ndim or \
+                x.shape[:ax] != t0.shape[:ax] or x.shape[ax + 1:] != t0.shape[ax + 1:]:
+            raise ValueError("inputs do not concatenate")
+    lens = np.asarray([x.shape[ax] for x in xs], np.int64)
+    shape = t0.shape[:ax] + (int(lens.sum()),) + t0.shape[ax + 1:]
+    Y = np.empty(shape, t0.dtype)
+    outer = int(np.prod(t0.shape[:ax], dtype=np.int64))
+    inner = int(np.prod(t0.shape[ax + 1:], dtype=np.int64))
+    ptrs = (C.c_void_p * len(xs))(*[x.ctypes.data for x in xs])
+    sc = np.asarray([np.float32(s) for _, s, _ in inputs], np.float32)
+    zp = np.asarray([int(z) for _, _, z in inputs], np.int32)
+    rc = lib().oracle_qlinear_concat(_TYPE[_tag8(t0)], len(xs), ptrs, _p(lens), _p(sc), _p(zp),
+                                     outer, inner, float(np.float32(y_scale)), int(y_zp), _p(Y))
+    _check(rc, "qlinear_concat")
+    return Y

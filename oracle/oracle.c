@@ -58,6 +58,25 @@
  *  R18 an 8-bit QGemm output: y = saturate(rne(real / y_scale) + y_zp).
  *  R19 DynamicQuantizeMatMul quantizes A per tensor to uint8 with R1-R4 over
  *      the whole tensor, then computes R15 + R17.
+ *  - same page, the element-wise quantized operators (QLinearAdd, QLinearMul,
+ *    MulInteger, QLinearLeakyRelu, QLinearSigmoid, ReduceSumInteger,
+ *    QLinearReduceMean, QLinearConcat), whose docs print the formulas:
+ *  R20 fp32 steps in the printed order, each rounded once; "quantize" is
+ *      QuantizeLinear's rule (rne of the IEEE quotient, + zero point,
+ *      saturate); inputs and output of QLinearAdd / Mul share one 8-bit type.
+ *      QLinearAdd: (A_scale*(A-A_zp) + B_scale*(B-B_zp)) / C_scale, + C_zp.
+ *      QLinearMul: the integer (A-A_zp)*(B-B_zp) times fl(A_scale*B_scale),
+ *      then / C_scale, + C_zp. Numpy (multidirectional) broadcasting.
+ *  R21 QLinearSigmoid: dequantize in fp32, 1 / (1 + exp(-x)) evaluated in
+ *      fp64 and rounded to fp32 once (so it does not depend on an fp32 exp's
+ *      last bit), then quantize.
+ *  R22 QLinearReduceMean: the mean of the dequantized elements is taken as
+ *      fl32(((double)S * x_scale) / count), S the exact integer sum of
+ *      (x - x_zp) (a float sum would depend on its order, which the doc does
+ *      not fix), then quantize. ReduceSumInteger: the exact sum, int32 for
+ *      int8 input and uint32 for uint8.
+ *  R23 QLinearConcat: each input is dequantized with its own scale / zero
+ *      point (fp32) and quantized with Y's.
  *
  * Arithmetic: fp32 where the pages fix fp32 tensors, IEEE division,
  * nearbyintf in the default round-to-nearest mode for ties-to-even, int64
@@ -67,6 +86,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 #define ORC_OK 0
 #define ORC_ERR_ARG (-1)
@@ -468,5 +488,157 @@ int oracle_qgemm(const void* A, int a_type, int transA, int64_t M, int64_t K, fl
             else
                 store_int8(Y, y_type, m * N + n, sat_add(rne(real / y_scale), y_zp, lo, hi));
         }
+    return ORC_OK;
+}
+
+/* ------------------------------------------ element-wise family (R20-R23) */
+
+#define ORC_MAXD 8
+
+/* numpy broadcasting of two shapes; returns ORC_ERR_ARG when they do not
+ * broadcast. */
+int oracle_broadcast_shape(int na, const int64_t* sa, int nb, const int64_t* sb, int* ny, int64_t* sy)
+{
+    int n = na > nb ? na : nb;
+    if (n > ORC_MAXD) return ORC_ERR_ARG;
+    for (int d = 0; d < n; ++d) {
+        int64_t a = d - (n - na) >= 0 ? sa[d - (n - na)] : 1;
+        int64_t b = d - (n - nb) >= 0 ? sb[d - (n - nb)] : 1;
+        if (a != b && a != 1 && b != 1) return ORC_ERR_ARG;
+        sy[d] = a == 1 ? b : a;
+    }
+    *ny = n;
+    return ORC_OK;
+}
+
+/* offset in a tensor of shape s (ns dims, right-aligned against the output
+ * of ny dims) of the output coordinate c (size-1 dims broadcast) */
+static int64_t bcast_offset(const int64_t* c, int ny, int ns, const int64_t* s)
+{
+    int64_t off = 0;
+    for (int d = 0; d < ns; ++d) {
+        int64_t cd = c[d + (ny - ns)];
+        off = off * s[d] + (s[d] == 1 ? 0 : cd);
+    }
+    return off;
+}
+
+static int quantize_f(float v, float y_scale, int y_zp, int y_type)
+{
+    int lo = (y_type == ORC_U8) ? 0 : -128;
+    int hi = (y_type == ORC_U8) ? 255 : 127;
+    return sat_add(rne(v / y_scale), y_zp, lo, hi);
+}
+
+/* op 0: QLinearAdd, 1: QLinearMul (Y of the inputs' 8-bit type t),
+ *    2: MulInteger (int32 Y; scales unused). */
+int oracle_qlinear_binary(int op, int t, const void* A, int na, const int64_t* sa, float a_scale, int32_t a_zp,
+                          const void* B, int nb, const int64_t* sb, float b_scale, int32_t b_zp,
+                          float c_scale, int32_t c_zp, void* Y)
+{
+    int ny;
+    int64_t sy[ORC_MAXD], c[ORC_MAXD];
+    if (oracle_broadcast_shape(na, sa, nb, sb, &ny, sy)) return ORC_ERR_ARG;
+    int64_t n = total_size(ny, sy);
+    float ab = a_scale * b_scale;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t r = i;
+        for (int d = ny - 1; d >= 0; --d) {
+            c[d] = r % sy[d];
+            r /= sy[d];
+        }
+        int32_t a = load_int8(A, t, bcast_offset(c, ny, na, sa)) - a_zp;
+        int32_t b = load_int8(B, t, bcast_offset(c, ny, nb, sb)) - b_zp;
+        if (op == 2) {
+            ((int32_t*)Y)[i] = a * b;
+        } else if (op == 0) {
+            float fa = (float)a * a_scale;
+            float fb = (float)b * b_scale;
+            float v = fa + fb;
+            store_int8(Y, t, i, quantize_f(v, c_scale, c_zp, t));
+        } else {
+            float v = (float)(a * b) * ab;
+            store_int8(Y, t, i, quantize_f(v, c_scale, c_zp, t));
+        }
+    }
+    return ORC_OK;
+}
+
+/* op 0: QLinearLeakyRelu (alpha), 1: QLinearSigmoid; X and Y of type t. */
+int oracle_qlinear_unary(int op, int t, const void* X, int64_t n, float x_scale, int32_t x_zp,
+                         float y_scale, int32_t y_zp, float alpha, void* Y)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float x = (float)(load_int8(X, t, i) - x_zp) * x_scale;
+        float v;
+        if (op == 0)
+            v = x < 0.0f ? alpha * x : x;
+        else
+            v = (float)(1.0 / (1.0 + exp(-(double)x)));
+        store_int8(Y, t, i, quantize_f(v, y_scale, y_zp, t));
+    }
+    return ORC_OK;
+}
+
+/* Reduction of X (ndim dims of shape s) over the dims whose bit is set in
+ * axes_mask; the output holds the kept dims in order (keepdims only changes
+ * the shape). op 0: ReduceSumInteger (Y int32 for int8 input, uint32 for
+ * uint8: written as 32-bit words), 1: QLinearReduceMean (Y of type t). */
+int oracle_reduce(int op, int t, const void* X, int ndim, const int64_t* s, int axes_mask,
+                  float x_scale, int32_t x_zp, float y_scale, int32_t y_zp, void* Y)
+{
+    if (ndim < 1 || ndim > ORC_MAXD) return ORC_ERR_ARG;
+    int64_t nout = 1, count = 1;
+    for (int d = 0; d < ndim; ++d) {
+        if (axes_mask & (1 << d)) count *= s[d];
+        else nout *= s[d];
+    }
+    int64_t n = total_size(ndim, s);
+    int64_t c[ORC_MAXD];
+    int64_t* acc = (int64_t*)calloc((size_t)(nout > 0 ? nout : 1), sizeof(int64_t));
+    if (!acc) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t r = i;
+        for (int d = ndim - 1; d >= 0; --d) {
+            c[d] = r % s[d];
+            r /= s[d];
+        }
+        int64_t o = 0;
+        for (int d = 0; d < ndim; ++d)
+            if (!(axes_mask & (1 << d))) o = o * s[d] + c[d];
+        acc[o] += load_int8(X, t, i) - (op == 1 ? x_zp : 0);
+    }
+    for (int64_t o = 0; o < nout; ++o) {
+        if (op == 0) {
+            if (t == ORC_U8) ((uint32_t*)Y)[o] = (uint32_t)acc[o];
+            else ((int32_t*)Y)[o] = (int32_t)acc[o];
+        } else {
+            float mean = (float)(((double)acc[o] * (double)x_scale) / (double)count);
+            store_int8(Y, t, o, quantize_f(mean, y_scale, y_zp, t));
+        }
+    }
+    free(acc);
+    return ORC_OK;
+}
+
+/* QLinearConcat of n_in tensors of type t along axis: input j has the
+ * shape of Y except dim `axis`, which is lens[j]; outer / inner are the
+ * products of Y's dims before / after axis. */
+int oracle_qlinear_concat(int t, int n_in, const void* const* xs, const int64_t* lens,
+                          const float* scales, const int32_t* zps, int64_t outer, int64_t inner,
+                          float y_scale, int32_t y_zp, void* Y)
+{
+    int64_t total = 0;
+    for (int j = 0; j < n_in; ++j) total += lens[j];
+    for (int64_t o = 0; o < outer; ++o) {
+        int64_t base = 0;
+        for (int j = 0; j < n_in; ++j) {
+            for (int64_t k = 0; k < lens[j] * inner; ++k) {
+                float x = (float)(load_int8(xs[j], t, o * lens[j] * inner + k) - zps[j]) * scales[j];
+                store_int8(Y, t, (o * total + base) * inner + k, quantize_f(x, y_scale, y_zp, t));
+            }
+            base += lens[j];
+        }
+    }
     return ORC_OK;
 }
