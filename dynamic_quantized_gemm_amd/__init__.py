@@ -1,5 +1,7 @@
-"""Python binding of libdqip.so: the dynamic quantized inner product and
-QuantizeLinear / DequantizeLinear on AMD Instinct MI355X (gfx950).
+"""Python binding of libdqip.so: the dynamic quantized inner product,
+QuantizeLinear / DequantizeLinear, the requantizing 1x1 QLinearConv, the
+quantized matrix products and the element-wise quantized operators on AMD
+Instinct MI355X (gfx950).
 
 Argument marshalling only: every step runs in the library's HIP kernels.
 The functions carry the names of the C entry points declared in
@@ -15,5 +17,6 @@ from ._binding import (  # noqa: F401
     dqip_last_error, dqip_profile_begin, dqip_profile_end, dqip_read_quantized_a, dqip_read_quantized_b, dqip_release,
     dqip_set_params, exported_symbols, load, qlinear_conv1x1, qlinear_dequantize, qlinear_quantize,
     DQ_QGEMM_K_MAX, dq_qgemm_forward, dq_qgemm_forward_accumulators, dq_qgemm_info, dq_qgemm_init,
-    dq_qgemm_release, dq_qgemm_set_b,
+    dq_qgemm_release, dq_qgemm_set_b, dq_mul_integer, dq_reduce_sum_integer, qlinear_add,
+    qlinear_concat, qlinear_leaky_relu, qlinear_mul, qlinear_reduce_mean, qlinear_sigmoid,
 )

@@ -58,6 +58,27 @@ _SIGNATURES = {
                                                 C.c_void_p]),
     "dq_qgemm_info": (C.c_char_p, [C.c_void_p]),
     "dq_qgemm_release": (None, [C.c_void_p]),
+    "qlinear_add": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
+    "qlinear_mul": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
+    "dq_mul_integer": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                 C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
+                                 C.c_void_p]),
+    "qlinear_leaky_relu": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_float, C.c_int, C.c_void_p, C.c_void_p]),
+    "qlinear_sigmoid": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
+    "dq_reduce_sum_integer": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                        C.c_int, C.c_void_p, C.c_void_p]),
+    "qlinear_reduce_mean": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                      C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p]),
+    "qlinear_concat": (C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
+                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
+                                 C.c_void_p]),
 }
 
 
@@ -289,3 +310,101 @@ def dq_qgemm_info(ctx):
 
 def dq_qgemm_release(ctx):
     load().dq_qgemm_release(ctx)
+
+
+# ----------------------------------------- element-wise quantized operators
+
+def _binary(fn, what, A, a_scale, a_zero_point, B, b_scale, b_zero_point, c_scale, c_zero_point,
+            type_, C_, stream, a_shape, b_shape):
+    sa = tuple(A.shape) if a_shape is None else tuple(a_shape)
+    sb = tuple(B.shape) if b_shape is None else tuple(b_shape)
+    pa, ka = _shape_arg(sa)
+    pb, kb = _shape_arg(sb)
+    if fn == "dq_mul_integer":
+        rc = load().dq_mul_integer(_ptr(A), len(sa), pa, _ptr(a_zero_point), _ptr(B), len(sb), pb,
+                                   _ptr(b_zero_point), type_, _ptr(C_), _stream(stream))
+    else:
+        rc = getattr(load(), fn)(_ptr(A), len(sa), pa, _ptr(a_scale), _ptr(a_zero_point), _ptr(B),
+                                 len(sb), pb, _ptr(b_scale), _ptr(b_zero_point), _ptr(c_scale),
+                                 _ptr(c_zero_point), type_, _ptr(C_), _stream(stream))
+    del ka, kb
+    _check(rc, what)
+
+
+def qlinear_add(A, a_scale, a_zero_point, B, b_scale, b_zero_point, c_scale, c_zero_point, type_,
+                C_, stream=None, a_shape=None, b_shape=None):
+    """A, B: 8-bit tensors broadcasting to C_'s shape (C_ written)."""
+    _binary("qlinear_add", "qlinear_add", A, a_scale, a_zero_point, B, b_scale, b_zero_point,
+            c_scale, c_zero_point, type_, C_, stream, a_shape, b_shape)
+
+
+def qlinear_mul(A, a_scale, a_zero_point, B, b_scale, b_zero_point, c_scale, c_zero_point, type_,
+                C_, stream=None, a_shape=None, b_shape=None):
+    _binary("qlinear_mul", "qlinear_mul", A, a_scale, a_zero_point, B, b_scale, b_zero_point,
+            c_scale, c_zero_point, type_, C_, stream, a_shape, b_shape)
+
+
+def dq_mul_integer(A, a_zero_point, B, b_zero_point, type_, C_, stream=None, a_shape=None,
+                   b_shape=None):
+    """C_: int32 tensor of the broadcast shape (written)."""
+    _binary("dq_mul_integer", "dq_mul_integer", A, None, a_zero_point, B, None, b_zero_point,
+            None, None, type_, C_, stream, a_shape, b_shape)
+
+
+def qlinear_leaky_relu(x, x_scale, x_zero_point, y_scale, y_zero_point, type_, y, alpha=0.01,
+                       n=None, stream=None):
+    n = int(x.numel()) if n is None else int(n)
+    _check(load().qlinear_leaky_relu(_ptr(x), n, _ptr(x_scale), _ptr(x_zero_point), _ptr(y_scale),
+                                     _ptr(y_zero_point), float(alpha), type_, _ptr(y),
+                                     _stream(stream)), "qlinear_leaky_relu")
+
+
+def qlinear_sigmoid(x, x_scale, x_zero_point, y_scale, y_zero_point, type_, y, n=None,
+                    stream=None):
+    n = int(x.numel()) if n is None else int(n)
+    _check(load().qlinear_sigmoid(_ptr(x), n, _ptr(x_scale), _ptr(x_zero_point), _ptr(y_scale),
+                                  _ptr(y_zero_point), type_, _ptr(y), _stream(stream)),
+           "qlinear_sigmoid")
+
+
+def _axes_arg(axes):
+    axes = [] if axes is None else [int(a) for a in axes]
+    arr = (C.c_int32 * max(1, len(axes)))(*axes)
+    return C.cast(arr, C.c_void_p), len(axes), arr
+
+
+def dq_reduce_sum_integer(x, type_, axes, y, shape=None, stream=None):
+    """y: int32 tensor holding the kept dims (written); axes None = all."""
+    shp = tuple(x.shape) if shape is None else tuple(shape)
+    sp, ks = _shape_arg(shp)
+    ap, na, ka = _axes_arg(axes)
+    _check(load().dq_reduce_sum_integer(_ptr(x), type_, len(shp), sp, ap if na else None, na,
+                                        _ptr(y), _stream(stream)), "dq_reduce_sum_integer")
+    del ks, ka
+
+
+def qlinear_reduce_mean(x, type_, axes, x_scale, x_zero_point, y_scale, y_zero_point, y,
+                        shape=None, stream=None):
+    shp = tuple(x.shape) if shape is None else tuple(shape)
+    sp, ks = _shape_arg(shp)
+    ap, na, ka = _axes_arg(axes)
+    _check(load().qlinear_reduce_mean(_ptr(x), type_, len(shp), sp, ap if na else None, na,
+                                      _ptr(x_scale), _ptr(x_zero_point), _ptr(y_scale),
+                                      _ptr(y_zero_point), _ptr(y), _stream(stream)),
+           "qlinear_reduce_mean")
+    del ks, ka
+
+
+def qlinear_concat(inputs, axis, y_scale, y_zero_point, type_, y, shapes=None, stream=None):
+    """inputs: sequence of (tensor, scale tensor, zero point tensor or None)."""
+    n = len(inputs)
+    shp = [tuple(t.shape) for t, _, _ in inputs] if shapes is None else [tuple(s) for s in shapes]
+    nd = len(shp[0]) if shp else 0
+    flat = (C.c_int64 * max(1, n * nd))(*[int(v) for s in shp for v in s])
+    xs = (C.c_void_p * max(1, n))(*[_ptr(t) for t, _, _ in inputs])
+    sc = (C.c_void_p * max(1, n))(*[_ptr(s) for _, s, _ in inputs])
+    zp = (C.c_void_p * max(1, n))(*[_ptr(z) for _, _, z in inputs])
+    _check(load().qlinear_concat(n, C.cast(xs, C.c_void_p), C.cast(flat, C.c_void_p), nd, int(axis),
+                                 C.cast(sc, C.c_void_p), C.cast(zp, C.c_void_p), _ptr(y_scale),
+                                 _ptr(y_zero_point), type_, _ptr(y), _stream(stream)),
+           "qlinear_concat")

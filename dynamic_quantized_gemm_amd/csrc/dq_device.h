@@ -98,6 +98,28 @@ __device__ __forceinline__ float qdiv_fast(float x, const QDiv& d) {
     return __builtin_fmaf(r, d.y, q0);
 }
 
+// Division of a 32-bit unsigned n by a runtime constant d >= 1 with one
+// multiply-high: q = (umulhi(n, m) + n) >> s, s = ceil(log2 d),
+// m = floor(2^32 (2^s - d) / d) + 1 (Granlund & Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, round-up variant).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.s = 0;
+    while ((1ull << f.s) < d) ++f.s;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    uint32_t hi = __umulhi(n, f.m);
+    return (uint32_t)(((uint64_t)hi + n) >> f.s);
+}
+
 // Byte offset of element (r, k) of an operand packed in MFMA fragment order:
 // 1 KiB fragments of 32 rows x 32 k, fragment (r/32, k/32) at index
 // (r/32) * KF + k/32 (KF = Kp/32); inside it, lane slot (r%32) + 32*((k%32)/16)

@@ -23,37 +23,15 @@
 
 namespace {
 
-// Division of a 32-bit unsigned n by a runtime constant d >= 1 with one
-// multiply-high: q = (umulhi(n, m) + n) >> s, s = ceil(log2 d),
-// m = floor(2^32 (2^s - d) / d) + 1 (Granlund & Montgomery, "Division by
-// invariant integers using multiplication", PLDI 1994, round-up variant).
-struct FastDiv {
-    uint32_t d, m, s;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-    FastDiv f;
-    f.d = d;
-    f.s = 0;
-    while ((1ull << f.s) < d) ++f.s;
-    f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
-    return f;
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-    uint32_t hi = __umulhi(n, f.m);
-    return (uint32_t)(((uint64_t)hi + n) >> f.s);
-}
-
 struct AxisMap {
-    FastDiv inner, cdim;
+    dq::FastDiv inner, cdim;
     int per_axis;
 };
 
 __device__ __forceinline__ uint32_t channel_of(uint32_t e, const AxisMap& a) {
     if (!a.per_axis) return 0;
-    uint32_t q = fdiv(e, a.inner);
-    return q - fdiv(q, a.cdim) * a.cdim.d;
+    uint32_t q = dq::fdiv(e, a.inner);
+    return q - dq::fdiv(q, a.cdim) * a.cdim.d;
 }
 
 __device__ __forceinline__ uint32_t channel_of64(uint64_t e, uint64_t inner, uint64_t cdim) {
@@ -162,11 +140,11 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
                                      : dq::f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // "rows" of inner elements: channel of row r is r % C
-    const uint32_t r0 = am.per_axis ? fdiv(eb, am.inner) : 0;
-    const uint32_t nrows = am.per_axis ? fdiv(last, am.inner) - r0 + 1 : 1;
+    const uint32_t r0 = am.per_axis ? dq::fdiv(eb, am.inner) : 0;
+    const uint32_t nrows = am.per_axis ? dq::fdiv(last, am.inner) - r0 + 1 : 1;
     for (uint32_t k = threadIdx.x; k < nrows; k += 256) {
         const uint32_t row = r0 + k;
-        const uint32_t c = am.per_axis ? row - fdiv(row, am.cdim) * am.cdim.d : 0;
+        const uint32_t c = am.per_axis ? row - dq::fdiv(row, am.cdim) * am.cdim.d : 0;
         const float sc = scale[c];
         const int z = load_zp<U8>(zp, c);
         const dq::QDiv d = dq::make_qdiv(sc);
@@ -182,7 +160,7 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
     for (int q = 0; q < 4; ++q) {
         const uint32_t e0 = base + q * 1024u;
         if ((uint64_t)e0 >= n) break;
-        const uint32_t k = am.per_axis ? fdiv(e0, am.inner) - r0 : 0;
+        const uint32_t k = am.per_axis ? dq::fdiv(e0, am.inner) - r0 : 0;
         if ((uint64_t)e0 + 4 > n) {  // the tensor's last partial vector
             for (uint64_t e = e0; e < n; ++e) {
                 const uint32_t c = channel_of((uint32_t)e, am);
@@ -314,8 +292,8 @@ AxisMap make_axis_map(const Plan& p, bool small) {
     AxisMap am{};
     am.per_axis = p.per_axis;
     if (p.per_axis && small) {
-        am.inner = make_fastdiv((uint32_t)p.inner);
-        am.cdim = make_fastdiv((uint32_t)p.cdim);
+        am.inner = dq::make_fastdiv((uint32_t)p.inner);
+        am.cdim = dq::make_fastdiv((uint32_t)p.cdim);
     }
     return am;
 }

@@ -295,6 +295,89 @@ const char* dq_qgemm_info(const dq_qgemm_ctx* ctx);
 /* Frees the context and its device memory; NULL is a no-op. */
 void dq_qgemm_release(dq_qgemm_ctx* ctx);
 
+/* ------------------------------------------------------------------------
+ * Element-wise quantized operators.
+ * onnxruntime quantization_defs.cc, the contrib schemas QLinearAdd,
+ * QLinearMul, MulInteger, QLinearLeakyRelu, QLinearSigmoid,
+ * ReduceSumInteger, QLinearReduceMean and QLinearConcat, whose docs print:
+ *   QLinearAdd  C = (A_scale (A - A_zp) + B_scale (B - B_zp)) / C_scale + C_zp
+ *   QLinearMul  C = ((A - A_zp) (B - B_zp)) (A_scale B_scale) / C_scale + C_zp
+ *   MulInteger  C (int32) = (A - A_zp) (B - B_zp)
+ *   QLinearLeakyRelu  quantize(alpha x) where x = dequantize(X) < 0, else
+ *                     quantize(x)
+ *   QLinearSigmoid    quantize(1 / (1 + exp(-dequantize(X))))
+ *   ReduceSumInteger  sum over axes; int32 for int8 X, uint32 for uint8 X
+ *   QLinearReduceMean quantize(mean over axes of dequantize(X))
+ *   QLinearConcat     the inputs joined along axis, each one dequantized
+ *                     with its own scale / zero point and quantized with Y's
+ * dequantize(x) = (x - zp) * scale and quantize(v) = saturate(rne(v / scale)
+ * + zp) as in QuantizeLinear (IEEE fp32 quotient, ties to even, [0,255] or
+ * [-128,127]). This library takes the fp32 steps one at a time in the
+ * printed order (A_scale * B_scale is one fp32 product); the sigmoid is
+ * evaluated in fp64 and rounded to fp32 once; the mean is
+ * fp32(fp64(S * x_scale) / count) with S the exact integer sum of x - x_zp.
+ *
+ * Common conventions: every tensor is a dense row-major DEVICE tensor of
+ * `type` (DQ_U8 or DQ_I8; all 8-bit tensors of one call share it), shapes
+ * are HOST arrays of ndim sizes (0 <= ndim <= 8 for the binary operators,
+ * 1 <= ndim <= 8 otherwise, sizes >= 0). Scales: one fp32 on the device;
+ * zero points: one value of `type` on the device (NULL = 0); every scale is
+ * finite and > 0 (results for others are unspecified). Zero output elements
+ * is a no-op. Asynchronous on `stream`. Errors: DQ_ERR_TYPE (type),
+ * DQ_ERR_ARG (NULL tensor or scale, negative size, shapes that do not
+ * broadcast or concatenate), DQ_ERR_RANGE (limits below, axis out of
+ * range), DQ_ERR_HIP.
+ *
+ * qlinear_add / qlinear_mul: A [a_shape], B [b_shape] broadcast numpy-style
+ * (multidirectional) to C's shape, which the caller allocates; C has fewer
+ * than 2^32 elements.
+ * dq_mul_integer: the same broadcast with an int32 C; A, B of `type`.
+ * qlinear_leaky_relu / qlinear_sigmoid: x and y hold n elements.
+ * dq_reduce_sum_integer / qlinear_reduce_mean: X [shape] reduced over the
+ * n_axes dims listed in axes (HOST int32, negative counts from the end,
+ * repeats allowed; n_axes = 0 reduces over every dim). y holds the kept
+ * dims in order (keepdims only changes its shape, which is the caller's):
+ * 32-bit words for the sum (int32 / uint32 bit patterns, wrapping modulo
+ * 2^32 like the int32 accumulation), `type` for the mean. Limits: fewer
+ * than 2^31 outputs, fewer than 2^32 elements per output, and at most 2^23
+ * elements per mean (the integer sum stays exact in int32); a mean over an
+ * empty dim is DQ_ERR_ARG, a sum over one is 0. ReduceSumInteger may zero
+ * y before adding into it with atomics: y must not alias x.
+ * qlinear_concat: n_inputs tensors xs[j] (HOST array of DEVICE pointers) of
+ * rank ndim, shapes in the HOST array shapes[j * ndim + d], equal in every
+ * dim but `axis`; x_scales[j] (HOST array of DEVICE pointers to one fp32)
+ * and x_zero_points[j] (HOST array of DEVICE pointers, NULL array or NULL
+ * entry = 0); y of the joined shape. An input with zero length along axis
+ * contributes nothing. One launch per input.
+ * ---------------------------------------------------------------------- */
+int qlinear_add(const void* A, int a_ndim, const int64_t* a_shape, const float* a_scale,
+                const void* a_zero_point, const void* B, int b_ndim, const int64_t* b_shape,
+                const float* b_scale, const void* b_zero_point, const float* c_scale,
+                const void* c_zero_point, dq_dtype type, void* C, void* stream);
+int qlinear_mul(const void* A, int a_ndim, const int64_t* a_shape, const float* a_scale,
+                const void* a_zero_point, const void* B, int b_ndim, const int64_t* b_shape,
+                const float* b_scale, const void* b_zero_point, const float* c_scale,
+                const void* c_zero_point, dq_dtype type, void* C, void* stream);
+int dq_mul_integer(const void* A, int a_ndim, const int64_t* a_shape, const void* a_zero_point,
+                   const void* B, int b_ndim, const int64_t* b_shape, const void* b_zero_point,
+                   dq_dtype type, int32_t* C, void* stream);
+int qlinear_leaky_relu(const void* x, int64_t n, const float* x_scale, const void* x_zero_point,
+                       const float* y_scale, const void* y_zero_point, float alpha,
+                       dq_dtype type, void* y, void* stream);
+int qlinear_sigmoid(const void* x, int64_t n, const float* x_scale, const void* x_zero_point,
+                    const float* y_scale, const void* y_zero_point, dq_dtype type, void* y,
+                    void* stream);
+int dq_reduce_sum_integer(const void* x, dq_dtype type, int ndim, const int64_t* shape,
+                          const int32_t* axes, int n_axes, void* y, void* stream);
+int qlinear_reduce_mean(const void* x, dq_dtype type, int ndim, const int64_t* shape,
+                        const int32_t* axes, int n_axes, const float* x_scale,
+                        const void* x_zero_point, const float* y_scale,
+                        const void* y_zero_point, void* y, void* stream);
+int qlinear_concat(int n_inputs, const void* const* xs, const int64_t* shapes, int ndim,
+                   int axis, const float* const* x_scales, const void* const* x_zero_points,
+                   const float* y_scale, const void* y_zero_point, dq_dtype type, void* y,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

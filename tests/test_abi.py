@@ -207,3 +207,49 @@ def test_fastdiv_constants_cover_every_quotient():
         hi = (ns * np.uint64(m)) >> np.uint64(32)
         q = (hi + ns) >> np.uint64(s)
         assert np.array_equal(q, ns // np.uint64(d)), d
+
+
+def test_elementwise_reject_bad_arguments(dq):
+    # every check below fails before anything is enqueued, so no device is used
+    lib = dq.load()
+    U8, I8 = dq.DQ_U8, dq.DQ_I8
+    s34, s4, s3 = _shape([3, 4]), _shape([4]), _shape([3])
+
+    def add(t=U8, na=2, sa=s34, nb=1, sb=s4, A=1, B=1, C_=1, sc=1):
+        return lib.qlinear_add(A, na, sa, sc, None, B, nb, sb, sc, None, sc, None, t, C_, None)
+
+    assert add(t=dq.DQ_F32) == dq.DQ_ERR_TYPE
+    assert add(sb=s3) == dq.DQ_ERR_ARG              # (3,4) and (3,) do not broadcast
+    assert add(na=9) == dq.DQ_ERR_ARG               # rank beyond 8
+    assert add(A=None) == dq.DQ_ERR_ARG
+    assert add(sc=None) == dq.DQ_ERR_ARG
+    assert add(sa=_shape([3, 0]), sb=_shape([0]), A=None, B=None, C_=None) == dq.DQ_OK
+    assert lib.qlinear_mul(1, 2, _shape([65536, 65536]), 1, None, 1, 0, None, 1, None, 1, None,
+                           U8, 1, None) == dq.DQ_ERR_RANGE   # 2^32 outputs
+    assert lib.dq_mul_integer(1, 2, s34, None, 1, 1, s3, None, I8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.dq_mul_integer(1, 2, s34, None, 1, 1, s4, None, dq.DQ_BF16, 1, None) == dq.DQ_ERR_TYPE
+    # one-code functions
+    assert lib.qlinear_sigmoid(1, -1, 1, None, 1, None, U8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_sigmoid(1, 16, None, None, 1, None, U8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_leaky_relu(1, 16, 1, None, 1, None, 0.1, dq.DQ_F32, 1, None) == dq.DQ_ERR_TYPE
+    assert lib.qlinear_leaky_relu(None, 0, None, None, None, None, 0.1, I8, None, None) == dq.DQ_OK
+    # reductions
+    axes = (C.c_int32 * 2)(1, 3)
+    assert lib.dq_reduce_sum_integer(1, U8, 2, s34, axes, 2, 1, None) == dq.DQ_ERR_RANGE
+    assert lib.dq_reduce_sum_integer(1, U8, 0, s34, None, 0, 1, None) == dq.DQ_ERR_ARG
+    assert lib.dq_reduce_sum_integer(1, U8, 2, s34, None, -1, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_reduce_mean(1, I8, 2, _shape([2, 0]), axes, 1, 1, None, 1, None, 1,
+                                   None) == dq.DQ_ERR_ARG          # mean over an empty dim
+    big = _shape([2, 1 << 24])
+    assert lib.qlinear_reduce_mean(1, I8, 2, big, axes, 1, 1, None, 1, None, 1,
+                                   None) == dq.DQ_ERR_RANGE        # 2^24 elements per mean
+    assert lib.qlinear_reduce_mean(1, U8, 2, s34, axes, 1, None, None, 1, None, 1,
+                                   None) == dq.DQ_ERR_ARG          # NULL x_scale
+    # concat
+    xs = (C.c_void_p * 2)(1, 1)
+    sc = (C.c_void_p * 2)(1, 1)
+    shapes = (C.c_int64 * 4)(2, 3, 2, 5)
+    assert lib.qlinear_concat(2, xs, shapes, 2, 2, sc, None, 1, None, U8, 1, None) == dq.DQ_ERR_RANGE
+    assert lib.qlinear_concat(2, xs, shapes, 2, 0, sc, None, 1, None, U8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_concat(0, xs, shapes, 2, 1, sc, None, 1, None, U8, 1, None) == dq.DQ_ERR_ARG
+    assert lib.qlinear_concat(2, xs, shapes, 2, 1, sc, None, 1, None, dq.DQ_F32, 1, None) == dq.DQ_ERR_TYPE

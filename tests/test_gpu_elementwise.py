@@ -1,0 +1,340 @@
+"""GPU parity of the element-wise quantized operators against the CPU oracle.
+
+Every output is an integer (8-bit codes, int32 products and sums), so the
+bar is bit-exact equality on every element. Cases cover each kernel variant:
+16-, 4- and 1-byte vectors, each broadcast pattern, unaligned pointers,
+ragged tails, tiny scales (the IEEE-division path), row, column and general
+reductions, split sums, and concat with empty and misaligned inputs.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_case import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _seed(*key):
+    """A seed that names the case (stable across processes, unlike hash())."""
+    return zlib.crc32(repr(key).encode())
+
+
+def _dev(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _scal(v, dt=np.float32):
+    return _dev(np.asarray([v], dt))
+
+
+def _zp(v, t):
+    return _scal(v, np.uint8 if t == "u8" else np.int8)
+
+
+def _codes(r, shape, t):
+    return (r.integers(0, 256, shape).astype(np.uint8) if t == "u8"
+            else r.integers(-128, 128, shape).astype(np.int8))
+
+
+def _type(dq, t):
+    return dq.DQ_U8 if t == "u8" else dq.DQ_I8
+
+
+def _tdt(t):
+    import torch
+
+    return torch.uint8 if t == "u8" else torch.int8
+
+
+# ================================================================= binary
+
+BIN_SHAPES = [
+    ((64, 1024), (64, 1024)),     # flat, 16-byte vectors
+    ((64, 1024), (1024,)),        # row vector B
+    ((64, 1024), (64, 1)),        # column vector B (broadcast byte)
+    ((1, 512), (300, 512)),       # A broadcast along rows
+    ((4096, 33), ()),             # scalar B, merged to one flat dim
+    ((3, 5, 36), (5, 1)),         # inner 36: 4-byte vectors
+    ((2, 3, 4, 5), (3, 1, 5)),    # inner 5: one element per lane
+    ((1000003,), (1000003,)),     # ragged flat
+    ((7,), (7,)),
+    ((2, 1, 3, 16), (4, 1, 16)),  # broadcast on both sides
+    ((0, 16), (16,)),             # empty
+]
+
+
+def _run_binary(dq, op, t, A, B, sa, za, sb, zb, sc, zc, offset=0):
+    import torch
+
+    shape = np.broadcast_shapes(A.shape, B.shape)
+    Ad, Bd = _dev(A), _dev(B)
+    if op == "mulint":
+        C = torch.empty(int(np.prod(shape)) + offset, dtype=torch.int32, device="cuda")[offset:]
+        dq.dq_mul_integer(Ad, _zp(za, t), Bd, _zp(zb, t), _type(dq, t), C, a_shape=A.shape,
+                          b_shape=B.shape)
+    else:
+        C = torch.empty(int(np.prod(shape)) + offset, dtype=_tdt(t), device="cuda")[offset:]
+        fn = dq.qlinear_add if op == "add" else dq.qlinear_mul
+        fn(Ad, _scal(sa), _zp(za, t), Bd, _scal(sb), _zp(zb, t), _scal(sc), _zp(zc, t),
+           _type(dq, t), C, a_shape=A.shape, b_shape=B.shape)
+    torch.cuda.synchronize()
+    return C.cpu().numpy().reshape(shape)
+
+
+def _want_binary(op, A, B, sa, za, sb, zb, sc, zc):
+    if op == "add":
+        return oracle.qlinear_add(A, sa, za, B, sb, zb, sc, zc)
+    if op == "mul":
+        return oracle.qlinear_mul(A, sa, za, B, sb, zb, sc, zc)
+    return oracle.mul_integer(A, za, B, zb)
+
+
+def _params(r, op, t):
+    lo, hi = (0, 256) if t == "u8" else (-128, 128)
+    za, zb, zc = (int(v) for v in r.integers(lo, hi, 3))
+    sa, sb = np.float32(r.uniform(0.002, 0.05)), np.float32(r.uniform(0.002, 0.05))
+    sc = np.float32(r.uniform(0.01, 0.1)) if op == "add" else np.float32(r.uniform(0.5, 5.0))
+    return sa, za, sb, zb, sc, zc
+
+
+@pytest.mark.parametrize("sa_,sb_", BIN_SHAPES)
+@pytest.mark.parametrize("t", ["u8", "i8"])
+@pytest.mark.parametrize("op", ["add", "mul", "mulint"])
+def test_binary_matches_oracle(gpu, op, t, sa_, sb_):
+    r = np.random.default_rng(_seed(op, t, sa_, sb_))
+    A, B = _codes(r, sa_, t), _codes(r, sb_, t)
+    p = _params(r, op, t)
+    log(f"binary {op} {t} {sa_} x {sb_}")
+    got = _run_binary(gpu, op, t, A, B, *p)
+    want = _want_binary(op, A, B, *p)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ"
+
+
+@pytest.mark.parametrize("op", ["add", "mul", "mulint"])
+def test_binary_swapped_operands_and_unaligned_output(gpu, op):
+    # B broadcast into A's place (the (0, 1) operand pattern) and an output
+    # one element past an aligned address (forces the one-element lanes)
+    r = np.random.default_rng(11)
+    A, B = _codes(r, (1024,), "u8"), _codes(r, (96, 1024), "u8")
+    p = _params(r, op, "u8")
+    want = _want_binary(op, A, B, *p)
+    assert np.array_equal(_run_binary(gpu, op, "u8", A, B, *p), want)
+    assert np.array_equal(_run_binary(gpu, op, "u8", A, B, *p, offset=1), want)
+
+
+@pytest.mark.parametrize("op", ["add", "mul"])
+@pytest.mark.parametrize("t", ["u8", "i8"])
+def test_binary_ties_saturation_and_tiny_scales(gpu, op, t):
+    # every (a, b) pair; power-of-two scales put many quotients exactly on
+    # .5 ties; a C_scale below 2^-100 takes the IEEE-division path
+    lo, hi = (0, 256) if t == "u8" else (-128, 128)
+    codes = np.arange(lo, hi).astype(np.uint8 if t == "u8" else np.int8)
+    A = np.repeat(codes, 256).reshape(256, 256)
+    B = np.tile(codes, 256).reshape(256, 256)
+    for sa, sb, sc in ((0.5, 0.25, 1.0), (0.125, 2.0, 4.0), (1e-20, 1e-20, 1e-33),
+                       (np.float32(0.0371), np.float32(0.0113), np.float32(0.0517))):
+        if op == "mul" and sc == 1e-33:
+            sc = 1e-38
+        za, zb, zc = (3, -2, 1) if t == "i8" else (131, 120, 128)
+        got = _run_binary(gpu, op, t, A, B, sa, za, sb, zb, sc, zc)
+        want = _want_binary(op, A, B, sa, za, sb, zb, sc, zc)
+        assert np.array_equal(got, want), f"scales {sa} {sb} {sc}: {(got != want).sum()} differ"
+
+
+def test_binary_bench_size(gpu):
+    # the size the benchmark times: [8192, 8192] uint8 plus a row vector
+    r = np.random.default_rng(12)
+    A, B = _codes(r, (8192, 8192), "u8"), _codes(r, (8192,), "u8")
+    p = _params(r, "add", "u8")
+    log("binary add at [8192, 8192] + [8192]")
+    got = _run_binary(gpu, "add", "u8", A, B, *p)
+    # 256 sampled rows: each output row depends only on its row of A and B
+    rows = np.sort(r.choice(8192, 256, replace=False))
+    want = oracle.qlinear_add(A[rows], p[0], p[1], B, p[2], p[3], p[4], p[5])
+    assert np.array_equal(got[rows], want)
+
+
+# ======================================================= one-code functions
+
+def _run_unary(dq, fn, t, X, xs, xz, ys, yz, alpha=0.01, offset=0):
+    import torch
+
+    n = X.size
+    xd = torch.empty(n + offset, dtype=_tdt(t), device="cuda")
+    xd[offset:] = _dev(X.reshape(-1))
+    y = torch.empty(n + offset, dtype=_tdt(t), device="cuda")
+    if fn == "leaky":
+        dq.qlinear_leaky_relu(xd[offset:], _scal(xs), _zp(xz, t), _scal(ys), _zp(yz, t),
+                              _type(dq, t), y[offset:], alpha=alpha)
+    else:
+        dq.qlinear_sigmoid(xd[offset:], _scal(xs), _zp(xz, t), _scal(ys), _zp(yz, t),
+                           _type(dq, t), y[offset:])
+    torch.cuda.synchronize()
+    return y[offset:].cpu().numpy().reshape(X.shape)
+
+
+def _want_unary(fn, X, xs, xz, ys, yz, alpha=0.01):
+    if fn == "leaky":
+        return oracle.qlinear_leaky_relu(X, xs, xz, ys, yz, alpha)
+    return oracle.qlinear_sigmoid(X, xs, xz, ys, yz)
+
+
+UNARY_PARAMS = [
+    (0.0625, 0, 1 / 256, -128, 0.01),
+    (0.05, 7, 0.02, 3, 0.2),
+    (np.float32(0.0371), -5, np.float32(0.0093), 11, 0.01),
+    (1e-30, 0, 1e-39, 0, 0.5),      # tiny output scale: IEEE division in the table
+    (0.5, 100, 0.25, 50, 1.0),
+]
+
+
+@pytest.mark.parametrize("fn", ["leaky", "sigmoid"])
+@pytest.mark.parametrize("t", ["u8", "i8"])
+@pytest.mark.parametrize("prm", UNARY_PARAMS)
+def test_unary_every_code(gpu, fn, t, prm):
+    xs, xz, ys, yz, alpha = prm
+    if t == "u8":
+        xz, yz = abs(xz) + 100, abs(yz) + 20
+        if fn == "sigmoid":
+            yz = 0
+    lo = 0 if t == "u8" else -128
+    X = np.arange(lo, lo + 256).astype(np.uint8 if t == "u8" else np.int8)
+    got = _run_unary(gpu, fn, t, X, xs, xz, ys, yz, alpha)
+    want = _want_unary(fn, X, xs, xz, ys, yz, alpha)
+    assert np.array_equal(got, want), f"{(got != want).sum()} codes differ"
+
+
+@pytest.mark.parametrize("fn", ["leaky", "sigmoid"])
+@pytest.mark.parametrize("n,offset", [(1000003, 0), (4096 * 1024, 0), (65537, 1), (15, 0), (1, 3)])
+def test_unary_streams(gpu, fn, n, offset):
+    r = np.random.default_rng(n + offset)
+    X = _codes(r, (n,), "i8")
+    got = _run_unary(gpu, fn, "i8", X, 0.04, -3, 0.01, 2, 0.1, offset=offset)
+    assert np.array_equal(got, _want_unary(fn, X, 0.04, -3, 0.01, 2, 0.1))
+
+
+# ============================================================== reductions
+
+REDUCE_GPU = [
+    ((3, 4, 5), [1]), ((3, 4, 5), [0, 2]), ((3, 4, 5), None), ((3, 4, 5), [-1]),
+    ((2, 3, 4, 5), [1, 2]), ((2, 3, 4, 5), [0, 3]), ((7,), [0]), ((6, 1, 4), [1]),
+    ((64, 512, 7, 7), [2, 3]),     # global average pool: rows of 49
+    ((256, 4096), [1]),            # rows, 16-byte chunks, 64 lanes a row
+    ((4096, 256), [0]),            # columns, split over workgroups for the sum
+    ((8, 49, 2048), [1]),          # columns of an NHWC pool
+    ((3, 1000, 5), [1]),           # columns, one byte a lane
+    ((2, 1 << 20), [1]),           # two long rows
+    ((1 << 18, 3), [0]),           # three long columns
+    ((70000, 2, 16), [1]),         # many column groups (more than 65535)
+    ((4, 6, 8), [0, 1, 2]),        # everything
+    ((5, 1, 7), [1]),              # only a size-1 dim reduced: count 1
+]
+
+
+def _run_reduce(dq, mode, t, X, axes, prm=None):
+    import torch
+
+    mask = oracle._axes_mask(X.ndim, axes)
+    kept = [n for d, n in enumerate(X.shape) if not mask >> d & 1]
+    nout = int(np.prod(kept)) if kept else 1
+    xd = _dev(X)
+    if mode == "sum":
+        y = torch.empty(nout, dtype=torch.int32, device="cuda")
+        dq.dq_reduce_sum_integer(xd, _type(dq, t), axes, y)
+    else:
+        xs, xz, ys, yz = prm
+        y = torch.empty(nout, dtype=_tdt(t), device="cuda")
+        dq.qlinear_reduce_mean(xd, _type(dq, t), axes, _scal(xs), _zp(xz, t), _scal(ys), _zp(yz, t),
+                               y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape,axes", REDUCE_GPU)
+@pytest.mark.parametrize("t", ["u8", "i8"])
+def test_reduce_sum_integer_matches_oracle(gpu, shape, axes, t):
+    r = np.random.default_rng(_seed(shape, str(axes), t))
+    X = _codes(r, shape, t)
+    log(f"reduce_sum {t} {shape} axes {axes}")
+    got = _run_reduce(gpu, "sum", t, X, axes)
+    want = oracle.reduce_sum_integer(X, axes, keepdims=False).reshape(-1)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{(got != want.view(np.int32)).sum()} differ"
+
+
+@pytest.mark.parametrize("shape,axes", REDUCE_GPU)
+@pytest.mark.parametrize("t", ["u8", "i8"])
+def test_qlinear_reduce_mean_matches_oracle(gpu, shape, axes, t):
+    r = np.random.default_rng(_seed(shape, str(axes), t, 1))
+    X = _codes(r, shape, t)
+    prm = (np.float32(0.0213), 5 if t == "i8" else 121, np.float32(0.0041), -7 if t == "i8" else 119)
+    log(f"reduce_mean {t} {shape} axes {axes}")
+    got = _run_reduce(gpu, "mean", t, X, axes, prm)
+    want = oracle.qlinear_reduce_mean(X, *prm, axes=axes, keepdims=False).reshape(-1)
+    assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ"
+
+
+def test_reduce_mean_ties(gpu):
+    # power-of-two scales: means like 1.5 and 2.5 land exactly on ties
+    X = np.array([[1, 2], [2, 3], [3, 4], [0, 5], [255, 255]], np.uint8)
+    got = _run_reduce(gpu, "mean", "u8", X, [1], (1.0, 0, 1.0, 0))
+    assert got.tolist() == oracle.qlinear_reduce_mean(X, 1.0, 0, 1.0, 0, [1], False).tolist()
+    assert got.tolist() == [2, 2, 4, 2, 255]
+
+
+def test_reduce_sum_wraps_like_int32(gpu):
+    # 2^24 codes of 255 sum to 255 * 2^24 >= 2^31: the int32 accumulation
+    # wraps, and its bit pattern is the exact uint32 sum
+    X = np.full((2, 1 << 24), 255, np.uint8)
+    got = _run_reduce(gpu, "sum", "u8", X, [1])
+    assert got.view(np.uint32).tolist() == [255 << 24] * 2
+
+
+def test_reduce_sum_over_an_empty_axis_is_zero(gpu):
+    import torch
+
+    y = torch.full((6,), 7, dtype=torch.int32, device="cuda")
+    x = torch.empty(0, dtype=torch.uint8, device="cuda")
+    gpu.dq_reduce_sum_integer(x, gpu.DQ_U8, [1], y, shape=(6, 0))
+    torch.cuda.synchronize()
+    assert y.cpu().tolist() == [0] * 6
+
+
+# ================================================================= concat
+
+CONCAT_CASES = [
+    (((2, 16, 8), (2, 32, 8), (2, 16, 8)), 1),     # 16-byte rows
+    (((4, 5, 7), (4, 3, 7)), 1),                   # ragged rows
+    (((3, 4), (5, 4), (1, 4)), 0),
+    (((6, 10), (6, 6)), -1),
+    (((2, 3, 49), (2, 0, 49), (2, 5, 49)), 1),     # an empty input
+    (((1, 64, 56, 56), (1, 32, 56, 56)), 1),       # NCHW channel concat
+    (((128, 256), (128, 512), (128, 256), (128, 1024)), 1),
+]
+
+
+@pytest.mark.parametrize("shapes,axis", CONCAT_CASES)
+@pytest.mark.parametrize("t", ["u8", "i8"])
+def test_qlinear_concat_matches_oracle(gpu, shapes, axis, t):
+    import torch
+
+    r = np.random.default_rng(_seed(shapes, axis, t))
+    lo, hi = (0, 256) if t == "u8" else (-128, 128)
+    ins = []
+    for i, s in enumerate(shapes):
+        x = _codes(r, s, t)
+        sc = np.float32(r.uniform(0.01, 0.05)) if i != 1 else np.float32(0.02)
+        ins.append((x, sc, int(r.integers(lo, hi))))
+    ys, yz = np.float32(0.02), int(r.integers(lo, hi))
+    want = oracle.qlinear_concat(ins, ys, yz, axis)
+    dev = [(_dev(x), _scal(s), _zp(z, t)) for x, s, z in ins]
+    y = torch.empty(want.shape, dtype=_tdt(t), device="cuda")
+    gpu.qlinear_concat(dev, axis, _scal(ys), _zp(yz, t), _type(gpu, t), y)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.array_equal(got, want), f"{(got != want).sum()} differ"
