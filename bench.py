@@ -14,7 +14,9 @@ The same JSON line carries:
   secondary    -- QuantizeLinear / DequantizeLinear on [64,256,56,56]
                   (GB/s, cold and warm cache), and the other inner-product
                   workloads (64x64x128 latency, the LSTM gate projections,
-                  8192^3 with a B quantized on every call);
+                  8192^3 with a B quantized on every call), the quantized
+                  matrix products, and the element-wise quantized operators
+                  (GB/s against the 8 TB/s HBM peak);
   cpu_baseline -- the CPU oracle on a bounded sample of rows of the same
                   4096^3 workload, single-threaded.
 
@@ -357,6 +359,114 @@ def bench_qgemm(dq, torch, kind, steps, flush):
             "us_cold_p90": round(cold[2] * 1e3, 2), "info": info}
 
 
+def bench_elementwise(dq, torch, steps, flush):
+    """The element-wise quantized operators (workloads.elementwise_case): GB/s
+    of algorithmic bytes (each input and output byte once), cold (median,
+    p10, p90 after a read flush; the flush's run time hides the host's
+    enqueue, so this is the kernel's time) and back to back. Calls go
+    straight to the C ABI with their arguments marshalled once."""
+    import ctypes as C
+
+    import workloads as W
+
+    lib = dq.load()
+    st = torch.cuda.current_stream().cuda_stream
+    out = {}
+
+    def ck(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: {rc} {lib.dqip_last_error()}")
+
+    def i64(vals):
+        return (C.c_int64 * max(1, len(vals)))(*[int(v) for v in vals])
+
+    for kind in W.ELEMENTWISE:
+        c = W.elementwise_case(kind)
+        t = dq.DQ_U8 if c["type"] == "u8" else dq.DQ_I8
+        tdt = torch.uint8 if c["type"] == "u8" else torch.int8
+        zdt = np.uint8 if c["type"] == "u8" else np.int8
+        xs = [dev_tensor(x, torch) for x in c["xs"]]
+        sc = [dev_tensor(np.array([v], np.float32), torch) for v in c["scales"]]
+        zp = [dev_tensor(np.array([v], zdt), torch) for v in c["zps"]]
+        P = lambda tt: tt.data_ptr()  # noqa: E731
+        keep = []
+        if kind in ("add", "add_rowvec", "mul", "mul_integer"):
+            A, B = xs
+            shape = np.broadcast_shapes(tuple(A.shape), tuple(B.shape))
+            sa, sb = i64(A.shape), i64(B.shape)
+            keep += [sa, sb]
+            if kind == "mul_integer":
+                Y = torch.empty(shape, dtype=torch.int32, device="cuda")
+                args = (P(A), A.dim(), sa, P(zp[0]), P(B), B.dim(), sb, P(zp[1]), t, P(Y), st)
+                call = lib.dq_mul_integer
+                nbytes = A.numel() + B.numel() + 4 * Y.numel()
+            else:
+                Y = torch.empty(shape, dtype=tdt, device="cuda")
+                args = (P(A), A.dim(), sa, P(sc[0]), P(zp[0]), P(B), B.dim(), sb, P(sc[1]), P(zp[1]),
+                        P(sc[2]), P(zp[2]), t, P(Y), st)
+                call = lib.qlinear_mul if kind == "mul" else lib.qlinear_add
+                nbytes = A.numel() + B.numel() + Y.numel()
+            desc = f"{c['type']} {tuple(A.shape)} with {tuple(B.shape)}"
+        elif kind in ("sigmoid", "leaky_relu"):
+            X = xs[0]
+            Y = torch.empty_like(X)
+            if kind == "sigmoid":
+                call = lib.qlinear_sigmoid
+                args = (P(X), X.numel(), P(sc[0]), P(zp[0]), P(sc[1]), P(zp[1]), t, P(Y), st)
+            else:
+                call = lib.qlinear_leaky_relu
+                args = (P(X), X.numel(), P(sc[0]), P(zp[0]), P(sc[1]), P(zp[1]), float(c["alpha"]), t,
+                        P(Y), st)
+            nbytes = 2 * X.numel()
+            desc = f"{c['type']} {X.numel()} codes"
+        elif kind.startswith(("sum_", "mean_")):
+            X = xs[0]
+            axes = (C.c_int32 * len(c["axes"]))(*c["axes"])
+            shp = i64(X.shape)
+            keep += [axes, shp]
+            nout = X.numel()
+            for a in c["axes"]:
+                nout //= X.shape[a]
+            if kind.startswith("sum_"):
+                Y = torch.empty(nout, dtype=torch.int32, device="cuda")
+                call = lib.dq_reduce_sum_integer
+                args = (P(X), t, X.dim(), shp, axes, len(c["axes"]), P(Y), st)
+                nbytes = X.numel() + 4 * nout
+            else:
+                Y = torch.empty(nout, dtype=tdt, device="cuda")
+                call = lib.qlinear_reduce_mean
+                args = (P(X), t, X.dim(), shp, axes, len(c["axes"]), P(sc[0]), P(zp[0]), P(sc[1]),
+                        P(zp[1]), P(Y), st)
+                nbytes = X.numel() + nout
+            desc = f"{c['type']} {tuple(X.shape)} over axes {c['axes']}"
+        else:  # concat
+            ax = c["axis"]
+            shape = list(xs[0].shape)
+            shape[ax] = sum(int(x.shape[ax]) for x in xs)
+            Y = torch.empty(shape, dtype=tdt, device="cuda")
+            n = len(xs)
+            xa = (C.c_void_p * n)(*[P(x) for x in xs])
+            sha = i64([v for x in xs for v in x.shape])
+            sca = (C.c_void_p * n)(*[P(v) for v in sc[:n]])
+            zpa = (C.c_void_p * n)(*[P(v) for v in zp[:n]])
+            keep += [xa, sha, sca, zpa]
+            call = lib.qlinear_concat
+            args = (n, C.cast(xa, C.c_void_p), C.cast(sha, C.c_void_p), xs[0].dim(), ax,
+                    C.cast(sca, C.c_void_p), C.cast(zpa, C.c_void_p), P(sc[n]), P(zp[n]), t, P(Y), st)
+            nbytes = 2 * Y.numel()
+            desc = f"{c['type']} {n} x {tuple(xs[0].shape)} along axis {ax}"
+        fn = lambda call=call, args=args, kind=kind: ck(call(*args), kind)  # noqa: E731
+        rec = _bw_record(nbytes, *time_cold_warm(fn, torch, steps, flush))
+        rec["workload"] = desc
+        rec["bytes_per_call"] = int(nbytes)
+        out[kind] = rec
+        log(f"bench: elementwise {kind}: {rec}")
+        del xs, sc, zp, Y, keep
+    out["timing"] = ("cold: median (p10, p90) of calls each after a 512 MiB read flush; warm: back to "
+                     "back on one buffer set (host-bound below ~15 us)")
+    return out
+
+
 def bench_dqip_case(dq, torch, case, steps, warmup, flush):
     """Back-to-back forwards (warm: a recurrence keeps its weights cache-
     resident), their per-phase kernel times, and single forwards after a
@@ -475,6 +585,8 @@ def main():
             log(f"bench: {name}")
             secondary[name] = bench_qgemm(dq, torch, kind, steps2, flush)
             log(f"bench: {secondary[name]}")
+        log("bench: element-wise quantized operators")
+        secondary["elementwise"] = bench_elementwise(dq, torch, steps2, flush)
         del flush
 
     cpu = None

@@ -156,6 +156,15 @@ __device__ __forceinline__ void store_bytes(uint8_t* p, const Bytes<E>& b) {
     }
 }
 
+// Keeps a lane's loads issued ahead of the work that uses them: the memory
+// clobber stops the loads from sinking below it and the scheduling barrier
+// stops later arithmetic from being hoisted above it, so all of them are in
+// flight before the first wait.
+__device__ __forceinline__ void issue_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ uint32_t byte_of(const uint32_t* w, int j) {
     return (w[j >> 2] >> (8 * (j & 3))) & 0xffu;
 }
@@ -214,8 +223,9 @@ __device__ __forceinline__ Bytes<E> lookup(const uint8_t* tab, const Bytes<E>& i
 }
 
 // Y = tab[X] over a flat tensor of n bytes in E-byte vectors (x, y
-// E-aligned); four vectors per lane in flight; the last n % E bytes by
-// block 0.
+// E-aligned). A block-iteration covers 1024 whole vectors, four per lane,
+// all loads issued before the first lookup; the vectors past the last whole
+// block-iteration and the last n % E bytes go to the grid's last block.
 template <bool U8, int F, int E>
 __global__ void __launch_bounds__(256)
 k_table_map(const uint8_t* __restrict__ x, uint64_t n, TableArgs a, uint8_t* __restrict__ y) {
@@ -223,23 +233,23 @@ k_table_map(const uint8_t* __restrict__ x, uint64_t n, TableArgs a, uint8_t* __r
     build_table<U8, F>(tab, a);
     __syncthreads();
     const uint64_t nv = n / E;
-    const uint64_t stride = (uint64_t)gridDim.x * 1024;
-    for (uint64_t base = (uint64_t)blockIdx.x * 1024 + threadIdx.x; base < nv; base += stride) {
+    const uint64_t nfull = nv / 1024;
+    for (uint64_t it = blockIdx.x; it < nfull; it += gridDim.x) {
+        const uint64_t base = it * 1024 + threadIdx.x;
         Bytes<E> v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint64_t i = std::min(base + q * 256, nv - 1);
-            v[q] = load_bytes<E>(x + i * E);
-        }
+        for (int q = 0; q < 4; ++q) v[q] = load_bytes<E>(x + (base + q * 256) * E);
+        issue_fence();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint64_t i = base + q * 256;
-            if (i < nv) store_bytes<E>(y + i * E, lookup<E>(tab, v[q]));
-        }
+        for (int q = 0; q < 4; ++q) store_bytes<E>(y + (base + q * 256) * E, lookup<E>(tab, v[q]));
     }
-    if (E > 1 && blockIdx.x == 0 && threadIdx.x < n % E) {
-        const uint64_t e = nv * E + threadIdx.x;
-        y[e] = tab[x[e]];
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = nfull * 1024 + threadIdx.x; i < nv; i += 256)
+            store_bytes<E>(y + i * E, lookup<E>(tab, load_bytes<E>(x + i * E)));
+        if (E > 1 && threadIdx.x < n % E) {
+            const uint64_t e = nv * E + threadIdx.x;
+            y[e] = tab[x[e]];
+        }
     }
 }
 
@@ -254,25 +264,23 @@ k_concat_part(const uint8_t* __restrict__ x, uint32_t nchunks, dq::FastDiv row_c
     __shared__ uint8_t tab[256];
     build_table<U8, FN_REQUANT>(tab, a);
     __syncthreads();
-    const uint64_t stride = (uint64_t)gridDim.x * 1024;
-    for (uint64_t base = (uint64_t)blockIdx.x * 1024 + threadIdx.x; base < nchunks; base += stride) {
+    auto put = [&](uint32_t c, const Bytes<E>& v) {
+        const uint32_t o = dq::fdiv(c, row_chunks);
+        const uint32_t k = c - o * row_chunks.d;
+        store_bytes<E>(y + (uint64_t)o * ystride + yoff + (uint64_t)k * E, lookup<E>(tab, v));
+    };
+    const uint32_t nfull = nchunks / 1024;
+    for (uint32_t it = blockIdx.x; it < nfull; it += gridDim.x) {
+        const uint32_t base = it * 1024 + threadIdx.x;
         Bytes<E> v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint64_t i = std::min(base + q * 256, (uint64_t)nchunks - 1);
-            v[q] = load_bytes<E>(x + i * E);
-        }
+        for (int q = 0; q < 4; ++q) v[q] = load_bytes<E>(x + (uint64_t)(base + q * 256) * E);
+        issue_fence();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint64_t i = base + q * 256;
-            if (i < nchunks) {
-                const uint32_t c = (uint32_t)i;
-                const uint32_t o = dq::fdiv(c, row_chunks);
-                const uint32_t k = c - o * row_chunks.d;
-                store_bytes<E>(y + (uint64_t)o * ystride + yoff + (uint64_t)k * E, lookup<E>(tab, v[q]));
-            }
-        }
+        for (int q = 0; q < 4; ++q) put(base + q * 256, v[q]);
     }
+    if (blockIdx.x == gridDim.x - 1)
+        for (uint32_t i = nfull * 1024 + threadIdx.x; i < nchunks; i += 256) put(i, load_bytes<E>(x + (uint64_t)i * E));
 }
 
 // ================================================================= binary
@@ -369,55 +377,65 @@ __global__ void __launch_bounds__(256) k_binary(BinArgs p) {
             ab = *p.a_scale * *p.b_scale;
         }
     }
-    const uint64_t stride = (uint64_t)gridDim.x * 1024;
-    for (uint64_t base = (uint64_t)blockIdx.x * 1024 + threadIdx.x; base < p.nchunks; base += stride) {
+    auto fetch = [&](uint32_t c, Bytes<E>& A, Bytes<E>& B) {
+        uint32_t oa, ob;
+        chunk_offsets<E>(p, c, oa, ob);
+        A = Bytes<E>{};
+        B = Bytes<E>{};
+        if (AV) A = load_bytes<E>(p.a + oa);
+        else A.w[0] = p.a[oa];
+        if (BV) B = load_bytes<E>(p.b + ob);
+        else B.w[0] = p.b[ob];
+    };
+    auto put = [&](uint32_t c, Bytes<E> A, Bytes<E> B) {
+#pragma unroll
+        for (int k = 0; k < (E + 3) / 4; ++k) {
+            A.w[k] ^= kFlip;
+            B.w[k] ^= kFlip;
+        }
+        if (OP == OP_MULINT) {
+            const int iza = (int)za, izb = (int)zb;
+            int32_t r[E];
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const int a = (int)(AV ? byte_of(A.w, j) : (A.w[0] & 0xffu)) - iza;
+                const int b = (int)(BV ? byte_of(B.w, j) : (B.w[0] & 0xffu)) - izb;
+                r[j] = __mul24(a, b);
+            }
+            int32_t* out = (int32_t*)p.c + (uint64_t)c * E;
+            if constexpr (E == 4) {
+                const dq::v4i v = {r[0], r[1], r[2], r[3]};
+                __builtin_nontemporal_store(v, reinterpret_cast<dq::v4i*>(out));
+            } else {
+#pragma unroll
+                for (int j = 0; j < E; ++j) out[j] = r[j];
+            }
+        } else {
+            Bytes<E> o;
+            if (q.fast)
+                o = quant_chunk<OP, true, E, AV, BV>(A, B, za, zb, sa, sb, ab, q);
+            else
+                o = quant_chunk<OP, false, E, AV, BV>(A, B, za, zb, sa, sb, ab, q);
+            store_bytes<E>((uint8_t*)p.c + (uint64_t)c * E, o);
+        }
+    };
+    // whole block-iterations of 1024 chunks: the eight loads of a lane are
+    // issued before any arithmetic; the rest goes to the grid's last block
+    const uint32_t nfull = p.nchunks / 1024;
+    for (uint32_t it = blockIdx.x; it < nfull; it += gridDim.x) {
+        const uint32_t base = it * 1024 + threadIdx.x;
         Bytes<E> A[4], B[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t c = (uint32_t)std::min(base + u * 256, (uint64_t)p.nchunks - 1);
-            uint32_t oa, ob;
-            chunk_offsets<E>(p, c, oa, ob);
-            A[u] = Bytes<E>{};
-            B[u] = Bytes<E>{};
-            if (AV) A[u] = load_bytes<E>(p.a + oa);
-            else A[u].w[0] = p.a[oa];
-            if (BV) B[u] = load_bytes<E>(p.b + ob);
-            else B[u].w[0] = p.b[ob];
+        for (int u = 0; u < 4; ++u) fetch(base + u * 256, A[u], B[u]);
+        issue_fence();
 #pragma unroll
-            for (int k = 0; k < (E + 3) / 4; ++k) {
-                A[u].w[k] ^= kFlip;
-                B[u].w[k] ^= kFlip;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint64_t c = base + u * 256;
-            if (c >= p.nchunks) continue;
-            if (OP == OP_MULINT) {
-                const int iza = (int)za, izb = (int)zb;
-                int32_t r[E];
-#pragma unroll
-                for (int j = 0; j < E; ++j) {
-                    const int a = (int)(AV ? byte_of(A[u].w, j) : (A[u].w[0] & 0xffu)) - iza;
-                    const int b = (int)(BV ? byte_of(B[u].w, j) : (B[u].w[0] & 0xffu)) - izb;
-                    r[j] = __mul24(a, b);
-                }
-                int32_t* out = (int32_t*)p.c + c * E;
-                if constexpr (E == 4) {
-                    const dq::v4i v = {r[0], r[1], r[2], r[3]};
-                    __builtin_nontemporal_store(v, reinterpret_cast<dq::v4i*>(out));
-                } else {
-#pragma unroll
-                    for (int j = 0; j < E; ++j) out[j] = r[j];
-                }
-            } else {
-                Bytes<E> o;
-                if (q.fast)
-                    o = quant_chunk<OP, true, E, AV, BV>(A[u], B[u], za, zb, sa, sb, ab, q);
-                else
-                    o = quant_chunk<OP, false, E, AV, BV>(A[u], B[u], za, zb, sa, sb, ab, q);
-                store_bytes<E>((uint8_t*)p.c + c * E, o);
-            }
+        for (int u = 0; u < 4; ++u) put(base + u * 256, A[u], B[u]);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint32_t c = nfull * 1024 + threadIdx.x; c < p.nchunks; c += 256) {
+            Bytes<E> A, B;
+            fetch(c, A, B);
+            put(c, A, B);
         }
     }
 }
@@ -568,15 +586,18 @@ k_reduce_cols(RedArgs a, uint32_t I, uint32_t CW, uint32_t gx, uint32_t rows_per
             for (int e = 0; e < E; ++e) c.tot[e] -= (int32_t)(128u * (uint32_t)mine);
         }
     }
+    // part[rs][col], col = cl * E + e over the block's CW * E columns: every
+    // thread then sums the RS partials of its columns
 #pragma unroll
     for (int e = 0; e < E; ++e) part[threadIdx.x * E + e] = c.tot[e];
     __syncthreads();
-    if (rs == 0 && j < nchunks) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            int32_t s = 0;
-            for (uint32_t t = 0; t < RS; ++t) s += part[(t * CW + cl) * E + e];
-            const uint64_t idx = (uint64_t)o * I + (uint64_t)j * E + e;
+    const uint32_t ncol = CW * E;
+    for (uint32_t col = threadIdx.x; col < ncol; col += 256) {
+        int32_t s = 0;
+        for (uint32_t t = 0; t < RS; ++t) s += part[t * ncol + col];
+        const uint32_t jj = (blockIdx.x - o * gx) * CW + col / E;
+        if (jj < nchunks) {
+            const uint64_t idx = (uint64_t)o * I + (uint64_t)jj * E + col % E;
             if (ATOMIC)
                 atomicAdd((int32_t*)a.y + idx, s);
             else
@@ -947,8 +968,15 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
         // columns
         const int E = vec_width(I, {(uintptr_t)x}, 16);
         const uint64_t nch = I / E;
+        // CW lanes side by side over a row (64: a wave reads 1 KiB of a row
+        // at 16 bytes a lane); the other 256 / CW lanes of the block take
+        // rows in turn. The sum fills the chip by splitting rows over
+        // workgroups; the mean narrows CW instead, down to 8 lanes (128
+        // bytes a row), while the grid would not fill it
         uint32_t CW = 1;
-        while (CW < 256 && CW < nch) CW *= 2;
+        while (CW < 64 && CW < nch) CW *= 2;
+        if (mode == 1)  // the mean cannot split rows over workgroups
+            while (CW > 8 && O * ((nch + CW - 1) / CW) < 2048) CW /= 2;
         const uint64_t gx = (nch + CW - 1) / CW;
         if (gx * O >= (UINT64_C(1) << 31) || I >= (UINT64_C(1) << 32))
             DQ_FAIL(DQ_ERR_RANGE, "%s: shape beyond the column kernel's grid", name);
@@ -957,8 +985,8 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
         uint64_t parts = 1;
         if (mode == 0) {
             const uint64_t blocks = gx * O;
-            const uint64_t rows_min = 1024;
-            while (blocks * parts < 1024 && count / (parts * 2) >= rows_min && parts < 65535) parts *= 2;
+            const uint64_t rows_min = 8 * (256 / CW);  // 8 rows a lane
+            while (blocks * parts < 2048 && count / (parts * 2) >= rows_min && parts < 65535) parts *= 2;
         }
         const uint64_t rpp = (count + parts - 1) / parts;
         if (parts > 1) {

@@ -27,6 +27,13 @@ pages describe in words (no public dataset or benchmark suite is involved):
   default: uint8 A with a zero point (or fp32 A ~N(0,1) with 1% x20
   outliers), int8 B with per-column scales and small per-column zero
   points, bias / int32 C per column, uint8 output for QGemm.
+* ``elementwise_case`` -- the element-wise quantized operators of the ORT
+  schemas at the sizes the benchmark times: uniform 8-bit codes, per-tensor
+  scales and zero points (QLinearAdd / Mul and MulInteger over [8192, 8192]
+  or [4096, 8192], optionally against a broadcast row vector; LeakyRelu /
+  Sigmoid over 64 Mi codes; ReduceSumInteger / QLinearReduceMean over
+  [16384, 4096] rows, [4096, 16384] columns and NCHW / NHWC global pooling
+  of [64, 2048, 7, 7]; QLinearConcat of two [32, 256, 56, 56] maps).
 """
 from __future__ import annotations
 
@@ -289,3 +296,46 @@ def qgemm_case(kind: str, seed: int = 5, M: int = 4096, N: int = 4096, K: int = 
     else:
         case["bias"] = r.uniform(-1.0, 1.0, N).astype(np.float32)
     return case
+
+
+def _codes(r, shape, t):
+    """Uniform 8-bit codes: raw random bytes viewed as uint8 or int8."""
+    n = int(np.prod(shape, dtype=np.int64))
+    w = r.integers(0, np.iinfo(np.uint64).max, (n + 7) // 8, dtype=np.uint64, endpoint=True)
+    b = w.view(np.uint8)[:n].reshape(shape)
+    return b if t == "u8" else b.view(np.int8)
+
+
+# shapes and per-tensor parameters of the element-wise workloads:
+# kind -> (input shapes, type, extra)
+ELEMENTWISE = {
+    "add": ([(8192, 8192), (8192, 8192)], "u8", {}),
+    "add_rowvec": ([(8192, 8192), (8192,)], "u8", {}),
+    "mul": ([(8192, 8192), (8192, 8192)], "u8", {}),
+    "mul_integer": ([(4096, 8192), (4096, 8192)], "u8", {}),
+    "sigmoid": ([(64 << 20,)], "u8", {}),
+    "leaky_relu": ([(64 << 20,)], "u8", {"alpha": 0.1}),
+    "sum_rows": ([(16384, 4096)], "u8", {"axes": [1]}),
+    "sum_cols": ([(4096, 16384)], "u8", {"axes": [0]}),
+    "mean_rows": ([(16384, 4096)], "u8", {"axes": [1]}),
+    "mean_pool_nchw": ([(64, 2048, 7, 7)], "u8", {"axes": [2, 3]}),
+    "mean_pool_nhwc": ([(64, 49, 2048)], "u8", {"axes": [1]}),
+    "concat": ([(32, 256, 56, 56), (32, 256, 56, 56)], "u8", {"axis": 1}),
+}
+
+
+def elementwise_case(kind: str, seed: int = 6):
+    """Inputs of one element-wise workload: uniform codes of the listed
+    shapes and per-tensor scales / zero points (one per input plus the
+    output's), all fixed by the seed."""
+    shapes, t, extra = ELEMENTWISE[kind]
+    r = rng(seed)
+    xs = [_codes(r, s, t) for s in shapes]
+    scales = [np.float32(v) for v in r.uniform(0.005, 0.05, len(shapes) + 1)]
+    lo, hi = (0, 256) if t == "u8" else (-128, 128)
+    zps = [int(v) for v in r.integers(lo, hi, len(shapes) + 1)]
+    if kind == "mul":
+        scales[-1] = np.float32(r.uniform(0.5, 4.0))
+    if kind == "sigmoid":
+        scales[-1], zps[-1] = np.float32(1.0 / 256), lo
+    return dict(name=kind, xs=xs, type=t, scales=scales, zps=zps, **extra)
