@@ -131,13 +131,13 @@ template <int E>
 __device__ __forceinline__ Bytes<E> load_bytes(const uint8_t* p) {
     Bytes<E> b;
     if constexpr (E == 16) {
-        const dq::u4 v = __builtin_nontemporal_load(reinterpret_cast<const dq::u4*>(p));
+        const dq::u4 v = *reinterpret_cast<const dq::u4*>(p);
         b.w[0] = v[0];
         b.w[1] = v[1];
         b.w[2] = v[2];
         b.w[3] = v[3];
     } else if constexpr (E == 4) {
-        b.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        b.w[0] = *reinterpret_cast<const uint32_t*>(p);
     } else {
         b.w[0] = *p;
     }
@@ -148,9 +148,9 @@ template <int E>
 __device__ __forceinline__ void store_bytes(uint8_t* p, const Bytes<E>& b) {
     if constexpr (E == 16) {
         const dq::u4 v = {b.w[0], b.w[1], b.w[2], b.w[3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<dq::u4*>(p));
+        *reinterpret_cast<dq::u4*>(p) = v;
     } else if constexpr (E == 4) {
-        __builtin_nontemporal_store(b.w[0], reinterpret_cast<uint32_t*>(p));
+        *reinterpret_cast<uint32_t*>(p) = b.w[0];
     } else {
         *p = (uint8_t)b.w[0];
     }
@@ -253,34 +253,58 @@ k_table_map(const uint8_t* __restrict__ x, uint64_t n, TableArgs a, uint8_t* __r
     }
 }
 
-// One input of QLinearConcat: `rows` rows of `len` bytes, contiguous in x,
-// go through the input's requantization table to y + o * ystride + yoff.
-// len, ystride, yoff and both pointers are multiples of E; rows * len / E
-// < 2^32.
+// QLinearConcat of up to kCatMax inputs in one launch. Input j owns blocks
+// [block0_j, block0_j + ceil(nchunks_j / 1024)): its rows (rows of len_j
+// bytes, contiguous in x_j) go through the input's requantization table to
+// y + o * ystride + yoff_j. len_j, ystride, yoff_j and every pointer are
+// multiples of E; nchunks_j = rows * len_j / E < 2^32. A block covers 1024
+// chunks, four per lane, loads issued before the table lookups.
+constexpr int kCatMax = 8;
+
+struct CatPart {
+    const uint8_t* x;
+    const float* scale;
+    const void* zp;
+    uint64_t yoff;
+    dq::FastDiv row_chunks;
+    uint32_t nchunks;
+    uint32_t block0;
+};
+
+struct CatArgs {
+    CatPart part[kCatMax];
+    int n;
+    uint64_t ystride;
+    const float* y_scale;
+    const void* y_zp;
+    uint8_t* y;
+};
+
 template <bool U8, int E>
-__global__ void __launch_bounds__(256)
-k_concat_part(const uint8_t* __restrict__ x, uint32_t nchunks, dq::FastDiv row_chunks,
-              uint64_t ystride, uint64_t yoff, TableArgs a, uint8_t* __restrict__ y) {
+__global__ void __launch_bounds__(256) k_concat(CatArgs a) {
     __shared__ uint8_t tab[256];
-    build_table<U8, FN_REQUANT>(tab, a);
+    int j = 0;
+    for (int k = 1; k < a.n; ++k)
+        if (blockIdx.x >= a.part[k].block0) j = k;
+    const CatPart& p = a.part[j];
+    build_table<U8, FN_REQUANT>(tab, TableArgs{p.scale, p.zp, a.y_scale, a.y_zp, 0.0f});
     __syncthreads();
     auto put = [&](uint32_t c, const Bytes<E>& v) {
-        const uint32_t o = dq::fdiv(c, row_chunks);
-        const uint32_t k = c - o * row_chunks.d;
-        store_bytes<E>(y + (uint64_t)o * ystride + yoff + (uint64_t)k * E, lookup<E>(tab, v));
+        const uint32_t o = dq::fdiv(c, p.row_chunks);
+        const uint32_t k = c - o * p.row_chunks.d;
+        store_bytes<E>(a.y + (uint64_t)o * a.ystride + p.yoff + (uint64_t)k * E, lookup<E>(tab, v));
     };
-    const uint32_t nfull = nchunks / 1024;
-    for (uint32_t it = blockIdx.x; it < nfull; it += gridDim.x) {
-        const uint32_t base = it * 1024 + threadIdx.x;
+    const uint32_t base = (blockIdx.x - p.block0) * 1024 + threadIdx.x;
+    if (base - threadIdx.x + 1024 <= p.nchunks) {
         Bytes<E> v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = load_bytes<E>(x + (uint64_t)(base + q * 256) * E);
+        for (int q = 0; q < 4; ++q) v[q] = load_bytes<E>(p.x + (uint64_t)(base + q * 256) * E);
         issue_fence();
 #pragma unroll
         for (int q = 0; q < 4; ++q) put(base + q * 256, v[q]);
+    } else {
+        for (uint32_t c = base; c < p.nchunks; c += 256) put(c, load_bytes<E>(p.x + (uint64_t)c * E));
     }
-    if (blockIdx.x == gridDim.x - 1)
-        for (uint32_t i = nfull * 1024 + threadIdx.x; i < nchunks; i += 256) put(i, load_bytes<E>(x + (uint64_t)i * E));
 }
 
 // ================================================================= binary
@@ -405,7 +429,7 @@ __global__ void __launch_bounds__(256) k_binary(BinArgs p) {
             int32_t* out = (int32_t*)p.c + (uint64_t)c * E;
             if constexpr (E == 4) {
                 const dq::v4i v = {r[0], r[1], r[2], r[3]};
-                __builtin_nontemporal_store(v, reinterpret_cast<dq::v4i*>(out));
+                *reinterpret_cast<dq::v4i*>(out) = v;
             } else {
 #pragma unroll
                 for (int j = 0; j < E; ++j) out[j] = r[j];
@@ -508,17 +532,71 @@ __global__ void __launch_bounds__(256) k_reduce_rows(RedArgs a, uint32_t O) {
     if (li == 0 && row < O) finish<U8, MODE>(a, row, acc);
 }
 
+// Short rows that are not a multiple of 16 bytes (e.g. 7 x 7 pooling): a
+// block's rows [row0, row0 + nrows) are one contiguous span of the tensor,
+// read in aligned 16-byte windows (bytewise only for a window that crosses
+// the tensor's end) into LDS; a thread then sums a row from LDS as 4-byte
+// words, masking the bytes of its neighbours in the first and last word.
+// x is 16-aligned; rows_per_block * count + 32 <= kStageBytes.
+constexpr uint32_t kStageBytes = 8192 + 32;
+
+template <bool U8, int MODE>
+__global__ void __launch_bounds__(256) k_reduce_rows_staged(RedArgs a, uint32_t O, uint32_t rows_per_block) {
+    __shared__ uint32_t span[kStageBytes / 4];
+    const uint64_t R = a.count;
+    const uint64_t n = (uint64_t)O * R;
+    const uint32_t row0 = blockIdx.x * rows_per_block;
+    const uint32_t nrows = std::min(rows_per_block, O - row0);
+    const uint64_t start = (uint64_t)row0 * R, end = start + (uint64_t)nrows * R;
+    const uint64_t ws = start & ~(uint64_t)15;
+    const uint32_t nw = (uint32_t)((((end + 15) & ~(uint64_t)15) - ws) / 16);
+    for (uint32_t w = threadIdx.x; w < nw; w += 256) {
+        const uint64_t off = ws + 16 * (uint64_t)w;
+        Bytes<16> v;
+        if (off + 16 <= n) {
+            v = load_bytes<16>(a.x + off);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t word = 0;
+                for (int b = 0; b < 4; ++b) {
+                    const uint64_t e = off + 4 * k + b;
+                    if (e < n) word |= (uint32_t)a.x[e] << (8 * b);
+                }
+                v.w[k] = word;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) span[4 * w + k] = v.w[k];
+    }
+    __syncthreads();
+    for (uint32_t r = threadIdx.x; r < nrows; r += 256) {
+        const uint32_t b0 = (uint32_t)((uint64_t)(row0 + r) * R - ws), b1 = b0 + (uint32_t)R;
+        int32_t acc = 0;
+        for (uint32_t d = b0 / 4; d < (b1 + 3) / 4; ++d) {
+            const int lo = (int)std::max<int64_t>((int64_t)b0 - 4 * (int64_t)d, 0);
+            const int hi = (int)std::min<int64_t>((int64_t)b1 - 4 * (int64_t)d, 4);
+            const uint32_t mask = (hi == 4 ? 0xffffffffu : ((1u << (8 * hi)) - 1u)) & ~((1u << (8 * lo)) - 1u);
+            Bytes<4> b;
+            b.w[0] = span[d] & mask;
+            acc = sum_bytes<U8, 4>(b, acc);
+        }
+        finish<U8, MODE>(a, row0 + r, acc);
+    }
+}
+
 // Columns: X is [O, R, I] (R = a.count), I % E == 0, x E-aligned. Block
 // (blockIdx.x = o * gx + column block, part = blockIdx.z): CW lanes over E-column
-// chunks times 256 / CW lanes over rows; rows [r0, r1) of part z. The
-// partial sums meet in LDS; ATOMIC adds each column's block sum into y.
+// chunks times 256 / CW lanes over rows, U rows a lane in flight; rows
+// [r0, r1) of part z. The partial sums meet in LDS; ATOMIC adds each
+// column's block sum into y.
 template <int E>
 struct ColAcc {
     uint32_t lo[(E + 3) / 4], hi[(E + 3) / 4];  // 16-bit pairs: bytes 0,2 and 1,3
     int32_t tot[E];
 };
 
-template <bool U8, int MODE, int E, bool ATOMIC>
+template <bool U8, int MODE, int E, bool ATOMIC, int U>
 __global__ void __launch_bounds__(256)
 k_reduce_cols(RedArgs a, uint32_t I, uint32_t CW, uint32_t gx, uint32_t rows_per_part) {
     __shared__ int32_t part[256 * E];
@@ -537,16 +615,17 @@ k_reduce_cols(RedArgs a, uint32_t I, uint32_t CW, uint32_t gx, uint32_t rows_per
     for (int k = 0; k < (E + 3) / 4; ++k) c.lo[k] = c.hi[k] = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c.tot[e] = 0;
-    uint32_t pending = 0;  // rows in the 16-bit partial sums
-    for (uint64_t rb = r0 + rs; rb < r1; rb += 4 * RS) {
-        Bytes<E> v[4];
+    uint32_t pending = 0;  // rows in the 16-bit partial sums (at most 255)
+    for (uint64_t rb = r0 + rs; rb < r1; rb += U * RS) {
+        Bytes<E> v[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             const uint64_t r = std::min(rb + (uint64_t)u * RS, r1 - 1);
             v[u] = load_bytes<E>(xo + r * I);
         }
+        issue_fence();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             const bool ok = rb + (uint64_t)u * RS < r1;
             if constexpr (E == 1) {
                 c.tot[0] += ok ? code8<U8>(v[u].w[0]) : 0;
@@ -559,7 +638,7 @@ k_reduce_cols(RedArgs a, uint32_t I, uint32_t CW, uint32_t gx, uint32_t rows_per
                 }
             }
         }
-        if (E > 1 && (pending += 4) >= 252) {
+        if (E > 1 && (pending += U) > 255 - U) {
 #pragma unroll
             for (int k = 0; k < E / 4; ++k) {
                 c.tot[4 * k] += (int32_t)(c.lo[k] & 0xffffu);
@@ -926,6 +1005,22 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
             if (i > rg && rg >= 0) I *= gs[i];
         }
         if (rg < 0) O = n;  // nothing reduced: every output is one element
+        if (I == 1 && count % 16 != 0 && count <= 4096 && (uintptr_t)x % 16 == 0) {
+            const uint32_t rpb = (uint32_t)std::min<uint64_t>(O, (kStageBytes - 32) / count);
+            const unsigned blocks = (unsigned)((O + rpb - 1) / rpb);
+#define DQ_STAGED(U, M) \
+    hipLaunchKernelGGL((k_reduce_rows_staged<U, M>), dim3(blocks), dim3(256), 0, s, a, (uint32_t)O, rpb)
+            if (mode == 0) {
+                if (u8) DQ_STAGED(true, 0);
+                else DQ_STAGED(false, 0);
+            } else {
+                if (u8) DQ_STAGED(true, 1);
+                else DQ_STAGED(false, 1);
+            }
+#undef DQ_STAGED
+            DQ_LAUNCH_CHECK(name);
+            return DQ_OK;
+        }
         if (I == 1) {
             const int E = vec_width(count, {(uintptr_t)x}, 16);
             const uint64_t nch = count / E;
@@ -982,10 +1077,12 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
             DQ_FAIL(DQ_ERR_RANGE, "%s: shape beyond the column kernel's grid", name);
         // ReduceSumInteger splits long columns over workgroups when the
         // grid would not fill the chip
+        // ... with at least four steps of eight rows a lane per part, which
+        // bounds the atomics to one per column per 32 * 256 / CW rows
         uint64_t parts = 1;
         if (mode == 0) {
             const uint64_t blocks = gx * O;
-            const uint64_t rows_min = 8 * (256 / CW);  // 8 rows a lane
+            const uint64_t rows_min = 32 * (256 / CW);
             while (blocks * parts < 2048 && count / (parts * 2) >= rows_min && parts < 65535) parts *= 2;
         }
         const uint64_t rpp = (count + parts - 1) / parts;
@@ -996,8 +1093,8 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
         }
         const dim3 grid((unsigned)(gx * O), 1, (unsigned)parts);
 #define DQ_COLS(U, M, EE, AT) \
-    hipLaunchKernelGGL((k_reduce_cols<U, M, EE, AT>), grid, dim3(256), 0, s, a, (uint32_t)I, CW, \
-                       (uint32_t)gx, (uint32_t)rpp)
+    hipLaunchKernelGGL((k_reduce_cols<U, M, EE, AT, (AT ? 8 : 4)>), grid, dim3(256), 0, s, a, (uint32_t)I, \
+                       CW, (uint32_t)gx, (uint32_t)rpp)
 #define DQ_COLS_E(U, M, AT)                     \
     do {                                        \
         if (E == 16) DQ_COLS(U, M, 16, AT);     \
@@ -1155,32 +1252,28 @@ extern "C" int qlinear_concat(int n_inputs, const void* const* xs, const int64_t
     hipStream_t s = (hipStream_t)stream;
     const bool u8 = type == DQ_U8;
     const uint64_t ystride = total * inner;
-    uint64_t base = 0;
-    for (int j = 0; j < n_inputs; ++j) {
-        const uint64_t len = (uint64_t)shapes[(size_t)j * ndim + axis] * inner;
-        const uint64_t yoff = base * inner;
-        base += (uint64_t)shapes[(size_t)j * ndim + axis];
-        if (len == 0) continue;
-        int E = 1;
-        for (int e : {16, 4}) {
-            if (len % e || ystride % e || yoff % e || (uintptr_t)xs[j] % e || (uintptr_t)y % e) continue;
-            E = e;
-            break;
+    // one vector width for the launch: every input's rows and offsets
+    int E = 16;
+    {
+        uint64_t base = 0;
+        for (int j = 0; j < n_inputs; ++j) {
+            const uint64_t len = (uint64_t)shapes[(size_t)j * ndim + axis] * inner;
+            const uint64_t yoff = base * inner;
+            base += (uint64_t)shapes[(size_t)j * ndim + axis];
+            if (len == 0) continue;
+            while (E > 1 && (len % E || yoff % E || (uintptr_t)xs[j] % E)) E /= 4;
         }
-        const uint64_t nch = outer * len / E;
-        if (nch >= (UINT64_C(1) << 32) || len / E >= (UINT64_C(1) << 32))
-            DQ_FAIL(DQ_ERR_RANGE, "%s: input %d too large", name, j);
-        const TableArgs ta{x_scales[j], x_zero_points ? x_zero_points[j] : nullptr, y_scale, y_zero_point,
-                           0.0f};
-        const dq::FastDiv rc_div = dq::make_fastdiv((uint32_t)(len / E));
-        const uint64_t want = (nch + 1023) / 1024;
-#define DQ_CAT(U, EE)                                                                               \
-    do {                                                                                            \
-        const unsigned g = (unsigned)std::max<uint64_t>(                                            \
-            1, std::min<uint64_t>(want, resident_blocks(k_concat_part<U, EE>, 256)));               \
-        hipLaunchKernelGGL((k_concat_part<U, EE>), dim3(g), dim3(256), 0, s, (const uint8_t*)xs[j], \
-                           (uint32_t)nch, rc_div, ystride, yoff, ta, (uint8_t*)y);                  \
-    } while (0)
+        while (E > 1 && (ystride % E || (uintptr_t)y % E)) E /= 4;
+    }
+    CatArgs ca{};
+    ca.ystride = ystride;
+    ca.y_scale = y_scale;
+    ca.y_zp = y_zero_point;
+    ca.y = (uint8_t*)y;
+    uint64_t blocks = 0, base = 0;
+    auto flush = [&]() -> int {
+        if (ca.n == 0) return DQ_OK;
+#define DQ_CAT(U, EE) hipLaunchKernelGGL((k_concat<U, EE>), dim3((unsigned)blocks), dim3(256), 0, s, ca)
         if (u8) {
             if (E == 16) DQ_CAT(true, 16);
             else if (E == 4) DQ_CAT(true, 4);
@@ -1192,6 +1285,31 @@ extern "C" int qlinear_concat(int n_inputs, const void* const* xs, const int64_t
         }
 #undef DQ_CAT
         DQ_LAUNCH_CHECK(name);
+        ca.n = 0;
+        blocks = 0;
+        return DQ_OK;
+    };
+    for (int j = 0; j < n_inputs; ++j) {
+        const uint64_t len = (uint64_t)shapes[(size_t)j * ndim + axis] * inner;
+        const uint64_t yoff = base * inner;
+        base += (uint64_t)shapes[(size_t)j * ndim + axis];
+        if (len == 0) continue;
+        const uint64_t nch = outer * len / E;
+        if (nch >= (UINT64_C(1) << 32) || len / E >= (UINT64_C(1) << 32))
+            DQ_FAIL(DQ_ERR_RANGE, "%s: input %d too large", name, j);
+        const uint64_t nb = (nch + 1023) / 1024;
+        if (ca.n == kCatMax || blocks + nb >= (UINT64_C(1) << 31))
+            if ((rc = flush())) return rc;
+        CatPart& p = ca.part[ca.n++];
+        p.x = (const uint8_t*)xs[j];
+        p.scale = x_scales[j];
+        p.zp = x_zero_points ? x_zero_points[j] : nullptr;
+        p.yoff = yoff;
+        p.row_chunks = dq::make_fastdiv((uint32_t)(len / E));
+        p.nchunks = (uint32_t)nch;
+        p.block0 = (uint32_t)blocks;
+        blocks += nb;
     }
+    if ((rc = flush())) return rc;
     return DQ_OK;
 }

@@ -348,7 +348,7 @@ void dq_qgemm_release(dq_qgemm_ctx* ctx);
  * dim but `axis`; x_scales[j] (HOST array of DEVICE pointers to one fp32)
  * and x_zero_points[j] (HOST array of DEVICE pointers, NULL array or NULL
  * entry = 0); y of the joined shape. An input with zero length along axis
- * contributes nothing. One launch per input.
+ * contributes nothing. One launch per eight inputs.
  * ---------------------------------------------------------------------- */
 int qlinear_add(const void* A, int a_ndim, const int64_t* a_shape, const float* a_scale,
                 const void* a_zero_point, const void* B, int b_ndim, const int64_t* b_shape,

@@ -234,6 +234,9 @@ REDUCE_GPU = [
     ((70000, 2, 16), [1]),         # many column groups (more than 65535)
     ((4, 6, 8), [0, 1, 2]),        # everything
     ((5, 1, 7), [1]),              # only a size-1 dim reduced: count 1
+    ((37, 4095), [1]),             # the longest rows staged through LDS
+    ((37, 4097), [1]),             # one past it: one byte a lane
+    ((1000, 13), [1]),             # short rows, many per block, ragged end
 ]
 
 
@@ -315,6 +318,8 @@ CONCAT_CASES = [
     (((2, 3, 49), (2, 0, 49), (2, 5, 49)), 1),     # an empty input
     (((1, 64, 56, 56), (1, 32, 56, 56)), 1),       # NCHW channel concat
     (((128, 256), (128, 512), (128, 256), (128, 1024)), 1),
+    (tuple((3, 16 * k + 16, 4) for k in range(10)), 1),   # ten inputs: two launches
+    (tuple((2, k + 1, 3) for k in range(9)), 1),          # nine ragged inputs
 ]
 
 
