@@ -52,6 +52,12 @@ def lib() -> C.CDLL:
         L.oracle_qgemm.argtypes = [vp, i32, i32, i64, i64, f32, i32, vp, i32, i32, i64,
                                    vp, i64, vp, i64, vp, i64, i64, f32, vp, i32, f32, i32,
                                    vp, vp]
+        L.oracle_f16_to_f32.argtypes = [C.c_uint16]
+        L.oracle_f16_to_f32.restype = C.c_float
+        L.oracle_f32_to_f16.argtypes = [C.c_float]
+        L.oracle_f32_to_f16.restype = C.c_uint16
+        L.oracle_f16_to_f32_array.argtypes = [vp, i64, vp]
+        L.oracle_f32_to_f16_array.argtypes = [vp, i64, vp]
         L.oracle_broadcast_shape.argtypes = [i32, vp, i32, vp, vp, vp]
         L.oracle_qlinear_binary.argtypes = [i32, i32, vp, i32, vp, f32, i32, vp, i32, vp,
                                             f32, i32, f32, i32, vp]
@@ -122,6 +128,34 @@ def quantize_linear(x, scale, zp, *, axis=None, y_type="i8"):
                                       _TYPE[y_type], _p(y))
     _check(rc, "quantize_linear")
     return y
+
+
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns (uint16) -> fp32, exactly (R24)."""
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, np.float32)
+    lib().oracle_f16_to_f32_array(_p(b), b.size, _p(out))
+    return out
+
+
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> binary16 bit patterns, round to nearest even (R24)."""
+    a = _c(x, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_f32_to_f16_array(_p(a), a.size, _p(out))
+    return out
+
+
+def quantize_linear_f16(x_bits, scale_bits, zp, *, axis=None, y_type="i8"):
+    """QuantizeLinear of an fp16 x with fp16 scales (bit patterns), R24."""
+    return quantize_linear(f16_to_f32(x_bits), f16_to_f32(np.atleast_1d(scale_bits)), zp,
+                           axis=axis, y_type=y_type)
+
+
+def dequantize_linear_f16(x, scale_bits, zp, *, axis=None, y_type="f16"):
+    """DequantizeLinear with fp16 scales: fp16 y (bit patterns) or fp32 y, R24."""
+    y = dequantize_linear(x, f16_to_f32(np.atleast_1d(scale_bits)), zp, axis=axis)
+    return f32_to_f16(y) if y_type == "f16" else y
 
 
 def dequantize_linear(x, scale, zp, *, axis=None):

@@ -77,6 +77,11 @@
  *      int8 input and uint32 for uint8.
  *  R23 QLinearConcat: each input is dequantized with its own scale / zero
  *      point (fp32) and quantized with Y's.
+ *  R24 fp16 QuantizeLinear / DequantizeLinear (the schemas allow fp16 x,
+ *      scales and y): fp16 values are read exactly as fp32 and the fp32
+ *      rules apply; an fp16 y is the fp32 result rounded once to nearest
+ *      even (the product (x - zp) * s has at most 19 significant bits, so it
+ *      is exact in fp32).
  *
  * Arithmetic: fp32 where the pages fix fp32 tensors, IEEE division,
  * nearbyintf in the default round-to-nearest mode for ties-to-even, int64
@@ -122,6 +127,52 @@ uint16_t oracle_f32_to_bf16(float f)
     uint32_t lower = v.u & 0xFFFFu;
     if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
     return (uint16_t)upper;
+}
+
+/* IEEE binary16 -> fp32 (exact): sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 is zero / subnormal (fraction * 2^-24), 31 is
+ * inf / NaN. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    float v;
+    if (e == 0) v = ldexpf((float)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexpf((float)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+/* fp32 -> binary16, round to nearest, ties to even; beyond the largest
+ * finite value (65504) by half an ulp or more -> inf; NaN -> quiet NaN. The
+ * scaled magnitudes below are exact in double. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000u : 0;
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+    if (isinf(f)) return (uint16_t)(sign | 0x7c00u);
+    double a = fabs((double)f);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);  /* a = frac * 2^e, frac in [0.5, 1) */
+    e -= 1;        /* a in [2^e, 2^(e+1)) */
+    if (e < -14) { /* subnormal range: units of 2^-24 */
+        double q = nearbyint(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)q); /* q == 1024 is the smallest normal */
+    }
+    double q = nearbyint(ldexp(a, 10 - e)); /* in [1024, 2048] */
+    if (q == 2048.0) { q = 1024.0; e += 1; }
+    if (e + 15 >= 31) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+void oracle_f16_to_f32_array(const uint16_t* h, int64_t n, float* f)
+{
+    for (int64_t i = 0; i < n; ++i) f[i] = oracle_f16_to_f32(h[i]);
+}
+
+void oracle_f32_to_f16_array(const float* f, int64_t n, uint16_t* h)
+{
+    for (int64_t i = 0; i < n; ++i) h[i] = oracle_f32_to_f16(f[i]);
 }
 
 /* round half to even (nearbyintf uses the current mode, which is the C
