@@ -10,7 +10,7 @@ are passed), ``stream`` defaults to torch's current stream. A missing library
 raises: there is no fallback.
 """
 from ._binding import (  # noqa: F401
-    DQ_ACT_IDENTITY, DQ_ACT_LEAKY_RELU, DQ_ACT_RELU, DQ_BF16, DQ_ERR_ALLOC, DQ_ERR_ARG,
+    DQ_ACT_IDENTITY, DQ_ACT_LEAKY_RELU, DQ_ACT_RELU, DQ_BF16, DQ_ERR_ALLOC, DQ_ERR_ARG, DQ_F16,
     DQ_ERR_HIP, DQ_ERR_RANGE, DQ_ERR_STATE, DQ_ERR_TYPE, DQ_F32, DQ_I8, DQ_K_MAX, DQ_OK,
     DQ_PER_TENSOR, DQ_U8, DQError, LIB_PATH, dqip_enabled, dqip_external_buffer_size,
     dqip_forward, dqip_forward_accumulators, dqip_info, dqip_init, dqip_internal_buffer_size,
@@ -19,4 +19,5 @@ from ._binding import (  # noqa: F401
     DQ_QGEMM_K_MAX, dq_qgemm_forward, dq_qgemm_forward_accumulators, dq_qgemm_info, dq_qgemm_init,
     dq_qgemm_release, dq_qgemm_set_b, dq_mul_integer, dq_reduce_sum_integer, qlinear_add,
     qlinear_concat, qlinear_leaky_relu, qlinear_mul, qlinear_reduce_mean, qlinear_sigmoid,
+    qlinear_dequantize_f16, qlinear_quantize_f16,
 )

@@ -10,7 +10,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdqip.so")
 
-DQ_F32, DQ_BF16, DQ_I8, DQ_U8 = 0, 1, 2, 3
+DQ_F32, DQ_BF16, DQ_I8, DQ_U8, DQ_F16 = 0, 1, 2, 3, 4
 DQ_ACT_IDENTITY, DQ_ACT_RELU, DQ_ACT_LEAKY_RELU = 0, 1, 2
 DQ_OK, DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_STATE, DQ_ERR_RANGE, DQ_ERR_ALLOC, DQ_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
@@ -58,6 +58,10 @@ _SIGNATURES = {
                                                 C.c_void_p]),
     "dq_qgemm_info": (C.c_char_p, [C.c_void_p]),
     "dq_qgemm_release": (None, [C.c_void_p]),
+    "qlinear_quantize_f16": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
+                                       C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
+    "qlinear_dequantize_f16": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int,
+                                         C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
     "qlinear_add": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
@@ -237,6 +241,28 @@ def qlinear_dequantize(x, x_type, x_scale, x_zero_point, y, axis=DQ_PER_TENSOR, 
     _check(load().qlinear_dequantize(_ptr(x), x_type, len(shp), sp, axis, _ptr(x_scale),
                                      _ptr(x_zero_point), _ptr(y), _stream(stream)),
            "qlinear_dequantize")
+    del keep
+
+
+def qlinear_quantize_f16(x, y_scale, y_zero_point, y_type, y, axis=DQ_PER_TENSOR, shape=None,
+                         stream=None):
+    """x, y_scale: fp16 tensors; y: int8/uint8 tensor of x's shape (written)."""
+    shp = tuple(x.shape) if shape is None else tuple(shape)
+    sp, keep = _shape_arg(shp)
+    _check(load().qlinear_quantize_f16(_ptr(x), len(shp), sp, axis, _ptr(y_scale),
+                                       _ptr(y_zero_point), y_type, _ptr(y), _stream(stream)),
+           "qlinear_quantize_f16")
+    del keep
+
+
+def qlinear_dequantize_f16(x, x_type, x_scale, x_zero_point, y_type, y, axis=DQ_PER_TENSOR,
+                           shape=None, stream=None):
+    """x_scale: fp16 tensor; y: fp16 (y_type DQ_F16) or fp32 (DQ_F32) tensor."""
+    shp = tuple(x.shape) if shape is None else tuple(shape)
+    sp, keep = _shape_arg(shp)
+    _check(load().qlinear_dequantize_f16(_ptr(x), x_type, len(shp), sp, axis, _ptr(x_scale),
+                                         _ptr(x_zero_point), y_type, _ptr(y), _stream(stream)),
+           "qlinear_dequantize_f16")
     del keep
 
 

@@ -38,6 +38,36 @@ __device__ __forceinline__ uint32_t channel_of64(uint64_t e, uint64_t inner, uin
     return (uint32_t)((e / inner) % cdim);
 }
 
+// fp16 tensors: values convert to fp32 exactly; an fp16 output is the fp32
+// value rounded once to nearest even (v_cvt_f16_f32 in the default mode).
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, uint64_t i) {
+    return (float)p[i];
+}
+
+// four consecutive elements (16 bytes of fp32, 8 of fp16) as fp32
+template <typename T>
+__device__ __forceinline__ dq::f4 ld4(const T* p) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(p));
+    } else {
+        const h4 h = *reinterpret_cast<const h4*>(p);
+        return dq::f4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void st4(T* p, dq::f4 v) {
+    if constexpr (sizeof(T) == 4) {
+        __builtin_nontemporal_store(v, reinterpret_cast<dq::f4*>(p));
+    } else {
+        const h4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        *reinterpret_cast<h4*>(p) = h;
+    }
+}
+
 template <bool U8>
 __device__ __forceinline__ int load_zp(const void* zp, uint32_t c) {
     if (!zp) return 0;
@@ -53,14 +83,14 @@ __device__ __forceinline__ int quant1(float x, float s, int zp) {
 
 // VEC: a 256-thread block covers 4096 consecutive elements as four
 // 1024-element slices; in slice q thread t handles elements 4t .. 4t+3, so
-// every load instruction of a wave reads 1 KiB of fp32 contiguously and
-// every store writes 256 contiguous bytes (x 16-byte aligned, y 4-byte
-// aligned, n < 2^32). CH4: inner % 4 == 0, so four adjacent elements share
-// one channel.
-template <bool U8, bool VEC, bool CH4>
+// every load instruction of a wave reads 1 KiB of fp32 (512 bytes of fp16)
+// contiguously and every store writes 256 contiguous bytes (x 16-byte
+// aligned, y 4-byte aligned, n < 2^32). CH4: inner % 4 == 0, so four
+// adjacent elements share one channel. XT: fp32 or fp16 x and scale.
+template <bool U8, bool VEC, bool CH4, typename XT>
 __global__ void __launch_bounds__(256)
-k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
-                  uint64_t cdim64, const float* __restrict__ scale,
+k_quantize_linear(const XT* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
+                  uint64_t cdim64, const XT* __restrict__ scale,
                   const void* __restrict__ zp, uint8_t* __restrict__ y) {
     if (VEC) {
         const uint32_t base = blockIdx.x * 4096u + threadIdx.x * 4u;
@@ -68,11 +98,11 @@ k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t 
         for (int q = 0; q < 4; ++q) {
             const uint32_t e0 = base + q * 1024u;
             if ((uint64_t)e0 + 4 <= n) {
-                const dq::f4 v = __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(x + e0));
+                const dq::f4 v = ld4(x + e0);
                 uint32_t packed = 0;
                 if (CH4) {
                     const uint32_t c = channel_of(e0, am);
-                    const dq::QDiv d = dq::make_qdiv(scale[c]);
+                    const dq::QDiv d = dq::make_qdiv(ld(scale, c));
                     const int z = load_zp<U8>(zp, c);
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
@@ -82,14 +112,14 @@ k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t 
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         const uint32_t c = channel_of(e0 + b, am);
-                        packed |= ((uint32_t)quant1<U8>(v[b], scale[c], load_zp<U8>(zp, c)) & 0xffu) << (8 * b);
+                        packed |= ((uint32_t)quant1<U8>(v[b], ld(scale, c), load_zp<U8>(zp, c)) & 0xffu) << (8 * b);
                     }
                 }
                 *reinterpret_cast<uint32_t*>(y + e0) = packed;
             } else {
                 for (uint64_t e = e0; e < n && e < (uint64_t)e0 + 4; ++e) {
                     const uint32_t c = channel_of((uint32_t)e, am);
-                    y[e] = (uint8_t)quant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                    y[e] = (uint8_t)quant1<U8>(ld(x, e), ld(scale, c), load_zp<U8>(zp, c));
                 }
             }
         }
@@ -98,7 +128,7 @@ k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t 
         const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
         if (t < n) {
             const uint32_t c = am.per_axis ? channel_of64(t, inner64, cdim64) : 0;
-            y[t] = (uint8_t)quant1<U8>(x[t], scale[c], load_zp<U8>(zp, c));
+            y[t] = (uint8_t)quant1<U8>(ld(x, t), ld(scale, c), load_zp<U8>(zp, c));
         }
     }
 }
@@ -118,9 +148,9 @@ k_quantize_linear(const float* __restrict__ x, uint64_t n, AxisMap am, uint64_t 
 // to the four packed low bytes at once (carry-free bytewise add).
 constexpr int kTabMax = 66;  // 4096 / 64 + 2
 
-template <bool U8>
+template <bool U8, typename XT>
 __global__ void __launch_bounds__(256)
-k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float* __restrict__ scale,
+k_quantize_tab(const XT* __restrict__ x, uint64_t n, AxisMap am, const XT* __restrict__ scale,
                const void* __restrict__ zp, uint8_t* __restrict__ y) {
     __shared__ float t_s[kTabMax], t_y[kTabMax], t_lo[kTabMax], t_hi[kTabMax];
     __shared__ uint32_t t_z[kTabMax];
@@ -136,8 +166,7 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t e0 = base + q * 1024u;
-        v[q] = (uint64_t)e0 + 4 <= n ? __builtin_nontemporal_load(reinterpret_cast<const dq::f4*>(x + e0))
-                                     : dq::f4{0.0f, 0.0f, 0.0f, 0.0f};
+        v[q] = (uint64_t)e0 + 4 <= n ? ld4(x + e0) : dq::f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // "rows" of inner elements: channel of row r is r % C
     const uint32_t r0 = am.per_axis ? dq::fdiv(eb, am.inner) : 0;
@@ -145,7 +174,7 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
     for (uint32_t k = threadIdx.x; k < nrows; k += 256) {
         const uint32_t row = r0 + k;
         const uint32_t c = am.per_axis ? row - dq::fdiv(row, am.cdim) * am.cdim.d : 0;
-        const float sc = scale[c];
+        const float sc = ld(scale, c);
         const int z = load_zp<U8>(zp, c);
         const dq::QDiv d = dq::make_qdiv(sc);
         t_s[k] = sc;
@@ -164,7 +193,7 @@ k_quantize_tab(const float* __restrict__ x, uint64_t n, AxisMap am, const float*
         if ((uint64_t)e0 + 4 > n) {  // the tensor's last partial vector
             for (uint64_t e = e0; e < n; ++e) {
                 const uint32_t c = channel_of((uint32_t)e, am);
-                y[e] = (uint8_t)quant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                y[e] = (uint8_t)quant1<U8>(ld(x, e), ld(scale, c), load_zp<U8>(zp, c));
             }
             break;
         }
@@ -204,12 +233,15 @@ __device__ __forceinline__ float dequant1(uint32_t byte, float s, int zp) {
 
 // VEC: the same 4096-element block split as quantize: in slice q thread t
 // reads the 4 codes 4t .. 4t+3 (256 contiguous bytes per wave) and writes
-// their 4 fp32 values (1 KiB contiguous per wave).
-template <bool U8, bool VEC, bool CH4>
+// their 4 values (1 KiB of fp32 or 512 bytes of fp16 contiguous per wave).
+// ST / YT: fp32 or fp16 scale and y. (x - zp) * s has at most 19
+// significant bits for an fp16 scale, so the fp32 product is exact and an
+// fp16 y is rounded once.
+template <bool U8, bool VEC, bool CH4, typename ST, typename YT>
 __global__ void __launch_bounds__(256)
 k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint64_t inner64,
-                    uint64_t cdim64, const float* __restrict__ scale,
-                    const void* __restrict__ zp, float* __restrict__ y) {
+                    uint64_t cdim64, const ST* __restrict__ scale,
+                    const void* __restrict__ zp, YT* __restrict__ y) {
     if (VEC) {
         const uint32_t base = blockIdx.x * 4096u + threadIdx.x * 4u;
         // every slice's codes are requested before the first store
@@ -227,7 +259,7 @@ k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint6
                 dq::f4 out;
                 if (CH4) {
                     const uint32_t c = channel_of(e0, am);
-                    const float s = scale[c];
+                    const float s = ld(scale, c);
                     const int z = load_zp<U8>(zp, c);
 #pragma unroll
                     for (int b = 0; b < 4; ++b) out[b] = dequant1<U8>(w >> (8 * b), s, z);
@@ -235,14 +267,14 @@ k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint6
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         const uint32_t c = channel_of(e0 + b, am);
-                        out[b] = dequant1<U8>(w >> (8 * b), scale[c], load_zp<U8>(zp, c));
+                        out[b] = dequant1<U8>(w >> (8 * b), ld(scale, c), load_zp<U8>(zp, c));
                     }
                 }
-                __builtin_nontemporal_store(out, reinterpret_cast<dq::f4*>(y + e0));
+                st4(y + e0, out);
             } else {
                 for (uint64_t e = e0; e < n && e < (uint64_t)e0 + 4; ++e) {
                     const uint32_t c = channel_of((uint32_t)e, am);
-                    y[e] = dequant1<U8>(x[e], scale[c], load_zp<U8>(zp, c));
+                    y[e] = (YT)dequant1<U8>(x[e], ld(scale, c), load_zp<U8>(zp, c));
                 }
             }
         }
@@ -250,7 +282,7 @@ k_dequantize_linear(const uint8_t* __restrict__ x, uint64_t n, AxisMap am, uint6
         const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
         if (t < n) {
             const uint32_t c = am.per_axis ? channel_of64(t, inner64, cdim64) : 0;
-            y[t] = dequant1<U8>(x[t], scale[c], load_zp<U8>(zp, c));
+            y[t] = (YT)dequant1<U8>(x[t], ld(scale, c), load_zp<U8>(zp, c));
         }
     }
 }
@@ -314,11 +346,9 @@ int dispatch(const Plan& p, const void* f32_side, const void* i8_side, Launch&& 
     return DQ_OK;
 }
 
-}  // namespace
-
-extern "C" int qlinear_quantize(const float* x, int ndim, const int64_t* shape, int axis,
-                                const float* y_scale, const void* y_zero_point,
-                                dq_dtype y_type, void* y, void* stream) {
+template <typename XT>
+int quantize_impl(const XT* x, int ndim, const int64_t* shape, int axis, const XT* y_scale,
+                  const void* y_zero_point, dq_dtype y_type, void* y, void* stream, const char* name) {
     Plan p;
     int rc = make_plan(ndim, shape, axis, &p);
     if (rc) return rc;
@@ -335,17 +365,17 @@ extern "C" int qlinear_quantize(const float* x, int ndim, const int64_t* shape, 
         const AxisMap am = make_axis_map(p, true);
         const unsigned blocks = (unsigned)((p.n + 4095) / 4096);
         if (u8)
-            hipLaunchKernelGGL((k_quantize_tab<true>), dim3(blocks), dim3(256), 0, s, x, p.n, am, y_scale,
+            hipLaunchKernelGGL((k_quantize_tab<true, XT>), dim3(blocks), dim3(256), 0, s, x, p.n, am, y_scale,
                                y_zero_point, (uint8_t*)y);
         else
-            hipLaunchKernelGGL((k_quantize_tab<false>), dim3(blocks), dim3(256), 0, s, x, p.n, am, y_scale,
+            hipLaunchKernelGGL((k_quantize_tab<false, XT>), dim3(blocks), dim3(256), 0, s, x, p.n, am, y_scale,
                                y_zero_point, (uint8_t*)y);
-        DQ_LAUNCH_CHECK("quantize_linear");
+        DQ_LAUNCH_CHECK(name);
         return DQ_OK;
     }
     rc = dispatch(p, x, y, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
-#define DQ_QL(U, V, C)                                                                     \
-    hipLaunchKernelGGL((k_quantize_linear<U, V, C>), dim3(blocks), dim3(256), 0, s, x, p.n, \
+#define DQ_QL(U, V, C)                                                                         \
+    hipLaunchKernelGGL((k_quantize_linear<U, V, C, XT>), dim3(blocks), dim3(256), 0, s, x, p.n, \
                        am, p.inner, p.cdim, y_scale, y_zero_point, (uint8_t*)y)
         if (u8) {
             if (!vec) DQ_QL(true, false, true);
@@ -359,13 +389,13 @@ extern "C" int qlinear_quantize(const float* x, int ndim, const int64_t* shape, 
 #undef DQ_QL
     });
     if (rc) return rc;
-    DQ_LAUNCH_CHECK("quantize_linear");
+    DQ_LAUNCH_CHECK(name);
     return DQ_OK;
 }
 
-extern "C" int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim, const int64_t* shape,
-                                  int axis, const float* x_scale, const void* x_zero_point,
-                                  float* y, void* stream) {
+template <typename ST, typename YT>
+int dequantize_impl(const void* x, dq_dtype x_type, int ndim, const int64_t* shape, int axis,
+                    const ST* x_scale, const void* x_zero_point, YT* y, void* stream, const char* name) {
     Plan p;
     int rc = make_plan(ndim, shape, axis, &p);
     if (rc) return rc;
@@ -376,8 +406,8 @@ extern "C" int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim, cons
     hipStream_t s = (hipStream_t)stream;
     const bool u8 = x_type == DQ_U8;
     rc = dispatch(p, y, x, [&](bool vec, bool ch16, AxisMap am, unsigned blocks) {
-#define DQ_DQL(U, V, C)                                                                       \
-    hipLaunchKernelGGL((k_dequantize_linear<U, V, C>), dim3(blocks), dim3(256), 0, s,          \
+#define DQ_DQL(U, V, C)                                                                           \
+    hipLaunchKernelGGL((k_dequantize_linear<U, V, C, ST, YT>), dim3(blocks), dim3(256), 0, s,      \
                        (const uint8_t*)x, p.n, am, p.inner, p.cdim, x_scale, x_zero_point, y)
         if (u8) {
             if (!vec) DQ_DQL(true, false, true);
@@ -391,6 +421,41 @@ extern "C" int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim, cons
 #undef DQ_DQL
     });
     if (rc) return rc;
-    DQ_LAUNCH_CHECK("dequantize_linear");
+    DQ_LAUNCH_CHECK(name);
     return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" int qlinear_quantize(const float* x, int ndim, const int64_t* shape, int axis,
+                                const float* y_scale, const void* y_zero_point,
+                                dq_dtype y_type, void* y, void* stream) {
+    return quantize_impl<float>(x, ndim, shape, axis, y_scale, y_zero_point, y_type, y, stream,
+                                "quantize_linear");
+}
+
+extern "C" int qlinear_quantize_f16(const void* x, int ndim, const int64_t* shape, int axis,
+                                    const void* y_scale, const void* y_zero_point, dq_dtype y_type,
+                                    void* y, void* stream) {
+    return quantize_impl<_Float16>((const _Float16*)x, ndim, shape, axis, (const _Float16*)y_scale,
+                                   y_zero_point, y_type, y, stream, "quantize_linear_f16");
+}
+
+extern "C" int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim, const int64_t* shape,
+                                  int axis, const float* x_scale, const void* x_zero_point,
+                                  float* y, void* stream) {
+    return dequantize_impl<float, float>(x, x_type, ndim, shape, axis, x_scale, x_zero_point, y, stream,
+                                         "dequantize_linear");
+}
+
+extern "C" int qlinear_dequantize_f16(const void* x, dq_dtype x_type, int ndim, const int64_t* shape,
+                                      int axis, const void* x_scale, const void* x_zero_point,
+                                      dq_dtype y_type, void* y, void* stream) {
+    if (y_type == DQ_F16)
+        return dequantize_impl<_Float16, _Float16>(x, x_type, ndim, shape, axis, (const _Float16*)x_scale,
+                                                   x_zero_point, (_Float16*)y, stream, "dequantize_linear_f16");
+    if (y_type == DQ_F32)
+        return dequantize_impl<_Float16, float>(x, x_type, ndim, shape, axis, (const _Float16*)x_scale,
+                                                x_zero_point, (float*)y, stream, "dequantize_linear_f16");
+    DQ_FAIL(DQ_ERR_TYPE, "DequantizeLinear with fp16 scales writes fp16 or fp32");
 }

@@ -29,8 +29,9 @@
 extern "C" {
 #endif
 
-/* Element types: fp32, bf16 (raw 16-bit patterns), int8, uint8. */
-typedef enum { DQ_F32 = 0, DQ_BF16 = 1, DQ_I8 = 2, DQ_U8 = 3 } dq_dtype;
+/* Element types: fp32, bf16 (raw 16-bit patterns), int8, uint8, fp16 (IEEE
+ * binary16 bit patterns). */
+typedef enum { DQ_F32 = 0, DQ_BF16 = 1, DQ_I8 = 2, DQ_U8 = 3, DQ_F16 = 4 } dq_dtype;
 
 /* Activations applied after dequantization and bias. Leaky ReLU takes its
  * slope from params[0] of dqip_set_params (default 0.01). */
@@ -194,6 +195,22 @@ int qlinear_quantize(const float* x, int ndim, const int64_t* shape, int axis,
 int qlinear_dequantize(const void* x, dq_dtype x_type, int ndim,
                        const int64_t* shape, int axis, const float* x_scale,
                        const void* x_zero_point, float* y, void* stream);
+
+/* The same operators on fp16 tensors. The schemas constrain QuantizeLinear's
+ * x and y_scale to one float type T1 and DequantizeLinear's x_scale and y to
+ * one float type T2, each fp16 or fp32, while DequantizeLinear's shape
+ * inference always makes y fp32. This library reads fp16 values exactly as
+ * fp32 and applies the rules above: qlinear_quantize_f16 takes fp16 x and
+ * y_scale; qlinear_dequantize_f16 takes fp16 x_scale and writes y as fp16
+ * (y_type DQ_F16: the exact product (x - zp) * s, at most 19 significant
+ * bits, rounded once to nearest even) or as fp32 (DQ_F32). Pointers,
+ * shapes, axis and errors as above (DQ_ERR_TYPE for another y_type). */
+int qlinear_quantize_f16(const void* x, int ndim, const int64_t* shape, int axis,
+                         const void* y_scale, const void* y_zero_point, dq_dtype y_type,
+                         void* y, void* stream);
+int qlinear_dequantize_f16(const void* x, dq_dtype x_type, int ndim, const int64_t* shape,
+                           int axis, const void* x_scale, const void* x_zero_point,
+                           dq_dtype y_type, void* y, void* stream);
 
 /* ------------------------------------------------------------------------
  * Requantizing 1x1 QLinearConv (stride 1, no padding, one group).

@@ -118,3 +118,66 @@ def test_qdq_full_size_per_axis(gpu):
     case = W.qdq_per_axis(seed=1)
     assert case["n_ties"] > 1000
     _check_both(gpu, case["x"], case["scale"], case["zp"], 1, "i8")
+
+
+# ------------------------------------------------------------- fp16 tensors
+
+def _f16_dev(bits):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.float16)
+
+
+@pytest.mark.parametrize("shape,axis", [
+    ((4, 32, 8, 8), 1), ((2, 16, 9, 11), 1), ((3, 5, 7), 2), ((1000003,), None), ((17,), 0),
+    ((64, 256, 28, 28), 1),
+])
+@pytest.mark.parametrize("y_type", ["i8", "u8"])
+def test_quantize_f16_matches_oracle(gpu, shape, axis, y_type):
+    import torch
+
+    r = np.random.default_rng(len(shape) * 7 + (axis or 0))
+    x = (r.standard_normal(shape) * 4).astype(np.float16)
+    nch = 1 if axis is None else shape[axis]
+    s = r.uniform(0.005, 0.05, nch).astype(np.float16)
+    lo, hi = (0, 256) if y_type == "u8" else (-10, 10)
+    z = r.integers(lo, hi, nch)
+    # planted exact ties: x = (k + 1/2) * s for a few elements of channel 0
+    xf = x.reshape(-1)
+    xf[:8] = ((np.arange(8) - 4 + 0.5) * s[0].astype(np.float32)).astype(np.float16)
+    want = oracle.quantize_linear_f16(x.view(np.uint16), s.view(np.uint16), z, axis=axis,
+                                      y_type=y_type)
+    zd = torch.from_numpy(z.astype(np.uint8 if y_type == "u8" else np.int8)).cuda()
+    y = torch.empty(shape, dtype=torch.uint8 if y_type == "u8" else torch.int8, device="cuda")
+    gpu.qlinear_quantize_f16(_f16_dev(x.view(np.uint16)), _f16_dev(s.view(np.uint16)), zd,
+                             gpu.DQ_U8 if y_type == "u8" else gpu.DQ_I8, y,
+                             axis=gpu.DQ_PER_TENSOR if axis is None else axis)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.array_equal(got, want), f"{(got != want).sum()} codes differ"
+
+
+@pytest.mark.parametrize("shape,axis", [((4, 32, 8, 8), 1), ((3, 5, 7), 2), ((1000003,), None),
+                                        ((64, 256, 28, 28), 1)])
+@pytest.mark.parametrize("y_type", ["f16", "f32"])
+def test_dequantize_f16_matches_oracle(gpu, shape, axis, y_type):
+    import torch
+
+    r = np.random.default_rng(len(shape) + 3)
+    q = r.integers(0, 256, shape).astype(np.uint8)
+    nch = 1 if axis is None else shape[axis]
+    s = r.uniform(1e-4, 2.0, nch).astype(np.float16)
+    s[0] = np.float16(6e-8)          # a subnormal fp16 scale
+    z = r.integers(0, 256, nch)
+    want = oracle.dequantize_linear_f16(q, s.view(np.uint16), z, axis=axis, y_type=y_type)
+    y = torch.empty(shape, dtype=torch.float16 if y_type == "f16" else torch.float32, device="cuda")
+    gpu.qlinear_dequantize_f16(torch.from_numpy(q).cuda(), gpu.DQ_U8, _f16_dev(s.view(np.uint16)),
+                               torch.from_numpy(z.astype(np.uint8)).cuda(),
+                               gpu.DQ_F16 if y_type == "f16" else gpu.DQ_F32, y,
+                               axis=gpu.DQ_PER_TENSOR if axis is None else axis)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    if y_type == "f16":
+        assert np.array_equal(got.view(np.uint16), want)
+    else:
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
