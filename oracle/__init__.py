@@ -58,6 +58,9 @@ def lib() -> C.CDLL:
         L.oracle_f32_to_f16.restype = C.c_uint16
         L.oracle_f16_to_f32_array.argtypes = [vp, i64, vp]
         L.oracle_f32_to_f16_array.argtypes = [vp, i64, vp]
+        L.oracle_qlinear_conv2d.argtypes = [vp, i32, i64, i64, i64, i64, f32, i32, vp, i32, i64,
+                                             i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                             i64, vp, vp, i64, vp, f32, i32, i32, vp, vp]
         L.oracle_broadcast_shape.argtypes = [i32, vp, i32, vp, vp, vp]
         L.oracle_qlinear_binary.argtypes = [i32, i32, vp, i32, vp, f32, i32, vp, i32, vp,
                                             f32, i32, f32, i32, vp]
@@ -293,6 +296,35 @@ def qlinear_conv(x, x_scale, x_zp, w, w_scale, w_zp, y_scale, y_zp, *, bias=None
 
 
 # ------------------------------------------------ QGemm family (R15-R19)
+
+def qlinear_conv2d(x, x_scale, x_zp, w, w_scale, w_zp, y_scale, y_zp, *, bias=None,
+                   strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1), group=1,
+                   y_type=None, with_acc=False):
+    """General 2-D QLinearConv (R11, R25). x [N, C, H, W], w [M, C/group, kH, kW]
+    8-bit; pads = (top, left, bottom, right); w_scale / w_zp scalars or per
+    output channel. Returns y (and the int32 sums with the bias)."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    N, C, H, W = x.shape
+    M, _, kH, kW = w.shape
+    ws = _c(np.atleast_1d(w_scale), np.float32)
+    wz = _c(np.atleast_1d(w_zp), np.int32)
+    if wz.size != ws.size:
+        wz = np.broadcast_to(wz, ws.shape).astype(np.int32).copy()
+    b = None if bias is None else _c(bias, np.int32)
+    oH = (H + pads[0] + pads[2] - dilations[0] * (kH - 1) - 1) // strides[0] + 1
+    oW = (W + pads[1] + pads[3] - dilations[1] * (kW - 1) - 1) // strides[1] + 1
+    yt = y_type or _tag8(x)
+    y = np.empty((N, M, oH, oW), _np_type(yt))
+    acc = np.empty((N, M, oH, oW), np.int32) if with_acc else None
+    rc = lib().oracle_qlinear_conv2d(_p(x), _TYPE[_tag8(x)], N, C, H, W, float(np.float32(x_scale)),
+                                     int(x_zp), _p(w), _TYPE[_tag8(w)], M, kH, kW, strides[0],
+                                     strides[1], pads[0], pads[1], pads[2], pads[3], dilations[0],
+                                     dilations[1], group, _p(ws), _p(wz), ws.size, _p(b),
+                                     float(np.float32(y_scale)), int(y_zp), _TYPE[yt], _p(y), _p(acc))
+    _check(rc, "qlinear_conv2d")
+    return (y, acc) if with_acc else y
+
 
 def _tag8(a):
     return "u8" if a.dtype == np.uint8 else "i8"

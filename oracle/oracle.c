@@ -77,6 +77,10 @@
  *      int8 input and uint32 for uint8.
  *  R23 QLinearConcat: each input is dequantized with its own scale / zero
  *      point (fp32) and quantized with Y's.
+ *  R25 QLinearConv's attributes (the page names kernel size, stride, pad
+ *      lengths and group): 2-D, strides, begin / end pads per axis,
+ *      dilations (default 1) and groups as in ONNX Conv; a tap outside the
+ *      image reads x_zero_point, i.e. a real 0.
  *  R24 fp16 QuantizeLinear / DequantizeLinear (the schemas allow fp16 x,
  *      scales and y): fp16 values are read exactly as fp32 and the fp32
  *      rules apply; an fp16 y is the fp32 result rounded once to nearest
@@ -471,6 +475,61 @@ int oracle_qlinear_conv(const void* x, int x_type, int64_t Nb, int64_t C,
                     real = real * w_scale[wi];
                     float q = real / y_scale;
                     int64_t yi = ((n * M + m) * oH + oh) * oW + ow;
+                    store_int8(y, y_type, yi, sat_add(rne(q), y_zp, lo, hi));
+                }
+        }
+    return ORC_OK;
+}
+
+/* General 2-D QLinearConv (ONNX QLinearConv, opset 10): x [Nb, C, H, W],
+ * w [M, C / group, kH, kW], y [Nb, M, oH, oW] with
+ *   oH = (H + pad_t + pad_b - dil_h (kH - 1) - 1) / stride_h + 1 (floor),
+ * likewise oW. Output channel m belongs to group g = m / (M / group) and
+ * reads input channels g (C / group) .. +C / group. A tap outside the image
+ * reads x_zp (R25: a padded input is a real 0, so it adds nothing), then R11
+ * requantizes. acc_out (optional) receives the int32 sums with the bias. */
+int oracle_qlinear_conv2d(const void* x, int x_type, int64_t Nb, int64_t C, int64_t H, int64_t W,
+                          float x_scale, int32_t x_zp, const void* w, int w_type, int64_t M,
+                          int64_t kH, int64_t kW, int64_t stride_h, int64_t stride_w,
+                          int64_t pad_t, int64_t pad_l, int64_t pad_b, int64_t pad_r,
+                          int64_t dil_h, int64_t dil_w, int64_t group, const float* w_scale,
+                          const int32_t* w_zp, int64_t w_len, const int32_t* bias, float y_scale,
+                          int32_t y_zp, int y_type, void* y, int32_t* acc_out)
+{
+    if (group < 1 || C % group || M % group || stride_h < 1 || stride_w < 1 || dil_h < 1 ||
+        dil_w < 1 || (w_len != 1 && w_len != M))
+        return ORC_ERR_ARG;
+    int64_t oH = (H + pad_t + pad_b - dil_h * (kH - 1) - 1) / stride_h + 1;
+    int64_t oW = (W + pad_l + pad_r - dil_w * (kW - 1) - 1) / stride_w + 1;
+    if (oH < 1 || oW < 1) return ORC_ERR_ARG;
+    int64_t Cg = C / group, Mg = M / group;
+    int lo = (y_type == ORC_U8) ? 0 : -128;
+    int hi = (y_type == ORC_U8) ? 255 : 127;
+    for (int64_t n = 0; n < Nb; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t g = m / Mg;
+            int64_t wi = (w_len == 1) ? 0 : m;
+            for (int64_t oh = 0; oh < oH; ++oh)
+                for (int64_t ow = 0; ow < oW; ++ow) {
+                    int64_t acc = 0;
+                    for (int64_t c = 0; c < Cg; ++c)
+                        for (int64_t r = 0; r < kH; ++r)
+                            for (int64_t s = 0; s < kW; ++s) {
+                                int64_t ih = oh * stride_h - pad_t + r * dil_h;
+                                int64_t iw = ow * stride_w - pad_l + s * dil_w;
+                                int xv = x_zp;
+                                if (ih >= 0 && ih < H && iw >= 0 && iw < W)
+                                    xv = load_int8(x, x_type, ((n * C + g * Cg + c) * H + ih) * W + iw);
+                                int64_t wk = ((m * Cg + c) * kH + r) * kW + s;
+                                acc += (int64_t)(load_int8(w, w_type, wk) - w_zp[wi]) * (xv - x_zp);
+                            }
+                    if (bias) acc += bias[m];
+                    if (acc > INT32_MAX || acc < INT32_MIN) return ORC_ERR_OVERFLOW;
+                    int64_t yi = ((n * M + m) * oH + oh) * oW + ow;
+                    if (acc_out) acc_out[yi] = (int32_t)acc;
+                    float real = (float)(int32_t)acc * x_scale;
+                    real = real * w_scale[wi];
+                    float q = real / y_scale;
                     store_int8(y, y_type, yi, sat_add(rne(q), y_zp, lo, hi));
                 }
         }
