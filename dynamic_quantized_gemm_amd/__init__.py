@@ -19,5 +19,6 @@ from ._binding import (  # noqa: F401
     DQ_QGEMM_K_MAX, dq_qgemm_forward, dq_qgemm_forward_accumulators, dq_qgemm_info, dq_qgemm_init,
     dq_qgemm_release, dq_qgemm_set_b, dq_mul_integer, dq_reduce_sum_integer, qlinear_add,
     qlinear_concat, qlinear_leaky_relu, qlinear_mul, qlinear_reduce_mean, qlinear_sigmoid,
-    qlinear_dequantize_f16, qlinear_quantize_f16,
+    qlinear_dequantize_f16, qlinear_quantize_f16, dq_qconv_forward, dq_qconv_info,
+    dq_qconv_init, dq_qconv_output_shape, dq_qconv_release, dq_qconv_set_w,
 )

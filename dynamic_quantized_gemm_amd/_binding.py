@@ -62,6 +62,16 @@ _SIGNATURES = {
                                        C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
     "qlinear_dequantize_f16": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int,
                                          C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
+    "dq_qconv_init": (C.c_int, [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                C.c_int64, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                C.c_int, C.c_int, C.c_int]),
+    "dq_qconv_output_shape": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dq_qconv_set_w": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                 C.c_void_p, C.c_void_p]),
+    "dq_qconv_forward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dq_qconv_info": (C.c_char_p, [C.c_void_p]),
+    "dq_qconv_release": (None, [C.c_void_p]),
     "qlinear_add": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
@@ -434,3 +444,47 @@ def qlinear_concat(inputs, axis, y_scale, y_zero_point, type_, y, shapes=None, s
                                  C.cast(sc, C.c_void_p), C.cast(zp, C.c_void_p), _ptr(y_scale),
                                  _ptr(y_zero_point), type_, _ptr(y), _stream(stream)),
            "qlinear_concat")
+
+
+# ------------------------------------------------------ general QLinearConv
+
+def dq_qconv_init(C_, H, W, M, kH, kW, x_type, w_type, y_type, strides=(1, 1),
+                  pads=(0, 0, 0, 0), dilations=(1, 1), group=1):
+    """Returns the context handle (an int). pads = (top, left, bottom, right)."""
+    st = (C.c_int64 * 2)(*[int(v) for v in strides])
+    pd = (C.c_int64 * 4)(*[int(v) for v in pads])
+    dl = (C.c_int64 * 2)(*[int(v) for v in dilations])
+    h = C.c_void_p()
+    _check(load().dq_qconv_init(C.byref(h), C_, H, W, M, kH, kW, C.cast(st, C.c_void_p),
+                                C.cast(pd, C.c_void_p), C.cast(dl, C.c_void_p), group, x_type,
+                                w_type, y_type), "dq_qconv_init")
+    return h.value
+
+
+def dq_qconv_output_shape(ctx):
+    oh, ow = C.c_int64(), C.c_int64()
+    _check(load().dq_qconv_output_shape(ctx, C.byref(oh), C.byref(ow)), "dq_qconv_output_shape")
+    return int(oh.value), int(ow.value)
+
+
+def dq_qconv_set_w(ctx, w, w_scale, w_zero_point=None, bias=None, stream=None):
+    _check(load().dq_qconv_set_w(ctx, _ptr(w), _ptr(w_scale), _ptr(w_zero_point),
+                                 int(w_scale.numel()), _ptr(bias), _stream(stream)),
+           "dq_qconv_set_w")
+
+
+def dq_qconv_forward(ctx, x, x_scale, x_zero_point, y_scale, y_zero_point, y, N=None,
+                     stream=None):
+    n = int(x.shape[0]) if N is None else int(N)
+    _check(load().dq_qconv_forward(ctx, _ptr(x), n, _ptr(x_scale), _ptr(x_zero_point),
+                                   _ptr(y_scale), _ptr(y_zero_point), _ptr(y), _stream(stream)),
+           "dq_qconv_forward")
+
+
+def dq_qconv_info(ctx):
+    r = load().dq_qconv_info(ctx)
+    return r.decode() if r else None
+
+
+def dq_qconv_release(ctx):
+    load().dq_qconv_release(ctx)

@@ -1,0 +1,565 @@
+// qconv.hip -- general 2-D QLinearConv on gfx950 matrix cores (implicit GEMM).
+//
+// ONNX "QLinearConv" (opset 10), description and inputs: x [N, C, H, W] and
+// w [M, C / group, kH, kW] are 8-bit with zero points (w's per tensor or per
+// output channel), the optional bias is int32 with scale x_scale * w_scale
+// and zero point 0, y is requantized with y_scale / y_zero_point; the output
+// size follows the kernel, strides and pads (ONNX Conv's attributes:
+// strides, begin / end pads, dilations, group). For output channel m of
+// group g and output pixel (oh, ow):
+//   acc  = sum_{c, kh, kw} (w[m,c,kh,kw] - w_zp[m]) * (x[n, g Cg + c, ih, iw] - x_zp)
+//          + bias[m],   ih = oh sh - pt + kh dh,  iw = ow sw - pl + kw dw
+//   real = ((float)acc * x_scale) * w_scale[m]
+//   y    = saturate(rne(real / y_scale) + y_zp)
+// where a tap outside the image reads x_zp (a padded input is a real 0).
+//
+// As in the 1x1 kernel the int8 MFMA takes w^ = w - a and x^ = x - b (a, b =
+// 128 for uint8, 0 for int8) and
+//   acc = sum w^ x^ + (b - x_zp) R[m] + (a - w_zp[m]) S[p] + K (a - w_zp[m]) (b - x_zp) + bias[m]
+// with R[m] = sum w^ over the K = Cg kH kW real taps (computed when the
+// weights are set) and S[p] = sum x^ over the same taps (one more MFMA
+// against 1s, only when some a - w_zp[m] can be non-zero). Padded channels
+// (past Cg in the last chunk) hold w^ = x^ = 0 and drop out of every term;
+// spatial pads hold x^ = x_zp - b and cancel exactly.
+//
+// The reduction runs over (input channel chunk of 32, kernel tap). A
+// workgroup of four waves owns 64 WM output channels x 64 (4 / WM) output
+// pixels of one image and group; per chunk it stages the input patch its
+// pixels need (all patch rows x all patch columns x 32 channels, channels
+// contiguous, spatial pads already holding x_zp) in LDS, so that for any
+// tap a lane's MFMA operand (16 channels of one input pixel) is one
+// ds_read_b128 at the lane's pixel offset plus a tap offset that is the same
+// for every lane. The weights are packed once per set_w into rows of
+// [tap][channel] (32-channel runs contiguous), read as 16-byte fragments.
+// The epilogue requantizes as the other quantizers do and stores whole
+// 16-byte row segments of y (NCHW).
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "dq_device.h"
+
+namespace {
+
+constexpr int kKC = 32;         // input channels per chunk
+constexpr int kThreads = 256;
+constexpr int kYPitch = 80;     // LDS bytes per staged output row (64 + 16)
+constexpr int kPatchMax = 112 * 1024;  // with the 20 KiB output stage, within 160 KiB of LDS
+constexpr int kKMax = 32768;    // real taps per output: int32 sums stay exact
+
+typedef dq::v4i v4i;
+
+struct ConvShape {
+    int C, H, W, M, KH, KW, sh, sw, pt, pl, dh, dw, G, Cg, Mg, OH, OW, P;
+    int T;     // KH * KW
+    int Kc;    // Cg rounded up to a chunk
+    int Mgp;   // Mg rounded up to the channel tile
+    int K;     // Cg * KH * KW real taps
+    int cpad;  // patch columns left of iw = 0 (a multiple of 4, >= pl)
+    int ncol;  // patch columns (a multiple of 4)
+    int mtiles;
+    dq::FastDiv ow_div;
+};
+
+struct ConvArgs {
+    const uint8_t* x;
+    const int8_t* wp;     // packed w^: [G * Mgp][T][Kc]
+    const int32_t* R;     // [G * Mgp]
+    const float* ws;      // [M]
+    const int32_t* wz;    // [M]
+    const int32_t* bias;  // [M]
+    const float* x_scale;
+    const void* x_zp;
+    const float* y_scale;
+    const void* y_zp;
+    uint8_t* y;
+    uint32_t xflip;       // 0x80808080 for a uint8 x
+    int kA, kB, x_u8, y_u8, vecx, vecy;
+    int y_lo, y_hi;       // y's saturation range
+};
+
+__device__ __forceinline__ int zp8(const void* zp, bool u8) {
+    if (!zp) return 0;
+    return u8 ? (int)*(const uint8_t*)zp : (int)*(const int8_t*)zp;
+}
+
+// Byte i of each of d0..d3, as one word (d0 in the low byte).
+__device__ __forceinline__ uint32_t gather_byte(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, int i) {
+    const int s = 8 * i;
+    return ((d0 >> s) & 0xffu) | (((d1 >> s) & 0xffu) << 8) | (((d2 >> s) & 0xffu) << 16) |
+           (((d3 >> s) & 0xffu) << 24);
+}
+
+template <bool XSUM, int WM>
+__global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t patch[];
+    __shared__ __attribute__((aligned(16))) uint8_t ys[4 * 64 * kYPitch];
+    constexpr int WP = 4 / WM, PT = 64 * WP, MT = 64 * WM;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wp = wave / WM;
+    const int n = blockIdx.z;
+    const int g = blockIdx.y / sh.mtiles, mt = blockIdx.y - g * sh.mtiles;
+    const int m0 = mt * MT + 64 * wm;  // this wave's first channel within the group
+    const int p0 = blockIdx.x * PT, pw0 = p0 + 64 * wp;
+
+    // the block's patch: output rows oh_a .. oh_b, input rows from ih0
+    const int oh_a = (int)dq::fdiv((uint32_t)p0, sh.ow_div);
+    const int oh_b = (int)dq::fdiv((uint32_t)(std::min(p0 + PT, sh.P) - 1), sh.ow_div);
+    const int ih0 = oh_a * sh.sh - sh.pt;
+    const int nr = (oh_b - oh_a) * sh.sh + (sh.KH - 1) * sh.dh + 1;
+
+    // the lane's two MFMA pixel rows: patch byte offsets for tap (0, 0)
+    int pix[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+        const int p = std::min(pw0 + 32 * pb + (lane & 31), sh.P - 1);
+        const int oh = (int)dq::fdiv((uint32_t)p, sh.ow_div), ow = p - oh * sh.OW;
+        const int r = (oh - oh_a) * sh.sh, c = ow * sh.sw - sh.pl + sh.cpad;
+        pix[pb] = (r * sh.ncol + c) * kKC + 16 * (lane >> 5);
+    }
+
+    const int x_zp = zp8(a.x_zp, a.x_u8);
+    const uint32_t zpf = ((uint32_t)(x_zp & 0xff) * 0x01010101u) ^ a.xflip;  // x_zp after the shift
+    const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
+    const int ncq = sh.ncol / 4;
+    const int units = nr * 8 * ncq;
+
+    dq::v16i acc[2][2], sacc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[i][0][r] = 0;
+            acc[i][1][r] = 0;
+            sacc[i][r] = 0;
+        }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const int8_t* wrow[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+        wrow[jb] = a.wp + (size_t)(g * sh.Mgp + m0 + 32 * jb + (lane & 31)) * sh.T * sh.Kc + 16 * (lane >> 5);
+
+    for (int c0 = 0; c0 < sh.Kc; c0 += kKC) {
+        __syncthreads();  // the previous chunk's operand reads are done
+        // stage the patch: a unit is 4 channels x 4 patch columns of one row,
+        // transposed in registers to 4 words of (column, 4 channels)
+        for (int u = tid; u < units; u += kThreads) {
+            const int colq = u % ncq, rest = u / ncq;
+            const int cq = rest & 7, r = rest >> 3;
+            const int ih = ih0 + r, iw0 = 4 * colq - sh.cpad;
+            uint32_t d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = c0 + 4 * cq + j;
+                if (c >= sh.Cg) {
+                    d[j] = 0u;  // a padded channel: x^ = 0
+                } else if (ih < 0 || ih >= sh.H) {
+                    d[j] = zpf;
+                } else {
+                    const uint8_t* row = xg + ((size_t)c * sh.H + ih) * sh.W;
+                    if (a.vecx && iw0 >= 0 && iw0 + 4 <= sh.W) {
+                        d[j] = *reinterpret_cast<const uint32_t*>(row + iw0) ^ a.xflip;
+                    } else {
+                        uint32_t v = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int iw = iw0 + e;
+                            const uint32_t b = (iw >= 0 && iw < sh.W) ? (uint32_t)row[iw] : (uint32_t)(x_zp & 0xff);
+                            v |= b << (8 * e);
+                        }
+                        d[j] = v ^ a.xflip;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint32_t*>(&patch[(r * sh.ncol + 4 * colq + i) * kKC + 4 * cq]) =
+                    gather_byte(d[0], d[1], d[2], d[3], i);
+        }
+        __syncthreads();
+
+        // taps: the weight fragments of tap t + 1 are requested before the
+        // MFMAs of tap t
+        v4i wf[2], wn[2];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) wf[jb] = *reinterpret_cast<const v4i*>(wrow[jb] + c0);
+        for (int t = 0; t < sh.T; ++t) {
+            const int tn = t + 1 < sh.T ? t + 1 : t;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+                wn[jb] = *reinterpret_cast<const v4i*>(wrow[jb] + (size_t)tn * sh.Kc + c0);
+            const int kh = t / sh.KW, kw = t - kh * sh.KW;
+            const int off = (kh * sh.dh * sh.ncol + kw * sh.dw) * kKC;
+            const v4i xf0 = *reinterpret_cast<const v4i*>(&patch[pix[0] + off]);
+            const v4i xf1 = *reinterpret_cast<const v4i*>(&patch[pix[1] + off]);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                acc[0][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf0, wf[jb], acc[0][jb], 0, 0, 0);
+                acc[1][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf1, wf[jb], acc[1][jb], 0, 0, 0);
+            }
+            if (XSUM) {
+                sacc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf0, ones, sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf1, ones, sacc[1], 0, 0, 0);
+            }
+            wf[0] = wn[0];
+            wf[1] = wn[1];
+        }
+    }
+
+    // ---- requantizing epilogue: lane holds channel (lane % 32) of block jb
+    // and, in accumulators 4q .. 4q+3, pixels 8q + 4 (lane / 32) + 0..3 of
+    // pixel block ib
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    constexpr float kBig = 4194304.0f;     // 2^22
+    const float x_scale = *a.x_scale;
+    const dq::QDiv yd = dq::make_qdiv(*a.y_scale);
+    const int y_zp = zp8(a.y_zp, a.y_u8);
+    const float lof = kMagic + (float)(a.y_lo - y_zp), hif = kMagic + (float)(a.y_hi - y_zp);
+    const uint32_t Yz = (uint32_t)(y_zp & 0xff) * 0x01010101u;
+    uint8_t* ysw = ys + 64 * wave * kYPitch;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const int ml = m0 + 32 * jb + (lane & 31);
+        const bool mok = ml < sh.Mg;
+        const int mg = g * sh.Mg + (mok ? ml : 0);
+        const int32_t R = a.R[g * sh.Mgp + ml];
+        const int coef = a.kA - (mok ? a.wz[mg] : 0);
+        const float wsc = mok ? a.ws[mg] : 0.0f;
+        const uint32_t xb = (uint32_t)(a.kB - x_zp);
+        const uint32_t rowc = xb * (uint32_t)R + (uint32_t)sh.K * ((uint32_t)coef * xb) +
+                              (uint32_t)(mok ? a.bias[mg] : 0);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t word;
+                if (yd.fast) {
+                    uint32_t b[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t v = (uint32_t)acc[ib][jb][4 * q + e] + rowc;
+                        if (XSUM) v += (uint32_t)coef * (uint32_t)sacc[ib][4 * q + e];
+                        float real = (float)(int32_t)v * x_scale;
+                        real = real * wsc;
+                        const float q0 = __builtin_amdgcn_fmed3f(real * yd.y, -kBig, kBig);
+                        const float rr = __builtin_fmaf(-q0, yd.s, real);
+                        const float tt = __builtin_fmaf(rr, yd.y, q0) + kMagic;
+                        b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(tt, lof, hif));
+                    }
+                    const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+                    word = ((packed & 0x7f7f7f7fu) + (Yz & 0x7f7f7f7fu)) ^ ((packed ^ Yz) & 0x80808080u);
+                } else {
+                    word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t v = (uint32_t)acc[ib][jb][4 * q + e] + rowc;
+                        if (XSUM) v += (uint32_t)coef * (uint32_t)sacc[ib][4 * q + e];
+                        float real = (float)(int32_t)v * x_scale;
+                        real = real * wsc;
+                        const int code = dq::sat_add(dq::rne(real / yd.s), y_zp, a.y_lo, a.y_hi);
+                        word |= ((uint32_t)code & 0xffu) << (8 * e);
+                    }
+                }
+                const int pp = 32 * ib + 8 * q + 4 * (lane >> 5);
+                *reinterpret_cast<uint32_t*>(&ysw[(32 * jb + (lane & 31)) * kYPitch + pp]) = word;
+            }
+        }
+    }
+    // the wave's 64 staged rows back as 16-byte segments (one wave's LDS
+    // operations complete in order: no barrier)
+    dq::wait_lgkm0();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int u = lane + 64 * it;
+        const int rr = u >> 2, qq = u & 3;
+        const int ml = m0 + rr, p = pw0 + 16 * qq;
+        if (ml < sh.Mg && p < sh.P) {
+            const v4i v = *reinterpret_cast<const v4i*>(&ysw[rr * kYPitch + 16 * qq]);
+            uint8_t* dst = a.y + ((size_t)n * sh.M + (size_t)g * sh.Mg + ml) * sh.P + p;
+            if (a.vecy && p + 16 <= sh.P) {
+                *reinterpret_cast<v4i*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (p + e < sh.P) dst[e] = (uint8_t)((uint32_t)v[e >> 2] >> (8 * (e & 3)));
+            }
+        }
+    }
+}
+
+// Packs w [M, Cg, kH, kW] into w^ rows [G * Mgp][T][Kc] (zeros past Cg and
+// Mg) and R[row] = sum of the row's w^. One workgroup per row.
+__global__ __launch_bounds__(256) void k_conv_pack_w(const uint8_t* __restrict__ w, ConvShape sh, int w_u8,
+                                                     int8_t* __restrict__ wp, int32_t* __restrict__ R) {
+    __shared__ int32_t part[256];
+    const int row = blockIdx.x;
+    const int g = row / sh.Mgp, ml = row - g * sh.Mgp;
+    const bool mok = ml < sh.Mg;
+    const int m = g * sh.Mg + ml;
+    const int len = sh.T * sh.Kc;
+    int32_t s = 0;
+    for (int i = threadIdx.x; i < len; i += 256) {
+        const int t = i / sh.Kc, c = i - t * sh.Kc;
+        int v = 0;
+        if (mok && c < sh.Cg) {
+            const uint32_t b = w[((size_t)m * sh.Cg + c) * sh.T + t];
+            v = w_u8 ? (int)b - 128 : (int)(int8_t)b;
+        }
+        wp[(size_t)row * len + i] = (int8_t)v;
+        s += v;
+    }
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int k = 128; k > 0; k >>= 1) {
+        if (threadIdx.x < k) part[threadIdx.x] += part[threadIdx.x + k];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) R[row] = part[0];
+}
+
+// Per output channel: scale, zero point (as int) and bias, from one or M
+// values.
+__global__ __launch_bounds__(256) void k_conv_params(const float* __restrict__ w_scale,
+                                                     const void* __restrict__ w_zp, int w_u8, int w_len,
+                                                     const int32_t* __restrict__ bias, int M,
+                                                     float* __restrict__ ws, int32_t* __restrict__ wz,
+                                                     int32_t* __restrict__ bo) {
+    const int m = blockIdx.x * 256 + threadIdx.x;
+    if (m >= M) return;
+    const int i = w_len == 1 ? 0 : m;
+    ws[m] = w_scale[i];
+    wz[m] = w_zp ? (w_u8 ? (int)((const uint8_t*)w_zp)[i] : (int)((const int8_t*)w_zp)[i]) : 0;
+    bo[m] = bias ? bias[m] : 0;
+}
+
+bool is_8bit(dq_dtype t) { return t == DQ_I8 || t == DQ_U8; }
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+struct dq_qconv_ctx {
+    ConvShape sh{};
+    dq_dtype x_type, w_type, y_type;
+    int wm = 1;            // waves over output channels
+    int patch_bytes = 0;
+    bool has_w = false, xsum = false;
+    int device = 0;
+    int8_t* wp = nullptr;
+    int32_t* R = nullptr;
+    float* ws = nullptr;
+    int32_t* wz = nullptr;
+    int32_t* bias = nullptr;
+    std::string info;
+};
+
+namespace {
+
+void free_ctx(dq_qconv_ctx* c) {
+    if (!c) return;
+    (void)hipFree(c->wp);
+    (void)hipFree(c->R);
+    (void)hipFree(c->ws);
+    (void)hipFree(c->wz);
+    (void)hipFree(c->bias);
+    delete c;
+}
+
+template <bool XSUM, int WM>
+int set_lds(int bytes) {
+    if (hipFuncSetAttribute((const void*)k_qconv<XSUM, WM>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
+        hipSuccess)
+        DQ_FAIL(DQ_ERR_HIP, "hipFuncSetAttribute failed for the conv kernel");
+    return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W, int64_t M, int64_t kH,
+                             int64_t kW, const int64_t* strides, const int64_t* pads,
+                             const int64_t* dilations, int64_t group, dq_dtype x_type, dq_dtype w_type,
+                             dq_dtype y_type) {
+    if (!ctx) DQ_FAIL(DQ_ERR_ARG, "ctx is NULL");
+    *ctx = nullptr;
+    if (!is_8bit(x_type) || !is_8bit(w_type) || !is_8bit(y_type))
+        DQ_FAIL(DQ_ERR_TYPE, "x, w and y must be DQ_I8 or DQ_U8");
+    const int64_t sh_ = strides ? strides[0] : 1, sw_ = strides ? strides[1] : 1;
+    const int64_t pt = pads ? pads[0] : 0, pl = pads ? pads[1] : 0, pb = pads ? pads[2] : 0, pr = pads ? pads[3] : 0;
+    const int64_t dh = dilations ? dilations[0] : 1, dw = dilations ? dilations[1] : 1;
+    if (C < 1 || H < 1 || W < 1 || M < 1 || kH < 1 || kW < 1 || sh_ < 1 || sw_ < 1 || dh < 1 || dw < 1 ||
+        pt < 0 || pl < 0 || pb < 0 || pr < 0 || group < 1)
+        DQ_FAIL(DQ_ERR_ARG, "sizes, strides, dilations and group must be >= 1 and pads >= 0");
+    if (C % group || M % group) DQ_FAIL(DQ_ERR_ARG, "group must divide C and M");
+    const int64_t lim = 1 << 20;
+    if (C > lim || H > lim || W > lim || M > lim || kH > 1024 || kW > 1024 || sh_ > 1024 || sw_ > 1024 ||
+        dh > 1024 || dw > 1024 || pt > 1024 || pl > 1024 || pb > 1024 || pr > 1024)
+        DQ_FAIL(DQ_ERR_RANGE, "a size or attribute beyond the kernel's range");
+    const int64_t oH = (H + pt + pb - dh * (kH - 1) - 1) / sh_ + 1;
+    const int64_t oW = (W + pl + pr - dw * (kW - 1) - 1) / sw_ + 1;
+    if (H + pt + pb - dh * (kH - 1) - 1 < 0 || W + pl + pr - dw * (kW - 1) - 1 < 0 || oH < 1 || oW < 1)
+        DQ_FAIL(DQ_ERR_ARG, "the kernel does not fit the padded input");
+    const int64_t Cg = C / group, Mg = M / group;
+    if (Cg * kH * kW > kKMax) DQ_FAIL(DQ_ERR_RANGE, "C / group * kH * kW exceeds %d (int32 sums)", kKMax);
+    if (oH * oW > (1LL << 30)) DQ_FAIL(DQ_ERR_RANGE, "output image too large");
+    dq_qconv_ctx* c = new dq_qconv_ctx();
+    ConvShape& s = c->sh;
+    s.C = (int)C; s.H = (int)H; s.W = (int)W; s.M = (int)M; s.KH = (int)kH; s.KW = (int)kW;
+    s.sh = (int)sh_; s.sw = (int)sw_; s.pt = (int)pt; s.pl = (int)pl; s.dh = (int)dh; s.dw = (int)dw;
+    s.G = (int)group; s.Cg = (int)Cg; s.Mg = (int)Mg; s.OH = (int)oH; s.OW = (int)oW; s.P = (int)(oH * oW);
+    s.T = s.KH * s.KW;
+    s.Kc = round_up(s.Cg, kKC);
+    s.K = (int)(Cg * kH * kW);
+    s.cpad = round_up(s.pl, 4);
+    const int max_iw = (s.OW - 1) * s.sw - s.pl + (s.KW - 1) * s.dw;
+    s.ncol = round_up(std::max(s.cpad + max_iw + 1, 4), 4);
+    s.ow_div = dq::make_fastdiv((uint32_t)s.OW);
+    // waves over channels: 1 (64 channels x 256 pixels) while a group has
+    // at most 64 channels, else 2 (128 x 128); the patch of the largest
+    // pixel run must fit the LDS budget
+    c->wm = Mg <= 64 ? 1 : 2;
+    for (;;) {
+        const int PT = 64 * (4 / c->wm);
+        const int rows = std::min(s.OH, (PT - 1) / s.OW + 2);
+        const int nr = (rows - 1) * s.sh + (s.KH - 1) * s.dh + 1;
+        const long long bytes = (long long)nr * s.ncol * kKC;
+        if (bytes <= kPatchMax) {
+            c->patch_bytes = (int)bytes;
+            break;
+        }
+        if (c->wm == 2) {
+            free_ctx(c);
+            DQ_FAIL(DQ_ERR_RANGE, "input patch of %lld bytes exceeds the LDS budget", bytes);
+        }
+        c->wm = 2;
+    }
+    s.Mgp = round_up(s.Mg, 64 * c->wm);
+    s.mtiles = s.Mgp / (64 * c->wm);
+    if ((long long)s.G * s.mtiles > 65535) {
+        free_ctx(c);
+        DQ_FAIL(DQ_ERR_RANGE, "too many channel tiles for one launch");
+    }
+    c->x_type = x_type;
+    c->w_type = w_type;
+    c->y_type = y_type;
+    int rc;
+    if (c->wm == 1) {
+        if ((rc = set_lds<true, 1>(c->patch_bytes)) || (rc = set_lds<false, 1>(c->patch_bytes))) {
+            free_ctx(c);
+            return rc;
+        }
+    } else {
+        if ((rc = set_lds<true, 2>(c->patch_bytes)) || (rc = set_lds<false, 2>(c->patch_bytes))) {
+            free_ctx(c);
+            return rc;
+        }
+    }
+    (void)hipGetDevice(&c->device);
+    const size_t rows = (size_t)s.G * s.Mgp;
+    if (hipMalloc(&c->wp, rows * s.T * s.Kc) != hipSuccess || hipMalloc(&c->R, rows * 4) != hipSuccess ||
+        hipMalloc(&c->ws, (size_t)s.M * 4) != hipSuccess || hipMalloc(&c->wz, (size_t)s.M * 4) != hipSuccess ||
+        hipMalloc(&c->bias, (size_t)s.M * 4) != hipSuccess) {
+        free_ctx(c);
+        DQ_FAIL(DQ_ERR_ALLOC, "device allocation for the packed weights failed");
+    }
+    char buf[256];
+    snprintf(buf, sizeof buf,
+             "gfx950 qconv implicit GEMM mfma_i32_32x32x32_i8: %d ch x %d px per workgroup, patch %d B "
+             "(%d x %d x 32), K = %d",
+             64 * c->wm, 64 * (4 / c->wm), c->patch_bytes, c->patch_bytes / (s.ncol * kKC), s.ncol, s.K);
+    c->info = buf;
+    *ctx = c;
+    return DQ_OK;
+}
+
+extern "C" int dq_qconv_output_shape(const dq_qconv_ctx* ctx, int64_t* oH, int64_t* oW) {
+    if (!ctx) DQ_FAIL(DQ_ERR_STATE, "no context");
+    if (oH) *oH = ctx->sh.OH;
+    if (oW) *oW = ctx->sh.OW;
+    return DQ_OK;
+}
+
+extern "C" int dq_qconv_set_w(dq_qconv_ctx* ctx, const void* w, const float* w_scale, const void* w_zero_point,
+                              int64_t w_len, const int32_t* bias, void* stream) {
+    if (!ctx) DQ_FAIL(DQ_ERR_STATE, "no context");
+    const ConvShape& s = ctx->sh;
+    if (!w || !w_scale) DQ_FAIL(DQ_ERR_ARG, "w and w_scale must not be NULL");
+    if (w_len != 1 && w_len != s.M) DQ_FAIL(DQ_ERR_ARG, "w_len must be 1 or M");
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != ctx->device) DQ_FAIL(DQ_ERR_STATE, "the context belongs to another device");
+    const hipStream_t st = (hipStream_t)stream;
+    const int wu8 = ctx->w_type == DQ_U8;
+    hipLaunchKernelGGL(k_conv_pack_w, dim3((unsigned)(s.G * s.Mgp)), dim3(256), 0, st, (const uint8_t*)w, s, wu8,
+                       ctx->wp, ctx->R);
+    DQ_LAUNCH_CHECK("conv weight packing");
+    hipLaunchKernelGGL(k_conv_params, dim3((unsigned)((s.M + 255) / 256)), dim3(256), 0, st, w_scale,
+                       w_zero_point, wu8, (int)w_len, bias, s.M, ctx->ws, ctx->wz, ctx->bias);
+    DQ_LAUNCH_CHECK("conv parameters");
+    // S[p] is needed when some w zero point differs from w's shift
+    std::vector<int32_t> wz(s.M);
+    DQ_HIP_CHECK(hipMemcpyAsync(wz.data(), ctx->wz, (size_t)s.M * 4, hipMemcpyDeviceToHost, st));
+    DQ_HIP_CHECK(hipStreamSynchronize(st));
+    const int kA = wu8 ? 128 : 0;
+    ctx->xsum = false;
+    for (int v : wz) ctx->xsum = ctx->xsum || v != kA;
+    ctx->has_w = true;
+    return DQ_OK;
+}
+
+extern "C" int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, const float* x_scale,
+                                const void* x_zero_point, const float* y_scale, const void* y_zero_point,
+                                void* y, void* stream) {
+    if (!ctx) DQ_FAIL(DQ_ERR_STATE, "no context");
+    if (!ctx->has_w) DQ_FAIL(DQ_ERR_STATE, "dq_qconv_set_w has not been called");
+    const ConvShape& s = ctx->sh;
+    if (N < 0) DQ_FAIL(DQ_ERR_ARG, "N must be >= 0");
+    if (N == 0) return DQ_OK;
+    if (N > 65535) DQ_FAIL(DQ_ERR_RANGE, "N exceeds 65535");
+    if (!x || !x_scale || !y_scale || !y) DQ_FAIL(DQ_ERR_ARG, "x, y and the scales must not be NULL");
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != ctx->device) DQ_FAIL(DQ_ERR_STATE, "the context belongs to another device");
+    ConvArgs a{};
+    a.x = (const uint8_t*)x;
+    a.wp = ctx->wp;
+    a.R = ctx->R;
+    a.ws = ctx->ws;
+    a.wz = ctx->wz;
+    a.bias = ctx->bias;
+    a.x_scale = x_scale;
+    a.x_zp = x_zero_point;
+    a.y_scale = y_scale;
+    a.y_zp = y_zero_point;
+    a.y = (uint8_t*)y;
+    a.x_u8 = ctx->x_type == DQ_U8;
+    a.y_u8 = ctx->y_type == DQ_U8;
+    a.xflip = a.x_u8 ? 0x80808080u : 0u;
+    a.y_lo = a.y_u8 ? 0 : -128;
+    a.y_hi = a.y_u8 ? 255 : 127;
+    a.kA = ctx->w_type == DQ_U8 ? 128 : 0;
+    a.kB = a.x_u8 ? 128 : 0;
+    a.vecx = s.W % 4 == 0 && (uintptr_t)x % 4 == 0;
+    a.vecy = s.P % 16 == 0 && (uintptr_t)y % 16 == 0;
+    const int PT = 64 * (4 / ctx->wm);
+    const dim3 grid((unsigned)((s.P + PT - 1) / PT), (unsigned)(s.G * s.mtiles), (unsigned)N);
+    const hipStream_t st = (hipStream_t)stream;
+    const size_t lds = (size_t)ctx->patch_bytes;
+    if (ctx->wm == 1) {
+        if (ctx->xsum) hipLaunchKernelGGL((k_qconv<true, 1>), grid, dim3(kThreads), lds, st, s, a);
+        else hipLaunchKernelGGL((k_qconv<false, 1>), grid, dim3(kThreads), lds, st, s, a);
+    } else {
+        if (ctx->xsum) hipLaunchKernelGGL((k_qconv<true, 2>), grid, dim3(kThreads), lds, st, s, a);
+        else hipLaunchKernelGGL((k_qconv<false, 2>), grid, dim3(kThreads), lds, st, s, a);
+    }
+    DQ_LAUNCH_CHECK("qconv");
+    return DQ_OK;
+}
+
+extern "C" const char* dq_qconv_info(const dq_qconv_ctx* ctx) { return ctx ? ctx->info.c_str() : nullptr; }
+
+extern "C" void dq_qconv_release(dq_qconv_ctx* ctx) { free_ctx(ctx); }

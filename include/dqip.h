@@ -313,6 +313,57 @@ const char* dq_qgemm_info(const dq_qgemm_ctx* ctx);
 void dq_qgemm_release(dq_qgemm_ctx* ctx);
 
 /* ------------------------------------------------------------------------
+ * General 2-D QLinearConv as an implicit GEMM.
+ * Defined by the ONNX "QLinearConv" operator (opset 10), description and
+ * inputs, with ONNX Conv's attributes (the page names kernel size, stride,
+ * pad lengths and group): x [N, C, H, W], w [M, C / group, kH, kW] and y
+ * [N, M, oH, oW] are dense row-major 8-bit DEVICE tensors,
+ *   oH = floor((H + pad_top + pad_bottom - dil_h (kH - 1) - 1) / stride_h) + 1
+ * (likewise oW); output channel m of group g = m / (M / group) reads input
+ * channels g C / group .. (g + 1) C / group - 1:
+ *   acc  = sum_{c, kh, kw} (w[m,c,kh,kw] - w_zp[m]) (x[n, gC/group + c, ih, iw] - x_zp) + bias[m]
+ *   real = ((float)acc * x_scale) * w_scale[m]
+ *   y    = saturate(rne(real / y_scale) + y_zp)
+ * with ih = oh stride_h - pad_top + kh dil_h, iw likewise; a tap outside the
+ * image reads x_zp (a padded input is a real 0).
+ *
+ * dq_qconv_init: C, H, W, M, kH, kW >= 1; strides[2] (h, w; NULL = 1, 1),
+ * pads[4] (top, left, bottom, right; NULL = 0), dilations[2] (NULL = 1, 1)
+ * are HOST arrays; group >= 1 divides C and M; x_type, w_type, y_type are
+ * DQ_I8 / DQ_U8. Limits: C / group * kH * kW <= 32768 (int32 sums), the
+ * input patch of a workgroup (rows x padded width x 32 bytes) <= 112 KiB.
+ * Allocates the context's device buffers (packed weights). Errors:
+ * DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_RANGE, DQ_ERR_ALLOC, DQ_ERR_HIP.
+ * dq_qconv_output_shape: oH, oW (host).
+ * dq_qconv_set_w: w (DEVICE, the shape above, w_type), w_scale (w_len fp32
+ * on the device, w_len = 1 or M), w_zero_point (w_len values of w_type on
+ * the device, NULL = 0), bias (M int32 on the device, NULL = none). Packs
+ * them into the context and synchronizes `stream`; the caller may free its
+ * tensors afterwards. Errors: DQ_ERR_STATE, DQ_ERR_ARG, DQ_ERR_HIP.
+ * dq_qconv_forward: x (N images), x_scale / y_scale (one fp32 each on the
+ * device), x_zero_point / y_zero_point (one value of x's / y's type on the
+ * device, NULL = 0), y (N x M x oH x oW). Asynchronous on `stream`; N = 0
+ * is a no-op. Errors: DQ_ERR_STATE (no weights, other device), DQ_ERR_ARG,
+ * DQ_ERR_RANGE (N > 65535), DQ_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+typedef struct dq_qconv_ctx dq_qconv_ctx;
+
+int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W, int64_t M, int64_t kH,
+                  int64_t kW, const int64_t* strides, const int64_t* pads,
+                  const int64_t* dilations, int64_t group, dq_dtype x_type, dq_dtype w_type,
+                  dq_dtype y_type);
+int dq_qconv_output_shape(const dq_qconv_ctx* ctx, int64_t* oH, int64_t* oW);
+int dq_qconv_set_w(dq_qconv_ctx* ctx, const void* w, const float* w_scale,
+                   const void* w_zero_point, int64_t w_len, const int32_t* bias, void* stream);
+int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, const float* x_scale,
+                     const void* x_zero_point, const float* y_scale, const void* y_zero_point,
+                     void* y, void* stream);
+/* The kernel shape the context runs (owned by it); NULL for NULL. */
+const char* dq_qconv_info(const dq_qconv_ctx* ctx);
+/* Frees the context and its device memory; NULL is a no-op. */
+void dq_qconv_release(dq_qconv_ctx* ctx);
+
+/* ------------------------------------------------------------------------
  * Element-wise quantized operators.
  * onnxruntime quantization_defs.cc, the contrib schemas QLinearAdd,
  * QLinearMul, MulInteger, QLinearLeakyRelu, QLinearSigmoid,

@@ -253,3 +253,31 @@ def test_elementwise_reject_bad_arguments(dq):
     assert lib.qlinear_concat(2, xs, shapes, 2, 0, sc, None, 1, None, U8, 1, None) == dq.DQ_ERR_ARG
     assert lib.qlinear_concat(0, xs, shapes, 2, 1, sc, None, 1, None, U8, 1, None) == dq.DQ_ERR_ARG
     assert lib.qlinear_concat(2, xs, shapes, 2, 1, sc, None, 1, None, dq.DQ_F32, 1, None) == dq.DQ_ERR_TYPE
+
+
+def test_qconv_init_rejects_bad_arguments(dq):
+    # every check below fails before any device call
+    lib = dq.load()
+    i64 = C.c_int64
+
+    def init(Ci=8, H=9, W=9, M=16, kH=3, kW=3, st=(1, 1), pads=(1, 1, 1, 1), dil=(1, 1), group=1,
+             xt=dq.DQ_U8, wt=dq.DQ_I8, yt=dq.DQ_U8):
+        s, p, d = (i64 * 2)(*st), (i64 * 4)(*pads), (i64 * 2)(*dil)
+        handle = C.c_void_p()
+        rc = lib.dq_qconv_init(C.byref(handle), Ci, H, W, M, kH, kW, C.cast(s, C.c_void_p),
+                               C.cast(p, C.c_void_p), C.cast(d, C.c_void_p), group, xt, wt, yt)
+        assert handle.value is None
+        return rc
+
+    assert init(xt=dq.DQ_F32) == dq.DQ_ERR_TYPE
+    assert init(yt=dq.DQ_BF16) == dq.DQ_ERR_TYPE
+    assert init(Ci=0) == dq.DQ_ERR_ARG
+    assert init(group=3) == dq.DQ_ERR_ARG                # does not divide 8 and 16
+    assert init(st=(0, 1)) == dq.DQ_ERR_ARG
+    assert init(pads=(1, -1, 1, 1)) == dq.DQ_ERR_ARG
+    assert init(H=2, pads=(0, 1, 0, 1)) == dq.DQ_ERR_ARG  # a 3x3 kernel on 2 rows, no pad
+    assert init(Ci=4096) == dq.DQ_ERR_RANGE               # 36864 taps per output
+    assert lib.dq_qconv_set_w(None, 1, 1, None, 1, None, None) == dq.DQ_ERR_STATE
+    assert lib.dq_qconv_forward(None, 1, 1, 1, None, 1, None, 1, None) == dq.DQ_ERR_STATE
+    assert lib.dq_qconv_info(None) is None
+    lib.dq_qconv_release(None)

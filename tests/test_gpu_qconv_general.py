@@ -1,0 +1,143 @@
+"""GPU parity of the general 2-D QLinearConv (implicit GEMM) against the CPU
+oracle: every output code bit-exact.
+
+Cases: the attribute sets pinned on the CPU (strides, asymmetric pads,
+dilations, groups, depthwise, 1x1 with stride), both 8-bit types of x, w
+and y, per-tensor and per-channel w zero points (the correction that needs
+the per-pixel sums), bias, multi-chunk channel counts, channel tiles that
+end inside a group, a ResNet stem (7x7 / 2 over 224x224), and the page's
+printed uint8 example.
+"""
+import json
+import os
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_case import log
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _seed(*key):
+    return zlib.crc32(repr(key).encode())
+
+
+def _codes(r, shape, t):
+    return (r.integers(0, 256, shape).astype(np.uint8) if t == "u8"
+            else r.integers(-128, 128, shape).astype(np.int8))
+
+
+def _run(dq, x, x_scale, x_zp, w, w_scale, w_zp, y_scale, y_zp, y_type, *, bias=None, strides=(1, 1),
+         pads=(0, 0, 0, 0), dilations=(1, 1), group=1, repeat=1):
+    import torch
+
+    N, C, H, W = x.shape
+    M, _, kH, kW = w.shape
+    T = {"u8": dq.DQ_U8, "i8": dq.DQ_I8}
+    tag = lambda a: "u8" if a.dtype == np.uint8 else "i8"  # noqa: E731
+    ctx = dq.dq_qconv_init(C, H, W, M, kH, kW, T[tag(x)], T[tag(w)], T[y_type], strides=strides,
+                           pads=pads, dilations=dilations, group=group)
+    try:
+        oH, oW = dq.dq_qconv_output_shape(ctx)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+        ws = dev(np.atleast_1d(np.asarray(w_scale, np.float32)))
+        wz = None if w_zp is None else dev(np.atleast_1d(np.asarray(w_zp)).astype(w.dtype))
+        dq.dq_qconv_set_w(ctx, dev(w), ws, wz, None if bias is None else dev(bias.astype(np.int32)))
+        y = torch.empty((N, M, oH, oW), dtype=torch.uint8 if y_type == "u8" else torch.int8,
+                        device="cuda")
+        xd = dev(x)
+        xs = dev(np.array([x_scale], np.float32))
+        xz = dev(np.array([x_zp], x.dtype))
+        ysd = dev(np.array([y_scale], np.float32))
+        yz = dev(np.array([y_zp], np.uint8 if y_type == "u8" else np.int8))
+        outs = []
+        for _ in range(repeat):
+            y.fill_(0)
+            dq.dq_qconv_forward(ctx, xd, xs, xz, ysd, yz, y)
+            torch.cuda.synchronize()
+            outs.append(y.cpu().numpy())
+        return outs, dq.dq_qconv_info(ctx)
+    finally:
+        dq.dq_qconv_release(ctx)
+
+
+CASES = [  # (N, C, H, W, M, kH, kW, strides, pads, dilations, group)
+    (1, 3, 9, 11, 4, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1),
+    (2, 4, 8, 8, 6, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 2),
+    (1, 6, 10, 7, 6, 3, 2, (1, 2), (0, 1, 2, 0), (2, 1), 3),
+    (1, 8, 7, 7, 8, 5, 5, (1, 1), (2, 2, 2, 2), (1, 1), 8),
+    (2, 2, 5, 6, 3, 1, 1, (2, 3), (0, 0, 1, 1), (1, 1), 1),
+    (1, 5, 12, 12, 4, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1), 1),
+    (1, 40, 9, 9, 70, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1),      # two chunks, two channel tiles
+    (1, 64, 6, 20, 130, 3, 3, (1, 1), (0, 2, 1, 3), (1, 2), 2),    # groups of 65 channels
+    (2, 33, 17, 3, 65, 2, 3, (3, 1), (2, 0, 0, 1), (1, 1), 1),
+    (3, 16, 15, 15, 16, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 16),   # depthwise 3x3
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("types", [("u8", "i8", "u8"), ("i8", "u8", "i8"), ("u8", "u8", "u8")])
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_qconv_matches_oracle(gpu, case, types, per_channel):
+    N, C, H, W, M, kH, kW, st, pads, dil, group = case
+    xt, wt, yt = types
+    r = np.random.default_rng(_seed(case, types, per_channel))
+    x = _codes(r, (N, C, H, W), xt)
+    w = _codes(r, (M, C // group, kH, kW), wt)
+    nw = M if per_channel else 1
+    ws = r.uniform(0.002, 0.01, nw).astype(np.float32)
+    lo, hi = (0, 256) if wt == "u8" else (-128, 128)
+    wz = r.integers(lo, hi, nw) if per_channel else np.array([128 if wt == "u8" else 0])
+    xz = int(r.integers(0, 256)) if xt == "u8" else int(r.integers(-128, 128))
+    bias = r.integers(-20000, 20000, M).astype(np.int32)
+    ys, yz = np.float32(r.uniform(0.05, 0.5)), (128 if yt == "u8" else 0)
+    log(f"qconv {case} {types} per_channel={per_channel}")
+    want = oracle.qlinear_conv2d(x, 0.02, xz, w, ws, wz, ys, yz, bias=bias, strides=st, pads=pads,
+                                 dilations=dil, group=group, y_type=yt)
+    (got,), info = _run(gpu, x, 0.02, xz, w, ws, wz, ys, yz, yt, bias=bias, strides=st, pads=pads,
+                        dilations=dil, group=group)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ ({info})"
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1)),      # ResNet stage 1, one wave over channels
+    (2, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1, 1, 1)),    # stride 2, 256 output channels
+    (1, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3, 3, 3)),     # the stem: 3 channels in a 32-channel chunk
+])
+def test_qconv_network_layers(gpu, shape):
+    N, C, H, W, M, kH, kW, st, pads = shape
+    r = np.random.default_rng(_seed(shape))
+    x = _codes(r, (N, C, H, W), "u8")
+    w = _codes(r, (M, C, kH, kW), "i8")
+    ws = r.uniform(0.0005, 0.002, M).astype(np.float32)
+    bias = r.integers(-5000, 5000, M).astype(np.int32)
+    log(f"qconv layer {shape}")
+    want = oracle.qlinear_conv2d(x, 0.02, 128, w, ws, np.zeros(M, np.int32), 0.1, 128, bias=bias,
+                                 strides=st, pads=pads, y_type="u8")
+    outs, info = _run(gpu, x, 0.02, 128, w, ws, None, 0.1, 128, "u8", bias=bias, strides=st, pads=pads,
+                      repeat=2)
+    for got in outs:
+        assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ ({info})"
+
+
+def test_qconv_printed_uint8_example(gpu):
+    g = json.load(open(os.path.join(GOLDEN, "qlinearconv_u8.json")))
+    x = np.array(g["x"], np.uint8).reshape(g["x_shape"])
+    w = np.array(g["w"], np.uint8).reshape(g["w_shape"])
+    (got,), _ = _run(gpu, x, g["x_scale"], g["x_zero_point"], w, g["w_scale"], g["w_zero_point"],
+                     g["y_scale"], g["y_zero_point"], "u8")
+    assert got.reshape(-1).tolist() == g["y"]
+
+
+def test_qconv_printed_int8_example(gpu):
+    g = json.load(open(os.path.join(GOLDEN, "qlinearconv_i8.json")))
+    x = np.array(g["x"], np.int8).reshape(g["x_shape"])
+    w = np.array(g["w"], np.int8).reshape(g["w_shape"])
+    (got,), _ = _run(gpu, x, g["x_scale"], g["x_zero_point"], w, g["w_scale"], g["w_zero_point"],
+                     g["y_scale"], g["y_zero_point"], "i8")
+    assert got.reshape(-1).tolist() == g["y"]
