@@ -467,6 +467,43 @@ def bench_elementwise(dq, torch, steps, flush):
     return out
 
 
+def bench_qconv_general(dq, torch, steps, flush):
+    """The general 2-D QLinearConv (implicit GEMM) on ResNet-shaped layers at
+    a batch of 8: uint8 x (zero point 128), int8 w per-channel scales, int32
+    bias, uint8 y. TOP/s of 2 N M oH oW (C / group) kH kW, cold and back to
+    back; a depthwise layer runs the direct kernel (GB/s there)."""
+    import workloads as W
+
+    out = {}
+    for name, (N, C, H, Wd, M, k, st, pad, grp) in W.QCONV_LAYERS.items():
+        c = W.qconv_layer_case(name)
+        ctx = dq.dq_qconv_init(C, H, Wd, M, k, k, dq.DQ_U8, dq.DQ_I8, dq.DQ_U8, strides=(st, st),
+                               pads=(pad, pad, pad, pad), group=grp)
+        try:
+            oh, ow = dq.dq_qconv_output_shape(ctx)
+            dq.dq_qconv_set_w(ctx, dev_tensor(c["w"], torch), dev_tensor(c["w_scale"], torch), None,
+                              dev_tensor(c["bias"], torch))
+            x = dev_tensor(c["x"], torch)
+            y = torch.empty((N, M, oh, ow), dtype=torch.uint8, device="cuda")
+            xs = dev_tensor(np.array([c["x_scale"]], np.float32), torch)
+            ys = dev_tensor(np.array([c["y_scale"]], np.float32), torch)
+            z = dev_tensor(np.array([128], np.uint8), torch)
+            fn = lambda: dq.dq_qconv_forward(ctx, x, xs, z, ys, z, y)  # noqa: E731
+            cold, warm = time_cold_warm(fn, torch, steps, flush)
+            ops = 2.0 * N * M * oh * ow * (C // grp) * k * k
+            nbytes = x.numel() + y.numel() + c["w"].size
+            out[name] = {"us_cold": round(cold[0] * 1e3, 2), "us_cold_p10": round(cold[1] * 1e3, 2),
+                         "us_cold_p90": round(cold[2] * 1e3, 2), "us_warm": round(warm * 1e3, 2),
+                         "TOPS_cold": round(ops / (cold[0] / 1e3) / 1e12, 1),
+                         "TOPS_warm": round(ops / (warm / 1e3) / 1e12, 1),
+                         "GBps_cold": round(nbytes / (cold[0] / 1e3) / 1e9, 1),
+                         "kernel": dq.dq_qconv_info(ctx)}
+            log(f"bench: qconv {name}: {out[name]}")
+        finally:
+            dq.dq_qconv_release(ctx)
+    return out
+
+
 def bench_dqip_case(dq, torch, case, steps, warmup, flush):
     """Back-to-back forwards (warm: a recurrence keeps its weights cache-
     resident), their per-phase kernel times, and single forwards after a
@@ -587,6 +624,8 @@ def main():
             log(f"bench: {secondary[name]}")
         log("bench: element-wise quantized operators")
         secondary["elementwise"] = bench_elementwise(dq, torch, steps2, flush)
+        log("bench: general QLinearConv")
+        secondary["qlinearconv_general"] = bench_qconv_general(dq, torch, steps2, flush)
         del flush
 
     cpu = None

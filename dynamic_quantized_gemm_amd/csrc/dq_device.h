@@ -168,6 +168,26 @@ __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_block)
 // asm statements with a memory clobber keep the compiler from moving memory
 // accesses across it; the scheduling barrier does the same for the
 // machine scheduler.
+// Keeps a lane's loads issued ahead of the work that uses them: the memory
+// clobber stops the loads from sinking below it and the scheduling barrier
+// stops later arithmetic from being hoisted above it, so all of them are in
+// flight before the first wait.
+__device__ __forceinline__ void issue_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// A wave reading back what its own lanes just wrote to LDS: the LDS
+// operations of one wave complete in order, so only the compiler has to be
+// kept from moving the reads above the writes (it may take two differently
+// typed views of one array for unrelated memory); the memory clobbers do
+// that, and the wait drains the writes.
+__device__ __forceinline__ void wave_lds_fence() {
+    asm volatile("" ::: "memory");
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);

@@ -49,12 +49,15 @@ constexpr int kThreads = 256;
 constexpr int kYPitch = 80;     // LDS bytes per staged output row (64 + 16)
 constexpr int kPatchMax = 112 * 1024;  // with the 20 KiB output stage, within 160 KiB of LDS
 constexpr int kKMax = 32768;    // real taps per output: int32 sums stay exact
+constexpr int kTapGroup = 9;    // taps whose weight fragments a lane holds at once
+constexpr int kTapMax = 1024;   // padded taps per kernel (a per-workgroup table of their offsets)
 
 typedef dq::v4i v4i;
 
 struct ConvShape {
     int C, H, W, M, KH, KW, sh, sw, pt, pl, dh, dw, G, Cg, Mg, OH, OW, P;
     int T;     // KH * KW
+    int Tp;    // T rounded up to a tap group (padded taps hold zero weights)
     int Kc;    // Cg rounded up to a chunk
     int Mgp;   // Mg rounded up to the channel tile
     int K;     // Cg * KH * KW real taps
@@ -66,7 +69,7 @@ struct ConvShape {
 
 struct ConvArgs {
     const uint8_t* x;
-    const int8_t* wp;     // packed w^: [G * Mgp][T][Kc]
+    const int8_t* wp;     // packed w^: [G * Mgp][Tp][Kc]
     const int32_t* R;     // [G * Mgp]
     const float* ws;      // [M]
     const int32_t* wz;    // [M]
@@ -93,11 +96,12 @@ __device__ __forceinline__ uint32_t gather_byte(uint32_t d0, uint32_t d1, uint32
            (((d3 >> s) & 0xffu) << 24);
 }
 
-template <bool XSUM, int WM>
+template <bool XSUM, int WM, int IB>
 __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t patch[];
     __shared__ __attribute__((aligned(16))) uint8_t ys[4 * 64 * kYPitch];
-    constexpr int WP = 4 / WM, PT = 64 * WP, MT = 64 * WM;
+    __shared__ int tapoff[kTapMax];  // patch byte offset of each tap (0 for padded taps)
+    constexpr int WP = 4 / WM, PT = 32 * IB * WP, MT = 64 * WM;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     const int n = blockIdx.z;
     const int g = blockIdx.y / sh.mtiles, mt = blockIdx.y - g * sh.mtiles;
     const int m0 = mt * MT + 64 * wm;  // this wave's first channel within the group
-    const int p0 = blockIdx.x * PT, pw0 = p0 + 64 * wp;
+    const int p0 = blockIdx.x * PT, pw0 = p0 + 32 * IB * wp;
 
     // the block's patch: output rows oh_a .. oh_b, input rows from ih0
     const int oh_a = (int)dq::fdiv((uint32_t)p0, sh.ow_div);
@@ -113,10 +117,10 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     const int ih0 = oh_a * sh.sh - sh.pt;
     const int nr = (oh_b - oh_a) * sh.sh + (sh.KH - 1) * sh.dh + 1;
 
-    // the lane's two MFMA pixel rows: patch byte offsets for tap (0, 0)
-    int pix[2];
+    // the lane's IB MFMA pixel rows: patch byte offsets for tap (0, 0)
+    int pix[IB];
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
+    for (int pb = 0; pb < IB; ++pb) {
         const int p = std::min(pw0 + 32 * pb + (lane & 31), sh.P - 1);
         const int oh = (int)dq::fdiv((uint32_t)p, sh.ow_div), ow = p - oh * sh.OW;
         const int r = (oh - oh_a) * sh.sh, c = ow * sh.sw - sh.pl + sh.cpad;
@@ -129,9 +133,9 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     const int ncq = sh.ncol / 4;
     const int units = nr * 8 * ncq;
 
-    dq::v16i acc[2][2], sacc[2];
+    dq::v16i acc[IB][2], sacc[IB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             acc[i][0][r] = 0;
@@ -139,77 +143,144 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
             sacc[i][r] = 0;
         }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-    const int8_t* wrow[2];
+    // weights: a uniform base (this wave's first channel row) plus a fixed
+    // 32-bit lane offset, so a fragment load needs no per-lane address math
+    const int8_t* wbase = a.wp + (size_t)(g * sh.Mgp + m0) * sh.Tp * sh.Kc;
+    uint32_t wlane[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
-        wrow[jb] = a.wp + (size_t)(g * sh.Mgp + m0 + 32 * jb + (lane & 31)) * sh.T * sh.Kc + 16 * (lane >> 5);
+        wlane[jb] = (uint32_t)((32 * jb + (lane & 31)) * sh.Tp * sh.Kc + 16 * (lane >> 5));
+    // the tap offsets, once per workgroup (made visible by the first
+    // chunk's barrier)
+    for (int t = tid; t < sh.Tp; t += kThreads) {
+        const int kh = t / sh.KW, kw = t - kh * sh.KW;
+        tapoff[t] = t < sh.T ? (kh * sh.dh * sh.ncol + kw * sh.dw) * kKC : 0;
+    }
 
-    for (int c0 = 0; c0 < sh.Kc; c0 += kKC) {
-        __syncthreads();  // the previous chunk's operand reads are done
-        // stage the patch: a unit is 4 channels x 4 patch columns of one row,
-        // transposed in registers to 4 words of (column, 4 channels)
-        for (int u = tid; u < units; u += kThreads) {
+    // Staging of a chunk's patch: a unit is 4 channels x 4 patch columns of
+    // one row, transposed in registers to 4 words of (column, 4 channels). A
+    // thread takes up to 4 units at a time and issues all their loads (from
+    // clamped addresses) before any value is used. With W % 4 == 0 (vecx) a
+    // column quad lies wholly inside or wholly outside the image, since the
+    // patch's first column sits at iw = -cpad, a multiple of 4; otherwise
+    // the bytes are loaded one by one.
+    struct Stage {
+        uint32_t raw[4][4][4];  // [unit][channel][byte or word]
+        bool inb[4][4];
+        int urc[4];
+    };
+    auto stage_load = [&](Stage& st, int c0, int ub) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = std::min(ub + k * kThreads, units - 1);
             const int colq = u % ncq, rest = u / ncq;
             const int cq = rest & 7, r = rest >> 3;
+            st.urc[k] = (r * sh.ncol + 4 * colq) * kKC + 4 * cq;
             const int ih = ih0 + r, iw0 = 4 * colq - sh.cpad;
-            uint32_t d[4];
+            const bool hin = ih >= 0 && ih < sh.H;
+            const int ihc = hin ? ih : 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int c = c0 + 4 * cq + j;
-                if (c >= sh.Cg) {
-                    d[j] = 0u;  // a padded channel: x^ = 0
-                } else if (ih < 0 || ih >= sh.H) {
-                    d[j] = zpf;
+                const bool cin = c < sh.Cg;
+                const uint8_t* row = xg + ((size_t)(cin ? c : 0) * sh.H + ihc) * sh.W;
+                st.inb[k][j] = cin;
+                if (a.vecx) {
+                    const bool win = hin && iw0 >= 0 && iw0 < sh.W;
+                    st.raw[k][j][0] = *reinterpret_cast<const uint32_t*>(row + (win ? iw0 : 0));
+                    st.raw[k][j][1] = win;
                 } else {
-                    const uint8_t* row = xg + ((size_t)c * sh.H + ih) * sh.W;
-                    if (a.vecx && iw0 >= 0 && iw0 + 4 <= sh.W) {
-                        d[j] = *reinterpret_cast<const uint32_t*>(row + iw0) ^ a.xflip;
-                    } else {
-                        uint32_t v = 0;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int iw = iw0 + e;
-                            const uint32_t b = (iw >= 0 && iw < sh.W) ? (uint32_t)row[iw] : (uint32_t)(x_zp & 0xff);
-                            v |= b << (8 * e);
-                        }
-                        d[j] = v ^ a.xflip;
+                    for (int e = 0; e < 4; ++e) {
+                        const int iw = iw0 + e;
+                        const bool win = hin && iw >= 0 && iw < sh.W;
+                        st.raw[k][j][e] = win ? 0x100u | row[win ? iw : 0] : 0u;
                     }
                 }
             }
+        }
+        dq::issue_fence();
+    };
+    auto stage_store = [&](const Stage& st, uint8_t* buf, int ub) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (ub + k * kThreads >= units) break;
+            uint32_t d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t v;
+                if (a.vecx) {
+                    v = st.raw[k][j][1] ? st.raw[k][j][0] : (uint32_t)(x_zp & 0xff) * 0x01010101u;
+                } else {
+                    v = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v |= ((st.raw[k][j][e] & 0x100u) ? (st.raw[k][j][e] & 0xffu) : (uint32_t)(x_zp & 0xff))
+                             << (8 * e);
+                }
+                d[j] = st.inb[k][j] ? v ^ a.xflip : 0u;  // a padded channel: x^ = 0
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint32_t*>(&patch[(r * sh.ncol + 4 * colq + i) * kKC + 4 * cq]) =
-                    gather_byte(d[0], d[1], d[2], d[3], i);
+                *reinterpret_cast<uint32_t*>(&buf[st.urc[k] + i * kKC]) = gather_byte(d[0], d[1], d[2], d[3], i);
         }
-        __syncthreads();
+    };
+    // The taps of a staged chunk: a tap group's weight fragments are all
+    // requested before its first MFMA; every MFMA runs (a padded tap has zero
+    // weights, reads the patch at tap (0, 0) and adds zeros to the pixel sums).
+    const v4i zeros = {0, 0, 0, 0};
+    auto mfma_chunk = [&](const uint8_t* buf, int c0) {
+        for (int tg = 0; tg < sh.Tp; tg += kTapGroup) {
+            v4i wf[kTapGroup][2];
+            const int8_t* wg = wbase + (size_t)tg * sh.Kc + c0;
+#pragma unroll
+            for (int i = 0; i < kTapGroup; ++i) {
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+                    wf[i][jb] = *reinterpret_cast<const v4i*>(wg + (size_t)i * sh.Kc + wlane[jb]);
+            }
+#pragma unroll
+            for (int i = 0; i < kTapGroup; ++i) {
+                const int t = tg + i;
+                const int off = tapoff[t];
+                const v4i ones_t = t < sh.T ? ones : zeros;
+                v4i xf[IB];
+#pragma unroll
+                for (int ib = 0; ib < IB; ++ib) xf[ib] = *reinterpret_cast<const v4i*>(&buf[pix[ib] + off]);
+#pragma unroll
+                for (int ib = 0; ib < IB; ++ib) {
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb)
+                        acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[ib], wf[i][jb], acc[ib][jb], 0, 0, 0);
+                    if (XSUM) sacc[ib] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[ib], ones_t, sacc[ib], 0, 0, 0);
+                }
+            }
+        }
+    };
 
-        // taps: the weight fragments of tap t + 1 are requested before the
-        // MFMAs of tap t
-        v4i wf[2], wn[2];
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) wf[jb] = *reinterpret_cast<const v4i*>(wrow[jb] + c0);
-        for (int t = 0; t < sh.T; ++t) {
-            const int tn = t + 1 < sh.T ? t + 1 : t;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-                wn[jb] = *reinterpret_cast<const v4i*>(wrow[jb] + (size_t)tn * sh.Kc + c0);
-            const int kh = t / sh.KW, kw = t - kh * sh.KW;
-            const int off = (kh * sh.dh * sh.ncol + kw * sh.dw) * kKC;
-            const v4i xf0 = *reinterpret_cast<const v4i*>(&patch[pix[0] + off]);
-            const v4i xf1 = *reinterpret_cast<const v4i*>(&patch[pix[1] + off]);
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                acc[0][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf0, wf[jb], acc[0][jb], 0, 0, 0);
-                acc[1][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf1, wf[jb], acc[1][jb], 0, 0, 0);
-            }
-            if (XSUM) {
-                sacc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf0, ones, sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf1, ones, sacc[1], 0, 0, 0);
-            }
-            wf[0] = wn[0];
-            wf[1] = wn[1];
+    for (int c0 = 0; c0 < sh.Kc; c0 += kKC) {
+        // the previous chunk's operand reads are done (a bare barrier: no
+        // wait for global memory)
+        dq::wait_lgkm0();
+        dq::lds_barrier();
+        for (int ub = tid; ub < units; ub += 4 * kThreads) {
+            Stage st;
+            stage_load(st, c0, ub);
+            stage_store(st, patch, ub);
         }
+        dq::wait_lgkm0();
+        dq::lds_barrier();
+        mfma_chunk(patch, c0);
     }
+
+    // The accumulators are read right below. The compiler inserts the wait
+    // states an MFMA result needs before a VALU read, but counting them
+    // across the blocks of the loop exit is its weak point: a fixed drain of
+    // 48 wait states (more than the 18 a 16-pass MFMA needs) makes the
+    // reads safe whatever path led here.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- requantizing epilogue: lane holds channel (lane % 32) of block jb
     // and, in accumulators 4q .. 4q+3, pixels 8q + 4 (lane / 32) + 0..3 of
@@ -234,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         const uint32_t rowc = xb * (uint32_t)R + (uint32_t)sh.K * ((uint32_t)coef * xb) +
                               (uint32_t)(mok ? a.bias[mg] : 0);
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
+        for (int ib = 0; ib < IB; ++ib) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 uint32_t word;
@@ -270,13 +341,13 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
             }
         }
     }
-    // the wave's 64 staged rows back as 16-byte segments (one wave's LDS
-    // operations complete in order: no barrier)
-    dq::wait_lgkm0();
+    // the wave's 64 staged rows (32 IB pixels each) back as 16-byte
+    // segments (one wave's LDS operations complete in order: no barrier)
+    dq::wave_lds_fence();
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < 2 * IB; ++it) {
         const int u = lane + 64 * it;
-        const int rr = u >> 2, qq = u & 3;
+        const int rr = u / (2 * IB), qq = u % (2 * IB);
         const int ml = m0 + rr, p = pw0 + 16 * qq;
         if (ml < sh.Mg && p < sh.P) {
             const v4i v = *reinterpret_cast<const v4i*>(&ysw[rr * kYPitch + 16 * qq]);
@@ -292,8 +363,49 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     }
 }
 
-// Packs w [M, Cg, kH, kW] into w^ rows [G * Mgp][T][Kc] (zeros past Cg and
-// Mg) and R[row] = sum of the row's w^. One workgroup per row.
+// Groups of few channels (depthwise and the like: Cg <= 4 and Mg <= 4),
+// where the implicit GEMM would pad almost all of K and of the channel tile:
+// one thread per output pixel, a workgroup per (image, output channel,
+// 256-pixel run), so the channel's weights are the same for every lane;
+// acc = sum (w^ + a - w_zp) (x - x_zp) in 24-bit multiply-adds (taps outside
+// the image add nothing), then the same requantization.
+__global__ __launch_bounds__(256) void k_qconv_direct(ConvShape sh, ConvArgs a) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y, n = blockIdx.z;
+    const int g = m / sh.Mg, ml = m - g * sh.Mg;
+    const int pc = p < sh.P ? p : sh.P - 1;
+    const int oh = (int)dq::fdiv((uint32_t)pc, sh.ow_div), ow = pc - oh * sh.OW;
+    const int x_zp = zp8(a.x_zp, a.x_u8);
+    const int coef = a.kA - a.wz[m];
+    const int8_t* wr = a.wp + (size_t)(g * sh.Mgp + ml) * sh.Tp * sh.Kc;
+    const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
+    int32_t acc = 0;
+    for (int c = 0; c < sh.Cg; ++c) {
+        const uint8_t* xc = xg + (size_t)c * sh.H * sh.W;
+        for (int kh = 0; kh < sh.KH; ++kh) {
+            const int ih = oh * sh.sh - sh.pt + kh * sh.dh;
+            if (ih < 0 || ih >= sh.H) continue;
+            const uint8_t* xr = xc + (size_t)ih * sh.W;
+            for (int kw = 0; kw < sh.KW; ++kw) {
+                const int iw = ow * sh.sw - sh.pl + kw * sh.dw;
+                const int wv = (int)wr[(kh * sh.KW + kw) * sh.Kc + c] + coef;
+                const int xv = (iw >= 0 && iw < sh.W)
+                                   ? (a.x_u8 ? (int)xr[iw] : (int)(int8_t)xr[iw]) - x_zp
+                                   : 0;
+                acc = __mul24(wv, xv) + acc;
+            }
+        }
+    }
+    if (p >= sh.P) return;
+    acc += a.bias[m];
+    float real = (float)acc * *a.x_scale;
+    real = real * a.ws[m];
+    const int code = dq::sat_add(dq::rne(real / *a.y_scale), zp8(a.y_zp, a.y_u8), a.y_lo, a.y_hi);
+    a.y[((size_t)n * sh.M + m) * sh.P + p] = (uint8_t)code;
+}
+
+// Packs w [M, Cg, kH, kW] into w^ rows [G * Mgp][Tp][Kc] (zeros past Cg,
+// T and Mg) and R[row] = sum of the row's w^. One workgroup per row.
 __global__ __launch_bounds__(256) void k_conv_pack_w(const uint8_t* __restrict__ w, ConvShape sh, int w_u8,
                                                      int8_t* __restrict__ wp, int32_t* __restrict__ R) {
     __shared__ int32_t part[256];
@@ -301,12 +413,12 @@ __global__ __launch_bounds__(256) void k_conv_pack_w(const uint8_t* __restrict__
     const int g = row / sh.Mgp, ml = row - g * sh.Mgp;
     const bool mok = ml < sh.Mg;
     const int m = g * sh.Mg + ml;
-    const int len = sh.T * sh.Kc;
+    const int len = sh.Tp * sh.Kc;
     int32_t s = 0;
     for (int i = threadIdx.x; i < len; i += 256) {
         const int t = i / sh.Kc, c = i - t * sh.Kc;
         int v = 0;
-        if (mok && c < sh.Cg) {
+        if (mok && c < sh.Cg && t < sh.T) {
             const uint32_t b = w[((size_t)m * sh.Cg + c) * sh.T + t];
             v = w_u8 ? (int)b - 128 : (int)(int8_t)b;
         }
@@ -347,6 +459,8 @@ struct dq_qconv_ctx {
     ConvShape sh{};
     dq_dtype x_type, w_type, y_type;
     int wm = 1;            // waves over output channels
+    bool direct = false;   // few channels per group: k_qconv_direct
+    int ib = 2;            // 32-pixel MFMA rows per wave
     int patch_bytes = 0;
     bool has_w = false, xsum = false;
     int device = 0;
@@ -370,12 +484,19 @@ void free_ctx(dq_qconv_ctx* c) {
     delete c;
 }
 
-template <bool XSUM, int WM>
+template <bool XSUM, int WM, int IB>
 int set_lds(int bytes) {
-    if (hipFuncSetAttribute((const void*)k_qconv<XSUM, WM>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_qconv<XSUM, WM, IB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            bytes) != hipSuccess)
         DQ_FAIL(DQ_ERR_HIP, "hipFuncSetAttribute failed for the conv kernel");
     return DQ_OK;
+}
+
+// the LDS budget of the two kernels a context may launch
+template <int WM>
+int set_lds2(int bytes) {
+    int rc = set_lds<true, WM, 2>(bytes);
+    return rc ? rc : set_lds<false, WM, 2>(bytes);
 }
 
 }  // namespace
@@ -405,6 +526,7 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
         DQ_FAIL(DQ_ERR_ARG, "the kernel does not fit the padded input");
     const int64_t Cg = C / group, Mg = M / group;
     if (Cg * kH * kW > kKMax) DQ_FAIL(DQ_ERR_RANGE, "C / group * kH * kW exceeds %d (int32 sums)", kKMax);
+    if (kH * kW > kTapMax - kTapGroup) DQ_FAIL(DQ_ERR_RANGE, "kH * kW exceeds %d", kTapMax - kTapGroup);
     if (oH * oW > (1LL << 30)) DQ_FAIL(DQ_ERR_RANGE, "output image too large");
     dq_qconv_ctx* c = new dq_qconv_ctx();
     ConvShape& s = c->sh;
@@ -412,6 +534,7 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     s.sh = (int)sh_; s.sw = (int)sw_; s.pt = (int)pt; s.pl = (int)pl; s.dh = (int)dh; s.dw = (int)dw;
     s.G = (int)group; s.Cg = (int)Cg; s.Mg = (int)Mg; s.OH = (int)oH; s.OW = (int)oW; s.P = (int)(oH * oW);
     s.T = s.KH * s.KW;
+    s.Tp = round_up(s.T, kTapGroup);
     s.Kc = round_up(s.Cg, kKC);
     s.K = (int)(Cg * kH * kW);
     s.cpad = round_up(s.pl, 4);
@@ -421,14 +544,18 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     // waves over channels: 1 (64 channels x 256 pixels) while a group has
     // at most 64 channels, else 2 (128 x 128); the patch of the largest
     // pixel run must fit the LDS budget
+    c->direct = Cg <= 4 && Mg <= 4;
     c->wm = Mg <= 64 ? 1 : 2;
+    // two 32-pixel MFMA rows a wave (one row gave more workgroups but was
+    // slower on every layer measured but the smallest)
+    c->ib = 2;
     for (;;) {
-        const int PT = 64 * (4 / c->wm);
+        const int PT = 32 * c->ib * (4 / c->wm);
         const int rows = std::min(s.OH, (PT - 1) / s.OW + 2);
         const int nr = (rows - 1) * s.sh + (s.KH - 1) * s.dh + 1;
         const long long bytes = (long long)nr * s.ncol * kKC;
-        if (bytes <= kPatchMax) {
-            c->patch_bytes = (int)bytes;
+        if (bytes <= kPatchMax || c->direct) {
+            c->patch_bytes = (int)std::min<long long>(bytes, kPatchMax);
             break;
         }
         if (c->wm == 2) {
@@ -439,38 +566,35 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     }
     s.Mgp = round_up(s.Mg, 64 * c->wm);
     s.mtiles = s.Mgp / (64 * c->wm);
-    if ((long long)s.G * s.mtiles > 65535) {
+    if ((long long)s.G * s.mtiles > 65535 || (c->direct && s.M > 65535)) {
         free_ctx(c);
         DQ_FAIL(DQ_ERR_RANGE, "too many channel tiles for one launch");
     }
     c->x_type = x_type;
     c->w_type = w_type;
     c->y_type = y_type;
-    int rc;
-    if (c->wm == 1) {
-        if ((rc = set_lds<true, 1>(c->patch_bytes)) || (rc = set_lds<false, 1>(c->patch_bytes))) {
-            free_ctx(c);
-            return rc;
-        }
-    } else {
-        if ((rc = set_lds<true, 2>(c->patch_bytes)) || (rc = set_lds<false, 2>(c->patch_bytes))) {
-            free_ctx(c);
-            return rc;
-        }
+    const int rc = c->wm == 1 ? set_lds2<1>(c->patch_bytes) : set_lds2<2>(c->patch_bytes);
+    if (rc) {
+        free_ctx(c);
+        return rc;
     }
     (void)hipGetDevice(&c->device);
     const size_t rows = (size_t)s.G * s.Mgp;
-    if (hipMalloc(&c->wp, rows * s.T * s.Kc) != hipSuccess || hipMalloc(&c->R, rows * 4) != hipSuccess ||
+    if (hipMalloc(&c->wp, rows * s.Tp * s.Kc) != hipSuccess || hipMalloc(&c->R, rows * 4) != hipSuccess ||
         hipMalloc(&c->ws, (size_t)s.M * 4) != hipSuccess || hipMalloc(&c->wz, (size_t)s.M * 4) != hipSuccess ||
         hipMalloc(&c->bias, (size_t)s.M * 4) != hipSuccess) {
         free_ctx(c);
         DQ_FAIL(DQ_ERR_ALLOC, "device allocation for the packed weights failed");
     }
     char buf[256];
-    snprintf(buf, sizeof buf,
-             "gfx950 qconv implicit GEMM mfma_i32_32x32x32_i8: %d ch x %d px per workgroup, patch %d B "
-             "(%d x %d x 32), K = %d",
-             64 * c->wm, 64 * (4 / c->wm), c->patch_bytes, c->patch_bytes / (s.ncol * kKC), s.ncol, s.K);
+    if (c->direct)
+        snprintf(buf, sizeof buf, "gfx950 qconv direct: one output pixel a lane, %d taps x %d channels", s.T, s.Cg);
+    else
+        snprintf(buf, sizeof buf,
+                 "gfx950 qconv implicit GEMM mfma_i32_32x32x32_i8: %d ch x %d px per workgroup, patch %d B "
+                 "(%d x %d x 32)%s, K = %d",
+                 64 * c->wm, 32 * c->ib * (4 / c->wm), c->patch_bytes, c->patch_bytes / (s.ncol * kKC), s.ncol,
+                 "", s.K);
     c->info = buf;
     *ctx = c;
     return DQ_OK;
@@ -545,17 +669,25 @@ extern "C" int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, con
     a.kB = a.x_u8 ? 128 : 0;
     a.vecx = s.W % 4 == 0 && (uintptr_t)x % 4 == 0;
     a.vecy = s.P % 16 == 0 && (uintptr_t)y % 16 == 0;
-    const int PT = 64 * (4 / ctx->wm);
-    const dim3 grid((unsigned)((s.P + PT - 1) / PT), (unsigned)(s.G * s.mtiles), (unsigned)N);
     const hipStream_t st = (hipStream_t)stream;
-    const size_t lds = (size_t)ctx->patch_bytes;
-    if (ctx->wm == 1) {
-        if (ctx->xsum) hipLaunchKernelGGL((k_qconv<true, 1>), grid, dim3(kThreads), lds, st, s, a);
-        else hipLaunchKernelGGL((k_qconv<false, 1>), grid, dim3(kThreads), lds, st, s, a);
-    } else {
-        if (ctx->xsum) hipLaunchKernelGGL((k_qconv<true, 2>), grid, dim3(kThreads), lds, st, s, a);
-        else hipLaunchKernelGGL((k_qconv<false, 2>), grid, dim3(kThreads), lds, st, s, a);
+    if (ctx->direct) {
+        const dim3 grid((unsigned)((s.P + 255) / 256), (unsigned)s.M, (unsigned)N);
+        hipLaunchKernelGGL(k_qconv_direct, grid, dim3(256), 0, st, s, a);
+        DQ_LAUNCH_CHECK("qconv direct");
+        return DQ_OK;
     }
+    const int PT = 32 * ctx->ib * (4 / ctx->wm);
+    const dim3 grid((unsigned)((s.P + PT - 1) / PT), (unsigned)(s.G * s.mtiles), (unsigned)N);
+    const size_t lds = (size_t)ctx->patch_bytes;
+#define DQ_CONV(XS, W_) hipLaunchKernelGGL((k_qconv<XS, W_, 2>), grid, dim3(kThreads), lds, st, s, a)
+    if (ctx->wm == 1) {
+        if (ctx->xsum) DQ_CONV(true, 1);
+        else DQ_CONV(false, 1);
+    } else {
+        if (ctx->xsum) DQ_CONV(true, 2);
+        else DQ_CONV(false, 2);
+    }
+#undef DQ_CONV
     DQ_LAUNCH_CHECK("qconv");
     return DQ_OK;
 }

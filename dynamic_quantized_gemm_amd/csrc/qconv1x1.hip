@@ -226,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1(
     }
     // the wave's 64 staged rows back as 16-byte segments (LDS operations of
     // one wave complete in order: no barrier)
+    dq::wave_lds_fence();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int u = lane + 64 * it;
@@ -517,6 +518,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1_p(
         if (next >= end) break;
         item = next;
     }
+    dq::wave_lds_fence();  // the last item's codes, staged by this wave
     store_staged<VEC, FULL>(ysw, y, prev_n, prev_p0, mw0, M, HW, lane);
 }
 

@@ -156,15 +156,6 @@ __device__ __forceinline__ void store_bytes(uint8_t* p, const Bytes<E>& b) {
     }
 }
 
-// Keeps a lane's loads issued ahead of the work that uses them: the memory
-// clobber stops the loads from sinking below it and the scheduling barrier
-// stops later arithmetic from being hoisted above it, so all of them are in
-// flight before the first wait.
-__device__ __forceinline__ void issue_fence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 __device__ __forceinline__ uint32_t byte_of(const uint32_t* w, int j) {
     return (w[j >> 2] >> (8 * (j & 3))) & 0xffu;
 }
@@ -239,7 +230,7 @@ k_table_map(const uint8_t* __restrict__ x, uint64_t n, TableArgs a, uint8_t* __r
         Bytes<E> v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = load_bytes<E>(x + (base + q * 256) * E);
-        issue_fence();
+        dq::issue_fence();
 #pragma unroll
         for (int q = 0; q < 4; ++q) store_bytes<E>(y + (base + q * 256) * E, lookup<E>(tab, v[q]));
     }
@@ -299,7 +290,7 @@ __global__ void __launch_bounds__(256) k_concat(CatArgs a) {
         Bytes<E> v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = load_bytes<E>(p.x + (uint64_t)(base + q * 256) * E);
-        issue_fence();
+        dq::issue_fence();
 #pragma unroll
         for (int q = 0; q < 4; ++q) put(base + q * 256, v[q]);
     } else {
@@ -451,7 +442,7 @@ __global__ void __launch_bounds__(256) k_binary(BinArgs p) {
         Bytes<E> A[4], B[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) fetch(base + u * 256, A[u], B[u]);
-        issue_fence();
+        dq::issue_fence();
 #pragma unroll
         for (int u = 0; u < 4; ++u) put(base + u * 256, A[u], B[u]);
     }
@@ -623,7 +614,7 @@ k_reduce_cols(RedArgs a, uint32_t I, uint32_t CW, uint32_t gx, uint32_t rows_per
             const uint64_t r = std::min(rb + (uint64_t)u * RS, r1 - 1);
             v[u] = load_bytes<E>(xo + r * I);
         }
-        issue_fence();
+        dq::issue_fence();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool ok = rb + (uint64_t)u * RS < r1;

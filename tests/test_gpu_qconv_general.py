@@ -105,22 +105,25 @@ def test_qconv_matches_oracle(gpu, case, types, per_channel):
 
 
 @pytest.mark.parametrize("shape", [
-    (2, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1)),      # ResNet stage 1, one wave over channels
-    (2, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1, 1, 1)),    # stride 2, 256 output channels
-    (1, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3, 3, 3)),     # the stem: 3 channels in a 32-channel chunk
+    (2, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1), 1),      # ResNet stage 1, one wave over channels
+    (2, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1, 1, 1), 1),    # stride 2, 256 output channels
+    (1, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3, 3, 3), 1),     # the stem: 3 channels in a 32-channel chunk
+    (1, 32, 64, 64, 256, 3, 3, (1, 1), (1, 1, 1, 1), 1),    # two MFMA pixel rows a wave
+    (2, 96, 28, 28, 96, 3, 3, (1, 1), (1, 1, 1, 1), 96),     # depthwise (the direct kernel)
+    (2, 96, 28, 28, 192, 3, 3, (2, 2), (0, 0, 1, 1), 96),    # depthwise, two outputs a channel, stride 2
 ])
 def test_qconv_network_layers(gpu, shape):
-    N, C, H, W, M, kH, kW, st, pads = shape
+    N, C, H, W, M, kH, kW, st, pads, group = shape
     r = np.random.default_rng(_seed(shape))
     x = _codes(r, (N, C, H, W), "u8")
-    w = _codes(r, (M, C, kH, kW), "i8")
+    w = _codes(r, (M, C // group, kH, kW), "i8")
     ws = r.uniform(0.0005, 0.002, M).astype(np.float32)
     bias = r.integers(-5000, 5000, M).astype(np.int32)
     log(f"qconv layer {shape}")
     want = oracle.qlinear_conv2d(x, 0.02, 128, w, ws, np.zeros(M, np.int32), 0.1, 128, bias=bias,
-                                 strides=st, pads=pads, y_type="u8")
+                                 strides=st, pads=pads, group=group, y_type="u8")
     outs, info = _run(gpu, x, 0.02, 128, w, ws, None, 0.1, 128, "u8", bias=bias, strides=st, pads=pads,
-                      repeat=2)
+                      group=group, repeat=2)
     for got in outs:
         assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ ({info})"
 

@@ -34,6 +34,11 @@ pages describe in words (no public dataset or benchmark suite is involved):
   Sigmoid over 64 Mi codes; ReduceSumInteger / QLinearReduceMean over
   [16384, 4096] rows, [4096, 16384] columns and NCHW / NHWC global pooling
   of [64, 2048, 7, 7]; QLinearConcat of two [32, 256, 56, 56] maps).
+* ``qconv_layer_case`` -- general QLinearConv layers of a ResNet-style
+  network at a batch of 8 (3x3 at 56x56 with 64 and 256 channels, 3x3 at
+  14x14 with 256, the 7x7 / 2 stem over 224x224, a depthwise 3x3): uniform
+  uint8 x, int8 w ~U{-127..127} with per-channel scales ~U(0.0005, 0.002),
+  int32 bias ~U{-5000..5000}.
 """
 from __future__ import annotations
 
@@ -339,3 +344,25 @@ def elementwise_case(kind: str, seed: int = 6):
     if kind == "sigmoid":
         scales[-1], zps[-1] = np.float32(1.0 / 256), lo
     return dict(name=kind, xs=xs, type=t, scales=scales, zps=zps, **extra)
+
+
+# name -> (N, C, H, W, M, k, stride, pad, group)
+QCONV_LAYERS = {
+    "resnet_3x3_64_56": (8, 64, 56, 56, 64, 3, 1, 1, 1),
+    "resnet_3x3_256_56": (8, 256, 56, 56, 256, 3, 1, 1, 1),
+    "resnet_3x3_256_14": (8, 256, 14, 14, 256, 3, 1, 1, 1),
+    "resnet_stem_7x7_s2": (8, 3, 224, 224, 64, 7, 2, 3, 1),
+    "depthwise_3x3_256_56": (8, 256, 56, 56, 256, 3, 1, 1, 256),
+}
+
+
+def qconv_layer_case(name: str, seed: int = 7):
+    """Inputs of one QLinearConv layer of QCONV_LAYERS (x [N,C,H,W] uint8,
+    w [M, C/group, k, k] int8, per-channel scales, bias)."""
+    N, C, H, W, M, k, st, pad, grp = QCONV_LAYERS[name]
+    r = rng(seed)
+    x = _codes(r, (N, C, H, W), "u8")
+    w = r.integers(-127, 128, (M, C // grp, k, k)).astype(np.int8)
+    return dict(name=name, x=x, w=w, w_scale=r.uniform(0.0005, 0.002, M).astype(np.float32),
+                bias=r.integers(-5000, 5000, M).astype(np.int32), x_scale=np.float32(0.02),
+                y_scale=np.float32(0.1))
