@@ -6,7 +6,9 @@ HIP library package and the HIP library never imports it.
 
 Every function takes and returns numpy arrays. Element types are named by
 the tags of ``workloads`` ("f32", "bf16", "i8", "u8"); bf16 tensors travel
-as uint16 bit patterns.
+as uint16 bit patterns. The DynamicQuantizeLSTM reference (readings
+R26-R28) is the module ``oracle.lstm``, written in numpy over this package's
+DynamicQuantizeMatMul.
 """
 from __future__ import annotations
 
