@@ -1,7 +1,7 @@
 """Python binding of libdqip.so: the dynamic quantized inner product,
 QuantizeLinear / DequantizeLinear, the requantizing 1x1 QLinearConv, the
-quantized matrix products and the element-wise quantized operators on AMD
-Instinct MI355X (gfx950).
+quantized matrix products, the element-wise quantized operators, the
+general QLinearConv and DynamicQuantizeLSTM on AMD Instinct MI355X (gfx950).
 
 Argument marshalling only: every step runs in the library's HIP kernels.
 The functions carry the names of the C entry points declared in
@@ -21,4 +21,7 @@ from ._binding import (  # noqa: F401
     qlinear_concat, qlinear_leaky_relu, qlinear_mul, qlinear_reduce_mean, qlinear_sigmoid,
     qlinear_dequantize_f16, qlinear_quantize_f16, dq_qconv_forward, dq_qconv_info,
     dq_qconv_init, dq_qconv_output_shape, dq_qconv_release, dq_qconv_set_w,
+    DQ_LSTM_BIDIRECTIONAL, DQ_LSTM_FORWARD, DQ_LSTM_HIDDEN_MAX, DQ_LSTM_REVERSE, RNN_ACTIVATIONS,
+    dq_lstm_forward, dq_lstm_info, dq_lstm_init, dq_lstm_release, dq_lstm_set_weights,
+    lstm_activation_slots,
 )

@@ -17,6 +17,18 @@ DQ_OK, DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_STATE, DQ_ERR_RANGE, DQ_ERR_ALLOC, DQ_ERR
 DQ_PER_TENSOR = -(2 ** 31)
 DQ_K_MAX = 65536
 DQ_QGEMM_K_MAX = 32768
+DQ_LSTM_FORWARD, DQ_LSTM_REVERSE, DQ_LSTM_BIDIRECTIONAL = 0, 1, 2
+DQ_LSTM_HIDDEN_MAX = 4096
+# dq_rnn_act: ONNX RNN activation name -> (code, takes alpha, default alpha,
+# takes beta, default beta)
+RNN_ACTIVATIONS = {
+    "sigmoid": (0, False, 0.0, False, 0.0), "tanh": (1, False, 0.0, False, 0.0),
+    "relu": (2, False, 0.0, False, 0.0), "affine": (3, True, 1.0, True, 0.0),
+    "leakyrelu": (4, True, 0.01, False, 0.0), "thresholdedrelu": (5, True, 1.0, False, 0.0),
+    "scaledtanh": (6, True, 1.0, True, 1.0), "hardsigmoid": (7, True, 0.2, True, 0.5),
+    "elu": (8, True, 1.0, False, 0.0), "softsign": (9, False, 0.0, False, 0.0),
+    "softplus": (10, False, 0.0, False, 0.0),
+}
 
 _lib = None
 
@@ -71,6 +83,16 @@ _SIGNATURES = {
     "dq_qconv_forward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dq_qconv_info": (C.c_char_p, [C.c_void_p]),
+    "dq_lstm_init": (C.c_int, [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                               C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                               C.c_float, C.c_int]),
+    "dq_lstm_set_weights": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p]),
+    "dq_lstm_forward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dq_lstm_info": (C.c_char_p, [C.c_void_p]),
+    "dq_lstm_release": (None, [C.c_void_p]),
     "dq_qconv_release": (None, [C.c_void_p]),
     "qlinear_add": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -488,3 +510,74 @@ def dq_qconv_info(ctx):
 
 def dq_qconv_release(ctx):
     load().dq_qconv_release(ctx)
+
+
+# ------------------------------------------------------ DynamicQuantizeLSTM
+
+def lstm_activation_slots(activations=None, activation_alpha=None, activation_beta=None, dirs=1):
+    """The ONNX attributes (names, and alpha / beta lists consumed in order by
+    the activations that take the parameter) as per-slot arrays for
+    dq_lstm_init: (codes, alphas, betas), 3 * dirs each."""
+    names = ["Sigmoid", "Tanh", "Tanh"] * dirs if activations is None else list(activations)
+    if len(names) != 3 * dirs:
+        raise ValueError(f"{3 * dirs} activations expected")
+    al = list(activation_alpha or [])
+    be = list(activation_beta or [])
+    codes, alphas, betas = [], [], []
+    for n in names:
+        key = n.lower()
+        if key not in RNN_ACTIVATIONS:
+            raise ValueError(f"activation {n} is not supported")
+        code, ta, da, tb, db = RNN_ACTIVATIONS[key]
+        codes.append(code)
+        alphas.append(al.pop(0) if ta and al else da)
+        betas.append(be.pop(0) if tb and be else db)
+    return codes, alphas, betas
+
+
+def dq_lstm_init(seq_length, batch_size, input_size, hidden_size, direction, w_type, r_type,
+                 activations=None, activation_alpha=None, activation_beta=None, clip=0.0,
+                 input_forget=0):
+    """direction: DQ_LSTM_* code or "forward" / "reverse" / "bidirectional";
+    activations etc. as the ONNX attributes. Returns the context handle."""
+    if isinstance(direction, str):
+        direction = {"forward": DQ_LSTM_FORWARD, "reverse": DQ_LSTM_REVERSE,
+                     "bidirectional": DQ_LSTM_BIDIRECTIONAL}[direction]
+    dirs = 2 if direction == DQ_LSTM_BIDIRECTIONAL else 1
+    codes, alphas, betas = lstm_activation_slots(activations, activation_alpha, activation_beta, dirs)
+    ca = (C.c_int * len(codes))(*codes)
+    aa = (C.c_float * len(alphas))(*alphas)
+    ba = (C.c_float * len(betas))(*betas)
+    h = C.c_void_p()
+    _check(load().dq_lstm_init(C.byref(h), int(seq_length), int(batch_size), int(input_size),
+                               int(hidden_size), int(direction), int(w_type), int(r_type),
+                               C.cast(ca, C.c_void_p), C.cast(aa, C.c_void_p),
+                               C.cast(ba, C.c_void_p), float(clip or 0.0), int(input_forget)),
+           "dq_lstm_init")
+    return h.value
+
+
+def dq_lstm_set_weights(ctx, W, W_scale, W_zero_point, R, R_scale, R_zero_point, B=None, P=None,
+                        stream=None):
+    _check(load().dq_lstm_set_weights(ctx, _ptr(W), _ptr(W_scale), int(W_scale.numel()),
+                                      _ptr(W_zero_point), _ptr(R), _ptr(R_scale),
+                                      int(R_scale.numel()), _ptr(R_zero_point), _ptr(B), _ptr(P),
+                                      _stream(stream)),
+           "dq_lstm_set_weights")
+
+
+def dq_lstm_forward(ctx, X, sequence_lens=None, initial_h=None, initial_c=None, Y=None, Y_h=None,
+                    Y_c=None, stream=None):
+    _check(load().dq_lstm_forward(ctx, _ptr(X), _ptr(sequence_lens), _ptr(initial_h),
+                                  _ptr(initial_c), _ptr(Y), _ptr(Y_h), _ptr(Y_c),
+                                  _stream(stream)),
+           "dq_lstm_forward")
+
+
+def dq_lstm_info(ctx):
+    r = load().dq_lstm_info(ctx)
+    return r.decode() if r else None
+
+
+def dq_lstm_release(ctx):
+    load().dq_lstm_release(ctx)

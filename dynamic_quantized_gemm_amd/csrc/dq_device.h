@@ -206,6 +206,16 @@ __device__ __forceinline__ int32_t acc_read(int32_t a) {
     return v;
 }
 
+// fp32 <-> an unsigned integer with the same order, for atomicMin /
+// atomicMax on fp32 values; f2ord(+0.0f) = 0x80000000, and -0 maps to +0.
+__device__ __forceinline__ uint32_t f2ord(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 // Wave-wide min / max over 64 lanes, returned as a wave-uniform value.
 // Within each row of 16 lanes, four DPP moves combine every lane with its
 // partners (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror:

@@ -51,15 +51,6 @@ constexpr size_t kAlign = 256;
 
 enum { SRC_I8 = 0, SRC_U8 = 1, SRC_F32 = 2 };
 
-// fp32 <-> an unsigned integer with the same order (atomicMin / atomicMax)
-__device__ __forceinline__ uint32_t f2ord(float f) {
-    const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float ord2f(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-
 // The tensor's min / max land in kMmSlots slot pairs (workgroup b adds to
 // slot b % kMmSlots), so no single address takes every workgroup's atomics;
 // mm[0 .. kMmSlots) hold minima, mm[kMmSlots .. 2 kMmSlots) maxima.
@@ -69,8 +60,8 @@ constexpr int kMmSlots = 64;
 // rule over the whole tensor); a whole wave calls it and gets uniform values.
 __device__ __forceinline__ void tensor_params(const uint32_t* mm, float& scale, int& zero) {
     const int lane = threadIdx.x & 63;
-    const float lo = dq::wave_min_uniform(ord2f(mm[lane]));
-    const float hi = dq::wave_max_uniform(ord2f(mm[kMmSlots + lane]));
+    const float lo = dq::wave_min_uniform(dq::ord2f(mm[lane]));
+    const float hi = dq::wave_max_uniform(dq::ord2f(mm[kMmSlots + lane]));
     if (hi == lo) {
         scale = 1.0f;
         zero = 0;
@@ -123,8 +114,8 @@ __global__ void __launch_bounds__(256) k_tensor_minmax(const float* __restrict__
         lo = __builtin_fminf(__builtin_fminf(s_lo[0], s_lo[1]), __builtin_fminf(s_lo[2], s_lo[3]));
         hi = __builtin_fmaxf(__builtin_fmaxf(s_hi[0], s_hi[1]), __builtin_fmaxf(s_hi[2], s_hi[3]));
         const int slot = blockIdx.x % kMmSlots;
-        atomicMin(&mm[slot], f2ord(lo));
-        atomicMax(&mm[kMmSlots + slot], f2ord(hi));
+        atomicMin(&mm[slot], dq::f2ord(lo));
+        atomicMax(&mm[kMmSlots + slot], dq::f2ord(hi));
     }
 }
 

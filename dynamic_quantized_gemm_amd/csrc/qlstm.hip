@@ -1,0 +1,733 @@
+// qlstm.hip -- DynamicQuantizeLSTM on gfx950.
+//
+// onnxruntime quantization_defs.cc, schema DynamicQuantizeLSTM (restated on
+// the graiphic.io DynamicQuantizeLSTM page), gives the tensors and the
+// attributes; the cell is the ONNX LSTM's. This file computes (the readings
+// are stated where the entry points are declared, include/dqip.h):
+//   xw  = X W + Wb, X [seq * batch, input] quantized per tensor to uint8 once
+//   per step s and direction d, for each batch entry b with s < L_b
+//   (t = s, or L_b - 1 - s when d runs in reverse):
+//     hr  = H_{s-1} R + Rb, H_{s-1} [batch, h] quantized per tensor to uint8
+//     pre = xw[t] + hr; peepholes, clip, activations (fp64, rounded once),
+//     C_s, H_s; Y[t] = H_s
+//   and for the other entries H, C held and Y[s] = 0.
+//
+// Layout and kernels:
+//  - The input projection of all times and both directions is one
+//    DynamicQuantizeMatMul on the QGemm path (qgemm.hip) with W's columns
+//    regrouped as [direction][unit][gate i, o, f, c] (k_lstm_pack_w), so the
+//    four gate inputs of one cell are one 16-byte load of xw.
+//  - R is packed once (k_lstm_pack_r) into v_mfma_i32_32x32x32_i8 fragments
+//    of 32 gate columns (8 units x 4 gates, unit-major) by 32 k; a uint8 R
+//    enters as code - 128. k_lstm_params writes the per-column vectors.
+//  - Each step is one launch of k_lstm_step. Workgroup (nt, bt, d) owns
+//    units 8 nt .. 8 nt + 7 of direction d for batch entries 32 bt ..
+//    32 bt + 31. It quantizes those rows of H_{s-1} into LDS in fragment
+//    order, with the per-tensor scale from the extremes the previous step
+//    left in 64 slots (atomics on order-preserving integers), multiplies
+//    them with its R fragments (the four waves split K; R is the first
+//    operand, so a lane's 16 accumulators are 4 units x 4 gates of one
+//    batch entry), sums the four partial tiles through LDS and leaves each
+//    thread the four gates of one cell. The cell update writes C in place,
+//    H_s into the other state buffer, Y, and H_s's extremes for the next
+//    step; the slot two steps ahead is cleared for the step after.
+//  - The integer sum is exact with A^ = q - 128, R^ = r - rho (rho = 128 for
+//    a uint8 R, else 0), alpha = 128 - zp_H, beta[n] = rho - rz[n]:
+//      sum = sum_k A^ R^ + beta * rowsum(A^) + alpha * colsum(R^)[n]
+//            + h * alpha * beta      (wrapping int32, exact for h <= 4096)
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "dq_device.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSlots = 64;      // extremes slots per step (workgroup b adds to slot b % 64)
+constexpr uint32_t kPlusZero = 0x80000000u;  // dq::f2ord(+0.0f)
+
+struct StepArgs {
+    const float* xw;      // [seq * batch][N], column d * 4h + 4u + g
+    const int8_t* rp;     // [dirs][NT][KFP][1024] packed R^
+    const int32_t* rcs;   // [dirs][NT * 32] column sums of R^
+    const int32_t* rbeta; // [dirs][NT * 32] rho - rz
+    const float* rsc;     // [dirs][NT * 32] R scale
+    const float* rbias;   // [dirs][NT * 32] Rb
+    const float* pp;      // [dirs][NT * 8][4] peepholes i, o, f, 0
+    const int32_t* lens;  // [batch] or NULL
+    const float* hin;     // [dirs][batch][h]
+    float* hout;          // [dirs][batch][h]
+    float* c;             // [dirs][batch][h], updated in place
+    float* y;             // [seq][dirs][batch][h] or NULL
+    float* yh;            // [dirs][batch][h], written by the last step (or NULL)
+    float* yc;
+    uint32_t* mm;         // [dirs][3][2][kSlots]
+    int s, seq, batch, h, N, NT, KFP, dirs;
+    int rd_slot, wr_slot, clr_slot;
+    int rev_mask;         // bit d set: direction d runs in reverse
+    int act[6];           // f, g, h of direction 0, then of direction 1
+    float alpha[6], beta[6];
+    float clip;           // <= 0: no clip
+    int input_forget;
+};
+
+// One ONNX RNN activation, evaluated in fp64 from the fp32 argument and
+// rounded to fp32 once.
+__device__ float rnn_act(int kind, float xf, float af, float bf) {
+    const double x = (double)xf, a = (double)af, b = (double)bf;
+    double r;
+    switch (kind) {
+        case DQ_RNN_SIGMOID: r = 1.0 / (1.0 + exp(-x)); break;
+        case DQ_RNN_TANH: r = tanh(x); break;
+        case DQ_RNN_RELU: r = x > 0.0 ? x : 0.0; break;
+        case DQ_RNN_AFFINE: r = a * x + b; break;
+        case DQ_RNN_LEAKY_RELU: r = x < 0.0 ? a * x : x; break;
+        case DQ_RNN_THRESHOLDED_RELU: r = x > a ? x : 0.0; break;
+        case DQ_RNN_SCALED_TANH: r = a * tanh(b * x); break;
+        case DQ_RNN_HARD_SIGMOID: r = fmin(fmax(a * x + b, 0.0), 1.0); break;
+        case DQ_RNN_ELU: r = x >= 0.0 ? x : a * expm1(x); break;
+        case DQ_RNN_SOFTSIGN: r = x / (1.0 + fabs(x)); break;
+        default:  // softplus = log(1 + e^x), split so that e^x cannot overflow
+            r = x == 0.0 ? 0.69314718055994530942 : x < 0.0 ? log1p(exp(x)) : x + log1p(exp(-x));
+    }
+    return (float)r;
+}
+
+__device__ __forceinline__ float clipv(float v, float c) {
+    return c > 0.0f ? __builtin_fminf(__builtin_fmaxf(v, -c), c) : v;
+}
+
+template <int CN, bool VEC>
+__global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t hq[];  // [KFP][1024] codes q - 128
+    __shared__ int32_t red[4][16][64];
+    __shared__ int32_t rowsum[32];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nt = blockIdx.x, bt = blockIdx.y, d = blockIdx.z;
+    const int h = a.h, batch = a.batch, KFP = a.KFP, KFW = KFP >> 2;
+
+    // this wave's first R fragments (k fragment 4 i + w), issued first
+    const dq::v4i* rbase =
+        reinterpret_cast<const dq::v4i*>(a.rp + (size_t)(d * a.NT + nt) * KFP * 1024) + lane;
+    dq::v4i rf[CN];
+#pragma unroll
+    for (int i = 0; i < CN; ++i) rf[i] = rbase[(size_t)(4 * i + w) * 64];
+
+    // per-tensor quantization of H_{s-1}: lo = min(0, min H), hi = max(0, max H)
+    const uint32_t* mmr = a.mm + ((size_t)d * 3 + a.rd_slot) * 2 * kSlots;
+    const float lo = dq::wave_min_uniform(dq::ord2f(mmr[lane]));
+    const float hi = dq::wave_max_uniform(dq::ord2f(mmr[kSlots + lane]));
+    float sc = 1.0f;
+    int zp = 0;
+    if (hi != lo) {
+        sc = (hi - lo) / 255.0f;
+        zp = dq::sat_add(dq::rne(-lo / sc), 0, 0, 255);
+    }
+    if (tid < 32) rowsum[tid] = 0;
+    if (nt == 0 && bt == 0 && tid < 2 * kSlots)
+        a.mm[((size_t)d * 3 + a.clr_slot) * 2 * kSlots + tid] = kPlusZero;
+    __syncthreads();
+
+    // rows 32 bt .. 32 bt + 31 of H_{s-1} to codes in fragment order; a
+    // thread takes 16 consecutive k of one row (k >= h and rows >= batch
+    // give code 0, which adds nothing to the sums)
+    {
+        const dq::QDiv qd = dq::make_qdiv(sc);
+        const int G16 = KFP * 2;  // 16-code groups per row
+        const float* hrows = a.hin + ((size_t)d * batch + (size_t)bt * 32) * h;
+        for (int g = tid; g < 32 * G16; g += kThreads) {
+            const int r = g / G16, k0 = (g - r * G16) * 16;
+            uint32_t pk[4] = {0u, 0u, 0u, 0u};
+            int rs = 0;
+            if (bt * 32 + r < batch && k0 < h) {
+                const float* src = hrows + (size_t)r * h + k0;
+                float v[16];
+                if (VEC) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const dq::f4 x4 = reinterpret_cast<const dq::f4*>(src)[j];
+                        v[4 * j] = x4[0]; v[4 * j + 1] = x4[1]; v[4 * j + 2] = x4[2]; v[4 * j + 3] = x4[3];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    int q = 0;
+                    if (VEC || k0 + j < h) {
+                        const float x = VEC ? v[j] : src[j];
+                        q = dq::sat_add(dq::rne(dq::qdiv(x, qd)), zp, 0, 255) - 128;
+                    }
+                    rs += q;
+                    pk[j >> 2] |= (uint32_t)(q & 0xff) << (8 * (j & 3));
+                }
+            }
+            *reinterpret_cast<dq::u4*>(hq + dq::frag_offset(r, k0, KFP)) = dq::u4{pk[0], pk[1], pk[2], pk[3]};
+            if (rs) atomicAdd(&rowsum[r], rs);
+        }
+    }
+    __syncthreads();
+
+    // sum_k A^ R^ for this wave's share of k, CN fragments per chunk
+    dq::v16i acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0;
+    const dq::v4i* hbase = reinterpret_cast<const dq::v4i*>(hq) + lane;
+    for (int c0 = 0; c0 < KFW; c0 += CN) {
+        const bool more = c0 + CN < KFW;
+        dq::v4i rn[CN];
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < CN; ++i) rn[i] = rbase[(size_t)(4 * (c0 + CN + i) + w) * 64];
+        }
+#pragma unroll
+        for (int i = 0; i < CN; ++i) {
+            const dq::v4i hf = hbase[(4 * (c0 + i) + w) * 64];
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(rf[i], hf, acc, 0, 0, 0);
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < CN; ++i) rf[i] = rn[i];
+        }
+    }
+    // let the last MFMA retire before its accumulators are read
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[w][e][lane] = acc[e];
+    __syncthreads();
+
+    // the cell of (unit u, batch entry b): accumulator rows 8 w + 4 half + e
+    // are gate e of unit 2 w + half of the tile
+    const int half = lane >> 5, bl = lane & 31;
+    const int b = bt * 32 + bl, ul = 2 * w + half, u = nt * 8 + ul;
+    float lo_n = 0.0f, hi_n = 0.0f;
+    if (b < batch && u < h) {
+        int L = a.lens ? a.lens[b] : a.seq;
+        L = L < 0 ? 0 : L > a.seq ? a.seq : L;
+        const size_t su = ((size_t)d * batch + b) * h + u;
+        const float c0 = a.c[su];
+        float hv, cv = c0;
+        if (a.s < L) {
+            const int t = ((a.rev_mask >> d) & 1) ? L - 1 - a.s : a.s;
+            const size_t pc = (size_t)d * a.NT * 32 + nt * 32 + 4 * ul;
+            const dq::f4 x4 = *reinterpret_cast<const dq::f4*>(a.xw + ((size_t)t * batch + b) * a.N +
+                                                               (size_t)d * 4 * h + 4 * u);
+            const dq::v4i cs4 = *reinterpret_cast<const dq::v4i*>(a.rcs + pc);
+            const dq::v4i be4 = *reinterpret_cast<const dq::v4i*>(a.rbeta + pc);
+            const dq::f4 rs4 = *reinterpret_cast<const dq::f4*>(a.rsc + pc);
+            const dq::f4 rb4 = *reinterpret_cast<const dq::f4*>(a.rbias + pc);
+            const dq::f4 p4 = *reinterpret_cast<const dq::f4*>(a.pp + ((size_t)d * a.NT * 8 + u) * 4);
+            const uint32_t al = (uint32_t)(128 - zp), rsum = (uint32_t)rowsum[bl];
+            float pre[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 4 * w + e;
+                uint32_t sum = (uint32_t)red[0][row][lane] + (uint32_t)red[1][row][lane] +
+                               (uint32_t)red[2][row][lane] + (uint32_t)red[3][row][lane];
+                const uint32_t be = (uint32_t)be4[e];
+                sum += be * rsum + al * (uint32_t)cs4[e] + (uint32_t)h * al * be;
+                const float hr = ((float)(int32_t)sum * sc) * rs4[e] + rb4[e];
+                pre[e] = x4[e] + hr;
+            }
+            const int f0 = 3 * d;
+            const float pi = clipv(pre[0] + p4[0] * c0, a.clip);
+            const float pf = clipv(pre[2] + p4[2] * c0, a.clip);
+            const float pg = clipv(pre[3], a.clip);
+            const float ig = rnn_act(a.act[f0], pi, a.alpha[f0], a.beta[f0]);
+            const float fg = a.input_forget ? 1.0f - ig : rnn_act(a.act[f0], pf, a.alpha[f0], a.beta[f0]);
+            const float gg = rnn_act(a.act[f0 + 1], pg, a.alpha[f0 + 1], a.beta[f0 + 1]);
+            cv = fg * c0 + ig * gg;
+            const float po = clipv(pre[1] + p4[1] * cv, a.clip);
+            const float og = rnn_act(a.act[f0], po, a.alpha[f0], a.beta[f0]);
+            hv = og * rnn_act(a.act[f0 + 2], cv, a.alpha[f0 + 2], a.beta[f0 + 2]);
+            a.c[su] = cv;
+            if (a.y) a.y[(((size_t)t * a.dirs + d) * batch + b) * h + u] = hv;
+        } else {
+            hv = a.hin[su];
+            if (a.y) a.y[(((size_t)a.s * a.dirs + d) * batch + b) * h + u] = 0.0f;
+        }
+        a.hout[su] = hv;
+        if (a.yh) a.yh[su] = hv;
+        if (a.yc) a.yc[su] = cv;
+        lo_n = __builtin_fminf(lo_n, hv);
+        hi_n = __builtin_fmaxf(hi_n, hv);
+    }
+    lo_n = dq::wave_min_uniform(lo_n);
+    hi_n = dq::wave_max_uniform(hi_n);
+    if (lane == 0) {
+        uint32_t* mmw = a.mm + ((size_t)d * 3 + a.wr_slot) * 2 * kSlots;
+        const int slot = (blockIdx.x + blockIdx.y * gridDim.x) % kSlots;
+        atomicMin(&mmw[slot], dq::f2ord(lo_n));
+        atomicMax(&mmw[kSlots + slot], dq::f2ord(hi_n));
+    }
+}
+
+// Every extremes slot of every direction to the encoding of +0.
+__global__ void k_lstm_mm_reset(uint32_t* mm, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) mm[i] = kPlusZero;
+}
+
+// The initial state (zeros where not given) into the state buffers, its
+// extremes into slot 0 of its direction; yh / yc (a sequence of length 0)
+// receive it as the final state.
+__global__ void __launch_bounds__(256) k_lstm_begin(const float* h0, const float* c0, int per_dir,
+                                                    float* hs, float* cs, uint32_t* mm, float* yh, float* yc) {
+    const int d = blockIdx.y;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    float hv = 0.0f;
+    if (i < per_dir) {
+        const size_t k = (size_t)d * per_dir + i;
+        hv = h0 ? h0[k] : 0.0f;
+        const float cv = c0 ? c0[k] : 0.0f;
+        hs[k] = hv;
+        cs[k] = cv;
+        if (yh) yh[k] = hv;
+        if (yc) yc[k] = cv;
+    }
+    const float lo = dq::wave_min_uniform(__builtin_fminf(hv, 0.0f));
+    const float hi = dq::wave_max_uniform(__builtin_fmaxf(hv, 0.0f));
+    if ((threadIdx.x & 63) == 0) {
+        uint32_t* m = mm + (size_t)d * 3 * 2 * kSlots;
+        const int slot = (blockIdx.x * 4 + (threadIdx.x >> 6)) % kSlots;
+        atomicMin(&m[slot], dq::f2ord(lo));
+        atomicMax(&m[kSlots + slot], dq::f2ord(hi));
+    }
+}
+
+// W [dirs][input][4h] -> Wcat [input][dirs * 4h], column d * 4h + 4u + g
+// taking W's column g * h + u.
+__global__ void k_lstm_pack_w(const uint8_t* W, int input, int h, int dirs, uint8_t* wcat) {
+    const size_t n = (size_t)input * dirs * 4 * h;
+    const size_t N = (size_t)dirs * 4 * h;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t k = i / N, col = i - k * N;
+        const int d = (int)(col / (4 * h)), p = (int)(col - (size_t)d * 4 * h);
+        const int u = p >> 2, g = p & 3;
+        wcat[i] = W[((size_t)d * input + k) * 4 * h + (size_t)g * h + u];
+    }
+}
+
+// R [dirs][h][4h] -> fragments [dirs][NT][KFP][1024] of R^ = r - rho: one
+// 16-byte lane slot per thread (gate column r, 16 k from 16 * khalf).
+__global__ void k_lstm_pack_r(const uint8_t* R, int h, int NT, int KFP, int dirs, int rho, int8_t* rp) {
+    const size_t nslots = (size_t)dirs * NT * KFP * 64;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nslots; i += (size_t)gridDim.x * blockDim.x) {
+        const int slot = (int)(i & 63);
+        const size_t frag = i >> 6;
+        const int kf = (int)(frag % KFP);
+        const size_t tile = frag / KFP;
+        const int nt = (int)(tile % NT), d = (int)(tile / NT);
+        const int r = slot & 31, kh = slot >> 5;
+        const int u = nt * 8 + (r >> 2), g = r & 3;
+        uint32_t pk[4] = {0u, 0u, 0u, 0u};
+        if (u < h) {
+            const uint8_t* col = R + (size_t)d * h * 4 * h + (size_t)g * h + u;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int k = kf * 32 + kh * 16 + j;
+                const int v = k < h ? (int)col[(size_t)k * 4 * h] - rho : 0;
+                pk[j >> 2] |= (uint32_t)(v & 0xff) << (8 * (j & 3));
+            }
+        }
+        *reinterpret_cast<dq::u4*>(rp + i * 16) = dq::u4{pk[0], pk[1], pk[2], pk[3]};
+    }
+}
+
+__device__ __forceinline__ int zp_at(const void* zp, bool u8, int64_t idx) {
+    if (!zp) return 0;
+    return u8 ? (int)reinterpret_cast<const uint8_t*>(zp)[idx] : (int)reinterpret_cast<const int8_t*>(zp)[idx];
+}
+
+struct ParamArgs {
+    const uint8_t* R;
+    const float *w_scale, *r_scale, *B, *P;
+    const void *w_zp, *r_zp;
+    int w_len, r_len;     // dirs or dirs * 4h
+    int w_u8, r_u8, rho;
+    int h, NT, dirs;
+    // projection vectors [dirs * 4h]
+    float* wsc;
+    uint8_t* wzp;
+    float* wb;
+    // step vectors [dirs][NT * 32] and peepholes [dirs][NT * 8][4]
+    int32_t* rcs;
+    int32_t* rbeta;
+    float* rsc;
+    float* rbias;
+    float* pp;
+};
+
+// One thread per packed gate column p of direction d (unit p / 4, gate p % 4).
+__global__ void k_lstm_params(ParamArgs a) {
+    const int d = blockIdx.y;
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    const int h = a.h;
+    if (p >= a.NT * 32) return;
+    const int u = p >> 2, g = p & 3;
+    const size_t q = (size_t)d * a.NT * 32 + p;
+    int32_t cs = 0, be = 0;
+    float rs = 0.0f, rb = 0.0f;
+    if (u < h) {
+        const int64_t col = (int64_t)g * h + u;  // column of W / R / B in the gate-blocked order
+        const int64_t wi = a.w_len == a.dirs ? d : (int64_t)d * 4 * h + col;
+        const int64_t ri = a.r_len == a.dirs ? d : (int64_t)d * 4 * h + col;
+        const size_t o = (size_t)d * 4 * h + p;
+        a.wsc[o] = a.w_scale[wi];
+        a.wzp[o] = (uint8_t)zp_at(a.w_zp, a.w_u8, wi);
+        a.wb[o] = a.B ? a.B[(size_t)d * 8 * h + col] : 0.0f;
+        // column sum of R^ = r - rho over the h rows
+        const size_t c0 = (size_t)d * h * 4 * h + col;
+        if (a.r_u8)
+            for (int k = 0; k < h; ++k) cs += (int)a.R[c0 + (size_t)k * 4 * h] - 128;
+        else
+            for (int k = 0; k < h; ++k) cs += (int)(int8_t)a.R[c0 + (size_t)k * 4 * h];
+        be = a.rho - zp_at(a.r_zp, a.r_u8, ri);
+        rs = a.r_scale[ri];
+        rb = a.B ? a.B[(size_t)d * 8 * h + 4 * h + col] : 0.0f;
+    }
+    a.rcs[q] = cs;
+    a.rbeta[q] = be;
+    a.rsc[q] = rs;
+    a.rbias[q] = rb;
+    if (g == 0) {
+        float* pq = a.pp + ((size_t)d * a.NT * 8 + u) * 4;
+        const bool on = a.P && u < h;
+        pq[0] = on ? a.P[(size_t)d * 3 * h + u] : 0.0f;
+        pq[1] = on ? a.P[(size_t)d * 3 * h + h + u] : 0.0f;
+        pq[2] = on ? a.P[(size_t)d * 3 * h + 2 * h + u] : 0.0f;
+        pq[3] = 0.0f;
+    }
+}
+
+template <int CN, bool VEC>
+int set_lds(int bytes) {
+    if (hipFuncSetAttribute((const void*)k_lstm_step<CN, VEC>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            bytes) != hipSuccess)
+        DQ_FAIL(DQ_ERR_HIP, "hipFuncSetAttribute failed for the LSTM step kernel");
+    return DQ_OK;
+}
+
+bool valid_act(int k) { return k >= DQ_RNN_SIGMOID && k <= DQ_RNN_SOFTPLUS; }
+
+// ONNX defaults of the activations that take alpha / beta
+float default_alpha(int k) {
+    switch (k) {
+        case DQ_RNN_LEAKY_RELU: return 0.01f;
+        case DQ_RNN_HARD_SIGMOID: return 0.2f;
+        case DQ_RNN_AFFINE:
+        case DQ_RNN_THRESHOLDED_RELU:
+        case DQ_RNN_SCALED_TANH:
+        case DQ_RNN_ELU: return 1.0f;
+        default: return 0.0f;
+    }
+}
+float default_beta(int k) {
+    switch (k) {
+        case DQ_RNN_HARD_SIGMOID: return 0.5f;
+        case DQ_RNN_SCALED_TANH: return 1.0f;
+        default: return 0.0f;
+    }
+}
+
+}  // namespace
+
+struct dq_lstm_ctx {
+    int64_t seq = 0, batch = 0, input = 0, h = 0;
+    int dirs = 1, direction = 0;
+    dq_dtype w_type = DQ_I8, r_type = DQ_I8;
+    int NT = 0, KFP = 0, CN = 1;
+    bool vec = false, has_w = false;
+    int act[6] = {0, 1, 1, 0, 1, 1};
+    float alpha[6] = {}, beta[6] = {};
+    float clip = 0.0f;
+    int input_forget = 0;
+    int device = 0;
+    dq_qgemm_ctx* qg = nullptr;
+    float* xw = nullptr;       // [seq * batch][dirs * 4h]
+    float* wsc = nullptr;      // [dirs * 4h]
+    uint8_t* wzp = nullptr;
+    float* wb = nullptr;
+    int8_t* rp = nullptr;
+    int32_t* rcs = nullptr;
+    int32_t* rbeta = nullptr;
+    float* rsc = nullptr;
+    float* rbias = nullptr;
+    float* pp = nullptr;
+    float* hs = nullptr;       // [2][dirs][batch][h]
+    float* cs = nullptr;       // [dirs][batch][h]
+    uint32_t* mm = nullptr;    // [dirs][3][2][kSlots]
+    std::string info;
+};
+
+namespace {
+
+void free_ctx(dq_lstm_ctx* c) {
+    if (!c) return;
+    dq_qgemm_release(c->qg);
+    void* bufs[] = {c->xw, c->wsc, c->wzp, c->wb, c->rp, c->rcs, c->rbeta, c->rsc, c->rbias, c->pp, c->hs, c->cs, c->mm};
+    for (void* p : bufs) (void)hipFree(p);
+    delete c;
+}
+
+int check_device(const dq_lstm_ctx* c) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != c->device) DQ_FAIL(DQ_ERR_STATE, "the context belongs to another device");
+    return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch_size, int64_t input_size,
+                            int64_t hidden_size, int direction, dq_dtype w_type, dq_dtype r_type,
+                            const int* activations, const float* activation_alpha, const float* activation_beta,
+                            float clip, int input_forget) {
+    if (!ctx) DQ_FAIL(DQ_ERR_ARG, "ctx is NULL");
+    *ctx = nullptr;
+    if (seq_length < 0 || batch_size < 0 || input_size < 1 || hidden_size < 1)
+        DQ_FAIL(DQ_ERR_ARG, "sizes must be seq, batch >= 0 and input, hidden >= 1");
+    if (direction < DQ_LSTM_FORWARD || direction > DQ_LSTM_BIDIRECTIONAL)
+        DQ_FAIL(DQ_ERR_ARG, "direction must be DQ_LSTM_FORWARD, _REVERSE or _BIDIRECTIONAL");
+    if ((w_type != DQ_I8 && w_type != DQ_U8) || (r_type != DQ_I8 && r_type != DQ_U8))
+        DQ_FAIL(DQ_ERR_TYPE, "W and R must be DQ_I8 or DQ_U8");
+    if (hidden_size > DQ_LSTM_HIDDEN_MAX)
+        DQ_FAIL(DQ_ERR_RANGE, "hidden_size exceeds %d", DQ_LSTM_HIDDEN_MAX);
+    if (input_size > DQ_QGEMM_K_MAX) DQ_FAIL(DQ_ERR_RANGE, "input_size exceeds %d", DQ_QGEMM_K_MAX);
+    const int dirs = direction == DQ_LSTM_BIDIRECTIONAL ? 2 : 1;
+    if ((batch_size + 31) / 32 > 65535) DQ_FAIL(DQ_ERR_RANGE, "batch_size exceeds %d", 65535 * 32);
+    const int64_t M = seq_length * batch_size;
+    if (M > (int64_t)INT32_MAX - 256) DQ_FAIL(DQ_ERR_RANGE, "seq_length * batch_size too large");
+    if (M * dirs * 4 * hidden_size > ((int64_t)1 << 36)) DQ_FAIL(DQ_ERR_RANGE, "input projection too large");
+    if (activations)
+        for (int i = 0; i < 3 * dirs; ++i)
+            if (!valid_act(activations[i])) DQ_FAIL(DQ_ERR_ARG, "activation %d is not a dq_rnn_act", activations[i]);
+
+    dq_lstm_ctx* c = new dq_lstm_ctx();
+    c->seq = seq_length;
+    c->batch = batch_size;
+    c->input = input_size;
+    c->h = hidden_size;
+    c->dirs = dirs;
+    c->direction = direction;
+    c->w_type = w_type;
+    c->r_type = r_type;
+    for (int i = 0; i < 3 * dirs; ++i) {
+        const int k = activations ? activations[i] : (i % 3 == 0 ? DQ_RNN_SIGMOID : DQ_RNN_TANH);
+        c->act[i] = k;
+        c->alpha[i] = activation_alpha ? activation_alpha[i] : default_alpha(k);
+        c->beta[i] = activation_beta ? activation_beta[i] : default_beta(k);
+    }
+    c->clip = clip > 0.0f ? clip : 0.0f;
+    c->input_forget = input_forget ? 1 : 0;
+    const int h = (int)hidden_size;
+    c->NT = (h + 7) / 8;
+    const int KF = (h + 31) / 32, KFW = (KF + 3) / 4;
+    c->CN = KFW <= 1 ? 1 : KFW <= 2 ? 2 : KFW <= 4 ? 4 : 8;
+    const int KFWp = (KFW + c->CN - 1) / c->CN * c->CN;
+    c->KFP = 4 * KFWp;
+    c->vec = h % 16 == 0;
+    int rc = DQ_OK;
+    const int lds = c->KFP * 1024;
+#define DQ_LDS(CN_) rc = c->vec ? set_lds<CN_, true>(lds) : set_lds<CN_, false>(lds)
+    switch (c->CN) {
+        case 1: DQ_LDS(1); break;
+        case 2: DQ_LDS(2); break;
+        case 4: DQ_LDS(4); break;
+        default: DQ_LDS(8); break;
+    }
+#undef DQ_LDS
+    if (rc) {
+        free_ctx(c);
+        return rc;
+    }
+    (void)hipGetDevice(&c->device);
+    const size_t N = (size_t)dirs * 4 * h, cols = (size_t)dirs * c->NT * 32;
+    const size_t state = (size_t)dirs * batch_size * h;
+    bool ok = hipMalloc(&c->wsc, N * 4) == hipSuccess && hipMalloc(&c->wzp, N) == hipSuccess &&
+              hipMalloc(&c->wb, N * 4) == hipSuccess &&
+              hipMalloc(&c->rp, (size_t)dirs * c->NT * c->KFP * 1024) == hipSuccess &&
+              hipMalloc(&c->rcs, cols * 4) == hipSuccess && hipMalloc(&c->rbeta, cols * 4) == hipSuccess &&
+              hipMalloc(&c->rsc, cols * 4) == hipSuccess && hipMalloc(&c->rbias, cols * 4) == hipSuccess &&
+              hipMalloc(&c->pp, (size_t)dirs * c->NT * 8 * 16) == hipSuccess &&
+              hipMalloc(&c->hs, std::max<size_t>(2 * state, 1) * 4) == hipSuccess &&
+              hipMalloc(&c->cs, std::max<size_t>(state, 1) * 4) == hipSuccess &&
+              hipMalloc(&c->mm, (size_t)dirs * 3 * 2 * kSlots * 4) == hipSuccess;
+    if (ok && M > 0) ok = hipMalloc(&c->xw, (size_t)M * N * 4) == hipSuccess;
+    if (!ok) {
+        free_ctx(c);
+        DQ_FAIL(DQ_ERR_ALLOC, "device allocation for the LSTM context failed");
+    }
+    if (M > 0) {
+        rc = dq_qgemm_init(&c->qg, M, (int64_t)N, input_size, DQ_F32, 0, w_type, 0, DQ_F32, 1.0f);
+        if (rc) {
+            free_ctx(c);
+            return rc;
+        }
+    }
+    char buf[320];
+    snprintf(buf, sizeof buf,
+             "gfx950 DynamicQuantizeLSTM: input projection = %s; step = one k_lstm_step<%d,%d> launch, "
+             "%d x %lld x %d workgroups of 8 units x 32 batch entries, mfma_i32_32x32x32_i8, LDS %d B",
+             c->qg ? dq_qgemm_info(c->qg) : "none", c->CN, (int)c->vec, c->NT, (long long)((batch_size + 31) / 32),
+             dirs, lds);
+    c->info = buf;
+    *ctx = c;
+    return DQ_OK;
+}
+
+extern "C" int dq_lstm_set_weights(dq_lstm_ctx* ctx, const void* W, const float* W_scale, int64_t W_scale_len,
+                                   const void* W_zero_point, const void* R, const float* R_scale,
+                                   int64_t R_scale_len, const void* R_zero_point, const float* B, const float* P,
+                                   void* stream) {
+    if (!ctx) DQ_FAIL(DQ_ERR_STATE, "no context");
+    if (!W || !W_scale || !R || !R_scale) DQ_FAIL(DQ_ERR_ARG, "W, R and their scales must not be NULL");
+    const int dirs = ctx->dirs;
+    const int64_t h = ctx->h;
+    if ((W_scale_len != dirs && W_scale_len != dirs * 4 * h) || (R_scale_len != dirs && R_scale_len != dirs * 4 * h))
+        DQ_FAIL(DQ_ERR_ARG, "scale lengths must be num_directions or num_directions * 4 * hidden_size");
+    if (int rc = check_device(ctx)) return rc;
+    const hipStream_t st = (hipStream_t)stream;
+    const size_t N = (size_t)dirs * 4 * h;
+    uint8_t* wcat = nullptr;
+    if (hipMalloc(&wcat, (size_t)ctx->input * N) != hipSuccess) DQ_FAIL(DQ_ERR_ALLOC, "device allocation failed");
+    const size_t nw = (size_t)ctx->input * N;
+    hipLaunchKernelGGL(k_lstm_pack_w, dim3((unsigned)std::min<size_t>((nw + 255) / 256, 65536)), dim3(256), 0, st,
+                       (const uint8_t*)W, (int)ctx->input, (int)h, dirs, wcat);
+    hipError_t e = hipGetLastError();
+    const int rho = ctx->r_type == DQ_U8 ? 128 : 0;
+    const size_t nslots = (size_t)dirs * ctx->NT * ctx->KFP * 64;
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(k_lstm_pack_r, dim3((unsigned)std::min<size_t>((nslots + 255) / 256, 65536)), dim3(256),
+                           0, st, (const uint8_t*)R, (int)h, ctx->NT, ctx->KFP, dirs, rho, ctx->rp);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+        ParamArgs p{};
+        p.R = (const uint8_t*)R;
+        p.w_scale = W_scale;
+        p.r_scale = R_scale;
+        p.B = B;
+        p.P = P;
+        p.w_zp = W_zero_point;
+        p.r_zp = R_zero_point;
+        p.w_len = (int)W_scale_len;
+        p.r_len = (int)R_scale_len;
+        p.w_u8 = ctx->w_type == DQ_U8;
+        p.r_u8 = ctx->r_type == DQ_U8;
+        p.rho = rho;
+        p.h = (int)h;
+        p.NT = ctx->NT;
+        p.dirs = dirs;
+        p.wsc = ctx->wsc;
+        p.wzp = ctx->wzp;
+        p.wb = ctx->wb;
+        p.rcs = ctx->rcs;
+        p.rbeta = ctx->rbeta;
+        p.rsc = ctx->rsc;
+        p.rbias = ctx->rbias;
+        p.pp = ctx->pp;
+        hipLaunchKernelGGL(k_lstm_params, dim3((unsigned)((ctx->NT * 32 + 255) / 256), (unsigned)dirs), dim3(256), 0,
+                           st, p);
+        e = hipGetLastError();
+    }
+    int rc = DQ_OK;
+    if (e != hipSuccess) {
+        dq_set_error("launch of the LSTM weight packing failed: %s", hipGetErrorString(e));
+        rc = DQ_ERR_HIP;
+    } else if (ctx->qg) {
+        rc = dq_qgemm_set_b(ctx->qg, wcat, ctx->wsc, (int64_t)N, ctx->wzp, (int64_t)N, stream);
+    }
+    if (rc == DQ_OK && hipStreamSynchronize(st) != hipSuccess) {
+        dq_set_error("hipStreamSynchronize failed after the LSTM weight packing");
+        rc = DQ_ERR_HIP;
+    }
+    (void)hipFree(wcat);
+    if (rc == DQ_OK) ctx->has_w = true;
+    return rc;
+}
+
+extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* sequence_lens, const float* initial_h,
+                               const float* initial_c, float* Y, float* Y_h, float* Y_c, void* stream) {
+    if (!ctx) DQ_FAIL(DQ_ERR_STATE, "no context");
+    if (!ctx->has_w) DQ_FAIL(DQ_ERR_STATE, "dq_lstm_set_weights has not been called");
+    if (int rc = check_device(ctx)) return rc;
+    const int64_t seq = ctx->seq, batch = ctx->batch, h = ctx->h;
+    const int dirs = ctx->dirs;
+    if (batch == 0) return DQ_OK;
+    if (seq > 0 && !X) DQ_FAIL(DQ_ERR_ARG, "X must not be NULL");
+    const hipStream_t st = (hipStream_t)stream;
+    if (seq > 0) {
+        if (int rc = dq_qgemm_forward(ctx->qg, X, nullptr, nullptr, nullptr, 0, 0, ctx->wb, nullptr, nullptr, ctx->xw,
+                                      stream))
+            return rc;
+    }
+    const int nmm = dirs * 3 * 2 * kSlots;
+    hipLaunchKernelGGL(k_lstm_mm_reset, dim3((nmm + 255) / 256), dim3(256), 0, st, ctx->mm, nmm);
+    DQ_LAUNCH_CHECK("LSTM extremes reset");
+    const size_t state = (size_t)dirs * batch * h;
+    const int per_dir = (int)(batch * h);
+    hipLaunchKernelGGL(k_lstm_begin, dim3((unsigned)((per_dir + 255) / 256), (unsigned)dirs), dim3(256), 0, st,
+                       initial_h, initial_c, per_dir, ctx->hs, ctx->cs, ctx->mm, seq == 0 ? Y_h : nullptr,
+                       seq == 0 ? Y_c : nullptr);
+    DQ_LAUNCH_CHECK("LSTM initial state");
+    StepArgs a{};
+    a.xw = ctx->xw;
+    a.rp = ctx->rp;
+    a.rcs = ctx->rcs;
+    a.rbeta = ctx->rbeta;
+    a.rsc = ctx->rsc;
+    a.rbias = ctx->rbias;
+    a.pp = ctx->pp;
+    a.lens = sequence_lens;
+    a.c = ctx->cs;
+    a.y = Y;
+    a.mm = ctx->mm;
+    a.seq = (int)seq;
+    a.batch = (int)batch;
+    a.h = (int)h;
+    a.N = (int)(dirs * 4 * h);
+    a.NT = ctx->NT;
+    a.KFP = ctx->KFP;
+    a.dirs = dirs;
+    a.rev_mask = ctx->direction == DQ_LSTM_REVERSE ? 1 : ctx->direction == DQ_LSTM_BIDIRECTIONAL ? 2 : 0;
+    for (int i = 0; i < 6; ++i) {
+        a.act[i] = ctx->act[i];
+        a.alpha[i] = ctx->alpha[i];
+        a.beta[i] = ctx->beta[i];
+    }
+    a.clip = ctx->clip;
+    a.input_forget = ctx->input_forget;
+    const dim3 grid((unsigned)ctx->NT, (unsigned)((batch + 31) / 32), (unsigned)dirs);
+    const size_t lds = (size_t)ctx->KFP * 1024;
+    for (int64_t s = 0; s < seq; ++s) {
+        a.s = (int)s;
+        a.rd_slot = (int)(s % 3);
+        a.wr_slot = (int)((s + 1) % 3);
+        a.clr_slot = (int)((s + 2) % 3);
+        a.hin = ctx->hs + (size_t)(s & 1) * state;
+        a.hout = ctx->hs + (size_t)((s + 1) & 1) * state;
+        a.yh = s == seq - 1 ? Y_h : nullptr;
+        a.yc = s == seq - 1 ? Y_c : nullptr;
+#define DQ_STEP(CN_)                                                                                       \
+    do {                                                                                                   \
+        if (ctx->vec) hipLaunchKernelGGL((k_lstm_step<CN_, true>), grid, dim3(kThreads), lds, st, a);     \
+        else hipLaunchKernelGGL((k_lstm_step<CN_, false>), grid, dim3(kThreads), lds, st, a);             \
+    } while (0)
+        switch (ctx->CN) {
+            case 1: DQ_STEP(1); break;
+            case 2: DQ_STEP(2); break;
+            case 4: DQ_STEP(4); break;
+            default: DQ_STEP(8); break;
+        }
+#undef DQ_STEP
+        DQ_LAUNCH_CHECK("LSTM step");
+    }
+    return DQ_OK;
+}
+
+extern "C" const char* dq_lstm_info(const dq_lstm_ctx* ctx) { return ctx ? ctx->info.c_str() : nullptr; }
+
+extern "C" void dq_lstm_release(dq_lstm_ctx* ctx) { free_ctx(ctx); }

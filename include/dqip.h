@@ -446,6 +446,100 @@ int qlinear_concat(int n_inputs, const void* const* xs, const int64_t* shapes, i
                    const float* y_scale, const void* y_zero_point, dq_dtype type, void* y,
                    void* stream);
 
+/* ------------------------------------------------------------------------
+ * DynamicQuantizeLSTM.
+ * onnxruntime quantization_defs.cc, schema DynamicQuantizeLSTM (restated on
+ * the graiphic.io DynamicQuantizeLSTM page), gives the tensors and
+ * attributes; the cell equations are the ONNX LSTM's, which the schema
+ * follows. Tensors (dense row-major, fp32 unless said otherwise; dirs = 2
+ * for DQ_LSTM_BIDIRECTIONAL, else 1; h = hidden_size; gate blocks of the 4h
+ * axis in the order i, o, f, c):
+ *   X [seq, batch, input]; W [dirs, input, 4h] and R [dirs, h, 4h] (8-bit);
+ *   W_scale / R_scale [dirs] (per tensor) or [dirs, 4h] (per column), zero
+ *   points of W's / R's type with the same length (NULL = 0); B [dirs, 8h]
+ *   = (Wb, Rb) (NULL = 0); P [dirs, 3h] peepholes i, o, f (NULL = 0);
+ *   sequence_lens [batch] int32 (NULL = all seq); initial_h / initial_c
+ *   [dirs, batch, h] (NULL = 0); outputs Y [seq, dirs, batch, h], Y_h and
+ *   Y_c [dirs, batch, h] (each may be NULL).
+ * The library computes (the schema leaves these open; this is the reading):
+ *   xw = DynamicQuantizeMatMul(X as [seq * batch, input], W) + Wb, X
+ *   quantized per tensor to uint8 once (lo = min(0, min X), hi = max(0,
+ *   max X), scale = (hi - lo) / 255, zp = sat(rne(-lo / scale))); at every
+ *   step hr = DynamicQuantizeMatMul(H_{s-1} [batch, h], R) + Rb with H
+ *   quantized the same way as a whole; each product is
+ *   ((float)sum * a_scale) * w_scale[n] + bias[n]. Then, in fp32 with one
+ *   rounding per operation:
+ *     pre = xw[t] + hr; pre_i += P_i * C_{s-1}; pre_f += P_f * C_{s-1};
+ *     i = f(clip(pre_i)); ft = input_forget ? 1 - i : f(clip(pre_f));
+ *     g = g(clip(pre_c)); C_s = ft * C_{s-1} + i * g;
+ *     pre_o += P_o * C_s; o = f(clip(pre_o)); H_s = o * h(C_s)
+ *   with every activation evaluated in fp64 and rounded to fp32 once, and
+ *   clip(v) = min(max(v, -clip), clip) for clip > 0 (clip <= 0: none; only
+ *   the four gate inputs are clipped). Entry b with length L takes steps
+ *   s < L at time t = s (forward) or t = L - 1 - s (reverse) and writes
+ *   Y[t]; at steps s >= L its H and C are held (and still enter H's
+ *   quantization) and Y[s] = 0. Lengths outside [0, seq] are clamped.
+ *   Y_h / Y_c are the state after the last step; a bidirectional LSTM runs
+ *   direction 0 forward and direction 1 in reverse, independently.
+ *
+ * dq_lstm_init: sizes (seq, batch >= 0; 1 <= input <= DQ_QGEMM_K_MAX;
+ * 1 <= hidden <= DQ_LSTM_HIDDEN_MAX), direction (DQ_LSTM_*), W / R types
+ * (DQ_I8 / DQ_U8), activations (3 * dirs dq_rnn_act values f, g, h per
+ * direction; NULL = Sigmoid, Tanh, Tanh), activation_alpha / _beta (3 * dirs
+ * values, one per activation slot, used by the activations that take the
+ * parameter; NULL = the ONNX defaults: LeakyRelu 0.01, HardSigmoid 0.2 /
+ * 0.5, Affine 1 / 0, ThresholdedRelu 1, ScaledTanh 1 / 1, Elu 1. The ONNX
+ * attribute lists, consumed in order by the activations that take them,
+ * map onto these slots), clip, input_forget. Allocates every device buffer
+ * of the context. Errors: DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_RANGE,
+ * DQ_ERR_ALLOC, DQ_ERR_HIP.
+ * dq_lstm_set_weights: W, R, scales, zero points, B, P as above (DEVICE);
+ * packs them into the context and synchronizes `stream`, so the caller may
+ * free them on return. Errors: DQ_ERR_STATE, DQ_ERR_ARG, DQ_ERR_ALLOC,
+ * DQ_ERR_HIP.
+ * dq_lstm_forward: X, sequence_lens, initial_h, initial_c, Y, Y_h, Y_c as
+ * above (DEVICE); one call runs the whole sequence, asynchronously on
+ * `stream` (calls on one context must not overlap: its state buffers are
+ * shared). Errors: DQ_ERR_STATE (no weights, other device), DQ_ERR_ARG,
+ * DQ_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+#define DQ_LSTM_HIDDEN_MAX 4096
+
+typedef enum { DQ_LSTM_FORWARD = 0, DQ_LSTM_REVERSE = 1, DQ_LSTM_BIDIRECTIONAL = 2 } dq_lstm_direction;
+
+/* The ONNX RNN activation functions. */
+typedef enum {
+    DQ_RNN_SIGMOID = 0,
+    DQ_RNN_TANH = 1,
+    DQ_RNN_RELU = 2,
+    DQ_RNN_AFFINE = 3,           /* alpha * x + beta */
+    DQ_RNN_LEAKY_RELU = 4,       /* x < 0 ? alpha * x : x */
+    DQ_RNN_THRESHOLDED_RELU = 5, /* x > alpha ? x : 0 */
+    DQ_RNN_SCALED_TANH = 6,      /* alpha * tanh(beta * x) */
+    DQ_RNN_HARD_SIGMOID = 7,     /* min(max(alpha * x + beta, 0), 1) */
+    DQ_RNN_ELU = 8,              /* x >= 0 ? x : alpha * (e^x - 1) */
+    DQ_RNN_SOFTSIGN = 9,         /* x / (1 + |x|) */
+    DQ_RNN_SOFTPLUS = 10         /* log(1 + e^x) */
+} dq_rnn_act;
+
+typedef struct dq_lstm_ctx dq_lstm_ctx;
+
+int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch_size, int64_t input_size,
+                 int64_t hidden_size, int direction, dq_dtype w_type, dq_dtype r_type,
+                 const int* activations, const float* activation_alpha,
+                 const float* activation_beta, float clip, int input_forget);
+int dq_lstm_set_weights(dq_lstm_ctx* ctx, const void* W, const float* W_scale, int64_t W_scale_len,
+                        const void* W_zero_point, const void* R, const float* R_scale,
+                        int64_t R_scale_len, const void* R_zero_point, const float* B,
+                        const float* P, void* stream);
+int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* sequence_lens,
+                    const float* initial_h, const float* initial_c, float* Y, float* Y_h,
+                    float* Y_c, void* stream);
+/* A short description of the kernels the context runs (owned by it). */
+const char* dq_lstm_info(const dq_lstm_ctx* ctx);
+/* Frees the context and its device memory; NULL is a no-op. */
+void dq_lstm_release(dq_lstm_ctx* ctx);
+
 #ifdef __cplusplus
 }
 #endif

@@ -281,3 +281,48 @@ def test_qconv_init_rejects_bad_arguments(dq):
     assert lib.dq_qconv_forward(None, 1, 1, 1, None, 1, None, 1, None) == dq.DQ_ERR_STATE
     assert lib.dq_qconv_info(None) is None
     lib.dq_qconv_release(None)
+
+
+def test_lstm_init_rejects_bad_arguments(dq):
+    # every check below fails before any device call
+    lib = dq.load()
+
+    def init(seq=4, batch=2, inp=8, hid=16, direction=0, wt=dq.DQ_I8, rt=dq.DQ_U8, acts=None):
+        handle = C.c_void_p()
+        a = None if acts is None else C.cast((C.c_int * len(acts))(*acts), C.c_void_p)
+        rc = lib.dq_lstm_init(C.byref(handle), seq, batch, inp, hid, direction, wt, rt, a, None,
+                              None, 0.0, 0)
+        assert handle.value is None
+        return rc
+
+    assert init(wt=dq.DQ_F32) == dq.DQ_ERR_TYPE
+    assert init(rt=dq.DQ_BF16) == dq.DQ_ERR_TYPE
+    assert init(hid=0) == dq.DQ_ERR_ARG
+    assert init(inp=0) == dq.DQ_ERR_ARG
+    assert init(seq=-1) == dq.DQ_ERR_ARG
+    assert init(direction=3) == dq.DQ_ERR_ARG
+    assert init(acts=[0, 1, 11]) == dq.DQ_ERR_ARG
+    assert init(hid=dq.DQ_LSTM_HIDDEN_MAX + 1) == dq.DQ_ERR_RANGE
+    assert init(inp=dq.DQ_QGEMM_K_MAX + 1) == dq.DQ_ERR_RANGE
+    assert lib.dq_lstm_set_weights(None, 1, 1, 1, None, 1, 1, 1, None, None, None, None) == dq.DQ_ERR_STATE
+    assert lib.dq_lstm_forward(None, 1, None, None, None, 1, None, None, None) == dq.DQ_ERR_STATE
+    assert lib.dq_lstm_info(None) is None
+    lib.dq_lstm_release(None)
+
+
+def test_lstm_activation_slots_follow_the_consumption_order(dq):
+    """The binding maps the ONNX attribute lists onto per-slot values the way
+    the oracle reads them (alpha / beta consumed in order by the activations
+    that take them, ONNX defaults for the rest)."""
+    from oracle import lstm as L
+
+    acts = ["LeakyRelu", "Tanh", "HardSigmoid", "Affine", "ScaledTanh", "Elu"]
+    codes, al, be = dq.lstm_activation_slots(acts, [0.1, 0.3, 2.0], [0.4], dirs=2)
+    ref = L.resolve_activations(acts, [0.1, 0.3, 2.0], [0.4], 2)
+    for (name, a, b), c, x, y in zip(ref, codes, al, be):
+        code, ta, da, tb, db = dq.RNN_ACTIVATIONS[name]
+        assert c == code
+        assert x == (a if a is not None else da) and y == (b if b is not None else db)
+    assert dq.lstm_activation_slots(None, None, None, 1)[0] == [0, 1, 1]
+    with pytest.raises(ValueError):
+        dq.lstm_activation_slots(["Sigmoid", "Tanh"], None, None, 1)

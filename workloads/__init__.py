@@ -366,3 +366,43 @@ def qconv_layer_case(name: str, seed: int = 7):
     return dict(name=name, x=x, w=w, w_scale=r.uniform(0.0005, 0.002, M).astype(np.float32),
                 bias=r.integers(-5000, 5000, M).astype(np.int32), x_scale=np.float32(0.02),
                 y_scale=np.float32(0.1))
+
+
+def lstm_case(seq: int = 128, batch: int = 32, input_size: int = 512, hidden: int = 512, *,
+              seed: int = 8, direction: str = "forward", w_type: str = "i8", r_type: str = "i8",
+              per_channel: bool = True, zero_points: bool = False, bias: bool = True,
+              peepholes: bool = False, initial: bool = True, lens=None):
+    """A DynamicQuantizeLSTM case (the gate-projection shapes above for the
+    defaults): X ~U(-1,1) [seq, batch, input]; W [dirs, input, 4h] and R
+    [dirs, h, 4h] uniform 8-bit codes (int8 in [-127, 127], uint8 in
+    [0, 255]) with scales ~U(0.5, 1.5) / (127 sqrt(K)) per column (or one
+    per direction), so gate inputs are O(1); zero points 0 (int8) / 128
+    (uint8) unless zero_points draws them per column from +-8 around that;
+    B ~U(-0.5, 0.5) [dirs, 8h]; P ~U(-0.5, 0.5) [dirs, 3h]; initial_h /
+    initial_c ~U(-1, 1); lens: None, or the int32 sequence_lens."""
+    dirs = 2 if direction == "bidirectional" else 1
+    r = rng(seed)
+    g = 4 * hidden
+
+    def weights(rows, t):
+        if t == "u8":
+            w = r.integers(0, 256, (dirs, rows, g)).astype(np.uint8)
+            base, dt = 128, np.uint8
+        else:
+            w = r.integers(-127, 128, (dirs, rows, g)).astype(np.int8)
+            base, dt = 0, np.int8
+        n = (dirs, g) if per_channel else (dirs,)
+        sc = (r.uniform(0.5, 1.5, n) / (127.0 * np.sqrt(rows))).astype(np.float32)
+        zp = (base + r.integers(-8, 9, n) if zero_points else np.full(n, base)).astype(dt)
+        return w, sc, zp
+
+    W, ws, wz = weights(input_size, w_type)
+    R, rs, rz = weights(hidden, r_type)
+    return dict(
+        X=r.uniform(-1, 1, (seq, batch, input_size)).astype(np.float32), W=W, W_scale=ws,
+        W_zp=wz, R=R, R_scale=rs, R_zp=rz, hidden=hidden, direction=direction,
+        B=r.uniform(-0.5, 0.5, (dirs, 8 * hidden)).astype(np.float32) if bias else None,
+        P=r.uniform(-0.5, 0.5, (dirs, 3 * hidden)).astype(np.float32) if peepholes else None,
+        initial_h=r.uniform(-1, 1, (dirs, batch, hidden)).astype(np.float32) if initial else None,
+        initial_c=r.uniform(-1, 1, (dirs, batch, hidden)).astype(np.float32) if initial else None,
+        sequence_lens=None if lens is None else np.asarray(lens, np.int32))
