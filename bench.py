@@ -15,8 +15,10 @@ The same JSON line carries:
                   (GB/s, cold and warm cache), and the other inner-product
                   workloads (64x64x128 latency, the LSTM gate projections,
                   8192^3 with a B quantized on every call), the quantized
-                  matrix products, and the element-wise quantized operators
-                  (GB/s against the 8 TB/s HBM peak);
+                  matrix products, the element-wise quantized operators
+                  (GB/s against the 8 TB/s HBM peak), the general
+                  QLinearConv layers and DynamicQuantizeLSTM over the
+                  gate-projection workload (one call = the whole sequence);
   cpu_baseline -- the CPU oracle on a bounded sample of rows of the same
                   4096^3 workload, single-threaded.
 
@@ -504,6 +506,45 @@ def bench_qconv_general(dq, torch, steps, flush):
     return out
 
 
+def bench_lstm(dq, torch, steps, flush):
+    """DynamicQuantizeLSTM on the gate-projection workload (seq 128, batch 32,
+    input 512, hidden 512, per-column int8 W and R), forward and
+    bidirectional: one forward call runs the whole sequence (the input
+    projection and 128 steps). us per sequence cold and back to back, tokens
+    (seq x batch) per second, and the TOP/s of the two products,
+    2 seq batch (input + hidden) 4 hidden per direction."""
+    import workloads as W
+
+    out = {}
+    for direction in ("forward", "bidirectional"):
+        c = W.lstm_case(direction=direction)
+        seq, batch, nin = c["X"].shape
+        h = c["hidden"]
+        dirs = 2 if direction == "bidirectional" else 1
+        ctx = dq.dq_lstm_init(seq, batch, nin, h, direction, dq.DQ_I8, dq.DQ_I8)
+        try:
+            t = lambda a: None if a is None else dev_tensor(a, torch)  # noqa: E731
+            dq.dq_lstm_set_weights(ctx, t(c["W"]), t(c["W_scale"]), t(c["W_zp"]), t(c["R"]),
+                                   t(c["R_scale"]), t(c["R_zp"]), t(c["B"]), t(c["P"]))
+            X, h0, c0 = t(c["X"]), t(c["initial_h"]), t(c["initial_c"])
+            Y = torch.empty((seq, dirs, batch, h), device="cuda")
+            Yh = torch.empty((dirs, batch, h), device="cuda")
+            Yc = torch.empty((dirs, batch, h), device="cuda")
+            fn = lambda: dq.dq_lstm_forward(ctx, X, None, h0, c0, Y, Yh, Yc)  # noqa: E731
+            cold, warm = time_cold_warm(fn, torch, steps, flush)
+            ops = 2.0 * seq * batch * (nin + h) * 4 * h * dirs
+            out[direction] = {"us_cold": round(cold[0] * 1e3, 1), "us_cold_p10": round(cold[1] * 1e3, 1),
+                              "us_cold_p90": round(cold[2] * 1e3, 1), "us_warm": round(warm * 1e3, 1),
+                              "us_per_step_warm": round(warm * 1e3 / seq, 2),
+                              "tokens_per_s_warm": round(seq * batch / (warm / 1e3)),
+                              "TOPS_warm": round(ops / (warm / 1e3) / 1e12, 2),
+                              "kernel": dq.dq_lstm_info(ctx)}
+            log(f"bench: lstm {direction}: {out[direction]}")
+        finally:
+            dq.dq_lstm_release(ctx)
+    return out
+
+
 def bench_dqip_case(dq, torch, case, steps, warmup, flush):
     """Back-to-back forwards (warm: a recurrence keeps its weights cache-
     resident), their per-phase kernel times, and single forwards after a
@@ -626,6 +667,8 @@ def main():
         secondary["elementwise"] = bench_elementwise(dq, torch, steps2, flush)
         log("bench: general QLinearConv")
         secondary["qlinearconv_general"] = bench_qconv_general(dq, torch, steps2, flush)
+        log("bench: DynamicQuantizeLSTM")
+        secondary["dynamic_quantize_lstm"] = bench_lstm(dq, torch, steps2, flush)
         del flush
 
     cpu = None

@@ -22,15 +22,20 @@
 //    enters as code - 128. k_lstm_params writes the per-column vectors.
 //  - Each step is one launch of k_lstm_step. Workgroup (nt, bt, d) owns
 //    units 8 nt .. 8 nt + 7 of direction d for batch entries 32 bt ..
-//    32 bt + 31. It quantizes those rows of H_{s-1} into LDS in fragment
-//    order, with the per-tensor scale from the extremes the previous step
-//    left in 64 slots (atomics on order-preserving integers), multiplies
-//    them with its R fragments (the four waves split K; R is the first
-//    operand, so a lane's 16 accumulators are 4 units x 4 gates of one
-//    batch entry), sums the four partial tiles through LDS and leaves each
-//    thread the four gates of one cell. The cell update writes C in place,
-//    H_s into the other state buffer, Y, and H_s's extremes for the next
-//    step; the slot two steps ahead is cleared for the step after.
+//    32 bt + 31. Its four waves split K: wave w multiplies k fragments
+//    4 j + w, R as the first MFMA operand (so a lane's 16 accumulators are
+//    4 units x 4 gates of one batch entry) and H_{s-1}'s codes as the
+//    second. Lane l's share of that operand is 16 values of one row of
+//    H_{s-1}, which the lane loads and quantizes itself, with the
+//    per-tensor scale from the extremes the previous step left in 64 slots
+//    (atomics on order-preserving integers): the codes never touch LDS.
+//    The four partial tiles are summed through LDS, leaving each thread the
+//    four gates of one cell; the cell update writes C in place, H_s into the
+//    other state buffer, Y, and H_s's extremes for the next step, and the
+//    slot two steps ahead is cleared for the step after. Every load of a
+//    step is issued at its start, at clamped addresses, so the kernel waits
+//    on memory once (then once more for its xw, issued when the cell's time
+//    is known and in flight during the product).
 //  - The integer sum is exact with A^ = q - 128, R^ = r - rho (rho = 128 for
 //    a uint8 R, else 0), alpha = 128 - zp_H, beta[n] = rho - rz[n]:
 //      sum = sum_k A^ R^ + beta * rowsum(A^) + alpha * colsum(R^)[n]
@@ -101,125 +106,191 @@ __device__ __forceinline__ float clipv(float v, float c) {
     return c > 0.0f ? __builtin_fminf(__builtin_fmaxf(v, -c), c) : v;
 }
 
-template <int CN, bool VEC>
+// The default activations (f = Sigmoid, g = h = Tanh) as inline code, so
+// that the independent gates of a cell overlap; the same evaluation as
+// rnn_act's.
+__device__ __forceinline__ float sigmoid_r(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
+__device__ __forceinline__ float tanh_r(float x) { return (float)tanh((double)x); }
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer, half to even
+
+// H codes of one MFMA operand: 16 values of one row to 16 codes q - 128 in
+// four words (byte e of word m is value 4 m + e), with
+//   q = saturate(rne(x / scale) + zp) = rne(clamp(x / scale, -zp, 255 - zp)) + zp.
+// The quotient is the IEEE one: the residual step of dq::qdiv when FAST
+// (|x / scale| <= 255 here, since lo <= x <= hi and hi - lo = 255 scale), else
+// the division. The magic add rounds half to even into the low mantissa bits,
+// the median clamps, and zp - 128 is added to four bytes at once (each true
+// sum lies in [-128, 127], so the carry-free bytewise add is exact).
+struct HQuant {
+    float s, y, lof, hif;
+    uint32_t z4;  // (zp - 128) in each byte
+};
+
+template <bool FAST>
+__device__ __forceinline__ dq::v4i quant16(const float (&x)[16], const HQuant& q, uint32_t valid16) {
+    dq::v4i out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = x[4 * m + e];
+            float t;
+            if (FAST) {
+                const float q0 = v * q.y;
+                t = __builtin_fmaf(__builtin_fmaf(-q0, q.s, v), q.y, q0);
+            } else {
+                t = v / q.s;
+            }
+            b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t + kMagic, q.lof, q.hif));
+        }
+        const uint32_t p = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+        const uint32_t c = ((p & 0x7f7f7f7fu) + (q.z4 & 0x7f7f7f7fu)) ^ ((p ^ q.z4) & 0x80808080u);
+        // invalid values (k >= h, rows >= batch) give code 0
+        const uint32_t nv = (valid16 >> (4 * m)) & 0xfu;
+        const uint32_t mask = (nv & 1u ? 0xffu : 0u) | (nv & 2u ? 0xff00u : 0u) | (nv & 4u ? 0xff0000u : 0u) |
+                              (nv & 8u ? 0xff000000u : 0u);
+        out[m] = (int)(c & mask);
+    }
+    return out;
+}
+
+template <int CN, bool VEC, bool DEF>
 __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t hq[];  // [KFP][1024] codes q - 128
     __shared__ int32_t red[4][16][64];
-    __shared__ int32_t rowsum[32];
+    __shared__ int32_t rsw[4][32];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nt = blockIdx.x, bt = blockIdx.y, d = blockIdx.z;
-    const int h = a.h, batch = a.batch, KFP = a.KFP, KFW = KFP >> 2;
+    const int h = a.h, batch = a.batch, KFW = a.KFP >> 2, nchunks = KFW / CN;
+    const float* hrows = a.hin + ((size_t)d * batch + (size_t)bt * 32) * h;
 
-    // this wave's first R fragments (k fragment 4 i + w), issued first
+    // Wave w multiplies k fragments 4 j + w (j < KFW), CN at a time. Lane l
+    // holds, as the second MFMA operand, 16 codes of row l % 32 of the tile
+    // at k = 32 kf + 16 (l / 32): it quantizes exactly those 16 values of
+    // H_{s-1}, so the codes never leave its registers.
     const dq::v4i* rbase =
-        reinterpret_cast<const dq::v4i*>(a.rp + (size_t)(d * a.NT + nt) * KFP * 1024) + lane;
-    dq::v4i rf[CN];
+        reinterpret_cast<const dq::v4i*>(a.rp + (size_t)(d * a.NT + nt) * a.KFP * 1024) + lane;
+    const int hr_row = lane & 31, hr_k = (lane >> 5) * 16;
+    const bool row_ok = bt * 32 + hr_row < batch;
+    const float* hsrc = hrows + (size_t)(row_ok ? hr_row : 0) * h;
+    auto load_chunk = [&](int c, dq::v4i (&rr)[CN], float (&hx)[CN][16], uint32_t (&vm)[CN]) {
 #pragma unroll
-    for (int i = 0; i < CN; ++i) rf[i] = rbase[(size_t)(4 * i + w) * 64];
+        for (int i = 0; i < CN; ++i) {
+            const int kf = 4 * (c * CN + i) + w;
+            rr[i] = rbase[(size_t)kf * 64];
+            const int k0 = kf * 32 + hr_k;
+            const int n = row_ok ? (h - k0 < 0 ? 0 : h - k0 > 16 ? 16 : h - k0) : 0;  // valid values
+            vm[i] = n == 16 ? 0xffffu : (1u << n) - 1u;
+            if (VEC) {  // h % 16 == 0: a group is whole or absent
+                const dq::f4* src = reinterpret_cast<const dq::f4*>(n ? hsrc + k0 : hrows);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const dq::f4 v = src[j];
+                    hx[i][4 * j] = v[0]; hx[i][4 * j + 1] = v[1]; hx[i][4 * j + 2] = v[2]; hx[i][4 * j + 3] = v[3];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) hx[i][j] = *(j < n ? hsrc + k0 + j : hrows);
+            }
+        }
+    };
+
+    // Every load of the step is issued here, at addresses clamped into the
+    // tensors where an index runs past them, so none waits for another: the
+    // first chunk of R fragments and H values, the extremes of H_{s-1}, and
+    // the inputs of the thread's cell (unit u, batch entry b; accumulator
+    // rows 8 w + 4 half + e are gate e of unit 2 w + half of the tile).
+    dq::v4i rf[CN];
+    float hx[CN][16];
+    uint32_t vm[CN];
+    load_chunk(0, rf, hx, vm);
+    const uint32_t* mmr = a.mm + ((size_t)d * 3 + a.rd_slot) * 2 * kSlots;
+    const uint32_t mlo = mmr[lane], mhi = mmr[kSlots + lane];
+    const int half = lane >> 5, bl = lane & 31;
+    const int b = bt * 32 + bl, ul = 2 * w + half, u = nt * 8 + ul;
+    const bool cell = b < batch && u < h;
+    const int bc = b < batch ? b : batch - 1, uc = u < h ? u : h - 1;
+    const size_t su = ((size_t)d * batch + bc) * h + uc;
+    const int lraw = a.lens ? a.lens[bc] : a.seq;
+    const float c0 = a.c[su], hold = a.hin[su];
+    const size_t pc = (size_t)d * a.NT * 32 + nt * 32 + 4 * ul;
+    const dq::v4i cs4 = *reinterpret_cast<const dq::v4i*>(a.rcs + pc);
+    const dq::v4i be4 = *reinterpret_cast<const dq::v4i*>(a.rbeta + pc);
+    const dq::f4 rs4 = *reinterpret_cast<const dq::f4*>(a.rsc + pc);
+    const dq::f4 rb4 = *reinterpret_cast<const dq::f4*>(a.rbias + pc);
+    const dq::f4 p4 = *reinterpret_cast<const dq::f4*>(a.pp + ((size_t)d * a.NT * 8 + u) * 4);
+    dq::issue_fence();
 
     // per-tensor quantization of H_{s-1}: lo = min(0, min H), hi = max(0, max H)
-    const uint32_t* mmr = a.mm + ((size_t)d * 3 + a.rd_slot) * 2 * kSlots;
-    const float lo = dq::wave_min_uniform(dq::ord2f(mmr[lane]));
-    const float hi = dq::wave_max_uniform(dq::ord2f(mmr[kSlots + lane]));
+    const float lo = dq::wave_min_uniform(dq::ord2f(mlo));
+    const float hi = dq::wave_max_uniform(dq::ord2f(mhi));
     float sc = 1.0f;
     int zp = 0;
     if (hi != lo) {
         sc = (hi - lo) / 255.0f;
         zp = dq::sat_add(dq::rne(-lo / sc), 0, 0, 255);
     }
-    if (tid < 32) rowsum[tid] = 0;
+    // the cell's time and its input projection, in flight during the product
+    const int L = lraw < 0 ? 0 : lraw > a.seq ? a.seq : lraw;
+    const bool live = cell && a.s < L;
+    const int t = live ? (((a.rev_mask >> d) & 1) ? L - 1 - a.s : a.s) : 0;
+    const dq::f4 x4 =
+        *reinterpret_cast<const dq::f4*>(a.xw + ((size_t)t * batch + bc) * a.N + (size_t)d * 4 * h + 4 * uc);
     if (nt == 0 && bt == 0 && tid < 2 * kSlots)
         a.mm[((size_t)d * 3 + a.clr_slot) * 2 * kSlots + tid] = kPlusZero;
-    __syncthreads();
 
-    // rows 32 bt .. 32 bt + 31 of H_{s-1} to codes in fragment order; a
-    // thread takes 16 consecutive k of one row (k >= h and rows >= batch
-    // give code 0, which adds nothing to the sums)
-    {
-        const dq::QDiv qd = dq::make_qdiv(sc);
-        const int G16 = KFP * 2;  // 16-code groups per row
-        const float* hrows = a.hin + ((size_t)d * batch + (size_t)bt * 32) * h;
-        for (int g = tid; g < 32 * G16; g += kThreads) {
-            const int r = g / G16, k0 = (g - r * G16) * 16;
-            uint32_t pk[4] = {0u, 0u, 0u, 0u};
-            int rs = 0;
-            if (bt * 32 + r < batch && k0 < h) {
-                const float* src = hrows + (size_t)r * h + k0;
-                float v[16];
-                if (VEC) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const dq::f4 x4 = reinterpret_cast<const dq::f4*>(src)[j];
-                        v[4 * j] = x4[0]; v[4 * j + 1] = x4[1]; v[4 * j + 2] = x4[2]; v[4 * j + 3] = x4[3];
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    int q = 0;
-                    if (VEC || k0 + j < h) {
-                        const float x = VEC ? v[j] : src[j];
-                        q = dq::sat_add(dq::rne(dq::qdiv(x, qd)), zp, 0, 255) - 128;
-                    }
-                    rs += q;
-                    pk[j >> 2] |= (uint32_t)(q & 0xff) << (8 * (j & 3));
-                }
-            }
-            *reinterpret_cast<dq::u4*>(hq + dq::frag_offset(r, k0, KFP)) = dq::u4{pk[0], pk[1], pk[2], pk[3]};
-            if (rs) atomicAdd(&rowsum[r], rs);
-        }
-    }
-    __syncthreads();
-
-    // sum_k A^ R^ for this wave's share of k, CN fragments per chunk
+    // sum_k A^ R^ over this wave's fragments, the next chunk's loads in
+    // flight while one is quantized and multiplied; rs sums the codes
+    const dq::QDiv qd = dq::make_qdiv(sc);
+    HQuant hq;
+    hq.s = sc;
+    hq.y = qd.y;
+    hq.lof = kMagic + (float)(0 - zp);
+    hq.hif = kMagic + (float)(255 - zp);
+    hq.z4 = (uint32_t)((zp - 128) & 0xff) * 0x01010101u;
     dq::v16i acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0;
-    const dq::v4i* hbase = reinterpret_cast<const dq::v4i*>(hq) + lane;
-    for (int c0 = 0; c0 < KFW; c0 += CN) {
-        const bool more = c0 + CN < KFW;
+    int rs = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        const bool more = c + 1 < nchunks;
         dq::v4i rn[CN];
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < CN; ++i) rn[i] = rbase[(size_t)(4 * (c0 + CN + i) + w) * 64];
-        }
+        float hn[CN][16];
+        uint32_t vn[CN];
+        if (more) load_chunk(c + 1, rn, hn, vn);
 #pragma unroll
         for (int i = 0; i < CN; ++i) {
-            const dq::v4i hf = hbase[(4 * (c0 + i) + w) * 64];
+            const dq::v4i hf = qd.fast ? quant16<true>(hx[i], hq, vm[i]) : quant16<false>(hx[i], hq, vm[i]);
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(rf[i], hf, acc, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) rs = __builtin_amdgcn_sdot4(hf[m], 0x01010101, rs, false);
         }
         if (more) {
 #pragma unroll
-            for (int i = 0; i < CN; ++i) rf[i] = rn[i];
+            for (int i = 0; i < CN; ++i) {
+                rf[i] = rn[i];
+                vm[i] = vn[i];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) hx[i][j] = hn[i][j];
+            }
         }
     }
     // let the last MFMA retire before its accumulators are read
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[w][e][lane] = acc[e];
+    rs += __shfl_xor(rs, 32);  // lanes l and l + 32 hold the two k halves of row l % 32
+    if (lane < 32) rsw[w][lane] = rs;
     __syncthreads();
 
-    // the cell of (unit u, batch entry b): accumulator rows 8 w + 4 half + e
-    // are gate e of unit 2 w + half of the tile
-    const int half = lane >> 5, bl = lane & 31;
-    const int b = bt * 32 + bl, ul = 2 * w + half, u = nt * 8 + ul;
     float lo_n = 0.0f, hi_n = 0.0f;
-    if (b < batch && u < h) {
-        int L = a.lens ? a.lens[b] : a.seq;
-        L = L < 0 ? 0 : L > a.seq ? a.seq : L;
-        const size_t su = ((size_t)d * batch + b) * h + u;
-        const float c0 = a.c[su];
+    if (cell) {
         float hv, cv = c0;
-        if (a.s < L) {
-            const int t = ((a.rev_mask >> d) & 1) ? L - 1 - a.s : a.s;
-            const size_t pc = (size_t)d * a.NT * 32 + nt * 32 + 4 * ul;
-            const dq::f4 x4 = *reinterpret_cast<const dq::f4*>(a.xw + ((size_t)t * batch + b) * a.N +
-                                                               (size_t)d * 4 * h + 4 * u);
-            const dq::v4i cs4 = *reinterpret_cast<const dq::v4i*>(a.rcs + pc);
-            const dq::v4i be4 = *reinterpret_cast<const dq::v4i*>(a.rbeta + pc);
-            const dq::f4 rs4 = *reinterpret_cast<const dq::f4*>(a.rsc + pc);
-            const dq::f4 rb4 = *reinterpret_cast<const dq::f4*>(a.rbias + pc);
-            const dq::f4 p4 = *reinterpret_cast<const dq::f4*>(a.pp + ((size_t)d * a.NT * 8 + u) * 4);
-            const uint32_t al = (uint32_t)(128 - zp), rsum = (uint32_t)rowsum[bl];
+        if (live) {
+            const uint32_t al = (uint32_t)(128 - zp);
+            const uint32_t rsum = (uint32_t)rsw[0][bl] + (uint32_t)rsw[1][bl] + (uint32_t)rsw[2][bl] +
+                                  (uint32_t)rsw[3][bl];
             float pre[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -235,17 +306,28 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
             const float pi = clipv(pre[0] + p4[0] * c0, a.clip);
             const float pf = clipv(pre[2] + p4[2] * c0, a.clip);
             const float pg = clipv(pre[3], a.clip);
-            const float ig = rnn_act(a.act[f0], pi, a.alpha[f0], a.beta[f0]);
-            const float fg = a.input_forget ? 1.0f - ig : rnn_act(a.act[f0], pf, a.alpha[f0], a.beta[f0]);
-            const float gg = rnn_act(a.act[f0 + 1], pg, a.alpha[f0 + 1], a.beta[f0 + 1]);
+            float ig, fg, gg;
+            if (DEF) {
+                ig = sigmoid_r(pi);
+                fg = a.input_forget ? 1.0f - ig : sigmoid_r(pf);
+                gg = tanh_r(pg);
+            } else {
+                ig = rnn_act(a.act[f0], pi, a.alpha[f0], a.beta[f0]);
+                fg = a.input_forget ? 1.0f - ig : rnn_act(a.act[f0], pf, a.alpha[f0], a.beta[f0]);
+                gg = rnn_act(a.act[f0 + 1], pg, a.alpha[f0 + 1], a.beta[f0 + 1]);
+            }
             cv = fg * c0 + ig * gg;
             const float po = clipv(pre[1] + p4[1] * cv, a.clip);
-            const float og = rnn_act(a.act[f0], po, a.alpha[f0], a.beta[f0]);
-            hv = og * rnn_act(a.act[f0 + 2], cv, a.alpha[f0 + 2], a.beta[f0 + 2]);
+            if (DEF) {
+                hv = sigmoid_r(po) * tanh_r(cv);
+            } else {
+                const float og = rnn_act(a.act[f0], po, a.alpha[f0], a.beta[f0]);
+                hv = og * rnn_act(a.act[f0 + 2], cv, a.alpha[f0 + 2], a.beta[f0 + 2]);
+            }
             a.c[su] = cv;
             if (a.y) a.y[(((size_t)t * a.dirs + d) * batch + b) * h + u] = hv;
         } else {
-            hv = a.hin[su];
+            hv = hold;
             if (a.y) a.y[(((size_t)a.s * a.dirs + d) * batch + b) * h + u] = 0.0f;
         }
         a.hout[su] = hv;
@@ -402,14 +484,6 @@ __global__ void k_lstm_params(ParamArgs a) {
     }
 }
 
-template <int CN, bool VEC>
-int set_lds(int bytes) {
-    if (hipFuncSetAttribute((const void*)k_lstm_step<CN, VEC>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            bytes) != hipSuccess)
-        DQ_FAIL(DQ_ERR_HIP, "hipFuncSetAttribute failed for the LSTM step kernel");
-    return DQ_OK;
-}
-
 bool valid_act(int k) { return k >= DQ_RNN_SIGMOID && k <= DQ_RNN_SOFTPLUS; }
 
 // ONNX defaults of the activations that take alpha / beta
@@ -440,6 +514,7 @@ struct dq_lstm_ctx {
     dq_dtype w_type = DQ_I8, r_type = DQ_I8;
     int NT = 0, KFP = 0, CN = 1;
     bool vec = false, has_w = false;
+    bool def_act = true;  // Sigmoid, Tanh, Tanh in every direction
     int act[6] = {0, 1, 1, 0, 1, 1};
     float alpha[6] = {}, beta[6] = {};
     float clip = 0.0f;
@@ -520,29 +595,18 @@ extern "C" int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch
         c->alpha[i] = activation_alpha ? activation_alpha[i] : default_alpha(k);
         c->beta[i] = activation_beta ? activation_beta[i] : default_beta(k);
     }
+    for (int i = 0; i < 3 * dirs; ++i)
+        c->def_act = c->def_act && c->act[i] == (i % 3 == 0 ? DQ_RNN_SIGMOID : DQ_RNN_TANH);
     c->clip = clip > 0.0f ? clip : 0.0f;
     c->input_forget = input_forget ? 1 : 0;
     const int h = (int)hidden_size;
     c->NT = (h + 7) / 8;
     const int KF = (h + 31) / 32, KFW = (KF + 3) / 4;
-    c->CN = KFW <= 1 ? 1 : KFW <= 2 ? 2 : KFW <= 4 ? 4 : 8;
+    c->CN = KFW <= 1 ? 1 : KFW <= 2 ? 2 : 4;
     const int KFWp = (KFW + c->CN - 1) / c->CN * c->CN;
     c->KFP = 4 * KFWp;
     c->vec = h % 16 == 0;
     int rc = DQ_OK;
-    const int lds = c->KFP * 1024;
-#define DQ_LDS(CN_) rc = c->vec ? set_lds<CN_, true>(lds) : set_lds<CN_, false>(lds)
-    switch (c->CN) {
-        case 1: DQ_LDS(1); break;
-        case 2: DQ_LDS(2); break;
-        case 4: DQ_LDS(4); break;
-        default: DQ_LDS(8); break;
-    }
-#undef DQ_LDS
-    if (rc) {
-        free_ctx(c);
-        return rc;
-    }
     (void)hipGetDevice(&c->device);
     const size_t N = (size_t)dirs * 4 * h, cols = (size_t)dirs * c->NT * 32;
     const size_t state = (size_t)dirs * batch_size * h;
@@ -569,10 +633,10 @@ extern "C" int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch
     }
     char buf[320];
     snprintf(buf, sizeof buf,
-             "gfx950 DynamicQuantizeLSTM: input projection = %s; step = one k_lstm_step<%d,%d> launch, "
-             "%d x %lld x %d workgroups of 8 units x 32 batch entries, mfma_i32_32x32x32_i8, LDS %d B",
-             c->qg ? dq_qgemm_info(c->qg) : "none", c->CN, (int)c->vec, c->NT, (long long)((batch_size + 31) / 32),
-             dirs, lds);
+             "gfx950 DynamicQuantizeLSTM: input projection = %s; step = one k_lstm_step<%d,%d,%d> launch, "
+             "%d x %lld x %d workgroups of 8 units x 32 batch entries, mfma_i32_32x32x32_i8, H quantized in registers",
+             c->qg ? dq_qgemm_info(c->qg) : "none", c->CN, (int)c->vec, (int)c->def_act, c->NT, (long long)((batch_size + 31) / 32),
+             dirs);
     c->info = buf;
     *ctx = c;
     return DQ_OK;
@@ -701,7 +765,6 @@ extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* 
     a.clip = ctx->clip;
     a.input_forget = ctx->input_forget;
     const dim3 grid((unsigned)ctx->NT, (unsigned)((batch + 31) / 32), (unsigned)dirs);
-    const size_t lds = (size_t)ctx->KFP * 1024;
     for (int64_t s = 0; s < seq; ++s) {
         a.s = (int)s;
         a.rd_slot = (int)(s % 3);
@@ -711,18 +774,24 @@ extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* 
         a.hout = ctx->hs + (size_t)((s + 1) & 1) * state;
         a.yh = s == seq - 1 ? Y_h : nullptr;
         a.yc = s == seq - 1 ? Y_c : nullptr;
-#define DQ_STEP(CN_)                                                                                       \
+#define DQ_STEP_(CN_, V_)                                                                                  \
     do {                                                                                                   \
-        if (ctx->vec) hipLaunchKernelGGL((k_lstm_step<CN_, true>), grid, dim3(kThreads), lds, st, a);     \
-        else hipLaunchKernelGGL((k_lstm_step<CN_, false>), grid, dim3(kThreads), lds, st, a);             \
+        if (ctx->def_act) hipLaunchKernelGGL((k_lstm_step<CN_, V_, true>), grid, dim3(kThreads), 0, st, a); \
+        else hipLaunchKernelGGL((k_lstm_step<CN_, V_, false>), grid, dim3(kThreads), 0, st, a);         \
+    } while (0)
+#define DQ_STEP(CN_)                    \
+    do {                                \
+        if (ctx->vec) DQ_STEP_(CN_, true);  \
+        else DQ_STEP_(CN_, false);          \
     } while (0)
         switch (ctx->CN) {
             case 1: DQ_STEP(1); break;
             case 2: DQ_STEP(2); break;
             case 4: DQ_STEP(4); break;
-            default: DQ_STEP(8); break;
+            default: DQ_STEP(4); break;
         }
 #undef DQ_STEP
+#undef DQ_STEP_
         DQ_LAUNCH_CHECK("LSTM step");
     }
     return DQ_OK;
