@@ -64,14 +64,14 @@ struct StepArgs {
     const float* rbias;   // [dirs][NT * 32] Rb
     const float* pp;      // [dirs][NT * 8][4] peepholes i, o, f, 0
     const int32_t* lens;  // [batch] or NULL
-    const float* hin;     // [dirs][batch][h]
-    float* hout;          // [dirs][batch][h]
+    const float* hin;     // H_{s-1} in the state layout (hpos)
+    float* hout;          // H_s in the state layout
     float* c;             // [dirs][batch][h], updated in place
     float* y;             // [seq][dirs][batch][h] or NULL
     float* yh;            // [dirs][batch][h], written by the last step (or NULL)
     float* yc;
     uint32_t* mm;         // [dirs][3][2][kSlots]
-    int s, seq, batch, h, N, NT, KFP, dirs;
+    int s, seq, batch, h, N, NT, KFP, BT, dirs;
     int rd_slot, wr_slot, clr_slot;
     int rev_mask;         // bit d set: direction d runs in reverse
     int act[6];           // f, g, h of direction 0, then of direction 1
@@ -100,6 +100,16 @@ __device__ float rnn_act(int kind, float xf, float af, float bf) {
             r = x == 0.0 ? 0.69314718055994530942 : x < 0.0 ? log1p(exp(x)) : x + log1p(exp(-x));
     }
     return (float)r;
+}
+
+// Index of H[d][b][u] in the state buffers: per direction and 32-entry batch
+// tile, [fragment kf][quarter j][lane][4] with kf = u / 32, j = (u % 16) / 4
+// and lane = b % 32 + 32 ((u % 32) / 16). Lane l's 16 values of fragment kf
+// (its share of the MFMA operand) are four 16-byte pieces 1 KiB apart, so a
+// wave's load instruction reads 1 KiB of consecutive bytes.
+__host__ __device__ __forceinline__ size_t hpos(int d, int b, int u, int BT, int KFP) {
+    const int lane = (b & 31) + ((u >> 4) & 1) * 32;
+    return ((((size_t)d * BT + (b >> 5)) * KFP + (u >> 5)) * 4 + ((u >> 2) & 3)) * 256 + lane * 4 + (u & 3);
 }
 
 __device__ __forceinline__ float clipv(float v, float c) {
@@ -156,14 +166,14 @@ __device__ __forceinline__ dq::v4i quant16(const float (&x)[16], const HQuant& q
     return out;
 }
 
-template <int CN, bool VEC, bool DEF>
+template <int CN, bool DEF>
 __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
     __shared__ int32_t red[4][16][64];
     __shared__ int32_t rsw[4][32];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nt = blockIdx.x, bt = blockIdx.y, d = blockIdx.z;
     const int h = a.h, batch = a.batch, KFW = a.KFP >> 2, nchunks = KFW / CN;
-    const float* hrows = a.hin + ((size_t)d * batch + (size_t)bt * 32) * h;
+    const float* htile = a.hin + ((size_t)d * a.BT + bt) * a.KFP * 1024 + lane * 4;
 
     // Wave w multiplies k fragments 4 j + w (j < KFW), CN at a time. Lane l
     // holds, as the second MFMA operand, 16 codes of row l % 32 of the tile
@@ -171,27 +181,21 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
     // H_{s-1}, so the codes never leave its registers.
     const dq::v4i* rbase =
         reinterpret_cast<const dq::v4i*>(a.rp + (size_t)(d * a.NT + nt) * a.KFP * 1024) + lane;
-    const int hr_row = lane & 31, hr_k = (lane >> 5) * 16;
-    const bool row_ok = bt * 32 + hr_row < batch;
-    const float* hsrc = hrows + (size_t)(row_ok ? hr_row : 0) * h;
+    const bool row_ok = bt * 32 + (lane & 31) < batch;
+    const int hr_k = (lane >> 5) * 16;
     auto load_chunk = [&](int c, dq::v4i (&rr)[CN], float (&hx)[CN][16], uint32_t (&vm)[CN]) {
 #pragma unroll
         for (int i = 0; i < CN; ++i) {
             const int kf = 4 * (c * CN + i) + w;
             rr[i] = rbase[(size_t)kf * 64];
             const int k0 = kf * 32 + hr_k;
-            const int n = row_ok ? (h - k0 < 0 ? 0 : h - k0 > 16 ? 16 : h - k0) : 0;  // valid values
+            const int n = row_ok ? (h - k0 < 0 ? 0 : h - k0 > 16 ? 16 : h - k0) : 0;  // values inside H
             vm[i] = n == 16 ? 0xffffu : (1u << n) - 1u;
-            if (VEC) {  // h % 16 == 0: a group is whole or absent
-                const dq::f4* src = reinterpret_cast<const dq::f4*>(n ? hsrc + k0 : hrows);
+            const float* src = htile + (size_t)kf * 1024;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const dq::f4 v = src[j];
-                    hx[i][4 * j] = v[0]; hx[i][4 * j + 1] = v[1]; hx[i][4 * j + 2] = v[2]; hx[i][4 * j + 3] = v[3];
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) hx[i][j] = *(j < n ? hsrc + k0 + j : hrows);
+            for (int j = 0; j < 4; ++j) {
+                const dq::f4 v = *reinterpret_cast<const dq::f4*>(src + j * 256);
+                hx[i][4 * j] = v[0]; hx[i][4 * j + 1] = v[1]; hx[i][4 * j + 2] = v[2]; hx[i][4 * j + 3] = v[3];
             }
         }
     };
@@ -213,7 +217,8 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
     const int bc = b < batch ? b : batch - 1, uc = u < h ? u : h - 1;
     const size_t su = ((size_t)d * batch + bc) * h + uc;
     const int lraw = a.lens ? a.lens[bc] : a.seq;
-    const float c0 = a.c[su], hold = a.hin[su];
+    const size_t sh = hpos(d, bc, uc, a.BT, a.KFP);
+    const float c0 = a.c[su], hold = a.hin[sh];
     const size_t pc = (size_t)d * a.NT * 32 + nt * 32 + 4 * ul;
     const dq::v4i cs4 = *reinterpret_cast<const dq::v4i*>(a.rcs + pc);
     const dq::v4i be4 = *reinterpret_cast<const dq::v4i*>(a.rbeta + pc);
@@ -330,7 +335,7 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
             hv = hold;
             if (a.y) a.y[(((size_t)a.s * a.dirs + d) * batch + b) * h + u] = 0.0f;
         }
-        a.hout[su] = hv;
+        a.hout[sh] = hv;
         if (a.yh) a.yh[su] = hv;
         if (a.yc) a.yc[su] = cv;
         lo_n = __builtin_fminf(lo_n, hv);
@@ -355,16 +360,18 @@ __global__ void k_lstm_mm_reset(uint32_t* mm, int n) {
 // The initial state (zeros where not given) into the state buffers, its
 // extremes into slot 0 of its direction; yh / yc (a sequence of length 0)
 // receive it as the final state.
-__global__ void __launch_bounds__(256) k_lstm_begin(const float* h0, const float* c0, int per_dir,
-                                                    float* hs, float* cs, uint32_t* mm, float* yh, float* yc) {
+__global__ void __launch_bounds__(256) k_lstm_begin(const float* h0, const float* c0, int batch, int h, int BT,
+                                                    int KFP, float* hs, float* cs, uint32_t* mm, float* yh,
+                                                    float* yc) {
     const int d = blockIdx.y;
+    const int per_dir = batch * h;
     const int i = blockIdx.x * 256 + threadIdx.x;
     float hv = 0.0f;
     if (i < per_dir) {
         const size_t k = (size_t)d * per_dir + i;
         hv = h0 ? h0[k] : 0.0f;
         const float cv = c0 ? c0[k] : 0.0f;
-        hs[k] = hv;
+        hs[hpos(d, i / h, i % h, BT, KFP)] = hv;
         cs[k] = cv;
         if (yh) yh[k] = hv;
         if (yc) yc[k] = cv;
@@ -513,7 +520,8 @@ struct dq_lstm_ctx {
     int dirs = 1, direction = 0;
     dq_dtype w_type = DQ_I8, r_type = DQ_I8;
     int NT = 0, KFP = 0, CN = 1;
-    bool vec = false, has_w = false;
+    bool has_w = false;
+    int BT = 0;
     bool def_act = true;  // Sigmoid, Tanh, Tanh in every direction
     int act[6] = {0, 1, 1, 0, 1, 1};
     float alpha[6] = {}, beta[6] = {};
@@ -531,7 +539,7 @@ struct dq_lstm_ctx {
     float* rsc = nullptr;
     float* rbias = nullptr;
     float* pp = nullptr;
-    float* hs = nullptr;       // [2][dirs][batch][h]
+    float* hs = nullptr;       // two state buffers of dirs * BT * KFP * 1024 (hpos)
     float* cs = nullptr;       // [dirs][batch][h]
     uint32_t* mm = nullptr;    // [dirs][3][2][kSlots]
     std::string info;
@@ -605,18 +613,19 @@ extern "C" int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch
     c->CN = KFW <= 1 ? 1 : KFW <= 2 ? 2 : 4;
     const int KFWp = (KFW + c->CN - 1) / c->CN * c->CN;
     c->KFP = 4 * KFWp;
-    c->vec = h % 16 == 0;
+    c->BT = (int)((batch_size + 31) / 32);
     int rc = DQ_OK;
     (void)hipGetDevice(&c->device);
     const size_t N = (size_t)dirs * 4 * h, cols = (size_t)dirs * c->NT * 32;
     const size_t state = (size_t)dirs * batch_size * h;
+    const size_t hstate = (size_t)dirs * c->BT * c->KFP * 1024;
     bool ok = hipMalloc(&c->wsc, N * 4) == hipSuccess && hipMalloc(&c->wzp, N) == hipSuccess &&
               hipMalloc(&c->wb, N * 4) == hipSuccess &&
               hipMalloc(&c->rp, (size_t)dirs * c->NT * c->KFP * 1024) == hipSuccess &&
               hipMalloc(&c->rcs, cols * 4) == hipSuccess && hipMalloc(&c->rbeta, cols * 4) == hipSuccess &&
               hipMalloc(&c->rsc, cols * 4) == hipSuccess && hipMalloc(&c->rbias, cols * 4) == hipSuccess &&
               hipMalloc(&c->pp, (size_t)dirs * c->NT * 8 * 16) == hipSuccess &&
-              hipMalloc(&c->hs, std::max<size_t>(2 * state, 1) * 4) == hipSuccess &&
+              hipMalloc(&c->hs, std::max<size_t>(2 * hstate, 1) * 4) == hipSuccess &&
               hipMalloc(&c->cs, std::max<size_t>(state, 1) * 4) == hipSuccess &&
               hipMalloc(&c->mm, (size_t)dirs * 3 * 2 * kSlots * 4) == hipSuccess;
     if (ok && M > 0) ok = hipMalloc(&c->xw, (size_t)M * N * 4) == hipSuccess;
@@ -633,9 +642,9 @@ extern "C" int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch
     }
     char buf[320];
     snprintf(buf, sizeof buf,
-             "gfx950 DynamicQuantizeLSTM: input projection = %s; step = one k_lstm_step<%d,%d,%d> launch, "
+             "gfx950 DynamicQuantizeLSTM: input projection = %s; step = one k_lstm_step<%d,%d> launch, "
              "%d x %lld x %d workgroups of 8 units x 32 batch entries, mfma_i32_32x32x32_i8, H quantized in registers",
-             c->qg ? dq_qgemm_info(c->qg) : "none", c->CN, (int)c->vec, (int)c->def_act, c->NT, (long long)((batch_size + 31) / 32),
+             c->qg ? dq_qgemm_info(c->qg) : "none", c->CN, (int)c->def_act, c->NT, (long long)((batch_size + 31) / 32),
              dirs);
     c->info = buf;
     *ctx = c;
@@ -731,11 +740,11 @@ extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* 
     const int nmm = dirs * 3 * 2 * kSlots;
     hipLaunchKernelGGL(k_lstm_mm_reset, dim3((nmm + 255) / 256), dim3(256), 0, st, ctx->mm, nmm);
     DQ_LAUNCH_CHECK("LSTM extremes reset");
-    const size_t state = (size_t)dirs * batch * h;
+    const size_t hstate = (size_t)dirs * ctx->BT * ctx->KFP * 1024;
     const int per_dir = (int)(batch * h);
     hipLaunchKernelGGL(k_lstm_begin, dim3((unsigned)((per_dir + 255) / 256), (unsigned)dirs), dim3(256), 0, st,
-                       initial_h, initial_c, per_dir, ctx->hs, ctx->cs, ctx->mm, seq == 0 ? Y_h : nullptr,
-                       seq == 0 ? Y_c : nullptr);
+                       initial_h, initial_c, (int)batch, (int)h, ctx->BT, ctx->KFP, ctx->hs, ctx->cs, ctx->mm,
+                       seq == 0 ? Y_h : nullptr, seq == 0 ? Y_c : nullptr);
     DQ_LAUNCH_CHECK("LSTM initial state");
     StepArgs a{};
     a.xw = ctx->xw;
@@ -755,6 +764,7 @@ extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* 
     a.N = (int)(dirs * 4 * h);
     a.NT = ctx->NT;
     a.KFP = ctx->KFP;
+    a.BT = ctx->BT;
     a.dirs = dirs;
     a.rev_mask = ctx->direction == DQ_LSTM_REVERSE ? 1 : ctx->direction == DQ_LSTM_BIDIRECTIONAL ? 2 : 0;
     for (int i = 0; i < 6; ++i) {
@@ -770,28 +780,21 @@ extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* 
         a.rd_slot = (int)(s % 3);
         a.wr_slot = (int)((s + 1) % 3);
         a.clr_slot = (int)((s + 2) % 3);
-        a.hin = ctx->hs + (size_t)(s & 1) * state;
-        a.hout = ctx->hs + (size_t)((s + 1) & 1) * state;
+        a.hin = ctx->hs + (size_t)(s & 1) * hstate;
+        a.hout = ctx->hs + (size_t)((s + 1) & 1) * hstate;
         a.yh = s == seq - 1 ? Y_h : nullptr;
         a.yc = s == seq - 1 ? Y_c : nullptr;
-#define DQ_STEP_(CN_, V_)                                                                                  \
-    do {                                                                                                   \
-        if (ctx->def_act) hipLaunchKernelGGL((k_lstm_step<CN_, V_, true>), grid, dim3(kThreads), 0, st, a); \
-        else hipLaunchKernelGGL((k_lstm_step<CN_, V_, false>), grid, dim3(kThreads), 0, st, a);         \
-    } while (0)
-#define DQ_STEP(CN_)                    \
-    do {                                \
-        if (ctx->vec) DQ_STEP_(CN_, true);  \
-        else DQ_STEP_(CN_, false);          \
+#define DQ_STEP(CN_)                                                                                      \
+    do {                                                                                                  \
+        if (ctx->def_act) hipLaunchKernelGGL((k_lstm_step<CN_, true>), grid, dim3(kThreads), 0, st, a);  \
+        else hipLaunchKernelGGL((k_lstm_step<CN_, false>), grid, dim3(kThreads), 0, st, a);              \
     } while (0)
         switch (ctx->CN) {
             case 1: DQ_STEP(1); break;
             case 2: DQ_STEP(2); break;
-            case 4: DQ_STEP(4); break;
             default: DQ_STEP(4); break;
         }
 #undef DQ_STEP
-#undef DQ_STEP_
         DQ_LAUNCH_CHECK("LSTM step");
     }
     return DQ_OK;
