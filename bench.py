@@ -597,7 +597,7 @@ def main():
                     help="no GPU: write profiles/traffic.json from rocprofv3 --pmc outputs")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, kernel_match="k_gemm<2, 2, 4, 4, 2, 1, 1, true>")
+        write_traffic(*args.write_traffic, kernel_match="k_gemm<2, 2, 4, 4, 2, 1, 1, true, false>")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path, so --gpus "
