@@ -51,6 +51,7 @@ constexpr int kPatchMax = 112 * 1024;  // with the 20 KiB output stage, within 1
 constexpr int kKMax = 32768;    // real taps per output: int32 sums stay exact
 constexpr int kTapGroup = 9;    // taps whose weight fragments a lane holds at once
 constexpr int kTapMax = 1024;   // padded taps per kernel (a per-workgroup table of their offsets)
+constexpr int kSplitBelow = 256;  // split the reduction when fewer workgroups than this would run
 
 typedef dq::v4i v4i;
 
@@ -82,12 +83,74 @@ struct ConvArgs {
     uint32_t xflip;       // 0x80808080 for a uint8 x
     int kA, kB, x_u8, y_u8, vecx, vecy;
     int y_lo, y_hi;       // y's saturation range
+    // split reduction: blockIdx.z = image * nsplit + split, each split walks
+    // cps chunks and leaves int32 partial sums for k_qconv_reduce
+    int nsplit, cps;
+    int32_t* part;        // [N * nsplit][M][P]: sum w^ x^ over the split's chunks
+    int32_t* spart;       // [N * nsplit][G][P]: sum x^ over them (XSUM)
+};
+
+// The requantization shared by the epilogue and the split reduction:
+// y = saturate(rne(((float)acc * x_scale) * w_scale / y_scale) + y_zp), with
+// the corrected quotient where the scale allows it (as the quantizers
+// round), the 1.5 * 2^23 rounding add, a median clamp against the saturation
+// bounds minus the zero point, and the zero point added to four packed
+// codes at once (carry-free bytewise add).
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kBig = 4194304.0f;     // 2^22
+
+struct YQuant {
+    float x_scale, lof, hif;
+    dq::QDiv yd;
+    int y_zp, y_lo, y_hi;
+    uint32_t Yz;
 };
 
 __device__ __forceinline__ int zp8(const void* zp, bool u8) {
     if (!zp) return 0;
     return u8 ? (int)*(const uint8_t*)zp : (int)*(const int8_t*)zp;
 }
+
+__device__ __forceinline__ YQuant make_yquant(const ConvArgs& a) {
+    YQuant q;
+    q.x_scale = *a.x_scale;
+    q.yd = dq::make_qdiv(*a.y_scale);
+    q.y_zp = zp8(a.y_zp, a.y_u8);
+    q.y_lo = a.y_lo;
+    q.y_hi = a.y_hi;
+    q.lof = kMagic + (float)(a.y_lo - q.y_zp);
+    q.hif = kMagic + (float)(a.y_hi - q.y_zp);
+    q.Yz = (uint32_t)(q.y_zp & 0xff) * 0x01010101u;
+    return q;
+}
+
+// four exact sums of one output channel (scale wsc) to four packed codes
+__device__ __forceinline__ uint32_t requant4(const uint32_t (&v)[4], float wsc, const YQuant& q) {
+    if (q.yd.fast) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float real = (float)(int32_t)v[e] * q.x_scale;
+            real = real * wsc;
+            const float q0 = __builtin_amdgcn_fmed3f(real * q.yd.y, -kBig, kBig);
+            const float rr = __builtin_fmaf(-q0, q.yd.s, real);
+            const float tt = __builtin_fmaf(rr, q.yd.y, q0) + kMagic;
+            b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(tt, q.lof, q.hif));
+        }
+        const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+        return ((packed & 0x7f7f7f7fu) + (q.Yz & 0x7f7f7f7fu)) ^ ((packed ^ q.Yz) & 0x80808080u);
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float real = (float)(int32_t)v[e] * q.x_scale;
+        real = real * wsc;
+        const int code = dq::sat_add(dq::rne(real / q.yd.s), q.y_zp, q.y_lo, q.y_hi);
+        word |= ((uint32_t)code & 0xffu) << (8 * e);
+    }
+    return word;
+}
+
 
 // Byte i of each of d0..d3, as one word (d0 in the low byte).
 __device__ __forceinline__ uint32_t gather_byte(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, int i) {
@@ -96,7 +159,7 @@ __device__ __forceinline__ uint32_t gather_byte(uint32_t d0, uint32_t d1, uint32
            (((d3 >> s) & 0xffu) << 24);
 }
 
-template <bool XSUM, int WM, int IB>
+template <bool XSUM, int WM, int IB, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t patch[];
     __shared__ __attribute__((aligned(16))) uint8_t ys[4 * 64 * kYPitch];
@@ -106,7 +169,9 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wp = wave / WM;
-    const int n = blockIdx.z;
+    const int n = SPLIT ? (int)blockIdx.z / a.nsplit : (int)blockIdx.z;
+    const int c_beg = SPLIT ? ((int)blockIdx.z - n * a.nsplit) * a.cps * kKC : 0;
+    const int c_end = SPLIT ? std::min(c_beg + a.cps * kKC, sh.Kc) : sh.Kc;
     const int g = blockIdx.y / sh.mtiles, mt = blockIdx.y - g * sh.mtiles;
     const int m0 = mt * MT + 64 * wm;  // this wave's first channel within the group
     const int p0 = blockIdx.x * PT, pw0 = p0 + 32 * IB * wp;
@@ -258,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         }
     };
 
-    for (int c0 = 0; c0 < sh.Kc; c0 += kKC) {
+    for (int c0 = c_beg; c0 < c_end; c0 += kKC) {
         // the previous chunk's operand reads are done (a bare barrier: no
         // wait for global memory)
         dq::wait_lgkm0();
@@ -282,16 +347,50 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- requantizing epilogue: lane holds channel (lane % 32) of block jb
-    // and, in accumulators 4q .. 4q+3, pixels 8q + 4 (lane / 32) + 0..3 of
-    // pixel block ib
-    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-    constexpr float kBig = 4194304.0f;     // 2^22
-    const float x_scale = *a.x_scale;
-    const dq::QDiv yd = dq::make_qdiv(*a.y_scale);
-    const int y_zp = zp8(a.y_zp, a.y_u8);
-    const float lof = kMagic + (float)(a.y_lo - y_zp), hif = kMagic + (float)(a.y_hi - y_zp);
-    const uint32_t Yz = (uint32_t)(y_zp & 0xff) * 0x01010101u;
+    // lane holds channel (lane % 32) of block jb and, in accumulators
+    // 4q .. 4q+3, pixels 8q + 4 (lane / 32) + 0..3 of pixel block ib
+    if (SPLIT) {
+        // the split's raw sums (four consecutive pixels a lane and group),
+        // and its pixel sums from one wave per pixel range
+        const bool vec4 = sh.P % 4 == 0;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int ml = m0 + 32 * jb + (lane & 31);
+            if (ml >= sh.Mg) continue;
+            int32_t* dst = a.part + ((size_t)blockIdx.z * sh.M + (size_t)g * sh.Mg + ml) * sh.P;
+#pragma unroll
+            for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int p = pw0 + 32 * ib + 8 * q + 4 * (lane >> 5);
+                    const v4i v = {acc[ib][jb][4 * q], acc[ib][jb][4 * q + 1], acc[ib][jb][4 * q + 2],
+                                   acc[ib][jb][4 * q + 3]};
+                    if (vec4 && p + 4 <= sh.P) {
+                        *reinterpret_cast<v4i*>(dst + p) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (p + e < sh.P) dst[p + e] = v[e];
+                    }
+                }
+        }
+        if (XSUM && wm == 0 && (lane & 31) == 0) {
+            int32_t* dst = a.spart + ((size_t)blockIdx.z * sh.G + g) * sh.P;
+#pragma unroll
+            for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int p = pw0 + 32 * ib + 8 * q + 4 * (lane >> 5) + e;
+                        if (p < sh.P) dst[p] = sacc[ib][4 * q + e];
+                    }
+        }
+        return;
+    }
+
+    // ---- requantizing epilogue
+    const YQuant yq = make_yquant(a);
     uint8_t* ysw = ys + 64 * wave * kYPitch;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
@@ -308,34 +407,13 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         for (int ib = 0; ib < IB; ++ib) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                uint32_t word;
-                if (yd.fast) {
-                    uint32_t b[4];
+                uint32_t v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint32_t v = (uint32_t)acc[ib][jb][4 * q + e] + rowc;
-                        if (XSUM) v += (uint32_t)coef * (uint32_t)sacc[ib][4 * q + e];
-                        float real = (float)(int32_t)v * x_scale;
-                        real = real * wsc;
-                        const float q0 = __builtin_amdgcn_fmed3f(real * yd.y, -kBig, kBig);
-                        const float rr = __builtin_fmaf(-q0, yd.s, real);
-                        const float tt = __builtin_fmaf(rr, yd.y, q0) + kMagic;
-                        b[e] = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(tt, lof, hif));
-                    }
-                    const uint32_t packed = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
-                    word = ((packed & 0x7f7f7f7fu) + (Yz & 0x7f7f7f7fu)) ^ ((packed ^ Yz) & 0x80808080u);
-                } else {
-                    word = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint32_t v = (uint32_t)acc[ib][jb][4 * q + e] + rowc;
-                        if (XSUM) v += (uint32_t)coef * (uint32_t)sacc[ib][4 * q + e];
-                        float real = (float)(int32_t)v * x_scale;
-                        real = real * wsc;
-                        const int code = dq::sat_add(dq::rne(real / yd.s), y_zp, a.y_lo, a.y_hi);
-                        word |= ((uint32_t)code & 0xffu) << (8 * e);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = (uint32_t)acc[ib][jb][4 * q + e] + rowc;
+                    if (XSUM) v[e] += (uint32_t)coef * (uint32_t)sacc[ib][4 * q + e];
                 }
+                const uint32_t word = requant4(v, wsc, yq);
                 const int pp = 32 * ib + 8 * q + 4 * (lane >> 5);
                 *reinterpret_cast<uint32_t*>(&ysw[(32 * jb + (lane & 31)) * kYPitch + pp]) = word;
             }
@@ -404,6 +482,50 @@ __global__ __launch_bounds__(256) void k_qconv_direct(ConvShape sh, ConvArgs a) 
     a.y[((size_t)n * sh.M + m) * sh.P + p] = (uint8_t)code;
 }
 
+// The split reduction: the partial sums of every split, the zero-point and
+// bias terms of the epilogue, then the same requantization. One thread per
+// four consecutive pixels of (image n, output channel m).
+template <bool XSUM>
+__global__ __launch_bounds__(256) void k_qconv_reduce(ConvShape sh, ConvArgs a) {
+    const int p = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int m = blockIdx.y, n = blockIdx.z;
+    if (p >= sh.P) return;
+    const int g = m / sh.Mg, ml = m - g * sh.Mg;
+    const int x_zp = zp8(a.x_zp, a.x_u8);
+    const int coef = a.kA - a.wz[m];
+    const uint32_t xb = (uint32_t)(a.kB - x_zp);
+    const uint32_t rowc = xb * (uint32_t)a.R[g * sh.Mgp + ml] + (uint32_t)sh.K * ((uint32_t)coef * xb) +
+                          (uint32_t)a.bias[m];
+    const bool whole = sh.P % 4 == 0;  // then p + 3 < P and the rows are 16-byte aligned
+    uint32_t v[4] = {rowc, rowc, rowc, rowc};
+    for (int s = 0; s < a.nsplit; ++s) {
+        const size_t z = (size_t)n * a.nsplit + s;
+        const int32_t* src = a.part + (z * sh.M + m) * sh.P + p;
+        const int32_t* ssrc = a.spart + (z * sh.G + g) * sh.P + p;
+        if (whole) {
+            const v4i t = *reinterpret_cast<const v4i*>(src);
+            v4i st = {0, 0, 0, 0};
+            if (XSUM) st = *reinterpret_cast<const v4i*>(ssrc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += (uint32_t)t[e] + (XSUM ? (uint32_t)coef * (uint32_t)st[e] : 0u);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (p + e < sh.P)
+                    v[e] += (uint32_t)src[e] + (XSUM ? (uint32_t)coef * (uint32_t)ssrc[e] : 0u);
+        }
+    }
+    const uint32_t word = requant4(v, a.ws[m], make_yquant(a));
+    uint8_t* dst = a.y + ((size_t)n * sh.M + m) * sh.P + p;
+    if (whole) {
+        *reinterpret_cast<uint32_t*>(dst) = word;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (p + e < sh.P) dst[e] = (uint8_t)(word >> (8 * e));
+    }
+}
+
 // Packs w [M, Cg, kH, kW] into w^ rows [G * Mgp][Tp][Kc] (zeros past Cg,
 // T and Mg) and R[row] = sum of the row's w^. One workgroup per row.
 __global__ __launch_bounds__(256) void k_conv_pack_w(const uint8_t* __restrict__ w, ConvShape sh, int w_u8,
@@ -469,6 +591,8 @@ struct dq_qconv_ctx {
     float* ws = nullptr;
     int32_t* wz = nullptr;
     int32_t* bias = nullptr;
+    int32_t* part = nullptr;  // split partial sums, grown on demand by forward
+    size_t part_bytes = 0;
     std::string info;
 };
 
@@ -481,22 +605,25 @@ void free_ctx(dq_qconv_ctx* c) {
     (void)hipFree(c->ws);
     (void)hipFree(c->wz);
     (void)hipFree(c->bias);
+    (void)hipFree(c->part);
     delete c;
 }
 
-template <bool XSUM, int WM, int IB>
+template <bool XSUM, int WM, int IB, bool SPLIT>
 int set_lds(int bytes) {
-    if (hipFuncSetAttribute((const void*)k_qconv<XSUM, WM, IB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_qconv<XSUM, WM, IB, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             bytes) != hipSuccess)
         DQ_FAIL(DQ_ERR_HIP, "hipFuncSetAttribute failed for the conv kernel");
     return DQ_OK;
 }
 
-// the LDS budget of the two kernels a context may launch
+// the LDS budget of the four kernels a context may launch
 template <int WM>
 int set_lds2(int bytes) {
-    int rc = set_lds<true, WM, 2>(bytes);
-    return rc ? rc : set_lds<false, WM, 2>(bytes);
+    int rc = set_lds<true, WM, 2, false>(bytes);
+    if (!rc) rc = set_lds<false, WM, 2, false>(bytes);
+    if (!rc) rc = set_lds<true, WM, 2, true>(bytes);
+    return rc ? rc : set_lds<false, WM, 2, true>(bytes);
 }
 
 }  // namespace
@@ -677,9 +804,52 @@ extern "C" int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, con
         return DQ_OK;
     }
     const int PT = 32 * ctx->ib * (4 / ctx->wm);
-    const dim3 grid((unsigned)((s.P + PT - 1) / PT), (unsigned)(s.G * s.mtiles), (unsigned)N);
+    const long long ptiles = (s.P + PT - 1) / PT, gy = (long long)s.G * s.mtiles;
     const size_t lds = (size_t)ctx->patch_bytes;
-#define DQ_CONV(XS, W_) hipLaunchKernelGGL((k_qconv<XS, W_, 2>), grid, dim3(kThreads), lds, st, s, a)
+    // Too few workgroups for the chip (deep layers: few pixels, many
+    // channels): split the chunks of the reduction over workgroups, leave
+    // int32 partial sums and requantize them in k_qconv_reduce.
+    const int chunks = s.Kc / kKC;
+    const long long wgs = ptiles * gy * N;
+    int nsplit = 1;
+    if (wgs < kSplitBelow && chunks >= 2) {
+        nsplit = (int)std::min<long long>(chunks, (kSplitBelow + wgs - 1) / wgs);
+        nsplit = (int)std::min<long long>(nsplit, 65535 / N);
+    }
+    if (nsplit > 1) {
+        a.cps = (chunks + nsplit - 1) / nsplit;
+        a.nsplit = (chunks + a.cps - 1) / a.cps;
+        const size_t need = (size_t)N * a.nsplit * ((size_t)s.M + (ctx->xsum ? s.G : 0)) * s.P * 4;
+        if (need > ctx->part_bytes) {
+            // the old buffer may still be in use by this stream's earlier work
+            DQ_HIP_CHECK(hipStreamSynchronize(st));
+            (void)hipFree(ctx->part);
+            ctx->part = nullptr;
+            ctx->part_bytes = 0;
+            if (hipMalloc(&ctx->part, need) != hipSuccess) DQ_FAIL(DQ_ERR_ALLOC, "device allocation of the split sums failed");
+            ctx->part_bytes = need;
+        }
+        a.part = ctx->part;
+        a.spart = ctx->part + (size_t)N * a.nsplit * s.M * s.P;
+        const dim3 grid((unsigned)ptiles, (unsigned)gy, (unsigned)(N * a.nsplit));
+#define DQ_CONV(XS, W_) hipLaunchKernelGGL((k_qconv<XS, W_, 2, true>), grid, dim3(kThreads), lds, st, s, a)
+        if (ctx->wm == 1) {
+            if (ctx->xsum) DQ_CONV(true, 1);
+            else DQ_CONV(false, 1);
+        } else {
+            if (ctx->xsum) DQ_CONV(true, 2);
+            else DQ_CONV(false, 2);
+        }
+#undef DQ_CONV
+        DQ_LAUNCH_CHECK("qconv split");
+        const dim3 rgrid((unsigned)((s.P + 1023) / 1024), (unsigned)s.M, (unsigned)N);
+        if (ctx->xsum) hipLaunchKernelGGL(k_qconv_reduce<true>, rgrid, dim3(256), 0, st, s, a);
+        else hipLaunchKernelGGL(k_qconv_reduce<false>, rgrid, dim3(256), 0, st, s, a);
+        DQ_LAUNCH_CHECK("qconv split reduction");
+        return DQ_OK;
+    }
+    const dim3 grid((unsigned)ptiles, (unsigned)gy, (unsigned)N);
+#define DQ_CONV(XS, W_) hipLaunchKernelGGL((k_qconv<XS, W_, 2, false>), grid, dim3(kThreads), lds, st, s, a)
     if (ctx->wm == 1) {
         if (ctx->xsum) DQ_CONV(true, 1);
         else DQ_CONV(false, 1);

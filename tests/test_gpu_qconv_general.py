@@ -111,6 +111,9 @@ def test_qconv_matches_oracle(gpu, case, types, per_channel):
     (1, 32, 64, 64, 256, 3, 3, (1, 1), (1, 1, 1, 1), 1),    # two MFMA pixel rows a wave
     (2, 96, 28, 28, 96, 3, 3, (1, 1), (1, 1, 1, 1), 96),     # depthwise (the direct kernel)
     (2, 96, 28, 28, 192, 3, 3, (2, 2), (0, 0, 1, 1), 96),    # depthwise, two outputs a channel, stride 2
+    (20, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1), 1),     # 260 workgroups: two chunks, reduction not split
+    (8, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1, 1, 1), 1),    # deep layer: the reduction split over 8 workgroups
+    (4, 512, 7, 7, 512, 3, 3, (1, 1), (1, 1, 1, 1), 1),      # deepest ResNet stage, 16 chunks in 8 splits
 ])
 def test_qconv_network_layers(gpu, shape):
     N, C, H, W, M, kH, kW, st, pads, group = shape
@@ -123,6 +126,29 @@ def test_qconv_network_layers(gpu, shape):
     want = oracle.qlinear_conv2d(x, 0.02, 128, w, ws, np.zeros(M, np.int32), 0.1, 128, bias=bias,
                                  strides=st, pads=pads, group=group, y_type="u8")
     outs, info = _run(gpu, x, 0.02, 128, w, ws, None, 0.1, 128, "u8", bias=bias, strides=st, pads=pads,
+                      group=group, repeat=2)
+    for got in outs:
+        assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ ({info})"
+
+
+@pytest.mark.parametrize("shape", [
+    (3, 96, 14, 14, 160, 3, 3, (1, 1), (1, 1, 1, 1), 1),     # split, three chunks, per-channel w zero points
+    (2, 70, 9, 13, 33, 3, 2, (2, 1), (0, 1, 2, 0), 1),       # split with ragged pixels and channels
+])
+def test_qconv_split_reduction_with_pixel_sums(gpu, shape):
+    """The split path with w zero points that differ from w's shift, so the
+    per-pixel sums of x travel through the partial buffer too."""
+    N, C, H, W, M, kH, kW, st, pads, group = shape
+    r = np.random.default_rng(_seed("split", shape))
+    x = _codes(r, (N, C, H, W), "u8")
+    w = _codes(r, (M, C // group, kH, kW), "i8")
+    ws = r.uniform(0.0005, 0.002, M).astype(np.float32)
+    wz = r.integers(-128, 128, M)
+    bias = r.integers(-5000, 5000, M).astype(np.int32)
+    log(f"qconv split {shape}")
+    want = oracle.qlinear_conv2d(x, 0.02, 117, w, ws, wz, 0.1, 128, bias=bias, strides=st, pads=pads,
+                                 group=group, y_type="u8")
+    outs, info = _run(gpu, x, 0.02, 117, w, ws, wz, 0.1, 128, "u8", bias=bias, strides=st, pads=pads,
                       group=group, repeat=2)
     for got in outs:
         assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ ({info})"
