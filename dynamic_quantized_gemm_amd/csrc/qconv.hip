@@ -68,9 +68,19 @@ struct ConvShape {
     dq::FastDiv ow_div;
 };
 
+// Byte offset of w^[row][tap t][channel c] in the packed weights: 1 KiB
+// MFMA fragments of 32 rows x 32 channels, fragment ((row / 32) Tp + t)
+// (Kc / 32) + c / 32, and inside it lane slot (row % 32) + 32 ((c % 32) / 16)
+// holds channels 16 ((c % 32) / 16) .. + 15 of the row: a wave's operand
+// load of one fragment reads 1 KiB of consecutive bytes.
+__host__ __device__ __forceinline__ size_t wpos(int row, int t, int c, int Tp, int Kc) {
+    const size_t frag = ((size_t)(row >> 5) * Tp + t) * (Kc >> 5) + (c >> 5);
+    return (frag << 10) + ((size_t)((row & 31) + ((c & 16) << 1)) << 4) + (c & 15);
+}
+
 struct ConvArgs {
     const uint8_t* x;
-    const int8_t* wp;     // packed w^: [G * Mgp][Tp][Kc]
+    const int8_t* wp;     // packed w^ (wpos), [G * Mgp] rows of [Tp][Kc]
     const int32_t* R;     // [G * Mgp]
     const float* ws;      // [M]
     const int32_t* wz;    // [M]
@@ -208,13 +218,12 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
             sacc[i][r] = 0;
         }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-    // weights: a uniform base (this wave's first channel row) plus a fixed
-    // 32-bit lane offset, so a fragment load needs no per-lane address math
-    const int8_t* wbase = a.wp + (size_t)(g * sh.Mgp + m0) * sh.Tp * sh.Kc;
-    uint32_t wlane[2];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-        wlane[jb] = (uint32_t)((32 * jb + (lane & 31)) * sh.Tp * sh.Kc + 16 * (lane >> 5));
+    // weights: this wave's fragments for tap t and chunk c0 start at
+    // wbase + (t (Kc / 32) + c0 / 32) KiB (+ Tp (Kc / 32) KiB for the second
+    // 32-channel block); each lane reads its 16 bytes at 16 lane
+    const int kc32 = sh.Kc >> 5;
+    const int8_t* wbase = a.wp + wpos(g * sh.Mgp + m0, 0, 0, sh.Tp, sh.Kc) + 16 * lane;
+    const size_t wjb = (size_t)sh.Tp * kc32 << 10;
     // the tap offsets, once per workgroup (made visible by the first
     // chunk's barrier)
     for (int t = tid; t < sh.Tp; t += kThreads) {
@@ -227,10 +236,12 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     // thread takes up to 4 units at a time and issues all their loads (from
     // clamped addresses) before any value is used. With W % 4 == 0 (vecx) a
     // column quad lies wholly inside or wholly outside the image, since the
-    // patch's first column sits at iw = -cpad, a multiple of 4; otherwise
-    // the bytes are loaded one by one.
+    // patch's first column sits at iw = -cpad, a multiple of 4; otherwise a
+    // quad inside a row is one unaligned 4-byte load and only the quads that
+    // straddle the row's ends are loaded byte by byte.
     struct Stage {
-        uint32_t raw[4][4][4];  // [unit][channel][byte or word]
+        uint32_t word[4][4];    // [unit][channel]: the quad's bytes (those inside the image)
+        uint32_t in4[4][4];     // which of the 4 bytes lie inside the image
         bool inb[4][4];
         int urc[4];
     };
@@ -252,73 +263,79 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
                 st.inb[k][j] = cin;
                 if (a.vecx) {
                     const bool win = hin && iw0 >= 0 && iw0 < sh.W;
-                    st.raw[k][j][0] = *reinterpret_cast<const uint32_t*>(row + (win ? iw0 : 0));
-                    st.raw[k][j][1] = win;
+                    st.word[k][j] = *reinterpret_cast<const uint32_t*>(row + (win ? iw0 : 0));
+                    st.in4[k][j] = win ? 0xfu : 0u;
+                } else if (hin && iw0 >= 0 && iw0 + 4 <= sh.W) {
+                    // a quad inside the row: one (possibly unaligned) 4-byte load
+                    uint32_t v;
+                    __builtin_memcpy(&v, row + iw0, 4);
+                    st.word[k][j] = v;
+                    st.in4[k][j] = 0xfu;
                 } else {
+                    uint32_t v = 0, m = 0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int iw = iw0 + e;
-                        const bool win = hin && iw >= 0 && iw < sh.W;
-                        st.raw[k][j][e] = win ? 0x100u | row[win ? iw : 0] : 0u;
+                        if (hin && iw >= 0 && iw < sh.W) {
+                            v |= (uint32_t)row[iw] << (8 * e);
+                            m |= 1u << e;
+                        }
                     }
+                    st.word[k][j] = v;
+                    st.in4[k][j] = m;
                 }
             }
         }
         dq::issue_fence();
     };
     auto stage_store = [&](const Stage& st, uint8_t* buf, int ub) {
+        const uint32_t zq = (uint32_t)(x_zp & 0xff) * 0x01010101u;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (ub + k * kThreads >= units) break;
-            uint32_t d[4];
+            if (ub + k * kThreads < units) {
+                uint32_t d[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t v;
-                if (a.vecx) {
-                    v = st.raw[k][j][1] ? st.raw[k][j][0] : (uint32_t)(x_zp & 0xff) * 0x01010101u;
-                } else {
-                    v = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v |= ((st.raw[k][j][e] & 0x100u) ? (st.raw[k][j][e] & 0xffu) : (uint32_t)(x_zp & 0xff))
-                             << (8 * e);
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t m = st.in4[k][j];
+                    const uint32_t bm = (m & 1u ? 0xffu : 0u) | (m & 2u ? 0xff00u : 0u) | (m & 4u ? 0xff0000u : 0u) |
+                                        (m & 8u ? 0xff000000u : 0u);
+                    const uint32_t v = (st.word[k][j] & bm) | (zq & ~bm);  // outside the image: x_zp
+                    d[j] = st.inb[k][j] ? v ^ a.xflip : 0u;                  // a padded channel: x^ = 0
                 }
-                d[j] = st.inb[k][j] ? v ^ a.xflip : 0u;  // a padded channel: x^ = 0
-            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint32_t*>(&buf[st.urc[k] + i * kKC]) = gather_byte(d[0], d[1], d[2], d[3], i);
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<uint32_t*>(&buf[st.urc[k] + i * kKC]) = gather_byte(d[0], d[1], d[2], d[3], i);
+            }
         }
     };
     // The taps of a staged chunk: a tap group's weight fragments are all
     // requested before its first MFMA; every MFMA runs (a padded tap has zero
     // weights, reads the patch at tap (0, 0) and adds zeros to the pixel sums).
     const v4i zeros = {0, 0, 0, 0};
-    auto mfma_chunk = [&](const uint8_t* buf, int c0) {
-        for (int tg = 0; tg < sh.Tp; tg += kTapGroup) {
-            v4i wf[kTapGroup][2];
-            const int8_t* wg = wbase + (size_t)tg * sh.Kc + c0;
+    auto load_w = [&](v4i (&wf)[kTapGroup][2], int tg, int c0) {
+        const int8_t* wg = wbase + (((size_t)tg * kc32 + (c0 >> 5)) << 10);
 #pragma unroll
-            for (int i = 0; i < kTapGroup; ++i) {
+        for (int i = 0; i < kTapGroup; ++i) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+                wf[i][jb] = *reinterpret_cast<const v4i*>(wg + (((size_t)i * kc32) << 10) + jb * wjb);
+        }
+    };
+    auto mfma_group = [&](const v4i (&wf)[kTapGroup][2], const uint8_t* buf, int tg) {
+#pragma unroll
+        for (int i = 0; i < kTapGroup; ++i) {
+            const int t = tg + i;
+            const int off = tapoff[t];
+            const v4i ones_t = t < sh.T ? ones : zeros;
+            v4i xf[IB];
+#pragma unroll
+            for (int ib = 0; ib < IB; ++ib) xf[ib] = *reinterpret_cast<const v4i*>(&buf[pix[ib] + off]);
+#pragma unroll
+            for (int ib = 0; ib < IB; ++ib) {
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb)
-                    wf[i][jb] = *reinterpret_cast<const v4i*>(wg + (size_t)i * sh.Kc + wlane[jb]);
-            }
-#pragma unroll
-            for (int i = 0; i < kTapGroup; ++i) {
-                const int t = tg + i;
-                const int off = tapoff[t];
-                const v4i ones_t = t < sh.T ? ones : zeros;
-                v4i xf[IB];
-#pragma unroll
-                for (int ib = 0; ib < IB; ++ib) xf[ib] = *reinterpret_cast<const v4i*>(&buf[pix[ib] + off]);
-#pragma unroll
-                for (int ib = 0; ib < IB; ++ib) {
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb)
-                        acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[ib], wf[i][jb], acc[ib][jb], 0, 0, 0);
-                    if (XSUM) sacc[ib] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[ib], ones_t, sacc[ib], 0, 0, 0);
-                }
+                    acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[ib], wf[i][jb], acc[ib][jb], 0, 0, 0);
+                if (XSUM) sacc[ib] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[ib], ones_t, sacc[ib], 0, 0, 0);
             }
         }
     };
@@ -335,7 +352,12 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         }
         dq::wait_lgkm0();
         dq::lds_barrier();
-        mfma_chunk(patch, c0);
+        // a tap group's weight fragments are all requested before its first MFMA
+        for (int tg = 0; tg < sh.Tp; tg += kTapGroup) {
+            v4i wf[kTapGroup][2];
+            load_w(wf, tg, c0);
+            mfma_group(wf, patch, tg);
+        }
     }
 
     // The accumulators are read right below. The compiler inserts the wait
@@ -455,7 +477,9 @@ __global__ __launch_bounds__(256) void k_qconv_direct(ConvShape sh, ConvArgs a) 
     const int oh = (int)dq::fdiv((uint32_t)pc, sh.ow_div), ow = pc - oh * sh.OW;
     const int x_zp = zp8(a.x_zp, a.x_u8);
     const int coef = a.kA - a.wz[m];
-    const int8_t* wr = a.wp + (size_t)(g * sh.Mgp + ml) * sh.Tp * sh.Kc;
+    // channels c < 4 of a row lie in one lane slot: tap t is kc32 KiB further
+    const int8_t* wr = a.wp + wpos(g * sh.Mgp + ml, 0, 0, sh.Tp, sh.Kc);
+    const size_t tstride = (size_t)(sh.Kc >> 5) << 10;
     const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
     int32_t acc = 0;
     for (int c = 0; c < sh.Cg; ++c) {
@@ -466,7 +490,7 @@ __global__ __launch_bounds__(256) void k_qconv_direct(ConvShape sh, ConvArgs a) 
             const uint8_t* xr = xc + (size_t)ih * sh.W;
             for (int kw = 0; kw < sh.KW; ++kw) {
                 const int iw = ow * sh.sw - sh.pl + kw * sh.dw;
-                const int wv = (int)wr[(kh * sh.KW + kw) * sh.Kc + c] + coef;
+                const int wv = (int)wr[(size_t)(kh * sh.KW + kw) * tstride + c] + coef;
                 const int xv = (iw >= 0 && iw < sh.W)
                                    ? (a.x_u8 ? (int)xr[iw] : (int)(int8_t)xr[iw]) - x_zp
                                    : 0;
@@ -544,7 +568,7 @@ __global__ __launch_bounds__(256) void k_conv_pack_w(const uint8_t* __restrict__
             const uint32_t b = w[((size_t)m * sh.Cg + c) * sh.T + t];
             v = w_u8 ? (int)b - 128 : (int)(int8_t)b;
         }
-        wp[(size_t)row * len + i] = (int8_t)v;
+        wp[wpos(row, t, c, sh.Tp, sh.Kc)] = (int8_t)v;
         s += v;
     }
     part[threadIdx.x] = s;
