@@ -343,8 +343,13 @@ void dq_qgemm_release(dq_qgemm_ctx* ctx);
  * dq_qconv_forward: x (N images), x_scale / y_scale (one fp32 each on the
  * device), x_zero_point / y_zero_point (one value of x's / y's type on the
  * device, NULL = 0), y (N x M x oH x oW). Asynchronous on `stream`; N = 0
- * is a no-op. Errors: DQ_ERR_STATE (no weights, other device), DQ_ERR_ARG,
- * DQ_ERR_RANGE (N > 65535), DQ_ERR_HIP.
+ * is a no-op. When the tiles of the N images would leave the chip
+ * under-filled (deep layers), the reduction is split over workgroups with
+ * int32 partial sums in a context buffer of N x splits x (M + group) x
+ * oH x oW int32; a call that needs a larger buffer than the context holds
+ * synchronizes `stream`, frees the old one and allocates it (calls on one
+ * context must not overlap). Errors: DQ_ERR_STATE (no weights, other
+ * device), DQ_ERR_ARG, DQ_ERR_RANGE (N > 65535), DQ_ERR_ALLOC, DQ_ERR_HIP.
  * ---------------------------------------------------------------------- */
 typedef struct dq_qconv_ctx dq_qconv_ctx;
 
