@@ -51,7 +51,12 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef DQ_LSTM_WAVES
+#define DQ_LSTM_WAVES 8
+#endif
+constexpr int kWaves = DQ_LSTM_WAVES;  // waves of a step workgroup: they split K, waves 0..3 update the cells
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxCN = kWaves >= 8 ? 2 : 4;  // fragments a wave holds at once (two waves a SIMD: 256 registers)
 constexpr int kSlots = 64;      // extremes slots per step (workgroup b adds to slot b % 64)
 constexpr uint32_t kPlusZero = 0x80000000u;  // dq::f2ord(+0.0f)
 
@@ -168,14 +173,14 @@ __device__ __forceinline__ dq::v4i quant16(const float (&x)[16], const HQuant& q
 
 template <int CN, bool DEF>
 __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
-    __shared__ int32_t red[4][16][64];
-    __shared__ int32_t rsw[4][32];
+    __shared__ int32_t red[kWaves][16][64];
+    __shared__ int32_t rsw[kWaves][32];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nt = blockIdx.x, bt = blockIdx.y, d = blockIdx.z;
-    const int h = a.h, batch = a.batch, KFW = a.KFP >> 2, nchunks = KFW / CN;
+    const int h = a.h, batch = a.batch, KFW = a.KFP / kWaves, nchunks = KFW / CN;
     const float* htile = a.hin + ((size_t)d * a.BT + bt) * a.KFP * 1024 + lane * 4;
 
-    // Wave w multiplies k fragments 4 j + w (j < KFW), CN at a time. Lane l
+    // Wave w multiplies k fragments kWaves j + w (j < KFW), CN at a time. Lane l
     // holds, as the second MFMA operand, 16 codes of row l % 32 of the tile
     // at k = 32 kf + 16 (l / 32): it quantizes exactly those 16 values of
     // H_{s-1}, so the codes never leave its registers.
@@ -186,7 +191,7 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
     auto load_chunk = [&](int c, dq::v4i (&rr)[CN], float (&hx)[CN][16], uint32_t (&vm)[CN]) {
 #pragma unroll
         for (int i = 0; i < CN; ++i) {
-            const int kf = 4 * (c * CN + i) + w;
+            const int kf = kWaves * (c * CN + i) + w;
             rr[i] = rbase[(size_t)kf * 64];
             const int k0 = kf * 32 + hr_k;
             const int n = row_ok ? (h - k0 < 0 ? 0 : h - k0 > 16 ? 16 : h - k0) : 0;  // values inside H
@@ -211,9 +216,11 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
     load_chunk(0, rf, hx, vm);
     const uint32_t* mmr = a.mm + ((size_t)d * 3 + a.rd_slot) * 2 * kSlots;
     const uint32_t mlo = mmr[lane], mhi = mmr[kSlots + lane];
-    const int half = lane >> 5, bl = lane & 31;
-    const int b = bt * 32 + bl, ul = 2 * w + half, u = nt * 8 + ul;
-    const bool cell = b < batch && u < h;
+    // (waves 4 and up take the mapping of wave w % 4 for their clamped
+    // loads but own no cell)
+    const int half = lane >> 5, bl = lane & 31, wc = w & 3;
+    const int b = bt * 32 + bl, ul = 2 * wc + half, u = nt * 8 + ul;
+    const bool cell = w < 4 && b < batch && u < h;
     const int bc = b < batch ? b : batch - 1, uc = u < h ? u : h - 1;
     const size_t su = ((size_t)d * batch + bc) * h + uc;
     const int lraw = a.lens ? a.lens[bc] : a.seq;
@@ -294,14 +301,16 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
         float hv, cv = c0;
         if (live) {
             const uint32_t al = (uint32_t)(128 - zp);
-            const uint32_t rsum = (uint32_t)rsw[0][bl] + (uint32_t)rsw[1][bl] + (uint32_t)rsw[2][bl] +
-                                  (uint32_t)rsw[3][bl];
+            uint32_t rsum = 0;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) rsum += (uint32_t)rsw[v][bl];
             float pre[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 4 * w + e;
-                uint32_t sum = (uint32_t)red[0][row][lane] + (uint32_t)red[1][row][lane] +
-                               (uint32_t)red[2][row][lane] + (uint32_t)red[3][row][lane];
+                const int row = 4 * wc + e;
+                uint32_t sum = 0;
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) sum += (uint32_t)red[v][row][lane];
                 const uint32_t be = (uint32_t)be4[e];
                 sum += be * rsum + al * (uint32_t)cs4[e] + (uint32_t)h * al * be;
                 const float hr = ((float)(int32_t)sum * sc) * rs4[e] + rb4[e];
@@ -341,6 +350,7 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
         lo_n = __builtin_fminf(lo_n, hv);
         hi_n = __builtin_fmaxf(hi_n, hv);
     }
+    if (w >= 4) return;
     lo_n = dq::wave_min_uniform(lo_n);
     hi_n = dq::wave_max_uniform(hi_n);
     if (lane == 0) {
@@ -609,10 +619,10 @@ extern "C" int dq_lstm_init(dq_lstm_ctx** ctx, int64_t seq_length, int64_t batch
     c->input_forget = input_forget ? 1 : 0;
     const int h = (int)hidden_size;
     c->NT = (h + 7) / 8;
-    const int KF = (h + 31) / 32, KFW = (KF + 3) / 4;
-    c->CN = KFW <= 1 ? 1 : KFW <= 2 ? 2 : 4;
+    const int KF = (h + 31) / 32, KFW = (KF + kWaves - 1) / kWaves;
+    c->CN = KFW <= 1 ? 1 : KFW <= 2 ? 2 : kMaxCN;
     const int KFWp = (KFW + c->CN - 1) / c->CN * c->CN;
-    c->KFP = 4 * KFWp;
+    c->KFP = kWaves * KFWp;
     c->BT = (int)((batch_size + 31) / 32);
     int rc = DQ_OK;
     (void)hipGetDevice(&c->device);
@@ -792,7 +802,7 @@ extern "C" int dq_lstm_forward(dq_lstm_ctx* ctx, const float* X, const int32_t* 
         switch (ctx->CN) {
             case 1: DQ_STEP(1); break;
             case 2: DQ_STEP(2); break;
-            default: DQ_STEP(4); break;
+            default: DQ_STEP(kMaxCN); break;
         }
 #undef DQ_STEP
         DQ_LAUNCH_CHECK("LSTM step");
