@@ -85,6 +85,29 @@ struct StepArgs {
     int input_forget;
 };
 
+// tanh in fp64 for a result that is rounded to fp32: for |x| >= 1/8,
+// 1 - 2 / (e^{2|x|} + 1) (the subtraction loses at most 3 of fp64's 53
+// bits); below, the Taylor series x + x^3 sum_k c_k x^{2k} through x^15
+// (c_k = 2^{2n} (2^{2n} - 1) B_{2n} / (2n)!: -1/3, 2/15, -17/315, 62/2835,
+// -1382/155925, 21844/6081075, -929569/638512875; the first omitted term is
+// below 2^-55 of the result for |x| < 1/8). Both are far inside the half
+// fp32 ulp that decides the rounding; the library's tanh carries extra-
+// precision arithmetic (about 150 fp64 instructions) that this does not need.
+__device__ __forceinline__ double tanh_d(double x) {
+    const double ax = fabs(x);
+    const double big = 1.0 - 2.0 / (exp(2.0 * ax) + 1.0);
+    const double x2 = ax * ax;
+    double p = -0.0014558343870513183;
+    p = fma(p, x2, 0.003592128036572481);
+    p = fma(p, x2, -0.008863235529902197);
+    p = fma(p, x2, 0.021869488536155203);
+    p = fma(p, x2, -0.05396825396825397);
+    p = fma(p, x2, 0.13333333333333333);
+    p = fma(p, x2, -0.3333333333333333);
+    const double small = fma(ax * x2, p, ax);
+    return copysign(ax < 0.125 ? small : big, x);
+}
+
 // One ONNX RNN activation, evaluated in fp64 from the fp32 argument and
 // rounded to fp32 once.
 __device__ float rnn_act(int kind, float xf, float af, float bf) {
@@ -92,12 +115,12 @@ __device__ float rnn_act(int kind, float xf, float af, float bf) {
     double r;
     switch (kind) {
         case DQ_RNN_SIGMOID: r = 1.0 / (1.0 + exp(-x)); break;
-        case DQ_RNN_TANH: r = tanh(x); break;
+        case DQ_RNN_TANH: r = tanh_d(x); break;
         case DQ_RNN_RELU: r = x > 0.0 ? x : 0.0; break;
         case DQ_RNN_AFFINE: r = a * x + b; break;
         case DQ_RNN_LEAKY_RELU: r = x < 0.0 ? a * x : x; break;
         case DQ_RNN_THRESHOLDED_RELU: r = x > a ? x : 0.0; break;
-        case DQ_RNN_SCALED_TANH: r = a * tanh(b * x); break;
+        case DQ_RNN_SCALED_TANH: r = a * tanh_d(b * x); break;
         case DQ_RNN_HARD_SIGMOID: r = fmin(fmax(a * x + b, 0.0), 1.0); break;
         case DQ_RNN_ELU: r = x >= 0.0 ? x : a * expm1(x); break;
         case DQ_RNN_SOFTSIGN: r = x / (1.0 + fabs(x)); break;
@@ -125,7 +148,7 @@ __device__ __forceinline__ float clipv(float v, float c) {
 // that the independent gates of a cell overlap; the same evaluation as
 // rnn_act's.
 __device__ __forceinline__ float sigmoid_r(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
-__device__ __forceinline__ float tanh_r(float x) { return (float)tanh((double)x); }
+__device__ __forceinline__ float tanh_r(float x) { return (float)tanh_d((double)x); }
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer, half to even
 

@@ -3,10 +3,11 @@
 Both sides quantize X and every H_{s-1} per tensor with the same fp32 rule,
 sum integers exactly and round each fp32 operation once in the same order;
 each activation is evaluated in fp64 and rounded once (the library's fp64
-exp / tanh and the host's can differ in the last fp64 bit, which moves an
-fp32 result by one unit in a few of 2^29 cases). So the outputs agree to
-fp32 rounding: |got - want| <= 1e-6 + 1e-5 |want| (the fp32 bar), and in
-practice bit for bit (the test reports how many values differ at all).
+exp and its tanh, accurate to a few fp64 units, differ from the host's in
+the last bits, which can move an fp32 result by one unit only when the exact
+value lies within a few 2^-52 of an fp32 rounding midpoint). So the outputs
+agree to fp32 rounding: |got - want| <= 1e-6 + 1e-5 |want| (the fp32 bar),
+and in practice bit for bit (the test reports how many values differ).
 
 Cases: the gate-projection workload at full size (seq 128, batch 32, input
 and hidden 512), forward / reverse / bidirectional, int8 and uint8 W and R
