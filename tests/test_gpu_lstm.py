@@ -16,8 +16,10 @@ zeros and ragged lengths, batch over one 32-entry tile, hidden sizes that
 are not a multiple of 8 or 16 (ragged unit tiles, the scalar H loader), a
 hidden size whose K runs over several fragment chunks, the largest hidden
 size (4096, 128 KiB of LDS), peepholes, clip, input_forget, every
-non-default activation with alpha / beta, missing optional inputs, an
-empty sequence and an empty batch, and a context run twice.
+non-default activation with alpha / beta, missing optional inputs,
+degenerate sizes (one hidden unit and one input feature, one entry and one
+step, a lone entry of length 0), an empty sequence and an empty batch, and
+a context run twice.
 """
 import zlib
 
@@ -109,6 +111,10 @@ CASES = {
                                        alpha=[0.8, 0.9, 0.05], beta=[1.3, -0.1])),
     "activations_relu_thresholded": (4, 2, 8, 16, {}, dict(activations=["Sigmoid", "Relu", "ThresholdedRelu"],
                                                            alpha=[0.2], clip=3.0)),
+    # degenerate sizes: one unit, one input feature, one batch entry, one step
+    "hidden_1_input_1": (4, 3, 1, 1, dict(direction="bidirectional", peepholes=True), {}),
+    "batch_1_seq_1": (1, 1, 5, 7, dict(w_type="u8", r_type="u8", zero_points=True), {}),
+    "one_entry_length_0": (3, 1, 6, 9, dict(direction="reverse", lens=[0]), {}),
 }
 
 
