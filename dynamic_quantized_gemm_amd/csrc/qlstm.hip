@@ -22,16 +22,17 @@
 //    enters as code - 128. k_lstm_params writes the per-column vectors.
 //  - Each step is one launch of k_lstm_step. Workgroup (nt, bt, d) owns
 //    units 8 nt .. 8 nt + 7 of direction d for batch entries 32 bt ..
-//    32 bt + 31. Its four waves split K: wave w multiplies k fragments
-//    4 j + w, R as the first MFMA operand (so a lane's 16 accumulators are
+//    32 bt + 31. Its eight waves split K: wave w multiplies k fragments
+//    8 j + w, R as the first MFMA operand (so a lane's 16 accumulators are
 //    4 units x 4 gates of one batch entry) and H_{s-1}'s codes as the
 //    second. Lane l's share of that operand is 16 values of one row of
 //    H_{s-1}, which the lane loads and quantizes itself, with the
 //    per-tensor scale from the extremes the previous step left in 64 slots
 //    (atomics on order-preserving integers): the codes never touch LDS.
-//    The four partial tiles are summed through LDS, leaving each thread the
-//    four gates of one cell; the cell update writes C in place, H_s into the
-//    other state buffer, Y, and H_s's extremes for the next step, and the
+//    The eight partial tiles are summed through LDS, leaving each thread of
+//    waves 0..3 the four gates of one cell; the cell update writes C in place, H_s into the
+//    other state buffer (stored in the order the next step's lanes load it,
+//    see hpos), Y, and H_s's extremes for the next step, and the
 //    slot two steps ahead is cleared for the step after. Every load of a
 //    step is issued at its start, at clamped addresses, so the kernel waits
 //    on memory once (then once more for its xw, issued when the cell's time

@@ -485,7 +485,8 @@ int qlinear_concat(int n_inputs, const void* const* xs, const int64_t* shapes, i
  *   Y[t]; at steps s >= L its H and C are held (and still enter H's
  *   quantization) and Y[s] = 0. Lengths outside [0, seq] are clamped.
  *   Y_h / Y_c are the state after the last step; a bidirectional LSTM runs
- *   direction 0 forward and direction 1 in reverse, independently.
+ *   direction 0 forward and direction 1 in reverse, independently. Inputs
+ *   are finite fp32 values (a NaN or infinity is not given a meaning).
  *
  * dq_lstm_init: sizes (seq, batch >= 0; 1 <= input <= DQ_QGEMM_K_MAX;
  * 1 <= hidden <= DQ_LSTM_HIDDEN_MAX), direction (DQ_LSTM_*), W / R types
