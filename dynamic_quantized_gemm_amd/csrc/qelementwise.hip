@@ -1068,12 +1068,15 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
             DQ_FAIL(DQ_ERR_RANGE, "%s: shape beyond the column kernel's grid", name);
         // ReduceSumInteger splits long columns over workgroups when the
         // grid would not fill the chip
-        // ... with at least four steps of eight rows a lane per part, which
-        // bounds the atomics to one per column per 32 * 256 / CW rows
+        // ... with at least one step of sixteen rows a lane per part (a
+        // lane keeps sixteen 16-byte loads in flight), which bounds the
+        // atomics to one per column per 16 * 256 / CW rows; finer parts
+        // measured slower (the atomics), coarser ones left the loads of a
+        // CU too few to cover the memory latency
         uint64_t parts = 1;
         if (mode == 0) {
             const uint64_t blocks = gx * O;
-            const uint64_t rows_min = 32 * (256 / CW);
+            const uint64_t rows_min = 16 * (256 / CW);
             while (blocks * parts < 2048 && count / (parts * 2) >= rows_min && parts < 65535) parts *= 2;
         }
         const uint64_t rpp = (count + parts - 1) / parts;
@@ -1084,7 +1087,7 @@ int run_reduce(int mode, const void* x, dq_dtype type, int ndim, const int64_t* 
         }
         const dim3 grid((unsigned)(gx * O), 1, (unsigned)parts);
 #define DQ_COLS(U, M, EE, AT) \
-    hipLaunchKernelGGL((k_reduce_cols<U, M, EE, AT, (AT ? 8 : 4)>), grid, dim3(256), 0, s, a, (uint32_t)I, \
+    hipLaunchKernelGGL((k_reduce_cols<U, M, EE, AT, (AT ? 16 : 4)>), grid, dim3(256), 0, s, a, (uint32_t)I, \
                        CW, (uint32_t)gx, (uint32_t)rpp)
 #define DQ_COLS_E(U, M, AT)                     \
     do {                                        \
