@@ -83,3 +83,18 @@ int dq_launch_gemm(const int8_t* sA, const int8_t* iBp, int M, int N, int Kp,
 
 // A short description of the kernels dq_launch_gemm picks for a shape.
 const char* dq_gemm_info(int M, int N, int Kp);
+
+// The tile configuration dq_launch_gemm picks: 2 = 256x256, 1 = 128x128,
+// 0 = 32x32 (small or skinny products).
+int dq_gemm_config(int M, int N);
+
+// The inner product of a small problem in one launch (dqip_small.hip): the
+// rows of A quantized inside the GEMM's workgroups. Applies when the GEMM
+// would take 32x32 tiles, K % 16 == 0, K <= kDqipSmallKMax and A is 16-byte
+// aligned; B is packed (constant). Writes C per ep (F32, BF16 or ACC) and,
+// for inspection, sA / scaleA / zeroA as the row quantizer does.
+constexpr int kDqipSmallKMax = 1024;
+bool dq_dqip_small_fits(int M, int N, int K, const void* A);
+int dq_launch_dqip_small(const void* A, bool bf16, int M, int N, int K, int Kp, const int8_t* iBp,
+                         const DqEpilogue& ep, int8_t* sA, float* scaleA, int32_t* zeroA, hipStream_t s,
+                         DqTiming t = {});

@@ -198,6 +198,24 @@ int run_forward(dqip_ctx* c, const void* A, const void* B, void* buf, void* out,
     int8_t* sA = (int8_t*)(w + c->lay.sA);
     float* scaleA = (float*)(w + c->lay.scaleA);
     int32_t* zeroA = (int32_t*)(w + c->lay.zeroA);
+    if (c->constB && dq_dqip_small_fits(M, N, K, A)) {
+        // small product: quantization and GEMM in one launch (timed as the GEMM phase)
+        DqEpilogue ep;
+        ep.scaleA = scaleA;
+        ep.zeroA = zeroA;
+        ep.scaleB = c->scaleB;
+        ep.colsumB = c->colsum;
+        ep.bias = c->bias ? c->biasv : nullptr;
+        ep.act = c->act;
+        ep.alpha = c->alpha;
+        ep.out = mode;
+        ep.C = out;
+        rc = dq_launch_dqip_small(A, c->typeA == DQ_BF16, M, N, K, Kp, c->iBt, ep, sA, scaleA, zeroA, s,
+                                  prof_phase(c, DQ_PHASE_GEMM));
+        if (rc) return rc;
+        prof_call_done(c);
+        return DQ_OK;
+    }
     rc = dq_launch_quant_rows(A, c->typeA == DQ_BF16, M, K, Kp, sA, scaleA, zeroA, s,
                               prof_phase(c, DQ_PHASE_QUANT_A));
     if (rc) return rc;

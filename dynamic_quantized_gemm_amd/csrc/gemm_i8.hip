@@ -537,6 +537,8 @@ int pick(int M, int N) {
 
 }  // namespace
 
+int dq_gemm_config(int M, int N) { return pick(M, N); }
+
 int dq_launch_gemm(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, const DqEpilogue& ep,
                    hipStream_t s, DqTiming t) {
     switch (pick(M, N)) {
