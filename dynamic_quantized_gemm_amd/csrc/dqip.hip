@@ -320,11 +320,16 @@ extern "C" int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype 
         delete c;
         return rc;
     }
-    char buf[512];
+    char buf[640];
+    // small products with a constant B run both steps in one launch when A
+    // is 16-byte aligned (dqip_small.hip); the alignment is the caller's
+    const bool small = constB && dq_gemm_config((int)M, (int)N) == 0 && K % 16 == 0 && K <= kDqipSmallKMax;
     snprintf(buf, sizeof buf,
-             "gfx950 A:%s B:%s%s C:%s | quant_rows 8-row blocks staged in LDS, whole-line fragment stores | %s%s | %s",
-             dtype_name(typeA), dtype_name(typeB), constB ? "(const)" : "(dynamic)",
-             dtype_name(typeC), constB ? "" : "quant_cols absmax+pack | ",
+             "gfx950 A:%s B:%s%s C:%s | %squant_rows 8-row blocks staged in LDS, whole-line fragment stores | %s%s | %s",
+             dtype_name(typeA), dtype_name(typeB), constB ? "(const)" : "(dynamic)", dtype_name(typeC),
+             small ? "one launch (dqip_small: rows quantized inside the 32x32 GEMM tiles) for a 16-byte-aligned A, "
+                     "else " : "",
+             constB ? "" : "quant_cols absmax+pack | ",
              avoidOverflow ? "B range [-64,63]" : "B range [-128,127]",
              dq_gemm_info((int)M, (int)N, (int)c->Kp));
     c->info = buf;
