@@ -137,10 +137,12 @@ def test_lstm_matches_oracle(gpu, name):
         assert np.array_equal(a, b), "a second forward on one context differs"
 
 
-def test_lstm_gate_projection_workload_full_size(gpu):
-    """seq 128, batch 32, input 512, hidden 512, per-column int8 W and R."""
-    c = workloads.lstm_case()
-    log("lstm full size: seq 128 batch 32 input 512 hidden 512")
+@pytest.mark.parametrize("direction", ["forward", "bidirectional"])
+def test_lstm_gate_projection_workload_full_size(gpu, direction):
+    """seq 128, batch 32, input 512, hidden 512, per-column int8 W and R:
+    the timed workload in both directions, with its seed and arguments."""
+    c = workloads.lstm_case(direction=direction)
+    log(f"lstm full size {direction}: seq 128 batch 32 input 512 hidden 512")
     _check(gpu, c)
 
 

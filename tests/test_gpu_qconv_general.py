@@ -170,3 +170,39 @@ def test_qconv_printed_int8_example(gpu):
     (got,), _ = _run(gpu, x, g["x_scale"], g["x_zero_point"], w, g["w_scale"], g["w_zero_point"],
                      g["y_scale"], g["y_zero_point"], "i8")
     assert got.reshape(-1).tolist() == g["y"]
+
+
+@pytest.mark.parametrize("name", [
+    "resnet_3x3_64_56", "resnet_3x3_256_56", "resnet_3x3_256_14", "resnet_stem_7x7_s2",
+    "depthwise_3x3_256_56"])
+def test_qconv_benchmark_layers_full_size(gpu, name):
+    """Each timed ResNet-shaped layer (batch 8) at its full size, seed and
+    arguments, in the same launch. The oracle computes a slice of it
+    exactly: output image n reads only x[n], and output channel m only
+    w[m], its scale, its bias and its group's input channels. The slice is
+    the first and last image, with 32 output channels spread over the layer
+    (32 whole groups for the depthwise layer)."""
+    import workloads
+
+    N, C, H, W, M, k, st, pad, grp = workloads.QCONV_LAYERS[name]
+    c = workloads.qconv_layer_case(name)
+    log(f"qconv benchmark layer {name}: {workloads.QCONV_LAYERS[name]}")
+    x, w = c["x"], c["w"]
+    (got,), info = _run(gpu, x, c["x_scale"], 128, w, c["w_scale"], None, c["y_scale"], 128, "u8",
+                        bias=c["bias"], strides=(st, st), pads=(pad,) * 4, group=grp)
+    imgs = [0, N - 1]
+    if grp == 1:
+        ms = np.unique(np.linspace(0, M - 1, 32).astype(int))
+        xs, g = x[imgs], 1
+    else:
+        per, cg = M // grp, C // grp
+        g0 = grp // 2
+        g = min(32, grp - g0)
+        ms = np.arange(g0 * per, (g0 + g) * per)
+        xs = x[imgs][:, g0 * cg:(g0 + g) * cg]
+    want = oracle.qlinear_conv2d(xs, c["x_scale"], 128, w[ms], c["w_scale"][ms], np.zeros(len(ms), np.int32),
+                                 c["y_scale"], 128, bias=c["bias"][ms], strides=(st, st), pads=(pad,) * 4,
+                                 group=g, y_type="u8")
+    part = got[imgs][:, ms]
+    assert part.shape == want.shape
+    assert np.array_equal(part, want), f"{(part != want).sum()} of {part.size} differ ({info})"
