@@ -343,3 +343,64 @@ def test_qlinear_concat_matches_oracle(gpu, shapes, axis, t):
     torch.cuda.synchronize()
     got = y.cpu().numpy()
     assert np.array_equal(got, want), f"{(got != want).sum()} differ"
+
+
+@pytest.mark.parametrize("kind", ["add", "add_rowvec", "mul", "mul_integer", "sigmoid", "leaky_relu",
+                                  "sum_rows", "sum_cols", "mean_rows", "mean_pool_nchw", "mean_pool_nhwc",
+                                  "concat"])
+def test_benchmark_workloads_full_size(gpu, kind):
+    """Every timed element-wise workload at its full size with its seed and
+    parameters. The oracle computes a sample of the outputs exactly: the
+    outputs of one row (batch entry, column) depend only on that row of
+    the inputs, and a one-code function only on its code."""
+    import torch
+    import workloads
+
+    c = workloads.elementwise_case(kind)
+    t, xs, sc, zp = c["type"], c["xs"], c["scales"], c["zps"]
+    r = np.random.default_rng(_seed("bench", kind))
+    log(f"element-wise benchmark workload {kind}: {[x.shape for x in xs]}")
+    if kind in ("add", "add_rowvec", "mul", "mul_integer"):
+        op = {"add": "add", "add_rowvec": "add", "mul": "mul", "mul_integer": "mulint"}[kind]
+        A, B = xs
+        got = _run_binary(gpu, op, t, A, B, sc[0], zp[0], sc[1], zp[1], sc[2], zp[2])
+        rows = np.sort(r.choice(A.shape[0], 256, replace=False))
+        Bs = B[rows] if B.ndim == A.ndim else B
+        want = _want_binary(op, A[rows], Bs, sc[0], zp[0], sc[1], zp[1], sc[2], zp[2])
+        part = got[rows]
+    elif kind in ("sigmoid", "leaky_relu"):
+        fn = "leaky" if kind == "leaky_relu" else "sigmoid"
+        X = xs[0]
+        got = _run_unary(gpu, fn, t, X, sc[0], zp[0], sc[1], zp[1], alpha=c.get("alpha", 0.01))
+        idx = np.unique(r.integers(0, X.size, 1 << 20))
+        want = _want_unary(fn, X[idx], sc[0], zp[0], sc[1], zp[1], alpha=c.get("alpha", 0.01))
+        part = got[idx]
+    elif kind == "concat":
+        ax = c["axis"]
+        shape = list(xs[0].shape)
+        shape[ax] = sum(x.shape[ax] for x in xs)
+        y = torch.empty(shape, dtype=_tdt(t), device="cuda")
+        gpu.qlinear_concat([(_dev(x), _scal(s), _zp(z, t)) for x, s, z in zip(xs, sc, zp)], ax,
+                           _scal(sc[len(xs)]), _zp(zp[len(xs)], t), _type(gpu, t), y)
+        torch.cuda.synchronize()
+        ns = np.sort(r.choice(shape[0], 4, replace=False))
+        want = oracle.qlinear_concat([(x[ns], s, z) for x, s, z in zip(xs, sc, zp)], sc[len(xs)],
+                                     zp[len(xs)], ax)
+        part = y.cpu().numpy()[ns]
+    else:
+        X, axes = xs[0], c["axes"]
+        mode = "sum" if kind.startswith("sum_") else "mean"
+        got = _run_reduce(gpu, mode, t, X, axes, None if mode == "sum" else (sc[0], zp[0], sc[1], zp[1]))
+        kept = [n for d, n in enumerate(X.shape) if d not in axes]
+        got = got.reshape(kept)
+        if axes == [0]:  # columns: each output is one column of X
+            cols = np.sort(r.choice(X.shape[1], 256, replace=False))
+            Xs, part = X[:, cols], got[cols]
+        else:  # the leading axis is kept: each output row reads one leading entry of X
+            ns = np.sort(r.choice(X.shape[0], min(64, X.shape[0]), replace=False))
+            Xs, part = X[ns], got[ns]
+        want = (oracle.reduce_sum_integer(Xs, axes=axes) if mode == "sum"
+                else oracle.qlinear_reduce_mean(Xs, sc[0], zp[0], sc[1], zp[1], axes=axes))
+        want = want.reshape(part.shape)
+    assert part.shape == want.shape, (part.shape, want.shape)
+    assert np.array_equal(part, want), f"{(part != want).sum()} of {part.size} differ"
