@@ -262,3 +262,34 @@ def test_qgemm_argument_errors_on_device(gpu):
         torch.cuda.synchronize()
     finally:
         dq.dq_qgemm_release(h)
+
+
+@pytest.mark.parametrize("kind", ["mitf", "dqmm", "qgemm"])
+def test_benchmark_products_full_size(gpu, kind):
+    """The three timed 4096^3 products (MatMulIntegerToFloat, DynamicQuantizeMatMul,
+    QGemm with uint8 Y) with their seed and arguments: the int32 sums and Y of
+    sampled rows against the oracle. A row of the result depends only on its
+    row of A, once DynamicQuantizeMatMul's per-tensor quantization has been
+    taken over the whole of A."""
+    import workloads
+
+    c = workloads.qgemm_case(kind)
+    A, B, M = c["A"], c["B"], c["M"]
+    kw = dict(b_scale=c["b_scale"], b_zp=c["b_zp"])
+    if kind != "dqmm":
+        kw.update(a_scale=c["a_scale"], a_zp=c["a_zp"])
+    if kind == "qgemm":
+        kw.update(C=c["C"], y_type="u8", y_scale=c["y_scale"], y_zp=c["y_zp"])
+    else:
+        kw["bias"] = c["bias"]
+    log(f"{c['name']} sampled rows")
+    got = run_qgemm(gpu, A, B, accumulators=True, **kw)
+    r = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, M - 1], r.integers(0, M, 30)]))
+    if kind == "dqmm":
+        sc, zp, q = oracle.quantize_tensor_u8(A)
+        want = oracle.qgemm(np.ascontiguousarray(q[rows]), B, sc, zp, c["b_scale"], c["b_zp"],
+                            bias=c["bias"], with_acc=True)
+    else:
+        want = _want(np.ascontiguousarray(A[rows]), B, **dict(kw))
+    _check({"Y": got["Y"][rows], "acc": got["acc"][rows]}, want, kw.get("y_type", "f32"), kw.get("bias"))
