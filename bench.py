@@ -234,6 +234,49 @@ def _bw_record(nbytes, cold, warm_ms):
             "us_warm": round(warm_ms * 1e3, 2), "GBps_warm": round(gb / (warm_ms / 1e3), 1)}
 
 
+def achievable(dq, torch, reps=5):
+    """What the chip reaches on its own, as context for the roofline
+    fractions (the library's measurement probes): the int8 MFMA rate of a
+    loop with nothing but the GEMM wave tile's MFMAs (one workgroup of four
+    waves per CU, as the 4096^3 GEMM runs), with random and with all-zero
+    operands, and the HBM rate of a plain 16-byte copy of 1 GiB (2 GiB moved
+    per call). Median of `reps` launches, HIP events on torch's current
+    stream (the stream the probes are launched on)."""
+    def med_ms(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    out = {}
+    wg, iters = 256, 2000
+    sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+    ops = float(wg) * 4 * iters * 32 * 65536
+    g = torch.Generator(device="cpu").manual_seed(0)
+    rnd = torch.randint(-128, 128, (65536,), generator=g, dtype=torch.int8).cuda()
+    for name, buf in (("random", rnd), ("zero", torch.zeros(65536, dtype=torch.int8, device="cuda"))):
+        ms = med_ms(lambda: dq.dq_probe_mfma_loop(buf, iters, wg, sink))
+        out[f"mfma_loop_TOPS_{name}_operands"] = round(ops / (ms / 1e3) / 1e12, 1)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = med_ms(lambda: dq.dq_probe_copy(src, dst, n))
+    out["copy_GBps"] = round(2.0 * n / (ms / 1e3) / 1e9, 1)
+    out["copy_frac_of_8TBps"] = round(2.0 * n / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 3)
+    del src, dst
+    out["mfma_loop_frac_of_5POPS_random"] = round(out["mfma_loop_TOPS_random_operands"] / INT8_PEAK_TOPS, 3)
+    out["how"] = (f"mfma: {wg} workgroups x 4 waves, each {iters} x 32 v_mfma_i32_32x32x32_i8 on register "
+                  f"operands (two alternating sets); copy: 1 GiB, four 16 B non-temporal loads a lane in flight; "
+                  f"median of {reps} launches")
+    return out
+
+
 def bench_qdq(dq, torch, steps):
     """QuantizeLinear and DequantizeLinear, per axis, [64,256,56,56] fp32 <->
     int8: GB/s of algorithmic bytes (4 + 1 per element), cold (Infinity
@@ -564,23 +607,125 @@ def bench_dqip_case(dq, torch, case, steps, warmup, flush):
             "gemm_TOPS": round(d.ops / (ph[2] / 1e3) / 1e12, 2) if ph[2] > 0 else None}
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The oracle as it is (single-threaded C) on a sample of rows of the
-    same workload, scaled to TOP/s of the whole inner product."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def _cpu_threads():
+    """Threads for the all-core oracle leg: the host's CPUs this process may
+    use, capped by OMP_NUM_THREADS (the share a GPU job is given)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else n
+
+
+def _oracle_rows(case, rows, threads):
+    """The oracle (unchanged, single-threaded C) over `rows`, split into
+    `threads` contiguous slices run at once from a thread pool (each call
+    releases the interpreter lock while in C; output rows are independent,
+    so the results are the same as one call's)."""
+    import concurrent.futures as cf
+
     import oracle
+
+    if threads == 1:
+        oracle.dqip_forward(case, rows=rows)
+        return
+    parts = [p for p in np.array_split(rows, threads) if p.size]
+    with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        list(ex.map(lambda p: oracle.dqip_forward(case, rows=p), parts))
+
+
+def cpu_baseline(case, budget_s=12.0, others=True):
+    """The oracle as it is (plain C, one output row after another) timed on
+    this host's cores on a bounded sample of rows of the same workload,
+    scaled to TOP/s of the whole inner product: once on one thread, once
+    with the rows split over every available thread. With `others`, the
+    oracle's single-thread time for the other configurations too (bounded
+    samples, each stated)."""
+    import oracle
+    import workloads as W
 
     N, K = case["N"], case["K"]
     t0 = time.perf_counter()
     oracle.dqip_forward(case, rows=np.arange(2))
-    t_probe = time.perf_counter() - t0
-    rows = int(max(2, min(512, 2 * budget_s / max(t_probe, 1e-3))))
+    t_probe = (time.perf_counter() - t0) / 2
+    rows1 = int(max(2, min(512, budget_s / 2 / max(t_probe, 1e-4))))
     t0 = time.perf_counter()
-    oracle.dqip_forward(case, rows=np.arange(rows))
-    dt = time.perf_counter() - t0
-    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOP/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{rows} of {case['M']} rows of the same workload (row quantization of the "
-                      f"sample, full B, {rows}x{N}x{K} integer sums, epilogue), {dt:.1f} s on 1 thread"}
+    _oracle_rows(case, np.arange(rows1), 1)
+    dt1 = time.perf_counter() - t0
+    threads = _cpu_threads()
+    rowsN = int(min(case["M"], rows1 * threads))
+    t0 = time.perf_counter()
+    _oracle_rows(case, np.arange(rowsN), threads)
+    dtN = time.perf_counter() - t0
+    v1 = 2.0 * rows1 * N * K / dt1 / 1e12
+    vN = 2.0 * rowsN * N * K / dtN / 1e12
+    rec = {"value": round(vN, 6), "unit": "TOP/s", "cores": threads, "kind": "oracle",
+           "sample": (f"{rowsN} of {case['M']} rows of the same 4096^3 workload split over {threads} "
+                      f"threads ({dtN:.1f} s); single thread: {rows1} rows in {dt1:.1f} s. Each call: "
+                      f"row quantization of its rows, the whole B's column sums, the rows' integer "
+                      f"sums and epilogue"),
+           "value_1_thread": round(v1, 6), "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+    if not others:
+        return rec
+    extra = {}
+    # c1: the whole 64x64x128 forward, median of 3
+    c1 = W.dqip_small()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.dqip_forward(c1)
+        ts.append(time.perf_counter() - t0)
+    extra["dqip_64x64x128"] = {"us_per_forward": round(float(np.median(ts)) * 1e6, 1)}
+    # c2: QuantizeLinear + DequantizeLinear over the whole [64,256,56,56] tensor
+    q = W.qdq_per_axis(seed=1)
+    t0 = time.perf_counter()
+    yq = oracle.quantize_linear(q["x"], q["scale"], q["zp"], axis=1)
+    tq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.dequantize_linear(yq, q["scale"], q["zp"], axis=1)
+    td = time.perf_counter() - t0
+    nb = 5 * q["x"].size
+    extra["qdq_64x256x56x56"] = {"quantize_GBps": round(nb / tq / 1e9, 3),
+                                 "dequantize_GBps": round(nb / td / 1e9, 3)}
+    # c4: the input projection on 256 of its 4096 rows, the recurrent step whole
+    c4 = W.dqip_lstm(recurrent=False)
+    t0 = time.perf_counter()
+    oracle.dqip_forward(c4, rows=np.arange(256))
+    t4 = time.perf_counter() - t0
+    c4r = W.dqip_lstm(recurrent=True)
+    t0 = time.perf_counter()
+    oracle.dqip_forward(c4r)
+    t4r = time.perf_counter() - t0
+    extra["lstm_input_4096x2048x512"] = {"TOPS": round(2.0 * 256 * c4["N"] * c4["K"] / t4 / 1e12, 6),
+                                         "sample": "256 of 4096 rows"}
+    extra["lstm_recurrent_32x2048x512"] = {"us_per_forward": round(t4r * 1e6, 1)}
+    # c5b: the 1x1 QLinearConv on one of the eight images
+    c = W.qconv1x1()
+    x1 = np.ascontiguousarray(c["x"][:1])
+    C_, HW = x1.shape[1], x1.shape[2] * x1.shape[3]
+    t0 = time.perf_counter()
+    oracle.qlinear_conv(x1.reshape(1, C_, HW, 1), c["x_scale"], int(c["x_zp"]), c["w"].reshape(-1, C_),
+                        c["w_scale"], np.zeros(c["w"].shape[0], np.int32), c["y_scale"], int(c["y_zp"]),
+                        bias=c["bias"], y_type="u8")
+    t5 = time.perf_counter() - t0
+    nb5 = (2 * C_ * HW + c["w"].size) * 8  # whole-batch bytes, time scaled from one image
+    extra["qlinearconv_1x1"] = {"GBps": round(nb5 / (8 * t5) / 1e9, 3), "sample": "image 0 of 8"}
+    rec["other_configs_1_thread"] = extra
+    return rec
 
 
 def main():
@@ -590,6 +735,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline only: no secondary configs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--detail", metavar="PATH", help="also write every secondary record in full to PATH")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scales the HBM traffic counters)")
     ap.add_argument("--write-traffic", nargs=4,
@@ -633,8 +779,13 @@ def main():
                 "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
                 "traffic": None if tr is None else tr["bytes_per_launch"],
                 "kernel": "gemm_i8 (int8 MFMA, fused dequant/bias/ReLU/bf16 epilogue)",
+                "scope": ("the GEMM kernel alone (its own launch duration); `value` is the whole "
+                          "forward, row quantization included"),
                 "avg_launch_us": round(gemm_ms * 1e3, 2),
                 "ops_per_launch": d.ops}
+    log("bench: achievable rates (MFMA-only loop, plain copy)")
+    ach = achievable(dq, torch)
+    log(f"bench: {ach}")
 
     secondary = {"dqip_4096_phases_us": {"quant_a": round(phases[0] * 1e3, 2),
                                          "gemm": round(gemm_ms * 1e3, 2),
@@ -674,9 +825,28 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
-        cpu = cpu_baseline(case)
+        cpu = cpu_baseline(case, others=not args.quick)
         log(f"bench: {cpu}")
 
+    # the metric's second half and the context of the first, also inside
+    # `roofline` (a record every reader of the line keeps whole)
+    roofline["achievable"] = {k: v for k, v in ach.items() if k != "how"}
+    qdq = None
+    if "qdq" in secondary:
+        qq, dd = secondary["qdq"]["quantize"], secondary["qdq"]["dequantize"]
+        qdq = {"workload": "QuantizeLinear / DequantizeLinear per channel (axis 1), x fp32 [64,256,56,56] <-> "
+                           "int8, 256.9 MB moved per call",
+               "quantize_GBps_cold": qq["GBps_cold"], "quantize_frac_cold": qq["frac_cold"],
+               "dequantize_GBps_cold": dd["GBps_cold"], "dequantize_frac_cold": dd["frac_cold"],
+               "quantize_us_cold": qq["us_cold"], "dequantize_us_cold": dd["us_cold"],
+               "quantize_GBps_stream": qq.get("GBps_stream"), "dequantize_GBps_stream": dd.get("GBps_stream"),
+               "peak_GBps": HBM_PEAK_GBS}
+        roofline["qdq"] = {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                           "quantize": {"achieved": qq["GBps_cold"], "frac": qq["frac_cold"],
+                                        "us": qq["us_cold"]},
+                           "dequantize": {"achieved": dd["GBps_cold"], "frac": dd["frac_cold"],
+                                          "us": dd["us_cold"]},
+                           "timing": "cold: after a 512 MiB read flush; 256.9 MB a call"}
     line = {
         "metric": "dyn-quant GEMM TOPS (% int8 MFMA peak) + Quantize/DequantizeLinear GB/s",
         "value": round(value, 2),
@@ -694,12 +864,31 @@ def main():
                                "1% x20 outliers, constant int8 B with per-column scales, fp32 "
                                "bias, ReLU, bf16 C",
                    "M": 4096, "N": 4096, "K": 4096, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2)},
+        "qdq": qdq,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "secondary": secondary,
+        "secondary": {k: compact(v) for k, v in secondary.items()},
         "info": info,
     }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"secondary": secondary, "cpu_baseline": cpu, "achievable": ach}, f, indent=1)
     print(json.dumps(line), flush=True)
+
+
+_KEEP = ("us_cold", "us_per_forward", "us_warm", "TOPS", "TOPS_cold", "TOPS_warm", "GBps_cold",
+         "frac_cold", "GBps_stream", "frac_stream", "gemm_TOPS", "phase_us", "us_per_step_warm",
+         "tokens_per_s_warm", "quant_a", "gemm", "host_enqueue")
+
+
+def compact(v):
+    """The few figures of a secondary record that the JSON line keeps (the
+    whole record is on stderr, and in --detail's file)."""
+    if not isinstance(v, dict):
+        return v
+    if any(k in v for k in _KEEP):
+        return {k: v[k] for k in _KEEP if k in v}
+    return {k: compact(x) for k, x in v.items() if isinstance(x, dict)}
 
 
 if __name__ == "__main__":

@@ -50,6 +50,8 @@ _SIGNATURES = {
     "dqip_forward_accumulators": (C.c_int, [C.c_void_p] * 6),
     "dqip_profile_begin": (C.c_int, [C.c_void_p, C.c_int]),
     "dqip_profile_end": (C.c_int, [C.c_void_p, C.POINTER(C.c_float), C.POINTER(C.c_int)]),
+    "dq_probe_mfma_loop": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
+    "dq_probe_copy": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlinear_quantize": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
                                    C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
     "qlinear_dequantize": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int,
@@ -144,13 +146,31 @@ def exported_symbols():
     return list(_SIGNATURES)
 
 
-def _ptr(t):
-    """Device (or host) pointer of a tensor / int / None."""
+_ELEM = {DQ_F32: 4, DQ_BF16: 2, DQ_I8: 1, DQ_U8: 1, DQ_F16: 2}
+
+
+def _ptr(t, what="tensor", nbytes=0):
+    """Device pointer of a tensor / int / None. A tensor must be a dense
+    (contiguous) device tensor of at least `nbytes` bytes: the kernels index
+    it as such, and a short or strided buffer would be read or written out of
+    bounds. A plain int is taken as a device pointer whose extent is the
+    caller's to guarantee."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if t.device.type != "cuda":
+        raise DQError(DQ_ERR_ARG, what, "not a device tensor")
+    if not t.is_contiguous():
+        raise DQError(DQ_ERR_ARG, what, "not contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise DQError(DQ_ERR_ARG, what, f"holds {have} bytes, {nbytes} needed")
     return t.data_ptr()
+
+
+# sizes of each context made by dqip_init, for the binding's extent checks
+_DQIP_DIMS = {}
 
 
 def _stream(stream):
@@ -177,7 +197,21 @@ def dqip_init(M, N, K, typeA, typeB, typeC, constB, bias, activation, avoidOverf
     h = C.c_void_p(ctx)
     _check(load().dqip_init(C.byref(h), M, N, K, typeA, typeB, typeC, int(bool(constB)),
                             int(bool(bias)), activation, int(bool(avoidOverflow))), "dqip_init")
+    if ctx is not None and ctx != h.value:
+        _DQIP_DIMS.pop(ctx, None)
+    _DQIP_DIMS[h.value] = (int(M), int(N), int(K), typeA, typeB, typeC)
     return h.value
+
+
+def _dims(ctx):
+    return _DQIP_DIMS.get(ctx, (0, 0, 0, DQ_I8, DQ_I8, DQ_I8))
+
+
+def _ext_bytes(ctx, buf):
+    """Bytes a work-buffer tensor must hold (0: no tensor to check)."""
+    if ctx in _DQIP_DIMS and buf is not None and not isinstance(buf, int):
+        return dqip_external_buffer_size(ctx)
+    return 0
 
 
 def dqip_enabled(ctx) -> bool:
@@ -203,21 +237,32 @@ def dqip_set_params(ctx, weight, scale=None, bias=None, params=None, stream=None
     if params is not None:
         arr = (C.c_float * len(params))(*params)
         p = C.cast(arr, C.c_void_p)
-    _check(load().dqip_set_params(ctx, _ptr(weight), _ptr(scale), _ptr(bias), p, _stream(stream)),
-           "dqip_set_params")
+    M, N, K, tA, tB, tC = _dims(ctx)
+    w = "dqip_set_params"
+    _check(load().dqip_set_params(ctx, _ptr(weight, w, K * N * _ELEM[tB]), _ptr(scale, w, 4 * N),
+                                  _ptr(bias, w, 4 * N), p, _stream(stream)), w)
+
+
+def _fwd_args(ctx, A, B, buf, out, out_elem, w):
+    M, N, K, tA, tB, tC = _dims(ctx)
+    ext = _ext_bytes(ctx, buf)
+    return (_ptr(A, w, M * K * _ELEM[tA]), _ptr(B, w, K * N * _ELEM[tB]), _ptr(buf, w, ext),
+            _ptr(out, w, M * N * (out_elem or _ELEM[tC])))
 
 
 def dqip_forward(ctx, A, B, buf, C_, stream=None):
-    _check(load().dqip_forward(ctx, _ptr(A), _ptr(B), _ptr(buf), _ptr(C_), _stream(stream)),
-           "dqip_forward")
+    _check(load().dqip_forward(ctx, *_fwd_args(ctx, A, B, buf, C_, 0, "dqip_forward"),
+                               _stream(stream)), "dqip_forward")
 
 
 def dqip_forward_accumulators(ctx, A, B, buf, acc, stream=None):
-    _check(load().dqip_forward_accumulators(ctx, _ptr(A), _ptr(B), _ptr(buf), _ptr(acc),
+    _check(load().dqip_forward_accumulators(ctx, *_fwd_args(ctx, A, B, buf, acc, 4,
+                                                            "dqip_forward_accumulators"),
                                             _stream(stream)), "dqip_forward_accumulators")
 
 
 def dqip_release(ctx):
+    _DQIP_DIMS.pop(ctx, None)
     load().dqip_release(ctx)
 
 
@@ -227,13 +272,19 @@ def dqip_last_error() -> str:
 
 
 def dqip_read_quantized_a(ctx, buf, uA=None, scaleA=None, zeroA=None, stream=None):
-    _check(load().dqip_read_quantized_a(ctx, _ptr(buf), _ptr(uA), _ptr(scaleA), _ptr(zeroA),
-                                        _stream(stream)), "dqip_read_quantized_a")
+    M, N, K = _dims(ctx)[:3]
+    w = "dqip_read_quantized_a"
+    ext = _ext_bytes(ctx, buf)
+    _check(load().dqip_read_quantized_a(ctx, _ptr(buf, w, ext), _ptr(uA, w, M * K), _ptr(scaleA, w, 4 * M),
+                                        _ptr(zeroA, w, 4 * M), _stream(stream)), w)
 
 
 def dqip_read_quantized_b(ctx, buf, iB=None, scaleB=None, colsumB=None, stream=None):
-    _check(load().dqip_read_quantized_b(ctx, _ptr(buf), _ptr(iB), _ptr(scaleB), _ptr(colsumB),
-                                        _stream(stream)), "dqip_read_quantized_b")
+    M, N, K = _dims(ctx)[:3]
+    w = "dqip_read_quantized_b"
+    ext = _ext_bytes(ctx, buf)
+    _check(load().dqip_read_quantized_b(ctx, _ptr(buf, w, ext), _ptr(iB, w, K * N), _ptr(scaleB, w, 4 * N),
+                                        _ptr(colsumB, w, 4 * N), _stream(stream)), w)
 
 
 def dqip_profile_begin(ctx, capacity):
@@ -248,7 +299,28 @@ def dqip_profile_end(ctx):
     return [float(v) for v in ms], int(n.value)
 
 
+# ------------------------------------------------------ measurement probes
+
+def dq_probe_mfma_loop(operands, iters, workgroups, sink, stream=None):
+    """operands: >= 64 KiB device tensor; sink: >= workgroups * 256 int32."""
+    w = "dq_probe_mfma_loop"
+    _check(load().dq_probe_mfma_loop(_ptr(operands, w, 65536), int(iters), int(workgroups),
+                                     _ptr(sink, w, 1024 * int(workgroups)), _stream(stream)), w)
+
+
+def dq_probe_copy(src, dst, nbytes, stream=None):
+    w = "dq_probe_copy"
+    _check(load().dq_probe_copy(_ptr(src, w, nbytes), _ptr(dst, w, nbytes), int(nbytes), _stream(stream)), w)
+
+
 # ------------------------------------------------------ Q / DQ operators
+
+def _numel(shape):
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
 
 def _shape_arg(shape):
     arr = (C.c_int64 * max(1, len(shape)))(*[int(s) for s in shape])
@@ -260,8 +332,9 @@ def qlinear_quantize(x, y_scale, y_zero_point, y_type, y, axis=DQ_PER_TENSOR, sh
     """x: fp32 tensor; y: int8/uint8 tensor of the same shape (written)."""
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, keep = _shape_arg(shp)
-    _check(load().qlinear_quantize(_ptr(x), len(shp), sp, axis, _ptr(y_scale), _ptr(y_zero_point),
-                                   y_type, _ptr(y), _stream(stream)), "qlinear_quantize")
+    n, w = _numel(shp), "qlinear_quantize"
+    _check(load().qlinear_quantize(_ptr(x, w, 4 * n), len(shp), sp, axis, _ptr(y_scale, w, 4),
+                                   _ptr(y_zero_point, w, 1), y_type, _ptr(y, w, n), _stream(stream)), w)
     del keep
 
 
@@ -270,9 +343,9 @@ def qlinear_dequantize(x, x_type, x_scale, x_zero_point, y, axis=DQ_PER_TENSOR, 
     """x: int8/uint8 tensor; y: fp32 tensor of the same shape (written)."""
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, keep = _shape_arg(shp)
-    _check(load().qlinear_dequantize(_ptr(x), x_type, len(shp), sp, axis, _ptr(x_scale),
-                                     _ptr(x_zero_point), _ptr(y), _stream(stream)),
-           "qlinear_dequantize")
+    n, w = _numel(shp), "qlinear_dequantize"
+    _check(load().qlinear_dequantize(_ptr(x, w, n), x_type, len(shp), sp, axis, _ptr(x_scale, w, 4),
+                                     _ptr(x_zero_point, w, 1), _ptr(y, w, 4 * n), _stream(stream)), w)
     del keep
 
 
@@ -313,10 +386,12 @@ def qlinear_conv1x1(x, x_type, x_scale, x_zero_point, w, w_type, w_scale, w_zero
         M = int(w.shape[0])
     if w_len is None:
         w_len = int(w_scale.numel())
-    _check(load().qlinear_conv1x1(_ptr(x), x_type, N, C_, HW, _ptr(x_scale), _ptr(x_zero_point),
-                                  _ptr(w), w_type, M, _ptr(w_scale), _ptr(w_zero_point), w_len,
-                                  _ptr(y_scale), _ptr(y_zero_point), y_type, _ptr(bias), _ptr(y),
-                                  _stream(stream)), "qlinear_conv1x1")
+    n = "qlinear_conv1x1"
+    _check(load().qlinear_conv1x1(_ptr(x, n, N * C_ * HW), x_type, N, C_, HW, _ptr(x_scale, n, 4),
+                                  _ptr(x_zero_point, n, 1), _ptr(w, n, M * C_), w_type, M,
+                                  _ptr(w_scale, n, 4 * w_len), _ptr(w_zero_point, n, w_len), w_len,
+                                  _ptr(y_scale, n, 4), _ptr(y_zero_point, n, 1), y_type,
+                                  _ptr(bias, n, 4 * M), _ptr(y, n, N * M * HW), _stream(stream)), n)
 
 
 # ------------------------------------------- QGemm / MatMulIntegerToFloat

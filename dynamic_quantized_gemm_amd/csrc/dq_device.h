@@ -196,6 +196,29 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// MFMA results and the instructions that read them. The matrix core does
+// not interlock its results against later VALU instructions: the ISA's table
+// of required independent instructions (CDNA3 / CDNA4 instruction set
+// references, dependency resolution for XDL / MFMA operations) asks for
+// NumPasses + 3 wait states between an XDL instruction that writes
+// accumulator registers and a VALU instruction or v_accvgpr_read that reads
+// them (RAW), with one more on gfx950 for ops of more than two passes; the
+// largest MFMA here has 16 passes, so at most 20. The compiler inserts these
+// wait states for reads it can see, but not for a read inside inline
+// assembly (acc_read below), whose operand it does not inspect for this
+// hazard. Every kernel therefore crosses one drain of kMfmaDrainWaitStates
+// (s_nop n gives n + 1 wait states) between its last MFMA and its first
+// read of the accumulators; the scheduling barriers keep the compiler from
+// moving an MFMA or a read across it. Cost: 24 cycles once per wave.
+constexpr int kMfmaReadWaitStates = 20;
+constexpr int kMfmaDrainWaitStates = 24;
+static_assert(kMfmaDrainWaitStates >= kMfmaReadWaitStates, "drain shorter than the ISA's requirement");
+__device__ __forceinline__ void mfma_result_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Reads one accumulator register that an MFMA left in the accumulation
 // register file (AGPRs). Handing the value to an explicit read at its point
 // of use keeps the register allocator from copying every accumulator into

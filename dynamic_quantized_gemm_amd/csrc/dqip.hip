@@ -271,14 +271,14 @@ extern "C" int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype 
         DQ_FAIL(DQ_ERR_ARG, "unknown activation %d", (int)activation);
     if (typeB == DQ_I8) avoidOverflow = 0;  // ignored for an already quantized B
 
-    if (dqip_ctx* old = *ctx) {
-        if (old->M == M && old->N == N && old->K == K && old->typeA == typeA &&
-            old->typeB == typeB && old->typeC == typeC && old->constB == constB &&
-            old->bias == bias && old->act == activation && old->avoid == avoidOverflow)
-            return DQ_OK;
-        dqip_release(old);
-        *ctx = nullptr;
-    }
+    // re-init: identical parameters keep the context; any change builds a
+    // new one, and the old one is released only once the new one exists, so
+    // a failed re-init leaves the caller's handle valid (and unchanged)
+    dqip_ctx* old = *ctx;
+    if (old && old->M == M && old->N == N && old->K == K && old->typeA == typeA &&
+        old->typeB == typeB && old->typeC == typeC && old->constB == constB &&
+        old->bias == bias && old->act == activation && old->avoid == avoidOverflow)
+        return DQ_OK;
     int dev = 0;
     DQ_HIP_CHECK(hipGetDevice(&dev));
     dqip_ctx* c = new dqip_ctx();
@@ -333,6 +333,7 @@ extern "C" int dqip_init(dqip_ctx** ctx, size_t M, size_t N, size_t K, dq_dtype 
              avoidOverflow ? "B range [-64,63]" : "B range [-128,127]",
              dq_gemm_info((int)M, (int)N, (int)c->Kp));
     c->info = buf;
+    if (old) dqip_release(old);
     *ctx = c;
     return DQ_OK;
 }

@@ -184,8 +184,8 @@ __global__ void __launch_bounds__(kThreads) k_dqip_small(SmallArgs a) {
         if (nt == 0 && gok[j])
             *reinterpret_cast<dq::v4i*>(a.sA + dq::frag_offset(row, k0, a.KFp)) = af;
     }
-    // let the last MFMA retire before its accumulators are read
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    // the last MFMA's results need the ISA's wait states before they are read
+    dq::mfma_result_drain();
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[w][e][lane] = acc[e];
     __syncthreads();

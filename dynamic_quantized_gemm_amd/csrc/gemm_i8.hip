@@ -270,6 +270,10 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         one(std::integral_constant<int, 3>{}, t + 3);
     }
     dq::wait_vmcnt<0>();  // the trailing copies land before LDS is reused
+    // the epilogue reads the accumulators through inline assembly
+    // (dq::acc_read), which the compiler does not check against the last
+    // MFMA: give the results the ISA's wait states first
+    dq::mfma_result_drain();
 
     // ---- epilogue (see the header). The wave's output rows are cut into
     // strips of 32 (one per A fragment row); as many strips as fit in the

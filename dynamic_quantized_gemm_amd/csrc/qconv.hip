@@ -360,14 +360,9 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         }
     }
 
-    // The accumulators are read right below. The compiler inserts the wait
-    // states an MFMA result needs before a VALU read, but counting them
-    // across the blocks of the loop exit is its weak point: a fixed drain of
-    // 48 wait states (more than the 18 a 16-pass MFMA needs) makes the
-    // reads safe whatever path led here.
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");
-    __builtin_amdgcn_sched_barrier(0);
+    // the accumulators are read right below: the last MFMA's results first
+    // need the ISA's wait states (dq::mfma_result_drain)
+    dq::mfma_result_drain();
 
     // lane holds channel (lane % 32) of block jb and, in accumulators
     // 4q .. 4q+3, pixels 8q + 4 (lane / 32) + 0..3 of pixel block ib

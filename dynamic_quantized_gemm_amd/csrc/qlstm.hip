@@ -312,8 +312,8 @@ __global__ void __launch_bounds__(kThreads) k_lstm_step(StepArgs a) {
             }
         }
     }
-    // let the last MFMA retire before its accumulators are read
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    // the last MFMA's results need the ISA's wait states before they are read
+    dq::mfma_result_drain();
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[w][e][lane] = acc[e];
     rs += __shfl_xor(rs, 32);  // lanes l and l + 32 hold the two k halves of row l % 32

@@ -75,8 +75,10 @@ typedef struct dqip_ctx dqip_ctx;
 /* Init(): create or re-create a context (same page, Init()).
  * *ctx NULL creates one. A non-NULL *ctx whose M, N, K, types, constB,
  * bias, activation and avoidOverflow all equal the arguments is kept as is
- * (parameters set earlier stay); otherwise it is released and re-created,
- * and dqip_set_params is needed again when constB is set.
+ * (parameters set earlier stay); otherwise a new context is created and,
+ * only once that has succeeded, the old one is released and *ctx replaced
+ * (dqip_set_params is needed again when constB is set). On any error *ctx
+ * is left unchanged: the old context stays valid and owned by the caller.
  * typeA, typeC in {DQ_F32, DQ_BF16}. typeB in {DQ_F32, DQ_I8} when constB
  * (DQ_I8 = B already quantized, avoidOverflow then ignored), in
  * {DQ_F32, DQ_BF16} when not. 1 <= M, N <= 2^31-1, 1 <= K <= DQ_K_MAX.
@@ -171,6 +173,25 @@ enum { DQ_PHASE_QUANT_A = 0, DQ_PHASE_QUANT_B = 1, DQ_PHASE_GEMM = 2, DQ_PHASES 
  * recording. Errors: DQ_ERR_STATE, DQ_ERR_ARG (capacity < 1), DQ_ERR_HIP. */
 int dqip_profile_begin(dqip_ctx* ctx, int capacity);
 int dqip_profile_end(dqip_ctx* ctx, float* ms, int* calls);
+
+/* ---- measurement probes (not operations of the pages) -----------------
+ * What the hardware reaches on its own, reported next to the published
+ * peaks as context for the kernels' roofline fractions. Both launch one
+ * kernel on `stream` (asynchronous; the caller times it, e.g. with events).
+ *
+ * dq_probe_mfma_loop: `workgroups` workgroups of 4 waves; each wave keeps
+ * 16 int32 32x32 accumulator blocks (the GEMM's 128x128 wave tile) and runs
+ * `iters` iterations of 32 v_mfma_i32_32x32x32_i8 (2 * 32*32*32 ops each)
+ * on register operands only, alternating two operand sets taken from
+ * `operands` (device, at least 65536 bytes: random codes, or zeros). Total
+ * work: workgroups * 4 * iters * 32 * 65536 int8 ops. sink (device, at
+ * least workgroups * 256 int32) receives one checksum per lane.
+ * dq_probe_copy: copies `bytes` (multiple of 16) from src to dst (device,
+ * 16-byte aligned, not overlapping): 16 KiB per workgroup of 256 threads,
+ * each thread's four 16-byte non-temporal loads issued before its stores.
+ * Errors: DQ_ERR_ARG, DQ_ERR_HIP. */
+int dq_probe_mfma_loop(const void* operands, int iters, int workgroups, int32_t* sink, void* stream);
+int dq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * QuantizeLinear / DequantizeLinear.

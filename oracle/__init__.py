@@ -26,10 +26,12 @@ _lib = None
 
 
 def lib() -> C.CDLL:
-    """Load oracle/liboracle.so, compiling it with gcc first if it is absent."""
+    """Load oracle/liboracle.so, compiling it with gcc first if it is absent
+    or older than oracle.c."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        if (not os.path.exists(_build.LIB)
+                or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
             _build.build()
         L = C.CDLL(_build.LIB)
         vp, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float

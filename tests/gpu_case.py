@@ -23,8 +23,10 @@ def to_dev(a, torch):
 
 
 def run_dqip(dq, case, *, ext_buf=False, accumulators=True, inspect=True, ctx=None,
-             keep_ctx=False, repeat=1):
+             keep_ctx=False, repeat=1, a_offset=0):
     """Init + set_params + forward (and accumulators / inspection).
+    a_offset: A placed that many bytes past a 256-byte aligned allocation
+    (a multiple of its element size), to reach the paths for unaligned A.
     Returns a dict of numpy arrays."""
     import torch
 
@@ -35,6 +37,13 @@ def run_dqip(dq, case, *, ext_buf=False, accumulators=True, inspect=True, ctx=No
     out = {}
     try:
         A = to_dev(case["A"], torch)
+        if a_offset:
+            es = A.element_size()
+            assert a_offset % es == 0
+            flat = torch.zeros(A.numel() + a_offset // es, dtype=A.dtype, device="cuda")
+            flat[a_offset // es:] = A.reshape(-1)
+            A = flat[a_offset // es:].view(A.shape)
+            assert A.data_ptr() % 16 == a_offset % 16
         B = to_dev(case["B"], torch)
         sB = to_dev(case.get("scaleB"), torch)
         bias = to_dev(case.get("bias"), torch)
@@ -107,3 +116,19 @@ def assert_close_c(got, want, typeC, bias=None, rtol=1e-5):
     assert ok.all(), (f"{(~ok).sum()} fp32 outputs beyond {rtol} relative; worst "
                       f"{(err / np.maximum(ref, 1e-30)).max():.3g}")
     return int((got == want).mean() * 100)
+
+
+def tile_rows(M, seed, tile=256):
+    """Rows to check at full size: two from every `tile`-row block (one at a
+    position that moves through the block from block to block, so that
+    successive blocks hit different waves, 32-row strips and lanes of a
+    256-row GEMM tile, and one drawn at random), plus the first and last
+    row. A row of C depends only on its row of A, so the oracle can compute
+    exactly these rows."""
+    r = np.random.default_rng(seed)
+    rows = [0, M - 1]
+    for t in range((M + tile - 1) // tile):
+        lo, hi = t * tile, min(M, (t + 1) * tile)
+        rows.append(lo + (37 * t + 11 * seed) % (hi - lo))
+        rows.append(int(r.integers(lo, hi)))
+    return np.unique(np.array(rows, np.int64))

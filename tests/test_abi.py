@@ -326,3 +326,49 @@ def test_lstm_activation_slots_follow_the_consumption_order(dq):
     assert dq.lstm_activation_slots(None, None, None, 1)[0] == [0, 1, 1]
     with pytest.raises(ValueError):
         dq.lstm_activation_slots(["Sigmoid", "Tanh"], None, None, 1)
+
+
+class _FakeDeviceTensor:
+    """Stands in for a device tensor on a machine without a GPU: only what
+    the binding's extent checks read."""
+
+    def __init__(self, numel, elem=4, contiguous=True, device="cuda"):
+        self._n, self._e, self._c = numel, elem, contiguous
+        self.device = type("D", (), {"type": device})()
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        raise AssertionError("the binding passed a rejected tensor on to the library")
+
+
+@pytest.mark.parametrize("bad,why", [
+    (_FakeDeviceTensor(16 * 63), "holds"),                  # one element short of [16, 64]
+    (_FakeDeviceTensor(16 * 64, contiguous=False), "contiguous"),
+    (_FakeDeviceTensor(16 * 64, device="cpu"), "device"),
+])
+def test_binding_checks_tensor_extents_before_any_call(dq, bad, why):
+    """A short, strided or host buffer is refused by the binding (the
+    kernels would index it as a dense device array of M*K elements)."""
+    h = 0xdead0000
+    dq._binding._DQIP_DIMS[h] = (16, 32, 64, dq.DQ_F32, dq.DQ_F32, dq.DQ_F32)
+    try:
+        with pytest.raises(dq.DQError) as e:
+            dq._binding._fwd_args(h, bad, None, None, None, 0, "dqip_forward")
+        assert e.value.status == dq.DQ_ERR_ARG and why in str(e.value)
+        ok = _FakeDeviceTensor(16 * 64)
+        out_short = _FakeDeviceTensor(16 * 32 - 1)
+        with pytest.raises(dq.DQError):
+            dq._binding._ptr(out_short, "dqip_forward", 16 * 32 * 4)
+        assert dq._binding._ptr(None, "x", 100) is None
+        assert dq._binding._ptr(1234, "x", 100) == 1234   # raw pointers: the caller's contract
+        del ok
+    finally:
+        dq._binding._DQIP_DIMS.pop(h, None)

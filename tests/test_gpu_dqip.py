@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_case import assert_close_c, log, run_dqip
+from gpu_case import assert_close_c, log, run_dqip, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,13 @@ SWEEP = [
     (64, 256, 333, "bf16", "f32", True, "f32", "leaky_relu", False),
     (5, 1, 70, "f32", "bf16", False, "f32", "identity", True),
     (300, 5, 16, "bf16", "i8", True, "f32", "relu", False),
+    # small products in one launch (constant B, K % 16 == 0, K <= 1024): each
+    # register depth of the kernel (K <= 128, 256, 512, 1024), bf16 output,
+    # leaky ReLU, and a K that ends half way through a 32-deep fragment
+    (32, 2048, 256, "f32", "i8", True, "bf16", "leaky_relu", False),
+    (48, 100, 1024, "bf16", "f32", True, "f32", "relu", False),
+    (7, 33, 272, "f32", "f32", True, "f32", "identity", True),
+    (70, 40, 496, "bf16", "i8", True, "bf16", "identity", False),
 ]
 
 
@@ -94,15 +101,17 @@ def test_row_quantizer_paths(gpu, M, K, tA):
     _compare_sampled(case, got, _sample_rows(M, 5))
 
 
-@pytest.mark.parametrize("tA,tB", [("f32", "f32"), ("bf16", "bf16")])
-def test_tiny_scales_stay_exact(gpu, tA, tB):
+@pytest.mark.parametrize("tA,tB,constB,K", [("f32", "f32", False, 300), ("bf16", "bf16", False, 300),
+                                             ("f32", "f32", True, 288), ("bf16", "f32", True, 288)])
+def test_tiny_scales_stay_exact(gpu, tA, tB, constB, K):
     """Rows of A and columns of B scaled down until their quantization scales
     fall below 2^-100 and into the subnormal range: there the quantizers'
     reciprocal-and-residual quotient is not exact and the IEEE division must
-    be taken; every code, scale and zero point stays bit-exact."""
-    log(f"dqip tiny scales A:{tA} B:{tB}")
-    case = W.dqip_random(70, 68, 300, seed=21, typeA="f32", typeB="f32", typeC="f32",
-                         constB=False, outliers=0.01)
+    be taken; every code, scale and zero point stays bit-exact. A constant B
+    with K % 16 == 0 runs the one-launch small-product kernel."""
+    log(f"dqip tiny scales A:{tA} B:{tB} const:{constB} K={K}")
+    case = W.dqip_random(70, 68, K, seed=21, typeA="f32", typeB="f32", typeC="f32",
+                         constB=constB, outliers=0.01)
     A, B = case["A"], case["B"]
     for i, f in ((1, 1e-33), (2, 1e-36), (3, 1e-38), (4, 3e-39)):
         A[i] *= np.float32(f)
@@ -113,6 +122,18 @@ def test_tiny_scales_stay_exact(gpu, tA, tB):
     if tB == "bf16":
         case["B"], case["typeB"] = W.to_bf16_bits(B), "bf16"
     _compare(case, run_dqip(gpu, case), oracle.dqip_forward(case))
+
+
+@pytest.mark.parametrize("tA", ["f32", "bf16"])
+def test_unaligned_a_takes_the_two_launch_path(gpu, tA):
+    """A small product whose A is only 4-byte aligned cannot use the one-
+    launch kernel (16-byte loads): the row quantizer's unaligned path and the
+    GEMM run instead, with the same results."""
+    log(f"dqip unaligned A ({tA})")
+    case = W.dqip_random(40, 24, 96, seed=4, typeA=tA, typeB="f32", constB=True, act="relu")
+    want = oracle.dqip_forward(case)
+    _compare(case, run_dqip(gpu, case, a_offset=4), want)
+    _compare(case, run_dqip(gpu, case), want)
 
 
 def test_no_bias_flag_and_null_bias(gpu):
@@ -160,6 +181,32 @@ def test_reinit_keeps_or_recreates(gpu):
             gpu.dqip_forward(h3, A, None, None, C)
         assert e.value.status == gpu.DQ_ERR_STATE
         h = h3
+    finally:
+        gpu.dqip_release(h)
+
+
+def test_failed_reinit_keeps_the_old_context(gpu, monkeypatch):
+    """A re-init whose allocations fail (forced from the host with
+    DQIP_FAIL_ALLOC) returns DQ_ERR_ALLOC and leaves the old context valid:
+    it still computes the same C and is released exactly once."""
+    import torch
+
+    log("dqip failed re-init")
+    case = W.dqip_random(16, 32, 64, seed=13, typeB="i8")
+    got = run_dqip(gpu, case, keep_ctx=True)
+    h = got["ctx"]
+    try:
+        monkeypatch.setenv("DQIP_FAIL_ALLOC", "1")
+        with pytest.raises(gpu.DQError) as e:
+            gpu.dqip_init(16, 32, 64, gpu.DQ_F32, gpu.DQ_I8, gpu.DQ_F32, True, True,
+                          gpu.DQ_ACT_RELU, False, ctx=h)
+        assert e.value.status == gpu.DQ_ERR_ALLOC
+        monkeypatch.delenv("DQIP_FAIL_ALLOC")
+        A = torch.from_numpy(case["A"]).cuda()
+        C = torch.empty((16, 32), device="cuda")
+        gpu.dqip_forward(h, A, None, None, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), got["C"])
     finally:
         gpu.dqip_release(h)
 
@@ -242,7 +289,9 @@ def test_full_4096_bf16_relu(gpu):
     assert np.array_equal(got["scaleA"].view(np.uint32), sA.view(np.uint32))
     assert np.array_equal(got["iB"], case["B"])
     assert np.array_equal(got["colsumB"], oracle.colsum(case["B"]))
-    rows = _sample_rows(case["M"], 1)
+    # C and the int32 sums: two rows from every 256-row tile, first and last
+    rows = tile_rows(case["M"], 1)
+    log(f"  {len(rows)} rows against the oracle")
     _compare_sampled(case, got, rows)
 
 
@@ -254,13 +303,14 @@ def test_full_lstm_gates(gpu, recurrent):
     if recurrent:
         _compare(case, got, oracle.dqip_forward(case))
     else:
-        _compare_sampled(case, got, _sample_rows(case["M"], 2, n=64))
+        _compare_sampled(case, got, tile_rows(case["M"], 2))
 
 
 def test_full_8192_dynamic_b(gpu):
     log("dqip full 8192^3 dynamic fp32 B, avoidOverflow")
     case = W.dqip_dynamic_b()
     got = run_dqip(gpu, case, accumulators=False)
-    rows = _sample_rows(case["M"], 3, n=6)
+    rows = tile_rows(case["M"], 3)
+    log(f"  {len(rows)} rows against the oracle")
     want = oracle.dqip_forward(case, rows=rows)
     _compare(case, got, want, rows=rows, check_b=True)

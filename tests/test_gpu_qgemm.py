@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_case import assert_close_c, log, to_dev
+from gpu_case import assert_close_c, log, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -214,7 +214,8 @@ def test_qgemm_extreme_sums_stay_exact(gpu):
 
 def test_qgemm_repeated_forwards_and_row_subset_at_4096(gpu):
     """4096^3 MatMulIntegerToFloat (u8 A with zero point, i8 B per column):
-    three forwards in a row, every int32 sum of sampled rows bit-exact."""
+    three forwards in a row, every int32 sum of two rows from every 256-row
+    tile (and the first and last rows) bit-exact."""
     log("matmul_integer_to_float 4096^3 sampled rows")
     r = np.random.default_rng(6)
     M = N = K = 4096
@@ -224,7 +225,7 @@ def test_qgemm_repeated_forwards_and_row_subset_at_4096(gpu):
     bv = r.uniform(-1, 1, N).astype(np.float32)
     kw = dict(a_scale=np.float32(0.02), a_zp=117, b_scale=bs, b_zp=bz, bias=bv)
     got = run_qgemm(gpu, A, B, accumulators=True, repeat=3, **kw)
-    rows = np.unique(np.concatenate([[0, M - 1], r.integers(0, M, 6)]))
+    rows = tile_rows(M, 6)
     Yw, accw = _want(np.ascontiguousarray(A[rows]), B, **kw)
     assert np.array_equal(got["acc"][rows], accw)
     assert_close_c(got["Y"][rows], Yw, "f32", bv)
@@ -268,7 +269,8 @@ def test_qgemm_argument_errors_on_device(gpu):
 def test_benchmark_products_full_size(gpu, kind):
     """The three timed 4096^3 products (MatMulIntegerToFloat, DynamicQuantizeMatMul,
     QGemm with uint8 Y) with their seed and arguments: the int32 sums and Y of
-    sampled rows against the oracle. A row of the result depends only on its
+    two rows from every 256-row tile (and the first and last rows) against
+    the oracle. A row of the result depends only on its
     row of A, once DynamicQuantizeMatMul's per-tensor quantization has been
     taken over the whole of A."""
     import workloads
@@ -284,8 +286,7 @@ def test_benchmark_products_full_size(gpu, kind):
         kw["bias"] = c["bias"]
     log(f"{c['name']} sampled rows")
     got = run_qgemm(gpu, A, B, accumulators=True, **kw)
-    r = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([[0, M - 1], r.integers(0, M, 30)]))
+    rows = tile_rows(M, 11)
     if kind == "dqmm":
         sc, zp, q = oracle.quantize_tensor_u8(A)
         want = oracle.qgemm(np.ascontiguousarray(q[rows]), B, sc, zp, c["b_scale"], c["b_zp"],
