@@ -36,6 +36,10 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <set>
+#include <utility>
 
 namespace {
 
@@ -43,6 +47,8 @@ constexpr int kRowsPerWave = 1;
 constexpr int kWavesPerBlock = 8;
 constexpr int kRowsPerBlock = kWavesPerBlock * kRowsPerWave;
 constexpr int kThreads = 64 * kWavesPerBlock;
+// dynamic LDS of the LDS-staged kernel: eight rows of at most 16384 codes
+constexpr size_t kLdsMax = (size_t)8 * 16384;
 
 __device__ __forceinline__ void row_params(float lo, float hi, float& scale, int& zero) {
     if (hi == lo) {
@@ -488,28 +494,49 @@ k_quant_rows_stream(const void* __restrict__ A, int M, int K, int KF, int8_t* __
     }
 }
 
+// Workgroups of k_quant_rows_lds<BF16, NV, WPR> resident at once with `lds`
+// bytes of dynamic LDS (what the registers and LDS allow, times the CUs),
+// cached per device and LDS size; thread-safe. The variant's dynamic-LDS
+// limit is raised once per device to the most any launch of it asks for
+// (eight rows of 16384 codes).
+template <bool BF16, int NV, int WPR>
+int resident_groups(size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<int, size_t>, int> cache;
+    static std::set<int> raised;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, lds);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    if (!raised.count(dev)) {
+        if (hipFuncSetAttribute((const void*)k_quant_rows_lds<BF16, NV, WPR>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax) != hipSuccess) {
+            (void)hipGetLastError();
+            return 256;  // not cached: the next call tries again
+        }
+        raised.insert(dev);
+    }
+    int cus = 0, per_cu = 0;
+    int resident = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_quant_rows_lds<BF16, NV, WPR>, 512, lds) ==
+            hipSuccess &&
+        cus * per_cu > 0)
+        resident = cus * per_cu;
+    else
+        (void)hipGetLastError();
+    cache.emplace(key, resident);
+    return resident;
+}
+
 template <bool BF16, int NV, int WPR>
 void launch_lds(hipStream_t s, DqTiming t, const void* A, int M, int K, int KF, int8_t* sA,
                 float* scaleA, int32_t* zeroA) {
     const int lds_row = (K + 255) & ~255;
     const size_t lds = (size_t)8 * lds_row;
-    // workgroups resident at once (the occupancy the registers and LDS
-    // allow), taken once per kernel variant
-    static int resident = 0;
-    if (resident == 0) {
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipFuncSetAttribute((const void*)k_quant_rows_lds<BF16, NV, WPR>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_quant_rows_lds<BF16, NV, WPR>, 512,
-                                                         lds) == hipSuccess &&
-            cus * per_cu > 0)
-            resident = cus * per_cu;
-        else
-            resident = 256;
-    }
-    const int groups = std::min(resident, (M + 7) / 8);
+    const int groups = std::min(resident_groups<BF16, NV, WPR>(lds), (M + 7) / 8);
     hipExtLaunchKernelGGL((k_quant_rows_lds<BF16, NV, WPR>), dim3((unsigned)groups), dim3(512), lds, s,
                           t.start, t.stop, 0, A, M, K, KF, lds_row, sA, scaleA, zeroA);
 }
