@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     dq_qconv_init, dq_qconv_output_shape, dq_qconv_release, dq_qconv_set_w,
     DQ_LSTM_BIDIRECTIONAL, DQ_LSTM_FORWARD, DQ_LSTM_HIDDEN_MAX, DQ_LSTM_REVERSE, RNN_ACTIVATIONS,
     dq_lstm_forward, dq_lstm_info, dq_lstm_init, dq_lstm_release, dq_lstm_set_weights,
-    lstm_activation_slots, dq_probe_copy, dq_probe_mfma_loop,
+    lstm_activation_slots, dq_probe_copy, dq_probe_mfma_loop, dqip_forward_noalloc,
+    DQIP_NOALLOC_SCRATCH_BYTES,
 )

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "dqip_set_params": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p]),
     "dqip_forward": (C.c_int, [C.c_void_p] + [C.c_void_p] * 5),
+    "dqip_forward_noalloc": (C.c_int, [C.c_void_p] * 5),
     "dqip_release": (None, [C.c_void_p]),
     "dqip_last_error": (C.c_char_p, []),
     "dqip_read_quantized_a": (C.c_int, [C.c_void_p] * 6),
@@ -253,6 +254,14 @@ def _fwd_args(ctx, A, B, buf, out, out_elem, w):
 def dqip_forward(ctx, A, B, buf, C_, stream=None):
     _check(load().dqip_forward(ctx, *_fwd_args(ctx, A, B, buf, C_, 0, "dqip_forward"),
                                _stream(stream)), "dqip_forward")
+
+
+DQIP_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def dqip_forward_noalloc(ctx, A, B, C_, stream=None):
+    a, b, _, c = _fwd_args(ctx, A, B, None, C_, 0, "dqip_forward_noalloc")
+    _check(load().dqip_forward_noalloc(ctx, a, b, c, _stream(stream)), "dqip_forward_noalloc")
 
 
 def dqip_forward_accumulators(ctx, A, B, buf, acc, stream=None):

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -384,6 +385,61 @@ extern "C" int dqip_forward(dqip_ctx* ctx, const void* A, const void* B, void* b
                             void* stream) {
     if (ctx && ctx->typeC != DQ_F32 && ctx->typeC != DQ_BF16) DQ_FAIL(DQ_ERR_TYPE, "bad typeC");
     return run_forward(ctx, A, B, buf, C, ctx && ctx->typeC == DQ_BF16 ? DQ_OUT_BF16 : DQ_OUT_F32,
+                       (hipStream_t)stream);
+}
+
+// ---- the forward that allocates nothing ---------------------------------
+// Its work buffer (quantized A with its row scales and zero points, and for
+// a non-constant B the quantized B, its scales, column sums and column
+// maxima) is this file-scope device array: one copy per GPU, resident from
+// the library's load on that GPU until the process ends. Host code never
+// passes the array's name (a host-side stand-in, not a device address) to a
+// kernel or a memory call: the device address is taken once per device with
+// hipGetSymbolAddress, with that device current, and used from then on.
+// Nothing in the buffer needs to start at zero: every kernel of the forward
+// writes what it later reads (the column maxima are cleared by a kernel).
+static __device__ __align__(256) uint8_t scratch[DQIP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    DQ_HIP_CHECK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) DQ_FAIL(DQ_ERR_STATE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            DQ_FAIL(DQ_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                    hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DQ_OK;
+}
+}  // namespace
+
+extern "C" int dqip_forward_noalloc(dqip_ctx* ctx, const void* A, const void* B, void* C,
+                                    void* stream) {
+    if (!ctx) DQ_FAIL(DQ_ERR_STATE, "context is NULL");
+    if (ctx->typeC != DQ_F32 && ctx->typeC != DQ_BF16) DQ_FAIL(DQ_ERR_TYPE, "bad typeC");
+    if (ctx->lay.total > (size_t)DQIP_NOALLOC_SCRATCH_BYTES)
+        DQ_FAIL(DQ_ERR_RANGE,
+                "dqip_forward_noalloc: the work buffer of this context needs %zu bytes, more than the "
+                "%zu-byte static scratch; use dqip_forward with a caller buffer",
+                ctx->lay.total, (size_t)DQIP_NOALLOC_SCRATCH_BYTES);
+    int rc = check_current_device(ctx);
+    if (rc) return rc;
+    void* w = nullptr;
+    rc = scratch_for_current_device(&w);
+    if (rc) return rc;
+    return run_forward(ctx, A, B, w, C, ctx->typeC == DQ_BF16 ? DQ_OUT_BF16 : DQ_OUT_F32,
                        (hipStream_t)stream);
 }
 

@@ -129,6 +129,22 @@ int dqip_set_params(dqip_ctx* ctx, const void* weight, const float* scale,
 int dqip_forward(dqip_ctx* ctx, const void* A, const void* B, void* buf,
                  void* C, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, hosts that forbid hipMalloc): the forward
+ * above with its work buffer in the library's own static device scratch of
+ * DQIP_NOALLOC_SCRATCH_BYTES (32 MiB; one copy per GPU the library runs on,
+ * held until the process ends). It calls no hipMalloc / hipFree and no
+ * allocating library routine. The context must need at most that much work
+ * buffer (dqip_external_buffer_size(ctx) <= DQIP_NOALLOC_SCRATCH_BYTES, e.g.
+ * a 4096 x 4096 x 4096 product with a constant B needs 16 MiB + 32 KiB),
+ * else DQ_ERR_RANGE and nothing is launched. Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialized by the caller. A, B, C as for
+ * dqip_forward. Errors: DQ_ERR_STATE, DQ_ERR_RANGE, DQ_ERR_ARG, DQ_ERR_TYPE,
+ * DQ_ERR_HIP. */
+#define DQIP_NOALLOC_SCRATCH_BYTES (32u << 20)
+int dqip_forward_noalloc(dqip_ctx* ctx, const void* A, const void* B, void* C, void* stream);
+
 /* Clear(): release the context and its device buffers (NULL is a no-op).
  * The caller makes sure no enqueued work still uses them. */
 void dqip_release(dqip_ctx* ctx);
