@@ -48,6 +48,22 @@ __device__ __forceinline__ u2 f32x4_to_bf16x4(f4 v) {
     return r;
 }
 
+// ReLU on four packed bf16 values, after the rounding: max(x, 0) per 16-bit
+// signed integer (v_pk_max_i16). A bf16 with its sign bit set (a negative
+// value or -0) is a negative int16 and becomes +0, any other is kept; and
+// rounding to nearest even is monotone and maps negatives to negatives or
+// -0, so bf16(relu(v)) == relu(bf16(v)) bit for bit. Two packed operations
+// replace four fp32 max operations.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
+    uint32_t r;
+    asm("v_pk_max_i16 %0, %1, 0" : "=v"(r) : "v"(w));
+    return r;
+}
+__device__ __forceinline__ u2 relu_bf16x4(u2 p) {
+    const u2 r = {relu_bf16x2(p[0]), relu_bf16x2(p[1])};
+    return r;
+}
+
 // saturate(r + zp) into [lo, hi] for an integral float r (possibly +-inf):
 // clamping r to [lo - zp, hi - zp] first is exact, since both bounds are
 // small integers, and keeps the int conversion in range.

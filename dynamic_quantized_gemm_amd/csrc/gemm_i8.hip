@@ -134,11 +134,6 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     const int8_t* b_tile = Bp + (size_t)(tn * BNF) * KF * 1024;
     const int lofs = lane * 16;
     // fragment f of a step (f < AF: A, else B) at step t
-    auto frag_src = [&](int f, int t) -> const int8_t* {
-        const int8_t* base = f < AF ? a_tile : b_tile;
-        const int g = f < AF ? f : f - AF;
-        return base + ((size_t)(g / KS) * KF + (size_t)t * KS + g % KS) * 1024;
-    };
     const int nsteps = KF / KS;
 
     // row / column parameters of the tile (column vectors hold Np entries)
@@ -179,10 +174,22 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         else if constexpr (k == 2) return st2;
         else return st3;
     };
+    // A copy's source is a per-step scalar base (the tile panel moved to
+    // step t) plus a fixed 32-bit offset per copy slot (fragment row block
+    // and k half inside the panel, and the lane's 16 bytes): the step moves
+    // one base, not every address (fewer instructions between the MFMAs).
+    uint32_t voff[FPW];
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+        const int f = wave + i * NW;
+        const int g = f < AF ? f : f - AF;
+        voff[i] = (uint32_t)(((g / KS) * KF + g % KS) * 1024) + (uint32_t)lofs;
+    }
     auto copy = [&](int i, int t, int8_t* dst) {
         const int f = wave + i * NW;
         const int tc = min(t, nsteps - 1);
-        dq::copy16_to_lds(frag_src(f, tc) + lofs, dst + f * 1024);
+        const int8_t* base = (f < AF ? a_tile : b_tile) + (size_t)tc * (KS * 1024);
+        dq::copy16_to_lds(base + voff[i], dst + f * 1024);
     };
 #pragma unroll
     for (int i = 0; i < FPW; ++i) copy(i, 0, st0);
@@ -385,13 +392,16 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                         const dq::v4i v = {sum[0], sum[1], sum[2], sum[3]};
                         *reinterpret_cast<dq::v4i*>(dst) = v;
                     } else {
+                        // a ReLU with bf16 output is applied after the
+                        // rounding, on the packed pairs (dq::relu_bf16x4)
+                        constexpr bool kReluPacked = OUT == DQ_OUT_BF16 && ACT == DQ_ACT_RELU;
                         dq::f4 val;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             float v = (float)sum[e] * sA[u];
                             v = v * sB[e];
                             if (BIAS) v = v + bv[e];
-                            val[e] = activate<ACT>(v, ep.alpha);
+                            val[e] = kReluPacked ? v : activate<ACT>(v, ep.alpha);
                         }
                         if (Q8) {
                             uint32_t b[4];
@@ -413,7 +423,8 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                             *reinterpret_cast<uint32_t*>(dst) =
                                 ((packed & 0x7f7f7f7fu) + (yZ & 0x7f7f7f7fu)) ^ ((packed ^ yZ) & 0x80808080u);
                         } else if (OUT == DQ_OUT_BF16) {
-                            *reinterpret_cast<dq::u2*>(dst) = dq::f32x4_to_bf16x4(val);
+                            const dq::u2 pk = dq::f32x4_to_bf16x4(val);
+                            *reinterpret_cast<dq::u2*>(dst) = kReluPacked ? dq::relu_bf16x4(pk) : pk;
                         } else {
                             *reinterpret_cast<dq::f4*>(dst) = val;
                         }
