@@ -112,7 +112,6 @@ class Dqip:
         self.dq.dqip_release(self.h)
 
 
-GEMM_SOURCES = ("csrc/gemm_i8.hip", "csrc/dq_device.h", "csrc/dq_kernels.h")
 
 
 def source_digest(files):
@@ -154,33 +153,58 @@ def _counter_means(csv_path, counter, match):
     return list(vals.values())
 
 
-def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_match):
-    """profiles/traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE and
-    WRITE_SIZE of the GEMM (bench.py --quick) and of the plain 1 GiB copy
-    (bench.py --copy-calibration). Each GEMM counter is scaled by
-    copy bytes / what the same counter reads for the copy."""
+def write_counters(copy_fetch_csv, copy_write_csv, specs):
+    """Adds HBM-traffic records to profiles/traffic.json from rocprofv3 --pmc
+    FETCH_SIZE / WRITE_SIZE runs, each spec "label=kernel substring=fetch
+    csv=write csv=algorithmic bytes per dispatch=source,source,...". The
+    counters (KiB per dispatch) are scaled by what the same counters read for
+    the plain 1 GiB copy (--copy-calibration)."""
     n = 1 << 30
     big = lambda v: [x for x in v if x * 1024 > n / 2]  # the 1 GiB copies only
     cf = big(_counter_means(copy_fetch_csv, "FETCH_SIZE", "copyBuffer"))
     cw = big(_counter_means(copy_write_csv, "WRITE_SIZE", "copyBuffer"))
     f_scale = n / (1024 * sum(cf) / len(cf))
     w_scale = n / (1024 * sum(cw) / len(cw))
-    gf = _counter_means(fetch_csv, "FETCH_SIZE", kernel_match)
-    gw = _counter_means(write_csv, "WRITE_SIZE", kernel_match)
-    fetch = 1024 * sum(gf) / len(gf) * f_scale
-    write = 1024 * sum(gw) / len(gw) * w_scale
-    rec = {"gemm_i8": {
-        "kernel": kernel_match, "dispatches": [len(gf), len(gw)],
-        "fetch_bytes": round(fetch), "write_bytes": round(write),
-        "bytes_per_launch": round(fetch + write),
-        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
-        "copy_counter_kib": [round(sum(cf) / len(cf), 1), round(sum(cw) / len(cw), 1)],
-        "sources": list(GEMM_SOURCES), "source_sha256": source_digest(GEMM_SOURCES)}}
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+    for spec in specs:
+        label, match, fcsv, wcsv, alg, srcs = spec.split("=")
+        gf = _counter_means(fcsv, "FETCH_SIZE", match)
+        gw = _counter_means(wcsv, "WRITE_SIZE", match)
+        fetch = 1024 * sum(gf) / len(gf) * f_scale
+        write = 1024 * sum(gw) / len(gw) * w_scale
+        sources = [x for x in srcs.split(",") if x]
+        rec[label] = {"kernel": match, "dispatches": [len(gf), len(gw)],
+                      "fetch_bytes": round(fetch), "write_bytes": round(write),
+                      "bytes_per_launch": round(fetch + write), "algorithmic_bytes": int(alg),
+                      "traffic_over_algorithmic": round((fetch + write) / int(alg), 3),
+                      "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+                      "copy_counter_kib": [round(sum(cf) / len(cf), 1), round(sum(cw) / len(cw), 1)],
+                      "sources": sources, "source_sha256": source_digest(sources)}
+        print(json.dumps({label: rec[label]}))
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    print(json.dumps(rec["gemm_i8"]))
+
+
+def summarize_pmc(csv_path, match):
+    """Mean of every counter per dispatch of the kernels whose name contains
+    `match`, from a rocprofv3 --pmc counter_collection.csv (printed as JSON)."""
+    import csv
+
+    per = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if match in row["Kernel_Name"]:
+                key = (row["Counter_Name"], row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    print(json.dumps({k: {"mean": round(sum(v) / len(v), 1), "dispatches": len(v)} for k, v in out.items()}))
 
 
 def copy_calibration(torch, mib=1024, reps=10):
@@ -738,12 +762,20 @@ def main():
     ap.add_argument("--detail", metavar="PATH", help="also write every secondary record in full to PATH")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scales the HBM traffic counters)")
-    ap.add_argument("--write-traffic", nargs=4,
-                    metavar=("GEMM_FETCH_CSV", "GEMM_WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="no GPU: write profiles/traffic.json from rocprofv3 --pmc outputs")
+    ap.add_argument("--only", choices=["headline", "qdq", "qconv1x1", "lstm_input", "lstm_recurrent",
+                                       "dqip_8192", "probes"],
+                    help="run one workload only (for profiler runs); prints a short record, not the line")
+    ap.add_argument("--write-counters", nargs="+", metavar="ARG",
+                    help="no GPU: COPY_FETCH_CSV COPY_WRITE_CSV then specs "
+                         "label=kernel=fetch_csv=write_csv=algorithmic_bytes=sources")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("CSV", "KERNEL_SUBSTRING"),
+                    help="no GPU: mean of each counter per dispatch of the matching kernels")
     args = ap.parse_args()
-    if args.write_traffic:
-        write_traffic(*args.write_traffic, kernel_match="k_gemm<2, 2, 4, 4, 2, 1, 1, true, false>")
+    if args.write_counters:
+        write_counters(args.write_counters[0], args.write_counters[1], args.write_counters[2:])
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path, so --gpus "
@@ -761,6 +793,9 @@ def main():
         copy_calibration(torch)
         return
     dq.load()
+    if args.only:
+        run_only(args.only, dq, torch, W, args.steps)
+        return
 
     log("bench: generating the 4096^3 workload")
     case = W.dqip_large()
@@ -874,6 +909,28 @@ def main():
         with open(args.detail, "w") as f:
             json.dump({"secondary": secondary, "cpu_baseline": cpu, "achievable": ach}, f, indent=1)
     print(json.dumps(line), flush=True)
+
+
+def run_only(which, dq, torch, W, steps):
+    """One workload alone, `steps` calls after three warm-up calls (profiler
+    runs: every dispatch of the run is that workload's)."""
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    if which == "headline":
+        d = Dqip(dq, torch, W.dqip_large())
+        ms, ph = d.timed(torch, steps, 3)
+        d.release()
+        rec = {"us_per_forward": round(ms * 1e3, 2), "phase_us": [round(x * 1e3, 2) for x in ph]}
+    elif which == "qdq":
+        rec = bench_qdq(dq, torch, steps)
+    elif which == "qconv1x1":
+        rec = bench_qconv(dq, torch, steps)
+    elif which in ("lstm_input", "lstm_recurrent"):
+        rec = bench_dqip_case(dq, torch, W.dqip_lstm(recurrent=which == "lstm_recurrent"), steps, 3, flush)
+    elif which == "dqip_8192":
+        rec = bench_dqip_case(dq, torch, W.dqip_dynamic_b(), steps, 3, flush)
+    else:
+        rec = achievable(dq, torch, reps=steps)
+    print(json.dumps({"only": which, "record": rec}), flush=True)
 
 
 _KEEP = ("us_cold", "us_per_forward", "us_warm", "TOPS", "TOPS_cold", "TOPS_warm", "GBps_cold",
