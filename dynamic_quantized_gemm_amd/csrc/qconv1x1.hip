@@ -261,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1(
 constexpr int kPP = 32;          // pixels per item
 constexpr int kPersistentGroups = 512;
 constexpr int kYPitchP = 48;     // LDS bytes per staged output row (32 + 16)
+constexpr int kWPitch = 272;     // LDS bytes per staged weight row (256 + 16)
 
 // The raw bytes of an item: lane handles pixels p .. p+3 (p = p0 + 4 (tid % 8))
 // of channels 8 (tid / 8) .. + 7 (pad: bytes that become x^ = 0).
@@ -307,7 +308,7 @@ __device__ __forceinline__ void store_staged(const uint8_t* ysw, uint8_t* __rest
     }
 }
 
-template <bool XU8, bool WU8, bool YU8, bool XSUM, bool VEC, bool FULL>
+template <bool XU8, bool WU8, bool YU8, bool XSUM, bool VEC, bool FULL, bool WCOAL>
 __global__ __launch_bounds__(kThreads) void k_qconv1x1_p(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int C, int HW, int M,
     const float* __restrict__ x_scale_p, const uint8_t* __restrict__ x_zp_p,
@@ -318,6 +319,10 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1_p(
     __shared__ __attribute__((aligned(16))) int8_t xs0[(kKC / 32) * 1024];
     __shared__ __attribute__((aligned(16))) int8_t xs1[(kKC / 32) * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t ys[kMT * kYPitchP];
+    // weight staging (WCOAL): each wave's 32-row half of its 64 rows at a
+    // time, rows kWPitch bytes apart (256 + 16: the fragment reads of 16
+    // rows at one column then fall on 16 distinct 4-bank groups)
+    __shared__ __attribute__((aligned(16))) int8_t wst[WCOAL ? 4 * 32 * kWPitch : 16];
 
     constexpr uint32_t kXor = 0x80808080u;
     constexpr int kA = WU8 ? 128 : 0;
@@ -370,6 +375,39 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1_p(
     // weight fragments of the wave (channels mw0 + 32 jb + lane % 32), once
     v4i wf[2][kKC / 32];
     int32_t rsum[2] = {0, 0};
+    if (WCOAL) {
+        // all 256 input channels of all 64 rows exist (C == kKC, M == kMT):
+        // the wave's rows are 16 KiB of consecutive bytes, read as whole
+        // 1 KiB pieces per instruction (lane l: row 4 i + l / 16, bytes
+        // 16 (l % 16) ..), staged in LDS per 32-row half and read back in
+        // fragment order (row l % 32, bytes 32 kk + 16 (l / 32) ..)
+        int8_t* stw = wst + wave * 32 * kWPitch;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            v4i raw[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                raw[i] = *reinterpret_cast<const v4i*>(w + (size_t)(mw0 + 32 * jb) * kKC + 1024 * i + 16 * lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<v4i*>(stw + (4 * i + (lane >> 4)) * kWPitch + 16 * (lane & 15)) = raw[i];
+            dq::wave_lds_fence();
+#pragma unroll
+            for (int kk = 0; kk < kKC / 32; ++kk) {
+                v4i v = *reinterpret_cast<const v4i*>(stw + (lane & 31) * kWPitch + 32 * kk + 16 * (lane >> 5));
+                if (WU8) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] ^= (int)kXor;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rsum[jb] = __builtin_amdgcn_sdot4(v[e], 0x01010101, rsum[jb], false);
+                wf[jb][kk] = v;
+            }
+            // the next half overwrites the staging rows: every read of
+            // this half has completed first
+            dq::wave_lds_fence();
+        }
+    } else {
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
         const int m = mw0 + 32 * jb + (lane & 31);
@@ -397,6 +435,7 @@ __global__ __launch_bounds__(kThreads) void k_qconv1x1_p(
             for (int e = 0; e < 4; ++e) rsum[jb] = __builtin_amdgcn_sdot4(v[e], 0x01010101, rsum[jb], false);
             wf[jb][kk] = v;
         }
+    }
     }
 
     // per-channel and per-tensor constants of the requantization
@@ -595,12 +634,15 @@ extern "C" int qlinear_conv1x1(const void* x, dq_dtype x_type, int64_t N, int64_
         // FULL: all 256 channels and every pixel of every tile exist, so no
         // load or store is conditional
         const bool full = vec && M == kMT && HW % kPP == 0;
-#define DQ_P(XU, WU, YU, XS, V, F)                                                                         \
-    hipLaunchKernelGGL((k_qconv1x1_p<XU, WU, YU, XS, V, F>), dim3(groups), dim3(kThreads), 0, s, xb, wb, Ci, \
+        // whole weight rows read as 1 KiB pieces: every row has kKC bytes
+        const bool wcoal = wvec && C == kKC && M == kMT && (uintptr_t)w % 16 == 0;
+#define DQ_P(XU, WU, YU, XS, V, F, WC)                                                                         \
+    hipLaunchKernelGGL((k_qconv1x1_p<XU, WU, YU, XS, V, F, WC>), dim3(groups), dim3(kThreads), 0, s, xb, wb, Ci, \
                        HWi, Mi, x_scale, xz, w_scale, wz, wpc, y_scale, yz, bias, wvec, ni, nt, px, yb)
 #define DQ_PX(XU, WU, YU, XS) \
-    if (full) DQ_P(XU, WU, YU, XS, true, true); else if (vec) DQ_P(XU, WU, YU, XS, true, false); \
-    else DQ_P(XU, WU, YU, XS, false, false);
+    if (full && wcoal) DQ_P(XU, WU, YU, XS, true, true, true); \
+    else if (full) DQ_P(XU, WU, YU, XS, true, true, false); else if (vec) DQ_P(XU, WU, YU, XS, true, false, false); \
+    else DQ_P(XU, WU, YU, XS, false, false, false);
 #define DQ_PV(XU, WU, YU) \
     if (xsum) { DQ_PX(XU, WU, YU, true) } else { DQ_PX(XU, WU, YU, false) }
         const bool xu = x_type == DQ_U8, wu = w_type == DQ_U8, yu = y_type == DQ_U8;
