@@ -8,7 +8,9 @@ import ctypes as C
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdqip.so")
+# DQIP_LIB_PATH selects another build of the same library (the test suite's
+# sanitizer build of the host code); the default is the in-tree library
+LIB_PATH = os.environ.get("DQIP_LIB_PATH") or os.path.join(PKG, "libdqip.so")
 
 DQ_F32, DQ_BF16, DQ_I8, DQ_U8, DQ_F16 = 0, 1, 2, 3, 4
 DQ_ACT_IDENTITY, DQ_ACT_RELU, DQ_ACT_LEAKY_RELU = 0, 1, 2

@@ -27,15 +27,22 @@
 
 #ifdef __cplusplus
 extern "C" {
+/* The enumerations are int-sized in C. Compiled as C++ they get int as
+ * their fixed underlying type, so that any int a C caller passes (an
+ * invalid code included, which the calls reject with an error) is a valid
+ * value of the parameter's type. */
+#define DQ_ENUM_INT : int
+#else
+#define DQ_ENUM_INT
 #endif
 
 /* Element types: fp32, bf16 (raw 16-bit patterns), int8, uint8, fp16 (IEEE
  * binary16 bit patterns). */
-typedef enum { DQ_F32 = 0, DQ_BF16 = 1, DQ_I8 = 2, DQ_U8 = 3, DQ_F16 = 4 } dq_dtype;
+typedef enum DQ_ENUM_INT { DQ_F32 = 0, DQ_BF16 = 1, DQ_I8 = 2, DQ_U8 = 3, DQ_F16 = 4 } dq_dtype;
 
 /* Activations applied after dequantization and bias. Leaky ReLU takes its
  * slope from params[0] of dqip_set_params (default 0.01). */
-typedef enum { DQ_ACT_IDENTITY = 0, DQ_ACT_RELU = 1, DQ_ACT_LEAKY_RELU = 2 } dq_act;
+typedef enum DQ_ENUM_INT { DQ_ACT_IDENTITY = 0, DQ_ACT_RELU = 1, DQ_ACT_LEAKY_RELU = 2 } dq_act;
 
 enum {
     DQ_OK = 0,
@@ -548,10 +555,10 @@ int qlinear_concat(int n_inputs, const void* const* xs, const int64_t* shapes, i
  * ---------------------------------------------------------------------- */
 #define DQ_LSTM_HIDDEN_MAX 4096
 
-typedef enum { DQ_LSTM_FORWARD = 0, DQ_LSTM_REVERSE = 1, DQ_LSTM_BIDIRECTIONAL = 2 } dq_lstm_direction;
+typedef enum DQ_ENUM_INT { DQ_LSTM_FORWARD = 0, DQ_LSTM_REVERSE = 1, DQ_LSTM_BIDIRECTIONAL = 2 } dq_lstm_direction;
 
 /* The ONNX RNN activation functions. */
-typedef enum {
+typedef enum DQ_ENUM_INT {
     DQ_RNN_SIGMOID = 0,
     DQ_RNN_TANH = 1,
     DQ_RNN_RELU = 2,

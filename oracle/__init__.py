@@ -30,10 +30,14 @@ def lib() -> C.CDLL:
     or older than oracle.c."""
     global _lib
     if _lib is None:
-        if (not os.path.exists(_build.LIB)
-                or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
-            _build.build()
-        L = C.CDLL(_build.LIB)
+        # DQ_ORACLE_LIB: another build of oracle.c (the test suite's
+        # sanitizer build); else the in-tree library, rebuilt when stale
+        path = os.environ.get("DQ_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build()
+        L = C.CDLL(path)
         vp, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
         L.oracle_bf16_to_f32.argtypes = [C.c_uint16]
         L.oracle_bf16_to_f32.restype = C.c_float
