@@ -17,19 +17,18 @@
 //   activation; store fp32, bf16 (round to nearest even) or, for
 //   inspection, the int32 sum itself.
 //
-// Operands arrive packed in MFMA fragment order (1 KiB = 32 rows x 32 k,
-// laid out exactly as v_mfma_i32_32x32x32_i8 takes them: lane l holds 16
-// codes of row l % 32), so
+// Operands arrive packed in fragment order (1 KiB = 32 rows x 32 k, lane l
+// of a wave holding 16 codes of row l % 32, k half l / 32), so
 //  - every global -> LDS copy moves one contiguous 1 KiB per wave, 16 bytes
 //    per lane, and lands in LDS in the same order,
-//  - every LDS read is lane-contiguous (ds_read_b128, no bank conflicts, no
-//    swizzle arithmetic),
+//  - every LDS read is one 16-byte piece per lane, 256 contiguous bytes per
+//    16 lanes (ds_read_b128, no bank conflicts, no swizzle arithmetic),
 //  - no bounds checks are needed: M, N are padded to 256 and K to 256.
 //
 // Kernel k_gemm<WM, WN, FM, FN, KS>: a workgroup of WM x WN waves computes a
-// (WM*FM*32) x (WN*FN*32) tile of C; each wave owns FM x FN 32x32 blocks
-// (16 int32 accumulators per lane per block). K advances 32*KS = 64 per
-// step. The fragments of a step go global -> LDS directly (gfx950
+// (WM*FM*32) x (WN*FN*32) tile of C; each wave owns 2FM x 2FN blocks of
+// 16x16, multiplied with v_mfma_i32_16x16x64_i8 (4 int32 accumulators per
+// lane per block). K advances 32*KS = 64 per step. The fragments of a step go global -> LDS directly (gfx950
 // global_load_lds_dwordx4, no trip through VGPRs) into a ring of four stage
 // buffers: while step t is multiplied out of its stage, the copies for steps
 // t+1 .. t+3 are in flight, so a copy has three steps of matrix work to
@@ -37,14 +36,18 @@
 // kernel waits for them itself (s_waitcnt vmcnt with the count of copies
 // still allowed in flight) and crosses one bare s_barrier per step. Within a
 // step the copies and the next sub-step's LDS reads are interleaved one by
-// one with the MFMAs (scheduling groups), so the vector memory path, the LDS
+// one with the MFMAs (in program order), so the vector memory path, the LDS
 // and the matrix cores work at the same time. The largest configuration,
 // 256x256 with four 128x128 waves, keeps 256 accumulator registers per lane
-// in AGPRs and multiplies for 1024 MFMA cycles per wave per step.
+// in AGPRs and issues 64 MFMAs per wave per step. Of gfx950's two int8 MFMA
+// shapes (32x32x32 and 16x16x64, the same operations per cycle) the 16x16x64
+// one moves fewer accumulator bits per operation; on this power-limited part
+// it runs at a higher clock (measured: an MFMA-only loop reaches 3.46 POP/s
+// against 2.9-3.2 for 32x32x32, random operands).
 //
-// The MFMA's first operand is the B fragment and its second the A fragment,
-// so the accumulator block is C^T: lane l holds row (l % 32) of the block and,
-// in accumulators 4g..4g+3, the four adjacent columns 8g + 4(l/32) + 0..3.
+// The MFMA's first operand is the B block and its second the A block, so
+// the accumulator block is C^T: lane l holds row (l % 16) of the block and,
+// in its four accumulators, the adjacent columns 4(l/16) + 0..3.
 // Epilogue: the tile's row and column parameters are staged in LDS when the
 // kernel starts; after the main loop each wave owns one quarter of the stage
 // memory. Its rows are finished in passes of as many 32-row strips as fit
@@ -198,78 +201,115 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
 #pragma unroll
     for (int i = 0; i < FPW; ++i) copy(i, 2, st2);
 
-    // a tile this large keeps its accumulators in AGPRs (16 registers per
-    // 32x32 block): read them one by one in the epilogue
-    constexpr bool kAgpr = FM * FN * 16 > 128;
-    dq::v16i acc[FM][FN];
+    // Each wave multiplies 2FM x 2FN blocks of 16x16 with
+    // v_mfma_i32_16x16x64_i8, 4 accumulators per lane per block, held in
+    // AGPRs and read one by one in the epilogue (dq::acc_read).
+    constexpr int HM = 2 * FM, HN = 2 * FN;  // 16-row / 16-column blocks per wave
+    dq::v4i acc[HM][HN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < HM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+        for (int j = 0; j < HN; ++j) acc[i][j] = dq::v4i{0, 0, 0, 0};
 
-    // Operand fragments of a sub-step (two register sets: one feeds the
-    // MFMAs while the other is being read).
-    static_assert(KS == 2, "a step is two 32-deep sub-steps");
-    dq::v4i fa[2][FM], fb[2][FN];
-    auto read = [&](const int8_t* L, int kk, int set) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            fa[set][i] = *reinterpret_cast<const dq::v4i*>(L + ((wm * FM + i) * KS + kk) * 1024 + lofs);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            fb[set][j] = *reinterpret_cast<const dq::v4i*>(L + (AF + (wn * FN + j) * KS + kk) * 1024 + lofs);
+    // Operand blocks. The 16x16x64 MFMA takes, in lane l, 16 codes of row
+    // (or column) l % 16 from k group l / 16 of a 64-deep step. Those 16
+    // codes sit, in the packed 32x32 fragments, in the 16-byte piece of
+    // packed lane (l % 16) + 16 h + 32 (g % 2) of the step's 32-deep
+    // fragment g / 2 (h: which half of the 32 rows). A and B are packed
+    // alike and read through the same map, so every k group meets the same
+    // k values in both operands: the integer sum is the same sum in another
+    // order (exact). Each lane still reads one 16-byte piece per block, and
+    // each group of 16 lanes a contiguous 256 bytes.
+    static_assert(KS == 2, "a step is two 32-deep packed fragments");
+    const int hofs = ((lane >> 5) & 1) * 1024 + ((lane >> 4) & 1) * 512 + (lane & 15) * 16;
+    auto rdA = [&](const int8_t* L, int hb) {
+        return *reinterpret_cast<const dq::v4i*>(L + (wm * FM + (hb >> 1)) * KS * 1024 + (hb & 1) * 256 + hofs);
     };
-    // One sub-step: the MFMAs on register set `set`, with FPK copies of step
-    // `ahead` (copy slots q0 ..) and the reads of (Lr, kr) into the other
-    // set interleaved one by one: one MFMA, then one copy and one read, ...
-    auto half = [&](int set, int q0, int ahead, int8_t* dst, const int8_t* Lr, int kr) {
-#pragma unroll
-        for (int q = 0; q < FPK; ++q)
-            if (q0 + q < FPW) copy(q0 + q, ahead, dst);
-        read(Lr, kr, set ^ 1);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int m = 0; m < FM * FN; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < FPK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            if (m < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    auto rdB = [&](const int8_t* L, int hb) {
+        return *reinterpret_cast<const dq::v4i*>(L + (AF + (wn * FN + (hb >> 1)) * KS) * 1024 + (hb & 1) * 256 + hofs);
     };
+    // The MFMA accumulates in place (dst = srcC). It is written as inline
+    // assembly: with 4-register accumulators the compiler's builtin form
+    // lets the register allocator move whole accumulator sets between
+    // AGPRs and VGPRs inside the loop (hundreds of moves a step). Hazards
+    // the compiler therefore does not see:
+    //  (1) the zeroing writes (VALU) before the first MFMA reads them as
+    //      srcC: an empty volatile statement per block pins the zeros in
+    //      their AGPRs, then a drain of more wait states than the ISA asks
+    //      for a VALU write followed by an MFMA srcC read;
+    //  (2) the epilogue's reads of the results: mfma_result_drain after the
+    //      loop.
+    // The operand VGPRs come from LDS reads, whose completion the
+    // compiler's waitcnt pass tracks for inline-assembly operands as for
+    // any other use; nothing but these MFMAs writes the accumulators, and
+    // consecutive updates of one block are a whole sub-step apart.
+    auto mfma = [](dq::v4i& c, const dq::v4i& b, const dq::v4i& a) {
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+    };
+#pragma unroll
+    for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < HN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    dq::mfma_result_drain();
 
-    // Step t multiplies stage L = t % 4; its first sub-step's fragments were
-    // read during step t - 1. The one barrier of the step sits between its
-    // two sub-steps: before it, this wave's reads of L have completed
-    // (lgkmcnt 0) and its copies of step t + 1 have landed (at most the
-    // copies of step t + 2 and the first half of step t + 3's are still in
-    // flight); after it, every wave's copies of step t + 1 are visible, so
-    // the second sub-step can read step t + 1's first fragments, and no wave
-    // reads L any more, so the copies of step t + 4, issued from step t + 1
-    // on, may overwrite it. No LDS read waits behind a barrier.
+    // A step is two sub-steps: the first multiplies the wave's upper FM row
+    // blocks (faL) by all its column blocks, the second the lower FM
+    // (faH). B blocks live for a whole step, in two register sets that
+    // alternate between steps. The first sub-step reads faH of the same
+    // step; the second, after the step's barrier, reads faL and the other B
+    // set of the next step. Within a sub-step the copies and reads are
+    // interleaved one by one with the MFMAs, in program order (the inline
+    // MFMAs are volatile, so the compiler keeps the order): one MFMA, then
+    // one copy and one read, ...
+    dq::v4i faL[FM], faH[FM], fb[2][HN];
+    // slots of a sub-step: its MFMAs, or more where a small tile has more
+    // copies or reads than MFMAs
+    constexpr int kSlots = FM * HN > FPK ? (FM * HN > FM + HN ? FM * HN : FM + HN)
+                                         : (FPK > FM + HN ? FPK : FM + HN);
+
+    // Step t multiplies stage L = t % 4; its faL and B blocks were read
+    // during step t - 1. The one barrier of the step sits between its two
+    // sub-steps: before it, this wave's reads of L have completed (lgkmcnt
+    // 0) and its copies of step t + 1 have landed (at most the copies of step
+    // t + 2 and the first half of step t + 3's are still in flight); after
+    // it, every wave's copies of step t + 1 are visible, so the second
+    // sub-step can read step t + 1's blocks, and no wave reads L any more,
+    // so the copies of step t + 4, issued from step t + 1 on, may overwrite
+    // it. No LDS read waits behind a barrier.
     // Not __syncthreads(): its fence would wait for every outstanding copy.
     auto one = [&](auto S, int t) {
+        constexpr int c = decltype(S)::value & 1;  // B register set of step t
         using SN = std::integral_constant<int, decltype(S)::value + 1>;
         using SA = std::integral_constant<int, decltype(S)::value + NSTAGE - 1>;
         const int8_t* L = stage(S);
+        const int8_t* Ln = stage(SN{});
         int8_t* dst = stage(SA{});
-        half(0, 0, t + NSTAGE - 1, dst, L, 1);
+#pragma unroll
+        for (int m = 0; m < kSlots; ++m) {
+            if (m < FM * HN) mfma(acc[m / HN][m % HN], fb[c][m % HN], faL[m / HN]);
+            if (m < FPK && m < FPW) copy(m, t + NSTAGE - 1, dst);
+            if (m < FM) faH[m] = rdA(L, FM + m);
+        }
         dq::wait_vmcnt_lgkm0<FPW + FPK>();
         dq::lds_barrier();
-        half(1, FPK, t + NSTAGE - 1, dst, stage(SN{}), 0);
+#pragma unroll
+        for (int m = 0; m < kSlots; ++m) {
+            if (m < FM * HN) mfma(acc[FM + m / HN][m % HN], fb[c][m % HN], faH[m / HN]);
+            if (m < FPK && FPK + m < FPW) copy(FPK + m, t + NSTAGE - 1, dst);
+            if (m < FM) faL[m] = rdA(Ln, m);
+            else if (m < FM + HN) fb[c ^ 1][m - FM] = rdB(Ln, m - FM);
+        }
     };
-    // step 0's copies, then its first fragments
+    // step 0's copies, then its first blocks
     dq::wait_vmcnt_lgkm0<2 * FPW>();
     dq::lds_barrier();
-    read(st0, 0, 0);
-    // unrolled by the ring size so every stage reference is static (the
-    // step count is a multiple of 4: Kp is a multiple of 256); the last
-    // step's look-ahead reads a re-loaded stage and is never used
+#pragma unroll
+    for (int i = 0; i < FM; ++i) faL[i] = rdA(st0, i);
+#pragma unroll
+    for (int j = 0; j < HN; ++j) fb[0][j] = rdB(st0, j);
+    // unrolled by the ring size so every stage reference and register set is
+    // static (the step count is a multiple of 4: Kp is a multiple of 256);
+    // the last step's look-ahead reads a re-loaded stage and is never used
     for (int t = 0; t < nsteps; t += NSTAGE) {
         one(std::integral_constant<int, 0>{}, t);
         one(std::integral_constant<int, 1>{}, t + 1);
@@ -298,7 +338,9 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     static_assert(SPP >= 1 && FM % SPP == 0 && NW <= NSTAGE, "epilogue strips do not fit in LDS");
     int8_t* region = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
     __syncthreads();  // every wave is done reading the stage buffers
-    const int rs = lane & 31;  // row inside a strip
+    // in a 16x16 accumulator block lane l holds row l % 16 and, in its four
+    // accumulators, the adjacent columns 4 (l / 16) + 0..3
+    const int rq = lane & 15;
     const int col0 = n0 + wn * FN * 32;
     // requantization of an 8-bit output: y = sat(rne(val / y_scale) + y_zp),
     // with the corrected quotient where the scale allows it (as the
@@ -323,23 +365,26 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         // rate; a 32-bit product would take the quarter-rate 64-bit multiply-
         // add): |128 - zeroA| <= 128 and -2^23 <= colsum < 2^23 for K <= 65536,
         // so the product is exact and the wrapping add gives the exact sum
-        int za[SPP], rb[SPP], cr[SPP];
-        float sA[SPP];
+        // the lane's two rows of each strip: 16 h + rq, h = 0, 1
+        int za[SPP][2], rb[SPP][2], cr[SPP][2];
+        float sA[SPP][2];
 #pragma unroll
-        for (int u = 0; u < SPP; ++u) {
-            const int rt = (wm * FM + p0 + u) * 32 + rs;  // tile row
-            za[u] = 128 - s_za[rt];
-            rb[u] = EXT ? s_rb[rt] : 0;
-            cr[u] = EXT ? s_crow[rt] : 0;
-            sA[u] = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
-        }
-        // column groups jg = 4 j + g; each group's parameters are read from
-        // LDS one group ahead, so their latency hides behind the previous
-        // group's arithmetic
+        for (int u = 0; u < SPP; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rt = (wm * FM + p0 + u) * 32 + 16 * h + rq;  // tile row
+                za[u][h] = 128 - s_za[rt];
+                rb[u][h] = EXT ? s_rb[rt] : 0;
+                cr[u][h] = EXT ? s_crow[rt] : 0;
+                sA[u][h] = OUT == DQ_OUT_ACC ? 0.0f : s_sa[rt];
+            }
+        // groups jg = 2 jb + h: column block jb, row half h; each column
+        // block's parameters are read from LDS one block ahead, so their
+        // latency hides behind the previous block's arithmetic
         dq::v4i csv[2], zbv[2], ccv[2];
         dq::f4 sBv[2], bvv[2];
-        auto params = [&](int jg, int set) {
-            const int ct = wn * FN * 32 + (jg >> 2) * 32 + 8 * (jg & 3) + 4 * (lane >> 5);  // tile column
+        auto params = [&](int jb, int set) {
+            const int ct = wn * FN * 32 + jb * 16 + 4 * (lane >> 4);  // tile column
             csv[set] = *reinterpret_cast<const dq::v4i*>(&s_cs[ct]);
             if (EXT) {
                 zbv[set] = *reinterpret_cast<const dq::v4i*>(&s_zb[ct]);
@@ -350,11 +395,12 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         };
         params(0, 0);
 #pragma clang loop unroll(full)
-        for (int jg = 0; jg < FN * 4; ++jg) {
-            const int j = jg >> 2, g = jg & 3, set = jg & 1;
-            if (jg + 1 < FN * 4) params(jg + 1, set ^ 1);
+        for (int jg = 0; jg < HN * 2; ++jg) {
+            const int jb = jg >> 1, h = jg & 1, set = jb & 1;
+            if (h == 0 && jb + 1 < HN) params(jb + 1, set ^ 1);
             {
-                const int cs_ = j * 32 + 8 * g + 4 * (lane >> 5);  // strip column
+                const int rs = 16 * h + rq;                  // strip row
+                const int cs_ = jb * 16 + 4 * (lane >> 4);  // strip column
                 const dq::v4i cs = csv[set];
                 dq::f4 sB = {0.0f, 0.0f, 0.0f, 0.0f}, bv = {0.0f, 0.0f, 0.0f, 0.0f};
                 if (OUT != DQ_OUT_ACC) sB = sBv[set];
@@ -365,9 +411,8 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                     int32_t sum[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        sum[e] = (int32_t)((uint32_t)(kAgpr ? dq::acc_read(acc[p0 + u][j][4 * g + e])
-                                                             : acc[p0 + u][j][4 * g + e]) +
-                                           (uint32_t)__mul24(za[u], cs[e]));
+                        sum[e] = (int32_t)((uint32_t)dq::acc_read(acc[2 * (p0 + u) + h][jb][e]) +
+                                           (uint32_t)__mul24(za[u][h], cs[e]));
                     if (EXT) {
                         // B zero points: + rowsumA[i] * zb[j], where rowsumA holds
                         // sum_k A^[i,k] + K * (shift - a_zp), |.| <= 255 K < 2^23
@@ -378,8 +423,8 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                         const int row = min(m0 + (wm * FM + p0 + u) * 32 + rs, M - 1);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            sum[e] = (int32_t)((uint32_t)sum[e] + (uint32_t)__mul24(rb[u], zb[e]) +
-                                               (uint32_t)cr[u] + (uint32_t)cc[e]);
+                            sum[e] = (int32_t)((uint32_t)sum[e] + (uint32_t)__mul24(rb[u][h], zb[e]) +
+                                               (uint32_t)cr[u][h] + (uint32_t)cc[e]);
                             if (ep.c_mode == 3) {
                                 const int col = min(col0 + cs_ + e, N - 1);
                                 sum[e] = (int32_t)((uint32_t)sum[e] +
@@ -398,7 +443,7 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
                         dq::f4 val;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            float v = (float)sum[e] * sA[u];
+                            float v = (float)sum[e] * sA[u][h];
                             v = v * sB[e];
                             if (BIAS) v = v + bv[e];
                             val[e] = kReluPacked ? v : activate<ACT>(v, ep.alpha);
@@ -565,8 +610,8 @@ int dq_launch_gemm(const int8_t* Ap, const int8_t* Bp, int M, int N, int Kp, con
 
 const char* dq_gemm_info(int M, int N, int) {
     switch (pick(M, N)) {
-        case 2: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 256x256, k-step 64 (4 waves x 128x128, accumulators in AGPRs), 4-stage global->LDS DMA ring, fused dequant epilogue";
-        case 1: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 128x128, k-step 64 (4 waves x 64x64), 4-stage global->LDS DMA ring, fused dequant epilogue";
-        default: return "gemm_i8 v_mfma_i32_32x32x32_i8 tile 32x32, k-step 64 (1 wave), 4-stage global->LDS DMA ring, fused dequant epilogue";
+        case 2: return "gemm_i8 v_mfma_i32_16x16x64_i8 tile 256x256, k-step 64 (4 waves x 128x128, accumulators in AGPRs), 4-stage global->LDS DMA ring, fused dequant epilogue";
+        case 1: return "gemm_i8 v_mfma_i32_16x16x64_i8 tile 128x128, k-step 64 (4 waves x 64x64), 4-stage global->LDS DMA ring, fused dequant epilogue";
+        default: return "gemm_i8 v_mfma_i32_16x16x64_i8 tile 32x32, k-step 64 (1 wave), 4-stage global->LDS DMA ring, fused dequant epilogue";
     }
 }
