@@ -284,9 +284,14 @@ def achievable(dq, torch, reps=5):
     ops = float(wg) * 4 * iters * 32 * 65536
     g = torch.Generator(device="cpu").manual_seed(0)
     rnd = torch.randint(-128, 128, (65536,), generator=g, dtype=torch.int8).cuda()
-    for name, buf in (("random", rnd), ("zero", torch.zeros(65536, dtype=torch.int8, device="cuda"))):
-        ms = med_ms(lambda: dq.dq_probe_mfma_loop(buf, iters, wg, sink))
-        out[f"mfma_loop_TOPS_{name}_operands"] = round(ops / (ms / 1e3) / 1e12, 1)
+    zero = torch.zeros(65536, dtype=torch.int8, device="cuda")
+    # the GEMM's instruction (16x16x64) with random and zero operands, and
+    # the 32x32x32 shape with random operands for comparison
+    for key, shape, buf in (("mfma_loop_TOPS_random_operands", 16, rnd),
+                            ("mfma_loop_TOPS_zero_operands", 16, zero),
+                            ("mfma32_loop_TOPS_random_operands", 32, rnd)):
+        ms = med_ms(lambda: dq.dq_probe_mfma_loop(buf, shape, iters, wg, sink))
+        out[key] = round(ops / (ms / 1e3) / 1e12, 1)
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -295,9 +300,9 @@ def achievable(dq, torch, reps=5):
     out["copy_frac_of_8TBps"] = round(2.0 * n / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 3)
     del src, dst
     out["mfma_loop_frac_of_5POPS_random"] = round(out["mfma_loop_TOPS_random_operands"] / INT8_PEAK_TOPS, 3)
-    out["how"] = (f"mfma: {wg} workgroups x 4 waves, each {iters} x 32 v_mfma_i32_32x32x32_i8 on register "
-                  f"operands (two alternating sets); copy: 1 GiB, four 16 B non-temporal loads a lane in flight; "
-                  f"median of {reps} launches")
+    out["how"] = (f"mfma: {wg} workgroups x 4 waves, each {iters} x 64 v_mfma_i32_16x16x64_i8 (the GEMM's "
+                  f"instruction; mfma32: 32 v_mfma_i32_32x32x32_i8) on register operands (two alternating "
+                  f"sets); copy: 1 GiB, four 16 B non-temporal loads a lane in flight; median of {reps} launches")
     return out
 
 
@@ -763,7 +768,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scales the HBM traffic counters)")
     ap.add_argument("--only", choices=["headline", "qdq", "qconv1x1", "lstm_input", "lstm_recurrent",
-                                       "dqip_8192", "probes"],
+                                       "dqip_8192", "mitf", "dqmm", "qgemm", "elementwise", "qconv_general",
+                                       "lstm", "probes"],
                     help="run one workload only (for profiler runs); prints a short record, not the line")
     ap.add_argument("--write-counters", nargs="+", metavar="ARG",
                     help="no GPU: COPY_FETCH_CSV COPY_WRITE_CSV then specs "
@@ -866,6 +872,8 @@ def main():
     # the metric's second half and the context of the first, also inside
     # `roofline` (a record every reader of the line keeps whole)
     roofline["achievable"] = {k: v for k, v in ach.items() if k != "how"}
+    roofline["achievable"]["gemm_frac_of_mfma_loop_random"] = round(
+        roofline["achieved"] / ach["mfma_loop_TOPS_random_operands"], 3)
     qdq = None
     if "qdq" in secondary:
         qq, dd = secondary["qdq"]["quantize"], secondary["qdq"]["dequantize"]
@@ -928,6 +936,14 @@ def run_only(which, dq, torch, W, steps):
         rec = bench_dqip_case(dq, torch, W.dqip_lstm(recurrent=which == "lstm_recurrent"), steps, 3, flush)
     elif which == "dqip_8192":
         rec = bench_dqip_case(dq, torch, W.dqip_dynamic_b(), steps, 3, flush)
+    elif which in ("mitf", "dqmm", "qgemm"):
+        rec = bench_qgemm(dq, torch, which, steps, flush)
+    elif which == "elementwise":
+        rec = bench_elementwise(dq, torch, steps, flush)
+    elif which == "qconv_general":
+        rec = bench_qconv_general(dq, torch, steps, flush)
+    elif which == "lstm":
+        rec = bench_lstm(dq, torch, steps, flush)
     else:
         rec = achievable(dq, torch, reps=steps)
     print(json.dumps({"only": which, "record": rec}), flush=True)

@@ -53,7 +53,7 @@ _SIGNATURES = {
     "dqip_forward_accumulators": (C.c_int, [C.c_void_p] * 6),
     "dqip_profile_begin": (C.c_int, [C.c_void_p, C.c_int]),
     "dqip_profile_end": (C.c_int, [C.c_void_p, C.POINTER(C.c_float), C.POINTER(C.c_int)]),
-    "dq_probe_mfma_loop": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
+    "dq_probe_mfma_loop": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
     "dq_probe_copy": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlinear_quantize": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
                                    C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
@@ -312,10 +312,10 @@ def dqip_profile_end(ctx):
 
 # ------------------------------------------------------ measurement probes
 
-def dq_probe_mfma_loop(operands, iters, workgroups, sink, stream=None):
-    """operands: >= 64 KiB device tensor; sink: >= workgroups * 256 int32."""
+def dq_probe_mfma_loop(operands, shape, iters, workgroups, sink, stream=None):
+    """operands: >= 64 KiB device tensor; shape 16 or 32; sink: >= workgroups * 256 int32."""
     w = "dq_probe_mfma_loop"
-    _check(load().dq_probe_mfma_loop(_ptr(operands, w, 65536), int(iters), int(workgroups),
+    _check(load().dq_probe_mfma_loop(_ptr(operands, w, 65536), int(shape), int(iters), int(workgroups),
                                      _ptr(sink, w, 1024 * int(workgroups)), _stream(stream)), w)
 
 

@@ -492,7 +492,13 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
             if (row < M && col < N) {
                 int8_t* C = reinterpret_cast<int8_t*>(ep.C) + ((size_t)row * N + col) * OB;
                 if (vec_store && col + EPC <= N) {
-                    *reinterpret_cast<dq::v4i*>(C) = v;
+                    // streaming store: C is written once and not read back
+                    // here, and a launch's C (tens of MiB) is far larger than
+                    // an XCD's L2; kept out of L2, it does not have to be
+                    // written back when the kernel ends (measured: 4096 x
+                    // 2048 x 512 fp32 C 13.7 -> 13.0 us, 4096^3 bf16 C
+                    // 55.8 -> 54.9 us)
+                    __builtin_nontemporal_store(v, reinterpret_cast<dq::v4i*>(C));
                 } else {
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) {

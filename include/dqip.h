@@ -203,17 +203,21 @@ int dqip_profile_end(dqip_ctx* ctx, float* ms, int* calls);
  * kernel on `stream` (asynchronous; the caller times it, e.g. with events).
  *
  * dq_probe_mfma_loop: `workgroups` workgroups of 4 waves; each wave keeps
- * 16 int32 32x32 accumulator blocks (the GEMM's 128x128 wave tile) and runs
- * `iters` iterations of 32 v_mfma_i32_32x32x32_i8 (2 * 32*32*32 ops each)
- * on register operands only, alternating two operand sets taken from
- * `operands` (device, at least 65536 bytes: random codes, or zeros). Total
- * work: workgroups * 4 * iters * 32 * 65536 int8 ops. sink (device, at
- * least workgroups * 256 int32) receives one checksum per lane.
+ * the int32 accumulators of a 128x128 tile (the GEMM's wave tile) and runs
+ * `iters` iterations on register operands only, alternating two operand
+ * sets taken from `operands` (device, at least 65536 bytes: random codes,
+ * or zeros). shape 32: 16 blocks of 32x32, 32 v_mfma_i32_32x32x32_i8 an
+ * iteration; shape 16: 64 blocks of 16x16, 64 v_mfma_i32_16x16x64_i8 an
+ * iteration (the GEMM's instruction). Either way an iteration is
+ * 32 * 65536 int8 ops: total workgroups * 4 * iters * 32 * 65536. sink
+ * (device, at least workgroups * 256 int32) receives one checksum per
+ * lane.
  * dq_probe_copy: copies `bytes` (multiple of 16) from src to dst (device,
  * 16-byte aligned, not overlapping): 16 KiB per workgroup of 256 threads,
  * each thread's four 16-byte non-temporal loads issued before its stores.
  * Errors: DQ_ERR_ARG, DQ_ERR_HIP. */
-int dq_probe_mfma_loop(const void* operands, int iters, int workgroups, int32_t* sink, void* stream);
+int dq_probe_mfma_loop(const void* operands, int shape, int iters, int workgroups, int32_t* sink,
+                       void* stream);
 int dq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* ------------------------------------------------------------------------
