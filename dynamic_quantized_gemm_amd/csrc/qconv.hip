@@ -66,6 +66,10 @@ struct ConvShape {
     int ncol;  // patch columns (a multiple of 4)
     int mtiles;
     dq::FastDiv ow_div;
+    // depthwise planes (k_qconv_dw): padded plane rows x columns, output
+    // strips of four pixels per row
+    int hp, wp, spr;
+    dq::FastDiv spr_div, w_div;
 };
 
 // Byte offset of w^[row][tap t][channel c] in the packed weights: 1 KiB
@@ -92,6 +96,8 @@ struct ConvArgs {
     uint8_t* y;
     uint32_t xflip;       // 0x80808080 for a uint8 x
     int kA, kB, x_u8, y_u8, vecx, vecy;
+    int vecy4;            // y 4-byte aligned and OW % 4 == 0 (k_qconv_dw's word stores)
+    int vecx_plane;       // x 4-byte aligned and H W % 4 == 0 (k_qconv_dw's word loads)
     int y_lo, y_hi;       // y's saturation range
     // split reduction: blockIdx.z = image * nsplit + split, each split walks
     // cps chunks and leaves int32 partial sums for k_qconv_reduce
@@ -501,6 +507,162 @@ __global__ __launch_bounds__(256) void k_qconv_direct(ConvShape sh, ConvArgs a) 
     a.y[((size_t)n * sh.M + m) * sh.P + p] = (uint8_t)code;
 }
 
+// Depthwise (one input and one output channel a group): a workgroup per
+// (image, channel) plane. The plane's x - x_zp (int16, exact) is staged in
+// LDS inside a border of zeros (a padded input is a real 0, so pads add
+// nothing), the channel's tap weights w - w_zp[m] sit in LDS too; each
+// thread then makes four adjacent outputs of a row at a time,
+// acc = sum (w - w_zp)(x - x_zp) + bias in 24-bit multiply-adds (|terms| <
+// 2^16, at most 1024 taps), and requantizes them as the other kernels do.
+// KS3 specializes the 3x3 kernel at stride and dilation 1, where the six
+// input columns of a strip's row are read once.
+typedef short s2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ s2 as_s2(uint32_t v) { return __builtin_bit_cast(s2, v); }
+
+constexpr int kDwLdsMax = 60 * 1024;  // dynamic LDS of the staged plane (with the 4 KiB of weights: 64 KiB)
+
+template <bool KS3>
+__global__ __launch_bounds__(256) void k_qconv_dw(ConvShape sh, ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) int16_t xs[];
+    __shared__ int32_t wsh[kTapMax];
+    const int tid = threadIdx.x;
+    const int m = blockIdx.x, n = blockIdx.y;
+    const int Wp = sh.wp;
+    // the staged plane and its slack (the last strip of a row may read up
+    // to 3 sw columns past the row, into the next one or the slack)
+    const int nel = sh.hp * Wp + 3 * sh.sw + 1;
+    for (int i = tid; i < (nel + 1) >> 1; i += 256) reinterpret_cast<int32_t*>(xs)[i] = 0;
+    const int8_t* wr = a.wp + wpos(m * sh.Mgp, 0, 0, sh.Tp, sh.Kc);
+    const size_t tstride = (size_t)(sh.Kc >> 5) << 10;
+    const int coef = a.kA - a.wz[m];
+    for (int t = tid; t < sh.T; t += 256) wsh[t] = (int)wr[(size_t)t * tstride] + coef;
+    __syncthreads();
+    const int x_zp = zp8(a.x_zp, a.x_u8);
+    const uint8_t* xp = a.x + ((size_t)n * sh.C + m) * sh.H * sh.W;
+    // the plane as 4-byte words (whole words when the plane's size and x
+    // allow it, else byte by byte), four words a thread in flight, each
+    // byte then placed at its padded position
+    const int hw = sh.H * sh.W;
+    const int nwords = (hw + 3) >> 2;
+    if (a.vecx_plane && (sh.W & 3) == 0) {
+        // a word never straddles two rows: one division a word
+        for (int i0 = tid; i0 < nwords; i0 += 4 * 256) {
+            uint32_t word[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                word[k] = *reinterpret_cast<const uint32_t*>(xp + 4 * min(i0 + 256 * k, nwords - 1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + 256 * k;
+                if (i >= nwords) break;
+                const int ih = (int)dq::fdiv((uint32_t)(4 * i), sh.w_div), iw = 4 * i - ih * sh.W;
+                const int r = ih + sh.pt, c = iw + sh.pl;
+                if (r >= sh.hp) continue;
+                int16_t* d = xs + r * Wp + c;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t b = (word[k] >> (8 * e)) & 0xffu;
+                    const int xv = a.x_u8 ? (int)b : (int)(int8_t)b;
+                    if (c + e < Wp) d[e] = (int16_t)(xv - x_zp);
+                }
+            }
+        }
+    } else
+    for (int i0 = tid; i0 < nwords; i0 += 4 * 256) {
+        uint32_t word[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = min(i0 + 256 * k, nwords - 1);
+            if (a.vecx_plane) {
+                word[k] = *reinterpret_cast<const uint32_t*>(xp + 4 * i);
+            } else {
+                word[k] = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * i + e < hw) word[k] |= (uint32_t)xp[4 * i + e] << (8 * e);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + 256 * k;
+            if (i >= nwords) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int f = 4 * i + e;
+                if (f >= hw) break;
+                const int ih = (int)dq::fdiv((uint32_t)f, sh.w_div), iw = f - ih * sh.W;
+                const int r = ih + sh.pt, c = iw + sh.pl;
+                const uint32_t b = (word[k] >> (8 * e)) & 0xffu;
+                const int xv = a.x_u8 ? (int)b : (int)(int8_t)b;
+                if (r < sh.hp && c < Wp) xs[r * Wp + c] = (int16_t)(xv - x_zp);
+            }
+        }
+    }
+    __syncthreads();
+    const YQuant yq = make_yquant(a);
+    const float wsc = a.ws[m];
+    const uint32_t bias = (uint32_t)a.bias[m];
+    uint8_t* yp = a.y + ((size_t)n * sh.M + m) * sh.P;
+    // 3x3: each kernel row's weights as int16 pairs (w0 w1), (w2 0), (0 w2)
+    s2 wA[3], wB[3], wC[3];
+    if (KS3) {
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int w0 = wsh[3 * kh], w1 = wsh[3 * kh + 1], w2 = wsh[3 * kh + 2];
+            wA[kh] = s2{(short)w0, (short)w1};
+            wB[kh] = s2{(short)w2, 0};
+            wC[kh] = s2{0, (short)w2};
+        }
+    }
+    const int total = sh.OH * sh.spr;
+    for (int s = tid; s < total; s += 256) {
+        const int oh = (int)dq::fdiv((uint32_t)s, sh.spr_div), ow0 = 4 * (s - oh * sh.spr);
+        int acc[4] = {0, 0, 0, 0};
+        if (KS3) {
+            // the row's six inputs as int16 pairs (x0 x1)(x2 x3)(x4 x5) from
+            // three aligned words (Wp and ow0 are even), the odd pairs by a
+            // byte shift, then two v_dot2_i32_i16 per output and row
+#pragma unroll
+            for (int kh = 0; kh < 3; ++kh) {
+                const uint32_t* row = reinterpret_cast<const uint32_t*>(xs + (oh + kh) * Wp + ow0);
+                const uint32_t p0 = row[0], p2 = row[1], p4 = row[2];
+                const uint32_t p1 = __builtin_amdgcn_alignbyte(p2, p0, 2);
+                const uint32_t p3 = __builtin_amdgcn_alignbyte(p4, p2, 2);
+                acc[0] = __builtin_amdgcn_sdot2(as_s2(p0), wA[kh], acc[0], false);
+                acc[0] = __builtin_amdgcn_sdot2(as_s2(p2), wB[kh], acc[0], false);
+                acc[1] = __builtin_amdgcn_sdot2(as_s2(p1), wA[kh], acc[1], false);
+                acc[1] = __builtin_amdgcn_sdot2(as_s2(p3), wB[kh], acc[1], false);
+                acc[2] = __builtin_amdgcn_sdot2(as_s2(p2), wA[kh], acc[2], false);
+                acc[2] = __builtin_amdgcn_sdot2(as_s2(p4), wB[kh], acc[2], false);
+                acc[3] = __builtin_amdgcn_sdot2(as_s2(p3), wA[kh], acc[3], false);
+                acc[3] = __builtin_amdgcn_sdot2(as_s2(p4), wC[kh], acc[3], false);
+            }
+        } else {
+            for (int kh = 0; kh < sh.KH; ++kh) {
+                const int16_t* row = xs + (oh * sh.sh + kh * sh.dh) * Wp + ow0 * sh.sw;
+                for (int kw = 0; kw < sh.KW; ++kw) {
+                    const int wv = wsh[kh * sh.KW + kw];
+                    const int16_t* rk = row + kw * sh.dw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = __mul24(wv, (int)rk[e * sh.sw]) + acc[e];
+                }
+            }
+        }
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (uint32_t)acc[e] + bias;
+        const uint32_t word = requant4(v, wsc, yq);
+        uint8_t* dst = yp + (size_t)oh * sh.OW + ow0;
+        if (a.vecy4 && ow0 + 4 <= sh.OW) {
+            *reinterpret_cast<uint32_t*>(dst) = word;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ow0 + e < sh.OW) dst[e] = (uint8_t)(word >> (8 * e));
+        }
+    }
+}
+
 // The split reduction: the partial sums of every split, the zero-point and
 // bias terms of the epilogue, then the same requantization. One thread per
 // four consecutive pixels of (image n, output channel m).
@@ -601,6 +763,8 @@ struct dq_qconv_ctx {
     dq_dtype x_type, w_type, y_type;
     int wm = 1;            // waves over output channels
     bool direct = false;   // few channels per group: k_qconv_direct
+    bool dw = false;       // depthwise with a plane that fits LDS: k_qconv_dw
+    int dw_lds = 0;        // its dynamic LDS bytes
     int ib = 2;            // 32-pixel MFMA rows per wave
     int patch_bytes = 0;
     bool has_w = false, xsum = false;
@@ -691,6 +855,19 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     // at most 64 channels, else 2 (128 x 128); the patch of the largest
     // pixel run must fit the LDS budget
     c->direct = Cg <= 4 && Mg <= 4;
+    s.hp = (s.OH - 1) * s.sh + (s.KH - 1) * s.dh + 1;
+    s.wp = round_up((s.OW - 1) * s.sw + (s.KW - 1) * s.dw + 1, 2);  // even: 4-byte aligned rows of int16
+    s.spr = (s.OW + 3) / 4;
+    s.spr_div = dq::make_fastdiv((uint32_t)s.spr);
+    s.w_div = dq::make_fastdiv((uint32_t)s.W);
+    if (Cg == 1 && Mg == 1) {
+        const long long nel = (long long)s.hp * s.wp + 3LL * s.sw + 1;
+        const long long bytes = (nel + 1) / 2 * 4;
+        if (bytes <= kDwLdsMax) {
+            c->dw = true;
+            c->dw_lds = (int)bytes;
+        }
+    }
     c->wm = Mg <= 64 ? 1 : 2;
     // two 32-pixel MFMA rows a wave (one row gave more workgroups but was
     // slower on every layer measured but the smallest)
@@ -733,7 +910,10 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
         DQ_FAIL(DQ_ERR_ALLOC, "device allocation for the packed weights failed");
     }
     char buf[256];
-    if (c->direct)
+    if (c->dw)
+        snprintf(buf, sizeof buf, "gfx950 qconv depthwise: a plane (%d x %d, padded) a workgroup in LDS, four outputs a lane, %d taps",
+                 s.hp, s.wp, s.T);
+    else if (c->direct)
         snprintf(buf, sizeof buf, "gfx950 qconv direct: one output pixel a lane, %d taps x %d channels", s.T, s.Cg);
     else
         snprintf(buf, sizeof buf,
@@ -815,7 +995,17 @@ extern "C" int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, con
     a.kB = a.x_u8 ? 128 : 0;
     a.vecx = s.W % 4 == 0 && (uintptr_t)x % 4 == 0;
     a.vecy = s.P % 16 == 0 && (uintptr_t)y % 16 == 0;
+    a.vecy4 = s.OW % 4 == 0 && (uintptr_t)y % 4 == 0;
+    a.vecx_plane = ((long long)s.H * s.W) % 4 == 0 && (uintptr_t)x % 4 == 0;
     const hipStream_t st = (hipStream_t)stream;
+    if (ctx->dw) {
+        const dim3 grid((unsigned)s.M, (unsigned)N);
+        const bool ks3 = s.KH == 3 && s.KW == 3 && s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1;
+        if (ks3) hipLaunchKernelGGL(k_qconv_dw<true>, grid, dim3(256), (size_t)ctx->dw_lds, st, s, a);
+        else hipLaunchKernelGGL(k_qconv_dw<false>, grid, dim3(256), (size_t)ctx->dw_lds, st, s, a);
+        DQ_LAUNCH_CHECK("qconv depthwise");
+        return DQ_OK;
+    }
     if (ctx->direct) {
         const dim3 grid((unsigned)((s.P + 255) / 256), (unsigned)s.M, (unsigned)N);
         hipLaunchKernelGGL(k_qconv_direct, grid, dim3(256), 0, st, s, a);

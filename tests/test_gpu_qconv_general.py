@@ -76,6 +76,8 @@ CASES = [  # (N, C, H, W, M, kH, kW, strides, pads, dilations, group)
     (1, 64, 6, 20, 130, 3, 3, (1, 1), (0, 2, 1, 3), (1, 2), 2),    # groups of 65 channels
     (2, 33, 17, 3, 65, 2, 3, (3, 1), (2, 0, 0, 1), (1, 1), 1),
     (3, 16, 15, 15, 16, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 16),   # depthwise 3x3
+    (2, 6, 13, 10, 6, 3, 3, (2, 1), (1, 0, 2, 1), (2, 1), 6),      # depthwise: strides, dilations, ragged rows
+    (1, 4, 9, 9, 4, 2, 4, (1, 3), (0, 1, 1, 2), (1, 1), 4),        # depthwise: even kernel, column stride 3
 ]
 
 
@@ -109,7 +111,8 @@ def test_qconv_matches_oracle(gpu, case, types, per_channel):
     (2, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1, 1, 1), 1),    # stride 2, 256 output channels
     (1, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3, 3, 3), 1),     # the stem: 3 channels in a 32-channel chunk
     (1, 32, 64, 64, 256, 3, 3, (1, 1), (1, 1, 1, 1), 1),    # two MFMA pixel rows a wave
-    (2, 96, 28, 28, 96, 3, 3, (1, 1), (1, 1, 1, 1), 96),     # depthwise (the direct kernel)
+    (2, 96, 28, 28, 96, 3, 3, (1, 1), (1, 1, 1, 1), 96),     # depthwise (a plane a workgroup in LDS)
+    (1, 2, 200, 200, 2, 3, 3, (1, 1), (1, 1, 1, 1), 2),      # depthwise plane too large for LDS: the direct kernel
     (2, 96, 28, 28, 192, 3, 3, (2, 2), (0, 0, 1, 1), 96),    # depthwise, two outputs a channel, stride 2
     (20, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1), 1),     # 260 workgroups: two chunks, reduction not split
     (8, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1, 1, 1), 1),    # deep layer: the reduction split over 8 workgroups
