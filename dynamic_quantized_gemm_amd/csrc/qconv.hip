@@ -70,6 +70,14 @@ struct ConvShape {
     // strips of four pixels per row
     int hp, wp, spr;
     dq::FastDiv spr_div, w_div;
+    // virtual channels (vc = 1, few channels a group, kernel rows of at most
+    // 8 taps): the implicit GEMM runs on a KH x 1 convolution whose 32
+    // channels are (kernel column kw, input channel c < 4) pairs, channel
+    // 4 kw + c of virtual column ow holding x[c, ih, ow sw - pl + kw dw]. The
+    // fields above then describe that virtual convolution (W = OW, KW = 1,
+    // stride, pad and dilation along columns 1 / 0 / 1, Cg = Kc = 32; K
+    // stays the real tap count), and these the real input.
+    int vc, rW, rsw, rpl, rdw, rCg, rKW;
 };
 
 // Byte offset of w^[row][tap t][channel c] in the packed weights: 1 KiB
@@ -210,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
 
     const int x_zp = zp8(a.x_zp, a.x_u8);
     const uint32_t zpf = ((uint32_t)(x_zp & 0xff) * 0x01010101u) ^ a.xflip;  // x_zp after the shift
-    const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
+    const uint8_t* xg = sh.vc ? a.x + ((size_t)n * sh.C + (size_t)g * sh.rCg) * sh.H * sh.rW
+                              : a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
     const int ncq = sh.ncol / 4;
     const int units = nr * 8 * ncq;
 
@@ -261,6 +270,30 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
             const int ih = ih0 + r, iw0 = 4 * colq - sh.cpad;
             const bool hin = ih >= 0 && ih < sh.H;
             const int ihc = hin ? ih : 0;
+            if (sh.vc) {
+                // virtual channels 4 cq .. + 3: kernel column kw = cq, input
+                // channels 0 .. 3, of virtual columns 4 colq .. + 3; a pair
+                // past the real channels or kernel columns holds x^ = 0
+                const int kw = cq;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool cin = j < sh.rCg && kw < sh.rKW;
+                    const uint8_t* row = xg + ((size_t)(cin ? j : 0) * sh.H + ihc) * sh.rW;
+                    uint32_t v = 0, m = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int iw = (4 * colq + e) * sh.rsw - sh.rpl + kw * sh.rdw;
+                        if (cin && hin && iw >= 0 && iw < sh.rW) {
+                            v |= (uint32_t)row[iw] << (8 * e);
+                            m |= 1u << e;
+                        }
+                    }
+                    st.word[k][j] = v;
+                    st.in4[k][j] = m;
+                    st.inb[k][j] = cin;
+                }
+                continue;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int c = c0 + 4 * cq + j;
@@ -721,7 +754,14 @@ __global__ __launch_bounds__(256) void k_conv_pack_w(const uint8_t* __restrict__
     for (int i = threadIdx.x; i < len; i += 256) {
         const int t = i / sh.Kc, c = i - t * sh.Kc;
         int v = 0;
-        if (mok && c < sh.Cg && t < sh.T) {
+        if (sh.vc) {
+            // virtual tap t = kernel row kh, virtual channel c = 4 kw + input channel
+            const int kw = c >> 2, ci = c & 3;
+            if (mok && ci < sh.rCg && kw < sh.rKW && t < sh.T) {
+                const uint32_t b = w[(((size_t)m * sh.rCg + ci) * sh.KH + t) * sh.rKW + kw];
+                v = w_u8 ? (int)b - 128 : (int)(int8_t)b;
+            }
+        } else if (mok && c < sh.Cg && t < sh.T) {
             const uint32_t b = w[((size_t)m * sh.Cg + c) * sh.T + t];
             v = w_u8 ? (int)b - 128 : (int)(int8_t)b;
         }
@@ -868,6 +908,19 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
             c->dw_lds = (int)bytes;
         }
     }
+    s.vc = 0;
+    if (!c->direct && !c->dw && Cg <= 4 && kW <= 8 && kW > 1) {
+        // the virtual convolution (see ConvShape): kW times fewer MFMAs than
+        // 32-channel chunks over every tap, and a patch of output columns
+        s.vc = 1;
+        s.rW = s.W; s.rsw = s.sw; s.rpl = s.pl; s.rdw = s.dw; s.rCg = s.Cg; s.rKW = s.KW;
+        s.W = s.OW; s.KW = 1; s.sw = 1; s.pl = 0; s.dw = 1; s.Cg = kKC;
+        s.T = s.KH;
+        s.Tp = round_up(s.T, kTapGroup);
+        s.Kc = kKC;
+        s.cpad = 0;
+        s.ncol = round_up(std::max(s.OW, 4), 4);
+    }
     c->wm = Mg <= 64 ? 1 : 2;
     // two 32-pixel MFMA rows a wave (one row gave more workgroups but was
     // slower on every layer measured but the smallest)
@@ -920,7 +973,7 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
                  "gfx950 qconv implicit GEMM mfma_i32_32x32x32_i8: %d ch x %d px per workgroup, patch %d B "
                  "(%d x %d x 32)%s, K = %d",
                  64 * c->wm, 32 * c->ib * (4 / c->wm), c->patch_bytes, c->patch_bytes / (s.ncol * kKC), s.ncol,
-                 "", s.K);
+                 s.vc ? ", virtual channels (kernel column, input channel)" : "", s.K);
     c->info = buf;
     *ctx = c;
     return DQ_OK;

@@ -78,6 +78,9 @@ CASES = [  # (N, C, H, W, M, kH, kW, strides, pads, dilations, group)
     (3, 16, 15, 15, 16, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 16),   # depthwise 3x3
     (2, 6, 13, 10, 6, 3, 3, (2, 1), (1, 0, 2, 1), (2, 1), 6),      # depthwise: strides, dilations, ragged rows
     (1, 4, 9, 9, 4, 2, 4, (1, 3), (0, 1, 1, 2), (1, 1), 4),        # depthwise: even kernel, column stride 3
+    (2, 3, 20, 23, 16, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 1),     # virtual channels (kernel column, channel)
+    (1, 4, 15, 17, 8, 5, 4, (1, 2), (2, 1, 0, 3), (1, 2), 1),      # virtual channels: 4 channels, column dilation
+    (1, 6, 9, 14, 12, 3, 8, (1, 3), (0, 2, 1, 4), (2, 1), 2),      # virtual channels: 8 kernel columns, 2 groups
 ]
 
 
