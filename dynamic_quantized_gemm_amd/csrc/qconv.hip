@@ -22,14 +22,17 @@
 // (past Cg in the last chunk) hold w^ = x^ = 0 and drop out of every term;
 // spatial pads hold x^ = x_zp - b and cancel exactly.
 //
-// The reduction runs over (input channel chunk of 32, kernel tap). A
-// workgroup of four waves owns 64 WM output channels x 64 (4 / WM) output
-// pixels of one image and group; per chunk it stages the input patch its
-// pixels need (all patch rows x all patch columns x 32 channels, channels
-// contiguous, spatial pads already holding x_zp) in LDS, so that for any
-// tap a lane's MFMA operand (16 channels of one input pixel) is one
-// ds_read_b128 at the lane's pixel offset plus a tap offset that is the same
-// for every lane. The weights are packed once per set_w into rows of
+// The reduction runs over (input channel chunk of 32, kernel tap). A first
+// kernel (k_conv_prep_x) writes the prepared input: per image, group and
+// chunk, rows x padded columns x 32 channels (channels contiguous, shifted
+// to int8, spatial pads holding x_zp - b), so that the input patch a
+// workgroup's pixels need for one chunk is one contiguous run. A workgroup
+// of four waves owns 64 WM output channels x 64 (4 / WM) output pixels of
+// one image and group and copies each chunk's patch straight into LDS
+// (global_load_lds_dwordx4; two buffers, the next chunk's copy in flight
+// during this chunk's MFMAs); for any tap a lane's MFMA operand (16 channels
+// of one input pixel) is then one ds_read_b128 at the lane's pixel offset
+// plus a tap offset that is the same for every lane. The weights are packed once per set_w into rows of
 // [tap][channel] (32-channel runs contiguous), read as 16-byte fragments.
 // The epilogue requantizes as the other quantizers do and stores whole
 // 16-byte row segments of y (NCHW).
@@ -69,14 +72,15 @@ struct ConvShape {
     // depthwise planes (k_qconv_dw): padded plane rows x columns, output
     // strips of four pixels per row
     int hp, wp, spr;
-    dq::FastDiv spr_div, w_div;
+    dq::FastDiv spr_div, w_div, wq_div;  // wq_div: W / 4 (k_conv_prep_t)
     // virtual channels (vc = 1, few channels a group, kernel rows of at most
     // 8 taps): the implicit GEMM runs on a KH x 1 convolution whose 32
     // channels are (kernel column kw, input channel c < 4) pairs, channel
-    // 4 kw + c of virtual column ow holding x[c, ih, ow sw - pl + kw dw]. The
-    // fields above then describe that virtual convolution (W = OW, KW = 1,
-    // stride, pad and dilation along columns 1 / 0 / 1, Cg = Kc = 32; K
-    // stays the real tap count), and these the real input.
+    // 4 kw + c of virtual column ow holding x[c, ih, ow sw - pl + kw dw]
+    // (made by k_conv_prep_x). The fields above then describe that virtual
+    // convolution (W = OW, KW = 1, stride, pad and dilation along columns
+    // 1 / 0 / 1, Cg = Kc = 32; K stays the real tap count), and these the
+    // real input.
     int vc, rW, rsw, rpl, rdw, rCg, rKW;
 };
 
@@ -103,8 +107,14 @@ struct ConvArgs {
     const void* y_zp;
     uint8_t* y;
     uint32_t xflip;       // 0x80808080 for a uint8 x
-    int kA, kB, x_u8, y_u8, vecx, vecy;
+    int kA, kB, x_u8, y_u8, vecy;
     int vecy4;            // y 4-byte aligned and OW % 4 == 0 (k_qconv_dw's word stores)
+    // the prepared input of the implicit GEMM (k_conv_prep_x): bytes per
+    // prepared row (ncol x 32) and per 32-channel chunk (rows x row bytes);
+    // bytes of one LDS patch buffer (a multiple of 1 KiB)
+    const uint8_t* xb;
+    size_t xb_rs, xb_cs;
+    int pbuf;
     int vecx_plane;       // x 4-byte aligned and H W % 4 == 0 (k_qconv_dw's word loads)
     int y_lo, y_hi;       // y's saturation range
     // split reduction: blockIdx.z = image * nsplit + split, each split walks
@@ -176,13 +186,6 @@ __device__ __forceinline__ uint32_t requant4(const uint32_t (&v)[4], float wsc, 
 }
 
 
-// Byte i of each of d0..d3, as one word (d0 in the low byte).
-__device__ __forceinline__ uint32_t gather_byte(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, int i) {
-    const int s = 8 * i;
-    return ((d0 >> s) & 0xffu) | (((d1 >> s) & 0xffu) << 8) | (((d2 >> s) & 0xffu) << 16) |
-           (((d3 >> s) & 0xffu) << 24);
-}
-
 template <bool XSUM, int WM, int IB, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t patch[];
@@ -200,28 +203,38 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
     const int m0 = mt * MT + 64 * wm;  // this wave's first channel within the group
     const int p0 = blockIdx.x * PT, pw0 = p0 + 32 * IB * wp;
 
-    // the block's patch: output rows oh_a .. oh_b, input rows from ih0
+    // the block's patch: output rows oh_a .. oh_b need prepared rows r0 ..
+    // r0 + nr - 1 (prepared row r holds input row r - pt), every prepared
+    // column, 32 channels: one contiguous run of the prepared input
     const int oh_a = (int)dq::fdiv((uint32_t)p0, sh.ow_div);
     const int oh_b = (int)dq::fdiv((uint32_t)(std::min(p0 + PT, sh.P) - 1), sh.ow_div);
-    const int ih0 = oh_a * sh.sh - sh.pt;
+    const int r0 = oh_a * sh.sh;
     const int nr = (oh_b - oh_a) * sh.sh + (sh.KH - 1) * sh.dh + 1;
+    const int pbytes = nr * sh.ncol * kKC;
 
     // the lane's IB MFMA pixel rows: patch byte offsets for tap (0, 0)
+    // (prepared column = input column + pl = ow sw + kw dw)
     int pix[IB];
 #pragma unroll
     for (int pb = 0; pb < IB; ++pb) {
         const int p = std::min(pw0 + 32 * pb + (lane & 31), sh.P - 1);
         const int oh = (int)dq::fdiv((uint32_t)p, sh.ow_div), ow = p - oh * sh.OW;
-        const int r = (oh - oh_a) * sh.sh, c = ow * sh.sw - sh.pl + sh.cpad;
+        const int r = (oh - oh_a) * sh.sh, c = ow * sh.sw;
         pix[pb] = (r * sh.ncol + c) * kKC + 16 * (lane >> 5);
     }
 
     const int x_zp = zp8(a.x_zp, a.x_u8);
-    const uint32_t zpf = ((uint32_t)(x_zp & 0xff) * 0x01010101u) ^ a.xflip;  // x_zp after the shift
-    const uint8_t* xg = sh.vc ? a.x + ((size_t)n * sh.C + (size_t)g * sh.rCg) * sh.H * sh.rW
-                              : a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
-    const int ncq = sh.ncol / 4;
-    const int units = nr * 8 * ncq;
+
+    // chunk cc's patch straight from the prepared input into LDS
+    // (global_load_lds_dwordx4: 1 KiB a wave instruction, no VGPRs); the
+    // last KiB may run past the patch, within the prepared buffer's slack
+    // and the LDS buffer's rounding
+    const uint8_t* xsrc = a.xb + ((size_t)(n * sh.G + g) * (sh.Kc / kKC)) * a.xb_cs + (size_t)r0 * a.xb_rs +
+                          16 * lane;
+    auto patch_copy = [&](int cc, uint8_t* dst) {
+        const uint8_t* src = xsrc + (size_t)cc * a.xb_cs;
+        for (int blk = wave; blk * 1024 < pbytes; blk += 4) dq::copy16_to_lds(src + blk * 1024, dst + blk * 1024);
+    };
 
     dq::v16i acc[IB][2], sacc[IB];
 #pragma unroll
@@ -246,107 +259,6 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         tapoff[t] = t < sh.T ? (kh * sh.dh * sh.ncol + kw * sh.dw) * kKC : 0;
     }
 
-    // Staging of a chunk's patch: a unit is 4 channels x 4 patch columns of
-    // one row, transposed in registers to 4 words of (column, 4 channels). A
-    // thread takes up to 4 units at a time and issues all their loads (from
-    // clamped addresses) before any value is used. With W % 4 == 0 (vecx) a
-    // column quad lies wholly inside or wholly outside the image, since the
-    // patch's first column sits at iw = -cpad, a multiple of 4; otherwise a
-    // quad inside a row is one unaligned 4-byte load and only the quads that
-    // straddle the row's ends are loaded byte by byte.
-    struct Stage {
-        uint32_t word[4][4];    // [unit][channel]: the quad's bytes (those inside the image)
-        uint32_t in4[4][4];     // which of the 4 bytes lie inside the image
-        bool inb[4][4];
-        int urc[4];
-    };
-    auto stage_load = [&](Stage& st, int c0, int ub) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int u = std::min(ub + k * kThreads, units - 1);
-            const int colq = u % ncq, rest = u / ncq;
-            const int cq = rest & 7, r = rest >> 3;
-            st.urc[k] = (r * sh.ncol + 4 * colq) * kKC + 4 * cq;
-            const int ih = ih0 + r, iw0 = 4 * colq - sh.cpad;
-            const bool hin = ih >= 0 && ih < sh.H;
-            const int ihc = hin ? ih : 0;
-            if (sh.vc) {
-                // virtual channels 4 cq .. + 3: kernel column kw = cq, input
-                // channels 0 .. 3, of virtual columns 4 colq .. + 3; a pair
-                // past the real channels or kernel columns holds x^ = 0
-                const int kw = cq;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool cin = j < sh.rCg && kw < sh.rKW;
-                    const uint8_t* row = xg + ((size_t)(cin ? j : 0) * sh.H + ihc) * sh.rW;
-                    uint32_t v = 0, m = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int iw = (4 * colq + e) * sh.rsw - sh.rpl + kw * sh.rdw;
-                        if (cin && hin && iw >= 0 && iw < sh.rW) {
-                            v |= (uint32_t)row[iw] << (8 * e);
-                            m |= 1u << e;
-                        }
-                    }
-                    st.word[k][j] = v;
-                    st.in4[k][j] = m;
-                    st.inb[k][j] = cin;
-                }
-                continue;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = c0 + 4 * cq + j;
-                const bool cin = c < sh.Cg;
-                const uint8_t* row = xg + ((size_t)(cin ? c : 0) * sh.H + ihc) * sh.W;
-                st.inb[k][j] = cin;
-                if (a.vecx) {
-                    const bool win = hin && iw0 >= 0 && iw0 < sh.W;
-                    st.word[k][j] = *reinterpret_cast<const uint32_t*>(row + (win ? iw0 : 0));
-                    st.in4[k][j] = win ? 0xfu : 0u;
-                } else if (hin && iw0 >= 0 && iw0 + 4 <= sh.W) {
-                    // a quad inside the row: one (possibly unaligned) 4-byte load
-                    uint32_t v;
-                    __builtin_memcpy(&v, row + iw0, 4);
-                    st.word[k][j] = v;
-                    st.in4[k][j] = 0xfu;
-                } else {
-                    uint32_t v = 0, m = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int iw = iw0 + e;
-                        if (hin && iw >= 0 && iw < sh.W) {
-                            v |= (uint32_t)row[iw] << (8 * e);
-                            m |= 1u << e;
-                        }
-                    }
-                    st.word[k][j] = v;
-                    st.in4[k][j] = m;
-                }
-            }
-        }
-        dq::issue_fence();
-    };
-    auto stage_store = [&](const Stage& st, uint8_t* buf, int ub) {
-        const uint32_t zq = (uint32_t)(x_zp & 0xff) * 0x01010101u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (ub + k * kThreads < units) {
-                uint32_t d[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t m = st.in4[k][j];
-                    const uint32_t bm = (m & 1u ? 0xffu : 0u) | (m & 2u ? 0xff00u : 0u) | (m & 4u ? 0xff0000u : 0u) |
-                                        (m & 8u ? 0xff000000u : 0u);
-                    const uint32_t v = (st.word[k][j] & bm) | (zq & ~bm);  // outside the image: x_zp
-                    d[j] = st.inb[k][j] ? v ^ a.xflip : 0u;                  // a padded channel: x^ = 0
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<uint32_t*>(&buf[st.urc[k] + i * kKC]) = gather_byte(d[0], d[1], d[2], d[3], i);
-            }
-        }
-    };
     // The taps of a staged chunk: a tap group's weight fragments are all
     // requested before its first MFMA; every MFMA runs (a padded tap has zero
     // weights, reads the patch at tap (0, 0) and adds zeros to the pixel sums).
@@ -379,24 +291,29 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
         }
     };
 
+    // Two patch buffers: chunk c's MFMAs run while chunk c + 1's copy is in
+    // flight. Per chunk: its first tap group's weights are requested, then
+    // the next patch's copies (so that waiting for the weights does not wait
+    // for the copies: vector memory operations complete in order), then the
+    // MFMAs; at the end every wave waits for its copies and its LDS reads,
+    // and one barrier makes the next patch visible and frees this one.
+    patch_copy(c_beg / kKC, patch);
+    dq::wait_vmcnt_lgkm0<0>();  // this wave's copies and tap offsets
+    dq::lds_barrier();
+    int bsel = 0;
     for (int c0 = c_beg; c0 < c_end; c0 += kKC) {
-        // the previous chunk's operand reads are done (a bare barrier: no
-        // wait for global memory)
-        dq::wait_lgkm0();
-        dq::lds_barrier();
-        for (int ub = tid; ub < units; ub += 4 * kThreads) {
-            Stage st;
-            stage_load(st, c0, ub);
-            stage_store(st, patch, ub);
-        }
-        dq::wait_lgkm0();
-        dq::lds_barrier();
-        // a tap group's weight fragments are all requested before its first MFMA
-        for (int tg = 0; tg < sh.Tp; tg += kTapGroup) {
-            v4i wf[kTapGroup][2];
+        const uint8_t* cur = patch + bsel * a.pbuf;
+        v4i wf[kTapGroup][2];
+        load_w(wf, 0, c0);
+        if (c0 + kKC < c_end) patch_copy(c0 / kKC + 1, patch + (bsel ^ 1) * a.pbuf);
+        mfma_group(wf, cur, 0);
+        for (int tg = kTapGroup; tg < sh.Tp; tg += kTapGroup) {
             load_w(wf, tg, c0);
-            mfma_group(wf, patch, tg);
+            mfma_group(wf, cur, tg);
         }
+        dq::wait_vmcnt_lgkm0<0>();
+        dq::lds_barrier();
+        bsel ^= 1;
     }
 
     // the accumulators are read right below: the last MFMA's results first
@@ -494,6 +411,151 @@ __global__ __launch_bounds__(kThreads) void k_qconv(ConvShape sh, ConvArgs a) {
                     if (p + e < sh.P) dst[e] = (uint8_t)((uint32_t)v[e >> 2] >> (8 * (e & 3)));
             }
         }
+    }
+}
+
+// The prepared input of the implicit GEMM: xb[n][g][chunk][r][col][32]
+// holds x^ = x - b (int8; b = 128 for uint8 x) of channel 32 chunk + j of
+// group g at input row r - pt, column col - pl; outside the image x_zp - b
+// (a padded input is a real 0, which the correction terms cancel), past the
+// group's channels 0. With virtual channels (sh.vc) channel j = 4 kw + c of
+// prepared column col holds input column col sw - pl + kw dw of channel c
+// (c < Cg, kw < KW; else 0). A thread makes the 32 bytes of one (row,
+// column): lanes run along columns, so each of its byte loads reads
+// consecutive bytes of one channel row across the wave, and its two 16-byte
+// stores are contiguous across the wave.
+__global__ __launch_bounds__(256) void k_conv_prep_x(ConvShape sh, ConvArgs a, int hx, uint8_t* __restrict__ xb) {
+    const int col = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int nch = sh.Kc / kKC;
+    const int z = blockIdx.z;  // (image G + group) chunks + chunk
+    const int ng = z / nch, cc = z - ng * nch;
+    const int n = ng / sh.G, g = ng - n * sh.G;
+    if (col >= sh.ncol || r >= hx) return;
+    const uint32_t flip = a.xflip & 0xffu;
+    const uint32_t zb = ((uint32_t)zp8(a.x_zp, a.x_u8) & 0xffu) ^ flip;  // x_zp - b as a byte
+    const int ih = r - sh.pt;
+    const bool hin = ih >= 0 && ih < sh.H;
+    // all 32 byte loads first, from clamped in-range addresses (so that
+    // they are in flight together), then the bytes of pads and padded
+    // channels replaced
+    uint32_t v[32];
+    bool use[32], in[32];
+    if (sh.vc) {
+        const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.rCg) * sh.H * sh.rW;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int kw = j >> 2, c = j & 3;
+            const int iw = col * sh.rsw - sh.rpl + kw * sh.rdw;
+            use[j] = c < sh.rCg && kw < sh.rKW;
+            in[j] = hin && iw >= 0 && iw < sh.rW;
+            const size_t off = ((size_t)(use[j] ? c : 0) * sh.H + (hin ? ih : 0)) * sh.rW +
+                               (size_t)min(max(iw, 0), sh.rW - 1);
+            v[j] = xg[off];
+        }
+    } else {
+        const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * sh.W;
+        const int iw = col - sh.pl;
+        const bool inside = hin && iw >= 0 && iw < sh.W;
+        const size_t pix = (size_t)(hin ? ih : 0) * sh.W + (size_t)min(max(iw, 0), sh.W - 1);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int c = cc * kKC + j;
+            use[j] = c < sh.Cg;
+            in[j] = inside;
+            v[j] = xg[(size_t)(use[j] ? c : 0) * sh.H * sh.W + pix];
+        }
+    }
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const uint32_t b = use[j] ? (in[j] ? (v[j] ^ flip) : zb) : 0u;
+        w[j >> 2] |= b << (8 * (j & 3));
+    }
+    uint8_t* dst = xb + ((size_t)z * hx + r) * a.xb_rs + (size_t)col * kKC;
+    const dq::u4 lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
+    *reinterpret_cast<dq::u4*>(dst) = lo;
+    *reinterpret_cast<dq::u4*>(dst + 16) = hi;
+}
+
+// The same preparation for real channels with W % 4 == 0, a 4-byte aligned
+// x and W <= 512: a workgroup turns four prepared rows of one chunk around
+// through LDS. Its 32 channel rows x 4 input rows are read with coalesced
+// 4-byte loads into LDS ([channel][row][column]); then each thread gathers
+// 16 channels of one prepared column (byte reads from LDS; pads, rows
+// outside the image and channels past the group filled in) and stores them
+// as one 16-byte piece, consecutive threads writing consecutive pieces.
+constexpr int kPrepRows = 4;
+constexpr int kPrepMaxW = 512;
+
+__global__ __launch_bounds__(256) void k_conv_prep_t(ConvShape sh, ConvArgs a, int hx, uint8_t* __restrict__ xb) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t t[];  // kKC * kPrepRows * W bytes
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nch = sh.Kc / kKC;
+    const int z = blockIdx.y;  // (image G + group) chunks + chunk
+    const int ng = z / nch, cc = z - ng * nch;
+    const int n = ng / sh.G, g = ng - n * sh.G;
+    const int W = sh.W;
+    const int nrb = (hx + kPrepRows - 1) / kPrepRows;
+    // row blocks blockIdx.x, + gridDim.x, ... (fewer, longer workgroups)
+    for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+    const int r0 = rb * kPrepRows;
+    const int ih0 = r0 - sh.pt;
+    // loads: the four input rows of one channel are one run of W words; a
+    // wave takes eight channels (one run each, lane = word), all eight loads
+    // in flight; words of rows outside the image or past hx and channels
+    // past the group are not stored (filled in below)
+    const uint8_t* xg = a.x + ((size_t)n * sh.C + (size_t)g * sh.Cg) * sh.H * W;
+    for (int k0 = 0; k0 < W; k0 += 64) {
+        const int k = k0 + lane;
+        const int i = (int)dq::fdiv((uint32_t)k, sh.wq_div);  // row of the run
+        const int ih = ih0 + i;
+        const bool rok = k < W && ih >= 0 && ih < sh.H && r0 + i < hx;
+        uint32_t v[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int c = cc * kKC + 8 * wave + b;
+            const bool ok = rok && c < sh.Cg;
+            v[b] = *reinterpret_cast<const uint32_t*>(xg + (ok ? ((size_t)c * sh.H + ih0) * W + 4 * (size_t)k : 0));
+        }
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int c = cc * kKC + 8 * wave + b;
+            if (rok && c < sh.Cg) *reinterpret_cast<uint32_t*>(&t[(8 * wave + b) * kPrepRows * W + 4 * k]) = v[b];
+        }
+    }
+    __syncthreads();
+    const uint32_t flip = a.xflip & 0xffu;
+    const uint32_t zb = ((uint32_t)zp8(a.x_zp, a.x_u8) & 0xffu) ^ flip;  // x_zp - b as a byte
+    // stores: thread (column, half h): 16 channels of one prepared column,
+    // row by row; consecutive threads write consecutive 16-byte pieces
+    const int h = tid & 1;
+    const int jn = min(16, sh.Cg - cc * kKC - 16 * h);  // real channels of the half
+    for (int i = 0; i < kPrepRows && r0 + i < hx; ++i) {
+        const int ih = ih0 + i;
+        const bool hin = ih >= 0 && ih < sh.H;
+        uint8_t* drow = xb + ((size_t)z * hx + r0 + i) * a.xb_rs + 16 * h;
+        const uint8_t* trow = t + (16 * h * kPrepRows + i) * W;
+        for (int col = tid >> 1; col < sh.ncol; col += 128) {
+            const int iw = col - sh.pl;
+            const bool in = hin && iw >= 0 && iw < W;
+            const int iwc = in ? iw : 0;
+            // all sixteen LDS reads first (unconditional, in-range rows),
+            // then the pads and padded channels replaced
+            uint32_t raw[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) raw[e] = trow[min(e, max(jn - 1, 0)) * kPrepRows * W + iwc];
+            uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t b = e < jn ? (in ? raw[e] ^ flip : zb) : 0u;
+                w[e >> 2] |= b << (8 * (e & 3));
+            }
+            const dq::u4 o = {w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<dq::u4*>(drow + (size_t)col * kKC) = o;
+        }
+    }
+    __syncthreads();  // the next row block overwrites the tile
     }
 }
 
@@ -816,6 +878,9 @@ struct dq_qconv_ctx {
     int32_t* bias = nullptr;
     int32_t* part = nullptr;  // split partial sums, grown on demand by forward
     size_t part_bytes = 0;
+    uint8_t* xb = nullptr;    // the prepared input, grown on demand by forward
+    size_t xb_bytes = 0;
+    int hx = 0;               // prepared rows an image and chunk
     std::string info;
 };
 
@@ -829,6 +894,7 @@ void free_ctx(dq_qconv_ctx* c) {
     (void)hipFree(c->wz);
     (void)hipFree(c->bias);
     (void)hipFree(c->part);
+    (void)hipFree(c->xb);
     delete c;
 }
 
@@ -887,9 +953,9 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     s.Tp = round_up(s.T, kTapGroup);
     s.Kc = round_up(s.Cg, kKC);
     s.K = (int)(Cg * kH * kW);
-    s.cpad = round_up(s.pl, 4);
-    const int max_iw = (s.OW - 1) * s.sw - s.pl + (s.KW - 1) * s.dw;
-    s.ncol = round_up(std::max(s.cpad + max_iw + 1, 4), 4);
+    // prepared columns: input columns -pl .. the last one a tap reads
+    s.cpad = s.pl;
+    s.ncol = (s.OW - 1) * s.sw + (s.KW - 1) * s.dw + 1;
     s.ow_div = dq::make_fastdiv((uint32_t)s.OW);
     // waves over channels: 1 (64 channels x 256 pixels) while a group has
     // at most 64 channels, else 2 (128 x 128); the patch of the largest
@@ -900,6 +966,7 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     s.spr = (s.OW + 3) / 4;
     s.spr_div = dq::make_fastdiv((uint32_t)s.spr);
     s.w_div = dq::make_fastdiv((uint32_t)s.W);
+    s.wq_div = dq::make_fastdiv((uint32_t)std::max(s.W / 4, 1));
     if (Cg == 1 && Mg == 1) {
         const long long nel = (long long)s.hp * s.wp + 3LL * s.sw + 1;
         const long long bytes = (nel + 1) / 2 * 4;
@@ -919,18 +986,20 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
         s.Tp = round_up(s.T, kTapGroup);
         s.Kc = kKC;
         s.cpad = 0;
-        s.ncol = round_up(std::max(s.OW, 4), 4);
+        s.ncol = s.OW;
     }
     c->wm = Mg <= 64 ? 1 : 2;
     // two 32-pixel MFMA rows a wave (one row gave more workgroups but was
     // slower on every layer measured but the smallest)
     c->ib = 2;
+    c->hx = (s.OH - 1) * s.sh + (s.KH - 1) * s.dh + 1;
     for (;;) {
+        // two patch buffers of the largest patch a workgroup copies
         const int PT = 32 * c->ib * (4 / c->wm);
         const int rows = std::min(s.OH, (PT - 1) / s.OW + 2);
         const int nr = (rows - 1) * s.sh + (s.KH - 1) * s.dh + 1;
-        const long long bytes = (long long)nr * s.ncol * kKC;
-        if (bytes <= kPatchMax || c->direct) {
+        const long long bytes = 2 * (((long long)nr * s.ncol * kKC + 1023) / 1024 * 1024);
+        if (bytes <= kPatchMax || c->direct || c->dw) {
             c->patch_bytes = (int)std::min<long long>(bytes, kPatchMax);
             break;
         }
@@ -1046,7 +1115,6 @@ extern "C" int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, con
     a.y_hi = a.y_u8 ? 255 : 127;
     a.kA = ctx->w_type == DQ_U8 ? 128 : 0;
     a.kB = a.x_u8 ? 128 : 0;
-    a.vecx = s.W % 4 == 0 && (uintptr_t)x % 4 == 0;
     a.vecy = s.P % 16 == 0 && (uintptr_t)y % 16 == 0;
     a.vecy4 = s.OW % 4 == 0 && (uintptr_t)y % 4 == 0;
     a.vecx_plane = ((long long)s.H * s.W) % 4 == 0 && (uintptr_t)x % 4 == 0;
@@ -1068,6 +1136,33 @@ extern "C" int dq_qconv_forward(dq_qconv_ctx* ctx, const void* x, int64_t N, con
     const int PT = 32 * ctx->ib * (4 / ctx->wm);
     const long long ptiles = (s.P + PT - 1) / PT, gy = (long long)s.G * s.mtiles;
     const size_t lds = (size_t)ctx->patch_bytes;
+    // the prepared input (k_conv_prep_x), 1 KiB of slack for the last copy
+    const int nch = s.Kc / kKC;
+    if ((long long)N * s.G * nch > 65535) DQ_FAIL(DQ_ERR_RANGE, "N * group * channel chunks exceeds 65535");
+    a.xb_rs = (size_t)s.ncol * kKC;
+    a.xb_cs = (size_t)ctx->hx * a.xb_rs;
+    a.pbuf = ctx->patch_bytes / 2;
+    const size_t xb_need = (size_t)N * s.G * nch * a.xb_cs + 1024;
+    if (xb_need > ctx->xb_bytes) {
+        // the old buffer may still be in use by this stream's earlier work
+        DQ_HIP_CHECK(hipStreamSynchronize(st));
+        (void)hipFree(ctx->xb);
+        ctx->xb = nullptr;
+        ctx->xb_bytes = 0;
+        if (hipMalloc(&ctx->xb, xb_need) != hipSuccess) DQ_FAIL(DQ_ERR_ALLOC, "device allocation of the prepared input failed");
+        ctx->xb_bytes = xb_need;
+    }
+    a.xb = ctx->xb;
+    if (!s.vc && s.W % 4 == 0 && s.W <= kPrepMaxW && (uintptr_t)x % 4 == 0) {
+        const dim3 pgrid((unsigned)((ctx->hx + kPrepRows - 1) / kPrepRows), (unsigned)(N * s.G * nch));
+        hipLaunchKernelGGL(k_conv_prep_t, pgrid, dim3(256), (size_t)kKC * kPrepRows * s.W, st, s, a, ctx->hx,
+                           ctx->xb);
+        DQ_LAUNCH_CHECK("qconv input preparation");
+    } else {
+        const dim3 pgrid((unsigned)((s.ncol + 63) / 64), (unsigned)((ctx->hx + 3) / 4), (unsigned)(N * s.G * nch));
+        hipLaunchKernelGGL(k_conv_prep_x, pgrid, dim3(256), 0, st, s, a, ctx->hx, ctx->xb);
+        DQ_LAUNCH_CHECK("qconv input preparation");
+    }
     // Too few workgroups for the chip (deep layers: few pixels, many
     // channels): split the chunks of the reduction over workgroups, leave
     // int32 partial sums and requantize them in k_qconv_reduce.
