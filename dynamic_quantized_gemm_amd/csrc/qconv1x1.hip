@@ -298,8 +298,7 @@ __device__ __forceinline__ void store_staged(const uint8_t* ysw, uint8_t* __rest
             const dq::v4i v = *reinterpret_cast<const dq::v4i*>(&ysw[rr * kYPitchP + 16 * q]);
             uint8_t* dst = y + ((size_t)n * M + m) * (size_t)HW + p;
             if (VEC || FULL) {
-                // streaming store (back to back: 16.5 -> 15.8 us)
-                __builtin_nontemporal_store(v, reinterpret_cast<dq::v4i*>(dst));
+                *reinterpret_cast<dq::v4i*>(dst) = v;
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
