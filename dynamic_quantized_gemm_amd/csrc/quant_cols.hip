@@ -71,9 +71,11 @@ k_col_absmax(const void* __restrict__ B, int K, int N, int kchunk, uint32_t* __r
 // rows. Each wave reads 8 whole row segments (lane = four adjacent columns,
 // one 16-byte fp32 / 8-byte bf16 load per row, all issued before any is
 // used), the four waves' maxima merge in LDS, and one atomicMax per column
-// and workgroup goes to memory. Row blocks run bottom-up: the pack pass that
-// follows walks top-down, so the rows read last here are still in the
-// memory-side cache when it starts. Out-of-range rows and columns load a
+// and workgroup goes to memory. Row blocks run bottom-up and the pack pass
+// that follows walks top-down, so it starts on the rows read most recently
+// (at these sizes that gains little: data read again right after a read of
+// 64-512 MiB comes back only 5-15% faster than from a cold start, so the
+// second pass costs about a full read of B). Out-of-range rows and columns load a
 // clamped in-range address (harmless for a maximum; the columns past N are
 // never stored).
 constexpr int kAmaxRowsPerWave = 8;

@@ -75,6 +75,35 @@ def test_sweep_odd_shapes(gpu, M, N, K, tA, tB, constB, tC, act, avoid):
     _compare(case, run_dqip(gpu, case, ext_buf=(M % 2 == 1)), oracle.dqip_forward(case))
 
 
+DYNAMIC_B = [
+    # (M, N, K, typeB, avoid): a non-constant B with N % 4 == 0 (the
+    # vectorized maxima and packing kernels), K ragged against the 256-deep
+    # padding and against the 64 x 64 packing tiles, N not a multiple of 8, bf16 B
+    (40, 520, 1040, "f32", False),
+    (24, 132, 4096, "bf16", True),
+    (16, 260, 4097, "f32", True),
+    (8, 64, 8192, "bf16", False),
+    (33, 1028, 2000, "f32", False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,tB,avoid", DYNAMIC_B)
+def test_dynamic_b_column_quantizer(gpu, M, N, K, tB, avoid):
+    """iB, scaleB and the column sums bit-exact (every column, every k) for
+    a B quantized on every call, with all-zero columns and columns whose
+    scales fall below 2^-100 (the IEEE division path); C against the oracle."""
+    log(f"dqip dynamic B {M}x{N}x{K} B:{tB} avoid:{avoid}")
+    case = W.dqip_random(M, N, K, seed=N + K, typeA="f32", typeB="f32", typeC="f32",
+                         constB=False, act="relu", avoid=avoid, outliers=0.01,
+                         zero_cols=(0, N - 1))
+    B = case["B"]
+    for j, f in ((3, 1e-33), (N // 2, 3e-38), (N - 5, 1e-36)):
+        B[:, j] *= np.float32(f)
+    if tB == "bf16":
+        case["B"], case["typeB"] = W.to_bf16_bits(B), "bf16"
+    _compare(case, run_dqip(gpu, case), oracle.dqip_forward(case))
+
+
 ROW_PATHS = [
     # (M, K, typeA): register-resident rows of 1..8 groups of 16 per lane,
     # several rows per wave (M above the persistent grid), odd row counts
