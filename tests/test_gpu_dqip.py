@@ -63,6 +63,14 @@ SWEEP = [
     (48, 100, 1024, "bf16", "f32", True, "f32", "relu", False),
     (7, 33, 272, "f32", "f32", True, "f32", "identity", True),
     (70, 40, 496, "bf16", "i8", True, "bf16", "identity", False),
+    # constant B with a short K on the 128 x 128 tiles: ragged M, N ending
+    # inside a 32-column block and (N % 4 != 0) inside a 4-column store,
+    # K ending half way through a 32-deep fragment
+    (1000, 1600, 512, "f32", "i8", True, "f32", "relu", False),
+    (700, 2100, 48, "bf16", "f32", True, "bf16", "leaky_relu", True),
+    (4100, 1030, 272, "f32", "f32", True, "f32", "identity", False),
+    (2048, 1024, 160, "bf16", "i8", True, "f32", "relu", False),
+    (1536, 1540, 96, "f32", "f32", True, "bf16", "identity", True),
 ]
 
 
@@ -151,6 +159,22 @@ def test_tiny_scales_stay_exact(gpu, tA, tB, constB, K):
     if tB == "bf16":
         case["B"], case["typeB"] = W.to_bf16_bits(B), "bf16"
     _compare(case, run_dqip(gpu, case), oracle.dqip_forward(case))
+
+
+def test_tiny_scales_and_unaligned_a_on_128_tiles(gpu):
+    """A product on the 128 x 128 GEMM tiles with rows whose scales fall
+    below 2^-100 and into the subnormal range (the IEEE division path) and
+    all-zero rows, with A 16-byte aligned and only 4-byte aligned (the row
+    quantizer's unaligned loads): both bit-exact against the oracle."""
+    log("dqip tiny scales + unaligned A, 128 x 128 tiles")
+    case = W.dqip_random(1024, 1600, 288, seed=31, typeA="f32", typeB="i8", typeC="f32",
+                         constB=True, act="relu", outliers=0.01, zero_rows=(5, 1023))
+    A = case["A"]
+    for i, f in ((1, 1e-33), (2, 1e-36), (3, 1e-38), (64, 3e-39), (130, 1e-35)):
+        A[i] *= np.float32(f)
+    want = oracle.dqip_forward(case)
+    _compare(case, run_dqip(gpu, case), want)
+    _compare(case, run_dqip(gpu, case, a_offset=4), want)
 
 
 @pytest.mark.parametrize("tA", ["f32", "bf16"])
