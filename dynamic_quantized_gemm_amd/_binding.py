@@ -348,14 +348,46 @@ def _shape_arg(shape):
     return C.cast(arr, C.c_void_p), arr
 
 
+def _axis_len(shape, axis):
+    """Entries of a per-axis scale / zero point (1 per tensor); 0 when the
+    axis is out of range (the library reports that error itself)."""
+    if axis == DQ_PER_TENSOR:
+        return 1
+    a = int(axis) + (len(shape) if axis < 0 else 0)
+    return int(shape[a]) if 0 <= a < len(shape) else 0
+
+
+def _bcast_numel(sa, sb):
+    """Elements of the numpy broadcast of two shapes (0 if they do not
+    broadcast: the library reports that error itself)."""
+    n = max(len(sa), len(sb))
+    a = (1,) * (n - len(sa)) + tuple(int(v) for v in sa)
+    b = (1,) * (n - len(sb)) + tuple(int(v) for v in sb)
+    out = 1
+    for x, y in zip(a, b):
+        if x != y and x != 1 and y != 1:
+            return 0
+        out *= y if x == 1 else x
+    return out
+
+
+def _kept_numel(shape, axes):
+    """Elements left after reducing `axes` (None or empty: all) of `shape`."""
+    if not axes:
+        return 1
+    nd = len(shape)
+    red = {int(a) + (nd if a < 0 else 0) for a in axes}
+    return _numel([d for i, d in enumerate(shape) if i not in red])
+
+
 def qlinear_quantize(x, y_scale, y_zero_point, y_type, y, axis=DQ_PER_TENSOR, shape=None,
                      stream=None):
     """x: fp32 tensor; y: int8/uint8 tensor of the same shape (written)."""
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, keep = _shape_arg(shp)
-    n, w = _numel(shp), "qlinear_quantize"
-    _check(load().qlinear_quantize(_ptr(x, w, 4 * n), len(shp), sp, axis, _ptr(y_scale, w, 4),
-                                   _ptr(y_zero_point, w, 1), y_type, _ptr(y, w, n), _stream(stream)), w)
+    n, w, na = _numel(shp), "qlinear_quantize", _axis_len(shp, axis)
+    _check(load().qlinear_quantize(_ptr(x, w, 4 * n), len(shp), sp, axis, _ptr(y_scale, w, 4 * na),
+                                   _ptr(y_zero_point, w, na), y_type, _ptr(y, w, n), _stream(stream)), w)
     del keep
 
 
@@ -364,9 +396,9 @@ def qlinear_dequantize(x, x_type, x_scale, x_zero_point, y, axis=DQ_PER_TENSOR, 
     """x: int8/uint8 tensor; y: fp32 tensor of the same shape (written)."""
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, keep = _shape_arg(shp)
-    n, w = _numel(shp), "qlinear_dequantize"
-    _check(load().qlinear_dequantize(_ptr(x, w, n), x_type, len(shp), sp, axis, _ptr(x_scale, w, 4),
-                                     _ptr(x_zero_point, w, 1), _ptr(y, w, 4 * n), _stream(stream)), w)
+    n, w, na = _numel(shp), "qlinear_dequantize", _axis_len(shp, axis)
+    _check(load().qlinear_dequantize(_ptr(x, w, n), x_type, len(shp), sp, axis, _ptr(x_scale, w, 4 * na),
+                                     _ptr(x_zero_point, w, na), _ptr(y, w, 4 * n), _stream(stream)), w)
     del keep
 
 
@@ -375,9 +407,10 @@ def qlinear_quantize_f16(x, y_scale, y_zero_point, y_type, y, axis=DQ_PER_TENSOR
     """x, y_scale: fp16 tensors; y: int8/uint8 tensor of x's shape (written)."""
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, keep = _shape_arg(shp)
-    _check(load().qlinear_quantize_f16(_ptr(x), len(shp), sp, axis, _ptr(y_scale),
-                                       _ptr(y_zero_point), y_type, _ptr(y), _stream(stream)),
-           "qlinear_quantize_f16")
+    n, w, na = _numel(shp), "qlinear_quantize_f16", _axis_len(shp, axis)
+    _check(load().qlinear_quantize_f16(_ptr(x, w, 2 * n), len(shp), sp, axis, _ptr(y_scale, w, 2 * na),
+                                       _ptr(y_zero_point, w, na), y_type, _ptr(y, w, n), _stream(stream)),
+           w)
     del keep
 
 
@@ -386,9 +419,12 @@ def qlinear_dequantize_f16(x, x_type, x_scale, x_zero_point, y_type, y, axis=DQ_
     """x_scale: fp16 tensor; y: fp16 (y_type DQ_F16) or fp32 (DQ_F32) tensor."""
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, keep = _shape_arg(shp)
-    _check(load().qlinear_dequantize_f16(_ptr(x), x_type, len(shp), sp, axis, _ptr(x_scale),
-                                         _ptr(x_zero_point), y_type, _ptr(y), _stream(stream)),
-           "qlinear_dequantize_f16")
+    n, w, na = _numel(shp), "qlinear_dequantize_f16", _axis_len(shp, axis)
+    ye = 2 if y_type == DQ_F16 else 4
+    _check(load().qlinear_dequantize_f16(_ptr(x, w, n), x_type, len(shp), sp, axis, _ptr(x_scale, w, 2 * na),
+                                         _ptr(x_zero_point, w, na), y_type, _ptr(y, w, ye * n),
+                                         _stream(stream)),
+           w)
     del keep
 
 
@@ -417,20 +453,32 @@ def qlinear_conv1x1(x, x_type, x_scale, x_zero_point, w, w_type, w_scale, w_zero
 
 # ------------------------------------------- QGemm / MatMulIntegerToFloat
 
+# sizes of each context made by dq_qgemm_init, for the extent checks
+_QGEMM_DIMS = {}
+
+
 def dq_qgemm_init(M, N, K, a_type, transA, b_type, transB, y_type, alpha=1.0):
     """Returns the context handle (an int)."""
     h = C.c_void_p()
     _check(load().dq_qgemm_init(C.byref(h), M, N, K, a_type, int(bool(transA)), b_type,
                                 int(bool(transB)), y_type, float(alpha)), "dq_qgemm_init")
+    _QGEMM_DIMS[h.value] = (int(M), int(N), int(K), a_type, y_type)
     return h.value
+
+
+def _qgemm_dims(ctx):
+    return _QGEMM_DIMS.get(ctx, (0, 0, 0, DQ_U8, DQ_U8))
 
 
 def dq_qgemm_set_b(ctx, B, b_scale, b_zero_point=None, stream=None):
     """B: 8-bit tensor ([K,N], or [N,K] with transB); b_scale: fp32 tensor of
     1 or N values; b_zero_point: tensor of B's type (1 or N values) or None."""
     bz_len = 0 if b_zero_point is None else int(b_zero_point.numel())
-    _check(load().dq_qgemm_set_b(ctx, _ptr(B), _ptr(b_scale), int(b_scale.numel()),
-                                 _ptr(b_zero_point), bz_len, _stream(stream)), "dq_qgemm_set_b")
+    M, N, K, _, _ = _qgemm_dims(ctx)
+    w = "dq_qgemm_set_b"
+    _check(load().dq_qgemm_set_b(ctx, _ptr(B, w, K * N), _ptr(b_scale, w, 4 * int(b_scale.numel())),
+                                 int(b_scale.numel()), _ptr(b_zero_point, w, bz_len), bz_len,
+                                 _stream(stream)), w)
 
 
 def _c_shape(C_):
@@ -445,16 +493,21 @@ def dq_qgemm_forward(ctx, A, a_scale, a_zero_point, C_, bias, y_scale, y_zero_po
                      stream=None):
     """C_: int32 tensor of shape (), (N,), (1, N), (M, 1) or (M, N), or None."""
     cr, cc = _c_shape(C_)
-    _check(load().dq_qgemm_forward(ctx, _ptr(A), _ptr(a_scale), _ptr(a_zero_point), _ptr(C_), cr,
-                                   cc, _ptr(bias), _ptr(y_scale), _ptr(y_zero_point), _ptr(Y),
-                                   _stream(stream)), "dq_qgemm_forward")
+    M, N, K, ta, ty = _qgemm_dims(ctx)
+    w = "dq_qgemm_forward"
+    _check(load().dq_qgemm_forward(ctx, _ptr(A, w, M * K * _ELEM[ta]), _ptr(a_scale, w, 4),
+                                   _ptr(a_zero_point, w, 1), _ptr(C_, w, 4 * cr * cc), cr, cc,
+                                   _ptr(bias, w, 4 * N), _ptr(y_scale, w, 4), _ptr(y_zero_point, w, 1),
+                                   _ptr(Y, w, M * N * _ELEM[ty]), _stream(stream)), w)
 
 
 def dq_qgemm_forward_accumulators(ctx, A, a_scale, a_zero_point, C_, acc, stream=None):
     cr, cc = _c_shape(C_)
-    _check(load().dq_qgemm_forward_accumulators(ctx, _ptr(A), _ptr(a_scale), _ptr(a_zero_point),
-                                                _ptr(C_), cr, cc, _ptr(acc), _stream(stream)),
-           "dq_qgemm_forward_accumulators")
+    M, N, K, ta, _ = _qgemm_dims(ctx)
+    w = "dq_qgemm_forward_accumulators"
+    _check(load().dq_qgemm_forward_accumulators(ctx, _ptr(A, w, M * K * _ELEM[ta]), _ptr(a_scale, w, 4),
+                                                _ptr(a_zero_point, w, 1), _ptr(C_, w, 4 * cr * cc), cr,
+                                                cc, _ptr(acc, w, 4 * M * N), _stream(stream)), w)
 
 
 def dq_qgemm_info(ctx):
@@ -463,6 +516,7 @@ def dq_qgemm_info(ctx):
 
 
 def dq_qgemm_release(ctx):
+    _QGEMM_DIMS.pop(ctx, None)
     load().dq_qgemm_release(ctx)
 
 
@@ -474,13 +528,17 @@ def _binary(fn, what, A, a_scale, a_zero_point, B, b_scale, b_zero_point, c_scal
     sb = tuple(B.shape) if b_shape is None else tuple(b_shape)
     pa, ka = _shape_arg(sa)
     pb, kb = _shape_arg(sb)
+    nc = _bcast_numel(sa, sb)
     if fn == "dq_mul_integer":
-        rc = load().dq_mul_integer(_ptr(A), len(sa), pa, _ptr(a_zero_point), _ptr(B), len(sb), pb,
-                                   _ptr(b_zero_point), type_, _ptr(C_), _stream(stream))
+        rc = load().dq_mul_integer(_ptr(A, what, _numel(sa)), len(sa), pa, _ptr(a_zero_point, what, 1),
+                                   _ptr(B, what, _numel(sb)), len(sb), pb, _ptr(b_zero_point, what, 1),
+                                   type_, _ptr(C_, what, 4 * nc), _stream(stream))
     else:
-        rc = getattr(load(), fn)(_ptr(A), len(sa), pa, _ptr(a_scale), _ptr(a_zero_point), _ptr(B),
-                                 len(sb), pb, _ptr(b_scale), _ptr(b_zero_point), _ptr(c_scale),
-                                 _ptr(c_zero_point), type_, _ptr(C_), _stream(stream))
+        rc = getattr(load(), fn)(_ptr(A, what, _numel(sa)), len(sa), pa, _ptr(a_scale, what, 4),
+                                 _ptr(a_zero_point, what, 1), _ptr(B, what, _numel(sb)), len(sb), pb,
+                                 _ptr(b_scale, what, 4), _ptr(b_zero_point, what, 1),
+                                 _ptr(c_scale, what, 4), _ptr(c_zero_point, what, 1), type_,
+                                 _ptr(C_, what, nc), _stream(stream))
     del ka, kb
     _check(rc, what)
 
@@ -508,17 +566,19 @@ def dq_mul_integer(A, a_zero_point, B, b_zero_point, type_, C_, stream=None, a_s
 def qlinear_leaky_relu(x, x_scale, x_zero_point, y_scale, y_zero_point, type_, y, alpha=0.01,
                        n=None, stream=None):
     n = int(x.numel()) if n is None else int(n)
-    _check(load().qlinear_leaky_relu(_ptr(x), n, _ptr(x_scale), _ptr(x_zero_point), _ptr(y_scale),
-                                     _ptr(y_zero_point), float(alpha), type_, _ptr(y),
-                                     _stream(stream)), "qlinear_leaky_relu")
+    w = "qlinear_leaky_relu"
+    _check(load().qlinear_leaky_relu(_ptr(x, w, n), n, _ptr(x_scale, w, 4), _ptr(x_zero_point, w, 1),
+                                     _ptr(y_scale, w, 4), _ptr(y_zero_point, w, 1), float(alpha), type_,
+                                     _ptr(y, w, n), _stream(stream)), w)
 
 
 def qlinear_sigmoid(x, x_scale, x_zero_point, y_scale, y_zero_point, type_, y, n=None,
                     stream=None):
     n = int(x.numel()) if n is None else int(n)
-    _check(load().qlinear_sigmoid(_ptr(x), n, _ptr(x_scale), _ptr(x_zero_point), _ptr(y_scale),
-                                  _ptr(y_zero_point), type_, _ptr(y), _stream(stream)),
-           "qlinear_sigmoid")
+    w = "qlinear_sigmoid"
+    _check(load().qlinear_sigmoid(_ptr(x, w, n), n, _ptr(x_scale, w, 4), _ptr(x_zero_point, w, 1),
+                                  _ptr(y_scale, w, 4), _ptr(y_zero_point, w, 1), type_, _ptr(y, w, n),
+                                  _stream(stream)), w)
 
 
 def _axes_arg(axes):
@@ -532,8 +592,9 @@ def dq_reduce_sum_integer(x, type_, axes, y, shape=None, stream=None):
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, ks = _shape_arg(shp)
     ap, na, ka = _axes_arg(axes)
-    _check(load().dq_reduce_sum_integer(_ptr(x), type_, len(shp), sp, ap if na else None, na,
-                                        _ptr(y), _stream(stream)), "dq_reduce_sum_integer")
+    w = "dq_reduce_sum_integer"
+    _check(load().dq_reduce_sum_integer(_ptr(x, w, _numel(shp)), type_, len(shp), sp, ap if na else None,
+                                        na, _ptr(y, w, 4 * _kept_numel(shp, axes)), _stream(stream)), w)
     del ks, ka
 
 
@@ -542,10 +603,11 @@ def qlinear_reduce_mean(x, type_, axes, x_scale, x_zero_point, y_scale, y_zero_p
     shp = tuple(x.shape) if shape is None else tuple(shape)
     sp, ks = _shape_arg(shp)
     ap, na, ka = _axes_arg(axes)
-    _check(load().qlinear_reduce_mean(_ptr(x), type_, len(shp), sp, ap if na else None, na,
-                                      _ptr(x_scale), _ptr(x_zero_point), _ptr(y_scale),
-                                      _ptr(y_zero_point), _ptr(y), _stream(stream)),
-           "qlinear_reduce_mean")
+    w = "qlinear_reduce_mean"
+    _check(load().qlinear_reduce_mean(_ptr(x, w, _numel(shp)), type_, len(shp), sp, ap if na else None,
+                                      na, _ptr(x_scale, w, 4), _ptr(x_zero_point, w, 1),
+                                      _ptr(y_scale, w, 4), _ptr(y_zero_point, w, 1),
+                                      _ptr(y, w, _kept_numel(shp, axes)), _stream(stream)), w)
     del ks, ka
 
 
@@ -555,9 +617,11 @@ def qlinear_concat(inputs, axis, y_scale, y_zero_point, type_, y, shapes=None, s
     shp = [tuple(t.shape) for t, _, _ in inputs] if shapes is None else [tuple(s) for s in shapes]
     nd = len(shp[0]) if shp else 0
     flat = (C.c_int64 * max(1, n * nd))(*[int(v) for s in shp for v in s])
-    xs = (C.c_void_p * max(1, n))(*[_ptr(t) for t, _, _ in inputs])
-    sc = (C.c_void_p * max(1, n))(*[_ptr(s) for _, s, _ in inputs])
-    zp = (C.c_void_p * max(1, n))(*[_ptr(z) for _, _, z in inputs])
+    w = "qlinear_concat"
+    xs = (C.c_void_p * max(1, n))(*[_ptr(t, w, _numel(s)) for (t, _, _), s in zip(inputs, shp)])
+    sc = (C.c_void_p * max(1, n))(*[_ptr(s, w, 4) for _, s, _ in inputs])
+    zp = (C.c_void_p * max(1, n))(*[_ptr(z, w, 1) for _, _, z in inputs])
+    _ptr(y, w, sum(_numel(s) for s in shp))
     _check(load().qlinear_concat(n, C.cast(xs, C.c_void_p), C.cast(flat, C.c_void_p), nd, int(axis),
                                  C.cast(sc, C.c_void_p), C.cast(zp, C.c_void_p), _ptr(y_scale),
                                  _ptr(y_zero_point), type_, _ptr(y), _stream(stream)),
@@ -576,7 +640,13 @@ def dq_qconv_init(C_, H, W, M, kH, kW, x_type, w_type, y_type, strides=(1, 1),
     _check(load().dq_qconv_init(C.byref(h), C_, H, W, M, kH, kW, C.cast(st, C.c_void_p),
                                 C.cast(pd, C.c_void_p), C.cast(dl, C.c_void_p), group, x_type,
                                 w_type, y_type), "dq_qconv_init")
+    oh, ow = dq_qconv_output_shape(h.value)
+    _QCONV_DIMS[h.value] = (int(C_), int(H), int(W), int(M), int(kH), int(kW), int(group), oh, ow)
     return h.value
+
+
+# sizes of each context made by dq_qconv_init, for the extent checks
+_QCONV_DIMS = {}
 
 
 def dq_qconv_output_shape(ctx):
@@ -586,17 +656,21 @@ def dq_qconv_output_shape(ctx):
 
 
 def dq_qconv_set_w(ctx, w, w_scale, w_zero_point=None, bias=None, stream=None):
-    _check(load().dq_qconv_set_w(ctx, _ptr(w), _ptr(w_scale), _ptr(w_zero_point),
-                                 int(w_scale.numel()), _ptr(bias), _stream(stream)),
-           "dq_qconv_set_w")
+    C_, H, W, M, kH, kW, g = _QCONV_DIMS.get(ctx, (0, 0, 0, 0, 0, 0, 1, 0, 0))[:7]
+    n, wl = "dq_qconv_set_w", int(w_scale.numel())
+    _check(load().dq_qconv_set_w(ctx, _ptr(w, n, M * (C_ // max(g, 1)) * kH * kW), _ptr(w_scale, n, 4 * wl),
+                                 _ptr(w_zero_point, n, wl), wl, _ptr(bias, n, 4 * M), _stream(stream)),
+           n)
 
 
 def dq_qconv_forward(ctx, x, x_scale, x_zero_point, y_scale, y_zero_point, y, N=None,
                      stream=None):
     n = int(x.shape[0]) if N is None else int(N)
-    _check(load().dq_qconv_forward(ctx, _ptr(x), n, _ptr(x_scale), _ptr(x_zero_point),
-                                   _ptr(y_scale), _ptr(y_zero_point), _ptr(y), _stream(stream)),
-           "dq_qconv_forward")
+    C_, H, W, M, _, _, _, oh, ow = _QCONV_DIMS.get(ctx, (0, 0, 0, 0, 0, 0, 1, 0, 0))
+    w = "dq_qconv_forward"
+    _check(load().dq_qconv_forward(ctx, _ptr(x, w, n * C_ * H * W), n, _ptr(x_scale, w, 4),
+                                   _ptr(x_zero_point, w, 1), _ptr(y_scale, w, 4), _ptr(y_zero_point, w, 1),
+                                   _ptr(y, w, n * M * oh * ow), _stream(stream)), w)
 
 
 def dq_qconv_info(ctx):
@@ -605,6 +679,7 @@ def dq_qconv_info(ctx):
 
 
 def dq_qconv_release(ctx):
+    _QCONV_DIMS.pop(ctx, None)
     load().dq_qconv_release(ctx)
 
 
@@ -650,24 +725,33 @@ def dq_lstm_init(seq_length, batch_size, input_size, hidden_size, direction, w_t
                                C.cast(ca, C.c_void_p), C.cast(aa, C.c_void_p),
                                C.cast(ba, C.c_void_p), float(clip or 0.0), int(input_forget)),
            "dq_lstm_init")
+    _LSTM_DIMS[h.value] = (int(seq_length), int(batch_size), int(input_size), int(hidden_size), dirs)
     return h.value
+
+
+# sizes of each context made by dq_lstm_init, for the extent checks
+_LSTM_DIMS = {}
 
 
 def dq_lstm_set_weights(ctx, W, W_scale, W_zero_point, R, R_scale, R_zero_point, B=None, P=None,
                         stream=None):
-    _check(load().dq_lstm_set_weights(ctx, _ptr(W), _ptr(W_scale), int(W_scale.numel()),
-                                      _ptr(W_zero_point), _ptr(R), _ptr(R_scale),
-                                      int(R_scale.numel()), _ptr(R_zero_point), _ptr(B), _ptr(P),
-                                      _stream(stream)),
-           "dq_lstm_set_weights")
+    seq, bt, ni, h, d = _LSTM_DIMS.get(ctx, (0, 0, 0, 0, 0))
+    n, ws, rs = "dq_lstm_set_weights", int(W_scale.numel()), int(R_scale.numel())
+    _check(load().dq_lstm_set_weights(ctx, _ptr(W, n, d * ni * 4 * h), _ptr(W_scale, n, 4 * ws), ws,
+                                      _ptr(W_zero_point, n, ws), _ptr(R, n, d * h * 4 * h),
+                                      _ptr(R_scale, n, 4 * rs), rs, _ptr(R_zero_point, n, rs),
+                                      _ptr(B, n, 4 * d * 8 * h), _ptr(P, n, 4 * d * 3 * h),
+                                      _stream(stream)), n)
 
 
 def dq_lstm_forward(ctx, X, sequence_lens=None, initial_h=None, initial_c=None, Y=None, Y_h=None,
                     Y_c=None, stream=None):
-    _check(load().dq_lstm_forward(ctx, _ptr(X), _ptr(sequence_lens), _ptr(initial_h),
-                                  _ptr(initial_c), _ptr(Y), _ptr(Y_h), _ptr(Y_c),
-                                  _stream(stream)),
-           "dq_lstm_forward")
+    seq, bt, ni, h, d = _LSTM_DIMS.get(ctx, (0, 0, 0, 0, 0))
+    n, st = "dq_lstm_forward", 4 * d * bt * h
+    _check(load().dq_lstm_forward(ctx, _ptr(X, n, 4 * seq * bt * ni), _ptr(sequence_lens, n, 4 * bt),
+                                  _ptr(initial_h, n, st), _ptr(initial_c, n, st),
+                                  _ptr(Y, n, 4 * seq * d * bt * h), _ptr(Y_h, n, st), _ptr(Y_c, n, st),
+                                  _stream(stream)), n)
 
 
 def dq_lstm_info(ctx):
@@ -676,4 +760,5 @@ def dq_lstm_info(ctx):
 
 
 def dq_lstm_release(ctx):
+    _LSTM_DIMS.pop(ctx, None)
     load().dq_lstm_release(ctx)
