@@ -1018,7 +1018,11 @@ extern "C" int dq_qconv_init(dq_qconv_ctx** ctx, int64_t C, int64_t H, int64_t W
     c->x_type = x_type;
     c->w_type = w_type;
     c->y_type = y_type;
-    const int rc = c->wm == 1 ? set_lds2<1>(c->patch_bytes) : set_lds2<2>(c->patch_bytes);
+    // the kernels' dynamic-LDS limit is one setting per kernel and device,
+    // shared by every context: raise it to the most any context may use
+    // (not this one's patch), so a later context with smaller patches
+    // cannot lower it under an earlier one's launches
+    const int rc = c->wm == 1 ? set_lds2<1>(kPatchMax) : set_lds2<2>(kPatchMax);
     if (rc) {
         free_ctx(c);
         return rc;

@@ -212,3 +212,54 @@ def test_qconv_benchmark_layers_full_size(gpu, name):
     part = got[imgs][:, ms]
     assert part.shape == want.shape
     assert np.array_equal(part, want), f"{(part != want).sum()} of {part.size} differ ({info})"
+
+
+def test_contexts_with_different_patch_sizes_coexist(gpu):
+    """The conv kernels' dynamic-LDS limit is one setting per kernel shared
+    by every context: a context with a large patch (the 7x7 / 2 stem's, 92
+    KiB) keeps running, with the same codes, after a context with a small
+    patch has been created and released; a slice checked against the
+    oracle."""
+    import torch
+
+    log("qconv contexts with different patch sizes")
+    r = np.random.default_rng(_seed("coexist"))
+    x = _codes(r, (1, 3, 224, 224), "u8")
+    w = _codes(r, (64, 3, 7, 7), "i8")
+    ws = r.uniform(0.001, 0.01, 64).astype(np.float32)
+    bias = r.integers(-2000, 2000, 64).astype(np.int32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    xs, ys = dev(np.float32([0.02])), dev(np.float32([0.05]))
+    z = dev(np.uint8([128]))
+    big = gpu.dq_qconv_init(3, 224, 224, 64, 7, 7, gpu.DQ_U8, gpu.DQ_I8, gpu.DQ_U8, strides=(2, 2),
+                            pads=(3, 3, 3, 3))
+    try:
+        oh, ow = gpu.dq_qconv_output_shape(big)
+        gpu.dq_qconv_set_w(big, dev(w), dev(ws), None, dev(bias))
+        xd = dev(x)
+        y = torch.empty((1, 64, oh, ow), dtype=torch.uint8, device="cuda")
+        outs = []
+
+        def run_big():
+            y.fill_(0)
+            gpu.dq_qconv_forward(big, xd, xs, z, ys, z, y)
+            torch.cuda.synchronize()
+            outs.append(y.cpu().numpy())
+
+        run_big()
+        small = gpu.dq_qconv_init(8, 9, 9, 8, 3, 3, gpu.DQ_U8, gpu.DQ_I8, gpu.DQ_U8, pads=(1, 1, 1, 1))
+        try:
+            gpu.dq_qconv_set_w(small, dev(_codes(r, (8, 8, 3, 3), "i8")), dev(np.float32([0.01])))
+            ysm = torch.empty((1, 8, 9, 9), dtype=torch.uint8, device="cuda")
+            gpu.dq_qconv_forward(small, dev(_codes(r, (1, 8, 9, 9), "u8")), xs, z, ys, z, ysm)
+            run_big()
+        finally:
+            gpu.dq_qconv_release(small)
+        run_big()
+    finally:
+        gpu.dq_qconv_release(big)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    ms = np.array([0, 21, 42, 63])
+    want = oracle.qlinear_conv2d(x, 0.02, 128, w[ms], ws[ms], np.zeros(len(ms), np.int32), 0.05, 128,
+                                 bias=bias[ms], strides=(2, 2), pads=(3, 3, 3, 3), group=1, y_type="u8")
+    assert np.array_equal(outs[0][:, ms], want)
