@@ -249,7 +249,7 @@ def dqip_set_params(ctx, weight, scale=None, bias=None, params=None, stream=None
     p = None
     if params is not None:
         arr = (C.c_float * len(params))(*params)
-        p = C.cast(arr, C.c_void_p)
+        p = C.addressof(arr)
     M, N, K, tA, tB, tC = _dims(ctx)
     w = "dqip_set_params"
     _check(load().dqip_set_params(ctx, _ptr(weight, w, K * N * _ELEM[tB]), _ptr(scale, w, 4 * N),
@@ -345,7 +345,7 @@ def _numel(shape):
 
 def _shape_arg(shape):
     arr = (C.c_int64 * max(1, len(shape)))(*[int(s) for s in shape])
-    return C.cast(arr, C.c_void_p), arr
+    return C.addressof(arr), arr
 
 
 def _axis_len(shape, axis):
@@ -584,7 +584,7 @@ def qlinear_sigmoid(x, x_scale, x_zero_point, y_scale, y_zero_point, type_, y, n
 def _axes_arg(axes):
     axes = [] if axes is None else [int(a) for a in axes]
     arr = (C.c_int32 * max(1, len(axes)))(*axes)
-    return C.cast(arr, C.c_void_p), len(axes), arr
+    return C.addressof(arr), len(axes), arr
 
 
 def dq_reduce_sum_integer(x, type_, axes, y, shape=None, stream=None):
@@ -622,8 +622,8 @@ def qlinear_concat(inputs, axis, y_scale, y_zero_point, type_, y, shapes=None, s
     sc = (C.c_void_p * max(1, n))(*[_ptr(s, w, 4) for _, s, _ in inputs])
     zp = (C.c_void_p * max(1, n))(*[_ptr(z, w, 1) for _, _, z in inputs])
     _ptr(y, w, sum(_numel(s) for s in shp))
-    _check(load().qlinear_concat(n, C.cast(xs, C.c_void_p), C.cast(flat, C.c_void_p), nd, int(axis),
-                                 C.cast(sc, C.c_void_p), C.cast(zp, C.c_void_p), _ptr(y_scale),
+    _check(load().qlinear_concat(n, C.addressof(xs), C.addressof(flat), nd, int(axis),
+                                 C.addressof(sc), C.addressof(zp), _ptr(y_scale),
                                  _ptr(y_zero_point), type_, _ptr(y), _stream(stream)),
            "qlinear_concat")
 
@@ -637,8 +637,8 @@ def dq_qconv_init(C_, H, W, M, kH, kW, x_type, w_type, y_type, strides=(1, 1),
     pd = (C.c_int64 * 4)(*[int(v) for v in pads])
     dl = (C.c_int64 * 2)(*[int(v) for v in dilations])
     h = C.c_void_p()
-    _check(load().dq_qconv_init(C.byref(h), C_, H, W, M, kH, kW, C.cast(st, C.c_void_p),
-                                C.cast(pd, C.c_void_p), C.cast(dl, C.c_void_p), group, x_type,
+    _check(load().dq_qconv_init(C.byref(h), C_, H, W, M, kH, kW, C.addressof(st),
+                                C.addressof(pd), C.addressof(dl), group, x_type,
                                 w_type, y_type), "dq_qconv_init")
     oh, ow = dq_qconv_output_shape(h.value)
     _QCONV_DIMS[h.value] = (int(C_), int(H), int(W), int(M), int(kH), int(kW), int(group), oh, ow)
@@ -722,8 +722,8 @@ def dq_lstm_init(seq_length, batch_size, input_size, hidden_size, direction, w_t
     h = C.c_void_p()
     _check(load().dq_lstm_init(C.byref(h), int(seq_length), int(batch_size), int(input_size),
                                int(hidden_size), int(direction), int(w_type), int(r_type),
-                               C.cast(ca, C.c_void_p), C.cast(aa, C.c_void_p),
-                               C.cast(ba, C.c_void_p), float(clip or 0.0), int(input_forget)),
+                               C.addressof(ca), C.addressof(aa),
+                               C.addressof(ba), float(clip or 0.0), int(input_forget)),
            "dq_lstm_init")
     _LSTM_DIMS[h.value] = (int(seq_length), int(batch_size), int(input_size), int(hidden_size), dirs)
     return h.value

@@ -49,6 +49,9 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "dq_device.h"
 
@@ -160,15 +163,27 @@ __device__ __forceinline__ uint32_t byte_of(const uint32_t* w, int j) {
     return (w[j >> 2] >> (8 * (j & 3))) & 0xffu;
 }
 
+// Workgroups of `kernel` resident at once on the current device (the
+// occupancy query times the CUs), cached per kernel, device and block size
+// (the queries cost more than a launch); thread-safe.
 template <typename K>
 unsigned resident_blocks(K kernel, int threads) {
+    static std::mutex mu;
+    static std::map<std::tuple<const void*, int, int>, unsigned> cache;
     int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+    if (hipGetDevice(&dev) != hipSuccess) return 2048;
+    const auto key = std::make_tuple((const void*)kernel, dev, threads);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) == hipSuccess &&
-        cus * per_cu > 0)
+        cus * per_cu > 0) {
+        cache.emplace(key, (unsigned)(cus * per_cu));
         return (unsigned)(cus * per_cu);
-    return 2048;
+    }
+    (void)hipGetLastError();
+    return 2048;  // not cached: the next call asks again
 }
 
 // ====================================================== one-code functions
