@@ -409,6 +409,66 @@ def dynamic_quantize_matmul(A, B, b_scale, b_zp=None, bias=None):
     return qgemm(q, B, sc, zp, b_scale, b_zp, bias=bias)
 
 
+def matmul_batches(a_shape, b_shape):
+    """R29: the shapes of an N-dimensional matrix product, by numpy.matmul's
+    rules (the schemas' shape inference is ONNX MatMul's, which follows
+    numpy). A 1-D A is a single row (that dimension is dropped from Y), a
+    1-D B a single column (likewise); the last two dimensions are the
+    matrices, the others are batch dimensions, aligned from the right and
+    broadcast where one side has 1. Returns (M, N, K, batch shape of Y,
+    output shape, [(a batch, b batch) for each Y batch in row-major order]),
+    the batch numbers counting A's and B's own batches in row-major order."""
+    a_shape, b_shape = tuple(int(d) for d in a_shape), tuple(int(d) for d in b_shape)
+    if len(a_shape) == 0 or len(b_shape) == 0:
+        raise ValueError("matmul needs at least one dimension per operand")
+    a_vec, b_vec = len(a_shape) == 1, len(b_shape) == 1
+    a2 = (1,) + a_shape if a_vec else a_shape
+    b2 = b_shape + (1,) if b_vec else b_shape
+    M, K = a2[-2], a2[-1]
+    Kb, N = b2[-2], b2[-1]
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: {K} and {Kb}")
+    ab, bb = a2[:-2], b2[:-2]
+    rank = max(len(ab), len(bb))
+    ab = (1,) * (rank - len(ab)) + ab
+    bb = (1,) * (rank - len(bb)) + bb
+    yb = []
+    for da, db in zip(ab, bb):
+        if da != db and da != 1 and db != 1:
+            raise ValueError(f"batch dimensions {a_shape[:-2]} and {b_shape[:-2]} do not broadcast")
+        yb.append(db if da == 1 else da)
+    pairs = []
+    for idx in np.ndindex(*yb):
+        ia = ib = 0
+        for d in range(rank):
+            ia = ia * ab[d] + (idx[d] if ab[d] > 1 else 0)
+            ib = ib * bb[d] + (idx[d] if bb[d] > 1 else 0)
+        pairs.append((ia, ib))
+    out = tuple(yb) + (() if a_vec else (M,)) + (() if b_vec else (N,))
+    return M, N, K, tuple(yb), out, pairs
+
+
+def matmul_integer_to_float_nd(A, B, a_scale, b_scale, a_zp=0, b_zp=None, bias=None):
+    """MatMulIntegerToFloat on N-dimensional A and B (R29): each batch of Y
+    is the 2-D product (R15, R17) of its A and B batches; b_scale, b_zp and
+    bias (1 or N values) serve every batch."""
+    A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
+    M, N, K, yb, out, pairs = matmul_batches(A.shape, B.shape)
+    Ab, Bb = A.reshape(-1, M, K), B.reshape(-1, K, N)
+    Y = np.empty((len(pairs), M, N), np.float32)
+    for z, (ia, ib) in enumerate(pairs):
+        Y[z] = matmul_integer_to_float(Ab[ia], Bb[ib], a_scale, b_scale, a_zp, b_zp, bias)
+    return Y.reshape(out)
+
+
+def dynamic_quantize_matmul_nd(A, B, b_scale, b_zp=None, bias=None):
+    """DynamicQuantizeMatMul on N-dimensional A and B (R19, R29): A is
+    quantized per tensor over all of its batches at once, then
+    MatMulIntegerToFloat on the codes."""
+    sc, zp, q = quantize_tensor_u8(A)
+    return matmul_integer_to_float_nd(q, B, sc, b_scale, zp, b_zp, bias)
+
+
 # ------------------------------------ element-wise quantized family (R20-R23)
 
 def broadcast_shape(sa, sb):

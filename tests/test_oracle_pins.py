@@ -590,3 +590,84 @@ def test_dynamic_quantize_matmul_per_tensor_hand_values():
     bound = 0.5 * float(sc) * np.abs(B.astype(np.float64) * bs[None, :]).sum(axis=0)
     Y = oracle.dynamic_quantize_matmul(A, B, bs, bias=bias)
     assert (np.abs(Y - exact) <= bound[None, :] * 1.001 + 1e-5).all()
+
+
+# ------------------------------------------------ N-dimensional products (R29)
+# MatMulIntegerToFloat / DynamicQuantizeMatMul take N-dimensional A and B and
+# infer Y's shape as ONNX MatMul does, which follows numpy.matmul: numpy's own
+# matmul fixes the shapes and the batch pairing here.
+
+ND_SHAPES = [
+    ((2, 3, 5, 7), (7, 4)),        # B 2-D: every A batch against the one B
+    ((2, 1, 5, 7), (3, 7, 4)),     # both broadcast: Y batches (2, 3)
+    ((5, 7), (2, 3, 7, 4)),        # A 2-D against B batches
+    ((4, 5, 7), (4, 7, 3)),        # equal batches
+    ((1, 5, 7), (4, 7, 3)),        # A batch of one, broadcast
+    ((3, 1, 2, 5, 7), (2, 1, 7, 4)),
+    ((7,), (2, 7, 4)),             # 1-D A: one row, dropped from Y
+    ((2, 5, 7), (7,)),             # 1-D B: one column, dropped from Y
+    ((7,), (7,)),                  # dot product: Y is a scalar
+]
+
+
+@pytest.mark.parametrize("sa,sb", ND_SHAPES)
+def test_matmul_nd_shapes_and_pairing_are_numpy_matmul(sa, sb):
+    M, N, K, yb, out, pairs = oracle.matmul_batches(sa, sb)
+    assert out == np.matmul(np.zeros(sa), np.zeros(sb)).shape
+    assert len(pairs) == int(np.prod(yb, dtype=np.int64))
+    # unit scales and zero points 0: Y is numpy's integer matmul exactly
+    # (every |sum| < 2^24)
+    r = np.random.default_rng(sum(sa) * 13 + sum(sb))
+    A, B = _q8(r, sa, True), _q8(r, sb, False)
+    Y = oracle.matmul_integer_to_float_nd(A, B, 1.0, 1.0)
+    want = np.matmul(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    assert Y.shape == want.shape and np.array_equal(Y, want)
+
+
+def test_matmul_nd_rejects_what_numpy_rejects():
+    for sa, sb in (((2, 5, 7), (3, 7, 4)), ((5, 7), (6, 4)), ((2, 3, 5, 7), (4, 7, 2))):
+        with pytest.raises(ValueError):
+            np.matmul(np.zeros(sa), np.zeros(sb))
+        with pytest.raises(ValueError):
+            oracle.matmul_batches(sa, sb)
+
+
+def test_matmul_integer_to_float_nd_zero_points_scales_and_bias():
+    # sums from numpy's int64 matmul of the shifted codes; the fp32 steps in
+    # R17's order, vectorized in numpy: ((float)sum * a_scale) * b_scale[n]
+    # + bias[n], each product and the sum rounded to fp32 once
+    r = np.random.default_rng(45)
+    A = _q8(r, (2, 1, 6, 37), True)
+    B = _q8(r, (3, 37, 5), False)
+    a_scale, a_zp = np.float32(0.021), 131
+    bs = r.uniform(0.01, 0.05, 5).astype(np.float32)
+    bz = r.integers(-9, 10, 5).astype(np.int32)
+    bias = r.uniform(-1, 1, 5).astype(np.float32)
+    Y = oracle.matmul_integer_to_float_nd(A, B, a_scale, bs, a_zp, bz, bias)
+    s = np.matmul(A.astype(np.int64) - a_zp, B.astype(np.int64) - bz.astype(np.int64))
+    want = (s.astype(np.float32) * a_scale).astype(np.float32) * bs
+    want = (want.astype(np.float32) + bias).astype(np.float32)
+    assert Y.shape == (2, 3, 6, 5) and np.array_equal(Y, want)
+
+
+def test_dynamic_quantize_matmul_nd_quantizes_the_whole_tensor():
+    # the batches span different ranges, so one scale for the whole tensor
+    # (R19) differs from a scale per batch; the result is MatMulIntegerToFloat
+    # on the codes of the whole tensor, within the quantization error of the
+    # float product
+    r = np.random.default_rng(46)
+    A = np.stack([r.normal(0, 1, (5, 33)), 4 * r.normal(0, 1, (5, 33))]).astype(np.float32)
+    B = _q8(r, (2, 33, 6), False)
+    bs = r.uniform(0.01, 0.05, 6).astype(np.float32)
+    bias = r.uniform(-1, 1, 6).astype(np.float32)
+    Y = oracle.dynamic_quantize_matmul_nd(A, B, bs, bias=bias)
+    lo, hi = min(0.0, float(A.min())), max(0.0, float(A.max()))
+    sc = np.float32(np.float32(hi) - np.float32(lo)) / np.float32(255)
+    tsc, zp, q = oracle.quantize_tensor_u8(A)
+    assert tsc == np.float32(sc)
+    assert np.array_equal(Y, oracle.matmul_integer_to_float_nd(q, B, tsc, bs, zp, bias=bias))
+    per_batch = oracle.dynamic_quantize_matmul(A[0], B[0], bs, bias=bias)
+    assert not np.array_equal(Y[0], per_batch)
+    exact = np.matmul(A.astype(np.float64), B.astype(np.float64) * bs) + bias
+    bound = 0.5 * float(sc) * np.abs(B.astype(np.float64) * bs).sum(axis=1, keepdims=True)
+    assert (np.abs(Y - exact) <= bound * 1.001 + 1e-5).all()
