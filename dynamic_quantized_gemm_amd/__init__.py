@@ -16,7 +16,8 @@ from ._binding import (  # noqa: F401
     dqip_forward, dqip_forward_accumulators, dqip_info, dqip_init, dqip_internal_buffer_size,
     dqip_last_error, dqip_profile_begin, dqip_profile_end, dqip_read_quantized_a, dqip_read_quantized_b, dqip_release,
     dqip_set_params, exported_symbols, load, qlinear_conv1x1, qlinear_dequantize, qlinear_quantize,
-    DQ_QGEMM_K_MAX, dq_qgemm_forward, dq_qgemm_forward_accumulators, dq_qgemm_info, dq_qgemm_init,
+    DQ_QGEMM_K_MAX, DQ_QGEMM_BATCH_MAX, DQ_QGEMM_BATCH_RANK_MAX, dq_qgemm_init_batched,
+    dq_qgemm_forward, dq_qgemm_forward_accumulators, dq_qgemm_info, dq_qgemm_init,
     dq_qgemm_release, dq_qgemm_set_b, dq_mul_integer, dq_reduce_sum_integer, qlinear_add,
     qlinear_concat, qlinear_leaky_relu, qlinear_mul, qlinear_reduce_mean, qlinear_sigmoid,
     qlinear_dequantize_f16, qlinear_quantize_f16, dq_qconv_forward, dq_qconv_info,

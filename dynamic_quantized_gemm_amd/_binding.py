@@ -19,6 +19,8 @@ DQ_OK, DQ_ERR_ARG, DQ_ERR_TYPE, DQ_ERR_STATE, DQ_ERR_RANGE, DQ_ERR_ALLOC, DQ_ERR
 DQ_PER_TENSOR = -(2 ** 31)
 DQ_K_MAX = 65536
 DQ_QGEMM_K_MAX = 32768
+DQ_QGEMM_BATCH_RANK_MAX = 8
+DQ_QGEMM_BATCH_MAX = 65536
 DQ_LSTM_FORWARD, DQ_LSTM_REVERSE, DQ_LSTM_BIDIRECTIONAL = 0, 1, 2
 DQ_LSTM_HIDDEN_MAX = 4096
 # dq_rnn_act: ONNX RNN activation name -> (code, takes alpha, default alpha,
@@ -65,6 +67,8 @@ _SIGNATURES = {
                                   C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dq_qgemm_init": (C.c_int, [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int,
                                 C.c_int, C.c_int, C.c_int, C.c_int, C.c_float]),
+    "dq_qgemm_init_batched": (C.c_int, [C.POINTER(C.c_void_p), C.c_int, C.c_void_p, C.c_void_p,
+                                        C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int]),
     "dq_qgemm_set_b": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
                                  C.c_int64, C.c_void_p]),
     "dq_qgemm_forward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -462,21 +466,43 @@ def dq_qgemm_init(M, N, K, a_type, transA, b_type, transB, y_type, alpha=1.0):
     h = C.c_void_p()
     _check(load().dq_qgemm_init(C.byref(h), M, N, K, a_type, int(bool(transA)), b_type,
                                 int(bool(transB)), y_type, float(alpha)), "dq_qgemm_init")
-    _QGEMM_DIMS[h.value] = (int(M), int(N), int(K), a_type, y_type)
+    _QGEMM_DIMS[h.value] = (int(M), int(N), int(K), a_type, y_type, 1, 1, 1)
+    return h.value
+
+
+def dq_qgemm_init_batched(a_batch, b_batch, M, N, K, a_type, b_type):
+    """a_batch / b_batch: the batch dimensions of A and B (sequences, the
+    shorter left-padded with 1 here). Returns the context handle (an int).
+    A is then [prod(a_batch), M, K], B [prod(b_batch), K, N] and Y (fp32)
+    [prod(broadcast batch), M, N]."""
+    ab, bb = [int(d) for d in a_batch], [int(d) for d in b_batch]
+    rank = max(len(ab), len(bb))
+    ab = [1] * (rank - len(ab)) + ab
+    bb = [1] * (rank - len(bb)) + bb
+    arr = C.c_int64 * max(rank, 1)
+    pa, pb = arr(*ab), arr(*bb)
+    h = C.c_void_p()
+    _check(load().dq_qgemm_init_batched(C.byref(h), rank, C.addressof(pa), C.addressof(pb), M, N, K,
+                                        a_type, b_type), "dq_qgemm_init_batched")
+    na = nb = ny = 1
+    for da, db in zip(ab, bb):
+        na, nb, ny = na * da, nb * db, ny * (db if da == 1 else da)
+    _QGEMM_DIMS[h.value] = (int(M), int(N), int(K), a_type, DQ_F32, na, nb, ny)
     return h.value
 
 
 def _qgemm_dims(ctx):
-    return _QGEMM_DIMS.get(ctx, (0, 0, 0, DQ_U8, DQ_U8))
+    return _QGEMM_DIMS.get(ctx, (0, 0, 0, DQ_U8, DQ_U8, 1, 1, 1))
 
 
 def dq_qgemm_set_b(ctx, B, b_scale, b_zero_point=None, stream=None):
-    """B: 8-bit tensor ([K,N], or [N,K] with transB); b_scale: fp32 tensor of
-    1 or N values; b_zero_point: tensor of B's type (1 or N values) or None."""
+    """B: 8-bit tensor ([K,N], or [N,K] with transB; [B batches, K, N] for a
+    batched context); b_scale: fp32 tensor of 1 or N values; b_zero_point:
+    tensor of B's type (1 or N values) or None."""
     bz_len = 0 if b_zero_point is None else int(b_zero_point.numel())
-    M, N, K, _, _ = _qgemm_dims(ctx)
+    M, N, K, _, _, _, nb, _ = _qgemm_dims(ctx)
     w = "dq_qgemm_set_b"
-    _check(load().dq_qgemm_set_b(ctx, _ptr(B, w, K * N), _ptr(b_scale, w, 4 * int(b_scale.numel())),
+    _check(load().dq_qgemm_set_b(ctx, _ptr(B, w, nb * K * N), _ptr(b_scale, w, 4 * int(b_scale.numel())),
                                  int(b_scale.numel()), _ptr(b_zero_point, w, bz_len), bz_len,
                                  _stream(stream)), w)
 
@@ -493,21 +519,21 @@ def dq_qgemm_forward(ctx, A, a_scale, a_zero_point, C_, bias, y_scale, y_zero_po
                      stream=None):
     """C_: int32 tensor of shape (), (N,), (1, N), (M, 1) or (M, N), or None."""
     cr, cc = _c_shape(C_)
-    M, N, K, ta, ty = _qgemm_dims(ctx)
+    M, N, K, ta, ty, na, _, ny = _qgemm_dims(ctx)
     w = "dq_qgemm_forward"
-    _check(load().dq_qgemm_forward(ctx, _ptr(A, w, M * K * _ELEM[ta]), _ptr(a_scale, w, 4),
+    _check(load().dq_qgemm_forward(ctx, _ptr(A, w, na * M * K * _ELEM[ta]), _ptr(a_scale, w, 4),
                                    _ptr(a_zero_point, w, 1), _ptr(C_, w, 4 * cr * cc), cr, cc,
                                    _ptr(bias, w, 4 * N), _ptr(y_scale, w, 4), _ptr(y_zero_point, w, 1),
-                                   _ptr(Y, w, M * N * _ELEM[ty]), _stream(stream)), w)
+                                   _ptr(Y, w, ny * M * N * _ELEM[ty]), _stream(stream)), w)
 
 
 def dq_qgemm_forward_accumulators(ctx, A, a_scale, a_zero_point, C_, acc, stream=None):
     cr, cc = _c_shape(C_)
-    M, N, K, ta, _ = _qgemm_dims(ctx)
+    M, N, K, ta, _, na, _, ny = _qgemm_dims(ctx)
     w = "dq_qgemm_forward_accumulators"
-    _check(load().dq_qgemm_forward_accumulators(ctx, _ptr(A, w, M * K * _ELEM[ta]), _ptr(a_scale, w, 4),
+    _check(load().dq_qgemm_forward_accumulators(ctx, _ptr(A, w, na * M * K * _ELEM[ta]), _ptr(a_scale, w, 4),
                                                 _ptr(a_zero_point, w, 1), _ptr(C_, w, 4 * cr * cc), cr,
-                                                cc, _ptr(acc, w, 4 * M * N), _stream(stream)), w)
+                                                cc, _ptr(acc, w, 4 * ny * M * N), _stream(stream)), w)
 
 
 def dq_qgemm_info(ctx):

@@ -36,6 +36,12 @@
 //  - k_a_params / k_b_params: per-row and per-column vectors for the GEMM.
 // Transposed 8-bit sources (A under transA, B without transB) go through the
 // column packer of quant_cols.hip.
+//
+// N-dimensional MatMulIntegerToFloat / DynamicQuantizeMatMul (the schemas'
+// A and B are N-dimensional, with numpy.matmul's batch broadcasting): with
+// a single B batch the A batches are just more rows of one product; else A
+// and B are packed batch by batch (each padded like a 2-D operand) and each
+// Y batch is one GEMM launch on its A and B batch.
 #include <stdio.h>
 #include <string.h>
 
@@ -336,6 +342,13 @@ struct dq_qgemm_ctx {
     int32_t* zeroA;      // [Mp]
     float* scaleA;       // [Mp]
     uint32_t* mm;        // 2 x kMmSlots words: per-tensor min / max slots (fp32 A)
+    // batches (dq_qgemm_init_batched): A and B hold nA and nB packed
+    // operands Mp x Kp and Np x Kp apart (their row and column vectors Mp
+    // and Np apart); Y batch z multiplies A batch ia[z] by B batch ib[z]
+    // (ia, ib empty: one product)
+    int batched;
+    int64_t nA, nB;
+    std::vector<int32_t> ia, ib;
     std::string info;
 };
 
@@ -376,6 +389,7 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
     } else if (!a_scale) {
         DQ_FAIL(DQ_ERR_ARG, "a_scale is NULL");
     }
+    if (Cm && c->batched) DQ_FAIL(DQ_ERR_ARG, "C is not an input of the N-dimensional products");
     if (Cm && !((c_rows == 1 || c_rows == c->M) && (c_cols == 1 || c_cols == c->N)))
         DQ_FAIL(DQ_ERR_ARG, "C of shape (%lld, %lld) does not broadcast to (%d, %d)", (long long)c_rows,
                 (long long)c_cols, c->M, c->N);
@@ -387,9 +401,12 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
     int rc = check_device(c);
     if (rc) return rc;
     const int M = c->M, N = c->N, K = c->K, Kp = c->Kp;
-    // A -> packed, row sums and per-row vectors
+    const size_t Mp = dq_mnp((size_t)M), Np = dq_mnp((size_t)N);
+    const size_t esz = c->a_type == DQ_F32 ? 4 : 1;
+    // A -> packed, row sums and per-row vectors, one A batch at a time (an
+    // fp32 A quantized with the min / max of all its batches)
     if (c->a_type == DQ_F32) {
-        const size_t n = (size_t)M * K;
+        const size_t n = (size_t)c->nA * M * K;
         hipLaunchKernelGGL(k_minmax_init, dim3(1), dim3(2 * kMmSlots), 0, s, c->mm);
         const bool vec = (uintptr_t)A % 16 == 0 && n % 4 == 0;
         const size_t need = (vec ? n / 4 : n + 255) / 256 + 1;
@@ -399,36 +416,37 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
         else
             hipLaunchKernelGGL((k_tensor_minmax<false>), dim3(blocks), dim3(256), 0, s, (const float*)A, n, c->mm);
         DQ_LAUNCH_CHECK("tensor_minmax");
-        RowOut o{c->rowsum, c->zeroA, c->scaleA, nullptr, nullptr, c->mm, c->alpha};
-        rc = launch_pack_rows<SRC_F32>(A, M, K, Kp, c->Ap, o, s);
-    } else if (!c->transA) {
-        RowOut o{c->rowsum, c->zeroA, c->scaleA, a_scale, a_zp, nullptr, c->alpha};
-        rc = c->a_type == DQ_U8 ? launch_pack_rows<SRC_U8>(A, M, K, Kp, c->Ap, o, s)
-                                : launch_pack_rows<SRC_I8>(A, M, K, Kp, c->Ap, o, s);
-    } else {
-        rc = dq_launch_pack_cols8(A, c->a_type == DQ_U8, K, M, Kp, c->Ap, c->rowsum, s);
-        if (!rc) {
-            hipLaunchKernelGGL(k_a_params, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, M, K,
-                               c->a_type == DQ_U8, a_scale, a_zp, c->alpha, c->rowsum, c->zeroA, c->scaleA);
-            DQ_LAUNCH_CHECK("a_params");
+    }
+    for (int64_t a = 0; a < c->nA && !rc; ++a) {
+        const void* Aa = static_cast<const char*>(A) + (size_t)a * M * K * esz;
+        int8_t* Apa = c->Ap + (size_t)a * Mp * Kp;
+        const size_t ro = (size_t)a * Mp;
+        if (c->a_type == DQ_F32) {
+            RowOut o{c->rowsum + ro, c->zeroA + ro, c->scaleA + ro, nullptr, nullptr, c->mm, c->alpha};
+            rc = launch_pack_rows<SRC_F32>(Aa, M, K, Kp, Apa, o, s);
+        } else if (!c->transA) {
+            RowOut o{c->rowsum + ro, c->zeroA + ro, c->scaleA + ro, a_scale, a_zp, nullptr, c->alpha};
+            rc = c->a_type == DQ_U8 ? launch_pack_rows<SRC_U8>(Aa, M, K, Kp, Apa, o, s)
+                                    : launch_pack_rows<SRC_I8>(Aa, M, K, Kp, Apa, o, s);
+        } else {
+            rc = dq_launch_pack_cols8(Aa, c->a_type == DQ_U8, K, M, Kp, Apa, c->rowsum + ro, s);
+            if (!rc) {
+                hipLaunchKernelGGL(k_a_params, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, M, K,
+                                   c->a_type == DQ_U8, a_scale, a_zp, c->alpha, c->rowsum + ro, c->zeroA + ro,
+                                   c->scaleA + ro);
+                DQ_LAUNCH_CHECK("a_params");
+            }
         }
     }
     if (rc) return rc;
     if (bias) DQ_HIP_CHECK(hipMemcpyAsync(c->biasv, bias, 4 * (size_t)N, hipMemcpyDeviceToDevice, s));
     DqEpilogue ep;
-    ep.scaleA = c->scaleA;
-    ep.zeroA = c->zeroA;
     ep.scaleB = c->scaleB;
-    ep.colsumB = c->colsum;
     ep.bias = bias ? c->biasv : nullptr;
     ep.act = DQ_ACT_IDENTITY;
     ep.alpha = 0.0f;
     ep.out = mode;
-    ep.C = Y;
-    if (c->zb_any) {
-        ep.rowsumA = c->rowsum;
-        ep.zeroB = c->zb;
-    }
+    if (c->zb_any) ep.zeroB = c->zb;
     if (Cm) {
         ep.addC = Cm;
         ep.c_rs = c_rows == 1 ? 0 : c_cols;
@@ -437,16 +455,29 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
     }
     ep.y_scale = y_scale;
     ep.y_zp = y_zp;
-    return dq_launch_gemm(c->Ap, c->Bp, M, N, Kp, ep, s);
+    const size_t osz = q8 ? 1 : 4;  // fp32 Y and int32 sums: 4 bytes
+    const size_t nY = c->ia.empty() ? 1 : c->ia.size();
+    for (size_t z = 0; z < nY && !rc; ++z) {
+        const size_t a = c->ia.empty() ? 0 : (size_t)c->ia[z], b = c->ib.empty() ? 0 : (size_t)c->ib[z];
+        ep.scaleA = c->scaleA + a * Mp;
+        ep.zeroA = c->zeroA + a * Mp;
+        ep.colsumB = c->colsum + b * Np;
+        if (c->zb_any) ep.rowsumA = c->rowsum + a * Mp;
+        ep.C = static_cast<char*>(Y) + z * M * N * osz;
+        rc = dq_launch_gemm(c->Ap + a * Mp * Kp, c->Bp + b * Np * Kp, M, N, Kp, ep, s);
+    }
+    return rc;
 }
 
 }  // namespace
 
-extern "C" int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K, dq_dtype a_type,
-                             int transA, dq_dtype b_type, int transB, dq_dtype y_type, float alpha) {
-    if (!ctx) DQ_FAIL(DQ_ERR_ARG, "ctx is NULL");
-    *ctx = nullptr;
-    if (M < 1 || N < 1 || K < 1) DQ_FAIL(DQ_ERR_ARG, "M, N, K must be >= 1");
+namespace {
+
+// Validates the types and shapes shared by both initializers and makes the
+// context with every device buffer: nA packed A batches and nB packed B
+// batches (B's per-column scale, zero-point and bias vectors are one set).
+int make_ctx(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K, int64_t nA, int64_t nB, dq_dtype a_type,
+             int transA, dq_dtype b_type, int transB, dq_dtype y_type, float alpha) {
     if (M > 0x7fffffff - 256 || N > 0x7fffffff - 256) DQ_FAIL(DQ_ERR_RANGE, "M and N must fit in int32");
     if (K > DQ_QGEMM_K_MAX) DQ_FAIL(DQ_ERR_RANGE, "K = %lld exceeds %d (int32 sums)", (long long)K, DQ_QGEMM_K_MAX);
     if (a_type != DQ_F32 && a_type != DQ_U8 && a_type != DQ_I8) DQ_FAIL(DQ_ERR_TYPE, "a_type must be f32, u8 or i8");
@@ -469,16 +500,19 @@ extern "C" int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K
     c->transA = transA ? 1 : 0;
     c->transB = transB ? 1 : 0;
     c->alpha = alpha;
+    c->nA = nA;
+    c->nB = nB;
     const size_t Mp = dq_mnp((size_t)M), Np = dq_mnp((size_t)N), Kp = (size_t)c->Kp;
-    if (!rc) rc = ctx_alloc(c, (void**)&c->Bp, Np * Kp);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->colsum, 4 * Np);
+    const size_t a_n = (size_t)nA, b_n = (size_t)nB;
+    if (!rc) rc = ctx_alloc(c, (void**)&c->Bp, b_n * Np * Kp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->colsum, 4 * b_n * Np);
     if (!rc) rc = ctx_alloc(c, (void**)&c->scaleB, 4 * Np);
     if (!rc) rc = ctx_alloc(c, (void**)&c->zb, 4 * Np);
     if (!rc) rc = ctx_alloc(c, (void**)&c->biasv, 4 * Np);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->Ap, Mp * Kp);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->rowsum, 4 * Mp);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->zeroA, 4 * Mp);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->scaleA, 4 * Mp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->Ap, a_n * Mp * Kp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->rowsum, 4 * a_n * Mp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->zeroA, 4 * a_n * Mp);
+    if (!rc) rc = ctx_alloc(c, (void**)&c->scaleA, 4 * a_n * Mp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->mm, 2 * kMmSlots * sizeof(uint32_t));
     if (!rc && hipMemset(c->biasv, 0, 4 * Np) != hipSuccess) rc = DQ_ERR_HIP;
     if (rc) {
@@ -496,6 +530,79 @@ extern "C" int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K
     return DQ_OK;
 }
 
+}  // namespace
+
+extern "C" int dq_qgemm_init(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K, dq_dtype a_type,
+                             int transA, dq_dtype b_type, int transB, dq_dtype y_type, float alpha) {
+    if (!ctx) DQ_FAIL(DQ_ERR_ARG, "ctx is NULL");
+    *ctx = nullptr;
+    if (M < 1 || N < 1 || K < 1) DQ_FAIL(DQ_ERR_ARG, "M, N, K must be >= 1");
+    return make_ctx(ctx, M, N, K, 1, 1, a_type, transA, b_type, transB, y_type, alpha);
+}
+
+extern "C" int dq_qgemm_init_batched(dq_qgemm_ctx** ctx, int batch_rank, const int64_t* a_batch,
+                                     const int64_t* b_batch, int64_t M, int64_t N, int64_t K,
+                                     dq_dtype a_type, dq_dtype b_type) {
+    if (!ctx) DQ_FAIL(DQ_ERR_ARG, "ctx is NULL");
+    *ctx = nullptr;
+    if (M < 1 || N < 1 || K < 1) DQ_FAIL(DQ_ERR_ARG, "M, N, K must be >= 1");
+    if (batch_rank < 0 || batch_rank > DQ_QGEMM_BATCH_RANK_MAX)
+        DQ_FAIL(DQ_ERR_ARG, "batch_rank must be in [0, %d]", DQ_QGEMM_BATCH_RANK_MAX);
+    if (batch_rank > 0 && (!a_batch || !b_batch)) DQ_FAIL(DQ_ERR_ARG, "a_batch and b_batch must not be NULL");
+    // the broadcast batch shape (numpy.matmul's rule) and the batch counts
+    int64_t yb[DQ_QGEMM_BATCH_RANK_MAX];
+    int64_t nA = 1, nB = 1, nY = 1;
+    for (int d = 0; d < batch_rank; ++d) {
+        const int64_t da = a_batch[d], db = b_batch[d];
+        if (da < 1 || db < 1) DQ_FAIL(DQ_ERR_ARG, "batch dimension %d must be >= 1 (A %lld, B %lld)", d,
+                                      (long long)da, (long long)db);
+        if (da != db && da != 1 && db != 1)
+            DQ_FAIL(DQ_ERR_ARG, "batch dimension %d does not broadcast (A %lld, B %lld)", d, (long long)da,
+                    (long long)db);
+        if (da > DQ_QGEMM_BATCH_MAX || db > DQ_QGEMM_BATCH_MAX)
+            DQ_FAIL(DQ_ERR_RANGE, "more than %d batches", DQ_QGEMM_BATCH_MAX);
+        yb[d] = da == 1 ? db : da;
+        nA *= da;
+        nB *= db;
+        nY *= yb[d];
+        if (nA > DQ_QGEMM_BATCH_MAX || nB > DQ_QGEMM_BATCH_MAX || nY > DQ_QGEMM_BATCH_MAX)
+            DQ_FAIL(DQ_ERR_RANGE, "more than %d batches", DQ_QGEMM_BATCH_MAX);
+    }
+    if (nB == 1) {
+        // one B: A's batches are rows of a single product ([nA * M, K])
+        if (nA * M > 0x7fffffff - 256) DQ_FAIL(DQ_ERR_RANGE, "batches * M must fit in int32");
+        const int rc = make_ctx(ctx, nA * M, N, K, 1, 1, a_type, 0, b_type, 0, DQ_F32, 1.0f);
+        if (!rc) (*ctx)->batched = 1;
+        return rc;
+    }
+    const int rc = make_ctx(ctx, M, N, K, nA, nB, a_type, 0, b_type, 0, DQ_F32, 1.0f);
+    if (rc) return rc;
+    dq_qgemm_ctx* c = *ctx;
+    c->batched = 1;
+    c->ia.resize((size_t)nY);
+    c->ib.resize((size_t)nY);
+    // Y batch z in row-major order of yb; A's (B's) batch number counts its
+    // own dimensions, a broadcast dimension (1) contributing index 0
+    for (int64_t z = 0; z < nY; ++z) {
+        int64_t rem = z, ia = 0, ib = 0, sa = 1, sb = 1;
+        for (int d = batch_rank - 1; d >= 0; --d) {
+            const int64_t i = rem % yb[d];
+            rem /= yb[d];
+            if (a_batch[d] > 1) ia += i * sa;
+            if (b_batch[d] > 1) ib += i * sb;
+            sa *= a_batch[d];
+            sb *= b_batch[d];
+        }
+        c->ia[(size_t)z] = (int32_t)ia;
+        c->ib[(size_t)z] = (int32_t)ib;
+    }
+    char buf[96];
+    snprintf(buf, sizeof buf, " | %lld products (%lld A, %lld B batches)", (long long)nY, (long long)nA,
+             (long long)nB);
+    c->info += buf;
+    return DQ_OK;
+}
+
 extern "C" int dq_qgemm_set_b(dq_qgemm_ctx* c, const void* B, const float* b_scale, int64_t b_scale_len,
                               const void* b_zero_point, int64_t b_zero_point_len, void* stream) {
     if (!c) DQ_FAIL(DQ_ERR_STATE, "context is NULL");
@@ -508,15 +615,20 @@ extern "C" int dq_qgemm_set_b(dq_qgemm_ctx* c, const void* B, const float* b_sca
     hipStream_t s = (hipStream_t)stream;
     const int N = c->N, K = c->K, Kp = c->Kp;
     const bool u8 = c->b_type == DQ_U8;
-    if (c->transB) {
-        RowOut o{c->colsum, nullptr, nullptr, nullptr, nullptr, nullptr, 1.0f};
-        rc = u8 ? launch_pack_rows<SRC_U8>(B, N, K, Kp, c->Bp, o, s)
-                : launch_pack_rows<SRC_I8>(B, N, K, Kp, c->Bp, o, s);
-    } else {
-        rc = dq_launch_pack_cols8(B, u8, K, N, Kp, c->Bp, c->colsum, s);
+    const int Np = (int)dq_mnp((size_t)N);
+    for (int64_t b = 0; b < c->nB && !rc; ++b) {
+        const void* Bb = static_cast<const char*>(B) + (size_t)b * K * N;
+        int8_t* Bpb = c->Bp + (size_t)b * Np * Kp;
+        int32_t* cs = c->colsum + (size_t)b * Np;
+        if (c->transB) {
+            RowOut o{cs, nullptr, nullptr, nullptr, nullptr, nullptr, 1.0f};
+            rc = u8 ? launch_pack_rows<SRC_U8>(Bb, N, K, Kp, Bpb, o, s)
+                    : launch_pack_rows<SRC_I8>(Bb, N, K, Kp, Bpb, o, s);
+        } else {
+            rc = dq_launch_pack_cols8(Bb, u8, K, N, Kp, Bpb, cs, s);
+        }
     }
     if (rc) return rc;
-    const int Np = (int)dq_mnp((size_t)N);
     hipLaunchKernelGGL(k_b_params, dim3((unsigned)((Np + 255) / 256)), dim3(256), 0, s, N, Np, u8, b_scale,
                        (int)b_scale_len, b_zero_point, (int)b_zero_point_len, c->scaleB, c->zb);
     DQ_LAUNCH_CHECK("b_params");

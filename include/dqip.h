@@ -355,6 +355,39 @@ int dq_qgemm_forward(dq_qgemm_ctx* ctx, const void* A, const float* a_scale,
 int dq_qgemm_forward_accumulators(dq_qgemm_ctx* ctx, const void* A, const float* a_scale,
                                   const void* a_zero_point, const int32_t* C, int64_t c_rows,
                                   int64_t c_cols, int32_t* acc, void* stream);
+/* ------------------------------------------------------------------------
+ * N-dimensional MatMulIntegerToFloat / DynamicQuantizeMatMul.
+ * onnxruntime quantization_defs.cc, schemas MatMulIntegerToFloat and
+ * DynamicQuantizeMatMul: A and B are "N-dimensional" matrices and Y's
+ * shape is inferred as ONNX MatMul's, i.e. numpy.matmul's rules: the last
+ * two dimensions are the matrices ([M,K] and [K,N]), the leading ones are
+ * batch dimensions aligned from the right, and a batch dimension of 1 is
+ * broadcast against the other side's (a 1-D operand is the caller's M = 1
+ * or N = 1 with that dimension left out of Y). b_scale, b_zero_point (1 or
+ * N values) and bias serve every batch; DynamicQuantizeMatMul quantizes
+ * its fp32 A per tensor over all batches at once.
+ *
+ * dq_qgemm_init_batched: batch_rank (0 <= rank <= DQ_QGEMM_BATCH_RANK_MAX)
+ * batch dimensions of A and of B (HOST arrays of batch_rank values >= 1,
+ * shorter ranks left-padded with 1 by the caller; NULL when the rank is 0),
+ * each pair equal or one of them 1; M, N, K as dq_qgemm_init; a_type
+ * DQ_F32 / DQ_U8 / DQ_I8, b_type DQ_U8 / DQ_I8; Y is fp32, alpha 1, no
+ * transposes. The broadcast batch count must not exceed DQ_QGEMM_BATCH_MAX.
+ * The context then takes, in dq_qgemm_set_b, B as [B batches][K][N]
+ * (dense row-major, batches in row-major order of b's batch dimensions), and
+ * in dq_qgemm_forward A as [A batches][M][K] and Y as [Y batches][M][N]
+ * (the broadcast batch shape, row-major); C must be NULL (these operators
+ * have none). When B has a single batch the batches of A are its rows (one
+ * [batches * M, K] product); otherwise each Y batch is one product.
+ * Errors: DQ_ERR_ARG (ranks, dimensions, broadcasting), DQ_ERR_RANGE,
+ * DQ_ERR_TYPE, DQ_ERR_ALLOC, DQ_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+#define DQ_QGEMM_BATCH_RANK_MAX 8
+#define DQ_QGEMM_BATCH_MAX 65536
+
+int dq_qgemm_init_batched(dq_qgemm_ctx** ctx, int batch_rank, const int64_t* a_batch,
+                          const int64_t* b_batch, int64_t M, int64_t N, int64_t K,
+                          dq_dtype a_type, dq_dtype b_type);
 /* A short description of the kernels the context runs (owned by it). */
 const char* dq_qgemm_info(const dq_qgemm_ctx* ctx);
 /* Frees the context and its device memory; NULL is a no-op. */

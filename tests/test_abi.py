@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(dq):
 
 def test_header_declares_the_quantized_matrix_products():
     names = declared_functions()
-    for n in ("dq_qgemm_init", "dq_qgemm_set_b", "dq_qgemm_forward",
+    for n in ("dq_qgemm_init", "dq_qgemm_init_batched", "dq_qgemm_set_b", "dq_qgemm_forward",
               "dq_qgemm_forward_accumulators", "dq_qgemm_info", "dq_qgemm_release"):
         assert n in names
 
@@ -71,9 +71,32 @@ def test_qgemm_init_rejects_bad_arguments(dq, args, code):
     assert dq.dqip_last_error()
 
 
+@pytest.mark.parametrize("ab,bb,mnk,types,code", [
+    ((2, 3), (3, 2), (4, 8, 16), (3, 2), "ARG"),        # 2 against 3 does not broadcast
+    ((0,), (1,), (4, 8, 16), (3, 2), "ARG"),            # empty batch dimension
+    ((2,), (2,), (0, 8, 16), (3, 2), "ARG"),            # M = 0
+    ((1,) * 9, (1,) * 9, (4, 8, 16), (3, 2), "ARG"),    # rank beyond DQ_QGEMM_BATCH_RANK_MAX
+    ((65537,), (1,), (4, 8, 16), (3, 2), "RANGE"),      # more than DQ_QGEMM_BATCH_MAX batches
+    ((300, 300), (1, 1), (4, 8, 16), (3, 2), "RANGE"),  # 90000 batches
+    ((2,), (2,), (4, 8, 32769), (3, 2), "RANGE"),       # K beyond DQ_QGEMM_K_MAX
+    ((2,), (2,), (4, 8, 16), (1, 2), "TYPE"),           # bf16 A
+    ((2,), (1,), (4, 8, 16), (3, 0), "TYPE"),           # fp32 B (the folded form too)
+])
+def test_qgemm_init_batched_rejects_bad_arguments(dq, ab, bb, mnk, types, code):
+    rank = len(ab)
+    arr = C.c_int64 * rank
+    h = C.c_void_p(None)
+    rc = dq.load().dq_qgemm_init_batched(C.byref(h), rank, arr(*ab), arr(*bb), *mnk, *types)
+    assert rc == getattr(dq, "DQ_ERR_" + code) and h.value is None
+    assert dq.dqip_last_error()
+
+
 def test_qgemm_null_handles(dq):
     L = dq.load()
     assert L.dq_qgemm_init(None, 4, 4, 4, 3, 0, 2, 0, 0, 1.0) == dq.DQ_ERR_ARG
+    assert L.dq_qgemm_init_batched(None, 0, None, None, 4, 4, 4, 3, 2) == dq.DQ_ERR_ARG
+    h = C.c_void_p(None)
+    assert L.dq_qgemm_init_batched(C.byref(h), 1, None, None, 4, 4, 4, 3, 2) == dq.DQ_ERR_ARG
     assert L.dq_qgemm_set_b(None, None, None, 1, None, 0, None) == dq.DQ_ERR_STATE
     assert L.dq_qgemm_forward(None, None, None, None, None, 0, 0, None, None, None, None,
                               None) == dq.DQ_ERR_STATE
