@@ -93,8 +93,23 @@ __global__ void __launch_bounds__(256) k_tensor_minmax(const float* __restrict__
     float lo = 0.0f, hi = 0.0f;
     const size_t stride = (size_t)gridDim.x * 256;
     if (VEC) {
+        // four 16-byte loads a thread in flight per pass, then the rest
         const dq::f4* a4 = reinterpret_cast<const dq::f4*>(A);
-        for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4; i += stride) {
+        const size_t n4 = n / 4;
+        size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+        for (; i + 3 * stride < n4; i += 4 * stride) {
+            dq::f4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = a4[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo = __builtin_fminf(lo, v[u][e]);
+                    hi = __builtin_fmaxf(hi, v[u][e]);
+                }
+        }
+        for (; i < n4; i += stride) {
             const dq::f4 v = a4[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
