@@ -11,8 +11,9 @@
 // of B is packed row j). K is padded to Kp (multiple of 256) with zero codes
 // in iBp, so the padding adds nothing to a sum; M and N are padded to
 // multiples of 256 (the largest tile) and the padding rows / columns are
-// never stored to C. Per-column vectors (scaleB, colsum, bias) hold Np
-// entries so the epilogue can read them in 16-byte vectors.
+// never stored to C. Per-column vectors (scaleB, colsum) hold Np entries so
+// the epilogue can read them in 16-byte vectors; a bias needs only N (the
+// kernels clamp its column index).
 constexpr int kKpAlign = 256;
 constexpr int kMNAlign = 256;
 
@@ -61,7 +62,7 @@ struct DqEpilogue {
     const int32_t* zeroA;
     const float* scaleB;
     const int32_t* colsumB;
-    const float* bias;  // NULL: no bias add
+    const float* bias;  // N values; NULL: no bias add
     int act;            // dq_act
     float alpha;        // leaky-ReLU slope
     int out;            // DQ_OUT_*

@@ -139,7 +139,8 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
     // fragment f of a step (f < AF: A, else B) at step t
     const int nsteps = KF / KS;
 
-    // row / column parameters of the tile (column vectors hold Np entries)
+    // row / column parameters of the tile (column vectors hold Np entries;
+    // bias may be a caller's tensor of N values, so its index is clamped)
     for (int c = threadIdx.x; c < BN; c += NT) {
         s_cs[c] = ep.colsumB[n0 + c];
         if (EXT) {
@@ -148,7 +149,7 @@ k_gemm(const int8_t* __restrict__ Ap, const int8_t* __restrict__ Bp, int M, int 
         }
         if (OUT != DQ_OUT_ACC) {
             s_sb[c] = ep.scaleB[n0 + c];
-            s_bias[c] = BIAS ? ep.bias[n0 + c] : 0.0f;
+            s_bias[c] = BIAS ? ep.bias[min(n0 + c, N - 1)] : 0.0f;
         }
     }
     for (int r = threadIdx.x; r < BM; r += NT) {

@@ -350,7 +350,6 @@ struct dq_qgemm_ctx {
     int32_t* colsum;     // [Np]
     float* scaleB;       // [Np]
     int32_t* zb;         // [Np]
-    float* biasv;        // [Np]: a forward's bias, zero past N
     // per forward
     int8_t* Ap;          // [Mp x Kp]
     int32_t* rowsum;     // [Mp]
@@ -454,10 +453,9 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
         }
     }
     if (rc) return rc;
-    if (bias) DQ_HIP_CHECK(hipMemcpyAsync(c->biasv, bias, 4 * (size_t)N, hipMemcpyDeviceToDevice, s));
     DqEpilogue ep;
     ep.scaleB = c->scaleB;
-    ep.bias = bias ? c->biasv : nullptr;
+    ep.bias = bias;  // N values: the GEMM clamps its column index
     ep.act = DQ_ACT_IDENTITY;
     ep.alpha = 0.0f;
     ep.out = mode;
@@ -523,13 +521,11 @@ int make_ctx(dq_qgemm_ctx** ctx, int64_t M, int64_t N, int64_t K, int64_t nA, in
     if (!rc) rc = ctx_alloc(c, (void**)&c->colsum, 4 * b_n * Np);
     if (!rc) rc = ctx_alloc(c, (void**)&c->scaleB, 4 * Np);
     if (!rc) rc = ctx_alloc(c, (void**)&c->zb, 4 * Np);
-    if (!rc) rc = ctx_alloc(c, (void**)&c->biasv, 4 * Np);
     if (!rc) rc = ctx_alloc(c, (void**)&c->Ap, a_n * Mp * Kp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->rowsum, 4 * a_n * Mp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->zeroA, 4 * a_n * Mp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->scaleA, 4 * a_n * Mp);
     if (!rc) rc = ctx_alloc(c, (void**)&c->mm, 2 * kMmSlots * sizeof(uint32_t));
-    if (!rc && hipMemset(c->biasv, 0, 4 * Np) != hipSuccess) rc = DQ_ERR_HIP;
     if (rc) {
         ctx_free(c);
         delete c;
