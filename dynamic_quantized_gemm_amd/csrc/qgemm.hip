@@ -152,6 +152,34 @@ struct RowOut {
     float alpha;
 };
 
+// 16 fp32 values from k0, quantized with the tensor's scale / zero point to
+// uint8 and packed as code - 128 (corrected quotient, rounding add, median
+// clamp, as the row quantizer); bytes past K stay zero (ALL: none is).
+template <bool ALL>
+__device__ __forceinline__ dq::u4 f32_codes(const float (&x)[16], int k0, int K, const dq::QDiv& d, int zero) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const float lof = kMagic - (float)zero, hif = kMagic + (float)(255 - zero);
+    dq::u4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + 4 * q + e;
+            uint32_t code;  // uA in [0, 255]
+            if (d.fast) {
+                const float t = dq::qdiv_fast(x[4 * q + e], d) + kMagic;
+                code = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t, lof, hif)) + (uint32_t)zero;
+            } else {
+                code = (uint32_t)dq::sat_add(dq::rne(x[4 * q + e] / d.s), zero, 0, 255);
+            }
+            if (ALL || k < K) w |= ((code & 0xffu) ^ 0x80u) << (8 * e);
+        }
+        o[q] = w;
+    }
+    return o;
+}
+
 // 16 codes of group g of row `row` (zero past K or past R), as packed int8.
 template <int SRC, bool VEC>
 __device__ __forceinline__ dq::u4 load_group(const void* __restrict__ src, int R, int K, int row, int g,
@@ -186,9 +214,6 @@ __device__ __forceinline__ dq::u4 load_group(const void* __restrict__ src, int R
         }
         return o;
     }
-    // fp32, quantized with the tensor's scale / zero point to uint8 and
-    // packed as code - 128 (corrected quotient, rounding add, median clamp,
-    // as the row quantizer); bytes past K stay zero
     const float* p = reinterpret_cast<const float*>(src) + (size_t)row * K + k0;
     float x[16];
     if (VEC) {
@@ -202,26 +227,7 @@ __device__ __forceinline__ dq::u4 load_group(const void* __restrict__ src, int R
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = k0 + e < K ? p[e] : 0.0f;
     }
-    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-    const float lof = kMagic - (float)zero, hif = kMagic + (float)(255 - zero);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int k = k0 + 4 * q + e;
-            uint32_t code;  // uA in [0, 255]
-            if (d.fast) {
-                const float t = dq::qdiv_fast(x[4 * q + e], d) + kMagic;
-                code = (uint32_t)__float_as_int(__builtin_amdgcn_fmed3f(t, lof, hif)) + (uint32_t)zero;
-            } else {
-                code = (uint32_t)dq::sat_add(dq::rne(x[4 * q + e] / d.s), zero, 0, 255);
-            }
-            if (VEC || k < K) w |= ((code & 0xffu) ^ 0x80u) << (8 * e);
-        }
-        o[q] = w;
-    }
-    return o;
+    return f32_codes<VEC>(x, k0, K, d, zero);
 }
 
 // A block packs rows 8 b .. 8 b + 7 over all of Kp (padding groups are
@@ -237,17 +243,57 @@ k_pack_rows(const void* __restrict__ src, int R, int K, int Kp, int8_t* __restri
     dq::QDiv d = {1.0f, 1.0f, true};
     int zero = 0;
     float tscale = 1.0f;
-    if (SRC == SRC_F32) {
-        tensor_params(out.mm, tscale, zero);  // the whole wave, before any branch
-        d = dq::make_qdiv(tscale);
-    }
     int sum = 0;
-#pragma unroll 4
-    for (int g = 8 * w + j; g < ngp; g += 32) {
-        const dq::u4 o = load_group<SRC, VEC>(src, R, K, row, g, d, zero);
+    auto put = [&](int g, const dq::u4& o) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) sum = __builtin_amdgcn_sdot4((int)o[q], 0x01010101, sum, false);
         *reinterpret_cast<dq::u4*>(dst + dq::frag_offset((size_t)row, (size_t)g * 16, (size_t)KF)) = o;
+    };
+    if constexpr (VEC && SRC != SRC_F32) {
+        // 8-bit source in whole 16-byte groups: a lane takes its groups GP at
+        // a time and issues the loads of the next GP before it codes and
+        // stores the current ones, so its reads stay in flight meanwhile
+        // (the plain loop below waits for each group: its loads sit under
+        // the group's bounds branch). Loads are unconditional at clamped
+        // addresses (a row past R reads row R - 1, a group past K the last
+        // group); those groups code as 0.
+        constexpr int GP = 8;      // groups per pass
+        const int ngk = K / 16;    // groups that hold data
+        const bool rin = row < R;
+        const dq::u4* rp = reinterpret_cast<const dq::u4*>(reinterpret_cast<const uint8_t*>(src) +
+                                                           (size_t)min(row, R - 1) * K);
+        const int npass = (ngp + 32 * GP - 1) / (32 * GP);
+        dq::u4 cur[GP], nxt[GP];
+        auto load = [&](int p, dq::u4 (&v)[GP]) {
+#pragma unroll
+            for (int u = 0; u < GP; ++u) v[u] = rp[min(8 * w + j + 32 * (GP * p + u), ngk - 1)];
+        };
+        load(0, cur);
+        for (int p = 0; p < npass; ++p) {
+            if (p + 1 < npass) load(p + 1, nxt);
+#pragma unroll
+            for (int u = 0; u < GP; ++u) {
+                const int g = 8 * w + j + 32 * (GP * p + u);
+                dq::u4 o = {0u, 0u, 0u, 0u};
+                if (rin && g < ngk) {
+                    o = cur[u];
+                    // code - 128 as int8 is the code with its top bit flipped
+                    if (SRC == SRC_U8)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) o[q] ^= 0x80808080u;
+                }
+                if (g < ngp) put(g, o);
+            }
+#pragma unroll
+            for (int u = 0; u < GP; ++u) cur[u] = nxt[u];
+        }
+    } else {
+        if (SRC == SRC_F32) {
+            tensor_params(out.mm, tscale, zero);  // the whole wave, before any branch
+            d = dq::make_qdiv(tscale);
+        }
+#pragma unroll 4
+        for (int g = 8 * w + j; g < ngp; g += 32) put(g, load_group<SRC, VEC>(src, R, K, row, g, d, zero));
     }
     // the row's sum: lanes r, r + 8, ..., r + 56 of each wave, then the waves
     sum += __shfl_xor(sum, 8, 64);
@@ -424,7 +470,10 @@ int run(dq_qgemm_ctx* c, const void* A, const float* a_scale, const void* a_zp, 
         hipLaunchKernelGGL(k_minmax_init, dim3(1), dim3(2 * kMmSlots), 0, s, c->mm);
         const bool vec = (uintptr_t)A % 16 == 0 && n % 4 == 0;
         const size_t need = (vec ? n / 4 : n + 255) / 256 + 1;
-        const unsigned blocks = (unsigned)(need < 2048 ? need : 2048);
+        // at most one workgroup a CU, each reading many vectors: 2048
+        // workgroups measured 4-5 us slower on 64 MiB (dispatch and the
+        // slots' atomics)
+        const unsigned blocks = (unsigned)(need < 256 ? need : 256);
         if (vec)
             hipLaunchKernelGGL((k_tensor_minmax<true>), dim3(blocks), dim3(256), 0, s, (const float*)A, n, c->mm);
         else
