@@ -28,8 +28,9 @@
 // block, and then stores whole lines (eight lanes per line). The loads of
 // the next rows are issued before the current ones are processed, so the
 // arithmetic and the stores overlap them. Other shapes take a wave-per-row
-// kernel (any K up to 8192 values, any alignment) or a two-pass streaming
-// kernel (longer rows, re-read from L2).
+// kernel (any K up to 8192 values, any alignment; also short aligned rows
+// of a small A, where the LDS block's barrier costs more than the scattered
+// stores) or a two-pass streaming kernel (longer rows, re-read from L2).
 #include "dq_device.h"
 #include "dq_kernels.h"
 
@@ -576,6 +577,17 @@ void launch_rows(dim3 grid, hipStream_t s, DqTiming t, const void* A, int M, int
     const int ngroups = (K + 15) / 16;
     const int nv = (ngroups + 63) / 64;
     if (VEC) {
+        // short rows of a small A: the wave-per-row kernel, stores straight
+        // from registers (no LDS block, no barrier). Measured back to back /
+        // cold: 4096 x 512 fp32 17.8 / 21.2 -> 16.6 / 20.6 us for the whole
+        // forward, 4096 x 1024 and 8192 x 512 likewise faster; from about
+        // 8 Mi values on, its scattered stores make the cold call slower
+        // (16384 x 1024: 31.5 -> 34.5 us)
+        if (nv <= 1 && (size_t)M * (size_t)K <= ((size_t)1 << 22)) {
+            hipExtLaunchKernelGGL((k_quant_rows<BF16, true, 1>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A,
+                                  M, K, KF, sA, scaleA, zeroA);
+            return;
+        }
         if (!launch_lds_for<BF16>(nv, s, t, A, M, K, KF, sA, scaleA, zeroA))
             hipExtLaunchKernelGGL((k_quant_rows_stream<BF16, true>), grid, dim3(kThreads), 0, s, t.start, t.stop, 0, A, M, K, KF, sA, scaleA, zeroA);
         return;
