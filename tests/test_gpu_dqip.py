@@ -367,3 +367,63 @@ def test_full_8192_dynamic_b(gpu):
     log(f"  {len(rows)} rows against the oracle")
     want = oracle.dqip_forward(case, rows=rows)
     _compare(case, got, want, rows=rows, check_b=True)
+
+
+# ------------------------------------------------------------ seeded random shapes
+
+def _random_cases(seed, n, big):
+    """n cases drawn from one seeded generator: shapes with ragged edges against
+    every tile (32, 128, 256) and the 256-deep K padding, both A types, a
+    constant B (fp32 or int8) or one quantized on every call (fp32 or bf16),
+    every activation and output type, bias on or off, avoidOverflow, planted
+    zero rows and columns, and A 16-byte aligned or not. big: shapes on the
+    256 x 256 tiles (checked on sampled rows)."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        if big:
+            M, N = int(r.integers(3000, 5200)), int(r.integers(3000, 5200))
+            K = int(r.integers(16, 1600))
+        else:
+            M, N = int(r.integers(1, 700)), int(r.integers(1, 700))
+            K = int(r.integers(1, 2100))
+        tA = ["f32", "bf16"][int(r.integers(2))]
+        constB = bool(r.integers(2))
+        tB = ["f32", "i8"][int(r.integers(2))] if constB else ["f32", "bf16"][int(r.integers(2))]
+        tC = ["f32", "bf16"][int(r.integers(2))]
+        act = ["identity", "relu", "leaky_relu"][int(r.integers(3))]
+        avoid = bool(r.integers(2)) and tB != "i8"
+        bias = bool(r.integers(4))  # three in four with a bias
+        a_offset = 0 if r.integers(4) else (4 if tA == "f32" else 2)
+        cases.append(dict(M=M, N=N, K=K, tA=tA, tB=tB, constB=constB, tC=tC, act=act, avoid=avoid,
+                          bias=bias, a_offset=a_offset, seed=int(r.integers(1 << 30))))
+    return cases
+
+
+def _run_random(gpu, p, rows=None):
+    M, N = p["M"], p["N"]
+    log(f"dqip random {M}x{N}x{p['K']} A:{p['tA']} B:{p['tB']} const:{p['constB']} C:{p['tC']} "
+        f"{p['act']} avoid:{p['avoid']} bias:{p['bias']} A offset:{p['a_offset']} seed:{p['seed']}")
+    case = W.dqip_random(M, N, p["K"], seed=p["seed"], typeA=p["tA"], typeB=p["tB"], typeC=p["tC"],
+                         constB=p["constB"], bias=p["bias"], act=p["act"], avoid=p["avoid"], alpha=0.2,
+                         outliers=0.01, zero_rows=(M // 2,) if M > 3 else (),
+                         zero_cols=(N // 3,) if N > 3 else ())
+    got = run_dqip(gpu, case, ext_buf=bool(p["seed"] & 1), a_offset=p["a_offset"])
+    if rows is None:
+        _compare(case, got, oracle.dqip_forward(case))
+    else:
+        _compare_sampled(case, got, rows)
+
+
+@pytest.mark.parametrize("p", _random_cases(2026, 28, big=False), ids=lambda p: f"{p['M']}x{p['N']}x{p['K']}")
+def test_random_shapes(gpu, p):
+    """Every output of the forward against the oracle, on seeded random cases."""
+    _run_random(gpu, p)
+
+
+@pytest.mark.parametrize("p", _random_cases(2027, 6, big=True), ids=lambda p: f"{p['M']}x{p['N']}x{p['K']}")
+def test_random_shapes_large_tiles(gpu, p):
+    """Seeded random cases on the 256 x 256 tiles: C and the int32 sums on two
+    rows of every 256-row tile plus the first and last, the quantized A, B,
+    scales and column sums whole."""
+    _run_random(gpu, p, rows=tile_rows(p["M"], p["seed"] % 97))
