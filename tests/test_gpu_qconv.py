@@ -126,3 +126,28 @@ def test_full_size_8x256x56x56(gpu):
         got = run_qconv(gpu, case)
         for n in range(got.shape[0]):
             assert np.array_equal(got[n], want[n]), f"call {call} image {n}: {np.sum(got[n] != want[n])} codes differ"
+
+
+def _random_conv_cases(seed, n):
+    """Seeded random 1x1 QLinearConv cases: batch 1-2, channels 1-600 in and
+    out (both sides of the persistent kernel's 256 limit), pixels 1-1200
+    (ragged against the 32-pixel items), every 8-bit type of x, w and y,
+    per-tensor or per-channel w scales, bias and w zero points on or off."""
+    r = np.random.default_rng(seed)
+    t8 = lambda: ["u8", "i8"][int(r.integers(2))]
+    return [dict(N=int(r.integers(1, 3)), C=int(r.integers(1, 600)), HW=int(r.integers(1, 1200)),
+                 M=int(r.integers(1, 600)), xt=t8(), wt=t8(), yt=t8(), pc=bool(r.integers(2)),
+                 bias=bool(r.integers(2)), wzp=bool(r.integers(2)), seed=int(r.integers(1 << 30)))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("p", _random_conv_cases(2029, 20),
+                         ids=lambda p: f"N{p['N']}C{p['C']}HW{p['HW']}M{p['M']}")
+def test_random_shapes(gpu, p):
+    """Every output code bit-exact against the oracle on seeded random cases."""
+    log(f"qconv1x1 random {p}")
+    case = W.qconv_random(p["N"], p["C"], p["HW"], p["M"], seed=p["seed"], x_type=p["xt"], w_type=p["wt"],
+                          y_type=p["yt"], per_channel=p["pc"], bias=p["bias"], w_zp=p["wzp"])
+    got = run_qconv(gpu, case)
+    want = oracle_qconv(case)
+    assert np.array_equal(got, want), f"{np.sum(got != want)} codes differ"

@@ -181,3 +181,41 @@ def test_dequantize_f16_matches_oracle(gpu, shape, axis, y_type):
         assert np.array_equal(got.view(np.uint16), want)
     else:
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def _random_qdq_cases(seed, n):
+    """Seeded random tensors of 1 to 5 dimensions (up to ~2 M elements, sizes
+    ragged against the kernels' 16-element vectors and 4096-element blocks),
+    an axis drawn over every position, negative ones included, or per tensor,
+    int8 or uint8 codes, with or without a zero point."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        nd = int(r.integers(1, 6))
+        while True:
+            shape = tuple(int(v) for v in r.integers(1, 90, nd))
+            if np.prod(shape) <= 2_000_000:
+                break
+        axis = None if r.integers(4) == 0 else int(r.integers(-nd, nd))
+        cases.append(dict(shape=shape, axis=axis, y_type=["i8", "u8"][int(r.integers(2))],
+                          has_zp=bool(r.integers(4)), seed=int(r.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("p", _random_qdq_cases(2028, 24), ids=lambda p: f"{p['shape']}-{p['axis']}")
+def test_qdq_random_shapes(gpu, p):
+    """Every code and every dequantized value bit-exact against the oracle, on
+    seeded random shapes and axes, with planted ties and saturating values."""
+    shape, axis, y_type = p["shape"], p["axis"], p["y_type"]
+    log(f"qdq random shape={shape} axis={axis} {y_type} zp={p['has_zp']} seed={p['seed']}")
+    ax = 0 if axis is None else axis % len(shape)
+    case = W.qdq_per_axis(seed=p["seed"], shape=shape, axis=ax, plant_every=29)
+    if axis is None:
+        scale, zp = np.float32([0.03]), np.array([5 if y_type == "u8" else -5])
+    else:
+        scale, zp = case["scale"], case["zp"]
+    if y_type == "u8":
+        zp = (np.asarray(zp).astype(np.int32) + 120).astype(np.uint8)
+    else:
+        zp = np.asarray(zp).astype(np.int8)
+    _check_both(gpu, case["x"], scale, zp if p["has_zp"] else None, axis, y_type)
