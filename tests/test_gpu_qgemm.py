@@ -294,3 +294,64 @@ def test_benchmark_products_full_size(gpu, kind):
     else:
         want = _want(np.ascontiguousarray(A[rows]), B, **dict(kw))
     _check({"Y": got["Y"][rows], "acc": got["acc"][rows]}, want, kw.get("y_type", "f32"), kw.get("bias"))
+
+
+# ------------------------------------------------------ seeded random cases
+
+def _random_qgemm_cases(seed, n):
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dyn = r.integers(4) == 0  # DynamicQuantizeMatMul: fp32 A quantized per tensor
+        p = dict(M=int(r.integers(1, 600)), N=int(r.integers(1, 600)), K=int(r.integers(1, 1500)),
+                 a=("f32" if dyn else ["u8", "i8"][int(r.integers(2))]), b_u8=bool(r.integers(2)),
+                 per_col=bool(r.integers(2)), bzp=[None, "tensor", "col"][int(r.integers(3))],
+                 seed=int(r.integers(1 << 30)))
+        if dyn:
+            p.update(tA=False, tB=False, C=None, alpha=1.0, y="f32", bias=bool(r.integers(2)))
+        else:
+            p.update(tA=bool(r.integers(2)), tB=bool(r.integers(2)),
+                     C=[None, "scalar", "N", "1N", "M1", "MN"][int(r.integers(6))],
+                     alpha=float(r.choice([1.0, 0.5, 1.75])), y=["f32", "u8", "i8"][int(r.integers(3))])
+            p["bias"] = p["y"] == "f32" and bool(r.integers(2))
+        out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("p", _random_qgemm_cases(2030, 24),
+                         ids=lambda p: f"{p['M']}x{p['N']}x{p['K']}-{p['a']}-{p['y']}")
+def test_random_quantized_products(gpu, p):
+    """Seeded random cases of the three operators: the int32 sums and 8-bit
+    outputs bit-exact, fp32 outputs within the bar. An 8-bit output's y_scale
+    is set from the oracle's fp32 output, so the codes spread over the range
+    and both ends saturate."""
+    log(f"quantized product random {p}")
+    M, N, K = p["M"], p["N"], p["K"]
+    r = np.random.default_rng(p["seed"])
+    if p["a"] == "f32":
+        A = r.normal(0.0, 1.0, (M, K)).astype(np.float32)
+        A[r.random((M, K)) < 0.01] *= 20.0
+    else:
+        A = _q8(r, (K, M) if p["tA"] else (M, K), p["a"] == "u8")
+    B = _q8(r, (N, K) if p["tB"] else (K, N), p["b_u8"])
+    bs = r.uniform(0.0005, 0.005, N if p["per_col"] else 1).astype(np.float32)
+    lo, hi = (100, 156) if p["b_u8"] else (-20, 21)
+    bz = None if p["bzp"] is None else r.integers(lo, hi, N if p["bzp"] == "col" else 1).astype(np.int32)
+    kw = dict(b_scale=bs, b_zp=bz)
+    if p["a"] != "f32":
+        kw.update(a_scale=np.float32(0.01), a_zp=int(r.integers(100, 156)) if p["a"] == "u8" else int(r.integers(-20, 21)),
+                  transA=p["tA"], transB=p["tB"], alpha=p["alpha"])
+        if p["C"] is not None:
+            shp = {"MN": (M, N), "N": (N,), "1N": (1, N), "M1": (M, 1), "scalar": ()}[p["C"]]
+            kw["C"] = r.integers(-20000, 20000, shp).astype(np.int32)
+    if p["bias"]:
+        kw["bias"] = r.uniform(-1, 1, N).astype(np.float32)
+    if p["y"] == "f32":
+        got = run_qgemm(gpu, A, B, accumulators=True, **kw)
+        _check(got, _want(A, B, **dict(kw)), "f32", kw.get("bias"))
+        return
+    yf, _ = _want(A, B, **dict(kw))
+    y_scale = np.float32(max(float(np.std(yf)), 1e-6) / 40.0)
+    y_zp = 128 if p["y"] == "u8" else 3
+    got = run_qgemm(gpu, A, B, accumulators=True, y_type=p["y"], y_scale=y_scale, y_zp=y_zp, **kw)
+    _check(got, _want(A, B, y_type=p["y"], y_scale=y_scale, y_zp=y_zp, **dict(kw)), p["y"])
