@@ -263,3 +263,62 @@ def test_contexts_with_different_patch_sizes_coexist(gpu):
     want = oracle.qlinear_conv2d(x, 0.02, 128, w[ms], ws[ms], np.zeros(len(ms), np.int32), 0.05, 128,
                                  bias=bias[ms], strides=(2, 2), pads=(3, 3, 3, 3), group=1, y_type="u8")
     assert np.array_equal(outs[0][:, ms], want)
+
+
+def _random_conv_cases(seed, n):
+    """Seeded random 2-D convolutions: 1 or 2 images, groups (1, 2, 4 or
+    depthwise, with a channel multiplier of 1 or 2), 1-80 channels a group,
+    kernels 1-7 each way, strides 1-3, dilations 1-2, each pad drawn on its
+    own, 1-40 rows and columns; at most about 2e8 multiply-adds a case."""
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        N = int(r.integers(1, 3))
+        kH, kW = int(r.integers(1, 8)), int(r.integers(1, 8))
+        st = (int(r.integers(1, 4)), int(r.integers(1, 4)))
+        dil = (int(r.integers(1, 3)), int(r.integers(1, 3)))
+        pads = tuple(int(r.integers(0, k)) if k > 1 else 0 for k in (kH, kW, kH, kW))
+        H, W = int(r.integers(1, 41)), int(r.integers(1, 41))
+        if H + pads[0] + pads[2] < dil[0] * (kH - 1) + 1 or W + pads[1] + pads[3] < dil[1] * (kW - 1) + 1:
+            continue
+        kind = int(r.integers(4))
+        if kind == 3:  # depthwise
+            C = int(r.integers(1, 65))
+            group, M = C, C * int(r.integers(1, 3))
+        else:
+            group = (1, 2, 4)[kind]
+            C, M = group * int(r.integers(1, 81)), group * int(r.integers(1, 81))
+        oH = (H + pads[0] + pads[2] - dil[0] * (kH - 1) - 1) // st[0] + 1
+        oW = (W + pads[1] + pads[3] - dil[1] * (kW - 1) - 1) // st[1] + 1
+        if N * M * oH * oW * (C // group) * kH * kW > 2e8:
+            continue
+        types = [("u8", "i8", "u8"), ("i8", "u8", "i8"), ("u8", "u8", "u8"), ("i8", "i8", "u8")][int(r.integers(4))]
+        cases.append(dict(case=(N, C, H, W, M, kH, kW, st, pads, dil, group), types=types,
+                          per_channel=bool(r.integers(2)), seed=int(r.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("p", _random_conv_cases(2031, 30), ids=lambda p: "-".join(map(str, p["case"][:7])))
+def test_qconv_random_attributes(gpu, p):
+    """Every output code bit-exact against the oracle on seeded random
+    attribute sets (the kernels picked by shape: implicit GEMM with or
+    without virtual channels and split reduction, depthwise, direct)."""
+    N, C, H, W, M, kH, kW, st, pads, dil, group = p["case"]
+    xt, wt, yt = p["types"]
+    r = np.random.default_rng(p["seed"])
+    x = _codes(r, (N, C, H, W), xt)
+    w = _codes(r, (M, C // group, kH, kW), wt)
+    nw = M if p["per_channel"] else 1
+    ws = r.uniform(0.002, 0.01, nw).astype(np.float32)
+    lo, hi = (0, 256) if wt == "u8" else (-128, 128)
+    wz = r.integers(lo, hi, nw) if p["per_channel"] else np.array([128 if wt == "u8" else 0])
+    xz = int(r.integers(0, 256)) if xt == "u8" else int(r.integers(-128, 128))
+    bias = r.integers(-20000, 20000, M).astype(np.int32)
+    ys, yz = np.float32(r.uniform(0.05, 0.5)), (128 if yt == "u8" else 0)
+    log(f"qconv random {p['case']} {p['types']} per_channel={p['per_channel']}")
+    want = oracle.qlinear_conv2d(x, 0.02, xz, w, ws, wz, ys, yz, bias=bias, strides=st, pads=pads,
+                                 dilations=dil, group=group, y_type=yt)
+    (got,), info = _run(gpu, x, 0.02, xz, w, ws, wz, ys, yz, yt, bias=bias, strides=st, pads=pads,
+                        dilations=dil, group=group)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ ({info})"
