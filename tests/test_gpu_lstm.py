@@ -189,3 +189,50 @@ def test_lstm_lengths_beyond_the_sequence_are_clamped(gpu):
     want = _oracle(okw)
     (got,), info = _gpu_lstm(gpu, c)
     _compare(got, want, info)
+
+
+_PLAIN_ACTS = ["Sigmoid", "Tanh", "Relu", "Softsign", "Softplus"]
+
+
+def _random_lstm_cases(seed, n):
+    """Seeded random cases: sequence 1-12, batch 1-70 (over the 32-entry
+    tiles), input 1-200, hidden 1-300 (ragged against the 8-unit tiles),
+    every direction, int8 or uint8 W and R, per-direction or per-column
+    scales, zero points, bias, peepholes, initial state and sequence_lens
+    (zero and ragged lengths) each on or off, clip, input_forget, and the
+    activations drawn from those without alpha / beta."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        seq, batch = int(r.integers(1, 13)), int(r.integers(1, 71))
+        direction = ["forward", "reverse", "bidirectional"][int(r.integers(3))]
+        opts = dict(direction=direction, w_type=["i8", "u8"][int(r.integers(2))],
+                    r_type=["i8", "u8"][int(r.integers(2))], per_channel=bool(r.integers(2)),
+                    zero_points=bool(r.integers(2)), bias=bool(r.integers(4)), peepholes=bool(r.integers(2)),
+                    initial=bool(r.integers(2)),
+                    lens=(None if r.integers(2) else [int(v) for v in r.integers(0, seq + 1, batch)]))
+        attrs = {}
+        if r.integers(3) == 0:
+            nact = 6 if direction == "bidirectional" else 3
+            attrs["activations"] = [_PLAIN_ACTS[int(i)] for i in r.integers(0, len(_PLAIN_ACTS), nact)]
+        if r.integers(3) == 0:
+            attrs["clip"] = float(r.uniform(0.5, 3.0))
+        if r.integers(4) == 0:
+            attrs["input_forget"] = 1
+        out.append(dict(seq=seq, batch=batch, nin=int(r.integers(1, 201)), h=int(r.integers(1, 301)),
+                        opts=opts, attrs=attrs, seed=int(r.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("p", _random_lstm_cases(2032, 20),
+                         ids=lambda p: f"s{p['seq']}b{p['batch']}i{p['nin']}h{p['h']}-{p['opts']['direction']}")
+def test_lstm_random_cases(gpu, p):
+    """Y, Y_h and Y_c within the fp32 bar of the oracle on seeded random cases."""
+    c = workloads.lstm_case(p["seq"], p["batch"], p["nin"], p["h"], seed=p["seed"], **p["opts"])
+    log(f"lstm random seq {p['seq']} batch {p['batch']} input {p['nin']} hidden {p['h']} {p['opts']} {p['attrs']}")
+    kw = dict(p["attrs"])
+    want = _oracle(c, activations=kw.get("activations"), activation_alpha=None, activation_beta=None,
+                   clip=kw.get("clip"), input_forget=kw.get("input_forget", 0))
+    (got,), info = _gpu_lstm(gpu, c, **kw)
+    log(f"  {info}")
+    _compare(got, want, info)
