@@ -404,3 +404,40 @@ def test_benchmark_workloads_full_size(gpu, kind):
         want = want.reshape(part.shape)
     assert part.shape == want.shape, (part.shape, want.shape)
     assert np.array_equal(part, want), f"{(part != want).sum()} of {part.size} differ"
+
+
+def _random_broadcast_cases(seed, n):
+    """Seeded random numpy-broadcast pairs: an output of rank 1-6 (dims 1-24,
+    at most ~300K elements); each operand drops some leading dims and sets
+    others to 1, on one side, the other or both."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        rank = int(r.integers(1, 7))
+        shape = [int(v) for v in r.integers(1, 25, rank)]
+        if np.prod(shape) > 300_000:
+            continue
+
+        def operand():
+            keep = int(r.integers(0, rank + 1)) if r.integers(3) == 0 else rank
+            s = shape[rank - keep:]
+            return tuple(1 if r.integers(3) == 0 else d for d in s)
+
+        out.append(dict(a=operand(), b=operand(), op=["add", "mul", "mulint"][int(r.integers(3))],
+                        t=["u8", "i8"][int(r.integers(2))], seed=int(r.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("p", _random_broadcast_cases(2033, 30), ids=lambda p: f"{p['op']}-{p['a']}x{p['b']}")
+def test_binary_random_broadcasts(gpu, p):
+    """Every output code bit-exact against the oracle on seeded random
+    broadcast shapes (the operands' canonical form: size-1 dims dropped,
+    neighbours merged)."""
+    r = np.random.default_rng(p["seed"])
+    A, B = _codes(r, p["a"], p["t"]), _codes(r, p["b"], p["t"])
+    prm = _params(r, p["op"], p["t"])
+    log(f"binary random {p['op']} {p['t']} {p['a']} x {p['b']}")
+    got = _run_binary(gpu, p["op"], p["t"], A, B, *prm)
+    want = _want_binary(p["op"], A, B, *prm)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ"
