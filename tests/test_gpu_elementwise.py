@@ -441,3 +441,44 @@ def test_binary_random_broadcasts(gpu, p):
     want = _want_binary(p["op"], A, B, *prm)
     assert got.shape == want.shape
     assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ"
+
+
+def _random_reduce_cases(seed, n):
+    """Seeded random reductions: rank 1-5 (dims 1-40, up to ~500K elements),
+    a random non-empty set of axes (negative indices allowed) or all of them,
+    sum or mean, int8 or uint8."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        rank = int(r.integers(1, 6))
+        shape = tuple(int(v) for v in r.integers(1, 41, rank))
+        if np.prod(shape) > 500_000:
+            continue
+        if r.integers(6) == 0:
+            axes = None
+        else:
+            ax = sorted(set(int(v) for v in r.integers(0, rank, int(r.integers(1, rank + 1)))))
+            axes = [a - rank if r.integers(2) else a for a in ax]
+        out.append(dict(shape=shape, axes=axes, mode=["sum", "mean"][int(r.integers(2))],
+                        t=["u8", "i8"][int(r.integers(2))], seed=int(r.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("p", _random_reduce_cases(2034, 30), ids=lambda p: f"{p['mode']}-{p['shape']}-{p['axes']}")
+def test_reduce_random_axes(gpu, p):
+    """ReduceSumInteger and QLinearReduceMean bit-exact against the oracle on
+    seeded random shapes and axis sets (rows, columns or the general kernel
+    by the canonical form)."""
+    r = np.random.default_rng(p["seed"])
+    t = p["t"]
+    X = _codes(r, p["shape"], t)
+    log(f"reduce random {p['mode']} {t} {p['shape']} axes {p['axes']}")
+    if p["mode"] == "sum":
+        got = _run_reduce(gpu, "sum", t, X, p["axes"])
+        want = oracle.reduce_sum_integer(X, p["axes"], keepdims=False).reshape(-1)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    else:
+        prm = (np.float32(0.0213), 5 if t == "i8" else 121, np.float32(0.0041), -7 if t == "i8" else 119)
+        got = _run_reduce(gpu, "mean", t, X, p["axes"], prm)
+        want = oracle.qlinear_reduce_mean(X, *prm, axes=p["axes"], keepdims=False).reshape(-1)
+        assert np.array_equal(got, want), f"{(got != want).sum()} of {got.size} differ"
